@@ -1,0 +1,67 @@
+"""Plant a mistake in a copy of the oracle (on the CPU) and require that some
+pin catches it.  This shows the pins are sensitive to the plausible errors: a
+dropped term, a wrong sign, index or operand order."""
+import importlib.util
+import os
+
+import pytest
+
+import oracle_pins
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "ssm_oracle.py")
+
+MUTATIONS = {
+    "update_sign": ("h = dA * h + dB * u[:, t, :, None]", "h = dA * h - dB * u[:, t, :, None]"),
+    "decay_sign": ("dA = np.exp(dtt * A[None, :, :])", "dA = np.exp(-dtt * A[None, :, :])"),
+    "readout_wrong_t": ("yt = np.sum(C[:, t, None, :] * h, axis=-1)",
+                        "yt = np.sum(C[:, max(t - 1, 0), None, :] * h, axis=-1)"),
+    "drop_D": ("            yt = yt + _f64(D)[None, :] * u[:, t, :]\n        y[:, t, :] = yt\n    if z",
+               "            yt = yt\n        y[:, t, :] = yt\n    if z"),
+    "gate_sigmoid": ("    if z is not None:\n        y = y * silu(z)\n    return y, h\n",
+                     "    if z is not None:\n        y = y * sigmoid(z)\n    return y, h\n"),
+    "conv_taps_reversed": ("xc += w[None, None, :, k] * xpad[:, k:k + L, :]",
+                           "xc += w[None, None, :, K - 1 - k] * xpad[:, k:k + L, :]"),
+    "conv_cache_shifted": ("xpad[:, L:L + K - 1, :]", "xpad[:, L - 1:L + K - 2, :]"),
+    "softplus_sign": ("return np.logaddexp(0.0, _f64(x))", "return np.logaddexp(0.0, -_f64(x))"),
+    "no_upper_clip": ("s = np.minimum(s, float(hi))", "s = s"),
+    "rank1_sum": ("_f64(dt_raw)[..., None] * _f64(w)[None, None, :]", "_f64(dt_raw)[..., None] + _f64(w)[None, None, :]"),
+    "zoh_wrong": ("dB = (dA - 1.0) / A[None, :, :] * B[:, t, None, :]", "dB = (dA - 1.0) * A[None, :, :] * B[:, t, None, :]"),
+    "decode_drops_cache": ("conv_cache=conv_cache if conv_w is not None else None", "conv_cache=None"),
+    "blelloch_order": ("tree[i] = op(tree[i], left)", "tree[i] = op(left, tree[i])"),
+    "compose_order": ("return (a1 * a2, a2 * b1 + b2)", "return (a1 * a2, a1 * b2 + b1)"),
+    "chunk_prod_reset": ("prod = prod * dA", "prod = dA"),
+    "ssd_exclusive_cumsum": ("dA = np.cumsum(dtc * A[None, None, :], axis=1)",
+                             "dA = np.cumsum(dtc * A[None, None, :], axis=1) - dtc * A[None, None, :]"),
+    "ssd_strict_mask": ("causal = ls[None, :] <= ls[:, None]", "causal = ls[None, :] < ls[:, None]"),
+    "ssd_state_drops_dt": ("wgt = np.exp(last[:, None, :] - dA) * dtc", "wgt = np.exp(last[:, None, :] - dA)"),
+    "ssd_state_no_decay": ("S = np.exp(last)[:, :, None, None] * S + np.einsum", "S = S + np.einsum"),
+    "ssd_prev_no_decay": ("o += np.exp(dA)[..., None] * np.einsum", "o += np.einsum"),
+    "ssd_group_map": ("return np.arange(H) // (H // G)", "return np.arange(H) % G"),
+    "ssd_cb_transposed": ('cb = np.einsum("blhn,bshn->bhls", Ch, Bh)', 'cb = np.einsum("blhn,bshn->bhsl", Ch, Bh)'),
+    "ssd_seq_dt_dropped": ("S = a[:, :, None, None] * S + (dt[:, t, :, None] * x[:, t])[..., None]",
+                           "S = a[:, :, None, None] * S + (x[:, t])[..., None]"),
+    "a_from_log_sign": ("return -np.exp(_f64(A_log))", "return np.exp(_f64(A_log))"),
+}
+
+
+def _load_mutant(name, old, new):
+    """The oracle's source with the first occurrence of `old` replaced by `new`."""
+    with open(ORACLE_SRC) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation {name}: pattern not found"
+    spec = importlib.util.spec_from_loader(f"oracle_mutant_{name}", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    exec(compile(src.replace(old, new, 1), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_some_pin_catches_mutation(name):
+    mod = _load_mutant(name, *MUTATIONS[name])
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as exc:  # a failing assertion or a crash both count
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"no pin caught the planted mistake {name}"
