@@ -1,0 +1,236 @@
+/*
+ * ssm_mi355x.h -- C ABI of the MI355X (gfx950) selective-scan library.
+ *
+ * Three entry points, one per path of the Mamba-style selective state space
+ * layer described by the pages:
+ *
+ *   ssm_scan_fwd        full-sequence (prefill) scan: causal depthwise conv1d
+ *                       + SiLU, dt = clip(softplus(dt_proj + dt_bias)), the
+ *                       diagonal recurrence h_t = exp(dt*A) h_{t-1} + dt*B_t*u_t,
+ *                       y_t = C_t . h_t + D*u_t, gate y * SiLU(z).  Page
+ *                       "Axon-SSM: selective state space model", sections
+ *                       "Algorithm", "SSM scan", "Discretization", "JIT-compiled
+ *                       kernels" and "Autoregressive decoding" (prefill,
+ *                       cache = None).
+ *   ssm_decode_step     one token of autoregressive decoding that updates
+ *                       [conv_cache, ssm_state] in place.  Same page, section
+ *                       "Autoregressive decoding" (decode, cache =
+ *                       [conv_cache, ssm_state]).
+ *   ssm_chunk_scan_fwd  multi-head chunked scan (scalar A per head): page "What
+ *                       is the Mamba model?", sections "chunkscan" and
+ *                       "chunkscan implementation", chunk output formula
+ *                       out[l] = sum_{s<=l} cb[l,s] e^{dA[l]-dA[s]} dt[s] x[s]
+ *                              + e^{dA[l]} C[l] prev_states + D x[l],
+ *                       with the chunk-final state carried to the next chunk.
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *    allocates nothing, keeps no per-call state, never copies between host and
+ *    device and never synchronises.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *    null stream) and the call returns at once.  Asynchronous kernel faults
+ *    surface at the caller's next synchronisation.
+ *  - Layouts are dense row-major in the order written next to each field, last
+ *    index fastest.  Pointers must be aligned to their element size.
+ *  - Every argument error is detected before anything is launched: the call
+ *    returns SSM_ERR_INVALID_ARG or SSM_ERR_UNSUPPORTED and writes nothing;
+ *    ssm_last_error() then names the field.  A failed launch returns
+ *    SSM_ERR_HIP.  NaN/Inf inputs are not checked; they propagate.
+ *  - Outputs (y, out) must not overlap any input.  State and cache outputs may
+ *    alias their inputs exactly (in-place update).
+ *  - Floating point: all arithmetic is fp32; bf16 inputs are widened exactly;
+ *    bf16 outputs are rounded to nearest-even.
+ */
+#ifndef SSM_MI355X_H
+#define SSM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+/* element types (int32 fields in the structs below) */
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+/* return codes */
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_INVALID_ARG = 1, /* a null required pointer, a negative size, bad bounds, wrong struct_size */
+  SSM_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement (e.g. d_state != 16) */
+  SSM_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_size query */
+  SSM_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} ssm_status_t;
+
+/* ------------------------------------------------------------------------
+ * Full-sequence scan (prefill).
+ *
+ * Shapes: Bt = batch, L = seqlen, E = dim (channels), N = d_state.
+ *   x             (Bt, L, E) x_dtype     pre-conv x_branch when conv_w != NULL, else u itself
+ *   conv_w        (E, K) f32 or NULL     causal depthwise conv; NULL skips conv and SiLU.
+ *                                        xc[t] = sum_k conv_w[e,k] * xpad[t+k] (+ conv_b[e]),
+ *                                        xpad = (conv_cache_in or zeros, x) along t, so
+ *                                        conv_w[e,K-1] multiplies the current token;
+ *                                        u = SiLU(xc).  K = conv_k must be 4.
+ *   conv_b        (E) f32 or NULL
+ *   conv_cache_in (Bt, E, K-1) f32 or NULL (zeros): raw pre-conv inputs before t=0, oldest first
+ *   conv_cache_out(Bt, E, K-1) f32 or NULL: the last K-1 raw inputs (including cache_in
+ *                                        values when L < K-1), oldest first; may alias conv_cache_in
+ *   dt            dt_rank1 != 0: (Bt, L) f32 r, and pre = dt_w[e] * r[b,t] (dt_proj 1 -> E)
+ *                 dt_rank1 == 0: (Bt, L, E) dt_dtype, and pre = dt[b,t,e]
+ *   dt_w          (E) f32, required iff dt_rank1
+ *   dt_bias       (E) f32 or NULL (zero)
+ *   dt_softplus   nonzero: dt = clip(softplus(pre + dt_bias), dt_min, dt_max)
+ *                 zero:    dt = clip(pre + dt_bias, dt_min, dt_max)
+ *   dt_min/dt_max clip bounds (inclusive); -INFINITY / +INFINITY disable a side; dt_min <= dt_max
+ *   A             (E, N) f32, the continuous-time diagonal (normally A = -exp(A_log) < 0)
+ *   B, C          (Bt, L, N) bc_dtype
+ *   D             (E) f32 or NULL (no skip term)
+ *   z             (Bt, L, E) z_dtype or NULL (no gate); z_dtype must equal x_dtype
+ *   ssm_state_in  (Bt, E, N) f32 or NULL (zeros, the prefill start)
+ *   ssm_state_out (Bt, E, N) f32 or NULL; may alias ssm_state_in
+ *   y             (Bt, L, E) y_dtype: y_t = (C_t . h_t + D*u_t) * SiLU(z_t)
+ *   workspace     device scratch of at least ssm_scan_workspace_size(p) bytes (may be
+ *                 NULL when that size is 0); 256-byte aligned; not touched by other calls
+ *   time_split    0: the library chooses; >= 1: split the sequence into that many
+ *                 segments scanned in parallel and combined (at most 16)
+ * Supported: N = 16.  L = 0 only copies the state/cache inputs to the outputs.
+ * ---------------------------------------------------------------------- */
+typedef struct ssm_scan_params {
+  uint32_t struct_size; /* = sizeof(ssm_scan_params_t) */
+  int32_t batch, seqlen, dim, d_state;
+  int32_t conv_k;
+  const void *x;
+  int32_t x_dtype;
+  const float *conv_w;
+  const float *conv_b;
+  const float *conv_cache_in;
+  float *conv_cache_out;
+  const void *dt;
+  int32_t dt_dtype;
+  int32_t dt_rank1;
+  const float *dt_w;
+  const float *dt_bias;
+  int32_t dt_softplus;
+  float dt_min, dt_max;
+  const float *A;
+  const void *B;
+  const void *C;
+  int32_t bc_dtype;
+  const float *D;
+  const void *z;
+  int32_t z_dtype;
+  const float *ssm_state_in;
+  float *ssm_state_out;
+  void *y;
+  int32_t y_dtype;
+  int32_t time_split;
+  void *workspace;
+  size_t workspace_bytes;
+} ssm_scan_params_t;
+
+ssm_status_t ssm_scan_fwd(const ssm_scan_params_t *p, void *stream);
+size_t ssm_scan_workspace_size(const ssm_scan_params_t *p);
+/* Validation only: the status ssm_scan_fwd would return before launching. */
+ssm_status_t ssm_scan_check(const ssm_scan_params_t *p);
+
+/* ------------------------------------------------------------------------
+ * One decode step, in place.  Shapes as above with L = 1:
+ *   x (Bt, E) x_dtype new token (pre-conv when conv_w != NULL); z (Bt, E) or NULL;
+ *   dt: dt_rank1 ? (Bt) f32 r : (Bt, E) dt_dtype;  B, C (Bt, N) bc_dtype;
+ *   conv_cache (Bt, E, K-1) f32, read then overwritten with the window shifted by one
+ *   (required iff conv_w != NULL);  ssm_state (Bt, E, N) f32, read then overwritten;
+ *   y (Bt, E) y_dtype.
+ * ssm_state and A must be 16-byte aligned.
+ * The result equals ssm_scan_fwd with L = 1, conv_cache_in = conv_cache_out =
+ * conv_cache and ssm_state_in = ssm_state_out = ssm_state.
+ * ---------------------------------------------------------------------- */
+typedef struct ssm_decode_params {
+  uint32_t struct_size; /* = sizeof(ssm_decode_params_t) */
+  int32_t batch, dim, d_state, conv_k;
+  const void *x;
+  int32_t x_dtype;
+  const float *conv_w;
+  const float *conv_b;
+  float *conv_cache;
+  const void *dt;
+  int32_t dt_dtype;
+  int32_t dt_rank1;
+  const float *dt_w;
+  const float *dt_bias;
+  int32_t dt_softplus;
+  float dt_min, dt_max;
+  const float *A;
+  const void *B;
+  const void *C;
+  int32_t bc_dtype;
+  const float *D;
+  const void *z;
+  int32_t z_dtype;
+  float *ssm_state;
+  void *y;
+  int32_t y_dtype;
+} ssm_decode_params_t;
+
+ssm_status_t ssm_decode_step(const ssm_decode_params_t *p, void *stream);
+ssm_status_t ssm_decode_check(const ssm_decode_params_t *p);
+
+/* ------------------------------------------------------------------------
+ * Multi-head chunked scan (SSD form), scalar A per head.
+ *   x         (Bt, L, H, P) x_dtype
+ *   dt        (Bt, L, H) f32 raw; dt = clip(softplus(dt + dt_bias[h]), dt_min, dt_max)
+ *             (softplus skipped when dt_softplus == 0)
+ *   dt_bias   (H) f32 or NULL
+ *   A         (H) f32 (negative)
+ *   B, C      (Bt, L, G, N) bc_dtype; head h reads group h / (H / G)
+ *   D         (H) f32 (d_per_channel == 0) or (H, P) f32 (d_per_channel != 0) or NULL
+ *   state_in  (Bt, H, P, N) f32 or NULL (zeros); state_out (Bt, H, P, N) f32 or NULL
+ *   out       (Bt, L, H, P) out_dtype
+ *   dA[l] = sum_{i<=l} dt[i] A_h inside each chunk of chunk_size tokens (inclusive);
+ *   state passing: S <- e^{dA[Q-1]} S + sum_s e^{dA[Q-1]-dA[s]} dt[s] x[s] (outer) B[s].
+ * Requires L % chunk_size == 0 (SSM_ERR_INVALID_ARG otherwise).
+ * Supported: N = 64, P % 16 == 0 and P <= 128, chunk_size = 128.
+ * ---------------------------------------------------------------------- */
+typedef struct ssm_chunk_params {
+  uint32_t struct_size; /* = sizeof(ssm_chunk_params_t) */
+  int32_t batch, seqlen, nheads, headdim, ngroups, d_state, chunk_size;
+  const void *x;
+  int32_t x_dtype;
+  const float *dt;
+  const float *dt_bias;
+  int32_t dt_softplus;
+  float dt_min, dt_max;
+  const float *A;
+  const void *B;
+  const void *C;
+  int32_t bc_dtype;
+  const float *D;
+  int32_t d_per_channel;
+  const float *state_in;
+  float *state_out;
+  void *out;
+  int32_t out_dtype;
+  void *workspace;
+  size_t workspace_bytes;
+} ssm_chunk_params_t;
+
+ssm_status_t ssm_chunk_scan_fwd(const ssm_chunk_params_t *p, void *stream);
+size_t ssm_chunk_scan_workspace_size(const ssm_chunk_params_t *p);
+ssm_status_t ssm_chunk_scan_check(const ssm_chunk_params_t *p);
+
+/* ------------------------------------------------------------------------ */
+const char *ssm_status_string(int32_t status);
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char *ssm_last_error(void);
+int32_t ssm_abi_version(void);
+/* sizeof of a params struct: which = 0 scan, 1 decode, 2 chunk; 0 otherwise. */
+size_t ssm_params_sizeof(int32_t which);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_MI355X_H */

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) selective-scan hot path: fused prefill scan, in-place decode
+step and multi-head chunked scan, as hand-written HIP kernels behind the C ABI
+of include/ssm_mi355x.h.  This package is the thin Python binding."""
+from .binding import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    SsmError,
+    chunk_scan_fwd,
+    decode_step,
+    lib,
+    scan_fwd,
+)

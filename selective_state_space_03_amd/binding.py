@@ -1,0 +1,289 @@
+"""Thin Python binding of libssm_mi355x.so (the C ABI in include/ssm_mi355x.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype, shape
+and contiguity, outputs and workspace are allocated with torch, and raw device
+pointers plus the current HIP stream go through ctypes.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssm_mi355x.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED", 3: "SSM_ERR_WORKSPACE", 4: "SSM_ERR_HIP"}
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_f32 = ctypes.c_float
+
+
+class ScanParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("batch", _i32), ("seqlen", _i32), ("dim", _i32), ("d_state", _i32),
+        ("conv_k", _i32), ("x", _vp), ("x_dtype", _i32), ("conv_w", _vp), ("conv_b", _vp),
+        ("conv_cache_in", _vp), ("conv_cache_out", _vp), ("dt", _vp), ("dt_dtype", _i32), ("dt_rank1", _i32),
+        ("dt_w", _vp), ("dt_bias", _vp), ("dt_softplus", _i32), ("dt_min", _f32), ("dt_max", _f32),
+        ("A", _vp), ("B", _vp), ("C", _vp), ("bc_dtype", _i32), ("D", _vp), ("z", _vp), ("z_dtype", _i32),
+        ("ssm_state_in", _vp), ("ssm_state_out", _vp), ("y", _vp), ("y_dtype", _i32), ("time_split", _i32),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("batch", _i32), ("dim", _i32), ("d_state", _i32), ("conv_k", _i32),
+        ("x", _vp), ("x_dtype", _i32), ("conv_w", _vp), ("conv_b", _vp), ("conv_cache", _vp),
+        ("dt", _vp), ("dt_dtype", _i32), ("dt_rank1", _i32), ("dt_w", _vp), ("dt_bias", _vp),
+        ("dt_softplus", _i32), ("dt_min", _f32), ("dt_max", _f32), ("A", _vp), ("B", _vp), ("C", _vp),
+        ("bc_dtype", _i32), ("D", _vp), ("z", _vp), ("z_dtype", _i32), ("ssm_state", _vp), ("y", _vp),
+        ("y_dtype", _i32),
+    ]
+
+
+class ChunkParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("batch", _i32), ("seqlen", _i32), ("nheads", _i32), ("headdim", _i32),
+        ("ngroups", _i32), ("d_state", _i32), ("chunk_size", _i32), ("x", _vp), ("x_dtype", _i32),
+        ("dt", _vp), ("dt_bias", _vp), ("dt_softplus", _i32), ("dt_min", _f32), ("dt_max", _f32),
+        ("A", _vp), ("B", _vp), ("C", _vp), ("bc_dtype", _i32), ("D", _vp), ("d_per_channel", _i32),
+        ("state_in", _vp), ("state_out", _vp), ("out", _vp), ("out_dtype", _i32),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+EXPORTED = [
+    "ssm_scan_fwd", "ssm_scan_workspace_size", "ssm_scan_check",
+    "ssm_decode_step", "ssm_decode_check",
+    "ssm_chunk_scan_fwd", "ssm_chunk_scan_workspace_size", "ssm_chunk_scan_check",
+    "ssm_status_string", "ssm_last_error", "ssm_abi_version", "ssm_params_sizeof",
+]
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (fails loudly when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing (run __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    L.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanParams), _vp]
+    L.ssm_scan_fwd.restype = _i32
+    L.ssm_scan_check.argtypes = [ctypes.POINTER(ScanParams)]
+    L.ssm_scan_check.restype = _i32
+    L.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanParams)]
+    L.ssm_scan_workspace_size.restype = ctypes.c_size_t
+    L.ssm_decode_step.argtypes = [ctypes.POINTER(DecodeParams), _vp]
+    L.ssm_decode_step.restype = _i32
+    L.ssm_decode_check.argtypes = [ctypes.POINTER(DecodeParams)]
+    L.ssm_decode_check.restype = _i32
+    L.ssm_chunk_scan_fwd.argtypes = [ctypes.POINTER(ChunkParams), _vp]
+    L.ssm_chunk_scan_fwd.restype = _i32
+    L.ssm_chunk_scan_check.argtypes = [ctypes.POINTER(ChunkParams)]
+    L.ssm_chunk_scan_check.restype = _i32
+    L.ssm_chunk_scan_workspace_size.argtypes = [ctypes.POINTER(ChunkParams)]
+    L.ssm_chunk_scan_workspace_size.restype = ctypes.c_size_t
+    L.ssm_status_string.argtypes = [_i32]
+    L.ssm_status_string.restype = ctypes.c_char_p
+    L.ssm_last_error.argtypes = []
+    L.ssm_last_error.restype = ctypes.c_char_p
+    L.ssm_abi_version.argtypes = []
+    L.ssm_abi_version.restype = _i32
+    L.ssm_params_sizeof.argtypes = [_i32]
+    L.ssm_params_sizeof.restype = ctypes.c_size_t
+    for i, st in enumerate((ScanParams, DecodeParams, ChunkParams)):
+        if L.ssm_params_sizeof(i) != ctypes.sizeof(st):
+            raise RuntimeError(f"ctypes mirror of params struct {i} does not match the library")
+    _lib = L
+    return L
+
+
+class SsmError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def _raise(status: int):
+    if status != 0:
+        raise SsmError(status, lib().ssm_last_error().decode())
+
+
+_DT = {torch.float32: SSM_F32, torch.bfloat16: SSM_BF16}
+
+
+def _code(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"{name}: dtype {t.dtype} not supported (float32 or bfloat16)")
+    return _DT[t.dtype]
+
+
+def _ptr(t, name, shape=None, dtype=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _bound(v, default):
+    return float(default if v is None else v)
+
+
+def scan_fwd(x, A, B, C, dt, *, D=None, z=None, conv_w=None, conv_b=None, conv_cache_in=None,
+             conv_cache_out=None, dt_rank1=False, dt_w=None, dt_bias=None, dt_softplus=True,
+             dt_min=None, dt_max=None, ssm_state_in=None, ssm_state_out=None, y=None,
+             y_dtype=None, time_split=0, workspace=None, stream=None):
+    """Full-sequence selective scan (ssm_scan_fwd).  Returns y (batch, L, E)."""
+    L_ = lib()
+    batch, seqlen, dim = x.shape
+    dev = x.device
+    d_state = A.shape[1]
+    if y is None:
+        y = torch.empty((batch, seqlen, dim), dtype=y_dtype or x.dtype, device=dev)
+    f32 = torch.float32
+    p = ScanParams()
+    p.struct_size = ctypes.sizeof(ScanParams)
+    p.batch, p.seqlen, p.dim, p.d_state = batch, seqlen, dim, d_state
+    p.conv_k = conv_w.shape[1] if conv_w is not None else 0
+    p.x = _ptr(x, "x", (batch, seqlen, dim), device=dev)
+    p.x_dtype = _code(x, "x")
+    p.conv_w = _ptr(conv_w, "conv_w", (dim, p.conv_k) if conv_w is not None else None, f32, dev)
+    p.conv_b = _ptr(conv_b, "conv_b", (dim,), f32, dev)
+    p.conv_cache_in = _ptr(conv_cache_in, "conv_cache_in", (batch, dim, 3), f32, dev)
+    p.conv_cache_out = _ptr(conv_cache_out, "conv_cache_out", (batch, dim, 3), f32, dev)
+    p.dt_rank1 = 1 if dt_rank1 else 0
+    p.dt = _ptr(dt, "dt", (batch, seqlen) if dt_rank1 else (batch, seqlen, dim), device=dev)
+    p.dt_dtype = _code(dt, "dt")
+    p.dt_w = _ptr(dt_w, "dt_w", (dim,), f32, dev)
+    p.dt_bias = _ptr(dt_bias, "dt_bias", (dim,), f32, dev)
+    p.dt_softplus = 1 if dt_softplus else 0
+    p.dt_min = _bound(dt_min, -math.inf)
+    p.dt_max = _bound(dt_max, math.inf)
+    p.A = _ptr(A, "A", (dim, d_state), f32, dev)
+    p.B = _ptr(B, "B", (batch, seqlen, d_state), device=dev)
+    p.C = _ptr(C, "C", (batch, seqlen, d_state), B.dtype, dev)
+    p.bc_dtype = _code(B, "B")
+    p.D = _ptr(D, "D", (dim,), f32, dev)
+    p.z = _ptr(z, "z", (batch, seqlen, dim), device=dev)
+    p.z_dtype = _code(z, "z") if z is not None else 0
+    p.ssm_state_in = _ptr(ssm_state_in, "ssm_state_in", (batch, dim, d_state), f32, dev)
+    p.ssm_state_out = _ptr(ssm_state_out, "ssm_state_out", (batch, dim, d_state), f32, dev)
+    p.y = _ptr(y, "y", (batch, seqlen, dim), device=dev)
+    p.y_dtype = _code(y, "y")
+    p.time_split = int(time_split)
+    need = L_.ssm_scan_workspace_size(ctypes.byref(p))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    p.workspace = _ptr(workspace, "workspace", device=dev)
+    p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _raise(L_.ssm_scan_fwd(ctypes.byref(p), _stream(dev, stream)))
+    return y
+
+
+def decode_step(x, A, B, C, dt, ssm_state, *, conv_cache=None, D=None, z=None, conv_w=None, conv_b=None,
+                dt_rank1=False, dt_w=None, dt_bias=None, dt_softplus=True, dt_min=None, dt_max=None,
+                y=None, y_dtype=None, stream=None):
+    """One decode step (ssm_decode_step): updates ssm_state and conv_cache in place, returns y (batch, E)."""
+    L_ = lib()
+    batch, dim = x.shape
+    dev = x.device
+    d_state = A.shape[1]
+    if y is None:
+        y = torch.empty((batch, dim), dtype=y_dtype or x.dtype, device=dev)
+    f32 = torch.float32
+    p = DecodeParams()
+    p.struct_size = ctypes.sizeof(DecodeParams)
+    p.batch, p.dim, p.d_state = batch, dim, d_state
+    p.conv_k = conv_w.shape[1] if conv_w is not None else 0
+    p.x = _ptr(x, "x", (batch, dim), device=dev)
+    p.x_dtype = _code(x, "x")
+    p.conv_w = _ptr(conv_w, "conv_w", (dim, p.conv_k) if conv_w is not None else None, f32, dev)
+    p.conv_b = _ptr(conv_b, "conv_b", (dim,), f32, dev)
+    p.conv_cache = _ptr(conv_cache, "conv_cache", (batch, dim, 3), f32, dev)
+    p.dt_rank1 = 1 if dt_rank1 else 0
+    p.dt = _ptr(dt, "dt", (batch,) if dt_rank1 else (batch, dim), device=dev)
+    p.dt_dtype = _code(dt, "dt")
+    p.dt_w = _ptr(dt_w, "dt_w", (dim,), f32, dev)
+    p.dt_bias = _ptr(dt_bias, "dt_bias", (dim,), f32, dev)
+    p.dt_softplus = 1 if dt_softplus else 0
+    p.dt_min = _bound(dt_min, -math.inf)
+    p.dt_max = _bound(dt_max, math.inf)
+    p.A = _ptr(A, "A", (dim, d_state), f32, dev)
+    p.B = _ptr(B, "B", (batch, d_state), device=dev)
+    p.C = _ptr(C, "C", (batch, d_state), B.dtype, dev)
+    p.bc_dtype = _code(B, "B")
+    p.D = _ptr(D, "D", (dim,), f32, dev)
+    p.z = _ptr(z, "z", (batch, dim), device=dev)
+    p.z_dtype = _code(z, "z") if z is not None else 0
+    p.ssm_state = _ptr(ssm_state, "ssm_state", (batch, dim, d_state), f32, dev)
+    p.y = _ptr(y, "y", (batch, dim), device=dev)
+    p.y_dtype = _code(y, "y")
+    _raise(L_.ssm_decode_step(ctypes.byref(p), _stream(dev, stream)))
+    return y
+
+
+def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size=128, D=None, dt_bias=None, dt_softplus=True, dt_min=None,
+                   dt_max=None, state_in=None, state_out=None, out=None, out_dtype=None, workspace=None,
+                   stream=None):
+    """Multi-head chunked scan (ssm_chunk_scan_fwd).  Returns out (batch, L, H, P)."""
+    L_ = lib()
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, d_state = B.shape[2], B.shape[3]
+    dev = x.device
+    if out is None:
+        out = torch.empty((batch, seqlen, nheads, headdim), dtype=out_dtype or x.dtype, device=dev)
+    f32 = torch.float32
+    p = ChunkParams()
+    p.struct_size = ctypes.sizeof(ChunkParams)
+    p.batch, p.seqlen, p.nheads, p.headdim = batch, seqlen, nheads, headdim
+    p.ngroups, p.d_state, p.chunk_size = ngroups, d_state, int(chunk_size)
+    p.x = _ptr(x, "x", (batch, seqlen, nheads, headdim), device=dev)
+    p.x_dtype = _code(x, "x")
+    p.dt = _ptr(dt, "dt", (batch, seqlen, nheads), f32, dev)
+    p.dt_bias = _ptr(dt_bias, "dt_bias", (nheads,), f32, dev)
+    p.dt_softplus = 1 if dt_softplus else 0
+    p.dt_min = _bound(dt_min, -math.inf)
+    p.dt_max = _bound(dt_max, math.inf)
+    p.A = _ptr(A, "A", (nheads,), f32, dev)
+    p.B = _ptr(B, "B", (batch, seqlen, ngroups, d_state), device=dev)
+    p.C = _ptr(C, "C", (batch, seqlen, ngroups, d_state), B.dtype, dev)
+    p.bc_dtype = _code(B, "B")
+    if D is not None:
+        p.d_per_channel = 1 if D.dim() == 2 else 0
+        p.D = _ptr(D, "D", (nheads, headdim) if D.dim() == 2 else (nheads,), f32, dev)
+    p.state_in = _ptr(state_in, "state_in", (batch, nheads, headdim, d_state), f32, dev)
+    p.state_out = _ptr(state_out, "state_out", (batch, nheads, headdim, d_state), f32, dev)
+    p.out = _ptr(out, "out", (batch, seqlen, nheads, headdim), device=dev)
+    p.out_dtype = _code(out, "out")
+    need = L_.ssm_chunk_scan_workspace_size(ctypes.byref(p))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    p.workspace = _ptr(workspace, "workspace", device=dev)
+    p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _raise(L_.ssm_chunk_scan_fwd(ctypes.byref(p), _stream(dev, stream)))
+    return out

@@ -1,0 +1,438 @@
+// Host side of the C ABI declared in include/ssm_mi355x.h: argument
+// validation (pure host code, runs without a GPU), workspace sizing, variant
+// choice and launch on the caller's stream.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <string>
+
+#include "../../include/ssm_mi355x.h"
+#include "ssm_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ssm_status_t fail(ssm_status_t s, const char* fmt, const char* what) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), fmt, what);
+  g_last_error = buf;
+  return s;
+}
+
+ssm_status_t ok() {
+  g_last_error.clear();
+  return SSM_OK;
+}
+
+bool valid_dtype(int32_t d) { return d == SSM_F32 || d == SSM_BF16; }
+size_t esize(int32_t d) { return d == SSM_BF16 ? 2 : 4; }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlaps(Range a, Range b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const auto a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Outward-rounded thresholds of the softplus/clip shortcut: pre >= sp_hi
+// guarantees softplus(pre) >= hi, pre <= sp_lo guarantees softplus(pre) <= lo.
+void softplus_thresholds(float lo, float hi, float* sp_lo, float* sp_hi) {
+  const float inf = std::numeric_limits<float>::infinity();
+  if (!(hi < inf)) {
+    *sp_hi = inf;
+  } else if (hi <= 0.0f) {
+    *sp_hi = -inf;
+  } else {
+    const double t = std::log(std::expm1(static_cast<double>(hi)));
+    float f = static_cast<float>(t);
+    if (static_cast<double>(f) < t) f = std::nextafter(f, inf);
+    *sp_hi = std::nextafter(f, inf);  // one more ulp of margin for the fp32 comparison
+  }
+  if (!(lo > 0.0f)) {
+    *sp_lo = -inf;
+  } else if (!(lo < inf)) {
+    *sp_lo = inf;
+  } else {
+    const double t = std::log(std::expm1(static_cast<double>(lo)));
+    float f = static_cast<float>(t);
+    if (static_cast<double>(f) > t) f = std::nextafter(f, -inf);
+    *sp_lo = std::nextafter(f, -inf);
+  }
+}
+
+ssm_status_t check_dt_bounds(float lo, float hi) {
+  if (std::isnan(lo) || std::isnan(hi)) return fail(SSM_ERR_INVALID_ARG, "%s is NaN", "dt_min/dt_max");
+  if (lo > hi) return fail(SSM_ERR_INVALID_ARG, "%s: dt_min > dt_max", "dt bounds");
+  return SSM_OK;
+}
+
+// ---------------------------------------------------------------- scan
+
+int scan_split(const ssm_scan_params_t* p) {
+  const int L = p->seqlen;
+  if (L <= 1) return 1;
+  int s = p->time_split;
+  if (s <= 0) {
+    const long groups = static_cast<long>(p->batch) * ((p->dim + 63) / 64);
+    const long target = 2048;  // waves: two per SIMD on 256 CUs x 4 SIMDs
+    s = groups >= target ? 1 : static_cast<int>((target + groups - 1) / groups);
+    s = std::min(s, std::max(1, L / 64));
+  }
+  s = std::min(std::min(s, ssm::kScanMaxSplit), L);
+  const int seg = (L + s - 1) / s;
+  return (L + seg - 1) / seg;
+}
+
+size_t scan_ws(const ssm_scan_params_t* p) {
+  if (p->batch <= 0 || p->seqlen <= 0) return 0;
+  return ssm::scan_bcr_bytes(p->batch, p->seqlen);
+}
+
+ssm_status_t scan_check(const ssm_scan_params_t* p) {
+  if (!p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "params");
+  if (p->struct_size != sizeof(ssm_scan_params_t))
+    return fail(SSM_ERR_INVALID_ARG, "%s does not match this library", "struct_size");
+  if (p->batch < 0 || p->seqlen < 0 || p->dim <= 0)
+    return fail(SSM_ERR_INVALID_ARG, "%s: negative size or dim <= 0", "batch/seqlen/dim");
+  if (p->d_state <= 0) return fail(SSM_ERR_INVALID_ARG, "%s must be positive", "d_state");
+  if (p->d_state != ssm::kScanN) return fail(SSM_ERR_UNSUPPORTED, "%s must be 16", "d_state");
+  if (!valid_dtype(p->x_dtype) || !valid_dtype(p->y_dtype) || !valid_dtype(p->bc_dtype) ||
+      !valid_dtype(p->dt_dtype) || (p->z && !valid_dtype(p->z_dtype)))
+    return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "x/y/bc/dt/z_dtype");
+  if (p->z && p->z_dtype != p->x_dtype) return fail(SSM_ERR_UNSUPPORTED, "%s must equal x_dtype", "z_dtype");
+  if (p->time_split < 0 || p->time_split > ssm::kScanMaxSplit)
+    return fail(SSM_ERR_INVALID_ARG, "%s must be in [0, 16]", "time_split");
+  if (!p->A) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "A");
+  if (p->conv_w) {
+    if (p->conv_k != ssm::kConvK) return fail(SSM_ERR_UNSUPPORTED, "%s must be 4", "conv_k");
+  } else if (p->conv_cache_in || p->conv_cache_out || p->conv_b) {
+    return fail(SSM_ERR_INVALID_ARG, "%s given without conv_w", "conv_b/conv_cache");
+  }
+  if (p->dt_rank1) {
+    if (p->dt_dtype != SSM_F32) return fail(SSM_ERR_UNSUPPORTED, "%s: rank-1 dt input must be f32", "dt_dtype");
+    if (!p->dt_w) return fail(SSM_ERR_INVALID_ARG, "%s is NULL with dt_rank1", "dt_w");
+  }
+  ssm_status_t s = check_dt_bounds(p->dt_min, p->dt_max);
+  if (s != SSM_OK) return s;
+  const size_t Bt = p->batch, L = p->seqlen, E = p->dim, N = p->d_state;
+  const size_t tok = Bt * L;
+  if (tok > 0) {
+    if (!p->x) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "x");
+    if (!p->y) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "y");
+    if (!p->B || !p->C) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "B/C");
+    if (!p->dt) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "dt");
+  }
+  if (Bt * ((E + 63) / 64) > 0x7fffffffULL) return fail(SSM_ERR_UNSUPPORTED, "%s too large", "batch*dim");
+  const Range y{p->y, tok * E * esize(p->y_dtype)};
+  const Range ins[] = {
+      {p->x, tok * E * esize(p->x_dtype)},
+      {p->z, p->z ? tok * E * esize(p->z_dtype) : 0},
+      {p->dt, p->dt_rank1 ? tok * 4 : tok * E * esize(p->dt_dtype)},
+      {p->B, tok * N * esize(p->bc_dtype)},
+      {p->C, tok * N * esize(p->bc_dtype)},
+      {p->A, E * N * 4},
+      {p->D, p->D ? E * 4 : 0},
+      {p->ssm_state_in, p->ssm_state_in ? Bt * E * N * 4 : 0},
+      {p->ssm_state_out, p->ssm_state_out ? Bt * E * N * 4 : 0},
+      {p->conv_cache_in, p->conv_cache_in ? Bt * E * 3 * 4 : 0},
+      {p->conv_cache_out, p->conv_cache_out ? Bt * E * 3 * 4 : 0},
+      {p->workspace, p->workspace_bytes},
+  };
+  for (const Range& r : ins)
+    if (overlaps(y, r)) return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "y");
+  if (p->ssm_state_out && p->ssm_state_out != p->ssm_state_in &&
+      overlaps({p->ssm_state_out, Bt * E * N * 4}, {p->ssm_state_in, p->ssm_state_in ? Bt * E * N * 4 : 0}))
+    return fail(SSM_ERR_INVALID_ARG, "%s partially overlaps ssm_state_in", "ssm_state_out");
+  const size_t need = scan_ws(p);
+  if (need > 0 && (!p->workspace || p->workspace_bytes < need))
+    return fail(SSM_ERR_WORKSPACE, "%s is missing or smaller than ssm_scan_workspace_size()", "workspace");
+  if (p->workspace && (reinterpret_cast<uintptr_t>(p->workspace) & 255))
+    return fail(SSM_ERR_INVALID_ARG, "%s must be 256-byte aligned", "workspace");
+  return SSM_OK;
+}
+
+// ---------------------------------------------------------------- decode
+
+ssm_status_t decode_check(const ssm_decode_params_t* p) {
+  if (!p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "params");
+  if (p->struct_size != sizeof(ssm_decode_params_t))
+    return fail(SSM_ERR_INVALID_ARG, "%s does not match this library", "struct_size");
+  if (p->batch < 0 || p->dim <= 0) return fail(SSM_ERR_INVALID_ARG, "%s: negative size or dim <= 0", "batch/dim");
+  if (p->d_state <= 0) return fail(SSM_ERR_INVALID_ARG, "%s must be positive", "d_state");
+  if (p->d_state != ssm::kScanN) return fail(SSM_ERR_UNSUPPORTED, "%s must be 16", "d_state");
+  if (!valid_dtype(p->x_dtype) || !valid_dtype(p->y_dtype) || !valid_dtype(p->bc_dtype) ||
+      !valid_dtype(p->dt_dtype) || (p->z && !valid_dtype(p->z_dtype)))
+    return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "x/y/bc/dt/z_dtype");
+  if (p->z && p->z_dtype != p->x_dtype) return fail(SSM_ERR_UNSUPPORTED, "%s must equal x_dtype", "z_dtype");
+  if (!p->A) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "A");
+  if (p->conv_w) {
+    if (p->conv_k != ssm::kConvK) return fail(SSM_ERR_UNSUPPORTED, "%s must be 4", "conv_k");
+    if (p->batch > 0 && !p->conv_cache) return fail(SSM_ERR_INVALID_ARG, "%s is NULL with conv_w", "conv_cache");
+  } else if (p->conv_cache || p->conv_b) {
+    return fail(SSM_ERR_INVALID_ARG, "%s given without conv_w", "conv_b/conv_cache");
+  }
+  if (p->dt_rank1) {
+    if (p->dt_dtype != SSM_F32) return fail(SSM_ERR_UNSUPPORTED, "%s: rank-1 dt input must be f32", "dt_dtype");
+    if (!p->dt_w) return fail(SSM_ERR_INVALID_ARG, "%s is NULL with dt_rank1", "dt_w");
+  }
+  ssm_status_t s = check_dt_bounds(p->dt_min, p->dt_max);
+  if (s != SSM_OK) return s;
+  const size_t Bt = p->batch, E = p->dim, N = p->d_state;
+  if (Bt > 0) {
+    if (!p->x || !p->y || !p->B || !p->C || !p->dt || !p->ssm_state)
+      return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "x/y/B/C/dt/ssm_state");
+  }
+  if (Bt * ((E + 63) / 64) > 0x7fffffffULL) return fail(SSM_ERR_UNSUPPORTED, "%s too large", "batch*dim");
+  if (Bt > 0 && ((reinterpret_cast<uintptr_t>(p->ssm_state) | reinterpret_cast<uintptr_t>(p->A)) & 15))
+    return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "ssm_state/A");
+  const Range y{p->y, Bt * E * esize(p->y_dtype)};
+  const Range ins[] = {
+      {p->x, Bt * E * esize(p->x_dtype)},
+      {p->z, p->z ? Bt * E * esize(p->z_dtype) : 0},
+      {p->dt, p->dt_rank1 ? Bt * 4 : Bt * E * esize(p->dt_dtype)},
+      {p->B, Bt * N * esize(p->bc_dtype)},
+      {p->C, Bt * N * esize(p->bc_dtype)},
+      {p->A, E * N * 4},
+      {p->ssm_state, Bt * E * N * 4},
+      {p->conv_cache, p->conv_cache ? Bt * E * 3 * 4 : 0},
+  };
+  for (const Range& r : ins)
+    if (overlaps(y, r)) return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "y");
+  return SSM_OK;
+}
+
+// ---------------------------------------------------------------- chunked SSD
+
+size_t chunk_ws(const ssm_chunk_params_t* p) {
+  if (p->batch <= 0 || p->seqlen <= 0) return 0;
+  return ssm::chunk_workspace_bytes(p->batch, p->seqlen, p->nheads, p->headdim, p->ngroups);
+}
+
+ssm_status_t chunk_check(const ssm_chunk_params_t* p) {
+  if (!p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "params");
+  if (p->struct_size != sizeof(ssm_chunk_params_t))
+    return fail(SSM_ERR_INVALID_ARG, "%s does not match this library", "struct_size");
+  if (p->batch < 0 || p->seqlen < 0 || p->nheads <= 0 || p->headdim <= 0 || p->ngroups <= 0 ||
+      p->d_state <= 0 || p->chunk_size <= 0)
+    return fail(SSM_ERR_INVALID_ARG, "%s: negative or zero size", "dims");
+  if (p->nheads % p->ngroups != 0) return fail(SSM_ERR_INVALID_ARG, "%s", "nheads must be a multiple of ngroups");
+  if (p->seqlen % p->chunk_size != 0) return fail(SSM_ERR_INVALID_ARG, "%s", "seqlen must be a multiple of chunk_size");
+  if (p->d_state != ssm::kSsdN) return fail(SSM_ERR_UNSUPPORTED, "%s must be 64", "d_state");
+  if (p->chunk_size != ssm::kSsdQ) return fail(SSM_ERR_UNSUPPORTED, "%s must be 128", "chunk_size");
+  if (p->headdim % 16 != 0 || p->headdim > ssm::kSsdMaxP)
+    return fail(SSM_ERR_UNSUPPORTED, "%s must be a multiple of 16 and at most 128", "headdim");
+  if (!valid_dtype(p->x_dtype) || !valid_dtype(p->bc_dtype) || !valid_dtype(p->out_dtype))
+    return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "x/bc/out_dtype");
+  if (!p->A) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "A");
+  ssm_status_t s = check_dt_bounds(p->dt_min, p->dt_max);
+  if (s != SSM_OK) return s;
+  const size_t Bt = p->batch, L = p->seqlen, H = p->nheads, P = p->headdim, G = p->ngroups, N = p->d_state;
+  const size_t tok = Bt * L;
+  if (tok > 0 && (!p->x || !p->out || !p->B || !p->C || !p->dt))
+    return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "x/out/B/C/dt");
+  const Range out{p->out, tok * H * P * esize(p->out_dtype)};
+  const Range ins[] = {
+      {p->x, tok * H * P * esize(p->x_dtype)},
+      {p->dt, tok * H * 4},
+      {p->B, tok * G * N * esize(p->bc_dtype)},
+      {p->C, tok * G * N * esize(p->bc_dtype)},
+      {p->A, H * 4},
+      {p->D, p->D ? (p->d_per_channel ? H * P * 4 : H * 4) : 0},
+      {p->dt_bias, p->dt_bias ? H * 4 : 0},
+      {p->state_in, p->state_in ? Bt * H * P * N * 4 : 0},
+      {p->state_out, p->state_out ? Bt * H * P * N * 4 : 0},
+      {p->workspace, p->workspace_bytes},
+  };
+  for (const Range& r : ins)
+    if (overlaps(out, r)) return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "out");
+  if (p->state_out && p->state_out != p->state_in &&
+      overlaps({p->state_out, Bt * H * P * N * 4}, {p->state_in, p->state_in ? Bt * H * P * N * 4 : 0}))
+    return fail(SSM_ERR_INVALID_ARG, "%s partially overlaps state_in", "state_out");
+  const size_t need = chunk_ws(p);
+  if (need > 0 && (!p->workspace || p->workspace_bytes < need))
+    return fail(SSM_ERR_WORKSPACE, "%s is missing or smaller than ssm_chunk_scan_workspace_size()", "workspace");
+  if (p->workspace && (reinterpret_cast<uintptr_t>(p->workspace) & 255))
+    return fail(SSM_ERR_INVALID_ARG, "%s must be 256-byte aligned", "workspace");
+  return SSM_OK;
+}
+
+ssm_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return ok();
+  return fail(SSM_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status_t ssm_scan_check(const ssm_scan_params_t* p) {
+  const ssm_status_t s = scan_check(p);
+  return s == SSM_OK ? ok() : s;
+}
+
+size_t ssm_scan_workspace_size(const ssm_scan_params_t* p) {
+  if (!p || p->struct_size != sizeof(ssm_scan_params_t)) return 0;
+  return scan_ws(p);
+}
+
+ssm_status_t ssm_scan_fwd(const ssm_scan_params_t* p, void* stream) {
+  const ssm_status_t s = scan_check(p);
+  if (s != SSM_OK) return s;
+  ssm::ScanLaunch l{};
+  ssm::ScanKernelArgs& k = l.k;
+  k.x = p->x;
+  k.z = p->z;
+  k.dt = p->dt_rank1 ? nullptr : p->dt;
+  k.y = p->y;
+  k.bcr = static_cast<const float*>(p->workspace);
+  k.A = p->A;
+  k.D = p->D;
+  k.dt_w = p->dt_rank1 ? p->dt_w : nullptr;
+  k.dt_bias = p->dt_bias;
+  k.conv_w = p->conv_w;
+  k.conv_b = p->conv_b;
+  k.conv_cache_in = p->conv_cache_in;
+  k.conv_cache_out = p->conv_cache_out;
+  k.state_in = p->ssm_state_in;
+  k.state_out = p->ssm_state_out;
+  k.batch = p->batch;
+  k.seqlen = p->seqlen;
+  k.dim = p->dim;
+  k.n_egroups = (p->dim + 63) / 64;
+  k.nseg = scan_split(p);
+  k.seg_len = p->seqlen > 0 ? (p->seqlen + k.nseg - 1) / k.nseg : 0;
+  k.dt_min = p->dt_min;
+  k.dt_max = p->dt_max;
+  softplus_thresholds(p->dt_min, p->dt_max, &k.sp_lo, &k.sp_hi);
+  k.dt_softplus = p->dt_softplus ? 1 : 0;
+  k.has_z = p->z ? 1 : 0;
+  l.x_dtype = p->x_dtype;
+  l.y_dtype = p->y_dtype;
+  l.bc_dtype = p->bc_dtype;
+  l.dt_mode = p->dt_rank1 ? 0 : (p->dt_dtype == SSM_BF16 ? 2 : 1);
+  l.conv = p->conv_w != nullptr;
+  l.B = p->B;
+  l.C = p->C;
+  l.r = p->dt_rank1 ? static_cast<const float*>(p->dt) : nullptr;
+  l.bcr_out = static_cast<float*>(p->workspace);
+  if (p->batch == 0) return ok();
+  return hip_status(ssm::launch_scan(l, static_cast<hipStream_t>(stream)));
+}
+
+ssm_status_t ssm_decode_check(const ssm_decode_params_t* p) {
+  const ssm_status_t s = decode_check(p);
+  return s == SSM_OK ? ok() : s;
+}
+
+ssm_status_t ssm_decode_step(const ssm_decode_params_t* p, void* stream) {
+  const ssm_status_t s = decode_check(p);
+  if (s != SSM_OK) return s;
+  if (p->batch == 0) return ok();
+  ssm::DecodeLaunch l{};
+  ssm::DecodeKernelArgs& k = l.k;
+  k.x = p->x;
+  k.z = p->z;
+  k.dt = p->dt;
+  k.B = p->B;
+  k.C = p->C;
+  k.y = p->y;
+  k.A = p->A;
+  k.D = p->D;
+  k.dt_w = p->dt_rank1 ? p->dt_w : nullptr;
+  k.dt_bias = p->dt_bias;
+  k.conv_w = p->conv_w;
+  k.conv_b = p->conv_b;
+  k.conv_cache = p->conv_cache;
+  k.state = p->ssm_state;
+  k.batch = p->batch;
+  k.dim = p->dim;
+  k.dt_min = p->dt_min;
+  k.dt_max = p->dt_max;
+  softplus_thresholds(p->dt_min, p->dt_max, &k.sp_lo, &k.sp_hi);
+  k.dt_softplus = p->dt_softplus ? 1 : 0;
+  k.has_z = p->z ? 1 : 0;
+  l.x_dtype = p->x_dtype;
+  l.y_dtype = p->y_dtype;
+  l.bc_dtype = p->bc_dtype;
+  l.dt_mode = p->dt_rank1 ? 0 : (p->dt_dtype == SSM_BF16 ? 2 : 1);
+  l.conv = p->conv_w != nullptr;
+  return hip_status(ssm::launch_decode(l, static_cast<hipStream_t>(stream)));
+}
+
+ssm_status_t ssm_chunk_scan_check(const ssm_chunk_params_t* p) {
+  const ssm_status_t s = chunk_check(p);
+  return s == SSM_OK ? ok() : s;
+}
+
+size_t ssm_chunk_scan_workspace_size(const ssm_chunk_params_t* p) {
+  if (!p || p->struct_size != sizeof(ssm_chunk_params_t)) return 0;
+  if (p->batch < 0 || p->seqlen < 0 || p->nheads <= 0 || p->headdim <= 0 || p->ngroups <= 0) return 0;
+  return chunk_ws(p);
+}
+
+ssm_status_t ssm_chunk_scan_fwd(const ssm_chunk_params_t* p, void* stream) {
+  const ssm_status_t s = chunk_check(p);
+  if (s != SSM_OK) return s;
+  if (p->batch == 0) return ok();
+  ssm::ChunkLaunch l{};
+  ssm::ChunkKernelArgs& k = l.k;
+  k.x = p->x;
+  k.dt = p->dt;
+  k.dt_bias = p->dt_bias;
+  k.A = p->A;
+  k.B = p->B;
+  k.C = p->C;
+  k.D = p->D;
+  k.state_in = p->state_in;
+  k.state_out = p->state_out;
+  k.out = p->out;
+  k.ws = static_cast<float*>(p->workspace);
+  k.batch = p->batch;
+  k.seqlen = p->seqlen;
+  k.nheads = p->nheads;
+  k.headdim = p->headdim;
+  k.ngroups = p->ngroups;
+  k.nchunks = p->seqlen / p->chunk_size;
+  k.d_per_channel = p->d_per_channel ? 1 : 0;
+  k.dt_min = p->dt_min;
+  k.dt_max = p->dt_max;
+  softplus_thresholds(p->dt_min, p->dt_max, &k.sp_lo, &k.sp_hi);
+  k.dt_softplus = p->dt_softplus ? 1 : 0;
+  l.x_dtype = p->x_dtype;
+  l.bc_dtype = p->bc_dtype;
+  l.out_dtype = p->out_dtype;
+  return hip_status(ssm::launch_chunk(l, static_cast<hipStream_t>(stream)));
+}
+
+const char* ssm_status_string(int32_t status) {
+  switch (status) {
+    case SSM_OK: return "SSM_OK";
+    case SSM_ERR_INVALID_ARG: return "SSM_ERR_INVALID_ARG";
+    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED";
+    case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE";
+    case SSM_ERR_HIP: return "SSM_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+const char* ssm_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+size_t ssm_params_sizeof(int32_t which) {
+  switch (which) {
+    case 0: return sizeof(ssm_scan_params_t);
+    case 1: return sizeof(ssm_decode_params_t);
+    case 2: return sizeof(ssm_chunk_params_t);
+    default: return 0;
+  }
+}
+
+}  // extern "C"

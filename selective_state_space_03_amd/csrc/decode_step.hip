@@ -1,0 +1,119 @@
+// One autoregressive decode step, in place, for gfx950.
+//
+// Page "Axon-SSM: selective state space model", section "Autoregressive
+// decoding": concatenate conv_cache with the new token, run exactly one step
+// of the scan from the previous ssm_state, return the updated
+// [conv_cache, ssm_state].  Per channel: window = (cache[0..2], x) -> causal
+// depthwise conv (k=4) + SiLU -> dt = clip(softplus(dt_proj + dt_bias)) ->
+// h = exp(dt*A) h + dt*B*u -> y = (C . h + D*u) * SiLU(z); cache <- window[1..3].
+//
+// The step reads and writes the whole (batch, E, 16) fp32 state, so it is
+// bound by HBM bandwidth.  Four lanes share one (batch, channel): each owns 4
+// of its 16 states, so every state load and store is one 16-byte access per
+// lane and a wave's accesses cover one contiguous 1 KiB span.  The readout is
+// summed across the four lanes with two cross-lane adds.
+#include <type_traits>
+
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+namespace {
+
+template <typename XT, typename YT, typename BT, int DTM, bool CONV>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeKernelArgs a) {
+  using DT = typename std::conditional<DTM == 2, bf16s, float>::type;
+  const int q = threadIdx.x & 3;
+  const size_t total = static_cast<size_t>(a.batch) * a.dim;
+  const size_t ch_raw = static_cast<size_t>(blockIdx.x) * 64 + (threadIdx.x >> 2);
+  const bool act = ch_raw < total;
+  const size_t ch = act ? ch_raw : total - 1;  // (b, e) flattened
+  const int b = static_cast<int>(ch / a.dim);
+  const int e = static_cast<int>(ch % a.dim);
+
+  float4* __restrict__ state4 = reinterpret_cast<float4*>(a.state);
+  const float4 hs = state4[ch * 4 + q];
+  const float4 a4 = reinterpret_cast<const float4*>(a.A)[static_cast<size_t>(e) * 4 + q];
+  const float xr = ld<XT>(a.x, ch);
+
+  float c0 = 0.0f, c1 = 0.0f, c2 = 0.0f;
+  float u = xr;
+  if (CONV) {
+    c0 = a.conv_cache[ch * 3 + 0];
+    c1 = a.conv_cache[ch * 3 + 1];
+    c2 = a.conv_cache[ch * 3 + 2];
+    const float* w = a.conv_w + static_cast<size_t>(e) * kConvK;
+    const float cb = a.conv_b ? a.conv_b[e] : 0.0f;
+    const float xc = fmaf(w[0], c0, fmaf(w[1], c1, fmaf(w[2], c2, fmaf(w[3], xr, cb))));
+    u = silu(xc);
+  }
+  const float dtb = a.dt_bias ? a.dt_bias[e] : 0.0f;
+  const float pre = (DTM == 0) ? fmaf(a.dt_w[e], static_cast<const float*>(a.dt)[b], dtb)
+                               : to_f32(static_cast<const DT*>(a.dt)[ch]) + dtb;
+  const float dt = a.dt_softplus ? dt_softplus_clip(pre, a.dt_min, a.dt_max, a.sp_lo, a.sp_hi)
+                                 : dt_clip(pre, a.dt_min, a.dt_max);
+  const float dtu = dt * u;
+
+  const BT* Bp = static_cast<const BT*>(a.B) + static_cast<size_t>(b) * kScanN + 4 * q;
+  const BT* Cp = static_cast<const BT*>(a.C) + static_cast<size_t>(b) * kScanN + 4 * q;
+  const float hin[4] = {hs.x, hs.y, hs.z, hs.w};
+  const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+  float hout[4];
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float an = exp2_fast(dt * (av[j] * kLog2e));
+    hout[j] = fmaf(an, hin[j], dtu * to_f32(Bp[j]));
+    acc = fmaf(to_f32(Cp[j]), hout[j], acc);
+  }
+  acc += __shfl_xor(acc, 1, 4);
+  acc += __shfl_xor(acc, 2, 4);
+
+  if (!act) return;
+  state4[ch * 4 + q] = make_float4(hout[0], hout[1], hout[2], hout[3]);
+  if (q == 0) {
+    float yv = fmaf(a.D ? a.D[e] : 0.0f, u, acc);
+    if (a.has_z) yv *= silu(ld<XT>(a.z, ch));
+    st<YT>(a.y, ch, yv);
+  }
+  if (CONV && q < 3) {
+    const float nv = (q == 0) ? c1 : (q == 1) ? c2 : xr;
+    a.conv_cache[ch * 3 + q] = nv;
+  }
+}
+
+template <typename XT, typename YT, typename BT, int DTM>
+hipError_t go(const DecodeLaunch& l, hipStream_t s) {
+  const size_t total = static_cast<size_t>(l.k.batch) * l.k.dim;
+  const unsigned blocks = static_cast<unsigned>((total + 63) / 64);
+  if (l.conv)
+    hipLaunchKernelGGL((decode_kernel<XT, YT, BT, DTM, true>), dim3(blocks), dim3(256), 0, s, l.k);
+  else
+    hipLaunchKernelGGL((decode_kernel<XT, YT, BT, DTM, false>), dim3(blocks), dim3(256), 0, s, l.k);
+  return hipGetLastError();
+}
+
+template <typename XT, typename YT, typename BT>
+hipError_t pick_dt(const DecodeLaunch& l, hipStream_t s) {
+  switch (l.dt_mode) {
+    case 0: return go<XT, YT, BT, 0>(l, s);
+    case 1: return go<XT, YT, BT, 1>(l, s);
+    default: return go<XT, YT, BT, 2>(l, s);
+  }
+}
+
+template <typename XT, typename YT>
+hipError_t pick_bc(const DecodeLaunch& l, hipStream_t s) {
+  return l.bc_dtype == kBF16 ? pick_dt<XT, YT, bf16s>(l, s) : pick_dt<XT, YT, float>(l, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeLaunch& l, hipStream_t stream) {
+  if (l.x_dtype == kBF16) {
+    return l.y_dtype == kBF16 ? pick_bc<bf16s, bf16s>(l, stream) : pick_bc<bf16s, float>(l, stream);
+  }
+  return l.y_dtype == kBF16 ? pick_bc<float, bf16s>(l, stream) : pick_bc<float, float>(l, stream);
+}
+
+}  // namespace ssm

@@ -1,0 +1,81 @@
+// Device helpers shared by the gfx950 kernels: element loads/stores for the
+// two storage types and the fp32 pointwise functions of the layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct bf16s {  // bf16 storage (bit pattern); arithmetic happens in fp32
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16s v) { return __uint_as_float(static_cast<uint32_t>(v.bits) << 16); }
+
+template <typename T>
+__device__ __forceinline__ float ld(const void* p, size_t i) {
+  return to_f32(static_cast<const T*>(p)[i]);
+}
+
+template <typename T>
+__device__ __forceinline__ void st(void* p, size_t i, float v);
+
+template <>
+__device__ __forceinline__ void st<float>(void* p, size_t i, float v) {
+  static_cast<float*>(p)[i] = v;
+}
+
+template <>
+__device__ __forceinline__ void st<bf16s>(void* p, size_t i, float v) {
+  // v_cvt_pk_bf16_f32: round to nearest even
+  __bf16 b = static_cast<__bf16>(v);
+  static_cast<uint16_t*>(p)[i] = __builtin_bit_cast(uint16_t, b);
+}
+
+// 2^x on the transcendental unit (v_exp_f32).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// SiLU(x) = x / (1 + e^-x).  For very negative x the exponential overflows to
+// +inf and the reciprocal to 0, giving -0; for large x it tends to x.
+__device__ __forceinline__ float silu(float x) {
+  return x * rcp_fast(1.0f + exp2_fast(-x * kLog2e));
+}
+
+// softplus(x) = max(x, 0) + log1p(e^-|x|).  log1p(w) is evaluated as
+// log(u) * w / (u - 1) with u = 1 + w, which keeps full relative accuracy for
+// small w (the rounding of u cancels between numerator and denominator).
+__device__ __forceinline__ float softplus(float x) {
+  const float w = exp2_fast(-fabsf(x) * kLog2e);
+  const float u = 1.0f + w;
+  const float l1p = (u == 1.0f) ? w : log2_fast(u) * kLn2 * (w * rcp_fast(u - 1.0f));
+  return fmaxf(x, 0.0f) + l1p;
+}
+
+// dt = clip(softplus(pre), lo, hi) with exact shortcuts: pre >= sp_hi implies
+// softplus(pre) >= hi and pre <= sp_lo implies softplus(pre) <= lo (softplus is
+// increasing; the host rounds the thresholds outward), so the transcendental
+// work only runs for lanes inside the unsaturated band.
+__device__ __forceinline__ float dt_softplus_clip(float pre, float lo, float hi, float sp_lo, float sp_hi) {
+  float r;
+  if (pre >= sp_hi) {
+    r = hi;
+  } else if (pre <= sp_lo) {
+    r = lo;
+  } else {
+    r = fminf(fmaxf(softplus(pre), lo), hi);
+  }
+  return r;
+}
+
+__device__ __forceinline__ float dt_clip(float pre, float lo, float hi) { return fminf(fmaxf(pre, lo), hi); }
+
+// Make a wave-uniform value provably uniform to the compiler (SGPR).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace ssm

@@ -1,0 +1,98 @@
+"""Helpers shared by the GPU parity tests: move a seeded workload to the GPU,
+call the HIP path through the binding, call the float64 oracle on the same
+arrays (optionally on a sample of channels), and compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import selective_state_space_03_amd as ssm
+import ssm_workloads as W
+from oracle import ssm_oracle as O
+
+DEV = torch.device("cuda:0")
+
+
+def dev_tensor(w: W.Workload, key: str, device=DEV):
+    a = w.arrays.get(key)
+    if a is None:
+        return None
+    if key in w.bf16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def check(got, want, tol, what, out_bf16=False):
+    """max |got - want| <= tol * max|want| (+ 2^-8 |want_i| when the output was
+    rounded to bf16, the rounding bound of the storage format itself)."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values in the GPU result"
+    if want.size == 0:
+        return 0.0
+    scale = float(np.max(np.abs(want)))
+    err = np.abs(got - want)
+    bound = tol * scale + (2.0 ** -8 * np.abs(want) if out_bf16 else 0.0)
+    worst = float(np.max(err - bound))
+    assert worst <= 0.0, (f"{what}: max|err| {float(np.max(err)):.3e} exceeds bound "
+                          f"(tol {tol:g} * max|ref| {scale:.3e}); worst excess {worst:.3e}")
+    return float(np.max(err)) / max(scale, 1e-300)
+
+
+# ---------------------------------------------------------------------- scan
+
+def scan_gpu(w: W.Workload, *, y_dtype=torch.float32, time_split=0, state_in=None, cache_in=None,
+             want_state=True, want_cache=True, y_fill=None):
+    o = w.opts
+    d = w.dims
+    Bt, E, N = d["batch"], d["dim"], d["d_state"]
+    st = torch.empty((Bt, E, N), dtype=torch.float32, device=DEV) if want_state else None
+    cc = torch.empty((Bt, E, 3), dtype=torch.float32, device=DEV) if (want_cache and o["conv"]) else None
+    y = None
+    if y_fill is not None:
+        y = torch.full((Bt, d["seqlen"], E), y_fill, dtype=y_dtype, device=DEV)
+    y = ssm.scan_fwd(
+        dev_tensor(w, "x"), dev_tensor(w, "A"), dev_tensor(w, "B"), dev_tensor(w, "C"), dev_tensor(w, "dt"),
+        D=dev_tensor(w, "D"), z=dev_tensor(w, "z"), conv_w=dev_tensor(w, "conv_w") if o["conv"] else None,
+        conv_cache_in=cache_in, conv_cache_out=cc, dt_rank1=o["dt_rank1"], dt_w=dev_tensor(w, "dt_w"),
+        dt_bias=dev_tensor(w, "dt_bias"), dt_softplus=o["dt_softplus"], dt_min=o["dt_min"], dt_max=o["dt_max"],
+        ssm_state_in=state_in, ssm_state_out=st, y=y, y_dtype=y_dtype, time_split=time_split)
+    torch.cuda.synchronize()
+    return y, st, cc
+
+
+def _sel(a, batches, channels, axis_e):
+    if a is None:
+        return None
+    if batches is not None:
+        a = a[batches]
+    if channels is not None:
+        a = np.take(a, channels, axis=axis_e)
+    return a
+
+
+def scan_oracle(w: W.Workload, *, state_in=None, cache_in=None, batches=None, channels=None):
+    """Oracle on (a sample of) the workload: batches / channels index lists.
+    Channels of the diagonal scan are independent, so a sample is exact."""
+    o = w.opts
+    f = w.f64
+    x = _sel(f("x"), batches, channels, 2)
+    z = _sel(f("z"), batches, channels, 2)
+    B = _sel(f("B"), batches, None, 2)
+    C = _sel(f("C"), batches, None, 2)
+    ch = (lambda v: v if channels is None or v is None else v[channels])
+    if o["dt_rank1"]:
+        dt_kw = dict(dt_raw=_sel(f("dt"), batches, None, 1), dt_w=ch(f("dt_w")))
+    else:
+        dt_kw = dict(dt=_sel(f("dt"), batches, channels, 2))
+    sti = _sel(state_in, batches, channels, 1) if state_in is not None else None
+    cci = _sel(cache_in, batches, channels, 1) if cache_in is not None else None
+    return O.ssm_layer_scan(
+        x, ch(f("A")), B, C, D=ch(f("D")), z=z, conv_w=ch(f("conv_w")) if o["conv"] else None,
+        conv_cache=cci, dt_bias=ch(f("dt_bias")), dt_softplus=o["dt_softplus"], dt_min=float(o["dt_min"]),
+        dt_max=float(o["dt_max"]), ssm_state=sti, **dt_kw)

@@ -1,0 +1,186 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, its struct layouts match the ctypes mirror, and argument validation
+rejects bad calls before anything reaches the GPU (no compute calls here)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_mi355x.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from selective_state_space_03_amd import binding
+
+    if not os.path.exists(binding.LIB_PATH):
+        from selective_state_space_03_amd import build as b
+
+        b.build()
+    return binding.lib()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(L):
+    from selective_state_space_03_amd import binding
+
+    names = _declared()
+    assert set(names) == set(binding.EXPORTED), names
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (ssm_\w+)", out))
+    for n in names:
+        assert n in exported, f"{n} not exported"
+        assert hasattr(L, n)
+
+
+def test_struct_layouts_and_version(L):
+    from selective_state_space_03_amd import binding
+
+    assert L.ssm_abi_version() == 1
+    assert L.ssm_params_sizeof(0) == ctypes.sizeof(binding.ScanParams)
+    assert L.ssm_params_sizeof(1) == ctypes.sizeof(binding.DecodeParams)
+    assert L.ssm_params_sizeof(2) == ctypes.sizeof(binding.ChunkParams)
+    assert L.ssm_params_sizeof(7) == 0
+    assert L.ssm_status_string(3) == b"SSM_ERR_WORKSPACE"
+
+
+# Fake, well-separated, 256-byte aligned "device" addresses: validation only
+# compares and range-checks pointers, it never dereferences them.
+def _addr(i):
+    return 0x10000000000 + i * 0x100000000
+
+
+def _scan(**kw):
+    from selective_state_space_03_amd import binding as b
+
+    p = b.ScanParams()
+    p.struct_size = ctypes.sizeof(b.ScanParams)
+    p.batch, p.seqlen, p.dim, p.d_state, p.conv_k = 2, 64, 128, 16, 4
+    p.x, p.y, p.A, p.B, p.C, p.dt, p.dt_w = (_addr(i) for i in range(1, 8))
+    p.x_dtype = p.y_dtype = p.bc_dtype = 1
+    p.dt_rank1 = 1
+    p.dt_softplus = 1
+    p.dt_min, p.dt_max = 1e-3, 0.1
+    p.workspace, p.workspace_bytes = _addr(20), 1 << 30
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _st(L, fn, p):
+    return fn(ctypes.byref(p))
+
+
+def test_scan_validation(L):
+    ok = _scan()
+    assert L.ssm_scan_check(ctypes.byref(ok)) == 0, L.ssm_last_error()
+    assert L.ssm_scan_workspace_size(ctypes.byref(ok)) == 2 * 64 * 48 * 4
+    cases = {
+        "d_state": (_scan(d_state=8), 2),
+        "neg": (_scan(batch=-1), 1),
+        "bounds": (_scan(dt_min=0.5, dt_max=0.1), 1),
+        "nan": (_scan(dt_min=math.nan), 1),
+        "conv_k": (_scan(conv_w=_addr(9), conv_k=3), 2),
+        "cache_without_conv": (_scan(conv_cache_in=_addr(9)), 1),
+        "rank1_bf16": (_scan(dt_dtype=1), 2),
+        "rank1_no_w": (_scan(dt_w=None), 1),
+        "null_x": (_scan(x=None), 1),
+        "split": (_scan(time_split=17), 1),
+        "dtype": (_scan(x_dtype=5), 1),
+        "z_dtype": (_scan(z=_addr(9), z_dtype=0), 2),
+        "y_over_x": (_scan(y=_addr(1) + 64), 1),
+        "workspace": (_scan(workspace_bytes=16), 3),
+        "no_workspace": (_scan(workspace=None, workspace_bytes=0), 3),
+        "ws_align": (_scan(workspace=_addr(20) + 8), 1),
+        "struct": (_scan(struct_size=8), 1),
+        "state_partial_alias": (_scan(ssm_state_in=_addr(10), ssm_state_out=_addr(10) + 4), 1),
+    }
+    for name, (p, want) in cases.items():
+        assert L.ssm_scan_check(ctypes.byref(p)) == want, (name, L.ssm_last_error())
+        assert L.ssm_last_error() != b""
+    # the launching entry point returns the same code without touching a device
+    bad = _scan(d_state=8)
+    assert L.ssm_scan_fwd(ctypes.byref(bad), None) == 2
+    # exact in-place aliasing of the state is allowed
+    alias = _scan(ssm_state_in=_addr(10), ssm_state_out=_addr(10))
+    assert L.ssm_scan_check(ctypes.byref(alias)) == 0
+    assert L.ssm_scan_check(None) == 1
+
+
+def _decode(**kw):
+    from selective_state_space_03_amd import binding as b
+
+    p = b.DecodeParams()
+    p.struct_size = ctypes.sizeof(b.DecodeParams)
+    p.batch, p.dim, p.d_state, p.conv_k = 64, 7680, 16, 4
+    p.x, p.y, p.A, p.B, p.C, p.dt, p.dt_w, p.ssm_state, p.conv_w, p.conv_cache = (_addr(i) for i in range(1, 11))
+    p.dt_rank1 = 1
+    p.dt_min, p.dt_max = 1e-3, 0.1
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_decode_validation(L):
+    assert L.ssm_decode_check(ctypes.byref(_decode())) == 0, L.ssm_last_error()
+    cases = {
+        "no_cache": (_decode(conv_cache=None), 1),
+        "state_align": (_decode(ssm_state=_addr(8) + 4), 1),
+        "d_state": (_decode(d_state=32), 2),
+        "no_state": (_decode(ssm_state=None), 1),
+        "y_over_state": (_decode(y=_addr(8) + 128), 1),
+    }
+    for name, (p, want) in cases.items():
+        assert L.ssm_decode_check(ctypes.byref(p)) == want, (name, L.ssm_last_error())
+    assert L.ssm_decode_step(ctypes.byref(_decode(d_state=32)), None) == 2
+
+
+def _chunk(**kw):
+    from selective_state_space_03_amd import binding as b
+
+    p = b.ChunkParams()
+    p.struct_size = ctypes.sizeof(b.ChunkParams)
+    p.batch, p.seqlen, p.nheads, p.headdim, p.ngroups, p.d_state, p.chunk_size = 1, 1024, 8, 96, 1, 64, 128
+    p.x, p.dt, p.A, p.B, p.C, p.out = (_addr(i) for i in range(1, 7))
+    p.x_dtype = p.bc_dtype = 1
+    p.dt_softplus = 1
+    p.dt_min, p.dt_max = 1e-3, 0.1
+    p.workspace, p.workspace_bytes = _addr(20), 1 << 32
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_chunk_validation(L):
+    assert L.ssm_chunk_scan_check(ctypes.byref(_chunk())) == 0, L.ssm_last_error()
+    cases = {
+        "ragged": (_chunk(seqlen=1000), 1),
+        "groups": (_chunk(ngroups=3), 1),
+        "d_state": (_chunk(d_state=16), 2),
+        "chunk": (_chunk(chunk_size=64, seqlen=1024), 2),
+        "headdim": (_chunk(headdim=100), 2),
+        "null_A": (_chunk(A=None), 1),
+        "out_over_x": (_chunk(out=_addr(1) + 2), 1),
+    }
+    for name, (p, want) in cases.items():
+        assert L.ssm_chunk_scan_check(ctypes.byref(p)) == want, (name, L.ssm_last_error())
+    assert L.ssm_chunk_scan_fwd(ctypes.byref(_chunk(seqlen=1000)), None) == 1
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+
+    import selective_state_space_03_amd as ssm
+
+    x = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError):
+        ssm.scan_fwd(x, torch.zeros(8, 16), torch.zeros(1, 4, 16), torch.zeros(1, 4, 16), torch.zeros(1, 4, 8))

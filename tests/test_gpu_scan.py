@@ -1,0 +1,174 @@
+"""GPU parity of ssm_scan_fwd (fused conv + dt + scan + gate) against the
+float64 oracle, through the C ABI.  Tolerances: max|err| <= 1e-5 max|y| for
+fp32 workloads, <= 2e-3 max|y| for bf16-input workloads (fp32 output), plus
+the 2^-8 |y| rounding bound of the format when y itself is bf16."""
+import numpy as np
+import pytest
+import torch
+
+import ssm_workloads as W
+from gpu_util import DEV, check, dev_tensor, np64, scan_gpu, scan_oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-3
+
+
+def _parity(w, tol, y_dtype=torch.float32, time_split=0):
+    y, st, cc = scan_gpu(w, y_dtype=y_dtype, time_split=time_split)
+    yo, ho, co = scan_oracle(w)
+    check(np64(y), yo, tol, f"{w.name} y split={time_split}", out_bf16=(y_dtype == torch.bfloat16))
+    check(np64(st), ho, tol, f"{w.name} state split={time_split}")
+    if cc is not None:
+        assert np.array_equal(np64(cc), co), "conv_cache_out must be the raw last inputs, bit for bit"
+
+
+@pytest.mark.parametrize("unsat", [False, True])
+@pytest.mark.parametrize("split", [0, 1, 2, 5, 16])
+def test_scan_tiny_fp32(unsat, split):
+    """Tiny fp32 scan: batch 1, L 64, E 16, N 16 (rank-1 dt, gate, D, no conv)."""
+    _parity(W.scan_tiny(unsaturated=unsat), TOL_F32, time_split=split)
+
+
+@pytest.mark.parametrize("unsat", [False, True])
+@pytest.mark.parametrize("split", [0, 1, 3, 16])
+def test_scan_prefill_recipe_small(unsat, split):
+    """The layer-prefill recipe (bf16 x/z, conv1d k=4 + SiLU, rank-1 dt, bf16 B/C)
+    at batch 2, L 300, E 200: several waves, a ragged channel tail (200 = 3*64 + 8)
+    and a ragged final time tile."""
+    _parity(W.scan_prefill(batch=2, seqlen=300, dim=200, unsaturated=unsat), TOL_BF16, time_split=split)
+
+
+def test_scan_prefill_recipe_bf16_out():
+    w = W.scan_prefill(batch=2, seqlen=300, dim=200)
+    _parity(w, TOL_BF16, y_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("unsat", [False, True])
+@pytest.mark.parametrize("split", [0, 1, 2])
+def test_scan_bulk_recipe_small(unsat, split):
+    """The bulk recipe (bf16 u/dt/z E-wide, bf16 B/C, no conv) at batch 3, L 257, E 136."""
+    _parity(W.scan_bulk(batch=3, seqlen=257, dim=136, unsaturated=unsat), TOL_BF16, time_split=split)
+
+
+@pytest.mark.parametrize("split", [1, 4])
+def test_scan_general_A(split):
+    """A whose rows are not multiples of their first entry exercises one
+    exponential per state (no power shortcut)."""
+    w = W.scan_tiny(batch=2, seqlen=150, dim=70, unsaturated=True)
+    rng = np.random.Generator(np.random.PCG64(7))
+    w.arrays["A"] = (-rng.uniform(0.3, 16.0, w.arrays["A"].shape)).astype(np.float32)
+    _parity(w, TOL_F32, time_split=split)
+
+
+def test_scan_fp32_with_conv():
+    """All-fp32 inputs with the conv on and a conv bias-free window from a given cache."""
+    w = W.scan_prefill(batch=2, seqlen=70, dim=96, unsaturated=True)
+    for k in ("x", "z", "B", "C"):
+        w.arrays[k] = W.bf16_to_f32(w.arrays[k])
+        w.bf16.discard(k)
+    _parity(w, TOL_F32, time_split=3)
+
+
+@pytest.mark.parametrize("L1", [1, 2, 3, 37])
+def test_scan_split_prefill_handover(L1):
+    """Prefill of the first L1 tokens, then the rest from the returned state and
+    conv cache (aliased in place), equals the oracle on the whole sequence."""
+    w = W.scan_prefill(batch=2, seqlen=90, dim=72, unsaturated=True)
+    yo, ho, co = scan_oracle(w)
+    first = W.Workload(w.name, "scan", dict(w.dims, seqlen=L1), {}, set(w.bf16), w.opts)
+    second = W.Workload(w.name, "scan", dict(w.dims, seqlen=90 - L1), {}, set(w.bf16), w.opts)
+    for k, a in w.arrays.items():
+        if a.ndim >= 2 and a.shape[:2] == (2, 90):
+            first.arrays[k], second.arrays[k] = a[:, :L1].copy(), a[:, L1:].copy()
+        else:
+            first.arrays[k] = second.arrays[k] = a
+    y1, st, cc = scan_gpu(first)
+    y2, st2, cc2 = scan_gpu(second, state_in=st, cache_in=cc)
+    check(np.concatenate([np64(y1), np64(y2)], axis=1), yo, TOL_BF16, "split prefill y")
+    check(np64(st2), ho, TOL_BF16, "split prefill state")
+    assert np.array_equal(np64(cc2), co)
+    # in-place: state and cache outputs aliasing their inputs
+    st_a, cc_a = st.clone(), cc.clone()
+    import selective_state_space_03_amd as ssm
+    o = w.opts
+    ssm.scan_fwd(dev_tensor(second, "x"), dev_tensor(second, "A"), dev_tensor(second, "B"),
+                 dev_tensor(second, "C"), dev_tensor(second, "dt"), D=dev_tensor(second, "D"),
+                 z=dev_tensor(second, "z"), conv_w=dev_tensor(second, "conv_w"), conv_cache_in=cc_a,
+                 conv_cache_out=cc_a, dt_rank1=True, dt_w=dev_tensor(second, "dt_w"),
+                 dt_bias=dev_tensor(second, "dt_bias"), dt_min=o["dt_min"], dt_max=o["dt_max"],
+                 ssm_state_in=st_a, ssm_state_out=st_a, y_dtype=torch.float32, time_split=4)
+    torch.cuda.synchronize()
+    check(np64(st_a), ho, TOL_BF16, "in-place state")
+    assert np.array_equal(np64(cc_a), co)
+
+
+@pytest.mark.parametrize("L", [0, 1, 2, 3, 5])
+def test_scan_short_sequences_with_cache(L):
+    """Sequences shorter than the conv window, started from a nonzero state and cache."""
+    w = W.scan_prefill(batch=2, seqlen=L, dim=130, unsaturated=True)
+    rng = np.random.Generator(np.random.PCG64(11))
+    st_in = rng.standard_normal((2, 130, 16)).astype(np.float32)
+    cc_in = rng.standard_normal((2, 130, 3)).astype(np.float32)
+    y, st, cc = scan_gpu(w, state_in=torch.from_numpy(st_in).to(DEV), cache_in=torch.from_numpy(cc_in).to(DEV))
+    yo, ho, co = scan_oracle(w, state_in=st_in.astype(np.float64), cache_in=cc_in.astype(np.float64))
+    check(np64(y), yo, TOL_BF16, f"L={L} y")
+    check(np64(st), ho, TOL_BF16, f"L={L} state")
+    assert np.array_equal(np64(cc), co)
+
+
+def test_scan_writes_every_output_and_is_deterministic():
+    w = W.scan_prefill(batch=2, seqlen=200, dim=200)
+    y1, s1, c1 = scan_gpu(w, y_fill=float("nan"), time_split=7)
+    assert torch.isfinite(y1).all()
+    y2, s2, c2 = scan_gpu(w, y_fill=float("nan"), time_split=7)
+    assert torch.equal(y1, y2) and torch.equal(s1, s2) and torch.equal(c1, c2)
+
+
+def test_scan_causality():
+    """Changing the inputs at t0 leaves every output before t0 bit-identical."""
+    w = W.scan_prefill(batch=1, seqlen=120, dim=64, unsaturated=True)
+    y1, _, _ = scan_gpu(w, time_split=4)
+    for k in ("x", "z", "B", "C", "dt"):
+        w2 = W.Workload(w.name, w.kind, w.dims, {kk: v.copy() for kk, v in w.arrays.items()}, set(w.bf16), w.opts)
+        a = w2.arrays[k]
+        if k in w2.bf16:
+            a[:, 70] = W.bf16_bits(W.bf16_to_f32(a[:, 70]) + 1.0)
+        else:
+            a[:, 70] += 1.0
+        y2, _, _ = scan_gpu(w2, time_split=4)
+        assert torch.equal(y1[:, :70], y2[:, :70]), k
+        assert not torch.equal(y1[:, 70], y2[:, 70]), k
+
+
+def _sample(n, k, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.sort(rng.choice(n, size=k, replace=False))
+
+
+def test_scan_prefill_full_size():
+    """Bit-Axon layer prefill at full size (batch 1, L 2048, E 7680), library's
+    own time split, both output dtypes; oracle on 96 sampled channels."""
+    w = W.scan_prefill()
+    ch = _sample(7680, 96, 21)
+    yo, ho, co = scan_oracle(w, channels=ch)
+    for y_dtype in (torch.float32, torch.bfloat16):
+        y, st, cc = scan_gpu(w, y_dtype=y_dtype)
+        idx = torch.from_numpy(ch).to(DEV)
+        check(np64(y.index_select(2, idx)), yo, TOL_BF16, "prefill full y", out_bf16=(y_dtype == torch.bfloat16))
+        check(np64(st.index_select(1, idx)), ho, TOL_BF16, "prefill full state")
+        assert np.array_equal(np64(cc.index_select(1, idx)), co)
+
+
+def test_scan_bulk_full_size():
+    """Bulk scan at full size (batch 8, L 4096, E 7680, bf16 u/dt/z); oracle on 48
+    sampled channels of batches 0 and 7."""
+    w = W.scan_bulk()
+    ch = _sample(7680, 48, 22)
+    yo, ho, _ = scan_oracle(w, batches=[0, 7], channels=ch)
+    y, st, _ = scan_gpu(w, y_dtype=torch.bfloat16)
+    idx = torch.from_numpy(ch).to(DEV)
+    bidx = torch.tensor([0, 7], device=DEV)
+    check(np64(y.index_select(0, bidx).index_select(2, idx)), yo, TOL_BF16, "bulk full y", out_bf16=True)
+    check(np64(st.index_select(0, bidx).index_select(1, idx)), ho, TOL_BF16, "bulk full state")
