@@ -95,8 +95,9 @@ typedef enum {
  *   y             (Bt, L, E) y_dtype: y_t = (C_t . h_t + D*u_t) * SiLU(z_t)
  *   workspace     device scratch of at least ssm_scan_workspace_size(p) bytes (may be
  *                 NULL when that size is 0); 256-byte aligned; not touched by other calls
- *   time_split    0: the library chooses; >= 1: split the sequence into that many
- *                 segments scanned in parallel and combined (at most 16)
+ *   time_split    0: the library chooses; >= 1: split the sequence into at most that
+ *                 many segments scanned in parallel and combined (at most 32; each
+ *                 segment keeps at least 4 steps)
  * Supported: N = 16.  L = 0 only copies the state/cache inputs to the outputs.
  * ---------------------------------------------------------------------- */
 typedef struct ssm_scan_params {
@@ -191,8 +192,9 @@ ssm_status_t ssm_decode_check(const ssm_decode_params_t *p);
  *   out       (Bt, L, H, P) out_dtype
  *   dA[l] = sum_{i<=l} dt[i] A_h inside each chunk of chunk_size tokens (inclusive);
  *   state passing: S <- e^{dA[Q-1]} S + sum_s e^{dA[Q-1]-dA[s]} dt[s] x[s] (outer) B[s].
- * Requires L % chunk_size == 0 (SSM_ERR_INVALID_ARG otherwise).
- * Supported: N = 64, P % 16 == 0 and P <= 128, chunk_size = 128.
+ * Requires L % chunk_size == 0 (SSM_ERR_INVALID_ARG otherwise) and x, B, C
+ * 16-byte aligned.
+ * Supported: x and B/C in bf16, N = 64, P % 16 == 0 and P <= 128, chunk_size = 128.
  * ---------------------------------------------------------------------- */
 typedef struct ssm_chunk_params {
   uint32_t struct_size; /* = sizeof(ssm_chunk_params_t) */

@@ -75,24 +75,31 @@ ssm_status_t check_dt_bounds(float lo, float hi) {
 
 // ---------------------------------------------------------------- scan
 
+// Number of time segments.  A wave issues at most about one VALU instruction
+// every 9 cycles on its own and needs 2-3 companions on its SIMD to keep the
+// VALU busy; the kernels hold 3 waves per SIMD (256 CUs x 4 SIMDs), so the
+// split makes batch * channel groups * segments fill those 3072 slots in one
+// round.  Segments keep at least 32 steps (the summary pass and the
+// composition cost a fixed amount per segment), and every segment past the
+// first starts at t >= 4, so only the first reads the conv cache (which the
+// last one may overwrite in place).
 int scan_split(const ssm_scan_params_t* p) {
   const int L = p->seqlen;
-  if (L <= 1) return 1;
   int s = p->time_split;
   if (s <= 0) {
     const long groups = static_cast<long>(p->batch) * ((p->dim + 63) / 64);
-    const long target = 2048;  // waves: two per SIMD on 256 CUs x 4 SIMDs
-    s = groups >= target ? 1 : static_cast<int>((target + groups - 1) / groups);
-    s = std::min(s, std::max(1, L / 64));
+    const long slots = 3 * 1024;
+    s = groups >= slots ? 1 : static_cast<int>(slots / groups);
+    s = std::min(s, std::max(1, L / 32));
   }
-  s = std::min(std::min(s, ssm::kScanMaxSplit), L);
+  s = std::min(std::min(s, ssm::kScanMaxSplit), std::max(1, L / 4));
+  if (s <= 1) return 1;
   const int seg = (L + s - 1) / s;
   return (L + seg - 1) / seg;
 }
 
 size_t scan_ws(const ssm_scan_params_t* p) {
-  if (p->batch <= 0 || p->seqlen <= 0) return 0;
-  return ssm::scan_bcr_bytes(p->batch, p->seqlen);
+  return ssm::scan_workspace_bytes(p->batch, p->seqlen, p->dim, scan_split(p));
 }
 
 ssm_status_t scan_check(const ssm_scan_params_t* p) {
@@ -108,7 +115,7 @@ ssm_status_t scan_check(const ssm_scan_params_t* p) {
     return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "x/y/bc/dt/z_dtype");
   if (p->z && p->z_dtype != p->x_dtype) return fail(SSM_ERR_UNSUPPORTED, "%s must equal x_dtype", "z_dtype");
   if (p->time_split < 0 || p->time_split > ssm::kScanMaxSplit)
-    return fail(SSM_ERR_INVALID_ARG, "%s must be in [0, 16]", "time_split");
+    return fail(SSM_ERR_INVALID_ARG, "%s must be in [0, 32]", "time_split");
   if (!p->A) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "A");
   if (p->conv_w) {
     if (p->conv_k != ssm::kConvK) return fail(SSM_ERR_UNSUPPORTED, "%s must be 4", "conv_k");
@@ -129,7 +136,10 @@ ssm_status_t scan_check(const ssm_scan_params_t* p) {
     if (!p->B || !p->C) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "B/C");
     if (!p->dt) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "dt");
   }
-  if (Bt * ((E + 63) / 64) > 0x7fffffffULL) return fail(SSM_ERR_UNSUPPORTED, "%s too large", "batch*dim");
+  if (Bt * ((E + 63) / 64) * ssm::kScanMaxSplit > 0x7fffffffULL)
+    return fail(SSM_ERR_UNSUPPORTED, "%s too large", "batch*dim");
+  if ((L + 64) * E * 4 >= 0x80000000ULL)
+    return fail(SSM_ERR_UNSUPPORTED, "%s: one batch row must stay under 2 GiB", "seqlen*dim");
   const Range y{p->y, tok * E * esize(p->y_dtype)};
   const Range ins[] = {
       {p->x, tok * E * esize(p->x_dtype)},
@@ -230,6 +240,10 @@ ssm_status_t chunk_check(const ssm_chunk_params_t* p) {
     return fail(SSM_ERR_UNSUPPORTED, "%s must be a multiple of 16 and at most 128", "headdim");
   if (!valid_dtype(p->x_dtype) || !valid_dtype(p->bc_dtype) || !valid_dtype(p->out_dtype))
     return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "x/bc/out_dtype");
+  if (p->x_dtype != SSM_BF16 || p->bc_dtype != SSM_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "%s must be bf16", "x_dtype/bc_dtype");
+  if ((reinterpret_cast<uintptr_t>(p->x) | reinterpret_cast<uintptr_t>(p->B) | reinterpret_cast<uintptr_t>(p->C)) & 15)
+    return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "x/B/C");
   if (!p->A) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "A");
   ssm_status_t s = check_dt_bounds(p->dt_min, p->dt_max);
   if (s != SSM_OK) return s;
@@ -289,9 +303,9 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_params_t* p, void* stream) {
   ssm::ScanKernelArgs& k = l.k;
   k.x = p->x;
   k.z = p->z;
-  k.dt = p->dt_rank1 ? nullptr : p->dt;
+  k.dt = p->dt;
   k.y = p->y;
-  k.bcr = static_cast<const float*>(p->workspace);
+  k.bc = static_cast<const float*>(p->workspace);
   k.A = p->A;
   k.D = p->D;
   k.dt_w = p->dt_rank1 ? p->dt_w : nullptr;
@@ -308,6 +322,9 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_params_t* p, void* stream) {
   k.n_egroups = (p->dim + 63) / 64;
   k.nseg = scan_split(p);
   k.seg_len = p->seqlen > 0 ? (p->seqlen + k.nseg - 1) / k.nseg : 0;
+  k.summ = k.nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(p->workspace) +
+                                                 ssm::scan_summary_offset(p->batch, p->seqlen))
+                      : nullptr;
   k.dt_min = p->dt_min;
   k.dt_max = p->dt_max;
   softplus_thresholds(p->dt_min, p->dt_max, &k.sp_lo, &k.sp_hi);
@@ -320,8 +337,7 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_params_t* p, void* stream) {
   l.conv = p->conv_w != nullptr;
   l.B = p->B;
   l.C = p->C;
-  l.r = p->dt_rank1 ? static_cast<const float*>(p->dt) : nullptr;
-  l.bcr_out = static_cast<float*>(p->workspace);
+  l.bc_out = static_cast<float*>(p->workspace);
   if (p->batch == 0) return ok();
   return hip_status(ssm::launch_scan(l, static_cast<hipStream_t>(stream)));
 }

@@ -1,0 +1,440 @@
+// Fused selective scan for gfx950 (kernel templates; included once per
+// storage-type pair by the scan_xy_*.hip units): causal depthwise conv1d (k=4) + SiLU, the
+// step size dt = clip(softplus(dt_proj + dt_bias), lo, hi), the diagonal
+// recurrence h_t = exp(dt*A) h_{t-1} + dt*B_t*u_t with readout
+// y_t = C_t . h_t + D*u_t, and the gate y * SiLU(z), in one pass over HBM.
+//
+// Page "Axon-SSM: selective state space model": section "Algorithm" (the
+// dataflow x_branch -> conv1d -> SiLU -> scan -> y * SiLU(z)), "SSM scan"
+// (sequential over seq_len), "JIT-compiled kernels" (_ssm_fma = dA*h + dB*x_t
+// fused with no intermediate tensors; _compute_dt = clip(softplus(dt +
+// dt_bias))), "Autoregressive decoding" (prefill builds conv_cache from the last
+// K-1 positions).  Page "What is the Mamba model?", sections "Parallel
+// prefix-scan" and "chunkscan": the sequence is cut into segments scanned in
+// parallel, each reduced to its affine map (prod exp(dt A), h_end from 0), the
+// maps composed in order, and every segment re-run from its incoming state.
+//
+// Mapping: one lane = one (batch, channel); its 16 fp32 states stay in VGPRs
+// for the whole segment.  A workgroup is one wave of 64 consecutive channels,
+// so each x/dt/z/y access of a step is one contiguous 128- or 256-byte
+// segment, issued as a buffer load whose per-lane offset never changes (the
+// step's position travels in the scalar offset).  B_t and C_t are the same for
+// every channel of a batch row: they are packed once into 128-byte fp32 rows
+// and each step reads its row with two scalar loads into SGPRs, which the
+// VALU takes as operands directly (an LDS broadcast would move 64 copies of
+// every value through the LDS return path, which then limits the loop).
+//
+// Time split (nseg > 1): launch 1 reduces segments 0..nseg-2 to their
+// summaries (segment 0 from the true initial state, the others from zero);
+// launch 2 composes them into every segment's incoming state and runs all
+// segments in full.  Summaries travel through the workspace.
+#include <type_traits>
+
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kBlk = kScanBlk;          // steps per block: one tile of vector loads
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any range: the store is dropped
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+// Memory the kernel never writes, in the constant address space: uniform
+// loads from it become scalar loads.
+typedef __attribute__((address_space(4))) float cfloat;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+template <typename T>
+struct BufIO;
+
+template <>
+struct BufIO<float> {
+  using raw = uint32_t;
+  static constexpr uint32_t bytes = 4;
+  __device__ static raw load(rsrc_t r, uint32_t vo, uint32_t so) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0);
+  }
+  __device__ static float f32(raw v) { return __uint_as_float(v); }
+  __device__ static void store(float v, rsrc_t r, uint32_t vo, uint32_t so) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, vo, so, 0);
+  }
+};
+
+template <>
+struct BufIO<bf16s> {
+  using raw = uint16_t;
+  static constexpr uint32_t bytes = 2;
+  __device__ static raw load(rsrc_t r, uint32_t vo, uint32_t so) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0);
+  }
+  __device__ static float f32(raw v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+  __device__ static void store(float v, rsrc_t r, uint32_t vo, uint32_t so) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v)), r, vo, so, 0);
+  }
+};
+
+struct LaneCtx {
+  int b, e;
+  bool act;
+  float al0;              // A[e, 0] * log2(e)
+  float d, dtw, dtb;
+  float cw0, cw1, cw2, cw3, cb;
+};
+
+// kMain: a whole sequence (nseg == 1) or, after kPass1, segments 1..nseg-1.
+// dA[n] = exp(dt A[e, n]).  POW: A[e, n] = (n+1) A[e, 0] for every n, so
+// exp(dt A[e, n]) = r^(n+1) with r = exp(dt A[e, 0]), the powers taken by a
+// depth-5 product tree.  Otherwise one exponential per state, with A[e, n]
+// log2(e) read back from the wave's LDS copy ([n / 4][lane] float4s).
+template <bool POW>
+__device__ __forceinline__ void decay(float dt, float al0, const float4* al2, float (&dA)[kScanN]) {
+  if (POW) {
+    dA[0] = exp2_fast(dt * al0);
+#pragma unroll
+    for (int k = 1; k < kScanN; ++k) dA[k] = (k & 1) ? dA[(k - 1) / 2] * dA[(k - 1) / 2] : dA[k - 1] * dA[0];
+  } else {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = al2[q * 64 + lane];
+      dA[4 * q + 0] = exp2_fast(dt * v.x);
+      dA[4 * q + 1] = exp2_fast(dt * v.y);
+      dA[4 * q + 2] = exp2_fast(dt * v.z);
+      dA[4 * q + 3] = exp2_fast(dt * v.w);
+    }
+  }
+}
+
+enum Mode { kPass1 = 1, kMain = 2 };
+
+template <typename XT, typename YT, int DTM, bool CONV, bool GATE>
+struct Scan {
+  using DT = typename std::conditional<DTM == 2, bf16s, float>::type;
+  using XIO = BufIO<XT>;
+  using DIO = BufIO<DT>;
+  using YIO = BufIO<YT>;
+
+  const ScanKernelArgs& a;
+  const LaneCtx c;
+  rsrc_t rx, rz, rdt, ry;
+  const cfloat* rows;              // this batch row's packed B/C rows (constant memory)
+  uint32_t vx, vdt, vy;            // per-lane byte offsets of this channel inside a (t, :) row
+  uint32_t rb_x, rb_dt, rb_y;      // bytes per time step
+  const float4* al2;               // A[e, n] log2(e) as [n / 4][lane] float4s (LDS)
+  float asat[kScanN];              // exp(dt_max A[e, n]): the decay on the upper clip
+
+  __device__ Scan(const ScanKernelArgs& a_, const LaneCtx& c_, const float4* al2_, const float (&asat_)[kScanN])
+      : a(a_), c(c_), al2(al2_) {
+    const uint32_t L = a.seqlen, E = a.dim;
+    const size_t tok0 = static_cast<size_t>(c.b) * L;  // first token of this batch row
+    rx = make_rsrc(static_cast<const char*>(a.x) + tok0 * E * XIO::bytes, L * E * XIO::bytes);
+    rz = make_rsrc(static_cast<const char*>(a.z ? a.z : a.x) + tok0 * E * XIO::bytes, L * E * XIO::bytes);
+    ry = make_rsrc(static_cast<char*>(a.y) + tok0 * E * YIO::bytes, L * E * YIO::bytes);
+    if constexpr (DTM == 0) {
+      rdt = make_rsrc(static_cast<const float*>(a.dt) + tok0, L * 4u);
+      vdt = 0;
+      rb_dt = 4;
+    } else {
+      rdt = make_rsrc(static_cast<const char*>(a.dt) + tok0 * E * DIO::bytes, L * E * DIO::bytes);
+      vdt = static_cast<uint32_t>(c.e) * DIO::bytes;
+      rb_dt = E * DIO::bytes;
+    }
+    rows = (const cfloat*)(a.bc + tok0 * kBcRow);
+    vx = static_cast<uint32_t>(c.e) * XIO::bytes;
+    vy = c.act ? static_cast<uint32_t>(c.e) * YIO::bytes : kOob;
+    rb_x = E * XIO::bytes;
+    rb_y = E * YIO::bytes;
+#pragma unroll
+    for (int n = 0; n < kScanN; ++n) asat[n] = asat_[n];
+  }
+
+  // Raw (pre-conv) input at time p: x when p >= 0, the cache entry K-1+p
+  // (oldest first) before the sequence, 0 at a fresh prefill.
+  __device__ __forceinline__ float raw_at(int p) const {
+    if (p >= a.seqlen) return 0.0f;  // only reachable for an empty segment
+    if (p >= 0) return XIO::f32(XIO::load(rx, vx, static_cast<uint32_t>(p) * rb_x));
+    if (a.conv_cache_in == nullptr) return 0.0f;
+    return a.conv_cache_in[(static_cast<size_t>(c.b) * a.dim + c.e) * (kConvK - 1) + (kConvK - 1 + p)];
+  }
+
+  struct Tile {
+    typename XIO::raw x[kBlk];
+    typename DIO::raw d[kBlk];
+    typename XIO::raw z[kBlk];
+  };
+
+  template <bool FULL>
+  __device__ __forceinline__ void load_block(int tb, int t1, Tile& T) const {
+    constexpr bool has_z = FULL && GATE;
+#pragma unroll
+    for (int i = 0; i < kBlk; ++i) {
+      const uint32_t t = static_cast<uint32_t>(min(tb + i, t1 - 1));
+      T.x[i] = XIO::load(rx, vx, t * rb_x);
+      T.d[i] = DIO::load(rdt, vdt, t * rb_dt);
+      if (has_z) T.z[i] = XIO::load(rz, vx, t * rb_x);
+    }
+  }
+
+  // One step.  FULL: readout, skip, gate, store.  Otherwise state update only
+  // and the running sum of dt for the segment's decay product.
+  template <bool POW, bool FULL>
+  __device__ __forceinline__ void step(int t, const Tile& T, int i, float (&h)[kScanN], float (&win)[3],
+                                       float& sdt) const {
+    constexpr bool has_z = FULL && GATE;
+    // the step's B/C row: wave-uniform scalar loads, in flight during the
+    // row-independent work below
+    const cfloat* row = rows + static_cast<size_t>(t) * kBcRow;
+    float bv[kScanN], cv[kScanN];
+#pragma unroll
+    for (int n = 0; n < kScanN; ++n) bv[n] = row[n];
+    if (FULL) {
+#pragma unroll
+      for (int n = 0; n < kScanN; ++n) cv[n] = row[kScanN + n];
+    }
+    float u = XIO::f32(T.x[i]);
+    if (CONV) {
+      const float xc = fmaf(c.cw0, win[0], fmaf(c.cw1, win[1], fmaf(c.cw2, win[2], fmaf(c.cw3, u, c.cb))));
+      win[0] = win[1];
+      win[1] = win[2];
+      win[2] = u;
+      u = silu(xc);
+    }
+    const float pre = (DTM == 0) ? fmaf(c.dtw, DIO::f32(T.d[i]), c.dtb) : DIO::f32(T.d[i]) + c.dtb;
+    // dt = clip(softplus(pre), lo, hi).  Lanes at or beyond the thresholds
+    // take the clip value directly (exact: softplus is increasing); softplus
+    // itself only runs when some lane of the wave is inside the band.
+    float dt;
+    if (a.dt_softplus) {
+      dt = (pre >= a.sp_hi) ? a.dt_max : a.dt_min;
+      const bool mid = (pre > a.sp_lo) && (pre < a.sp_hi);
+      if (__any(mid)) {
+        const float sp = softplus(pre);
+        dt = mid ? __builtin_amdgcn_fmed3f(sp, a.dt_min, a.dt_max) : dt;
+      }
+    } else {
+      dt = __builtin_amdgcn_fmed3f(pre, a.dt_min, a.dt_max);
+    }
+    if (!FULL) sdt += dt;
+    const float dtu = dt * u;
+    const float gate = has_z ? silu(XIO::f32(T.z[i])) : 1.0f;
+    if (__all(dt == a.dt_max)) {
+      // every lane on the upper clip: exp(dt_max A[e, n]) was computed once,
+      // by the same arithmetic as decay()
+#pragma unroll
+      for (int n = 0; n < kScanN; ++n) h[n] = fmaf(asat[n], h[n], dtu * bv[n]);
+    } else {
+      float dA[kScanN];
+      decay<POW>(dt, c.al0, al2, dA);
+#pragma unroll
+      for (int n = 0; n < kScanN; ++n) h[n] = fmaf(dA[n], h[n], dtu * bv[n]);
+    }
+    if (!FULL) {
+      // nothing reads the state between steps of the summary pass; pin it
+      // here, or the compiler interleaves several steps of the recurrence and
+      // runs out of registers
+#pragma unroll
+      for (int n = 0; n < kScanN; ++n) asm volatile("" : "+v"(h[n]));
+    }
+    if (FULL) {
+      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int n = 0; n < kScanN; ++n) acc[n & 3] = fmaf(cv[n], h[n], acc[n & 3]);
+      const float yv = fmaf(c.d, u, (acc[0] + acc[1]) + (acc[2] + acc[3])) * gate;
+      YIO::store(yv, ry, vy, static_cast<uint32_t>(t) * rb_y);
+    }
+  }
+
+  // Steps [tb, min(tb + kBlk, t1)) with this block's tile T, while the next
+  // block's loads go into N.  The prefetch is issued unconditionally (its
+  // offsets are clamped to the segment) so every block issues the same loads
+  // and the waits before each step only cover that step's own loads.  Two
+  // tiles alternate roles so no register copy ever waits on a load in flight.
+  template <bool POW, bool FULL>
+  __device__ __forceinline__ void block(int tb, int t1, const Tile& T, Tile& N, float (&h)[kScanN],
+                                        float (&win)[3], float& sdt) const {
+    load_block<FULL>(tb + kBlk, t1, N);
+    if (tb + kBlk <= t1) {
+#pragma unroll
+      for (int i = 0; i < kBlk; ++i) {
+        step<POW, FULL>(tb + i, T, i, h, win, sdt);
+        // each step's scalar loads stay inside the step: hoisted across steps
+        // they would need a second set of SGPRs
+        asm volatile("" ::: "memory");
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBlk; ++i) {
+        if (tb + i < t1) step<POW, FULL>(tb + i, T, i, h, win, sdt);
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+
+  // Scan steps [t0, t1) from state h.
+  template <bool POW, bool FULL>
+  __device__ __forceinline__ void run(int t0, int t1, float (&h)[kScanN], float (&win)[3], float& sdt) const {
+    if (t0 >= t1) return;
+    Tile ta, tb_;
+    load_block<FULL>(t0, t1, ta);
+#pragma unroll 1
+    for (int tb = t0;; tb += 2 * kBlk) {
+      block<POW, FULL>(tb, t1, ta, tb_, h, win, sdt);
+      if (tb + kBlk >= t1) break;
+      block<POW, FULL>(tb + kBlk, t1, tb_, ta, h, win, sdt);
+      if (tb + 2 * kBlk >= t1) break;
+    }
+  }
+};
+
+template <typename XT, typename YT, int DTM, bool CONV, bool GATE, int MODE>
+__global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
+  const int lane = threadIdx.x;
+  // block -> (segment, batch, channel group), channel groups fastest: the
+  // neighbouring workgroups, spread over the XCDs, share their B/C rows.
+  int bid = blockIdx.x;
+  const int g = uniform(bid % a.n_egroups);
+  bid /= a.n_egroups;
+  LaneCtx c;
+  c.b = uniform(bid % a.batch);
+  const int seg = uniform(bid / a.batch);
+  const int e_raw = g * 64 + lane;
+  c.act = e_raw < a.dim;
+  c.e = c.act ? e_raw : a.dim - 1;
+
+  __shared__ float4 s_al2[4 * 64];
+  bool prog = true;
+  const float a0 = a.A[static_cast<size_t>(c.e) * kScanN];
+  float al2v[kScanN];
+#pragma unroll
+  for (int n = 0; n < kScanN; ++n) {
+    const float an = a.A[static_cast<size_t>(c.e) * kScanN + n];
+    al2v[n] = an * kLog2e;
+    prog = prog && (an == static_cast<float>(n + 1) * a0);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    s_al2[q * 64 + lane] = make_float4(al2v[4 * q], al2v[4 * q + 1], al2v[4 * q + 2], al2v[4 * q + 3]);
+  c.al0 = al2v[0];
+  c.d = a.D ? a.D[c.e] : 0.0f;
+  c.dtw = a.dt_w ? a.dt_w[c.e] : 0.0f;
+  c.dtb = a.dt_bias ? a.dt_bias[c.e] : 0.0f;
+  if (CONV) {
+    c.cw0 = a.conv_w[c.e * kConvK + 0];
+    c.cw1 = a.conv_w[c.e * kConvK + 1];
+    c.cw2 = a.conv_w[c.e * kConvK + 2];
+    c.cw3 = a.conv_w[c.e * kConvK + 3];
+    c.cb = a.conv_b ? a.conv_b[c.e] : 0.0f;
+  } else {
+    c.cw0 = c.cw1 = c.cw2 = c.cw3 = c.cb = 0.0f;
+  }
+  const bool use_pow = __all(prog);
+  // the decay factors on the upper clip, with the arithmetic of the steps
+  float asat[kScanN];
+  if (use_pow) decay<true>(a.dt_max, c.al0, s_al2, asat);
+  else decay<false>(a.dt_max, c.al0, s_al2, asat);
+  const Scan<XT, YT, DTM, CONV, GATE> S(a, c, s_al2, asat);
+  const int t0 = seg * a.seg_len;
+  const int t1 = min(t0 + a.seg_len, a.seqlen);
+  float win[3] = {0.0f, 0.0f, 0.0f};
+  if (CONV) {
+    win[0] = S.raw_at(t0 - 3);
+    win[1] = S.raw_at(t0 - 2);
+    win[2] = S.raw_at(t0 - 1);
+  }
+  float h[kScanN];
+  float sdt = 0.0f;
+  const size_t sbase = (static_cast<size_t>(c.b) * a.dim + c.e) * kScanN;
+  // summaries: [(b, g)][segment][16 states + sum dt][lane]
+  float* summ = a.summ + (static_cast<size_t>(c.b) * a.n_egroups + g) * (a.nseg - 1) * (kScanN + 1) * 64;
+
+  if (MODE == kMain && seg > 0) {
+    // state entering this segment: segment 0's end state, then the summaries
+    // of segments 1..seg-1 applied in order: h <- exp(A sum dt) h + h_end
+#pragma unroll
+    for (int n = 0; n < kScanN; ++n) h[n] = summ[n * 64 + lane];
+    for (int j = 1; j < seg; ++j) {
+      const float* sj = summ + static_cast<size_t>(j) * (kScanN + 1) * 64;
+      const float sd = sj[kScanN * 64 + lane];
+#pragma unroll
+      for (int n = 0; n < kScanN; ++n) h[n] = fmaf(exp2_fast(al2v[n] * sd), h[n], sj[n * 64 + lane]);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < kScanN; ++n) h[n] = (seg == 0 && a.state_in) ? a.state_in[sbase + n] : 0.0f;
+  }
+
+  if (MODE == kPass1) {
+    // summary of segments 0..nseg-2: the end state from the true initial state
+    // (segment 0) or from zero (the others), and the sum of dt
+    if (use_pow) S.template run<true, false>(t0, t1, h, win, sdt);
+    else S.template run<false, false>(t0, t1, h, win, sdt);
+    float* ss = summ + static_cast<size_t>(seg) * (kScanN + 1) * 64;
+#pragma unroll
+    for (int n = 0; n < kScanN; ++n) ss[n * 64 + lane] = h[n];
+    ss[kScanN * 64 + lane] = sdt;
+    return;
+  }
+  if (use_pow) S.template run<true, true>(t0, t1, h, win, sdt);
+  else S.template run<false, true>(t0, t1, h, win, sdt);
+  if (seg == a.nseg - 1 && c.act) {
+    if (a.state_out) {
+#pragma unroll
+      for (int n = 0; n < kScanN; ++n) a.state_out[sbase + n] = h[n];
+    }
+    if (CONV && a.conv_cache_out) {
+      const size_t cbase = (static_cast<size_t>(c.b) * a.dim + c.e) * (kConvK - 1);
+      a.conv_cache_out[cbase + 0] = win[0];
+      a.conv_cache_out[cbase + 1] = win[1];
+      a.conv_cache_out[cbase + 2] = win[2];
+    }
+  }
+}
+
+template <typename XT, typename YT, int DTM, bool CONV, bool GATE>
+hipError_t launch_scan_t(const ScanLaunch& l, hipStream_t stream) {
+  const ScanKernelArgs& a = l.k;
+  const unsigned groups = static_cast<unsigned>(a.batch) * static_cast<unsigned>(a.n_egroups);
+  if (groups == 0) return hipSuccess;
+  if (a.nseg > 1) {
+    hipLaunchKernelGGL((scan_kernel<XT, YT, DTM, CONV, GATE, kPass1>), dim3(groups * (a.nseg - 1)), dim3(64), 0,
+                       stream, a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL((scan_kernel<XT, YT, DTM, CONV, GATE, kMain>), dim3(groups * a.nseg), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename XT, typename YT, int DTM, bool CONV>
+hipError_t pick_gate(const ScanLaunch& l, hipStream_t s) {
+  return l.k.has_z ? launch_scan_t<XT, YT, DTM, CONV, true>(l, s) : launch_scan_t<XT, YT, DTM, CONV, false>(l, s);
+}
+
+template <typename XT, typename YT, int DTM>
+hipError_t pick_conv(const ScanLaunch& l, hipStream_t s) {
+  return l.conv ? pick_gate<XT, YT, DTM, true>(l, s) : pick_gate<XT, YT, DTM, false>(l, s);
+}
+
+template <typename XT, typename YT>
+hipError_t pick_dt(const ScanLaunch& l, hipStream_t s) {
+  switch (l.dt_mode) {
+    case 0: return pick_conv<XT, YT, 0>(l, s);
+    case 1: return pick_conv<XT, YT, 1>(l, s);
+    default: return pick_conv<XT, YT, 2>(l, s);
+  }
+}
+
+}  // namespace
+
+// Launch for one (x dtype, y dtype) pair; defined in scan_xy_*.hip.
+template <>
+hipError_t launch_scan_xy<SSM_SCAN_XT, SSM_SCAN_YT>(const ScanLaunch& l, hipStream_t stream) {
+  return pick_dt<SSM_SCAN_XT, SSM_SCAN_YT>(l, stream);
+}
+
+}  // namespace ssm

@@ -10,19 +10,21 @@ namespace ssm {
 enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
 
 // ---- fused scan ----------------------------------------------------------
-// B, C and the rank-1 dt input are repacked per (batch, t) into one fp32 row
-// so the scan kernel reads them with wave-uniform scalar loads.
-constexpr int kScanN = 16;          // d_state handled by the fused scan
-constexpr int kBcrRow = 48;         // floats per packed row: B[16] C[16] r pad
-constexpr int kScanMaxSplit = 16;   // segments per workgroup (one wave each)
+// B and C are repacked per (batch, t) into one fp32 row [B0..B15, C0..C15] so
+// the scan kernel reads them with wave-uniform scalar loads.
+constexpr int kScanN = 16;         // d_state handled by the fused scan
+constexpr int kBcRow = 32;         // floats per packed row
+constexpr int kScanMaxSplit = 32;  // time segments per sequence
 constexpr int kConvK = 4;
+constexpr int kScanBlk = 4;        // steps per tile of prefetched vector loads
 
 struct ScanKernelArgs {
   const void* x;
   const void* z;
-  const void* dt;        // full-width dt (DTM 1/2); unused for rank-1
+  const void* dt;        // rank-1 r (batch, seqlen) f32, or full (batch, seqlen, dim)
   void* y;
-  const float* bcr;      // (batch*seqlen, kBcrRow)
+  const float* bc;       // packed rows (batch*seqlen + padding, kBcRow)
+  float* summ;           // per-segment summaries (time split only)
   const float* A;        // (dim, 16)
   const float* D;        // (dim) or null
   const float* dt_w;     // (dim) or null
@@ -45,11 +47,14 @@ struct ScanLaunch {
   bool conv;
   const void* B;
   const void* C;
-  const float* r;  // rank-1 dt input (batch, seqlen) or null
-  float* bcr_out;  // workspace
+  float* bc_out;  // = k.bc, written by the packing kernel
 };
 
-size_t scan_bcr_bytes(int batch, int seqlen);
+struct bf16s;
+size_t scan_workspace_bytes(int batch, int seqlen, int dim, int nseg);
+template <typename XT, typename YT>
+hipError_t launch_scan_xy(const ScanLaunch& l, hipStream_t stream);
+size_t scan_summary_offset(int batch, int seqlen);
 hipError_t launch_scan(const ScanLaunch& l, hipStream_t stream);
 
 // ---- decode step ---------------------------------------------------------

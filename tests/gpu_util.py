@@ -96,3 +96,41 @@ def scan_oracle(w: W.Workload, *, state_in=None, cache_in=None, batches=None, ch
         x, ch(f("A")), B, C, D=ch(f("D")), z=z, conv_w=ch(f("conv_w")) if o["conv"] else None,
         conv_cache=cci, dt_bias=ch(f("dt_bias")), dt_softplus=o["dt_softplus"], dt_min=float(o["dt_min"]),
         dt_max=float(o["dt_max"]), ssm_state=sti, **dt_kw)
+
+
+# ---------------------------------------------------------------------- SSD
+
+def ssd_gpu(w: W.Workload, *, out_dtype=torch.float32, state_in=None, want_state=True, D_override=None):
+    d = w.dims
+    o = w.opts
+    st = (torch.empty((d["batch"], d["nheads"], d["headdim"], d["d_state"]), dtype=torch.float32, device=DEV)
+          if want_state else None)
+    D = dev_tensor(w, "D") if D_override is None else torch.from_numpy(D_override).to(DEV)
+    out = ssm.chunk_scan_fwd(dev_tensor(w, "x"), dev_tensor(w, "dt"), dev_tensor(w, "A"), dev_tensor(w, "B"),
+                             dev_tensor(w, "C"), chunk_size=d["chunk_size"], D=D, dt_bias=dev_tensor(w, "dt_bias"),
+                             dt_softplus=o["dt_softplus"], dt_min=o["dt_min"], dt_max=o["dt_max"],
+                             state_in=state_in, state_out=st, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, st
+
+
+def ssd_oracle(w: W.Workload, *, heads=None, state_in=None, D_override=None, sequential=False):
+    """Oracle on (a sample of) the heads; heads are independent given B, C."""
+    o = w.opts
+    f = w.f64
+    hs = slice(None) if heads is None else heads
+    x = f("x")[:, :, hs]
+    dt = O.compute_dt(f("dt")[:, :, hs], f("dt_bias")[hs], float(o["dt_min"]), float(o["dt_max"]),
+                      use_softplus=o["dt_softplus"])
+    A = f("A")[hs]
+    D = (f("D") if D_override is None else np.asarray(D_override, np.float64))[hs]
+    Bm, Cm = f("B"), f("C")
+    H = w.dims["nheads"]
+    G = w.dims["ngroups"]
+    if heads is not None and G > 1:  # keep each sampled head's own group
+        grp = np.asarray(heads) // (H // G)
+        Bm, Cm = Bm[:, :, grp], Cm[:, :, grp]
+    st = None if state_in is None else np.asarray(state_in, np.float64)[:, hs]
+    if sequential:
+        return O.ssd_scan_sequential(x, dt, A, Bm, Cm, D=D, state=st)
+    return O.ssd_chunk_scan(x, dt, A, Bm, Cm, D=D, state=st, chunk_size=w.dims["chunk_size"])

@@ -32,7 +32,7 @@ def test_scan_tiny_fp32(unsat, split):
 
 
 @pytest.mark.parametrize("unsat", [False, True])
-@pytest.mark.parametrize("split", [0, 1, 3, 16])
+@pytest.mark.parametrize("split", [0, 1, 3, 16, 32])
 def test_scan_prefill_recipe_small(unsat, split):
     """The layer-prefill recipe (bf16 x/z, conv1d k=4 + SiLU, rank-1 dt, bf16 B/C)
     at batch 2, L 300, E 200: several waves, a ragged channel tail (200 = 3*64 + 8)
