@@ -1,0 +1,376 @@
+#!/usr/bin/env python3
+"""Throughput of the selective-scan hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|bulk]
+                    [--no-parts] [--no-cpu]
+
+A step is one ssm_scan_fwd call (conv1d + SiLU, dt, scan, readout, skip, gate,
+final state and conv cache) over one batch of the workload, with every input
+already resident in HBM.  The default workload is the Bit-Axon layer prefill
+(batch 1, L 2048, E 7680, N 16, bf16 x/z/B/C, bf16 y); --workload bulk times
+the bulk scan (batch 8, L 4096, E 7680, bf16 u/dt/z/y).  Inputs are the seeded
+synthetic recipes of ssm_workloads.py.
+
+Prints ONE JSON line.  Besides the throughput it carries
+* roofline: the main scan kernel's duration, measured with HIP events that the
+  library records on its own launch stream around that kernel, against its
+  roofline (FLOPS_PER_CH_STEP and the byte counts beside each workload give
+  the algorithmic work per unit);
+* cpu_baseline: the float64 oracle on the same workload on this host's CPU;
+* parts: the other entry points at their workloads (bulk scan, 8-layer decode
+  step, chunked SSD), each with its own kernel roofline.
+Counters of HBM traffic come from rocprofv3 runs recorded in profiles/; they
+are reported only while the kernel sources still hash to the recorded value.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selective-scan tokens/s and achieved HBM GB/s (% of peak) at E=7680, N=16"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix, published
+
+# Algorithmic work per unit, counted from the definition of each step (each
+# input read once, each output written once; FMA = 2 flops, exp/log/div = 1).
+# Scan flops per channel-step: decay 16 x (mul + exp) = 32; state 1 + 16 x (mul
+# + fma) = 49; readout 16 fma + D fma = 34; gate SiLU + mul = 5: 120.  The conv
+# (4 fma = 8), SiLU of its output (4) and the rank-1 dt with softplus and clip
+# (6) add 18 for the layer prefill.
+FLOPS_PER_CH_STEP = {"prefill": 138.0, "bulk": 120.0}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=("prefill", "bulk"), default="prefill")
+    ap.add_argument("--no-parts", action="store_true", help="skip the decode / SSD / other-scan lines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--only", choices=("prefill", "bulk", "decode", "ssd", "copy"), default=None,
+                    help="run just this workload's timed loop, no JSON line (for profiler runs); 'copy' "
+                         "copies 1 GiB device to device, the calibration for the HBM byte counters")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------- helpers
+
+def sources_digest():
+    """sha256 over the HIP sources; a recorded counter profile is used only while it matches."""
+    d = os.path.join(ROOT, "selective_state_space_03_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel_key):
+    """HBM bytes per launch from profiles/pmc_traffic.txt (FETCH_SIZE and
+    WRITE_SIZE per dispatch, each scaled by the copy-kernel calibration), or None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("#") or "=" not in line:
+                continue
+            k, v = line.split("=", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("sources_sha256") != sources_digest():
+        return None
+    try:
+        fetch = float(rec[f"{kernel_key}.fetch_kib"]) * float(rec["copy.fetch_factor"])
+        write = float(rec[f"{kernel_key}.write_kib"]) * float(rec["copy.write_factor"])
+    except KeyError:
+        return None
+    return (fetch + write) * 1024.0
+
+
+def dev_tensor(torch, w, key, device):
+    a = w.arrays.get(key)
+    if a is None:
+        return None
+    if key in w.bf16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class KernelTimer:
+    """Per-launch HIP events that the library records around its main kernel."""
+
+    def __init__(self, torch, ssm, n):
+        self.torch, self.ssm = torch, ssm
+        self.pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(n)]
+        self.i = 0
+
+    def arm(self):
+        s, e = self.pairs[self.i]
+        self.ssm.set_timing_events(s, e)
+        self.i += 1
+
+    def disarm(self):
+        self.ssm.set_timing_events(None, None)
+
+    def mean_ms(self):
+        ts = [s.elapsed_time(e) for s, e in self.pairs[: self.i]]
+        return float(np.mean(ts)), float(np.median(ts))
+
+
+def timed_loop(torch, ssm, calls, steps, warmup, per_step=1):
+    """Warm up, then run `steps` steps (each `per_step` consecutive calls from the
+    rotating list) between two synchronisations; returns wall ms/step and the
+    mean/median duration of the main kernel per call."""
+    n = len(calls)
+    for i in range(warmup * per_step):
+        calls[i % n].run()
+    torch.cuda.synchronize()
+    timer = KernelTimer(torch, ssm, steps * per_step)
+    t0 = time.perf_counter()
+    for i in range(steps * per_step):
+        timer.arm()
+        calls[i % n].run()
+    timer.disarm()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    kmean, kmed = timer.mean_ms()
+    return wall_ms, kmean, kmed
+
+
+# ------------------------------------------------------------------- workloads
+
+def scan_calls(torch, ssm, W, which, sets, device):
+    w = W.scan_prefill() if which == "prefill" else W.scan_bulk()
+    o, d = w.opts, w.dims
+    calls = []
+    for _ in range(sets):
+        x, A, B, C, dt = (dev_tensor(torch, w, k, device) for k in ("x", "A", "B", "C", "dt"))
+        y = torch.empty((d["batch"], d["seqlen"], d["dim"]), dtype=torch.bfloat16, device=device)
+        st = torch.empty((d["batch"], d["dim"], d["d_state"]), dtype=torch.float32, device=device)
+        cc = torch.empty((d["batch"], d["dim"], 3), dtype=torch.float32, device=device) if o["conv"] else None
+        calls.append(ssm.scan_fwd(
+            x, A, B, C, dt, D=dev_tensor(torch, w, "D", device), z=dev_tensor(torch, w, "z", device),
+            conv_w=dev_tensor(torch, w, "conv_w", device) if o["conv"] else None, conv_cache_out=cc,
+            dt_rank1=o["dt_rank1"], dt_w=dev_tensor(torch, w, "dt_w", device),
+            dt_bias=dev_tensor(torch, w, "dt_bias", device), dt_softplus=o["dt_softplus"],
+            dt_min=o["dt_min"], dt_max=o["dt_max"], ssm_state_out=st, y=y, prepare=True))
+    Bt, L, E, N = d["batch"], d["seqlen"], d["dim"], d["d_state"]
+    # algorithmic bytes: x/u, z (and E-wide dt) in, y out (bf16); B, C (bf16)
+    # and the rank-1 r; per-channel parameters; state (and conv cache) out.
+    ew = 2 * Bt * L * E * (3 if which == "prefill" else 4)
+    small = 2 * 2 * Bt * L * N + (4 * Bt * L if which == "prefill" else 0)
+    params = 4 * E * (N + 1 + (2 + 4 if which == "prefill" else 1))
+    outs = 4 * Bt * E * N + (4 * Bt * E * 3 if o["conv"] else 0)
+    return w, calls, dict(batch=Bt, seq_len=L, dim=E, d_state=N, bytes=ew + small + params + outs)
+
+
+def decode_calls(torch, ssm, W, layers, ring, device):
+    """Config of the batched decode step: batch 64, E 7680, N 16, fp32; `layers`
+    independent state/cache sets (like stacked layers, 37 MB each) so the
+    states stream from HBM instead of the last-level cache."""
+    w = W.decode_stream(prefill=0, steps=ring)
+    t = lambda k: torch.from_numpy(np.ascontiguousarray(w.arrays[k])).to(device)
+    X, Z, R, Bm, Cm = (t(k) for k in ("x", "z", "dt", "B", "C"))
+    A, D, cw, dw, db = (t(k) for k in ("A", "D", "conv_w", "dt_w", "dt_bias"))
+    g = torch.Generator(device="cpu").manual_seed(44)
+    Bt, E, N = w.dims["batch"], w.dims["dim"], w.dims["d_state"]
+    states = [torch.randn((Bt, E, N), generator=g).mul_(0.1).to(device) for _ in range(layers)]
+    caches = [torch.randn((Bt, E, 3), generator=g).to(device) for _ in range(layers)]
+    ys = [torch.empty((Bt, E), dtype=torch.float32, device=device) for _ in range(layers)]
+    calls = []
+    for s in range(ring):
+        for l in range(layers):
+            calls.append(ssm.decode_step(X[s], A, Bm[s], Cm[s], R[s], states[l], conv_cache=caches[l], D=D,
+                                         z=Z[s], conv_w=cw, dt_rank1=True, dt_w=dw, dt_bias=db,
+                                         dt_min=w.opts["dt_min"], dt_max=w.opts["dt_max"], y=ys[l],
+                                         prepare=True))
+    # per call: state r+w, cache r+w, x, z, y (fp32), r, B, C, parameters
+    byts = 2 * 4 * Bt * E * N + 2 * 4 * Bt * E * 3 + 3 * 4 * Bt * E + 4 * Bt * (1 + 2 * N) + 4 * E * (N + 4 + 3)
+    return calls, dict(batch=Bt, dim=E, d_state=N, layers=layers, bytes=byts)
+
+
+def ssd_calls(torch, ssm, W, device):
+    w = W.ssd_long()
+    d = w.dims
+    x, dtr, A, B, C, D, db = (dev_tensor(torch, w, k, device) for k in ("x", "dt", "A", "B", "C", "D", "dt_bias"))
+    out = torch.empty(x.shape, dtype=torch.bfloat16, device=device)
+    st = torch.empty((d["batch"], d["nheads"], d["headdim"], d["d_state"]), dtype=torch.float32, device=device)
+    call = ssm.chunk_scan_fwd(x, dtr, A, B, C, chunk_size=d["chunk_size"], D=D, dt_bias=db,
+                              dt_softplus=w.opts["dt_softplus"], dt_min=w.opts["dt_min"], dt_max=w.opts["dt_max"],
+                              state_out=st, out=out, prepare=True)
+    Bt, L, H, P, G, N, Q = (d[k] for k in ("batch", "seqlen", "nheads", "headdim", "ngroups", "d_state",
+                                            "chunk_size"))
+    byts = 2 * 2 * Bt * L * H * P + 2 * 2 * Bt * L * G * N + 4 * Bt * L * H + 4 * Bt * H * P * N + 4 * 3 * H
+    # dense flops: C.B^T per chunk and group, intra-chunk (causal half), state
+    # readout and chunk-state update per head
+    nch = L // Q
+    flops = Bt * nch * (2 * Q * Q * N * G + H * (Q * Q * P + 2 * Q * N * P + 2 * Q * N * P))
+    return [call], dict(batch=Bt, seq_len=L, nheads=H, headdim=P, d_state=N, chunk_size=Q, bytes=byts,
+                        flops=flops)
+
+
+def roof_hbm(nbytes, kernel_ms, traffic):
+    gbs = nbytes / (kernel_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+# ----------------------------------------------------------------------- CPU
+
+def cpu_baseline(W):
+    """The float64 oracle on the whole layer-prefill workload, single-threaded."""
+    from oracle import ssm_oracle as O
+    from threadpoolctl import threadpool_limits
+    w = W.scan_prefill()
+    f, o = w.f64, w.opts
+    args = dict(D=f("D"), z=f("z"), conv_w=f("conv_w"), dt_raw=f("dt"), dt_w=f("dt_w"), dt_bias=f("dt_bias"),
+                dt_softplus=o["dt_softplus"], dt_min=float(o["dt_min"]), dt_max=float(o["dt_max"]))
+    x, A, B, C = f("x"), f("A"), f("B"), f("C")
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.ssm_layer_scan(x, A, B, C, **args)
+        dt = time.perf_counter() - t0
+    tokens = w.dims["batch"] * w.dims["seqlen"]
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole layer-prefill workload (1 x 2048 tokens x 7680 channels, float64 numpy, "
+                      f"{dt:.1f} s on one core of {len(os.sched_getaffinity(0))} available)"}
+
+
+# ---------------------------------------------------------------------- main
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (nothing here shards or "
+              f"communicates across GPUs)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import selective_state_space_03_amd as ssm
+    import ssm_workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    ssm.lib()
+
+    if a.only == "copy":
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(a.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy: {a.steps} x 1 GiB device to device")
+        return
+    if a.only in ("decode", "ssd"):
+        calls, cfg = decode_calls(torch, ssm, W, 8, 16, dev) if a.only == "decode" else ssd_calls(torch, ssm, W, dev)
+        per = cfg.get("layers", 1)
+        wall, kmean, _ = timed_loop(torch, ssm, calls, a.steps, a.warmup, per_step=per)
+        log(f"{a.only}: {wall:.3f} ms/step, kernel {kmean * 1e3:.1f} us")
+        return
+
+    which = a.only or a.workload
+    # rotate buffer sets so the working set exceeds the 256 MB last-level cache
+    sets = 4 if which == "prefill" else 1
+    log(f"generating the {which} workload ({sets} buffer set(s))")
+    w, calls, cfg = scan_calls(torch, ssm, W, which, sets, dev)
+    wall, kmean, kmed = timed_loop(torch, ssm, calls, a.steps, a.warmup)
+    log(f"{which}: {wall:.3f} ms/step, main kernel mean {kmean * 1e3:.1f} us median {kmed * 1e3:.1f} us")
+    if a.only:
+        return
+    tokens = cfg["batch"] * cfg["seq_len"]
+    ch_steps = tokens * cfg["dim"]
+    value = tokens / (wall * 1e-3)
+    gflop = FLOPS_PER_CH_STEP[which] * ch_steps / 1e9
+    achieved_tf = gflop / kmean  # GFLOP / ms = TFLOP/s
+    traffic = recorded_traffic(f"scan_main_{which}")
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(wall, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": ("Bit-Axon SSM layer prefill" if which == "prefill" else "bulk selective scan"),
+                   "batch": cfg["batch"], "seq_len": cfg["seq_len"], "dim": cfg["dim"], "d_state": cfg["d_state"],
+                   "storage": "bf16 in/out, fp32 state", "buffer_sets": sets},
+        "hbm_gbps": round(cfg["bytes"] / (wall * 1e-3) / 1e9, 1),
+        "hbm_frac": round(cfg["bytes"] / (wall * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "channel_steps_per_s": round(ch_steps / (wall * 1e-3), 1),
+        "roofline": {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved_tf / FP32_VECTOR_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "scan_kernel (full-segment pass)",
+                     "kernel_us": round(kmean * 1e3, 2), "algorithmic_bytes": cfg["bytes"],
+                     "hbm_frac_of_kernel": round(cfg["bytes"] / (kmean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    del calls
+    torch.cuda.empty_cache()
+
+    if not a.no_parts:
+        parts = {}
+        other = "bulk" if which == "prefill" else "prefill"
+        log(f"part: {other} scan")
+        _, c2, cfg2 = scan_calls(torch, ssm, W, other, 4 if other == "prefill" else 1, dev)
+        st = 10 if other == "bulk" else 50
+        wall2, km2, _ = timed_loop(torch, ssm, c2, st, 2)
+        tok2 = cfg2["batch"] * cfg2["seq_len"]
+        parts[f"scan_{other}"] = {
+            "tokens_per_s": round(tok2 / (wall2 * 1e-3), 1), "ms_per_call": round(wall2, 4),
+            "hbm_gbps": round(cfg2["bytes"] / (wall2 * 1e-3) / 1e9, 1),
+            "roofline": roof_hbm(cfg2["bytes"], km2, recorded_traffic(f"scan_main_{other}")),
+            "config": {k: cfg2[k] for k in ("batch", "seq_len", "dim", "d_state")}}
+        del c2
+        torch.cuda.empty_cache()
+
+        log("part: decode step (8 state sets)")
+        c3, cfg3 = decode_calls(torch, ssm, W, 8, 16, dev)
+        wall3, km3, _ = timed_loop(torch, ssm, c3, 64, 4, per_step=cfg3["layers"])
+        per_call = wall3 / cfg3["layers"]
+        parts["decode_step"] = {
+            "tokens_per_s": round(cfg3["batch"] / (per_call * 1e-3), 1), "us_per_step": round(per_call * 1e3, 2),
+            "roofline": roof_hbm(cfg3["bytes"], km3, recorded_traffic("decode")),
+            "config": {k: cfg3[k] for k in ("batch", "dim", "d_state", "layers")}}
+        del c3
+        torch.cuda.empty_cache()
+
+        log("part: chunked SSD")
+        c4, cfg4 = ssd_calls(torch, ssm, W, dev)
+        wall4, km4, _ = timed_loop(torch, ssm, c4, 5, 1)
+        r4 = roof_hbm(cfg4["bytes"], km4, recorded_traffic("ssd"))
+        r4["mfma_tflops"] = round(cfg4["flops"] / (km4 * 1e-3) / 1e12, 2)
+        r4["mfma_frac"] = round(r4["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
+        parts["chunk_scan"] = {
+            "tokens_per_s": round(cfg4["seq_len"] * cfg4["batch"] / (wall4 * 1e-3), 1),
+            "ms_per_call": round(wall4, 4), "roofline": r4,
+            "config": {k: cfg4[k] for k in ("batch", "seq_len", "nheads", "headdim", "d_state", "chunk_size")}}
+        del c4
+        torch.cuda.empty_cache()
+        out["parts"] = parts
+
+    if not a.no_cpu:
+        log("oracle on the host CPU")
+        cb = cpu_baseline(W)
+        if which != "prefill":
+            cb["sample"] += " (the oracle baseline is quoted on the layer prefill)"
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

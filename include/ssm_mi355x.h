@@ -231,6 +231,15 @@ int32_t ssm_abi_version(void);
 /* sizeof of a params struct: which = 0 scan, 1 decode, 2 chunk; 0 otherwise. */
 size_t ssm_params_sizeof(int32_t which);
 
+/* Kernel timing for measurement tools.  start and stop are hipEvent_t handles
+ * owned by the caller (both NULL switches timing off).  While set, each entry
+ * point called on this thread records start on its stream right before the
+ * launch of its main kernel (the full-segment scan kernel of ssm_scan_fwd, the
+ * only kernel of the other two) and stop right after it, so
+ * hipEventElapsedTime(start, stop) is that kernel's duration.  The events are
+ * only recorded, never created, synchronised or destroyed by the library. */
+void ssm_set_timing_events(void *start, void *stop);
+
 #ifdef __cplusplus
 }
 #endif

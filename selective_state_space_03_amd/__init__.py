@@ -3,10 +3,12 @@ step and multi-head chunked scan, as hand-written HIP kernels behind the C ABI
 of include/ssm_mi355x.h.  This package is the thin Python binding."""
 from .binding import (  # noqa: F401
     EXPORTED,
+    Call,
     LIB_PATH,
     SsmError,
     chunk_scan_fwd,
     decode_step,
     lib,
     scan_fwd,
+    set_timing_events,
 )

@@ -62,7 +62,7 @@ EXPORTED = [
     "ssm_scan_fwd", "ssm_scan_workspace_size", "ssm_scan_check",
     "ssm_decode_step", "ssm_decode_check",
     "ssm_chunk_scan_fwd", "ssm_chunk_scan_workspace_size", "ssm_chunk_scan_check",
-    "ssm_status_string", "ssm_last_error", "ssm_abi_version", "ssm_params_sizeof",
+    "ssm_status_string", "ssm_last_error", "ssm_abi_version", "ssm_params_sizeof", "ssm_set_timing_events",
 ]
 
 _lib = None
@@ -100,6 +100,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_abi_version.restype = _i32
     L.ssm_params_sizeof.argtypes = [_i32]
     L.ssm_params_sizeof.restype = ctypes.c_size_t
+    L.ssm_set_timing_events.argtypes = [_vp, _vp]
+    L.ssm_set_timing_events.restype = None
     for i, st in enumerate((ScanParams, DecodeParams, ChunkParams)):
         if L.ssm_params_sizeof(i) != ctypes.sizeof(st):
             raise RuntimeError(f"ctypes mirror of params struct {i} does not match the library")
@@ -150,6 +152,33 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+class Call:
+    """One marshalled entry-point call.  run() enqueues it (again) on the same
+    stream with the same buffers and returns the output tensor; the tensors
+    the call reads and writes are kept alive here."""
+
+    def __init__(self, fn, params, stream, out, keep):
+        self._fn, self._p, self._stream, self.out, self._keep = fn, params, stream, out, keep
+
+    def run(self):
+        _raise(self._fn(ctypes.byref(self._p), self._stream))
+        return self.out
+
+
+def set_timing_events(start=None, stop=None):
+    """Record two torch.cuda.Event objects around the main kernel of the
+    following entry-point calls on this thread (None, None: stop recording)."""
+    if (start is None) != (stop is None):
+        raise ValueError("give both events or neither")
+    if start is None:
+        lib().ssm_set_timing_events(None, None)
+        return
+    for ev in (start, stop):
+        if not ev.cuda_event:  # torch creates the HIP event at its first record
+            ev.record()
+    lib().ssm_set_timing_events(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event))
+
+
 def _bound(v, default):
     return float(default if v is None else v)
 
@@ -157,8 +186,9 @@ def _bound(v, default):
 def scan_fwd(x, A, B, C, dt, *, D=None, z=None, conv_w=None, conv_b=None, conv_cache_in=None,
              conv_cache_out=None, dt_rank1=False, dt_w=None, dt_bias=None, dt_softplus=True,
              dt_min=None, dt_max=None, ssm_state_in=None, ssm_state_out=None, y=None,
-             y_dtype=None, time_split=0, workspace=None, stream=None):
-    """Full-sequence selective scan (ssm_scan_fwd).  Returns y (batch, L, E)."""
+             y_dtype=None, time_split=0, workspace=None, stream=None, prepare=False):
+    """Full-sequence selective scan (ssm_scan_fwd).  Returns y (batch, L, E), or
+    with prepare=True a Call that enqueues this same call again on each run()."""
     L_ = lib()
     batch, seqlen, dim = x.shape
     dev = x.device
@@ -201,14 +231,17 @@ def scan_fwd(x, A, B, C, dt, *, D=None, z=None, conv_w=None, conv_b=None, conv_c
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     p.workspace = _ptr(workspace, "workspace", device=dev)
     p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _raise(L_.ssm_scan_fwd(ctypes.byref(p), _stream(dev, stream)))
-    return y
+    call = Call(L_.ssm_scan_fwd, p, _stream(dev, stream), y, (x, A, B, C, dt, D, z, conv_w, conv_b, conv_cache_in,
+                                                             conv_cache_out, dt_w, dt_bias, ssm_state_in,
+                                                             ssm_state_out, workspace))
+    return call if prepare else call.run()
 
 
 def decode_step(x, A, B, C, dt, ssm_state, *, conv_cache=None, D=None, z=None, conv_w=None, conv_b=None,
                 dt_rank1=False, dt_w=None, dt_bias=None, dt_softplus=True, dt_min=None, dt_max=None,
-                y=None, y_dtype=None, stream=None):
-    """One decode step (ssm_decode_step): updates ssm_state and conv_cache in place, returns y (batch, E)."""
+                y=None, y_dtype=None, stream=None, prepare=False):
+    """One decode step (ssm_decode_step): updates ssm_state and conv_cache in place, returns y (batch, E)
+    (with prepare=True, a Call that enqueues this same step again on each run())."""
     L_ = lib()
     batch, dim = x.shape
     dev = x.device
@@ -243,14 +276,16 @@ def decode_step(x, A, B, C, dt, ssm_state, *, conv_cache=None, D=None, z=None, c
     p.ssm_state = _ptr(ssm_state, "ssm_state", (batch, dim, d_state), f32, dev)
     p.y = _ptr(y, "y", (batch, dim), device=dev)
     p.y_dtype = _code(y, "y")
-    _raise(L_.ssm_decode_step(ctypes.byref(p), _stream(dev, stream)))
-    return y
+    call = Call(L_.ssm_decode_step, p, _stream(dev, stream), y, (x, A, B, C, dt, ssm_state, conv_cache, D, z,
+                                                                conv_w, conv_b, dt_w, dt_bias))
+    return call if prepare else call.run()
 
 
 def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size=128, D=None, dt_bias=None, dt_softplus=True, dt_min=None,
                    dt_max=None, state_in=None, state_out=None, out=None, out_dtype=None, workspace=None,
-                   stream=None):
-    """Multi-head chunked scan (ssm_chunk_scan_fwd).  Returns out (batch, L, H, P)."""
+                   stream=None, prepare=False):
+    """Multi-head chunked scan (ssm_chunk_scan_fwd).  Returns out (batch, L, H, P), or
+    with prepare=True a Call that enqueues this same call again on each run()."""
     L_ = lib()
     batch, seqlen, nheads, headdim = x.shape
     ngroups, d_state = B.shape[2], B.shape[3]
@@ -285,5 +320,6 @@ def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size=128, D=None, dt_bias=None, dt_s
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     p.workspace = _ptr(workspace, "workspace", device=dev)
     p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _raise(L_.ssm_chunk_scan_fwd(ctypes.byref(p), _stream(dev, stream)))
-    return out
+    call = Call(L_.ssm_chunk_scan_fwd, p, _stream(dev, stream), out, (x, dt, A, B, C, D, dt_bias, state_in,
+                                                                     state_out, workspace))
+    return call if prepare else call.run()

@@ -14,6 +14,7 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local ssm::TimingEvents g_timing;
 
 ssm_status_t fail(ssm_status_t s, const char* fmt, const char* what) {
   char buf[256];
@@ -284,6 +285,10 @@ ssm_status_t hip_status(hipError_t e) {
 
 }  // namespace
 
+namespace ssm {
+TimingEvents timing_events() { return g_timing; }
+}  // namespace ssm
+
 extern "C" {
 
 ssm_status_t ssm_scan_check(const ssm_scan_params_t* p) {
@@ -441,6 +446,11 @@ const char* ssm_status_string(int32_t status) {
 const char* ssm_last_error(void) { return g_last_error.c_str(); }
 
 int32_t ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+void ssm_set_timing_events(void* start, void* stop) {
+  g_timing.start = static_cast<hipEvent_t>(start);
+  g_timing.stop = static_cast<hipEvent_t>(stop);
+}
 
 size_t ssm_params_sizeof(int32_t which) {
   switch (which) {

@@ -86,11 +86,12 @@ template <typename XT, typename YT, typename BT, int DTM>
 hipError_t go(const DecodeLaunch& l, hipStream_t s) {
   const size_t total = static_cast<size_t>(l.k.batch) * l.k.dim;
   const unsigned blocks = static_cast<unsigned>((total + 63) / 64);
-  if (l.conv)
-    hipLaunchKernelGGL((decode_kernel<XT, YT, BT, DTM, true>), dim3(blocks), dim3(256), 0, s, l.k);
-  else
-    hipLaunchKernelGGL((decode_kernel<XT, YT, BT, DTM, false>), dim3(blocks), dim3(256), 0, s, l.k);
-  return hipGetLastError();
+  return timed_launch(s, [&] {
+    if (l.conv)
+      hipLaunchKernelGGL((decode_kernel<XT, YT, BT, DTM, true>), dim3(blocks), dim3(256), 0, s, l.k);
+    else
+      hipLaunchKernelGGL((decode_kernel<XT, YT, BT, DTM, false>), dim3(blocks), dim3(256), 0, s, l.k);
+  });
 }
 
 template <typename XT, typename YT, typename BT>

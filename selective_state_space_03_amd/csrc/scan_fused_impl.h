@@ -406,8 +406,9 @@ hipError_t launch_scan_t(const ScanLaunch& l, hipStream_t stream) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL((scan_kernel<XT, YT, DTM, CONV, GATE, kMain>), dim3(groups * a.nseg), dim3(64), 0, stream, a);
-  return hipGetLastError();
+  return timed_launch(stream, [&] {
+    hipLaunchKernelGGL((scan_kernel<XT, YT, DTM, CONV, GATE, kMain>), dim3(groups * a.nseg), dim3(64), 0, stream, a);
+  });
 }
 
 template <typename XT, typename YT, int DTM, bool CONV>

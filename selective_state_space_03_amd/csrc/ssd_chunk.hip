@@ -333,8 +333,7 @@ hipError_t go(const ChunkLaunch& l, hipStream_t s) {
   const ChunkKernelArgs& k = l.k;
   const unsigned blocks = static_cast<unsigned>(k.batch) * k.nheads * (k.headdim / PT);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((ssd_kernel<OT, PT>), dim3(blocks), dim3(256), 0, s, k);
-  return hipGetLastError();
+  return timed_launch(s, [&] { hipLaunchKernelGGL((ssd_kernel<OT, PT>), dim3(blocks), dim3(256), 0, s, k); });
 }
 
 }  // namespace

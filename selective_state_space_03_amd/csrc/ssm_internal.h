@@ -9,6 +9,28 @@ namespace ssm {
 
 enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
 
+// Caller-supplied HIP events recorded around the main kernel of the next
+// entry-point calls on this thread (null: nothing recorded).
+struct TimingEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+TimingEvents timing_events();
+
+// Launches `launch` on `s` between the timing events, when set.
+template <typename F>
+hipError_t timed_launch(hipStream_t s, F&& launch) {
+  const TimingEvents ev = timing_events();
+  if (ev.start != nullptr) {
+    const hipError_t e = hipEventRecord(ev.start, s);
+    if (e != hipSuccess) return e;
+  }
+  launch();
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess && ev.stop != nullptr) err = hipEventRecord(ev.stop, s);
+  return err;
+}
+
 // ---- fused scan ----------------------------------------------------------
 // B and C are repacked per (batch, t) into one fp32 row [B0..B15, C0..C15] so
 // the scan kernel reads them with wave-uniform scalar loads.
