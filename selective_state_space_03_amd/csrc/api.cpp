@@ -84,18 +84,27 @@ ssm_status_t check_dt_bounds(float lo, float hi) {
 // composition cost a fixed amount per segment), and every segment past the
 // first starts at t >= 4, so only the first reads the conv cache (which the
 // last one may overwrite in place).
+// Segment length for s segments: ceil(L / s) rounded up to whole tiles, so
+// only the last segment of a sequence ends inside a tile.
+int scan_seg_len(int L, int s) {
+  const int seg = (L + s - 1) / s;
+  return (seg + ssm::kScanBlk - 1) / ssm::kScanBlk * ssm::kScanBlk;
+}
+
 int scan_split(const ssm_scan_params_t* p) {
   const int L = p->seqlen;
   int s = p->time_split;
   if (s <= 0) {
     const long groups = static_cast<long>(p->batch) * ((p->dim + 63) / 64);
-    const long slots = 3 * 1024;
+    // enough waves to keep ~6 per SIMD (256 CUs x 4 SIMDs) busy: the extra
+    // summary pass costs less than running the scan at low occupancy
+    const long slots = 6 * 1024;
     s = groups >= slots ? 1 : static_cast<int>(slots / groups);
     s = std::min(s, std::max(1, L / 32));
   }
   s = std::min(std::min(s, ssm::kScanMaxSplit), std::max(1, L / 4));
   if (s <= 1) return 1;
-  const int seg = (L + s - 1) / s;
+  const int seg = scan_seg_len(L, s);
   return (L + seg - 1) / seg;
 }
 
@@ -326,7 +335,7 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_params_t* p, void* stream) {
   k.dim = p->dim;
   k.n_egroups = (p->dim + 63) / 64;
   k.nseg = scan_split(p);
-  k.seg_len = p->seqlen > 0 ? (p->seqlen + k.nseg - 1) / k.nseg : 0;
+  k.seg_len = p->seqlen > 0 ? (k.nseg > 1 ? scan_seg_len(p->seqlen, k.nseg) : p->seqlen) : 0;
   k.summ = k.nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(p->workspace) +
                                                  ssm::scan_summary_offset(p->batch, p->seqlen))
                       : nullptr;

@@ -43,8 +43,10 @@ __global__ void pack_bc_kernel(const BT* __restrict__ B, const BT* __restrict__ 
   out[i] = col < kScanN ? to_f32(B[row * kScanN + col]) : to_f32(C[row * kScanN + col - kScanN]);
 }
 
+// One row more than there are tokens: each step also loads the next step's
+// row, which after the last token is this padding row.
 size_t bc_bytes(int batch, int seqlen) {
-  const size_t rows = static_cast<size_t>(batch) * seqlen;
+  const size_t rows = static_cast<size_t>(batch) * seqlen + 1;
   return (rows * kBcRow * sizeof(float) + 255) & ~static_cast<size_t>(255);
 }
 

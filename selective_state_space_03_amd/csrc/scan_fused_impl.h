@@ -118,46 +118,61 @@ struct Scan {
   using XIO = BufIO<XT>;
   using DIO = BufIO<DT>;
   using YIO = BufIO<YT>;
+  static constexpr bool kWideDt = DTM != 0;                            // dt given per channel
+  static constexpr bool kDtSharesX = kWideDt && DIO::bytes == XIO::bytes;  // same byte offsets as x
 
   const ScanKernelArgs& a;
   const LaneCtx c;
   rsrc_t rx, rz, rdt, ry;
   const cfloat* rows;              // this batch row's packed B/C rows (constant memory)
-  uint32_t vx, vdt, vy;            // per-lane byte offsets of this channel inside a (t, :) row
+  uint32_t vo_x[kBlk];             // per-lane byte offset of step i of a tile (x and z)
+  uint32_t vo_d[kBlk];             // the same for an E-wide dt of another element size
+  uint32_t vy;                     // per-lane byte offset in a y row; out of range for idle lanes
   uint32_t rb_x, rb_dt, rb_y;      // bytes per time step
+  float dt_min, dt_max, sp_lo, sp_hi;
+  float sat_pre;                   // pre-activations at or above this give dt = dt_max
+  bool dt_softplus;
   const float4* al2;               // A[e, n] log2(e) as [n / 4][lane] float4s (LDS)
-  float asat[kScanN];              // exp(dt_max A[e, n]): the decay on the upper clip
 
-  __device__ Scan(const ScanKernelArgs& a_, const LaneCtx& c_, const float4* al2_, const float (&asat_)[kScanN])
+  __device__ Scan(const ScanKernelArgs& a_, const LaneCtx& c_, const float4* al2_)
       : a(a_), c(c_), al2(al2_) {
     const uint32_t L = a.seqlen, E = a.dim;
     const size_t tok0 = static_cast<size_t>(c.b) * L;  // first token of this batch row
+    // each descriptor covers exactly this batch row: loads past its end read 0
     rx = make_rsrc(static_cast<const char*>(a.x) + tok0 * E * XIO::bytes, L * E * XIO::bytes);
     rz = make_rsrc(static_cast<const char*>(a.z ? a.z : a.x) + tok0 * E * XIO::bytes, L * E * XIO::bytes);
     ry = make_rsrc(static_cast<char*>(a.y) + tok0 * E * YIO::bytes, L * E * YIO::bytes);
-    if constexpr (DTM == 0) {
-      rdt = make_rsrc(static_cast<const float*>(a.dt) + tok0, L * 4u);
-      vdt = 0;
-      rb_dt = 4;
-    } else {
-      rdt = make_rsrc(static_cast<const char*>(a.dt) + tok0 * E * DIO::bytes, L * E * DIO::bytes);
-      vdt = static_cast<uint32_t>(c.e) * DIO::bytes;
-      rb_dt = E * DIO::bytes;
-    }
-    rows = (const cfloat*)(a.bc + tok0 * kBcRow);
-    vx = static_cast<uint32_t>(c.e) * XIO::bytes;
-    vy = c.act ? static_cast<uint32_t>(c.e) * YIO::bytes : kOob;
     rb_x = E * XIO::bytes;
     rb_y = E * YIO::bytes;
+    if constexpr (kWideDt) {
+      rdt = make_rsrc(static_cast<const char*>(a.dt) + tok0 * E * DIO::bytes, L * E * DIO::bytes);
+      rb_dt = E * DIO::bytes;
+    } else {
+      // the rank-1 input r[b, t]: every lane loads the same word (a vector
+      // load, so it is prefetched with the tile and waited for in order)
+      rdt = make_rsrc(static_cast<const float*>(a.dt) + tok0, L * 4u);
+      rb_dt = 4;
+    }
+    rows = (const cfloat*)(a.bc + tok0 * kBcRow);
 #pragma unroll
-    for (int n = 0; n < kScanN; ++n) asat[n] = asat_[n];
+    for (int i = 0; i < kBlk; ++i) {
+      vo_x[i] = static_cast<uint32_t>(c.e) * XIO::bytes + i * rb_x;
+      vo_d[i] = (kWideDt ? static_cast<uint32_t>(c.e) * DIO::bytes : 0u) + i * rb_dt;
+    }
+    vy = c.act ? static_cast<uint32_t>(c.e) * YIO::bytes : kOob;
+    dt_min = a.dt_min;
+    dt_max = a.dt_max;
+    sp_lo = a.sp_lo;
+    sp_hi = a.sp_hi;
+    dt_softplus = a.dt_softplus != 0;
+    sat_pre = dt_softplus ? sp_hi : dt_max;
   }
 
   // Raw (pre-conv) input at time p: x when p >= 0, the cache entry K-1+p
   // (oldest first) before the sequence, 0 at a fresh prefill.
   __device__ __forceinline__ float raw_at(int p) const {
     if (p >= a.seqlen) return 0.0f;  // only reachable for an empty segment
-    if (p >= 0) return XIO::f32(XIO::load(rx, vx, static_cast<uint32_t>(p) * rb_x));
+    if (p >= 0) return XIO::f32(XIO::load(rx, vo_x[0], static_cast<uint32_t>(p) * rb_x));
     if (a.conv_cache_in == nullptr) return 0.0f;
     return a.conv_cache_in[(static_cast<size_t>(c.b) * a.dim + c.e) * (kConvK - 1) + (kConvK - 1 + p)];
   }
@@ -168,34 +183,45 @@ struct Scan {
     typename XIO::raw z[kBlk];
   };
 
+  // Loads of steps tb .. tb+kBlk-1.  Steps past the segment are loaded too
+  // (and never used); past the batch row the descriptor returns zeros.
   template <bool FULL>
-  __device__ __forceinline__ void load_block(int tb, int t1, Tile& T) const {
+  __device__ __forceinline__ void load_block(int tb, Tile& T) const {
     constexpr bool has_z = FULL && GATE;
+    const uint32_t sx = static_cast<uint32_t>(tb) * rb_x;
+    const uint32_t sd = static_cast<uint32_t>(tb) * rb_dt;
 #pragma unroll
     for (int i = 0; i < kBlk; ++i) {
-      const uint32_t t = static_cast<uint32_t>(min(tb + i, t1 - 1));
-      T.x[i] = XIO::load(rx, vx, t * rb_x);
-      T.d[i] = DIO::load(rdt, vdt, t * rb_dt);
-      if (has_z) T.z[i] = XIO::load(rz, vx, t * rb_x);
+      T.x[i] = XIO::load(rx, vo_x[i], sx);
+      T.d[i] = DIO::load(rdt, kDtSharesX ? vo_x[i] : vo_d[i], kDtSharesX ? sx : sd);
+      if (has_z) T.z[i] = XIO::load(rz, vo_x[i], sx);
     }
   }
 
   // One step.  FULL: readout, skip, gate, store.  Otherwise state update only
   // and the running sum of dt for the segment's decay product.
-  template <bool POW, bool FULL>
-  __device__ __forceinline__ void step(int t, const Tile& T, int i, float (&h)[kScanN], float (&win)[3],
-                                       float& sdt) const {
-    constexpr bool has_z = FULL && GATE;
-    // the step's B/C row: wave-uniform scalar loads, in flight during the
-    // row-independent work below
+  // The packed B/C row of step t into SGPRs (wave-uniform scalar loads).
+  template <bool FULL>
+  __device__ __forceinline__ void load_row(int t, float (&bv)[kScanN], float (&cv)[kScanN]) const {
     const cfloat* row = rows + static_cast<size_t>(t) * kBcRow;
-    float bv[kScanN], cv[kScanN];
 #pragma unroll
     for (int n = 0; n < kScanN; ++n) bv[n] = row[n];
     if (FULL) {
 #pragma unroll
       for (int n = 0; n < kScanN; ++n) cv[n] = row[kScanN + n];
     }
+  }
+
+  // One step with the B/C row of step t in bv/cv; ends by loading the row of
+  // step t+1 into them, so its latency is covered by the row-independent
+  // work at the start of the next step.  FULL: readout, skip, gate, store.
+  // Otherwise state update only and the running sum of dt for the segment's
+  // decay product.
+  template <bool POW, bool FULL>
+  __device__ __forceinline__ void step(int t, const Tile& T, int i, float (&h)[kScanN], float (&win)[3],
+                                       float& sdt, float (&dA)[kScanN], float (&bv)[kScanN],
+                                       float (&cv)[kScanN]) const {
+    constexpr bool has_z = FULL && GATE;
     float u = XIO::f32(T.x[i]);
     if (CONV) {
       const float xc = fmaf(c.cw0, win[0], fmaf(c.cw1, win[1], fmaf(c.cw2, win[2], fmaf(c.cw3, u, c.cb))));
@@ -204,35 +230,33 @@ struct Scan {
       win[2] = u;
       u = silu(xc);
     }
-    const float pre = (DTM == 0) ? fmaf(c.dtw, DIO::f32(T.d[i]), c.dtb) : DIO::f32(T.d[i]) + c.dtb;
-    // dt = clip(softplus(pre), lo, hi).  Lanes at or beyond the thresholds
-    // take the clip value directly (exact: softplus is increasing); softplus
-    // itself only runs when some lane of the wave is inside the band.
+    const float pre = kWideDt ? DIO::f32(T.d[i]) + c.dtb : fmaf(c.dtw, DIO::f32(T.d[i]), c.dtb);
+    // dt = clip(softplus(pre), lo, hi).  When every lane of the wave is at or
+    // beyond the upper threshold, dt is dt_max everywhere (exact: softplus is
+    // increasing), and the decay factors of the previous step are reused if
+    // they were the dt_max ones too.  Otherwise lanes beyond either threshold
+    // take the clip value, softplus runs only if some lane lies inside the
+    // band, and the decay is recomputed.
     float dt;
-    if (a.dt_softplus) {
-      dt = (pre >= a.sp_hi) ? a.dt_max : a.dt_min;
-      const bool mid = (pre > a.sp_lo) && (pre < a.sp_hi);
+    const bool all_sat = __all(pre >= sat_pre);
+    if (all_sat) {
+      dt = dt_max;
+    } else if (dt_softplus) {
+      dt = (pre >= sp_hi) ? dt_max : dt_min;
+      const bool mid = (pre > sp_lo) && (pre < sp_hi);
       if (__any(mid)) {
         const float sp = softplus(pre);
-        dt = mid ? __builtin_amdgcn_fmed3f(sp, a.dt_min, a.dt_max) : dt;
+        dt = mid ? __builtin_amdgcn_fmed3f(sp, dt_min, dt_max) : dt;
       }
     } else {
-      dt = __builtin_amdgcn_fmed3f(pre, a.dt_min, a.dt_max);
+      dt = __builtin_amdgcn_fmed3f(pre, dt_min, dt_max);
     }
+    decay<POW>(dt, c.al0, al2, dA);
     if (!FULL) sdt += dt;
     const float dtu = dt * u;
     const float gate = has_z ? silu(XIO::f32(T.z[i])) : 1.0f;
-    if (__all(dt == a.dt_max)) {
-      // every lane on the upper clip: exp(dt_max A[e, n]) was computed once,
-      // by the same arithmetic as decay()
 #pragma unroll
-      for (int n = 0; n < kScanN; ++n) h[n] = fmaf(asat[n], h[n], dtu * bv[n]);
-    } else {
-      float dA[kScanN];
-      decay<POW>(dt, c.al0, al2, dA);
-#pragma unroll
-      for (int n = 0; n < kScanN; ++n) h[n] = fmaf(dA[n], h[n], dtu * bv[n]);
-    }
+    for (int n = 0; n < kScanN; ++n) h[n] = fmaf(dA[n], h[n], dtu * bv[n]);
     if (!FULL) {
       // nothing reads the state between steps of the summary pass; pin it
       // here, or the compiler interleaves several steps of the recurrence and
@@ -247,46 +271,61 @@ struct Scan {
       const float yv = fmaf(c.d, u, (acc[0] + acc[1]) + (acc[2] + acc[3])) * gate;
       YIO::store(yv, ry, vy, static_cast<uint32_t>(t) * rb_y);
     }
+    load_row<FULL>(t + 1, bv, cv);
   }
 
-  // Steps [tb, min(tb + kBlk, t1)) with this block's tile T, while the next
-  // block's loads go into N.  The prefetch is issued unconditionally (its
-  // offsets are clamped to the segment) so every block issues the same loads
-  // and the waits before each step only cover that step's own loads.  Two
-  // tiles alternate roles so no register copy ever waits on a load in flight.
+  // The kBlk steps of a full tile.  The scheduling barrier keeps each step's
+  // scalar loads inside the step (hoisted across steps they would need a
+  // second set of SGPRs).
   template <bool POW, bool FULL>
-  __device__ __forceinline__ void block(int tb, int t1, const Tile& T, Tile& N, float (&h)[kScanN],
-                                        float (&win)[3], float& sdt) const {
-    load_block<FULL>(tb + kBlk, t1, N);
-    if (tb + kBlk <= t1) {
+  __device__ __forceinline__ void block(int tb, const Tile& T, float (&h)[kScanN], float (&win)[3],
+                                        float& sdt, float (&dA)[kScanN], float (&bv)[kScanN], float (&cv)[kScanN]) const {
 #pragma unroll
-      for (int i = 0; i < kBlk; ++i) {
-        step<POW, FULL>(tb + i, T, i, h, win, sdt);
-        // each step's scalar loads stay inside the step: hoisted across steps
-        // they would need a second set of SGPRs
-        asm volatile("" ::: "memory");
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kBlk; ++i) {
-        if (tb + i < t1) step<POW, FULL>(tb + i, T, i, h, win, sdt);
-        asm volatile("" ::: "memory");
-      }
+    for (int i = 0; i < kBlk; ++i) {
+      step<POW, FULL>(tb + i, T, i, h, win, sdt, dA, bv, cv);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // Scan steps [t0, t1) from state h.
+  // The steps tb .. t1-1 (fewer than kBlk) of an already loaded tile.
+  template <bool POW, bool FULL>
+  __device__ __forceinline__ void partial(int tb, int t1, const Tile& T, float (&h)[kScanN], float (&win)[3],
+                                          float& sdt, float (&dA)[kScanN], float (&bv)[kScanN], float (&cv)[kScanN]) const {
+#pragma unroll
+    for (int i = 0; i < kBlk - 1; ++i) {
+      if (tb + i < t1) step<POW, FULL>(tb + i, T, i, h, win, sdt, dA, bv, cv);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Scan steps [t0, t1) from state h.  Two tiles alternate: while one is
+  // consumed the next one's loads are in flight, and as the roles swap by
+  // program position no register copy ever waits on a load.
   template <bool POW, bool FULL>
   __device__ __forceinline__ void run(int t0, int t1, float (&h)[kScanN], float (&win)[3], float& sdt) const {
     if (t0 >= t1) return;
-    Tile ta, tb_;
-    load_block<FULL>(t0, t1, ta);
+    const int nfull = (t1 - t0) / kBlk;
+    float dA[kScanN];               // decay factors of the current step
+    float bv[kScanN], cv[kScanN];   // B/C row of the current step
+    load_row<FULL>(t0, bv, cv);
+    Tile A, B;
+    load_block<FULL>(t0, A);
+    int tb = t0;
+    int k = 0;
 #pragma unroll 1
-    for (int tb = t0;; tb += 2 * kBlk) {
-      block<POW, FULL>(tb, t1, ta, tb_, h, win, sdt);
-      if (tb + kBlk >= t1) break;
-      block<POW, FULL>(tb + kBlk, t1, tb_, ta, h, win, sdt);
-      if (tb + 2 * kBlk >= t1) break;
+    for (; k + 2 <= nfull; k += 2) {
+      load_block<FULL>(tb + kBlk, B);
+      block<POW, FULL>(tb, A, h, win, sdt, dA, bv, cv);
+      load_block<FULL>(tb + 2 * kBlk, A);
+      block<POW, FULL>(tb + kBlk, B, h, win, sdt, dA, bv, cv);
+      tb += 2 * kBlk;
+    }
+    if (k < nfull) {
+      load_block<FULL>(tb + kBlk, B);
+      block<POW, FULL>(tb, A, h, win, sdt, dA, bv, cv);
+      partial<POW, FULL>(tb + kBlk, t1, B, h, win, sdt, dA, bv, cv);
+    } else {
+      partial<POW, FULL>(tb, t1, A, h, win, sdt, dA, bv, cv);
     }
   }
 };
@@ -333,11 +372,7 @@ __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
     c.cw0 = c.cw1 = c.cw2 = c.cw3 = c.cb = 0.0f;
   }
   const bool use_pow = __all(prog);
-  // the decay factors on the upper clip, with the arithmetic of the steps
-  float asat[kScanN];
-  if (use_pow) decay<true>(a.dt_max, c.al0, s_al2, asat);
-  else decay<false>(a.dt_max, c.al0, s_al2, asat);
-  const Scan<XT, YT, DTM, CONV, GATE> S(a, c, s_al2, asat);
+  const Scan<XT, YT, DTM, CONV, GATE> S(a, c, s_al2);
   const int t0 = seg * a.seg_len;
   const int t1 = min(t0 + a.seg_len, a.seqlen);
   float win[3] = {0.0f, 0.0f, 0.0f};
