@@ -136,23 +136,34 @@ class KernelTimer:
         return float(np.mean(ts)), float(np.median(ts))
 
 
-def timed_loop(torch, ssm, calls, steps, warmup, per_step=1):
+def timed_loop(torch, ssm, calls, steps, warmup, per_step=1, per_launch=True):
     """Warm up, then run `steps` steps (each `per_step` consecutive calls from the
-    rotating list) between two synchronisations; returns wall ms/step and the
-    mean/median duration of the main kernel per call."""
+    rotating list) between two synchronisations.  Returns wall ms per step and
+    the main kernel's mean and median duration per call: from the HIP events
+    the library records around that kernel (per_launch), or, for entry points
+    that launch nothing else, from two events around the whole timed region
+    divided by the number of calls (back-to-back launches, gaps included)."""
     n = len(calls)
     for i in range(warmup * per_step):
         calls[i % n].run()
     torch.cuda.synchronize()
-    timer = KernelTimer(torch, ssm, steps * per_step)
+    timer = KernelTimer(torch, ssm, steps * per_step) if per_launch else None
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    r0.record()
     for i in range(steps * per_step):
-        timer.arm()
+        if timer:
+            timer.arm()
         calls[i % n].run()
-    timer.disarm()
+    r1.record()
+    if timer:
+        timer.disarm()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    kmean, kmed = timer.mean_ms()
+    if timer:
+        kmean, kmed = timer.mean_ms()
+    else:
+        kmean = kmed = r0.elapsed_time(r1) / (steps * per_step)
     return wall_ms, kmean, kmed
 
 
@@ -183,7 +194,7 @@ def scan_calls(torch, ssm, W, which, sets, device):
     return w, calls, dict(batch=Bt, seq_len=L, dim=E, d_state=N, bytes=ew + small + params + outs)
 
 
-def decode_calls(torch, ssm, W, layers, ring, device):
+def decode_calls(torch, ssm, W, layers, ring, device, stream=None):
     """Config of the batched decode step: batch 64, E 7680, N 16, fp32; `layers`
     independent state/cache sets (like stacked layers, 37 MB each) so the
     states stream from HBM instead of the last-level cache."""
@@ -202,10 +213,41 @@ def decode_calls(torch, ssm, W, layers, ring, device):
             calls.append(ssm.decode_step(X[s], A, Bm[s], Cm[s], R[s], states[l], conv_cache=caches[l], D=D,
                                          z=Z[s], conv_w=cw, dt_rank1=True, dt_w=dw, dt_bias=db,
                                          dt_min=w.opts["dt_min"], dt_max=w.opts["dt_max"], y=ys[l],
-                                         prepare=True))
+                                         stream=stream, prepare=True))
     # per call: state r+w, cache r+w, x, z, y (fp32), r, B, C, parameters
     byts = 2 * 4 * Bt * E * N + 2 * 4 * Bt * E * 3 + 3 * 4 * Bt * E + 4 * Bt * (1 + 2 * N) + 4 * E * (N + 4 + 3)
     return calls, dict(batch=Bt, dim=E, d_state=N, layers=layers, bytes=byts)
+
+
+def decode_graph(torch, ssm, W, device, layers=8, ring=16):
+    """The decode steps of `ring` tokens through `layers` state sets, captured
+    once in a HIP graph (as a serving loop would run them): replays time the
+    kernels without the Python launch cost."""
+    stream = torch.cuda.Stream(device)
+    calls, cfg = decode_calls(torch, ssm, W, layers, ring, device, stream=stream)
+    stream.wait_stream(torch.cuda.current_stream(device))
+    for c in calls:  # warm-up outside the graph
+        c.run()
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for c in calls:
+            c.run()
+    torch.cuda.synchronize()
+    return graph, len(calls), cfg
+
+
+def graph_time(torch, graph, launches, replays):
+    """Mean ms per launch over `replays` graph replays (events around them)."""
+    graph.replay()
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for _ in range(replays):
+        graph.replay()
+    r1.record()
+    torch.cuda.synchronize()
+    return r0.elapsed_time(r1) / (replays * launches)
 
 
 def ssd_calls(torch, ssm, W, device):
@@ -281,11 +323,15 @@ def main():
         torch.cuda.synchronize()
         log(f"copy: {a.steps} x 1 GiB device to device")
         return
-    if a.only in ("decode", "ssd"):
-        calls, cfg = decode_calls(torch, ssm, W, 8, 16, dev) if a.only == "decode" else ssd_calls(torch, ssm, W, dev)
-        per = cfg.get("layers", 1)
-        wall, kmean, _ = timed_loop(torch, ssm, calls, a.steps, a.warmup, per_step=per)
-        log(f"{a.only}: {wall:.3f} ms/step, kernel {kmean * 1e3:.1f} us")
+    if a.only == "decode":
+        graph, launches, cfg = decode_graph(torch, ssm, W, dev)
+        per_call = graph_time(torch, graph, launches, a.steps)
+        log(f"decode: {per_call * 1e3:.2f} us per layer-step ({launches} launches per graph, {a.steps} replays)")
+        return
+    if a.only == "ssd":
+        calls, cfg = ssd_calls(torch, ssm, W, dev)
+        wall, kmean, _ = timed_loop(torch, ssm, calls, a.steps, a.warmup, per_launch=False)
+        log(f"ssd: {wall:.3f} ms/step, kernel {kmean * 1e3:.1f} us")
         return
 
     which = a.only or a.workload
@@ -338,20 +384,20 @@ def main():
         del c2
         torch.cuda.empty_cache()
 
-        log("part: decode step (8 state sets)")
-        c3, cfg3 = decode_calls(torch, ssm, W, 8, 16, dev)
-        wall3, km3, _ = timed_loop(torch, ssm, c3, 64, 4, per_step=cfg3["layers"])
-        per_call = wall3 / cfg3["layers"]
+        log("part: decode step (8 state sets, replayed from a HIP graph)")
+        graph, launches, cfg3 = decode_graph(torch, ssm, W, dev)
+        per_call = graph_time(torch, graph, launches, 8)
         parts["decode_step"] = {
             "tokens_per_s": round(cfg3["batch"] / (per_call * 1e-3), 1), "us_per_step": round(per_call * 1e3, 2),
-            "roofline": roof_hbm(cfg3["bytes"], km3, recorded_traffic("decode")),
+            "roofline": roof_hbm(cfg3["bytes"], per_call, recorded_traffic("decode")),
+            "timing": "HIP graph of 16 tokens x 8 layers, events around 8 replays",
             "config": {k: cfg3[k] for k in ("batch", "dim", "d_state", "layers")}}
-        del c3
+        del graph
         torch.cuda.empty_cache()
 
         log("part: chunked SSD")
         c4, cfg4 = ssd_calls(torch, ssm, W, dev)
-        wall4, km4, _ = timed_loop(torch, ssm, c4, 5, 1)
+        wall4, km4, _ = timed_loop(torch, ssm, c4, 5, 1, per_launch=False)
         r4 = roof_hbm(cfg4["bytes"], km4, recorded_traffic("ssd"))
         r4["mfma_tflops"] = round(cfg4["flops"] / (km4 * 1e-3) / 1e12, 2)
         r4["mfma_frac"] = round(r4["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)

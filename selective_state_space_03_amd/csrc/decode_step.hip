@@ -20,6 +20,21 @@
 namespace ssm {
 namespace {
 
+// The state is read once and written once per step: non-temporal accesses
+// keep it from displacing the parameters (A, conv weights, ...) that every
+// step re-reads from the caches, and measured ~12% faster at batch 64.
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_stream(const float4* p) {
+  const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_stream(float4* p, float4 v) {
+  const v4f w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<v4f*>(p));
+}
+
 template <typename XT, typename YT, typename BT, int DTM, bool CONV>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeKernelArgs a) {
   using DT = typename std::conditional<DTM == 2, bf16s, float>::type;
@@ -32,7 +47,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeKernelArgs a) {
   const int e = static_cast<int>(ch % a.dim);
 
   float4* __restrict__ state4 = reinterpret_cast<float4*>(a.state);
-  const float4 hs = state4[ch * 4 + q];
+  const float4 hs = load_stream(state4 + ch * 4 + q);
   const float4 a4 = reinterpret_cast<const float4*>(a.A)[static_cast<size_t>(e) * 4 + q];
   const float xr = ld<XT>(a.x, ch);
 
@@ -70,7 +85,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeKernelArgs a) {
   acc += __shfl_xor(acc, 2, 4);
 
   if (!act) return;
-  state4[ch * 4 + q] = make_float4(hout[0], hout[1], hout[2], hout[3]);
+  store_stream(state4 + ch * 4 + q, make_float4(hout[0], hout[1], hout[2], hout[3]));
   if (q == 0) {
     float yv = fmaf(a.D ? a.D[e] : 0.0f, u, acc);
     if (a.has_z) yv *= silu(ld<XT>(a.z, ch));
