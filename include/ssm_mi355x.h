@@ -193,7 +193,7 @@ ssm_status_t ssm_decode_check(const ssm_decode_params_t *p);
  *   dA[l] = sum_{i<=l} dt[i] A_h inside each chunk of chunk_size tokens (inclusive);
  *   state passing: S <- e^{dA[Q-1]} S + sum_s e^{dA[Q-1]-dA[s]} dt[s] x[s] (outer) B[s].
  * Requires L % chunk_size == 0 (SSM_ERR_INVALID_ARG otherwise) and x, B, C
- * 16-byte aligned.
+ * and out 16-byte aligned.
  * Supported: x and B/C in bf16, N = 64, P % 16 == 0 and P <= 128, chunk_size = 128.
  * ---------------------------------------------------------------------- */
 typedef struct ssm_chunk_params {

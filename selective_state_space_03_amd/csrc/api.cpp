@@ -252,8 +252,9 @@ ssm_status_t chunk_check(const ssm_chunk_params_t* p) {
     return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "x/bc/out_dtype");
   if (p->x_dtype != SSM_BF16 || p->bc_dtype != SSM_BF16)
     return fail(SSM_ERR_UNSUPPORTED, "%s must be bf16", "x_dtype/bc_dtype");
-  if ((reinterpret_cast<uintptr_t>(p->x) | reinterpret_cast<uintptr_t>(p->B) | reinterpret_cast<uintptr_t>(p->C)) & 15)
-    return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "x/B/C");
+  if ((reinterpret_cast<uintptr_t>(p->x) | reinterpret_cast<uintptr_t>(p->B) | reinterpret_cast<uintptr_t>(p->C) |
+       reinterpret_cast<uintptr_t>(p->out)) & 15)
+    return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "x/B/C/out");
   if (!p->A) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "A");
   ssm_status_t s = check_dt_bounds(p->dt_min, p->dt_max);
   if (s != SSM_OK) return s;

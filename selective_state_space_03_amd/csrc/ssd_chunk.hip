@@ -56,23 +56,42 @@ struct alignas(16) Smem {
   uint16_t B[kQ][kRowN];    // B chunk, row-major [s][n]
   uint16_t Bt[kN][kRowQ];   // B chunk transposed [n][s]
   uint16_t Xt[PT][kRowQ];   // x chunk slice transposed [p][s]
+  uint16_t XWh[PT][kRowQ];  // wS[s] x[s][p], transposed, bf16 high part
+  uint16_t XWl[PT][kRowQ];  //                              bf16 low part
   uint16_t Shi[PT][kRowN];  // state entering the chunk, [p][n], bf16 high part
   uint16_t Slo[PT][kRowN];  //                                   bf16 low part
+  float O[kQ][PT + 4];      // the chunk's output tile, stored to HBM row by row
+  float EL[8][kQ];          // 2^(dA[l] - dA[16 J]) for l >= 16 J
+  float ESD[kQ];            // 2^(dA[16 (s / 16)] - dA[s]) dt[s]
   float dA[kQ];             // inclusive cumsum of dt * A * log2(e)
   float dt[kQ];             // dt after softplus and clip
   float wS[kQ];             // 2^(dA[Q-1] - dA[s]) * dt[s]: state-update weights
   float eA[kQ];             // 2^dA[l]: decay of the incoming state
 };
 
-// Registers holding one chunk's global loads until they are stored to LDS.
+// Workgroup of NW = 4 * (PT / 16) waves.  Loads: C and B as 16-byte pieces,
+// RPT consecutive rows per thread (so B can be written transposed with one
+// LDS store per n); x two rows per thread.
+template <int PT>
+struct Shape {
+  static constexpr int NPT = PT / 16;        // 16-wide subtiles of the headdim slice
+  static constexpr int NW = 4 * NPT;         // waves
+  static constexpr int NT = 64 * NW;         // threads
+  static constexpr int RPT = 1024 / NT;      // rows of C / B per thread (8 pieces per row)
+  static constexpr int XPR = PT / 8;         // x pieces per row
+  static constexpr int XT = 64 * XPR;        // threads loading x (2 rows each)
+};
+
+template <int PT>
 struct ChunkRegs {
-  uint4 c[4], b[4], x[4];
+  uint4 c[Shape<PT>::RPT], b[Shape<PT>::RPT], x[2];
   float dt;
 };
 
 template <typename OT, int PT>
-__global__ __launch_bounds__(256) void ssd_kernel(ChunkKernelArgs a) {
-  constexpr int NPT = PT / 16;  // 16-wide subtiles of the headdim slice
+__global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
+  using Sh = Shape<PT>;
+  constexpr int NPT = Sh::NPT, NW = Sh::NW, NT = Sh::NT, RPT = Sh::RPT, XPR = Sh::XPR;
   __shared__ Smem<PT> sm;
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -91,239 +110,323 @@ __global__ __launch_bounds__(256) void ssd_kernel(ChunkKernelArgs a) {
   const int H = a.nheads, P = a.headdim, G = a.ngroups, L = a.seqlen;
   const float Al2 = a.A[h] * kLog2e;
   const float dtb = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  // The decay between positions s <= l of a chunk is 2^(dA[l] - dA[s]).  It is
+  // factored through the start of s's 16-block, 2^(dA[l] - dA[16 J]) times
+  // 2^(dA[16 J] - dA[s]), two tables shared by the workgroup, when the second
+  // factor cannot overflow: |dt A| log2(e) below 6 per step (the 15 steps of a
+  // block then stay under 2^90).  Otherwise each element takes its own
+  // exponential.
+  const bool factored = a.dt_max * fabsf(Al2) < 6.0f;
 
   const uint16_t* __restrict__ xg = static_cast<const uint16_t*>(a.x);
   const uint16_t* __restrict__ Bg = static_cast<const uint16_t*>(a.B);
   const uint16_t* __restrict__ Cg = static_cast<const uint16_t*>(a.C);
 
-  // load assignment: thread -> 4 consecutive rows x 8 columns (16 bytes)
-  const int rg = tid >> 3, pc = tid & 7;               // C / B: 32 row groups x 8 pieces
-  constexpr int XPC = PT / 8;                          // x pieces per row
-  const int rgx = tid / XPC, pcx = tid % XPC;          // x: 32 row groups x XPC pieces
-  const bool xload = tid < 32 * XPC;
+  const int rg = tid >> 3, pc = tid & 7;            // C / B: row group, 8-column piece
+  const int rgx = tid / XPR, pcx = tid % XPR;       // x: row pair, 8-column piece
+  const bool xload = tid < Sh::XT;
 
-  auto load_chunk = [&](int c, ChunkRegs& R) {
+  auto load_chunk = [&](int c, ChunkRegs<PT>& R) {
     const size_t tok = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t row = tok + 4 * rg + i;
+    for (int i = 0; i < RPT; ++i) {
+      const size_t row = tok + RPT * rg + i;
       R.c[i] = *reinterpret_cast<const uint4*>(Cg + (row * G + g) * kN + 8 * pc);
       R.b[i] = *reinterpret_cast<const uint4*>(Bg + (row * G + g) * kN + 8 * pc);
     }
     if (xload) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const size_t row = tok + 4 * rgx + i;
+      for (int i = 0; i < 2; ++i) {
+        const size_t row = tok + 2 * rgx + i;
         R.x[i] = *reinterpret_cast<const uint4*>(xg + (row * H + h) * P + p0 + 8 * pcx);
       }
     }
     if (tid < kQ) R.dt = a.dt[(tok + tid) * H + h];
   };
 
-  auto store_chunk = [&](const ChunkRegs& R) {
+  // bf16 j of a 16-byte piece
+  auto half = [](const uint4& v, int j) -> uint32_t {
+    return (reinterpret_cast<const uint32_t*>(&v)[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+  };
+
+  auto store_chunk = [&](const ChunkRegs<PT>& R) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(&sm.C[4 * rg + i][8 * pc]) = R.c[i];
-      *reinterpret_cast<uint4*>(&sm.B[4 * rg + i][8 * pc]) = R.b[i];
+    for (int i = 0; i < RPT; ++i) {
+      *reinterpret_cast<uint4*>(&sm.C[RPT * rg + i][8 * pc]) = R.c[i];
+      *reinterpret_cast<uint4*>(&sm.B[RPT * rg + i][8 * pc]) = R.b[i];
     }
-    // B transposed: 4 consecutive s for each of the 8 n of this piece
+    // B transposed: RPT consecutive s for each of the 8 n of this piece
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int sh = (j & 1) * 16;
-      uint32_t lo = ((reinterpret_cast<const uint32_t*>(&R.b[0])[j >> 1] >> sh) & 0xffffu) |
-                    (((reinterpret_cast<const uint32_t*>(&R.b[1])[j >> 1] >> sh) & 0xffffu) << 16);
-      uint32_t hi = ((reinterpret_cast<const uint32_t*>(&R.b[2])[j >> 1] >> sh) & 0xffffu) |
-                    (((reinterpret_cast<const uint32_t*>(&R.b[3])[j >> 1] >> sh) & 0xffffu) << 16);
-      *reinterpret_cast<uint2*>(&sm.Bt[8 * pc + j][4 * rg]) = make_uint2(lo, hi);
+      if constexpr (RPT == 4) {
+        const uint32_t lo = half(R.b[0], j) | (half(R.b[1], j) << 16);
+        const uint32_t hi = half(R.b[2], j) | (half(R.b[3], j) << 16);
+        *reinterpret_cast<uint2*>(&sm.Bt[8 * pc + j][4 * rg]) = make_uint2(lo, hi);
+      } else {
+        *reinterpret_cast<uint32_t*>(&sm.Bt[8 * pc + j][2 * rg]) = half(R.b[0], j) | (half(R.b[1], j) << 16);
+      }
     }
     if (xload) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int sh = (j & 1) * 16;
-        uint32_t lo = ((reinterpret_cast<const uint32_t*>(&R.x[0])[j >> 1] >> sh) & 0xffffu) |
-                      (((reinterpret_cast<const uint32_t*>(&R.x[1])[j >> 1] >> sh) & 0xffffu) << 16);
-        uint32_t hi = ((reinterpret_cast<const uint32_t*>(&R.x[2])[j >> 1] >> sh) & 0xffffu) |
-                      (((reinterpret_cast<const uint32_t*>(&R.x[3])[j >> 1] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<uint2*>(&sm.Xt[8 * pcx + j][4 * rgx]) = make_uint2(lo, hi);
-      }
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint32_t*>(&sm.Xt[8 * pcx + j][2 * rgx]) = half(R.x[0], j) | (half(R.x[1], j) << 16);
     }
     if (tid < kQ) {
       const float pre = R.dt + dtb;
-      const float d = a.dt_softplus ? dt_softplus_clip(pre, a.dt_min, a.dt_max, a.sp_lo, a.sp_hi)
-                                    : __builtin_amdgcn_fmed3f(pre, a.dt_min, a.dt_max);
-      sm.dt[tid] = d;
-      sm.wS[tid] = d * Al2;  // per-step log2 decay, scanned below
+      sm.dt[tid] = a.dt_softplus ? dt_softplus_clip(pre, a.dt_min, a.dt_max, a.sp_lo, a.sp_hi)
+                                 : __builtin_amdgcn_fmed3f(pre, a.dt_min, a.dt_max);
     }
   };
 
-  // state accumulators: wave w owns n in [16w, 16w+16) for every p subtile;
-  // lane holds S[p = 16pt + 4lg + r][n = 16w + li]
-  f32x4 S[NPT];
+  // State block of this wave: n in [16 nb, 16 nb + 16), p in [16 ps, 16 ps + 16);
+  // lane holds S[p = 16 ps + 4 lg + r][n = 16 nb + li].
+  const int nb = w & 3, ps = w >> 2;
+  f32x4 S;
   const size_t sbase = ((static_cast<size_t>(b) * H + h) * P + p0) * kN;
 #pragma unroll
-  for (int pt = 0; pt < NPT; ++pt) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int p = 16 * pt + 4 * lg + r;
-      S[pt][r] = a.state_in ? a.state_in[sbase + static_cast<size_t>(p) * kN + 16 * w + li] : 0.0f;
-    }
+  for (int r = 0; r < 4; ++r) {
+    const int p = 16 * ps + 4 * lg + r;
+    S[r] = a.state_in ? a.state_in[sbase + static_cast<size_t>(p) * kN + 16 * nb + li] : 0.0f;
   }
   auto publish_state = [&]() {
 #pragma unroll
-    for (int pt = 0; pt < NPT; ++pt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = 16 * pt + 4 * lg + r;
-        uint16_t hi, lo;
-        split_bf16(S[pt][r], hi, lo);
-        sm.Shi[p][16 * w + li] = hi;
-        sm.Slo[p][16 * w + li] = lo;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int p = 16 * ps + 4 * lg + r;
+      uint16_t hi, lo;
+      split_bf16(S[r], hi, lo);
+      sm.Shi[p][16 * nb + li] = hi;
+      sm.Slo[p][16 * nb + li] = lo;
     }
   };
   publish_state();
 
-  const float* Dp = a.D;
-  ChunkRegs R;
+  // Output items of this wave: 16-row block I of the chunk and 16-column
+  // subtile pt; (w, 0) and (7 - w, NPT - 1) have 9 causal 16x16 blocks
+  // between them, for every wave.
+  const int I0 = w, I1 = 7 - w;
+  const int pt1 = NPT - 1;
+  float dv0 = 0.0f, dv1 = 0.0f;  // D for the lane's output column of each item
+  if (a.D) {
+    const int pa = p0 + li, pb = p0 + 16 * pt1 + li;
+    dv0 = a.d_per_channel ? a.D[static_cast<size_t>(h) * P + pa] : a.D[h];
+    dv1 = a.d_per_channel ? a.D[static_cast<size_t>(h) * P + pb] : a.D[h];
+  }
+
+  ChunkRegs<PT> R;
   load_chunk(0, R);
   for (int c = 0; c < a.nchunks; ++c) {
-    __syncthreads();  // previous chunk's LDS readers are done
+    __syncthreads();  // the previous chunk's LDS readers are done
     store_chunk(R);
     if (c + 1 < a.nchunks) load_chunk(c + 1, R);
     __syncthreads();
-    if (w == 0) {
-      // inclusive scan of the per-step log2 decays: two steps per lane
-      const float v0 = sm.wS[2 * lane], v1 = sm.wS[2 * lane + 1];
+
+    // Every wave scans the chunk's log2 decays in registers (lane: steps
+    // 2 lane and 2 lane + 1), then writes its share of the tables.
+    {
+      const float2 dt2 = *reinterpret_cast<const float2*>(&sm.dt[2 * lane]);
+      const float v0 = dt2.x * Al2, v1 = dt2.y * Al2;
       float incl = v0 + v1;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const float t = __shfl_up(incl, o);
         if (lane >= o) incl += t;
       }
-      const float excl = incl - (v0 + v1);
-      const float d0 = excl + v0, d1 = incl;
+      const float d0 = incl - v1, d1 = incl;  // dA[2 lane], dA[2 lane + 1]
       const float last = __shfl(incl, 63);
-      sm.dA[2 * lane] = d0;
-      sm.dA[2 * lane + 1] = d1;
-      sm.eA[2 * lane] = exp2_fast(d0);
-      sm.eA[2 * lane + 1] = exp2_fast(d1);
-      sm.wS[2 * lane] = exp2_fast(last - d0) * sm.dt[2 * lane];
-      sm.wS[2 * lane + 1] = exp2_fast(last - d1) * sm.dt[2 * lane + 1];
+      // 16-blocks: wave w fills EL[J] for J = w, w + NW, ...
+#pragma unroll
+      for (int J = w; J < 8; J += NW) {
+        const float ref = __shfl(d0, 8 * J);  // dA[16 J]
+        if (2 * lane >= 16 * J) {
+          sm.EL[J][2 * lane] = exp2_fast(d0 - ref);
+          sm.EL[J][2 * lane + 1] = exp2_fast(d1 - ref);
+        }
+      }
+      if (w == 0) {
+        const float ref = __shfl(d0, 8 * (lane >> 3));  // dA at the start of this lane's 16-block
+        sm.ESD[2 * lane] = exp2_fast(ref - d0) * dt2.x;
+        sm.ESD[2 * lane + 1] = exp2_fast(ref - d1) * dt2.y;
+        sm.dA[2 * lane] = d0;
+        sm.dA[2 * lane + 1] = d1;
+      } else if (w == 1) {
+        sm.eA[2 * lane] = exp2_fast(d0);
+        sm.eA[2 * lane + 1] = exp2_fast(d1);
+        sm.wS[2 * lane] = exp2_fast(last - d0) * dt2.x;
+        sm.wS[2 * lane + 1] = exp2_fast(last - d1) * dt2.y;
+      }
     }
     __syncthreads();
-    const size_t tok0 = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
 
-    // ---- output rows: blocks I = w and 7 - w
-#pragma unroll 1
-    for (int bi = 0; bi < 2; ++bi) {
-      const int I = bi == 0 ? w : 7 - w;
-      const int l_row = 16 * I + li;  // row of cb held by this lane in the M layout
-      const float dAl = sm.dA[l_row];
-      f32x4 acc[NPT];
+    // x weighted for the state update, split into bf16 high and low parts:
+    // XW[p][s] = wS[s] x[s][p] (every thread a few elements)
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) acc[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      for (int J = 0; J <= I; ++J) {
-        f32x4 cbt = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int idx = tid; idx < PT * (kQ / 8); idx += NT) {
+      const int p = idx / (kQ / 8), s0 = 8 * (idx % (kQ / 8));
+      const bf16x8 xr = *reinterpret_cast<const bf16x8*>(&sm.Xt[p][s0]);
+      const float4 w0 = *reinterpret_cast<const float4*>(&sm.wS[s0]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&sm.wS[s0 + 4]);
+      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      bf16x8 hi8, lo8;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sm.B[16 * J + li][32 * kk + 8 * lg]);
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.C[16 * I + li][32 * kk + 8 * lg]);
-          cbt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, cbt, 0, 0, 0);
-        }
-        // cbt[r] = cb[l = 16I + li][s = 16J + 4lg + r]
-        const float4 dAs = *reinterpret_cast<const float4*>(&sm.dA[16 * J + 4 * lg]);
-        const float4 dts = *reinterpret_cast<const float4*>(&sm.dt[16 * J + 4 * lg]);
-        const float dAsv[4] = {dAs.x, dAs.y, dAs.z, dAs.w};
-        const float dtsv[4] = {dts.x, dts.y, dts.z, dts.w};
-        s16x4 mhi, mlo;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s = 16 * J + 4 * lg + r;
-          const float ex = (s <= l_row) ? dAl - dAsv[r] : kNegInf;  // mask before the exponential
-          const float m = cbt[r] * exp2_fast(ex) * dtsv[r];
-          uint16_t hi, lo;
-          split_bf16(m, hi, lo);
-          mhi[r] = static_cast<short>(hi);
-          mlo[r] = static_cast<short>(lo);
-        }
-#pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) {
-          const s16x4 xv = *reinterpret_cast<const s16x4*>(&sm.Xt[16 * pt + li][16 * J + 4 * lg]);
-          acc[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mhi, xv, acc[pt], 0, 0, 0);
-          acc[pt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mlo, xv, acc[pt], 0, 0, 0);
-        }
+      for (int j = 0; j < 8; ++j) {
+        const float v = static_cast<float>(xr[j]) * wv[j];
+        const __bf16 hv = static_cast<__bf16>(v);
+        hi8[j] = hv;
+        lo8[j] = static_cast<__bf16>(v - static_cast<float>(hv));
       }
-      // readout of the incoming state: (C_I S^T)[l][p], scaled by 2^dA[l]
+      *reinterpret_cast<bf16x8*>(&sm.XWh[p][s0]) = hi8;
+      *reinterpret_cast<bf16x8*>(&sm.XWl[p][s0]) = lo8;
+    }
+
+    // Intra-chunk sums of both items: 16x16 blocks J = 0..I of each, walked
+    // together (k-th block of each item in step k) with the LDS operands of
+    // step k + 1 loaded while step k computes.  M = cb . decay . dt, masked
+    // on the diagonal block, split into bf16 high and low parts for the MFMA.
+    struct Ops {
+      float el;     // factored: 2^(dA[l] - dA[16 J]); otherwise dA[l]
+      float4 e4;    // factored: 2^(dA[16 J] - dA[s]) dt[s]; otherwise dA[s]
+      s16x4 xv;     // x[s][p] for the MFMA B operand
+    };
+    auto load_ops = [&](int I, int J, int pt) {
+      Ops o;
+      const int l_row = 16 * I + li, s0 = 16 * J + 4 * lg;
+      o.el = factored ? sm.EL[J][l_row] : sm.dA[l_row];
+      o.e4 = *reinterpret_cast<const float4*>(factored ? &sm.ESD[s0] : &sm.dA[s0]);
+      o.xv = *reinterpret_cast<const s16x4*>(&sm.Xt[16 * pt + li][s0]);
+      return o;
+    };
+    // cb^T block (I, J) from the B rows of block J and the C rows of block I:
+    // cb[r] = cb[l = 16 I + li][s = 16 J + 4 lg + r]
+    auto intra = [&](int I, int J, const bf16x8 (&bj)[2], const bf16x8 (&ci)[2], const Ops& o, f32x4& acc_hi,
+                     f32x4& acc_lo) {
+      f32x4 cb = {0.0f, 0.0f, 0.0f, 0.0f};
+      cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bj[0], ci[0], cb, 0, 0, 0);
+      cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bj[1], ci[1], cb, 0, 0, 0);
+      const int l_row = 16 * I + li;
+      const float ev[4] = {o.e4.x, o.e4.y, o.e4.z, o.e4.w};
+      float dv4[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (!factored) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&sm.dt[16 * J + 4 * lg]);
+        dv4[0] = d4.x; dv4[1] = d4.y; dv4[2] = d4.z; dv4[3] = d4.w;
+      }
+      s16x4 mhi, mlo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float m = factored ? cb[r] * o.el * ev[r] : cb[r] * exp2_fast(o.el - ev[r]) * dv4[r];
+        // causal mask (only the diagonal block has s > l), applied after the
+        // product so a masked overflow never reaches the sum
+        const float mv = (J < I || 16 * J + 4 * lg + r <= l_row) ? m : 0.0f;
+        uint16_t hi, lo;
+        split_bf16(mv, hi, lo);
+        mhi[r] = static_cast<short>(hi);
+        mlo[r] = static_cast<short>(lo);
+      }
+      acc_hi = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mhi, o.xv, acc_hi, 0, 0, 0);
+      acc_lo = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mlo, o.xv, acc_lo, 0, 0, 0);
+    };
+    auto rows16 = [&](const uint16_t (*M)[kRowN], int blk, bf16x8 (&v)[2]) {
+      v[0] = *reinterpret_cast<const bf16x8*>(&M[16 * blk + li][8 * lg]);
+      v[1] = *reinterpret_cast<const bf16x8*>(&M[16 * blk + li][32 + 8 * lg]);
+    };
+    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 a0h = zero4, a0l = zero4, a1h = zero4, a1l = zero4;
+    {
+      bf16x8 c0[2], c1[2], bj[2];
+      rows16(sm.C, I0, c0);
+      rows16(sm.C, I1, c1);
+      rows16(sm.B, 0, bj);
+      Ops o0 = load_ops(I0, 0, 0), o1 = load_ops(I1, 0, pt1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        // block k + 1's operands while block k computes (past an item's
+        // diagonal they are valid LDS, loaded and not used)
+        const int kn = k < 7 ? k + 1 : 7;
+        bf16x8 bn[2];
+        rows16(sm.B, kn, bn);
+        const Ops n0 = load_ops(I0, kn, 0), n1 = load_ops(I1, kn, pt1);
+        if (k <= I0) intra(I0, k, bj, c0, o0, a0h, a0l);
+        if (k <= I1) intra(I1, k, bj, c1, o1, a1h, a1l);
+        bj[0] = bn[0];
+        bj[1] = bn[1];
+        o0 = n0;
+        o1 = n1;
+      }
+    }
+
+    // Readout of the incoming state, (C_I S^T)[l][p] scaled by 2^dA[l], plus
+    // the skip, into the LDS output tile.  Lane holds rows l = 16 I + 4 lg + r
+    // at column p = 16 pt + li.
+    auto finish = [&](const int I, const int pt, const f32x4& acc_hi, const f32x4& acc_lo, const float dv) {
+      f32x4 sr_hi = zero4, sr_lo = zero4;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sm.C[16 * I + li][32 * kk + 8 * lg]);
+        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(&sm.Shi[16 * pt + li][32 * kk + 8 * lg]);
+        const bf16x8 sl = *reinterpret_cast<const bf16x8*>(&sm.Slo[16 * pt + li][32 * kk + 8 * lg]);
+        sr_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, sh, sr_hi, 0, 0, 0);
+        sr_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, sl, sr_lo, 0, 0, 0);
+      }
+      const int p = 16 * pt + li;
       const float4 e4 = *reinterpret_cast<const float4*>(&sm.eA[16 * I + 4 * lg]);
       const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
+      const s16x4 xv = *reinterpret_cast<const s16x4*>(&sm.Xt[p][16 * I + 4 * lg]);
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) {
-        f32x4 sr = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int r = 0; r < 4; ++r) {
+        const float xr = bf16_val(static_cast<uint16_t>(xv[r]));
+        sm.O[16 * I + 4 * lg + r][p] = fmaf(dv, xr, fmaf(ev[r], sr_hi[r] + sr_lo[r], acc_hi[r] + acc_lo[r]));
+      }
+    };
+    finish(I0, 0, a0h, a0l, dv0);
+    finish(I1, pt1, a1h, a1l, dv1);
+    __syncthreads();  // output tile and XW complete; every wave is done reading Shi/Slo
+
+    // ---- the output tile to HBM: whole 16-byte pieces of each row
+    const size_t tok0 = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
+    if constexpr (sizeof(OT) == 4) {
+      constexpr int PPR = PT / 4;  // float4 pieces per row
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sm.C[16 * I + li][32 * kk + 8 * lg]);
-          const bf16x8 sh = *reinterpret_cast<const bf16x8*>(&sm.Shi[16 * pt + li][32 * kk + 8 * lg]);
-          const bf16x8 sl = *reinterpret_cast<const bf16x8*>(&sm.Slo[16 * pt + li][32 * kk + 8 * lg]);
-          sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, sh, sr, 0, 0, 0);
-          sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, sl, sr, 0, 0, 0);
-        }
-        // lane holds rows l = 16I + 4lg + r at column p = 16pt + li
-        const int p = 16 * pt + li;
-        const s16x4 xv = *reinterpret_cast<const s16x4*>(&sm.Xt[p][16 * I + 4 * lg]);
-        const float dv = Dp ? (a.d_per_channel ? Dp[static_cast<size_t>(h) * P + p0 + p] : Dp[h]) : 0.0f;
+      for (int idx = tid; idx < kQ * PPR; idx += NT) {
+        const int l = idx / PPR, q = idx % PPR;
+        const float4 v = *reinterpret_cast<const float4*>(&sm.O[l][4 * q]);
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + ((tok0 + l) * H + h) * P + p0 + 4 * q) = v;
+      }
+    } else {
+      constexpr int PPR = PT / 8;  // 8-value pieces per row
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int l = 16 * I + 4 * lg + r;
-          const float xr = bf16_val(static_cast<uint16_t>(xv[r]));
-          const float yv = fmaf(dv, xr, fmaf(ev[r], sr[r], acc[pt][r]));
-          const size_t o = ((tok0 + l) * H + h) * P + p0 + p;
-          if constexpr (sizeof(OT) == 4) {
-            static_cast<float*>(a.out)[o] = yv;
-          } else {
-            static_cast<uint16_t*>(a.out)[o] = bf16_bits(yv);
-          }
-        }
+      for (int idx = tid; idx < kQ * PPR; idx += NT) {
+        const int l = idx / PPR, q = idx % PPR;
+        const float4 v0 = *reinterpret_cast<const float4*>(&sm.O[l][8 * q]);
+        const float4 v1 = *reinterpret_cast<const float4*>(&sm.O[l][8 * q + 4]);
+        uint4 o;
+        o.x = bf16_bits(v0.x) | (static_cast<uint32_t>(bf16_bits(v0.y)) << 16);
+        o.y = bf16_bits(v0.z) | (static_cast<uint32_t>(bf16_bits(v0.w)) << 16);
+        o.z = bf16_bits(v1.x) | (static_cast<uint32_t>(bf16_bits(v1.y)) << 16);
+        o.w = bf16_bits(v1.z) | (static_cast<uint32_t>(bf16_bits(v1.w)) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + ((tok0 + l) * H + h) * P + p0 + 8 * q) = o;
       }
     }
 
-    __syncthreads();  // every wave is done reading Shi/Slo
-    // ---- state update: S <- 2^dA[Q-1] S + (wS . x)^T B
+    // ---- state update of this wave's block: S <- 2^dA[Q-1] S + XW^T B
     const float dlast = exp2_fast(sm.dA[kQ - 1]);
+    f32x4 acc_hi = S * dlast, acc_lo = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int pt = 0; pt < NPT; ++pt) {
-      f32x4 acc = S[pt] * dlast;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int s0 = 32 * kk + 8 * lg;
-        const bf16x8 xr = *reinterpret_cast<const bf16x8*>(&sm.Xt[16 * pt + li][s0]);
-        const float4 w0 = *reinterpret_cast<const float4*>(&sm.wS[s0]);
-        const float4 w1 = *reinterpret_cast<const float4*>(&sm.wS[s0 + 4]);
-        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        bf16x8 hi8, lo8;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float v = static_cast<float>(xr[j]) * wv[j];
-          const __bf16 hv = static_cast<__bf16>(v);
-          hi8[j] = hv;
-          lo8[j] = static_cast<__bf16>(v - static_cast<float>(hv));
-        }
-        const bf16x8 bt = *reinterpret_cast<const bf16x8*>(&sm.Bt[16 * w + li][s0]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi8, bt, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo8, bt, acc, 0, 0, 0);
-      }
-      S[pt] = acc;
+    for (int kk = 0; kk < 4; ++kk) {
+      const int s0 = 32 * kk + 8 * lg;
+      const bf16x8 xh = *reinterpret_cast<const bf16x8*>(&sm.XWh[16 * ps + li][s0]);
+      const bf16x8 xl = *reinterpret_cast<const bf16x8*>(&sm.XWl[16 * ps + li][s0]);
+      const bf16x8 bt = *reinterpret_cast<const bf16x8*>(&sm.Bt[16 * nb + li][s0]);
+      acc_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bt, acc_hi, 0, 0, 0);
+      acc_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bt, acc_lo, 0, 0, 0);
     }
+    S = acc_hi + acc_lo;
     publish_state();
   }
 
   if (a.state_out) {
 #pragma unroll
-    for (int pt = 0; pt < NPT; ++pt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = 16 * pt + 4 * lg + r;
-        a.state_out[sbase + static_cast<size_t>(p) * kN + 16 * w + li] = S[pt][r];
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int p = 16 * ps + 4 * lg + r;
+      a.state_out[sbase + static_cast<size_t>(p) * kN + 16 * nb + li] = S[r];
     }
   }
 }
@@ -333,7 +436,9 @@ hipError_t go(const ChunkLaunch& l, hipStream_t s) {
   const ChunkKernelArgs& k = l.k;
   const unsigned blocks = static_cast<unsigned>(k.batch) * k.nheads * (k.headdim / PT);
   if (blocks == 0) return hipSuccess;
-  return timed_launch(s, [&] { hipLaunchKernelGGL((ssd_kernel<OT, PT>), dim3(blocks), dim3(256), 0, s, k); });
+  return timed_launch(s, [&] {
+    hipLaunchKernelGGL((ssd_kernel<OT, PT>), dim3(blocks), dim3(Shape<PT>::NT), 0, s, k);
+  });
 }
 
 }  // namespace
