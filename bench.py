@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=("prefill", "bulk"), default="prefill")
+    ap.add_argument("--split", type=int, default=0,
+                    help="time segments per sequence for the scan (0: the library's choice)")
     ap.add_argument("--no-parts", action="store_true", help="skip the decode / SSD / other-scan lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--only", choices=("prefill", "bulk", "decode", "ssd", "copy"), default=None,
@@ -169,7 +171,7 @@ def timed_loop(torch, ssm, calls, steps, warmup, per_step=1, per_launch=True):
 
 # ------------------------------------------------------------------- workloads
 
-def scan_calls(torch, ssm, W, which, sets, device):
+def scan_calls(torch, ssm, W, which, sets, device, stream=None, split=0):
     w = W.scan_prefill() if which == "prefill" else W.scan_bulk()
     o, d = w.opts, w.dims
     calls = []
@@ -183,7 +185,7 @@ def scan_calls(torch, ssm, W, which, sets, device):
             conv_w=dev_tensor(torch, w, "conv_w", device) if o["conv"] else None, conv_cache_out=cc,
             dt_rank1=o["dt_rank1"], dt_w=dev_tensor(torch, w, "dt_w", device),
             dt_bias=dev_tensor(torch, w, "dt_bias", device), dt_softplus=o["dt_softplus"],
-            dt_min=o["dt_min"], dt_max=o["dt_max"], ssm_state_out=st, y=y, prepare=True))
+            dt_min=o["dt_min"], dt_max=o["dt_max"], ssm_state_out=st, y=y, stream=stream, time_split=split, prepare=True))
     Bt, L, E, N = d["batch"], d["seqlen"], d["dim"], d["d_state"]
     # algorithmic bytes: x/u, z (and E-wide dt) in, y out (bf16); B, C (bf16)
     # and the rank-1 r; per-channel parameters; state (and conv cache) out.
@@ -235,6 +237,37 @@ def decode_graph(torch, ssm, W, device, layers=8, ring=16):
             c.run()
     torch.cuda.synchronize()
     return graph, len(calls), cfg
+
+
+def capture_each(torch, calls, stream):
+    """One HIP graph per prepared call (all on `stream`), captured after a
+    warm-up run of each call."""
+    stream.wait_stream(torch.cuda.current_stream())
+    for c in calls:
+        c.run()
+    stream.synchronize()
+    graphs = []
+    for c in calls:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            c.run()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def timed_graphs(torch, graphs, steps, warmup):
+    """Warm up, then replay exactly `steps` graphs (round robin over the buffer
+    sets) between two synchronisations; returns wall ms per step."""
+    n = len(graphs)
+    for i in range(warmup):
+        graphs[i % n].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % n].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
 
 
 def graph_time(torch, graph, launches, replays):
@@ -338,9 +371,17 @@ def main():
     # rotate buffer sets so the working set exceeds the 256 MB last-level cache
     sets = 4 if which == "prefill" else 1
     log(f"generating the {which} workload ({sets} buffer set(s))")
-    w, calls, cfg = scan_calls(torch, ssm, W, which, sets, dev)
-    wall, kmean, kmed = timed_loop(torch, ssm, calls, a.steps, a.warmup)
-    log(f"{which}: {wall:.3f} ms/step, main kernel mean {kmean * 1e3:.1f} us median {kmed * 1e3:.1f} us")
+    stream = torch.cuda.Stream(dev)
+    w, calls, cfg = scan_calls(torch, ssm, W, which, sets, dev, stream=stream, split=a.split)
+    with torch.cuda.stream(stream):
+        eager, kmean, kmed = timed_loop(torch, ssm, calls, a.steps, a.warmup)
+    # the timed steps: each call's launches replayed from a HIP graph, as a
+    # serving or training loop runs them (no Python between the kernels)
+    graphs = capture_each(torch, calls, stream)
+    wall = timed_graphs(torch, graphs, a.steps, a.warmup)
+    log(f"{which}: {wall:.3f} ms/step (graph replay), {eager:.3f} ms/step eager, main kernel mean "
+        f"{kmean * 1e3:.1f} us median {kmed * 1e3:.1f} us")
+    del graphs
     if a.only:
         return
     tokens = cfg["batch"] * cfg["seq_len"]
@@ -356,6 +397,9 @@ def main():
         "config": {"workload": ("Bit-Axon SSM layer prefill" if which == "prefill" else "bulk selective scan"),
                    "batch": cfg["batch"], "seq_len": cfg["seq_len"], "dim": cfg["dim"], "d_state": cfg["d_state"],
                    "storage": "bf16 in/out, fp32 state", "buffer_sets": sets},
+        "timing": "each step one ssm_scan_fwd call replayed from a HIP graph; eager_ms_per_step launches it "
+                  "from Python",
+        "eager_ms_per_step": round(eager, 4),
         "hbm_gbps": round(cfg["bytes"] / (wall * 1e-3) / 1e9, 1),
         "hbm_frac": round(cfg["bytes"] / (wall * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "channel_steps_per_s": round(ch_steps / (wall * 1e-3), 1),

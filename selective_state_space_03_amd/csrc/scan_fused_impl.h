@@ -25,9 +25,10 @@
 // every value through the LDS return path, which then limits the loop).
 //
 // Time split (nseg > 1): launch 1 reduces segments 0..nseg-2 to their
-// summaries (segment 0 from the true initial state, the others from zero);
-// launch 2 composes them into every segment's incoming state and runs all
-// segments in full.  Summaries travel through the workspace.
+// summaries (segment 0 from the true initial state, the others from zero), a
+// small launch composes them in order into every segment's incoming state
+// (scan_fused.hip), and launch 3 runs all segments in full.  Summaries travel
+// through the workspace.
 #include <type_traits>
 
 #include "ssm_device.h"
@@ -198,30 +199,30 @@ struct Scan {
     }
   }
 
-  // One step.  FULL: readout, skip, gate, store.  Otherwise state update only
-  // and the running sum of dt for the segment's decay product.
-  // The packed B/C row of step t into SGPRs (wave-uniform scalar loads).
-  template <bool FULL>
-  __device__ __forceinline__ void load_row(int t, float (&bv)[kScanN], float (&cv)[kScanN]) const {
+  // B_t (the first half of the packed row of step t) into SGPRs: wave-uniform
+  // scalar loads.
+  __device__ __forceinline__ void load_b(int t, float (&bv)[kScanN]) const {
     const cfloat* row = rows + static_cast<size_t>(t) * kBcRow;
 #pragma unroll
     for (int n = 0; n < kScanN; ++n) bv[n] = row[n];
+  }
+
+  // One step with B_t in bv.  C_t is loaded at the start of the step (it is
+  // first needed by the readout at its end), B_{t+1} after the readout, so
+  // its latency is covered by the row-independent work at the start of the
+  // next step and at most one row of each is held in SGPRs.  FULL: readout,
+  // skip, gate, store.  Otherwise state update only and the running sum of
+  // dt for the segment's decay product.
+  template <bool POW, bool FULL>
+  __device__ __forceinline__ void step(int t, const Tile& T, int i, float (&h)[kScanN], float (&win)[3],
+                                       float& sdt, const float (&asat)[kScanN], float (&bv)[kScanN]) const {
+    constexpr bool has_z = FULL && GATE;
+    float cv[kScanN];
     if (FULL) {
+      const cfloat* row = rows + static_cast<size_t>(t) * kBcRow;
 #pragma unroll
       for (int n = 0; n < kScanN; ++n) cv[n] = row[kScanN + n];
     }
-  }
-
-  // One step with the B/C row of step t in bv/cv; ends by loading the row of
-  // step t+1 into them, so its latency is covered by the row-independent
-  // work at the start of the next step.  FULL: readout, skip, gate, store.
-  // Otherwise state update only and the running sum of dt for the segment's
-  // decay product.
-  template <bool POW, bool FULL>
-  __device__ __forceinline__ void step(int t, const Tile& T, int i, float (&h)[kScanN], float (&win)[3],
-                                       float& sdt, float (&dA)[kScanN], float (&bv)[kScanN],
-                                       float (&cv)[kScanN]) const {
-    constexpr bool has_z = FULL && GATE;
     float u = XIO::f32(T.x[i]);
     if (CONV) {
       const float xc = fmaf(c.cw0, win[0], fmaf(c.cw1, win[1], fmaf(c.cw2, win[2], fmaf(c.cw3, u, c.cb))));
@@ -233,30 +234,40 @@ struct Scan {
     const float pre = kWideDt ? DIO::f32(T.d[i]) + c.dtb : fmaf(c.dtw, DIO::f32(T.d[i]), c.dtb);
     // dt = clip(softplus(pre), lo, hi).  When every lane of the wave is at or
     // beyond the upper threshold, dt is dt_max everywhere (exact: softplus is
-    // increasing), and the decay factors of the previous step are reused if
-    // they were the dt_max ones too.  Otherwise lanes beyond either threshold
-    // take the clip value, softplus runs only if some lane lies inside the
-    // band, and the decay is recomputed.
-    float dt;
-    const bool all_sat = __all(pre >= sat_pre);
-    if (all_sat) {
-      dt = dt_max;
-    } else if (dt_softplus) {
-      dt = (pre >= sp_hi) ? dt_max : dt_min;
-      const bool mid = (pre > sp_lo) && (pre < sp_hi);
-      if (__any(mid)) {
-        const float sp = softplus(pre);
-        dt = mid ? __builtin_amdgcn_fmed3f(sp, dt_min, dt_max) : dt;
-      }
-    } else {
-      dt = __builtin_amdgcn_fmed3f(pre, dt_min, dt_max);
-    }
-    decay<POW>(dt, c.al0, al2, dA);
-    if (!FULL) sdt += dt;
-    const float dtu = dt * u;
+    // increasing) and the decay factors are the per-segment exp(dt_max A).
+    // Otherwise lanes beyond either threshold take the clip value, softplus
+    // runs only if some lane lies inside the band, and the decay factors are
+    // computed for the step.  Both branches update h in place
+    // (h = (a h) + dt u B).
     const float gate = has_z ? silu(XIO::f32(T.z[i])) : 1.0f;
+    if (__all(pre >= sat_pre)) {
+      if (!FULL) sdt += dt_max;
+      const float dtu = dt_max * u;
 #pragma unroll
-    for (int n = 0; n < kScanN; ++n) h[n] = fmaf(dA[n], h[n], dtu * bv[n]);
+      for (int n = 0; n < kScanN; ++n) h[n] = fmaf(dtu, bv[n], asat[n] * h[n]);
+    } else {
+      float dt;
+      if (dt_softplus) {
+        dt = (pre >= sp_hi) ? dt_max : dt_min;
+        const bool mid = (pre > sp_lo) && (pre < sp_hi);
+        if (__any(mid)) {
+          const float sp = softplus(pre);
+          dt = mid ? __builtin_amdgcn_fmed3f(sp, dt_min, dt_max) : dt;
+        }
+      } else {
+        dt = __builtin_amdgcn_fmed3f(pre, dt_min, dt_max);
+      }
+      if (!FULL) sdt += dt;
+      const float dtu = dt * u;
+      float dA[kScanN];
+      decay<POW>(dt, c.al0, al2, dA);
+#pragma unroll
+      for (int n = 0; n < kScanN; ++n) h[n] = fmaf(dtu, bv[n], dA[n] * h[n]);
+      // keeps this update in its branch (merged with the other one, the decay
+      // factors would be copied into common registers every step)
+#pragma unroll
+      for (int n = 0; n < kScanN; ++n) asm volatile("" : "+v"(h[n]));
+    }
     if (!FULL) {
       // nothing reads the state between steps of the summary pass; pin it
       // here, or the compiler interleaves several steps of the recurrence and
@@ -271,7 +282,7 @@ struct Scan {
       const float yv = fmaf(c.d, u, (acc[0] + acc[1]) + (acc[2] + acc[3])) * gate;
       YIO::store(yv, ry, vy, static_cast<uint32_t>(t) * rb_y);
     }
-    load_row<FULL>(t + 1, bv, cv);
+    load_b(t + 1, bv);
   }
 
   // The kBlk steps of a full tile.  The scheduling barrier keeps each step's
@@ -279,10 +290,10 @@ struct Scan {
   // second set of SGPRs).
   template <bool POW, bool FULL>
   __device__ __forceinline__ void block(int tb, const Tile& T, float (&h)[kScanN], float (&win)[3],
-                                        float& sdt, float (&dA)[kScanN], float (&bv)[kScanN], float (&cv)[kScanN]) const {
+                                        float& sdt, const float (&asat)[kScanN], float (&bv)[kScanN]) const {
 #pragma unroll
     for (int i = 0; i < kBlk; ++i) {
-      step<POW, FULL>(tb + i, T, i, h, win, sdt, dA, bv, cv);
+      step<POW, FULL>(tb + i, T, i, h, win, sdt, asat, bv);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -290,10 +301,10 @@ struct Scan {
   // The steps tb .. t1-1 (fewer than kBlk) of an already loaded tile.
   template <bool POW, bool FULL>
   __device__ __forceinline__ void partial(int tb, int t1, const Tile& T, float (&h)[kScanN], float (&win)[3],
-                                          float& sdt, float (&dA)[kScanN], float (&bv)[kScanN], float (&cv)[kScanN]) const {
+                                          float& sdt, const float (&asat)[kScanN], float (&bv)[kScanN]) const {
 #pragma unroll
     for (int i = 0; i < kBlk - 1; ++i) {
-      if (tb + i < t1) step<POW, FULL>(tb + i, T, i, h, win, sdt, dA, bv, cv);
+      if (tb + i < t1) step<POW, FULL>(tb + i, T, i, h, win, sdt, asat, bv);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -305,9 +316,10 @@ struct Scan {
   __device__ __forceinline__ void run(int t0, int t1, float (&h)[kScanN], float (&win)[3], float& sdt) const {
     if (t0 >= t1) return;
     const int nfull = (t1 - t0) / kBlk;
-    float dA[kScanN];               // decay factors of the current step
-    float bv[kScanN], cv[kScanN];   // B/C row of the current step
-    load_row<FULL>(t0, bv, cv);
+    float asat[kScanN];             // exp(dt_max A[e, n]): the decay on the upper clip
+    decay<POW>(dt_max, c.al0, al2, asat);
+    float bv[kScanN];               // B of the current step
+    load_b(t0, bv);
     Tile A, B;
     load_block<FULL>(t0, A);
     int tb = t0;
@@ -315,17 +327,17 @@ struct Scan {
 #pragma unroll 1
     for (; k + 2 <= nfull; k += 2) {
       load_block<FULL>(tb + kBlk, B);
-      block<POW, FULL>(tb, A, h, win, sdt, dA, bv, cv);
+      block<POW, FULL>(tb, A, h, win, sdt, asat, bv);
       load_block<FULL>(tb + 2 * kBlk, A);
-      block<POW, FULL>(tb + kBlk, B, h, win, sdt, dA, bv, cv);
+      block<POW, FULL>(tb + kBlk, B, h, win, sdt, asat, bv);
       tb += 2 * kBlk;
     }
     if (k < nfull) {
       load_block<FULL>(tb + kBlk, B);
-      block<POW, FULL>(tb, A, h, win, sdt, dA, bv, cv);
-      partial<POW, FULL>(tb + kBlk, t1, B, h, win, sdt, dA, bv, cv);
+      block<POW, FULL>(tb, A, h, win, sdt, asat, bv);
+      partial<POW, FULL>(tb + kBlk, t1, B, h, win, sdt, asat, bv);
     } else {
-      partial<POW, FULL>(tb, t1, A, h, win, sdt, dA, bv, cv);
+      partial<POW, FULL>(tb, t1, A, h, win, sdt, asat, bv);
     }
   }
 };
@@ -388,16 +400,11 @@ __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
   float* summ = a.summ + (static_cast<size_t>(c.b) * a.n_egroups + g) * (a.nseg - 1) * (kScanN + 1) * 64;
 
   if (MODE == kMain && seg > 0) {
-    // state entering this segment: segment 0's end state, then the summaries
-    // of segments 1..seg-1 applied in order: h <- exp(A sum dt) h + h_end
+    // state entering this segment, left in slot seg-1 by the composition of
+    // the summaries (scan_compose_kernel)
+    const float* sin = summ + static_cast<size_t>(seg - 1) * (kScanN + 1) * 64;
 #pragma unroll
-    for (int n = 0; n < kScanN; ++n) h[n] = summ[n * 64 + lane];
-    for (int j = 1; j < seg; ++j) {
-      const float* sj = summ + static_cast<size_t>(j) * (kScanN + 1) * 64;
-      const float sd = sj[kScanN * 64 + lane];
-#pragma unroll
-      for (int n = 0; n < kScanN; ++n) h[n] = fmaf(exp2_fast(al2v[n] * sd), h[n], sj[n * 64 + lane]);
-    }
+    for (int n = 0; n < kScanN; ++n) h[n] = sin[n * 64 + lane];
   } else {
 #pragma unroll
     for (int n = 0; n < kScanN; ++n) h[n] = (seg == 0 && a.state_in) ? a.state_in[sbase + n] : 0.0f;
@@ -438,7 +445,9 @@ hipError_t launch_scan_t(const ScanLaunch& l, hipStream_t stream) {
   if (a.nseg > 1) {
     hipLaunchKernelGGL((scan_kernel<XT, YT, DTM, CONV, GATE, kPass1>), dim3(groups * (a.nseg - 1)), dim3(64), 0,
                        stream, a);
-    const hipError_t err = hipGetLastError();
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    err = launch_scan_compose(a, stream);
     if (err != hipSuccess) return err;
   }
   return timed_launch(stream, [&] {

@@ -74,6 +74,9 @@ struct ScanLaunch {
 
 struct bf16s;
 size_t scan_workspace_bytes(int batch, int seqlen, int dim, int nseg);
+// Turns the segment summaries into the state entering each segment, in place
+// (slot k then holds the state entering segment k+1).
+hipError_t launch_scan_compose(const ScanKernelArgs& a, hipStream_t stream);
 template <typename XT, typename YT>
 hipError_t launch_scan_xy(const ScanLaunch& l, hipStream_t stream);
 size_t scan_summary_offset(int batch, int seqlen);
