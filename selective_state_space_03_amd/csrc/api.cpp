@@ -78,12 +78,14 @@ ssm_status_t check_dt_bounds(float lo, float hi) {
 
 // Number of time segments.  A wave issues at most about one VALU instruction
 // every 9 cycles on its own and needs 2-3 companions on its SIMD to keep the
-// VALU busy; the kernels hold 3 waves per SIMD (256 CUs x 4 SIMDs), so the
-// split makes batch * channel groups * segments fill those 3072 slots in one
-// round.  Segments keep at least 32 steps (the summary pass and the
-// composition cost a fixed amount per segment), and every segment past the
-// first starts at t >= 4, so only the first reads the conv cache (which the
-// last one may overwrite in place).
+// VALU busy, so the split makes batch * channel groups * segments as large as
+// the device holds at once for the full-segment kernel (its resident
+// workgroups per CU from the occupancy calculator, times the CUs: 3 x 1024 on
+// MI355X at the kernels' register use), and no larger: one more segment past
+// that runs as a second, mostly idle round.  Segments keep at least 32 steps
+// (the summary pass and the composition cost a fixed amount per segment), and
+// every segment past the first starts at t >= 4, so only the first reads the
+// conv cache (which the last one may overwrite in place).
 // Segment length for s segments: ceil(L / s) rounded up to whole tiles, so
 // only the last segment of a sequence ends inside a tile.
 int scan_seg_len(int L, int s) {
@@ -91,14 +93,25 @@ int scan_seg_len(int L, int s) {
   return (seg + ssm::kScanBlk - 1) / ssm::kScanBlk * ssm::kScanBlk;
 }
 
+// The kernel variant a call selects (what the occupancy depends on).
+ssm::ScanLaunch scan_variant(const ssm_scan_params_t* p) {
+  ssm::ScanLaunch l{};
+  l.x_dtype = p->x_dtype;
+  l.y_dtype = p->y_dtype;
+  l.bc_dtype = p->bc_dtype;
+  l.dt_mode = p->dt_rank1 ? 0 : (p->dt_dtype == SSM_BF16 ? 2 : 1);
+  l.conv = p->conv_w != nullptr;
+  l.k.has_z = p->z ? 1 : 0;
+  return l;
+}
+
 int scan_split(const ssm_scan_params_t* p) {
   const int L = p->seqlen;
   int s = p->time_split;
   if (s <= 0) {
     const long groups = static_cast<long>(p->batch) * ((p->dim + 63) / 64);
-    // enough waves to keep ~6 per SIMD (256 CUs x 4 SIMDs) busy: the extra
-    // summary pass costs less than running the scan at low occupancy
-    const long slots = 6 * 1024;
+    long slots = ssm::scan_resident_waves(scan_variant(p));
+    if (slots <= 0) slots = 3 * 1024;  // no device to ask: MI355X at 3 waves per SIMD
     s = groups >= slots ? 1 : static_cast<int>(slots / groups);
     s = std::min(s, std::max(1, L / 32));
   }
@@ -345,11 +358,12 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_params_t* p, void* stream) {
   softplus_thresholds(p->dt_min, p->dt_max, &k.sp_lo, &k.sp_hi);
   k.dt_softplus = p->dt_softplus ? 1 : 0;
   k.has_z = p->z ? 1 : 0;
-  l.x_dtype = p->x_dtype;
-  l.y_dtype = p->y_dtype;
-  l.bc_dtype = p->bc_dtype;
-  l.dt_mode = p->dt_rank1 ? 0 : (p->dt_dtype == SSM_BF16 ? 2 : 1);
-  l.conv = p->conv_w != nullptr;
+  const ssm::ScanLaunch v = scan_variant(p);
+  l.x_dtype = v.x_dtype;
+  l.y_dtype = v.y_dtype;
+  l.bc_dtype = v.bc_dtype;
+  l.dt_mode = v.dt_mode;
+  l.conv = v.conv;
   l.B = p->B;
   l.C = p->C;
   l.bc_out = static_cast<float*>(p->workspace);

@@ -101,6 +101,24 @@ size_t scan_workspace_bytes(int batch, int seqlen, int dim, int nseg) {
 
 size_t scan_summary_offset(int batch, int seqlen) { return bc_bytes(batch, seqlen); }
 
+long scan_resident_waves(const ScanLaunch& l) {
+  // CU count per device, asked once (no runtime query inside stream capture)
+  static int cu_count[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int cus = __atomic_load_n(&cu_count[dev], __ATOMIC_RELAXED);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+    __atomic_store_n(&cu_count[dev], cus, __ATOMIC_RELAXED);
+  }
+  int per_cu;
+  if (l.x_dtype == kBF16)
+    per_cu = l.y_dtype == kBF16 ? scan_occupancy_xy<bf16s, bf16s>(l) : scan_occupancy_xy<bf16s, float>(l);
+  else
+    per_cu = l.y_dtype == kBF16 ? scan_occupancy_xy<float, bf16s>(l) : scan_occupancy_xy<float, float>(l);
+  return static_cast<long>(cus) * per_cu;
+}
+
 hipError_t launch_scan(const ScanLaunch& l, hipStream_t stream) {
   const size_t rows = static_cast<size_t>(l.k.batch) * l.k.seqlen;
   if (rows > 0) {

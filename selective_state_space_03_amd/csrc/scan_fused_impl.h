@@ -474,12 +474,46 @@ hipError_t pick_dt(const ScanLaunch& l, hipStream_t s) {
   }
 }
 
+// Resident workgroups (one wave each) per CU of the full-segment kernel of a
+// variant, from the runtime's occupancy calculator; cached per variant.
+template <typename XT, typename YT, int DTM, bool CONV, bool GATE>
+int occupancy_t() {
+  static int cached = 0;
+  int n = __atomic_load_n(&cached, __ATOMIC_RELAXED);
+  if (n > 0) return n;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_kernel<XT, YT, DTM, CONV, GATE, kMain>, 64, 0) !=
+          hipSuccess ||
+      n <= 0)
+    return 0;
+  __atomic_store_n(&cached, n, __ATOMIC_RELAXED);
+  return n;
+}
+
+template <typename XT, typename YT, int DTM, bool CONV>
+int occ_gate(const ScanLaunch& l) {
+  return l.k.has_z ? occupancy_t<XT, YT, DTM, CONV, true>() : occupancy_t<XT, YT, DTM, CONV, false>();
+}
+
+template <typename XT, typename YT, int DTM>
+int occ_conv(const ScanLaunch& l) {
+  return l.conv ? occ_gate<XT, YT, DTM, true>(l) : occ_gate<XT, YT, DTM, false>(l);
+}
+
 }  // namespace
 
 // Launch for one (x dtype, y dtype) pair; defined in scan_xy_*.hip.
 template <>
 hipError_t launch_scan_xy<SSM_SCAN_XT, SSM_SCAN_YT>(const ScanLaunch& l, hipStream_t stream) {
   return pick_dt<SSM_SCAN_XT, SSM_SCAN_YT>(l, stream);
+}
+
+template <>
+int scan_occupancy_xy<SSM_SCAN_XT, SSM_SCAN_YT>(const ScanLaunch& l) {
+  switch (l.dt_mode) {
+    case 0: return occ_conv<SSM_SCAN_XT, SSM_SCAN_YT, 0>(l);
+    case 1: return occ_conv<SSM_SCAN_XT, SSM_SCAN_YT, 1>(l);
+    default: return occ_conv<SSM_SCAN_XT, SSM_SCAN_YT, 2>(l);
+  }
 }
 
 }  // namespace ssm

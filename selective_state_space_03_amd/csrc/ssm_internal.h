@@ -79,6 +79,11 @@ size_t scan_workspace_bytes(int batch, int seqlen, int dim, int nseg);
 hipError_t launch_scan_compose(const ScanKernelArgs& a, hipStream_t stream);
 template <typename XT, typename YT>
 hipError_t launch_scan_xy(const ScanLaunch& l, hipStream_t stream);
+template <typename XT, typename YT>
+int scan_occupancy_xy(const ScanLaunch& l);
+// Workgroups of the full-segment scan kernel that the current device holds at
+// once (CUs x resident workgroups per CU), or 0 when it cannot be queried.
+long scan_resident_waves(const ScanLaunch& l);
 size_t scan_summary_offset(int batch, int seqlen);
 hipError_t launch_scan(const ScanLaunch& l, hipStream_t stream);
 
