@@ -145,7 +145,8 @@ ssm_status_t ssm_scan_check(const ssm_scan_params_t *p);
  *   conv_cache (Bt, E, K-1) f32, read then overwritten with the window shifted by one
  *   (required iff conv_w != NULL);  ssm_state (Bt, E, N) f32, read then overwritten;
  *   y (Bt, E) y_dtype.
- * ssm_state and A must be 16-byte aligned.
+ * ssm_state, A and conv_w must be 16-byte aligned, B and C aligned to 4
+ * elements (16 bytes in f32, 8 in bf16); batch * dim < 2^31.
  * The result equals ssm_scan_fwd with L = 1, conv_cache_in = conv_cache_out =
  * conv_cache and ssm_state_in = ssm_state_out = ssm_state.
  * ---------------------------------------------------------------------- */

@@ -222,9 +222,12 @@ ssm_status_t decode_check(const ssm_decode_params_t* p) {
     if (!p->x || !p->y || !p->B || !p->C || !p->dt || !p->ssm_state)
       return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "x/y/B/C/dt/ssm_state");
   }
-  if (Bt * ((E + 63) / 64) > 0x7fffffffULL) return fail(SSM_ERR_UNSUPPORTED, "%s too large", "batch*dim");
-  if (Bt > 0 && ((reinterpret_cast<uintptr_t>(p->ssm_state) | reinterpret_cast<uintptr_t>(p->A)) & 15))
-    return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "ssm_state/A");
+  if (Bt * E > 0x7fffffffULL) return fail(SSM_ERR_UNSUPPORTED, "%s too large", "batch*dim");
+  if (Bt > 0 && ((reinterpret_cast<uintptr_t>(p->ssm_state) | reinterpret_cast<uintptr_t>(p->A) |
+                  reinterpret_cast<uintptr_t>(p->conv_w)) & 15))
+    return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "ssm_state/A/conv_w");
+  if (Bt > 0 && ((reinterpret_cast<uintptr_t>(p->B) | reinterpret_cast<uintptr_t>(p->C)) & (p->bc_dtype == SSM_BF16 ? 7 : 15)))
+    return fail(SSM_ERR_INVALID_ARG, "%s must be aligned to 4 elements", "B/C");
   const Range y{p->y, Bt * E * esize(p->y_dtype)};
   const Range ins[] = {
       {p->x, Bt * E * esize(p->x_dtype)},

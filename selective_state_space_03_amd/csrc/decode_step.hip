@@ -35,31 +35,51 @@ __device__ __forceinline__ void store_stream(float4* p, float4 v) {
   __builtin_nontemporal_store(w, reinterpret_cast<v4f*>(p));
 }
 
+// 4 consecutive elements from a 4-element-aligned address
+__device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
+  const float4 f = *reinterpret_cast<const float4*>(p);
+  v[0] = f.x;
+  v[1] = f.y;
+  v[2] = f.z;
+  v[3] = f.w;
+}
+
+__device__ __forceinline__ void load4(const bf16s* p, float (&v)[4]) {
+  const uint2 r = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(r.x << 16);
+  v[1] = __uint_as_float(r.x & 0xffff0000u);
+  v[2] = __uint_as_float(r.y << 16);
+  v[3] = __uint_as_float(r.y & 0xffff0000u);
+}
+
 template <typename XT, typename YT, typename BT, int DTM, bool CONV>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeKernelArgs a) {
   using DT = typename std::conditional<DTM == 2, bf16s, float>::type;
   const int q = threadIdx.x & 3;
-  const size_t total = static_cast<size_t>(a.batch) * a.dim;
-  const size_t ch_raw = static_cast<size_t>(blockIdx.x) * 64 + (threadIdx.x >> 2);
+  // (b, e) flattened; batch * dim < 2^31, so 32-bit index arithmetic
+  const uint32_t total = static_cast<uint32_t>(a.batch) * static_cast<uint32_t>(a.dim);
+  const uint32_t ch_raw = blockIdx.x * 64u + (threadIdx.x >> 2);
   const bool act = ch_raw < total;
-  const size_t ch = act ? ch_raw : total - 1;  // (b, e) flattened
-  const int b = static_cast<int>(ch / a.dim);
-  const int e = static_cast<int>(ch % a.dim);
+  const uint32_t ch = act ? ch_raw : total - 1;
+  const uint32_t b = ch / static_cast<uint32_t>(a.dim);
+  const uint32_t e = ch - b * static_cast<uint32_t>(a.dim);
 
   float4* __restrict__ state4 = reinterpret_cast<float4*>(a.state);
-  const float4 hs = load_stream(state4 + ch * 4 + q);
+  const float4 hs = load_stream(state4 + static_cast<size_t>(ch) * 4 + q);
   const float4 a4 = reinterpret_cast<const float4*>(a.A)[static_cast<size_t>(e) * 4 + q];
   const float xr = ld<XT>(a.x, ch);
 
   float c0 = 0.0f, c1 = 0.0f, c2 = 0.0f;
   float u = xr;
   if (CONV) {
-    c0 = a.conv_cache[ch * 3 + 0];
-    c1 = a.conv_cache[ch * 3 + 1];
-    c2 = a.conv_cache[ch * 3 + 2];
-    const float* w = a.conv_w + static_cast<size_t>(e) * kConvK;
+    // lanes 0..2 of the quad each load one cache entry; the quad shares them
+    const float cq = q < 3 ? __builtin_nontemporal_load(a.conv_cache + static_cast<size_t>(ch) * 3 + q) : 0.0f;
+    c0 = __shfl(cq, 0, 4);
+    c1 = __shfl(cq, 1, 4);
+    c2 = __shfl(cq, 2, 4);
+    const float4 w = reinterpret_cast<const float4*>(a.conv_w)[e];
     const float cb = a.conv_b ? a.conv_b[e] : 0.0f;
-    const float xc = fmaf(w[0], c0, fmaf(w[1], c1, fmaf(w[2], c2, fmaf(w[3], xr, cb))));
+    const float xc = fmaf(w.x, c0, fmaf(w.y, c1, fmaf(w.z, c2, fmaf(w.w, xr, cb))));
     u = silu(xc);
   }
   const float dtb = a.dt_bias ? a.dt_bias[e] : 0.0f;
@@ -69,8 +89,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeKernelArgs a) {
                                  : dt_clip(pre, a.dt_min, a.dt_max);
   const float dtu = dt * u;
 
-  const BT* Bp = static_cast<const BT*>(a.B) + static_cast<size_t>(b) * kScanN + 4 * q;
-  const BT* Cp = static_cast<const BT*>(a.C) + static_cast<size_t>(b) * kScanN + 4 * q;
+  // this lane's 4 entries of B and C: one aligned 4-element load each
+  float bq[4], cq4[4];
+  load4(static_cast<const BT*>(a.B) + static_cast<size_t>(b) * kScanN + 4 * q, bq);
+  load4(static_cast<const BT*>(a.C) + static_cast<size_t>(b) * kScanN + 4 * q, cq4);
   const float hin[4] = {hs.x, hs.y, hs.z, hs.w};
   const float av[4] = {a4.x, a4.y, a4.z, a4.w};
   float hout[4];
@@ -78,14 +100,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeKernelArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float an = exp2_fast(dt * (av[j] * kLog2e));
-    hout[j] = fmaf(an, hin[j], dtu * to_f32(Bp[j]));
-    acc = fmaf(to_f32(Cp[j]), hout[j], acc);
+    hout[j] = fmaf(an, hin[j], dtu * bq[j]);
+    acc = fmaf(cq4[j], hout[j], acc);
   }
   acc += __shfl_xor(acc, 1, 4);
   acc += __shfl_xor(acc, 2, 4);
 
   if (!act) return;
-  store_stream(state4 + ch * 4 + q, make_float4(hout[0], hout[1], hout[2], hout[3]));
+  store_stream(state4 + static_cast<size_t>(ch) * 4 + q, make_float4(hout[0], hout[1], hout[2], hout[3]));
   if (q == 0) {
     float yv = fmaf(a.D ? a.D[e] : 0.0f, u, acc);
     if (a.has_z) yv *= silu(ld<XT>(a.z, ch));
@@ -93,7 +115,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeKernelArgs a) {
   }
   if (CONV && q < 3) {
     const float nv = (q == 0) ? c1 : (q == 1) ? c2 : xr;
-    a.conv_cache[ch * 3 + q] = nv;
+    __builtin_nontemporal_store(nv, a.conv_cache + static_cast<size_t>(ch) * 3 + q);
   }
 }
 
