@@ -52,30 +52,36 @@ size_t bc_bytes(int batch, int seqlen) {
 }
 
 // Affine composition of the segment summaries, one thread per (batch,
-// channel): slot 0 already holds segment 0's end state (it started from the
-// true initial state), and for k = 1 .. nseg-2 the state entering segment k+1
-// is exp(A sum dt_k) h + h_end_k, written over slot k.
-__global__ __launch_bounds__(64) void scan_compose_kernel(ScanKernelArgs a) {
-  const int lane = threadIdx.x;
+// channel, state): slot 0 already holds segment 0's end state (it started from
+// the true initial state), and for k = 1 .. nseg-2 the state entering segment
+// k+1 is exp(A sum dt_k) h + h_end_k, written over slot k.  Every summary is
+// loaded before the chain starts, so the chain waits for memory once.
+// Block: 64 channels x 4 states; grid: (batch x channel groups, 4).
+__global__ __launch_bounds__(256) void scan_compose_kernel(ScanKernelArgs a) {
+  constexpr int K = kScanMaxSplit - 1;  // summary slots at most
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int gid = blockIdx.x;  // batch * n_egroups + channel group
   const int g = gid % a.n_egroups;
   const int e = min(g * 64 + lane, a.dim - 1);
-  float* summ = a.summ + static_cast<size_t>(gid) * (a.nseg - 1) * (kScanN + 1) * 64;
-  float al2[kScanN], h[kScanN];
+  const int nk = a.nseg - 1;   // slots in use
+  float* summ = a.summ + static_cast<size_t>(gid) * nk * (kScanN + 1) * 64;
+  const float al2 = a.A[static_cast<size_t>(e) * kScanN + n] * kLog2e;
+  float hend[K], sd[K];
 #pragma unroll
-  for (int n = 0; n < kScanN; ++n) {
-    al2[n] = a.A[static_cast<size_t>(e) * kScanN + n] * kLog2e;
-    h[n] = summ[n * 64 + lane];
+  for (int k = 1; k < K; ++k) {
+    if (k < nk) {
+      const float* sk = summ + static_cast<size_t>(k) * (kScanN + 1) * 64;
+      hend[k] = sk[n * 64 + lane];
+      sd[k] = sk[kScanN * 64 + lane];
+    }
   }
-  // unrolled so several summaries' loads are in flight ahead of the chain
-#pragma unroll 4
-  for (int k = 1; k < a.nseg - 1; ++k) {
-    float* sk = summ + static_cast<size_t>(k) * (kScanN + 1) * 64;
-    const float sd = sk[kScanN * 64 + lane];
+  float h = summ[n * 64 + lane];
 #pragma unroll
-    for (int n = 0; n < kScanN; ++n) {
-      h[n] = fmaf(exp2_fast(al2[n] * sd), h[n], sk[n * 64 + lane]);
-      sk[n * 64 + lane] = h[n];
+  for (int k = 1; k < K; ++k) {
+    if (k < nk) {
+      h = fmaf(exp2_fast(al2 * sd[k]), h, hend[k]);
+      summ[static_cast<size_t>(k) * (kScanN + 1) * 64 + n * 64 + lane] = h;
     }
   }
 }
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(64) void scan_compose_kernel(ScanKernelArgs a) {
 hipError_t launch_scan_compose(const ScanKernelArgs& a, hipStream_t stream) {
   if (a.nseg <= 2) return hipSuccess;  // slot 0 is already the state entering segment 1
   const unsigned groups = static_cast<unsigned>(a.batch) * static_cast<unsigned>(a.n_egroups);
-  hipLaunchKernelGGL(scan_compose_kernel, dim3(groups), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(scan_compose_kernel, dim3(groups, kScanN / 4), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
