@@ -138,10 +138,16 @@ def test_decode_validation(L):
         "d_state": (_decode(d_state=32), 2),
         "no_state": (_decode(ssm_state=None), 1),
         "y_over_state": (_decode(y=_addr(8) + 128), 1),
+        "bc_align": (_decode(B=_addr(4) + 4), 1),
+        "bc_align_bf16": (_decode(C=_addr(5) + 4, bc_dtype=1), 1),
+        "conv_w_align": (_decode(conv_w=_addr(9) + 4), 1),
+        "too_many_channels": (_decode(batch=1 << 20, dim=1 << 12), 2),
     }
     for name, (p, want) in cases.items():
         assert L.ssm_decode_check(ctypes.byref(p)) == want, (name, L.ssm_last_error())
     assert L.ssm_decode_step(ctypes.byref(_decode(d_state=32)), None) == 2
+    # bf16 B/C need only 8-byte alignment
+    assert L.ssm_decode_check(ctypes.byref(_decode(B=_addr(4) + 8, C=_addr(5) + 8, bc_dtype=1))) == 0
 
 
 def _chunk(**kw):
@@ -170,6 +176,8 @@ def test_chunk_validation(L):
         "headdim": (_chunk(headdim=100), 2),
         "null_A": (_chunk(A=None), 1),
         "out_over_x": (_chunk(out=_addr(1) + 2), 1),
+        "out_align": (_chunk(out=_addr(6) + 8), 1),
+        "x_align": (_chunk(x=_addr(1) + 2), 1),
     }
     for name, (p, want) in cases.items():
         assert L.ssm_chunk_scan_check(ctypes.byref(p)) == want, (name, L.ssm_last_error())
