@@ -41,6 +41,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Column of element s in row r of the transposed tiles (Bt, Xt): the 16-byte
+// blocks of a row are permuted by the row's 8-row group, so the transposing
+// stores (one row per 8-row group across the lanes of a wave) fall in
+// different banks.  Reads of 4 or 8 consecutive elements inside one block stay
+// contiguous.
+__device__ __forceinline__ int swz(int r, int s) { return ((((s >> 3) ^ (r >> 3)) & 15) << 3) | (s & 7); }
+
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
 __device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
@@ -54,8 +61,8 @@ template <int PT>
 struct alignas(16) Smem {
   uint16_t C[kQ][kRowN];    // C chunk, row-major [l][n]
   uint16_t B[kQ][kRowN];    // B chunk, row-major [s][n]
-  uint16_t Bt[kN][kRowQ];   // B chunk transposed [n][s]
-  uint16_t Xt[PT][kRowQ];   // x chunk slice transposed [p][s]
+  uint16_t Bt[kN][kRowQ];   // B chunk transposed [n][swz(n, s)]
+  uint16_t Xt[PT][kRowQ];   // x chunk slice transposed [p][swz(p, s)]
   uint16_t XWh[PT][kRowQ];  // wS[s] x[s][p], transposed, bf16 high part
   uint16_t XWl[PT][kRowQ];  //                              bf16 low part
   uint16_t Shi[PT][kRowN];  // state entering the chunk, [p][n], bf16 high part
@@ -127,21 +134,22 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
   const bool xload = tid < Sh::XT;
 
   auto load_chunk = [&](int c, ChunkRegs<PT>& R) {
+    // chunk bases are wave-uniform; per-lane offsets fit in 32 bits
     const size_t tok = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
+    const uint16_t* Cc = Cg + (tok * G + g) * kN;
+    const uint16_t* Bc = Bg + (tok * G + g) * kN;
+    const uint16_t* xc = xg + (tok * H + h) * P + p0;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const size_t row = tok + RPT * rg + i;
-      R.c[i] = *reinterpret_cast<const uint4*>(Cg + (row * G + g) * kN + 8 * pc);
-      R.b[i] = *reinterpret_cast<const uint4*>(Bg + (row * G + g) * kN + 8 * pc);
+      const int o = (RPT * rg + i) * G * kN + 8 * pc;
+      R.c[i] = *reinterpret_cast<const uint4*>(Cc + o);
+      R.b[i] = *reinterpret_cast<const uint4*>(Bc + o);
     }
     if (xload) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const size_t row = tok + 2 * rgx + i;
-        R.x[i] = *reinterpret_cast<const uint4*>(xg + (row * H + h) * P + p0 + 8 * pcx);
-      }
+      for (int i = 0; i < 2; ++i) R.x[i] = *reinterpret_cast<const uint4*>(xc + (2 * rgx + i) * H * P + 8 * pcx);
     }
-    if (tid < kQ) R.dt = a.dt[(tok + tid) * H + h];
+    if (tid < kQ) R.dt = a.dt[tok * H + h + tid * H];
   };
 
   // bf16 j of a 16-byte piece
@@ -161,15 +169,15 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
       if constexpr (RPT == 4) {
         const uint32_t lo = half(R.b[0], j) | (half(R.b[1], j) << 16);
         const uint32_t hi = half(R.b[2], j) | (half(R.b[3], j) << 16);
-        *reinterpret_cast<uint2*>(&sm.Bt[8 * pc + j][4 * rg]) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(&sm.Bt[8 * pc + j][swz(8 * pc + j, 4 * rg)]) = make_uint2(lo, hi);
       } else {
-        *reinterpret_cast<uint32_t*>(&sm.Bt[8 * pc + j][2 * rg]) = half(R.b[0], j) | (half(R.b[1], j) << 16);
+        *reinterpret_cast<uint32_t*>(&sm.Bt[8 * pc + j][swz(8 * pc + j, 2 * rg)]) = half(R.b[0], j) | (half(R.b[1], j) << 16);
       }
     }
     if (xload) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<uint32_t*>(&sm.Xt[8 * pcx + j][2 * rgx]) = half(R.x[0], j) | (half(R.x[1], j) << 16);
+        *reinterpret_cast<uint32_t*>(&sm.Xt[8 * pcx + j][swz(8 * pcx + j, 2 * rgx)]) = half(R.x[0], j) | (half(R.x[1], j) << 16);
     }
     if (tid < kQ) {
       const float pre = R.dt + dtb;
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
 #pragma unroll
     for (int idx = tid; idx < PT * (kQ / 8); idx += NT) {
       const int p = idx / (kQ / 8), s0 = 8 * (idx % (kQ / 8));
-      const bf16x8 xr = *reinterpret_cast<const bf16x8*>(&sm.Xt[p][s0]);
+      const bf16x8 xr = *reinterpret_cast<const bf16x8*>(&sm.Xt[p][swz(p, s0)]);
       const float4 w0 = *reinterpret_cast<const float4*>(&sm.wS[s0]);
       const float4 w1 = *reinterpret_cast<const float4*>(&sm.wS[s0 + 4]);
       const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
       const int l_row = 16 * I + li, s0 = 16 * J + 4 * lg;
       o.el = factored ? sm.EL[J][l_row] : sm.dA[l_row];
       o.e4 = *reinterpret_cast<const float4*>(factored ? &sm.ESD[s0] : &sm.dA[s0]);
-      o.xv = *reinterpret_cast<const s16x4*>(&sm.Xt[16 * pt + li][s0]);
+      o.xv = *reinterpret_cast<const s16x4*>(&sm.Xt[16 * pt + li][swz(16 * pt + li, s0)]);
       return o;
     };
     // cb^T block (I, J) from the B rows of block J and the C rows of block I:
@@ -369,7 +377,7 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
       const int p = 16 * pt + li;
       const float4 e4 = *reinterpret_cast<const float4*>(&sm.eA[16 * I + 4 * lg]);
       const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
-      const s16x4 xv = *reinterpret_cast<const s16x4*>(&sm.Xt[p][16 * I + 4 * lg]);
+      const s16x4 xv = *reinterpret_cast<const s16x4*>(&sm.Xt[p][swz(p, 16 * I + 4 * lg)]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float xr = bf16_val(static_cast<uint16_t>(xv[r]));
@@ -414,7 +422,7 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
       const int s0 = 32 * kk + 8 * lg;
       const bf16x8 xh = *reinterpret_cast<const bf16x8*>(&sm.XWh[16 * ps + li][s0]);
       const bf16x8 xl = *reinterpret_cast<const bf16x8*>(&sm.XWl[16 * ps + li][s0]);
-      const bf16x8 bt = *reinterpret_cast<const bf16x8*>(&sm.Bt[16 * nb + li][s0]);
+      const bf16x8 bt = *reinterpret_cast<const bf16x8*>(&sm.Bt[16 * nb + li][swz(16 * nb + li, s0)]);
       acc_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bt, acc_hi, 0, 0, 0);
       acc_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bt, acc_lo, 0, 0, 0);
     }
