@@ -355,14 +355,23 @@ def _heads_to_groups(H, G):
     return np.arange(H) // (H // G)
 
 
-def ssd_scan_sequential(x, dt, A, B, C, D=None, state=None):
+def _gate(out, z):
+    """out * SiLU(z) when a gate is given (applied after the D skip, as the
+    Axon-SSM page's y * SiLU(z) is for the layer scan)."""
+    if z is None:
+        return out
+    return out * silu(_f64(z))
+
+
+def ssd_scan_sequential(x, dt, A, B, C, D=None, state=None, z=None):
     """Plain definition of the multi-head scan the chunked form computes: for
     head h with scalar A_h and state S (P, N),
         S_t = exp(dt_t A_h) S_{t-1} + dt_t x_t (outer) B_t[g(h)]
-        out_t = S_t C_t[g(h)] + D_h x_t
+        out_t = (S_t C_t[g(h)] + D_h x_t) * SiLU(z_t)   (gate optional)
     x: (Bt, L, H, P); dt: (Bt, L, H) (already softplus/clipped); A: (H);
-    B, C: (Bt, L, G, N); D: (H) or (H, P); state: (Bt, H, P, N) or None.
-    Returns (out (Bt, L, H, P), S_L (Bt, H, P, N))."""
+    B, C: (Bt, L, G, N); D: (H) or (H, P); state: (Bt, H, P, N) or None;
+    z: (Bt, L, H, P) or None.  With L = 1 this is one decode step of the
+    chunked form's state.  Returns (out (Bt, L, H, P), S_L (Bt, H, P, N))."""
     x = _f64(x)
     dt = _f64(dt)
     A = _f64(A)
@@ -382,10 +391,10 @@ def ssd_scan_sequential(x, dt, A, B, C, D=None, state=None):
     if D is not None:
         Dv = _f64(D)
         out = out + x * (Dv[None, None, :, None] if Dv.ndim == 1 else Dv[None, None])
-    return out, S
+    return _gate(out, z), S
 
 
-def ssd_chunk_scan(x, dt, A, B, C, D=None, state=None, chunk_size=128):
+def ssd_chunk_scan(x, dt, A, B, C, D=None, state=None, chunk_size=128, z=None):
     """Chunked SSD scan (velog page, "chunkscan implementation").  For every
     chunk in order, with dA[l] = sum_{i<=l} dt[i] A_h inside the chunk
     (inclusive cumulative sum) and cb[l, s] = C[l] . B[s]:
@@ -398,7 +407,9 @@ def ssd_chunk_scan(x, dt, A, B, C, D=None, state=None, chunk_size=128):
     next chunk (the inter-chunk scan over chunk-final states) follows from the
     unrolled product-sum form:
       prev_states <- e^{dA[Q-1]} prev_states + sum_s e^{dA[Q-1]-dA[s]} dt[s] x[s] (outer) B[s]
-    The sequence length must be a whole number of chunks."""
+    A sequence that is not a whole number of chunks ends with a shorter chunk,
+    to which the same formulas apply with its own length in place of Q.  An
+    optional gate multiplies the output (after D) by SiLU(z)."""
     x = _f64(x)
     dt = _f64(dt)
     A = _f64(A)
@@ -407,15 +418,13 @@ def ssd_chunk_scan(x, dt, A, B, C, D=None, state=None, chunk_size=128):
     Bt, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     Q = int(chunk_size)
-    if L % Q != 0:
-        raise ValueError("seqlen must be a multiple of chunk_size")
     g = _heads_to_groups(H, G)
     S = np.zeros((Bt, H, P, N)) if state is None else _f64(state).copy()
     out = np.zeros((Bt, L, H, P))
-    ls = np.arange(Q)
-    causal = ls[None, :] <= ls[:, None]  # [l, s] : s <= l
-    for c in range(L // Q):
-        sl = slice(c * Q, (c + 1) * Q)
+    for c in range((L + Q - 1) // Q):
+        sl = slice(c * Q, min((c + 1) * Q, L))
+        ls = np.arange(sl.stop - sl.start)
+        causal = ls[None, :] <= ls[:, None]  # [l, s] : s <= l
         xc = x[:, sl]  # (Bt, Q, H, P)
         dtc = dt[:, sl]  # (Bt, Q, H)
         dA = np.cumsum(dtc * A[None, None, :], axis=1)  # (Bt, Q, H)
@@ -436,4 +445,4 @@ def ssd_chunk_scan(x, dt, A, B, C, D=None, state=None, chunk_size=128):
     if D is not None:
         Dv = _f64(D)
         out = out + x * (Dv[None, None, :, None] if Dv.ndim == 1 else Dv[None, None])
-    return out, S
+    return _gate(out, z), S

@@ -203,6 +203,58 @@ def pin_ssd_chunked_equals_sequential(orc):
         _close(Sc, S, 1e-11, f"ssd chunked state Q={Q}")
 
 
+def pin_ssd_ragged_chunks(orc):
+    """A sequence that is not a whole number of chunks (its last chunk shorter)
+    gives the plain recurrence too, for lengths below, at and across chunk
+    boundaries."""
+    x, dt, A, Bm, Cm, D, S0 = _ssd_inputs(108, L=45)
+    for L in (1, 7, 16, 17, 45):
+        args = (x[:, :L], dt[:, :L], A, Bm[:, :L], Cm[:, :L])
+        out, S = orc.ssd_scan_sequential(*args, D=D, state=S0)
+        for Q in (4, 16, 32):
+            oc, Sc = orc.ssd_chunk_scan(*args, D=D, state=S0, chunk_size=Q)
+            _close(oc, out, 1e-11, f"ssd ragged out L={L} Q={Q}")
+            _close(Sc, S, 1e-11, f"ssd ragged state L={L} Q={Q}")
+
+
+def pin_ssd_gate(orc):
+    """The gate multiplies the ungated output (D included) by SiLU(z) = z
+    sigmoid(z), sigmoid from scipy's expit where available; z = 0 zeroes the
+    output; the gate leaves the state alone; both forms agree."""
+    x, dt, A, Bm, Cm, D, S0 = _ssd_inputs(109, L=20)
+    z = _rng(110).standard_normal(x.shape) * 3.0
+    try:
+        from scipy.special import expit
+    except ImportError:  # pragma: no cover
+        expit = lambda v: 0.5 * (1.0 + np.tanh(0.5 * v))
+    o0, S0s = orc.ssd_scan_sequential(x, dt, A, Bm, Cm, D=D, state=S0)
+    og, Sg = orc.ssd_scan_sequential(x, dt, A, Bm, Cm, D=D, state=S0, z=z)
+    _close(og, o0 * z * expit(z), 1e-12, "ssd gate = SiLU(z) factor")
+    _close(Sg, S0s, 0.0, "ssd gate leaves the state")
+    oz, _ = orc.ssd_scan_sequential(x, dt, A, Bm, Cm, D=D, state=S0, z=np.zeros_like(z))
+    assert np.all(oz == 0.0), "z = 0 must zero the gated output"
+    oc, _ = orc.ssd_chunk_scan(x, dt, A, Bm, Cm, D=D, state=S0, chunk_size=8, z=z)
+    _close(oc, og, 1e-11, "ssd gate chunked vs sequential")
+
+
+def pin_ssd_prefill_then_decode(orc):
+    """Chunked prefill of the first T0 tokens, then one-token steps from the
+    returned state, equal one pass over all tokens (outputs and final state)."""
+    x, dt, A, Bm, Cm, D, S0 = _ssd_inputs(111, L=23)
+    z = _rng(112).standard_normal(x.shape)
+    full, Sf = orc.ssd_chunk_scan(x, dt, A, Bm, Cm, D=D, state=S0, chunk_size=8, z=z)
+    T0 = 11
+    o1, S = orc.ssd_chunk_scan(x[:, :T0], dt[:, :T0], A, Bm[:, :T0], Cm[:, :T0], D=D, state=S0, chunk_size=8,
+                               z=z[:, :T0])
+    outs = [o1]
+    for t in range(T0, x.shape[1]):
+        ot, S = orc.ssd_scan_sequential(x[:, t:t + 1], dt[:, t:t + 1], A, Bm[:, t:t + 1], Cm[:, t:t + 1], D=D,
+                                        state=S, z=z[:, t:t + 1])
+        outs.append(ot)
+    _close(np.concatenate(outs, axis=1), full, 1e-11, "ssd prefill + decode out")
+    _close(S, Sf, 1e-11, "ssd prefill + decode state")
+
+
 def pin_ssd_equals_channel_scan(orc):
     """The multi-head scan is the diagonal scan on E = H*P channels whose
     d_state entries all decay with the head's scalar A and whose B, C are the
@@ -456,6 +508,9 @@ ALL_PINS = [
     pin_single_step,
     pin_chunked_equals_sequential,
     pin_ssd_chunked_equals_sequential,
+    pin_ssd_ragged_chunks,
+    pin_ssd_gate,
+    pin_ssd_prefill_then_decode,
     pin_ssd_equals_channel_scan,
     pin_prefill_then_decode,
     pin_conv_cache_contents,

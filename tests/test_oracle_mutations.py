@@ -41,6 +41,10 @@ MUTATIONS = {
     "ssd_seq_dt_dropped": ("S = a[:, :, None, None] * S + (dt[:, t, :, None] * x[:, t])[..., None]",
                            "S = a[:, :, None, None] * S + (x[:, t])[..., None]"),
     "a_from_log_sign": ("return -np.exp(_f64(A_log))", "return np.exp(_f64(A_log))"),
+    "ssd_ragged_tail_dropped": ("for c in range((L + Q - 1) // Q):", "for c in range(L // Q):"),
+    "ssd_gate_sigmoid": ("    return out * silu(_f64(z))", "    return out * sigmoid(_f64(z))"),
+    "ssd_seq_gate_dropped": ("    return _gate(out, z), S\n\n\ndef ssd_chunk_scan",
+                          "    return out, S\n\n\ndef ssd_chunk_scan"),
 }
 
 
