@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 /* element types (int32 fields in the structs below) */
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
@@ -193,8 +193,9 @@ ssm_status_t ssm_decode_check(const ssm_decode_params_t *p);
  *   out       (Bt, L, H, P) out_dtype
  *   dA[l] = sum_{i<=l} dt[i] A_h inside each chunk of chunk_size tokens (inclusive);
  *   state passing: S <- e^{dA[Q-1]} S + sum_s e^{dA[Q-1]-dA[s]} dt[s] x[s] (outer) B[s].
- * Requires L % chunk_size == 0 (SSM_ERR_INVALID_ARG otherwise) and x, B, C
- * and out 16-byte aligned.
+ * A sequence that is not a whole number of chunks ends with a shorter chunk
+ * (the same formulas over its own length).  x, B, C, out (and z) must be
+ * 16-byte aligned.
  * Supported: x and B/C in bf16, N = 64, P % 16 == 0 and P <= 128, chunk_size = 128.
  * ---------------------------------------------------------------------- */
 typedef struct ssm_chunk_params {
@@ -218,6 +219,8 @@ typedef struct ssm_chunk_params {
   int32_t out_dtype;
   void *workspace;
   size_t workspace_bytes;
+  const void *z;        /* (Bt, L, H, P) z_dtype or NULL: out *= SiLU(z) after the D skip */
+  int32_t z_dtype;
 } ssm_chunk_params_t;
 
 ssm_status_t ssm_chunk_scan_fwd(const ssm_chunk_params_t *p, void *stream);

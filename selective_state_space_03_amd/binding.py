@@ -54,7 +54,7 @@ class ChunkParams(ctypes.Structure):
         ("dt", _vp), ("dt_bias", _vp), ("dt_softplus", _i32), ("dt_min", _f32), ("dt_max", _f32),
         ("A", _vp), ("B", _vp), ("C", _vp), ("bc_dtype", _i32), ("D", _vp), ("d_per_channel", _i32),
         ("state_in", _vp), ("state_out", _vp), ("out", _vp), ("out_dtype", _i32),
-        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t), ("z", _vp), ("z_dtype", _i32),
     ]
 
 
@@ -282,7 +282,7 @@ def decode_step(x, A, B, C, dt, ssm_state, *, conv_cache=None, D=None, z=None, c
 
 
 def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size=128, D=None, dt_bias=None, dt_softplus=True, dt_min=None,
-                   dt_max=None, state_in=None, state_out=None, out=None, out_dtype=None, workspace=None,
+                   dt_max=None, state_in=None, state_out=None, out=None, out_dtype=None, z=None, workspace=None,
                    stream=None, prepare=False):
     """Multi-head chunked scan (ssm_chunk_scan_fwd).  Returns out (batch, L, H, P), or
     with prepare=True a Call that enqueues this same call again on each run()."""
@@ -315,11 +315,13 @@ def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size=128, D=None, dt_bias=None, dt_s
     p.state_out = _ptr(state_out, "state_out", (batch, nheads, headdim, d_state), f32, dev)
     p.out = _ptr(out, "out", (batch, seqlen, nheads, headdim), device=dev)
     p.out_dtype = _code(out, "out")
+    p.z = _ptr(z, "z", (batch, seqlen, nheads, headdim), device=dev)
+    p.z_dtype = _code(z, "z") if z is not None else 0
     need = L_.ssm_chunk_scan_workspace_size(ctypes.byref(p))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     p.workspace = _ptr(workspace, "workspace", device=dev)
     p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     call = Call(L_.ssm_chunk_scan_fwd, p, _stream(dev, stream), out, (x, dt, A, B, C, D, dt_bias, state_in,
-                                                                     state_out, workspace))
+                                                                     state_out, workspace, z))
     return call if prepare else call.run()

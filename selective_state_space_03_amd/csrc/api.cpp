@@ -259,7 +259,6 @@ ssm_status_t chunk_check(const ssm_chunk_params_t* p) {
       p->d_state <= 0 || p->chunk_size <= 0)
     return fail(SSM_ERR_INVALID_ARG, "%s: negative or zero size", "dims");
   if (p->nheads % p->ngroups != 0) return fail(SSM_ERR_INVALID_ARG, "%s", "nheads must be a multiple of ngroups");
-  if (p->seqlen % p->chunk_size != 0) return fail(SSM_ERR_INVALID_ARG, "%s", "seqlen must be a multiple of chunk_size");
   if (p->d_state != ssm::kSsdN) return fail(SSM_ERR_UNSUPPORTED, "%s must be 64", "d_state");
   if (p->chunk_size != ssm::kSsdQ) return fail(SSM_ERR_UNSUPPORTED, "%s must be 128", "chunk_size");
   if (p->headdim % 16 != 0 || p->headdim > ssm::kSsdMaxP)
@@ -268,9 +267,10 @@ ssm_status_t chunk_check(const ssm_chunk_params_t* p) {
     return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "x/bc/out_dtype");
   if (p->x_dtype != SSM_BF16 || p->bc_dtype != SSM_BF16)
     return fail(SSM_ERR_UNSUPPORTED, "%s must be bf16", "x_dtype/bc_dtype");
+  if (p->z && !valid_dtype(p->z_dtype)) return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "z_dtype");
   if ((reinterpret_cast<uintptr_t>(p->x) | reinterpret_cast<uintptr_t>(p->B) | reinterpret_cast<uintptr_t>(p->C) |
-       reinterpret_cast<uintptr_t>(p->out)) & 15)
-    return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "x/B/C/out");
+       reinterpret_cast<uintptr_t>(p->out) | reinterpret_cast<uintptr_t>(p->z)) & 15)
+    return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "x/B/C/out/z");
   if (!p->A) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "A");
   ssm_status_t s = check_dt_bounds(p->dt_min, p->dt_max);
   if (s != SSM_OK) return s;
@@ -290,6 +290,7 @@ ssm_status_t chunk_check(const ssm_chunk_params_t* p) {
       {p->state_in, p->state_in ? Bt * H * P * N * 4 : 0},
       {p->state_out, p->state_out ? Bt * H * P * N * 4 : 0},
       {p->workspace, p->workspace_bytes},
+      {p->z, p->z ? tok * H * P * esize(p->z_dtype) : 0},
   };
   for (const Range& r : ins)
     if (overlaps(out, r)) return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "out");
@@ -447,7 +448,9 @@ ssm_status_t ssm_chunk_scan_fwd(const ssm_chunk_params_t* p, void* stream) {
   k.nheads = p->nheads;
   k.headdim = p->headdim;
   k.ngroups = p->ngroups;
-  k.nchunks = p->seqlen / p->chunk_size;
+  k.nchunks = (p->seqlen + p->chunk_size - 1) / p->chunk_size;
+  k.z = p->z;
+  k.z_bf16 = p->z && p->z_dtype == SSM_BF16 ? 1 : 0;
   k.d_per_channel = p->d_per_channel ? 1 : 0;
   k.dt_min = p->dt_min;
   k.dt_max = p->dt_max;

@@ -28,6 +28,8 @@
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
+#include <type_traits>
+
 namespace ssm {
 namespace {
 
@@ -93,9 +95,13 @@ template <int PT>
 struct ChunkRegs {
   uint4 c[Shape<PT>::RPT], b[Shape<PT>::RPT], x[2];
   float dt;
+  int valid;  // tokens of this chunk inside the sequence (fewer in a ragged last chunk)
 };
 
-template <typename OT, int PT>
+// GATE: the output is multiplied by SiLU(z).  Whole chunks run in the loop;
+// a ragged last chunk (L not a multiple of Q) runs after it in its own copy
+// of the chunk step, so the loop carries no row tests.
+template <typename OT, int PT, bool GATE>
 __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
   using Sh = Shape<PT>;
   constexpr int NPT = Sh::NPT, NW = Sh::NW, NT = Sh::NT, RPT = Sh::RPT, XPR = Sh::XPR;
@@ -133,23 +139,35 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
   const int rgx = tid / XPR, pcx = tid % XPR;       // x: row pair, 8-column piece
   const bool xload = tid < Sh::XT;
 
-  auto load_chunk = [&](int c, ChunkRegs<PT>& R) {
+  // Rows past the end of the sequence (the ragged last chunk) load as zeros,
+  // and their dt is set to 0 below: they add nothing to the state, do not
+  // decay it, and their outputs are not stored.
+  auto load_chunk = [&](int c, ChunkRegs<PT>& R, auto ragged) {
+    constexpr bool kRag = decltype(ragged)::value;
     // chunk bases are wave-uniform; per-lane offsets fit in 32 bits
     const size_t tok = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
+    R.valid = kRag ? L - c * kQ : kQ;
     const uint16_t* Cc = Cg + (tok * G + g) * kN;
     const uint16_t* Bc = Bg + (tok * G + g) * kN;
     const uint16_t* xc = xg + (tok * H + h) * P + p0;
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int o = (RPT * rg + i) * G * kN + 8 * pc;
-      R.c[i] = *reinterpret_cast<const uint4*>(Cc + o);
-      R.b[i] = *reinterpret_cast<const uint4*>(Bc + o);
+      const int r = RPT * rg + i;
+      const int o = r * G * kN + 8 * pc;
+      const bool in = !kRag || r < R.valid;
+      R.c[i] = in ? *reinterpret_cast<const uint4*>(Cc + o) : z4;
+      R.b[i] = in ? *reinterpret_cast<const uint4*>(Bc + o) : z4;
     }
     if (xload) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) R.x[i] = *reinterpret_cast<const uint4*>(xc + (2 * rgx + i) * H * P + 8 * pcx);
+      for (int i = 0; i < 2; ++i) {
+        const int r = 2 * rgx + i;
+        const bool in = !kRag || r < R.valid;
+        R.x[i] = in ? *reinterpret_cast<const uint4*>(xc + r * H * P + 8 * pcx) : z4;
+      }
     }
-    if (tid < kQ) R.dt = a.dt[tok * H + h + tid * H];
+    if (tid < R.valid) R.dt = a.dt[tok * H + h + tid * H];
   };
 
   // bf16 j of a 16-byte piece
@@ -157,7 +175,8 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
     return (reinterpret_cast<const uint32_t*>(&v)[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
   };
 
-  auto store_chunk = [&](const ChunkRegs<PT>& R) {
+  auto store_chunk = [&](const ChunkRegs<PT>& R, auto ragged) {
+    constexpr bool kRag = decltype(ragged)::value;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       *reinterpret_cast<uint4*>(&sm.C[RPT * rg + i][8 * pc]) = R.c[i];
@@ -181,8 +200,9 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
     }
     if (tid < kQ) {
       const float pre = R.dt + dtb;
-      sm.dt[tid] = a.dt_softplus ? dt_softplus_clip(pre, a.dt_min, a.dt_max, a.sp_lo, a.sp_hi)
-                                 : __builtin_amdgcn_fmed3f(pre, a.dt_min, a.dt_max);
+      const float d = a.dt_softplus ? dt_softplus_clip(pre, a.dt_min, a.dt_max, a.sp_lo, a.sp_hi)
+                                    : __builtin_amdgcn_fmed3f(pre, a.dt_min, a.dt_max);
+      sm.dt[tid] = !kRag || tid < R.valid ? d : 0.0f;
     }
   };
 
@@ -221,11 +241,14 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
   }
 
   ChunkRegs<PT> R;
-  load_chunk(0, R);
-  for (int c = 0; c < a.nchunks; ++c) {
+  const int nfull = L / kQ;  // whole chunks; a ragged one follows when L % Q != 0
+  // One chunk step: stage chunk c (already in R) in LDS, prefetch the next
+  // whole chunk, emit the chunk's outputs and advance the state.
+  auto chunk_step = [&](const int c, auto ragged) {
+    constexpr bool kRag = decltype(ragged)::value;
     __syncthreads();  // the previous chunk's LDS readers are done
-    store_chunk(R);
-    if (c + 1 < a.nchunks) load_chunk(c + 1, R);
+    store_chunk(R, ragged);
+    if (!kRag && c + 1 < nfull) load_chunk(c + 1, R, std::false_type{});
     __syncthreads();
 
     // Every wave scans the chunk's log2 decays in registers (lane: steps
@@ -384,33 +407,64 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
         sm.O[16 * I + 4 * lg + r][p] = fmaf(dv, xr, fmaf(ev[r], sr_hi[r] + sr_lo[r], acc_hi[r] + acc_lo[r]));
       }
     };
+    // The output pieces: thread tid stores 8 values of row l = tid / PPR (all
+    // of the tile's pieces, one per thread).  Its gate values are fetched
+    // here so that their latency overlaps the state readout.
+    constexpr int PPR = PT / 8;  // 8-value pieces per row
+    static_assert(kQ * PPR == NT, "one output piece per thread");
+    const int ol = tid / PPR, oq = tid % PPR;
+    const size_t tok0 = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
+    const size_t e0 = ((tok0 + ol) * H + h) * P + p0 + 8 * oq;
+    const bool orow = !kRag || ol < L - c * kQ;
+    uint4 zr0 = make_uint4(0u, 0u, 0u, 0u), zr1 = zr0;
+    if constexpr (GATE) {
+      if (orow) {
+        if (a.z_bf16) {
+          zr0 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.z) + e0);
+        } else {
+          zr0 = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.z) + e0);
+          zr1 = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.z) + e0 + 4);
+        }
+      }
+    }
     finish(I0, 0, a0h, a0l, dv0);
     finish(I1, pt1, a1h, a1l, dv1);
     __syncthreads();  // output tile and XW complete; every wave is done reading Shi/Slo
 
-    // ---- the output tile to HBM: whole 16-byte pieces of each row
-    const size_t tok0 = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
-    if constexpr (sizeof(OT) == 4) {
-      constexpr int PPR = PT / 4;  // float4 pieces per row
+    // ---- the output tile to HBM: whole 16-byte pieces of each row (rows of
+    // the sequence only), times SiLU(z) when gated
+    if (orow) {
+      const float4 v0 = *reinterpret_cast<const float4*>(&sm.O[ol][8 * oq]);
+      const float4 v1 = *reinterpret_cast<const float4*>(&sm.O[ol][8 * oq + 4]);
+      float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      if constexpr (GATE) {
+        float zv[8];
+        if (a.z_bf16) {
+          const uint32_t zw[4] = {zr0.x, zr0.y, zr0.z, zr0.w};
 #pragma unroll
-      for (int idx = tid; idx < kQ * PPR; idx += NT) {
-        const int l = idx / PPR, q = idx % PPR;
-        const float4 v = *reinterpret_cast<const float4*>(&sm.O[l][4 * q]);
-        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + ((tok0 + l) * H + h) * P + p0 + 4 * q) = v;
+          for (int j = 0; j < 4; ++j) {
+            zv[2 * j] = __uint_as_float(zw[j] << 16);
+            zv[2 * j + 1] = __uint_as_float(zw[j] & 0xffff0000u);
+          }
+        } else {
+          const uint32_t zw[8] = {zr0.x, zr0.y, zr0.z, zr0.w, zr1.x, zr1.y, zr1.z, zr1.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) zv[j] = __uint_as_float(zw[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] *= silu(zv[j]);
       }
-    } else {
-      constexpr int PPR = PT / 8;  // 8-value pieces per row
-#pragma unroll
-      for (int idx = tid; idx < kQ * PPR; idx += NT) {
-        const int l = idx / PPR, q = idx % PPR;
-        const float4 v0 = *reinterpret_cast<const float4*>(&sm.O[l][8 * q]);
-        const float4 v1 = *reinterpret_cast<const float4*>(&sm.O[l][8 * q + 4]);
+      if constexpr (sizeof(OT) == 4) {
+        float* o = static_cast<float*>(a.out) + e0;
+        *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
         uint4 o;
-        o.x = bf16_bits(v0.x) | (static_cast<uint32_t>(bf16_bits(v0.y)) << 16);
-        o.y = bf16_bits(v0.z) | (static_cast<uint32_t>(bf16_bits(v0.w)) << 16);
-        o.z = bf16_bits(v1.x) | (static_cast<uint32_t>(bf16_bits(v1.y)) << 16);
-        o.w = bf16_bits(v1.z) | (static_cast<uint32_t>(bf16_bits(v1.w)) << 16);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + ((tok0 + l) * H + h) * P + p0 + 8 * q) = o;
+        o.x = bf16_bits(v[0]) | (static_cast<uint32_t>(bf16_bits(v[1])) << 16);
+        o.y = bf16_bits(v[2]) | (static_cast<uint32_t>(bf16_bits(v[3])) << 16);
+        o.z = bf16_bits(v[4]) | (static_cast<uint32_t>(bf16_bits(v[5])) << 16);
+        o.w = bf16_bits(v[6]) | (static_cast<uint32_t>(bf16_bits(v[7])) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + e0) = o;
       }
     }
 
@@ -428,6 +482,12 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
     }
     S = acc_hi + acc_lo;
     publish_state();
+  };
+  if (nfull > 0) load_chunk(0, R, std::false_type{});
+  for (int c = 0; c < nfull; ++c) chunk_step(c, std::false_type{});
+  if (nfull * kQ < L) {
+    load_chunk(nfull, R, std::true_type{});
+    chunk_step(nfull, std::true_type{});
   }
 
   if (a.state_out) {
@@ -445,7 +505,10 @@ hipError_t go(const ChunkLaunch& l, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>(k.batch) * k.nheads * (k.headdim / PT);
   if (blocks == 0) return hipSuccess;
   return timed_launch(s, [&] {
-    hipLaunchKernelGGL((ssd_kernel<OT, PT>), dim3(blocks), dim3(Shape<PT>::NT), 0, s, k);
+    if (k.z != nullptr)
+      hipLaunchKernelGGL((ssd_kernel<OT, PT, true>), dim3(blocks), dim3(Shape<PT>::NT), 0, s, k);
+    else
+      hipLaunchKernelGGL((ssd_kernel<OT, PT, false>), dim3(blocks), dim3(Shape<PT>::NT), 0, s, k);
   });
 }
 

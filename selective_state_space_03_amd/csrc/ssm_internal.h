@@ -132,8 +132,9 @@ struct ChunkKernelArgs {
   const float* state_in;
   float* state_out;
   void* out;
+  const void* z;  // gate (Bt, L, H, P) or null
   float* ws;  // workspace
-  int batch, seqlen, nheads, headdim, ngroups, nchunks, d_per_channel;
+  int batch, seqlen, nheads, headdim, ngroups, nchunks, d_per_channel, z_bf16;
   float dt_min, dt_max, sp_lo, sp_hi;
   int dt_softplus;
 };

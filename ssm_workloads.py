@@ -192,11 +192,12 @@ def decode_stream(batch=64, dim=7680, d_state=16, prefill=256, steps=1024, seed=
 
 
 def ssd_long(batch=1, seqlen=65536, nheads=80, headdim=96, ngroups=1, d_state=64, chunk_size=128,
-             seed=5, unsaturated=False):
+             seed=5, unsaturated=False, gated=False):
     """Long-context chunked SSD.  Draws: x ~ N(0,1) -> bf16 (batch, L, H, P);
     B, C ~ N(0,1) -> bf16 (batch, L, G, N); A_log ~ U[0, ln 16] (H) with
     A = -exp(A_log) stored in fp32; dt_raw ~ N(0,1) fp32 (batch, L, H);
-    dt_bias ~ N(0, 0.5) (H); D ~ N(0,1) (H).  Zero initial state."""
+    dt_bias ~ N(0, 0.5) (H); D ~ N(0,1) (H); with gated, last, a gate
+    z ~ N(0,1) -> bf16 (batch, L, H, P).  Zero initial state."""
     rng = np.random.Generator(np.random.PCG64(seed))
     x = bf16_bits(_normal(rng, (batch, seqlen, nheads, headdim)))
     B = bf16_bits(_normal(rng, (batch, seqlen, ngroups, d_state)))
@@ -205,10 +206,13 @@ def ssd_long(batch=1, seqlen=65536, nheads=80, headdim=96, ngroups=1, d_state=64
     dt_raw = _normal(rng, (batch, seqlen, nheads), 2.0 if unsaturated else 1.0)
     b_dt = _normal(rng, (nheads,), 1.0, -4.0) if unsaturated else _normal(rng, (nheads,), 0.5)
     D = _normal(rng, (nheads,))
+    arrays = dict(x=x, B=B, C=C, A=A, dt=dt_raw, dt_bias=b_dt, D=D)
+    if gated:
+        arrays["z"] = bf16_bits(_normal(rng, (batch, seqlen, nheads, headdim)))
     return Workload(
-        "ssd_long" + ("_unsat" if unsaturated else ""), "ssd",
+        "ssd_long" + ("_unsat" if unsaturated else "") + ("_gated" if gated else ""), "ssd",
         dict(batch=batch, seqlen=seqlen, nheads=nheads, headdim=headdim, ngroups=ngroups,
              d_state=d_state, chunk_size=chunk_size),
-        dict(x=x, B=B, C=C, A=A, dt=dt_raw, dt_bias=b_dt, D=D),
-        {"x", "B", "C"},
+        arrays,
+        {"x", "B", "C", "z"} if gated else {"x", "B", "C"},
         dict(dt_softplus=True, dt_min=DT_MIN, dt_max=DT_MAX))

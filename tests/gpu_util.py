@@ -100,16 +100,24 @@ def scan_oracle(w: W.Workload, *, state_in=None, cache_in=None, batches=None, ch
 
 # ---------------------------------------------------------------------- SSD
 
-def ssd_gpu(w: W.Workload, *, out_dtype=torch.float32, state_in=None, want_state=True, D_override=None):
+def ssd_gpu(w: W.Workload, *, out_dtype=torch.float32, state_in=None, want_state=True, D_override=None,
+            z_f32=False):
+    """The workload's gate z (when it has one) goes in as bf16, or as its fp32
+    widening with z_f32."""
     d = w.dims
     o = w.opts
     st = (torch.empty((d["batch"], d["nheads"], d["headdim"], d["d_state"]), dtype=torch.float32, device=DEV)
           if want_state else None)
     D = dev_tensor(w, "D") if D_override is None else torch.from_numpy(D_override).to(DEV)
+    z = None
+    if "z" in w.arrays:
+        z = dev_tensor(w, "z")
+        if z_f32:
+            z = z.float()
     out = ssm.chunk_scan_fwd(dev_tensor(w, "x"), dev_tensor(w, "dt"), dev_tensor(w, "A"), dev_tensor(w, "B"),
                              dev_tensor(w, "C"), chunk_size=d["chunk_size"], D=D, dt_bias=dev_tensor(w, "dt_bias"),
                              dt_softplus=o["dt_softplus"], dt_min=o["dt_min"], dt_max=o["dt_max"],
-                             state_in=state_in, state_out=st, out_dtype=out_dtype)
+                             state_in=state_in, state_out=st, out_dtype=out_dtype, z=z)
     torch.cuda.synchronize()
     return out, st
 
@@ -131,6 +139,7 @@ def ssd_oracle(w: W.Workload, *, heads=None, state_in=None, D_override=None, seq
         grp = np.asarray(heads) // (H // G)
         Bm, Cm = Bm[:, :, grp], Cm[:, :, grp]
     st = None if state_in is None else np.asarray(state_in, np.float64)[:, hs]
+    z = f("z")[:, :, hs] if "z" in w.arrays else None
     if sequential:
-        return O.ssd_scan_sequential(x, dt, A, Bm, Cm, D=D, state=st)
-    return O.ssd_chunk_scan(x, dt, A, Bm, Cm, D=D, state=st, chunk_size=w.dims["chunk_size"])
+        return O.ssd_scan_sequential(x, dt, A, Bm, Cm, D=D, state=st, z=z)
+    return O.ssd_chunk_scan(x, dt, A, Bm, Cm, D=D, state=st, chunk_size=w.dims["chunk_size"], z=z)

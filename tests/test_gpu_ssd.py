@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import ssm_workloads as W
-from gpu_util import DEV, check, np64, ssd_gpu, ssd_oracle
+import selective_state_space_03_amd as ssm
+from gpu_util import DEV, check, dev_tensor, np64, ssd_gpu, ssd_oracle
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -79,3 +80,58 @@ def test_ssd_long_full_size():
         check(np64(st.index_select(1, hidx)), so, TOL, "ssd full state")
         del out, st
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("seqlen", [1, 100, 129, 300, 511])
+def test_ssd_ragged_last_chunk(seqlen):
+    """L not a multiple of Q: the last chunk is shorter; its missing rows add
+    nothing and are not stored (the bytes past L stay as they were)."""
+    w = _small(seqlen=seqlen, unsaturated=True)
+    out, st = ssd_gpu(w)
+    oo, so = ssd_oracle(w)
+    check(np64(out), oo, TOL, f"ssd ragged out L={seqlen}")
+    check(np64(st), so, TOL, f"ssd ragged state L={seqlen}")
+    oo, so = ssd_oracle(w, sequential=True)
+    check(np64(out), oo, TOL, f"ssd ragged out vs sequential L={seqlen}")
+    check(np64(st), so, TOL, f"ssd ragged state vs sequential L={seqlen}")
+
+
+def test_ssd_ragged_leaves_padding_untouched():
+    """Outputs are written only for tokens of the sequence: a view of a larger
+    buffer keeps its bytes past the last token."""
+    w = _small(batch=1, seqlen=200, unsaturated=True)
+    d = w.dims
+    big = torch.full((1, 256, d["nheads"], d["headdim"]), 7.0, device=DEV)
+    view = big[:, :200]
+    o = w.opts
+    ssm.chunk_scan_fwd(dev_tensor(w, "x"), dev_tensor(w, "dt"), dev_tensor(w, "A"), dev_tensor(w, "B"),
+                       dev_tensor(w, "C"), chunk_size=d["chunk_size"], D=dev_tensor(w, "D"),
+                       dt_bias=dev_tensor(w, "dt_bias"), dt_softplus=o["dt_softplus"], dt_min=o["dt_min"],
+                       dt_max=o["dt_max"], out=view)
+    torch.cuda.synchronize()
+    assert bool((big[:, 200:] == 7.0).all())
+    oo, _ = ssd_oracle(w)
+    check(np64(view), oo, TOL, "ssd ragged into view")
+
+
+@pytest.mark.parametrize("z_f32,out_bf16", [(False, False), (True, False), (False, True)])
+def test_ssd_gate(z_f32, out_bf16):
+    """out * SiLU(z) with z in bf16 or fp32, ragged tail included."""
+    w = _small(seqlen=400, gated=True, unsaturated=True)
+    out, st = ssd_gpu(w, z_f32=z_f32, out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    oo, so = ssd_oracle(w)
+    check(np64(out), oo, TOL, "ssd gated out", out_bf16=out_bf16)
+    check(np64(st), so, TOL, "ssd gated state")
+    oo, _ = ssd_oracle(w, sequential=True)
+    check(np64(out), oo, TOL, "ssd gated out vs sequential", out_bf16=out_bf16)
+
+
+def test_ssd_gate_full_size():
+    """Gated long-context scan at full size, heads 0 and 79 against the oracle."""
+    w = W.ssd_long(gated=True)
+    heads = [0, 79]
+    oo, so = ssd_oracle(w, heads=heads)
+    out, st = ssd_gpu(w, out_dtype=torch.bfloat16)
+    hidx = torch.tensor(heads, device=DEV)
+    check(np64(out.index_select(2, hidx)), oo, TOL, "ssd gated full out", out_bf16=True)
+    check(np64(st.index_select(1, hidx)), so, TOL, "ssd gated full state")
