@@ -18,7 +18,7 @@ Prints ONE JSON line.  Besides the throughput it carries
   the algorithmic work per unit);
 * cpu_baseline: the float64 oracle on the same workload on this host's CPU;
 * parts: the other entry points at their workloads (bulk scan, 8-layer decode
-  step, chunked SSD), each with its own kernel roofline.
+  step, chunked SSD, SSD-form decode step), each with its own kernel roofline.
 Counters of HBM traffic come from rocprofv3 runs recorded in profiles/; they
 are reported only while the kernel sources still hash to the recorded value.
 """
@@ -60,7 +60,7 @@ def parse():
                     help="time segments per sequence for the scan (0: the library's choice)")
     ap.add_argument("--no-parts", action="store_true", help="skip the decode / SSD / other-scan lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--only", choices=("prefill", "bulk", "decode", "ssd", "copy"), default=None,
+    ap.add_argument("--only", choices=("prefill", "bulk", "decode", "ssd", "ssd_decode", "copy"), default=None,
                     help="run just this workload's timed loop, no JSON line (for profiler runs); 'copy' "
                          "copies 1 GiB device to device, the calibration for the HBM byte counters")
     return ap.parse_args()
@@ -221,12 +221,39 @@ def decode_calls(torch, ssm, W, layers, ring, device, stream=None):
     return calls, dict(batch=Bt, dim=E, d_state=N, layers=layers, bytes=byts)
 
 
-def decode_graph(torch, ssm, W, device, layers=8, ring=16):
+def ssd_decode_calls(torch, ssm, W, layers, ring, device, stream=None):
+    """Decode step of the multi-head scan at serving size: batch 64, 80 heads x
+    96, 1 group, N 64, bf16 x/B/C/out, fp32 state (126 MB per state set);
+    `layers` state sets so the states stream from HBM."""
+    w = W.ssd_decode(steps=ring)
+    d = w.dims
+    X, R, Bm, Cm = (dev_tensor(torch, w, k, device) for k in ("x", "dt", "B", "C"))
+    A, D, db = (dev_tensor(torch, w, k, device) for k in ("A", "D", "dt_bias"))
+    Bt, H, P, G, N = (d[k] for k in ("batch", "nheads", "headdim", "ngroups", "d_state"))
+    g = torch.Generator(device="cpu").manual_seed(45)
+    states = [torch.randn((Bt, H, P, N), generator=g).to(device) for _ in range(layers)]
+    outs = [torch.empty((Bt, H, P), dtype=torch.bfloat16, device=device) for _ in range(layers)]
+    xs = [X[:, s].contiguous() for s in range(ring)]
+    rs = [R[:, s].contiguous() for s in range(ring)]
+    bs = [Bm[:, s].contiguous() for s in range(ring)]
+    cs = [Cm[:, s].contiguous() for s in range(ring)]
+    calls = []
+    for s in range(ring):
+        for l in range(layers):
+            calls.append(ssm.chunk_decode_step(xs[s], rs[s], A, bs[s], cs[s], states[l], D=D, dt_bias=db,
+                                               dt_min=w.opts["dt_min"], dt_max=w.opts["dt_max"], out=outs[l],
+                                               stream=stream, prepare=True))
+    # per call: state r+w (fp32), x and out (bf16), dt (fp32), B and C (bf16), A/D/bias
+    byts = 2 * 4 * Bt * H * P * N + 2 * 2 * Bt * H * P + 4 * Bt * H + 2 * 2 * Bt * G * N + 4 * 3 * H
+    return calls, dict(batch=Bt, nheads=H, headdim=P, ngroups=G, d_state=N, layers=layers, bytes=byts)
+
+
+def decode_graph(torch, ssm, W, device, layers=8, ring=16, make=None):
     """The decode steps of `ring` tokens through `layers` state sets, captured
     once in a HIP graph (as a serving loop would run them): replays time the
     kernels without the Python launch cost."""
     stream = torch.cuda.Stream(device)
-    calls, cfg = decode_calls(torch, ssm, W, layers, ring, device, stream=stream)
+    calls, cfg = (make or decode_calls)(torch, ssm, W, layers, ring, device, stream=stream)
     stream.wait_stream(torch.cuda.current_stream(device))
     for c in calls:  # warm-up outside the graph
         c.run()
@@ -375,6 +402,12 @@ def main():
         per_call = graph_time(torch, graph, launches, a.steps)
         log(f"decode: {per_call * 1e3:.2f} us per layer-step ({launches} launches per graph, {a.steps} replays)")
         return
+    if a.only == "ssd_decode":
+        graph, launches, cfg = decode_graph(torch, ssm, W, dev, layers=4, ring=8, make=ssd_decode_calls)
+        per_call = graph_time(torch, graph, launches, a.steps)
+        log(f"ssd_decode: {per_call * 1e3:.2f} us per step ({launches} launches per graph, {a.steps} replays), "
+            f"{cfg['bytes'] / (per_call * 1e-3) / 1e9:.0f} GB/s")
+        return
     if a.only == "ssd":
         calls, cfg = ssd_calls(torch, ssm, W, dev)
         wall, kmean, _ = timed_loop(torch, ssm, calls, a.steps, a.warmup, per_launch=False)
@@ -465,6 +498,17 @@ def main():
             "ms_per_call": round(wall4, 4), "roofline": r4,
             "config": {k: cfg4[k] for k in ("batch", "seq_len", "nheads", "headdim", "d_state", "chunk_size")}}
         del c4
+        torch.cuda.empty_cache()
+
+        log("part: SSD-form decode step (4 state sets, replayed from a HIP graph)")
+        graph, launches, cfg5 = decode_graph(torch, ssm, W, dev, layers=4, ring=8, make=ssd_decode_calls)
+        per_call = graph_time(torch, graph, launches, 8)
+        parts["chunk_decode_step"] = {
+            "tokens_per_s": round(cfg5["batch"] / (per_call * 1e-3), 1), "us_per_step": round(per_call * 1e3, 2),
+            "roofline": roof_hbm(cfg5["bytes"], per_call, recorded_traffic("ssd_decode")),
+            "timing": "HIP graph of 8 tokens x 4 state sets, events around 8 replays",
+            "config": {k: cfg5[k] for k in ("batch", "nheads", "headdim", "ngroups", "d_state", "layers")}}
+        del graph
         torch.cuda.empty_cache()
         out["parts"] = parts
 

@@ -227,19 +227,67 @@ ssm_status_t ssm_chunk_scan_fwd(const ssm_chunk_params_t *p, void *stream);
 size_t ssm_chunk_scan_workspace_size(const ssm_chunk_params_t *p);
 ssm_status_t ssm_chunk_scan_check(const ssm_chunk_params_t *p);
 
+/* ------------------------------------------------------------------------
+ * One decode step of the multi-head scan, in place (page "What is the Mamba
+ * model?", section "chunkscan": the state that the chunked scan passes from
+ * chunk to chunk, advanced by a chunk of one token).  For each (b, h):
+ *   dt = clip(softplus(dt_raw[b,h] + dt_bias[h]), dt_min, dt_max)   (softplus
+ *        skipped when dt_softplus == 0)
+ *   state[b,h,p,n] <- e^{dt A_h} state[b,h,p,n] + dt x[b,h,p] B[b,g,n]
+ *   out[b,h,p] = (sum_n C[b,g,n] state[b,h,p,n] + D x[b,h,p]) * SiLU(z[b,h,p])
+ * with g = h / (H / G) and the gate only when z != NULL.
+ *   x         (Bt, H, P) x_dtype
+ *   dt        (Bt, H) f32 raw;  dt_bias (H) f32 or NULL;  A (H) f32
+ *   B, C      (Bt, G, N) bc_dtype
+ *   D         (H) f32 (d_per_channel == 0) or (H, P) f32 or NULL
+ *   z         (Bt, H, P) z_dtype or NULL
+ *   state     (Bt, H, P, N) f32, read then overwritten (the layout of the
+ *             chunked scan's state_in / state_out)
+ *   out       (Bt, H, P) out_dtype; must not overlap any input
+ * The result equals ssm_chunk_scan_fwd with L = 1 and state_in = state_out =
+ * state.  state must be 16-byte aligned; B and C aligned to 8 elements (32
+ * bytes in f32, 16 in bf16).  Supported: N in {16, 32, 64, 128};
+ * batch * H * P < 2^31.  All dtypes f32 or bf16.
+ * ---------------------------------------------------------------------- */
+typedef struct ssm_chunk_decode_params {
+  uint32_t struct_size; /* = sizeof(ssm_chunk_decode_params_t) */
+  int32_t batch, nheads, headdim, ngroups, d_state;
+  const void *x;
+  int32_t x_dtype;
+  const float *dt;
+  const float *dt_bias;
+  int32_t dt_softplus;
+  float dt_min, dt_max;
+  const float *A;
+  const void *B;
+  const void *C;
+  int32_t bc_dtype;
+  const float *D;
+  int32_t d_per_channel;
+  const void *z;
+  int32_t z_dtype;
+  float *state;
+  void *out;
+  int32_t out_dtype;
+} ssm_chunk_decode_params_t;
+
+ssm_status_t ssm_chunk_decode_step(const ssm_chunk_decode_params_t *p, void *stream);
+ssm_status_t ssm_chunk_decode_check(const ssm_chunk_decode_params_t *p);
+
 /* ------------------------------------------------------------------------ */
 const char *ssm_status_string(int32_t status);
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char *ssm_last_error(void);
 int32_t ssm_abi_version(void);
-/* sizeof of a params struct: which = 0 scan, 1 decode, 2 chunk; 0 otherwise. */
+/* sizeof of a params struct: which = 0 scan, 1 decode, 2 chunk, 3 chunk
+ * decode; 0 otherwise. */
 size_t ssm_params_sizeof(int32_t which);
 
 /* Kernel timing for measurement tools.  start and stop are hipEvent_t handles
  * owned by the caller (both NULL switches timing off).  While set, each entry
  * point called on this thread records start on its stream right before the
  * launch of its main kernel (the full-segment scan kernel of ssm_scan_fwd, the
- * only kernel of the other two) and stop right after it, so
+ * only kernel of the others) and stop right after it, so
  * hipEventElapsedTime(start, stop) is that kernel's duration.  The events are
  * only recorded, never created, synchronised or destroyed by the library. */
 void ssm_set_timing_events(void *start, void *stop);

@@ -58,10 +58,21 @@ class ChunkParams(ctypes.Structure):
     ]
 
 
+class ChunkDecodeParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("batch", _i32), ("nheads", _i32), ("headdim", _i32), ("ngroups", _i32),
+        ("d_state", _i32), ("x", _vp), ("x_dtype", _i32), ("dt", _vp), ("dt_bias", _vp), ("dt_softplus", _i32),
+        ("dt_min", _f32), ("dt_max", _f32), ("A", _vp), ("B", _vp), ("C", _vp), ("bc_dtype", _i32),
+        ("D", _vp), ("d_per_channel", _i32), ("z", _vp), ("z_dtype", _i32), ("state", _vp), ("out", _vp),
+        ("out_dtype", _i32),
+    ]
+
+
 EXPORTED = [
     "ssm_scan_fwd", "ssm_scan_workspace_size", "ssm_scan_check",
     "ssm_decode_step", "ssm_decode_check",
     "ssm_chunk_scan_fwd", "ssm_chunk_scan_workspace_size", "ssm_chunk_scan_check",
+    "ssm_chunk_decode_step", "ssm_chunk_decode_check",
     "ssm_status_string", "ssm_last_error", "ssm_abi_version", "ssm_params_sizeof", "ssm_set_timing_events",
 ]
 
@@ -92,6 +103,10 @@ def lib() -> ctypes.CDLL:
     L.ssm_chunk_scan_check.restype = _i32
     L.ssm_chunk_scan_workspace_size.argtypes = [ctypes.POINTER(ChunkParams)]
     L.ssm_chunk_scan_workspace_size.restype = ctypes.c_size_t
+    L.ssm_chunk_decode_step.argtypes = [ctypes.POINTER(ChunkDecodeParams), _vp]
+    L.ssm_chunk_decode_step.restype = _i32
+    L.ssm_chunk_decode_check.argtypes = [ctypes.POINTER(ChunkDecodeParams)]
+    L.ssm_chunk_decode_check.restype = _i32
     L.ssm_status_string.argtypes = [_i32]
     L.ssm_status_string.restype = ctypes.c_char_p
     L.ssm_last_error.argtypes = []
@@ -102,7 +117,7 @@ def lib() -> ctypes.CDLL:
     L.ssm_params_sizeof.restype = ctypes.c_size_t
     L.ssm_set_timing_events.argtypes = [_vp, _vp]
     L.ssm_set_timing_events.restype = None
-    for i, st in enumerate((ScanParams, DecodeParams, ChunkParams)):
+    for i, st in enumerate((ScanParams, DecodeParams, ChunkParams, ChunkDecodeParams)):
         if L.ssm_params_sizeof(i) != ctypes.sizeof(st):
             raise RuntimeError(f"ctypes mirror of params struct {i} does not match the library")
     _lib = L
@@ -324,4 +339,42 @@ def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size=128, D=None, dt_bias=None, dt_s
     p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     call = Call(L_.ssm_chunk_scan_fwd, p, _stream(dev, stream), out, (x, dt, A, B, C, D, dt_bias, state_in,
                                                                      state_out, workspace, z))
+    return call if prepare else call.run()
+
+
+def chunk_decode_step(x, dt, A, B, C, state, *, D=None, dt_bias=None, dt_softplus=True, dt_min=None, dt_max=None,
+                      z=None, out=None, out_dtype=None, stream=None, prepare=False):
+    """One decode step of the multi-head scan (ssm_chunk_decode_step): x (batch, H, P), dt (batch, H),
+    B/C (batch, G, N), state (batch, H, P, N) f32 updated in place.  Returns out (batch, H, P), or
+    with prepare=True a Call that enqueues this same step again on each run()."""
+    L_ = lib()
+    batch, nheads, headdim = x.shape
+    ngroups, d_state = B.shape[1], B.shape[2]
+    dev = x.device
+    if out is None:
+        out = torch.empty((batch, nheads, headdim), dtype=out_dtype or x.dtype, device=dev)
+    f32 = torch.float32
+    p = ChunkDecodeParams()
+    p.struct_size = ctypes.sizeof(ChunkDecodeParams)
+    p.batch, p.nheads, p.headdim, p.ngroups, p.d_state = batch, nheads, headdim, ngroups, d_state
+    p.x = _ptr(x, "x", (batch, nheads, headdim), device=dev)
+    p.x_dtype = _code(x, "x")
+    p.dt = _ptr(dt, "dt", (batch, nheads), f32, dev)
+    p.dt_bias = _ptr(dt_bias, "dt_bias", (nheads,), f32, dev)
+    p.dt_softplus = 1 if dt_softplus else 0
+    p.dt_min = _bound(dt_min, -math.inf)
+    p.dt_max = _bound(dt_max, math.inf)
+    p.A = _ptr(A, "A", (nheads,), f32, dev)
+    p.B = _ptr(B, "B", (batch, ngroups, d_state), device=dev)
+    p.C = _ptr(C, "C", (batch, ngroups, d_state), B.dtype, dev)
+    p.bc_dtype = _code(B, "B")
+    if D is not None:
+        p.d_per_channel = 1 if D.dim() == 2 else 0
+        p.D = _ptr(D, "D", (nheads, headdim) if D.dim() == 2 else (nheads,), f32, dev)
+    p.z = _ptr(z, "z", (batch, nheads, headdim), device=dev)
+    p.z_dtype = _code(z, "z") if z is not None else 0
+    p.state = _ptr(state, "state", (batch, nheads, headdim, d_state), f32, dev)
+    p.out = _ptr(out, "out", (batch, nheads, headdim), device=dev)
+    p.out_dtype = _code(out, "out")
+    call = Call(L_.ssm_chunk_decode_step, p, _stream(dev, stream), out, (x, dt, A, B, C, state, D, dt_bias, z))
     return call if prepare else call.run()

@@ -305,6 +305,50 @@ ssm_status_t chunk_check(const ssm_chunk_params_t* p) {
   return SSM_OK;
 }
 
+// ---------------------------------------------------------------- SSD decode
+
+ssm_status_t chunk_decode_check(const ssm_chunk_decode_params_t* p) {
+  if (!p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "params");
+  if (p->struct_size != sizeof(ssm_chunk_decode_params_t))
+    return fail(SSM_ERR_INVALID_ARG, "%s does not match this library", "struct_size");
+  if (p->batch < 0 || p->nheads <= 0 || p->headdim <= 0 || p->ngroups <= 0 || p->d_state <= 0)
+    return fail(SSM_ERR_INVALID_ARG, "%s: negative or zero size", "dims");
+  if (p->nheads % p->ngroups != 0) return fail(SSM_ERR_INVALID_ARG, "%s", "nheads must be a multiple of ngroups");
+  if (p->d_state != 16 && p->d_state != 32 && p->d_state != 64 && p->d_state != 128)
+    return fail(SSM_ERR_UNSUPPORTED, "%s must be 16, 32, 64 or 128", "d_state");
+  if (!valid_dtype(p->x_dtype) || !valid_dtype(p->bc_dtype) || !valid_dtype(p->out_dtype) ||
+      (p->z && !valid_dtype(p->z_dtype)))
+    return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "x/bc/out/z_dtype");
+  if (!p->A) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "A");
+  ssm_status_t s = check_dt_bounds(p->dt_min, p->dt_max);
+  if (s != SSM_OK) return s;
+  const size_t Bt = p->batch, H = p->nheads, P = p->headdim, G = p->ngroups, N = p->d_state;
+  const size_t rows = Bt * H * P;
+  if (rows > 0x7fffffffULL) return fail(SSM_ERR_UNSUPPORTED, "%s too large", "batch*nheads*headdim");
+  if (Bt == 0) return SSM_OK;
+  if (!p->x || !p->out || !p->B || !p->C || !p->dt || !p->state)
+    return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "x/out/B/C/dt/state");
+  if (reinterpret_cast<uintptr_t>(p->state) & 15)
+    return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "state");
+  if ((reinterpret_cast<uintptr_t>(p->B) | reinterpret_cast<uintptr_t>(p->C)) & (p->bc_dtype == SSM_BF16 ? 15 : 31))
+    return fail(SSM_ERR_INVALID_ARG, "%s must be aligned to 8 elements", "B/C");
+  const Range out{p->out, rows * esize(p->out_dtype)};
+  const Range ins[] = {
+      {p->x, rows * esize(p->x_dtype)},
+      {p->dt, Bt * H * 4},
+      {p->dt_bias, p->dt_bias ? H * 4 : 0},
+      {p->A, H * 4},
+      {p->B, Bt * G * N * esize(p->bc_dtype)},
+      {p->C, Bt * G * N * esize(p->bc_dtype)},
+      {p->D, p->D ? (p->d_per_channel ? H * P * 4 : H * 4) : 0},
+      {p->z, p->z ? rows * esize(p->z_dtype) : 0},
+      {p->state, rows * N * 4},
+  };
+  for (const Range& r : ins)
+    if (overlaps(out, r)) return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "out");
+  return SSM_OK;
+}
+
 ssm_status_t hip_status(hipError_t e) {
   if (e == hipSuccess) return ok();
   return fail(SSM_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
@@ -462,6 +506,45 @@ ssm_status_t ssm_chunk_scan_fwd(const ssm_chunk_params_t* p, void* stream) {
   return hip_status(ssm::launch_chunk(l, static_cast<hipStream_t>(stream)));
 }
 
+ssm_status_t ssm_chunk_decode_check(const ssm_chunk_decode_params_t* p) {
+  const ssm_status_t s = chunk_decode_check(p);
+  return s == SSM_OK ? ok() : s;
+}
+
+ssm_status_t ssm_chunk_decode_step(const ssm_chunk_decode_params_t* p, void* stream) {
+  const ssm_status_t s = chunk_decode_check(p);
+  if (s != SSM_OK) return s;
+  if (p->batch == 0) return ok();
+  ssm::ChunkDecodeLaunch l{};
+  ssm::ChunkDecodeKernelArgs& k = l.k;
+  k.x = p->x;
+  k.dt = p->dt;
+  k.dt_bias = p->dt_bias;
+  k.A = p->A;
+  k.B = p->B;
+  k.C = p->C;
+  k.D = p->D;
+  k.z = p->z;
+  k.state = p->state;
+  k.out = p->out;
+  k.rows = static_cast<unsigned>(static_cast<size_t>(p->batch) * p->nheads * p->headdim);
+  k.nheads = p->nheads;
+  k.headdim = p->headdim;
+  k.ngroups = p->ngroups;
+  k.heads_per_group = p->nheads / p->ngroups;
+  k.d_per_channel = p->d_per_channel ? 1 : 0;
+  k.z_bf16 = p->z && p->z_dtype == SSM_BF16 ? 1 : 0;
+  k.dt_min = p->dt_min;
+  k.dt_max = p->dt_max;
+  softplus_thresholds(p->dt_min, p->dt_max, &k.sp_lo, &k.sp_hi);
+  k.dt_softplus = p->dt_softplus ? 1 : 0;
+  l.x_dtype = p->x_dtype;
+  l.bc_dtype = p->bc_dtype;
+  l.out_dtype = p->out_dtype;
+  l.d_state = p->d_state;
+  return hip_status(ssm::launch_chunk_decode(l, static_cast<hipStream_t>(stream)));
+}
+
 const char* ssm_status_string(int32_t status) {
   switch (status) {
     case SSM_OK: return "SSM_OK";
@@ -487,6 +570,7 @@ size_t ssm_params_sizeof(int32_t which) {
     case 0: return sizeof(ssm_scan_params_t);
     case 1: return sizeof(ssm_decode_params_t);
     case 2: return sizeof(ssm_chunk_params_t);
+    case 3: return sizeof(ssm_chunk_decode_params_t);
     default: return 0;
   }
 }

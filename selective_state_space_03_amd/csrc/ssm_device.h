@@ -75,6 +75,20 @@ __device__ __forceinline__ float dt_softplus_clip(float pre, float lo, float hi,
 
 __device__ __forceinline__ float dt_clip(float pre, float lo, float hi) { return fminf(fmaxf(pre, lo), hi); }
 
+// Non-temporal 16-byte load and store, for data touched once per launch (a
+// recurrent state streamed through a decode step).
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_stream(const float4* p) {
+  const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_stream(float4* p, float4 v) {
+  const v4f w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<v4f*>(p));
+}
+
 // Make a wave-uniform value provably uniform to the compiler (SGPR).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

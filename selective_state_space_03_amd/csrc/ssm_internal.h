@@ -147,4 +147,29 @@ struct ChunkLaunch {
 size_t chunk_workspace_bytes(int batch, int seqlen, int nheads, int headdim, int ngroups);
 hipError_t launch_chunk(const ChunkLaunch& l, hipStream_t stream);
 
+// ---- SSD-form decode step ------------------------------------------------
+struct ChunkDecodeKernelArgs {
+  const void* x;        // (Bt, H, P)
+  const float* dt;      // (Bt, H) raw
+  const float* dt_bias; // (H) or null
+  const float* A;       // (H)
+  const void* B;        // (Bt, G, N)
+  const void* C;
+  const float* D;       // (H) or (H, P) or null
+  const void* z;        // (Bt, H, P) or null
+  float* state;         // (Bt, H, P, N), in place
+  void* out;            // (Bt, H, P)
+  unsigned rows;        // Bt * H * P
+  int nheads, headdim, ngroups, heads_per_group, d_per_channel, z_bf16;
+  float dt_min, dt_max, sp_lo, sp_hi;
+  int dt_softplus;
+};
+
+struct ChunkDecodeLaunch {
+  ChunkDecodeKernelArgs k;
+  int x_dtype, bc_dtype, out_dtype, d_state;
+};
+
+hipError_t launch_chunk_decode(const ChunkDecodeLaunch& l, hipStream_t stream);
+
 }  // namespace ssm

@@ -216,3 +216,17 @@ def ssd_long(batch=1, seqlen=65536, nheads=80, headdim=96, ngroups=1, d_state=64
         arrays,
         {"x", "B", "C", "z"} if gated else {"x", "B", "C"},
         dict(dt_softplus=True, dt_min=DT_MIN, dt_max=DT_MAX))
+
+
+def ssd_decode(batch=64, nheads=80, headdim=96, ngroups=1, d_state=64, steps=1, seed=9, gated=False,
+               unsaturated=True):
+    """Batched decode steps of the multi-head scan: the draws of ssd_long with
+    L = steps tokens per sequence (x, B, C, z in bf16; dt_raw, dt_bias, A, D in
+    fp32), plus a starting state state0 ~ N(0,1) fp32 (batch, H, P, N) from a
+    generator of its own (seed + 1)."""
+    w = ssd_long(batch=batch, seqlen=steps, nheads=nheads, headdim=headdim, ngroups=ngroups, d_state=d_state,
+                 seed=seed, unsaturated=unsaturated, gated=gated)
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    w.arrays["state0"] = _normal(rng, (batch, nheads, headdim, d_state))
+    w.name = "ssd_decode" + ("_gated" if gated else "")
+    return w

@@ -128,8 +128,9 @@ def ssd_oracle(w: W.Workload, *, heads=None, state_in=None, D_override=None, seq
     f = w.f64
     hs = slice(None) if heads is None else heads
     x = f("x")[:, :, hs]
-    dt = O.compute_dt(f("dt")[:, :, hs], f("dt_bias")[hs], float(o["dt_min"]), float(o["dt_max"]),
-                      use_softplus=o["dt_softplus"])
+    bias = f("dt_bias")
+    dt = O.compute_dt(f("dt")[:, :, hs], None if bias is None else bias[hs], float(o["dt_min"]),
+                      float(o["dt_max"]), use_softplus=o["dt_softplus"])
     A = f("A")[hs]
     D = (f("D") if D_override is None else np.asarray(D_override, np.float64))[hs]
     Bm, Cm = f("B"), f("C")
@@ -143,3 +144,27 @@ def ssd_oracle(w: W.Workload, *, heads=None, state_in=None, D_override=None, seq
     if sequential:
         return O.ssd_scan_sequential(x, dt, A, Bm, Cm, D=D, state=st, z=z)
     return O.ssd_chunk_scan(x, dt, A, Bm, Cm, D=D, state=st, chunk_size=w.dims["chunk_size"], z=z)
+
+
+# ---------------------------------------------------------------------- SSD decode
+
+def ssd_decode_gpu(w: W.Workload, state, t=0, *, out_dtype=torch.float32, x_f32=False, bc_f32=False, z_f32=False,
+                   D_override=None, stream=None):
+    """One ssm_chunk_decode_step on token t of the workload; state (Bt, H, P, N)
+    fp32 on the device is updated in place.  x / B, C / z go in as bf16 or
+    widened to fp32."""
+    o = w.opts
+
+    def tok(key, f32):
+        a = dev_tensor(w, key)
+        if a is None:
+            return None
+        a = a[:, t].contiguous()
+        return a.float() if f32 else a
+
+    D = dev_tensor(w, "D") if D_override is None else torch.from_numpy(D_override).to(DEV)
+    out = ssm.chunk_decode_step(tok("x", x_f32), tok("dt", False), dev_tensor(w, "A"), tok("B", bc_f32),
+                                tok("C", bc_f32), state, D=D, dt_bias=dev_tensor(w, "dt_bias"),
+                                dt_softplus=o["dt_softplus"], dt_min=o["dt_min"], dt_max=o["dt_max"],
+                                z=tok("z", z_f32), out_dtype=out_dtype, stream=stream)
+    return out

@@ -49,6 +49,7 @@ def test_struct_layouts_and_version(L):
     assert L.ssm_params_sizeof(0) == ctypes.sizeof(binding.ScanParams)
     assert L.ssm_params_sizeof(1) == ctypes.sizeof(binding.DecodeParams)
     assert L.ssm_params_sizeof(2) == ctypes.sizeof(binding.ChunkParams)
+    assert L.ssm_params_sizeof(3) == ctypes.sizeof(binding.ChunkDecodeParams)
     assert L.ssm_params_sizeof(7) == 0
     assert L.ssm_status_string(3) == b"SSM_ERR_WORKSPACE"
 
@@ -186,6 +187,54 @@ def test_chunk_validation(L):
     assert L.ssm_chunk_scan_fwd(ctypes.byref(_chunk(d_state=16)), None) == 2
     # a sequence that is not a whole number of chunks is accepted
     assert L.ssm_chunk_scan_check(ctypes.byref(_chunk(seqlen=1000))) == 0, L.ssm_last_error()
+
+
+def _cdec(**kw):
+    from selective_state_space_03_amd import binding as b
+
+    p = b.ChunkDecodeParams()
+    p.struct_size = ctypes.sizeof(b.ChunkDecodeParams)
+    p.batch, p.nheads, p.headdim, p.ngroups, p.d_state = 64, 80, 96, 1, 64
+    p.x, p.dt, p.A, p.B, p.C, p.state, p.out = (_addr(i) for i in range(1, 8))
+    p.x_dtype = p.bc_dtype = p.out_dtype = 1
+    p.dt_softplus = 1
+    p.dt_min, p.dt_max = 1e-3, 0.1
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_chunk_decode_validation(L):
+    assert L.ssm_chunk_decode_check(ctypes.byref(_cdec())) == 0, L.ssm_last_error()
+    for n in (16, 32, 128):
+        assert L.ssm_chunk_decode_check(ctypes.byref(_cdec(d_state=n))) == 0, (n, L.ssm_last_error())
+    cases = {
+        "struct_size": (_cdec(struct_size=8), 1),
+        "groups": (_cdec(ngroups=3), 1),
+        "d_state": (_cdec(d_state=48), 2),
+        "d_state_256": (_cdec(d_state=256), 2),
+        "dtype": (_cdec(x_dtype=5), 1),
+        "z_dtype": (_cdec(z=_addr(8), z_dtype=3), 1),
+        "null_A": (_cdec(A=None), 1),
+        "null_state": (_cdec(state=None), 1),
+        "state_align": (_cdec(state=_addr(6) + 4), 1),
+        "bc_align_bf16": (_cdec(B=_addr(4) + 8), 1),
+        "bc_align_f32": (_cdec(bc_dtype=0, C=_addr(5) + 16), 1),
+        "out_over_state": (_cdec(out=_addr(6) + 256), 1),
+        "out_over_z": (_cdec(z=_addr(8), out=_addr(8) + 2), 1),
+        "dt_nan": (_cdec(dt_min=math.nan), 1),
+        "dt_order": (_cdec(dt_min=1.0, dt_max=0.5), 1),
+        "too_many_rows": (_cdec(batch=1 << 20, nheads=64, headdim=64), 2),
+    }
+    for name, (p, want) in cases.items():
+        assert L.ssm_chunk_decode_check(ctypes.byref(p)) == want, (name, L.ssm_last_error())
+    assert L.ssm_last_error() != b""
+    # batch 0 is a no-op that needs no buffers
+    assert L.ssm_chunk_decode_step(ctypes.byref(_cdec(batch=0, x=None, state=None, out=None)), None) == 0
+    assert L.ssm_chunk_decode_step(ctypes.byref(_cdec(d_state=48)), None) == 2
+    # aligned to 8 elements is enough for B/C
+    assert L.ssm_chunk_decode_check(ctypes.byref(_cdec(B=_addr(4) + 16, C=_addr(5) + 16))) == 0
+    assert L.ssm_chunk_decode_check(ctypes.byref(_cdec(bc_dtype=0, B=_addr(4) + 32))) == 0
 
 
 def test_binding_refuses_cpu_tensors(L):

@@ -95,3 +95,50 @@ def test_chunk_scan_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, out_ref) and torch.equal(st, st_ref)
+
+
+def test_chunk_scan_gated_ragged_graph_replays():
+    w = W.ssd_long(seqlen=300, nheads=4, headdim=32, gated=True)
+    o = w.opts
+    x, dtr, A, B, C, D, db, z = (dev_tensor(w, k) for k in ("x", "dt", "A", "B", "C", "D", "dt_bias", "z"))
+    kw = dict(chunk_size=128, D=D, dt_bias=db, dt_min=o["dt_min"], dt_max=o["dt_max"], z=z)
+    st_ref = torch.empty((1, 4, 32, 64), dtype=torch.float32, device=DEV)
+    out_ref = ssm.chunk_scan_fwd(x, dtr, A, B, C, state_out=st_ref, out_dtype=torch.bfloat16, **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream(DEV)
+    st = torch.empty_like(st_ref)
+    out = torch.empty_like(out_ref)
+    call = ssm.chunk_scan_fwd(x, dtr, A, B, C, state_out=st, out=out, stream=stream, prepare=True, **kw)
+    g = _capture(call, stream)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        st.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_ref) and torch.equal(st, st_ref)
+
+
+def test_chunk_decode_graph_replays():
+    w = W.ssd_decode(batch=4, nheads=8, headdim=32, ngroups=2, d_state=64, gated=True)
+    o = w.opts
+    tok = lambda k: dev_tensor(w, k)[:, 0].contiguous()
+    x, dtr, B, C, z = (tok(k) for k in ("x", "dt", "B", "C", "z"))
+    A, D, db = (dev_tensor(w, k) for k in ("A", "D", "dt_bias"))
+    st0 = torch.from_numpy(w.arrays["state0"]).to(DEV)
+    kw = dict(D=D, dt_bias=db, dt_min=o["dt_min"], dt_max=o["dt_max"], z=z)
+    st_ref = st0.clone()
+    out_ref = ssm.chunk_decode_step(x, dtr, A, B, C, st_ref, out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream(DEV)
+    st = st0.clone()
+    out = torch.empty_like(out_ref)
+    call = ssm.chunk_decode_step(x, dtr, A, B, C, st, out=out, stream=stream, prepare=True, **kw)
+    g = _capture(call, stream)
+    for _ in range(3):
+        st.copy_(st0)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_ref) and torch.equal(st, st_ref)
