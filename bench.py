@@ -19,8 +19,8 @@ Prints ONE JSON line.  Besides the throughput it carries
 * cpu_baseline: the float64 oracle on the same workload on this host's CPU;
 * parts: the other entry points at their workloads (bulk scan, 8-layer decode
   step, chunked SSD, SSD-form decode step), each with its own kernel roofline.
-Counters of HBM traffic come from rocprofv3 runs recorded in profiles/; they
-are reported only while the kernel sources still hash to the recorded value.
+Counters of HBM traffic come from rocprofv3 runs recorded in profiles/; each
+is reported only while its kernel's sources still hash to the recorded value.
 """
 from __future__ import annotations
 
@@ -72,20 +72,32 @@ def log(msg):
 
 # --------------------------------------------------------------------- helpers
 
-def sources_digest():
-    """sha256 over the HIP sources; a recorded counter profile is used only while it matches."""
+# The HIP sources each recorded counter profile depends on (its kernel's own
+# files and the shared device header); a profile is used only while they hash
+# to the recorded value.
+SCAN_SOURCES = ("scan_fused.hip", "scan_fused_impl.h", "scan_xy_bb.hip", "scan_xy_bf.hip", "scan_xy_fb.hip",
+                "scan_xy_ff.hip")
+KERNEL_SOURCES = {
+    "scan_main_prefill": SCAN_SOURCES, "scan_pass1_prefill": SCAN_SOURCES,
+    "scan_main_bulk": SCAN_SOURCES, "scan_pass1_bulk": SCAN_SOURCES,
+    "decode": ("decode_step.hip",), "ssd": ("ssd_chunk.hip",), "ssd_decode": ("ssd_decode.hip",),
+}
+
+
+def sources_digest(kernel_key):
+    """sha256 over the HIP sources of one kernel (plus the shared device header)."""
     d = os.path.join(ROOT, "selective_state_space_03_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(KERNEL_SOURCES[kernel_key] + ("ssm_device.h",)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
 def recorded_traffic(kernel_key):
     """HBM bytes per launch from profiles/pmc_traffic.txt (FETCH_SIZE and
-    WRITE_SIZE per dispatch, each scaled by the copy-kernel calibration), or None."""
+    WRITE_SIZE per dispatch, each scaled by the copy-kernel calibration), or
+    None when none is recorded for the kernel's current sources."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -97,7 +109,7 @@ def recorded_traffic(kernel_key):
                 continue
             k, v = line.split("=", 1)
             rec[k.strip()] = v.strip()
-    if rec.get("sources_sha256") != sources_digest():
+    if rec.get(f"{kernel_key}.sources") != sources_digest(kernel_key):
         return None
     try:
         fetch = float(rec[f"{kernel_key}.fetch_kib"]) * float(rec["copy.fetch_factor"])
