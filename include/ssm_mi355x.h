@@ -274,13 +274,38 @@ typedef struct ssm_chunk_decode_params {
 ssm_status_t ssm_chunk_decode_step(const ssm_chunk_decode_params_t *p, void *stream);
 ssm_status_t ssm_chunk_decode_check(const ssm_chunk_decode_params_t *p);
 
+/* ------------------------------------------------------------------------
+ * A projection of the layer (page "Axon-SSM: selective state space model",
+ * section "Algorithm": in_proj D -> 2E and out_proj E -> D), no bias:
+ *   out[r, o] = sum_i x[r, i] * weight[o, i]
+ *   x       (rows, in_features) x_dtype: bf16 is used as it is; f32 enters the
+ *           matrix cores as a bf16 pair (value and remainder), which keeps
+ *           about 16 mantissa bits
+ *   weight  (out_features, in_features) bf16 (the (out, in) layout of a weight)
+ *   out     (rows, out_features) out_dtype; must not overlap x or weight
+ * fp32 accumulation.  x, weight and out must be 16-byte aligned;
+ * in_features % 8 == 0; out_features % 4 == 0.
+ * ---------------------------------------------------------------------- */
+typedef struct ssm_linear_params {
+  uint32_t struct_size; /* = sizeof(ssm_linear_params_t) */
+  int32_t rows, in_features, out_features;
+  const void *x;
+  int32_t x_dtype;
+  const void *weight;
+  void *out;
+  int32_t out_dtype;
+} ssm_linear_params_t;
+
+ssm_status_t ssm_linear_fwd(const ssm_linear_params_t *p, void *stream);
+ssm_status_t ssm_linear_check(const ssm_linear_params_t *p);
+
 /* ------------------------------------------------------------------------ */
 const char *ssm_status_string(int32_t status);
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char *ssm_last_error(void);
 int32_t ssm_abi_version(void);
 /* sizeof of a params struct: which = 0 scan, 1 decode, 2 chunk, 3 chunk
- * decode; 0 otherwise. */
+ * decode, 4 linear; 0 otherwise. */
 size_t ssm_params_sizeof(int32_t which);
 
 /* Kernel timing for measurement tools.  start and stop are hipEvent_t handles

@@ -55,6 +55,8 @@ __all__ = [
     "selective_scan",
     "ssm_layer_scan",
     "decode_step",
+    "linear",
+    "ssm_layer_forward",
     "affine_compose",
     "blelloch_exclusive_scan",
     "selective_scan_chunked",
@@ -249,6 +251,45 @@ def decode_step(x_t, A, B_t, C_t, *, conv_cache, ssm_state, D=None, z_t=None, co
         dt_w=dt_w, dt_bias=dt_bias, dt_softplus=dt_softplus, dt_min=dt_min, dt_max=dt_max,
         ssm_state=ssm_state)
     return y[:, 0, :], cache, h
+
+
+# --------------------------------------------------------------------------
+# The whole layer (Axon-SSM page, "Algorithm": in_proj, conv + SiLU, x_proj,
+# dt_proj, scan, gate, out_proj)
+# --------------------------------------------------------------------------
+
+def linear(x, W):
+    """A projection of the layer dataflow with weight W of shape (out, in) and
+    no bias: y[..., o] = sum_i x[..., i] W[o, i]."""
+    return _f64(x) @ _f64(W).T
+
+
+def ssm_layer_forward(hidden, W_in, conv_w, W_x, dt_w, dt_bias, A, W_out, *, D=None, conv_b=None,
+                      conv_cache=None, ssm_state=None, dt_softplus=True, dt_min=None, dt_max=None):
+    """The Axon-SSM layer forward, in the order of the page's "Algorithm" dataflow.
+
+    hidden (Bt, L, Dm); W_in (2E, Dm); conv_w (E, K); W_x (2N+1, E); dt_w, dt_bias
+    (E); A (E, N); W_out (Dm, E); D (E) or None.
+      xz = in_proj(hidden), split into x_branch = xz[..., :E] and z = xz[..., E:]
+      u = SiLU(causal depthwise conv1d(x_branch))
+      (B, C, dt_raw) = x_proj(u), in that order: columns [0, N), [N, 2N), 2N
+      dt = clip(softplus(dt_proj(dt_raw) + dt_bias)) with the rank-1 dt_proj
+      y = scan(u, dt, A, B, C) + D*u, gated by SiLU(z)
+      out = out_proj(y)
+    Returns (out (Bt, L, Dm), ssm_state_out (Bt, E, N), conv_cache_out (Bt, E, K-1)).
+    """
+    E = _f64(W_in).shape[0] // 2
+    N = _f64(A).shape[1]
+    xz = linear(hidden, W_in)
+    x_branch, z = xz[..., :E], xz[..., E:]
+    xc, _ = causal_depthwise_conv1d(x_branch, conv_w, conv_b, conv_cache)
+    u = silu(xc)
+    dbc = linear(u, W_x)
+    B, C, dt_raw = dbc[..., :N], dbc[..., N:2 * N], dbc[..., 2 * N]
+    y, h, cache = ssm_layer_scan(x_branch, A, B, C, D=D, z=z, conv_w=conv_w, conv_b=conv_b, conv_cache=conv_cache,
+                                 dt_raw=dt_raw, dt_w=dt_w, dt_bias=dt_bias, dt_softplus=dt_softplus,
+                                 dt_min=dt_min, dt_max=dt_max, ssm_state=ssm_state)
+    return linear(y, W_out), h, cache
 
 
 # --------------------------------------------------------------------------

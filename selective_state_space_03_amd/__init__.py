@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     chunk_scan_fwd,
     decode_step,
     lib,
+    linear_fwd,
     scan_fwd,
     set_timing_events,
 )

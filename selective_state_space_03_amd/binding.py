@@ -68,11 +68,19 @@ class ChunkDecodeParams(ctypes.Structure):
     ]
 
 
+class LinearParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("rows", _i32), ("in_features", _i32), ("out_features", _i32),
+        ("x", _vp), ("x_dtype", _i32), ("weight", _vp), ("out", _vp), ("out_dtype", _i32),
+    ]
+
+
 EXPORTED = [
     "ssm_scan_fwd", "ssm_scan_workspace_size", "ssm_scan_check",
     "ssm_decode_step", "ssm_decode_check",
     "ssm_chunk_scan_fwd", "ssm_chunk_scan_workspace_size", "ssm_chunk_scan_check",
     "ssm_chunk_decode_step", "ssm_chunk_decode_check",
+    "ssm_linear_fwd", "ssm_linear_check",
     "ssm_status_string", "ssm_last_error", "ssm_abi_version", "ssm_params_sizeof", "ssm_set_timing_events",
 ]
 
@@ -107,6 +115,10 @@ def lib() -> ctypes.CDLL:
     L.ssm_chunk_decode_step.restype = _i32
     L.ssm_chunk_decode_check.argtypes = [ctypes.POINTER(ChunkDecodeParams)]
     L.ssm_chunk_decode_check.restype = _i32
+    L.ssm_linear_fwd.argtypes = [ctypes.POINTER(LinearParams), _vp]
+    L.ssm_linear_fwd.restype = _i32
+    L.ssm_linear_check.argtypes = [ctypes.POINTER(LinearParams)]
+    L.ssm_linear_check.restype = _i32
     L.ssm_status_string.argtypes = [_i32]
     L.ssm_status_string.restype = ctypes.c_char_p
     L.ssm_last_error.argtypes = []
@@ -117,7 +129,7 @@ def lib() -> ctypes.CDLL:
     L.ssm_params_sizeof.restype = ctypes.c_size_t
     L.ssm_set_timing_events.argtypes = [_vp, _vp]
     L.ssm_set_timing_events.restype = None
-    for i, st in enumerate((ScanParams, DecodeParams, ChunkParams, ChunkDecodeParams)):
+    for i, st in enumerate((ScanParams, DecodeParams, ChunkParams, ChunkDecodeParams, LinearParams)):
         if L.ssm_params_sizeof(i) != ctypes.sizeof(st):
             raise RuntimeError(f"ctypes mirror of params struct {i} does not match the library")
     _lib = L
@@ -377,4 +389,27 @@ def chunk_decode_step(x, dt, A, B, C, state, *, D=None, dt_bias=None, dt_softplu
     p.out = _ptr(out, "out", (batch, nheads, headdim), device=dev)
     p.out_dtype = _code(out, "out")
     call = Call(L_.ssm_chunk_decode_step, p, _stream(dev, stream), out, (x, dt, A, B, C, state, D, dt_bias, z))
+    return call if prepare else call.run()
+
+
+def linear_fwd(x, weight, *, out=None, out_dtype=None, stream=None, prepare=False):
+    """A projection without bias (ssm_linear_fwd): out[..., o] = sum_i x[..., i] weight[o, i], with x
+    (..., in) bf16 or f32 and weight (out, in) bf16.  Returns out (..., out), or with prepare=True a
+    Call that enqueues this same call again on each run()."""
+    L_ = lib()
+    n_out, n_in = weight.shape
+    lead = tuple(x.shape[:-1])
+    rows = math.prod(lead)
+    dev = x.device
+    if out is None:
+        out = torch.empty(lead + (n_out,), dtype=out_dtype or x.dtype, device=dev)
+    p = LinearParams()
+    p.struct_size = ctypes.sizeof(LinearParams)
+    p.rows, p.in_features, p.out_features = rows, n_in, n_out
+    p.x = _ptr(x, "x", lead + (n_in,), device=dev)
+    p.x_dtype = _code(x, "x")
+    p.weight = _ptr(weight, "weight", (n_out, n_in), torch.bfloat16, dev)
+    p.out = _ptr(out, "out", lead + (n_out,), device=dev)
+    p.out_dtype = _code(out, "out")
+    call = Call(L_.ssm_linear_fwd, p, _stream(dev, stream), out, (x, weight))
     return call if prepare else call.run()

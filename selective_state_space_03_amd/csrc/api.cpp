@@ -349,6 +349,31 @@ ssm_status_t chunk_decode_check(const ssm_chunk_decode_params_t* p) {
   return SSM_OK;
 }
 
+// ---------------------------------------------------------------- projections
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+ssm_status_t linear_check(const ssm_linear_params_t* p) {
+  if (!p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "params");
+  if (p->struct_size != sizeof(ssm_linear_params_t))
+    return fail(SSM_ERR_INVALID_ARG, "%s does not match this library", "struct_size");
+  if (p->rows < 0 || p->in_features <= 0 || p->out_features <= 0)
+    return fail(SSM_ERR_INVALID_ARG, "%s: negative or zero size", "rows/in_features/out_features");
+  if (!valid_dtype(p->x_dtype) || !valid_dtype(p->out_dtype))
+    return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "x/out_dtype");
+  if (p->in_features % 8 != 0) return fail(SSM_ERR_UNSUPPORTED, "%s must be a multiple of 8", "in_features");
+  if (p->out_features % 4 != 0) return fail(SSM_ERR_UNSUPPORTED, "%s must be a multiple of 4", "out_features");
+  if (p->rows == 0) return SSM_OK;
+  if (!p->x || !p->weight || !p->out) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "x/weight/out");
+  if (!aligned16(p->x) || !aligned16(p->weight) || !aligned16(p->out))
+    return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "x/weight/out");
+  const size_t M = p->rows, K = p->in_features, N = p->out_features;
+  const Range out{p->out, M * N * esize(p->out_dtype)};
+  if (overlaps(out, {p->x, M * K * esize(p->x_dtype)}) || overlaps(out, {p->weight, N * K * 2}))
+    return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "out");
+  return SSM_OK;
+}
+
 ssm_status_t hip_status(hipError_t e) {
   if (e == hipSuccess) return ok();
   return fail(SSM_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
@@ -545,6 +570,30 @@ ssm_status_t ssm_chunk_decode_step(const ssm_chunk_decode_params_t* p, void* str
   return hip_status(ssm::launch_chunk_decode(l, static_cast<hipStream_t>(stream)));
 }
 
+ssm_status_t ssm_linear_check(const ssm_linear_params_t* p) {
+  const ssm_status_t s = linear_check(p);
+  return s == SSM_OK ? ok() : s;
+}
+
+ssm_status_t ssm_linear_fwd(const ssm_linear_params_t* p, void* stream) {
+  const ssm_status_t s = linear_check(p);
+  if (s != SSM_OK) return s;
+  if (p->rows == 0) return ok();
+  ssm::GemmArgs g{};
+  g.A = p->x;
+  g.W = static_cast<const uint16_t*>(p->weight);
+  g.C0 = p->out;
+  g.C1 = nullptr;
+  g.lda = p->in_features;
+  g.ldw = p->in_features;
+  g.ldc0 = g.ldc1 = p->out_features;
+  g.M = p->rows;
+  g.N = p->out_features;
+  g.K = p->in_features;
+  g.n_split = p->out_features;
+  return hip_status(ssm::launch_gemm(g, p->x_dtype, p->out_dtype, static_cast<hipStream_t>(stream)));
+}
+
 const char* ssm_status_string(int32_t status) {
   switch (status) {
     case SSM_OK: return "SSM_OK";
@@ -571,6 +620,7 @@ size_t ssm_params_sizeof(int32_t which) {
     case 1: return sizeof(ssm_decode_params_t);
     case 2: return sizeof(ssm_chunk_params_t);
     case 3: return sizeof(ssm_chunk_decode_params_t);
+    case 4: return sizeof(ssm_linear_params_t);
     default: return 0;
   }
 }

@@ -150,21 +150,20 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
     const uint16_t* Cc = Cg + (tok * G + g) * kN;
     const uint16_t* Bc = Bg + (tok * G + g) * kN;
     const uint16_t* xc = xg + (tok * H + h) * P + p0;
-    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = RPT * rg + i;
       const int o = r * G * kN + 8 * pc;
       const bool in = !kRag || r < R.valid;
-      R.c[i] = in ? *reinterpret_cast<const uint4*>(Cc + o) : z4;
-      R.b[i] = in ? *reinterpret_cast<const uint4*>(Bc + o) : z4;
+      R.c[i] = load16_if(Cc + o, in);
+      R.b[i] = load16_if(Bc + o, in);
     }
     if (xload) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = 2 * rgx + i;
         const bool in = !kRag || r < R.valid;
-        R.x[i] = in ? *reinterpret_cast<const uint4*>(xc + r * H * P + 8 * pcx) : z4;
+        R.x[i] = load16_if(xc + r * H * P + 8 * pcx, in);
       }
     }
     if (tid < R.valid) R.dt = a.dt[tok * H + h + tid * H];

@@ -89,6 +89,16 @@ __device__ __forceinline__ void store_stream(float4* p, float4 v) {
   __builtin_nontemporal_store(w, reinterpret_cast<v4f*>(p));
 }
 
+// 16 bytes from p where ok holds, zeros elsewhere (lanes without ok issue no
+// load).  Returning by value keeps the zero out of memory: a conditional
+// between a global location and a local zero would make the compiler take the
+// local's address and load through a generic pointer.
+__device__ __forceinline__ uint4 load16_if(const void* p, bool ok) {
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (ok) v = *static_cast<const uint4*>(p);
+  return v;
+}
+
 // Make a wave-uniform value provably uniform to the compiler (SGPR).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -230,3 +230,28 @@ def ssd_decode(batch=64, nheads=80, headdim=96, ngroups=1, d_state=64, steps=1, 
     w.arrays["state0"] = _normal(rng, (batch, nheads, headdim, d_state))
     w.name = "ssd_decode" + ("_gated" if gated else "")
     return w
+
+
+def layer_prefill(batch=1, seqlen=2048, d_model=2560, dim=7680, d_state=16, seed=11):
+    """The whole Axon-SSM layer forward with random weights of the page's shapes
+    (D 2560, E 7680, N 16).  Draws, in order: hidden ~ N(0,1) -> bf16
+    (batch, L, D); W_in ~ N(0,1)/sqrt(D) -> bf16 (2E, D); conv_w ~ N(0,0.5)
+    (E, 4); W_x ~ N(0,1)/sqrt(E) -> bf16 (2N+1, E); dt_w ~ N(0,0.5) (E);
+    dt_bias ~ N(0,0.5) (E); D ~ N(0,1) (E); W_out ~ N(0,1)/sqrt(E) -> bf16
+    (D, E).  A = -(1..N) per channel; zero state and conv cache."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    hidden = bf16_bits(_normal(rng, (batch, seqlen, d_model)))
+    W_in = bf16_bits(_normal(rng, (2 * dim, d_model), 1.0 / np.sqrt(d_model)))
+    conv_w = _normal(rng, (dim, 4), 0.5)
+    W_x = bf16_bits(_normal(rng, (2 * d_state + 1, dim), 1.0 / np.sqrt(dim)))
+    dt_w = _normal(rng, (dim,), 0.5)
+    dt_bias = _normal(rng, (dim,), 0.5)
+    D = _normal(rng, (dim,))
+    W_out = bf16_bits(_normal(rng, (d_model, dim), 1.0 / np.sqrt(dim)))
+    A = -np.tile(np.arange(1, d_state + 1, dtype=np.float32), (dim, 1))
+    return Workload(
+        "layer_prefill", "layer",
+        dict(batch=batch, seqlen=seqlen, d_model=d_model, dim=dim, d_state=d_state),
+        dict(hidden=hidden, W_in=W_in, conv_w=conv_w, W_x=W_x, dt_w=dt_w, dt_bias=dt_bias, D=D, W_out=W_out, A=A),
+        {"hidden", "W_in", "W_x", "W_out"},
+        dict(dt_softplus=True, dt_min=DT_MIN, dt_max=DT_MAX))

@@ -501,6 +501,121 @@ def pin_ssd_terms(orc):
            "ssd one-token out")
 
 
+
+def pin_linear_brute_force(orc):
+    """linear(x, W) is the sum over the input index of x times W[out, in], by loops."""
+    rng = _rng(71)
+    x = rng.standard_normal((2, 3, 5))
+    W = rng.standard_normal((4, 5))
+    want = np.zeros((2, 3, 4))
+    for b in range(2):
+        for t in range(3):
+            for o in range(4):
+                acc = 0.0
+                for i in range(5):
+                    acc += x[b, t, i] * W[o, i]
+                want[b, t, o] = acc
+    _close(orc.linear(x, W), want, 1e-13, "linear")
+
+
+def _layer_weights(rng, Dm, E, N, K=4):
+    return dict(W_in=rng.standard_normal((2 * E, Dm)) * 0.3, conv_w=rng.standard_normal((E, K)) * 0.5,
+                W_x=rng.standard_normal((2 * N + 1, E)) * 0.3, dt_w=rng.standard_normal(E) * 0.5,
+                dt_bias=rng.standard_normal(E) * 0.5, A=-np.tile(np.arange(1, N + 1, dtype=np.float64), (E, 1)),
+                W_out=rng.standard_normal((Dm, E)) * 0.3, D=rng.standard_normal(E))
+
+
+def pin_layer_wiring(orc):
+    """The layer with structured weights reduces to pieces computed here by hand:
+    in_proj = [I; 2I] makes x_branch = hidden and z = 2 hidden, out_proj = I
+    returns y, and x_proj rows that are unit vectors pick B, C and dt_raw out of
+    the post-conv activation u = SiLU(conv(x_branch)) (B first, then C, then
+    dt_raw, as the dataflow lists them).  The scan is then the plain
+    recurrence, written out here."""
+    rng = _rng(72)
+    Bt, L, E, N = 2, 9, 6, 2
+    hidden = rng.standard_normal((Bt, L, E))
+    conv_w = rng.standard_normal((E, 4)) * 0.5
+    W_in = np.concatenate([np.eye(E), 2.0 * np.eye(E)])
+    pick = [4, 1, 0, 5, 3]  # B from channels 4, 1; C from 0, 5; dt_raw from 3
+    W_x = np.zeros((2 * N + 1, E))
+    for j, e in enumerate(pick):
+        W_x[j, e] = 1.0
+    dt_w = rng.uniform(0.5, 1.5, E)
+    dt_bias = rng.standard_normal(E) * 0.3
+    A = -np.tile(np.arange(1, N + 1, dtype=np.float64), (E, 1))
+    D = rng.standard_normal(E)
+    out, h_end, cache = orc.ssm_layer_forward(hidden, W_in, conv_w, W_x, dt_w, dt_bias, A, np.eye(E), D=D,
+                                              dt_min=1e-3, dt_max=0.5)
+    # by hand: conv (cross-correlation, zero history), SiLU, the picks, the scan
+    u = np.zeros((Bt, L, E))
+    for b in range(Bt):
+        for t in range(L):
+            for e in range(E):
+                acc = 0.0
+                for k in range(4):
+                    tt = t - 3 + k
+                    if tt >= 0:
+                        acc += conv_w[e, k] * hidden[b, tt, e]
+                u[b, t, e] = acc * _sig(acc)
+    y = np.zeros((Bt, L, E))
+    h = np.zeros((Bt, E, N))
+    for b in range(Bt):
+        for t in range(L):
+            Bv = [u[b, t, pick[0]], u[b, t, pick[1]]]
+            Cv = [u[b, t, pick[2]], u[b, t, pick[3]]]
+            r = u[b, t, pick[4]]
+            for e in range(E):
+                pre = dt_w[e] * r + dt_bias[e]
+                dt = min(max(math.log1p(math.exp(pre)), 1e-3), 0.5)
+                acc = 0.0
+                for n in range(N):
+                    h[b, e, n] = math.exp(dt * A[e, n]) * h[b, e, n] + dt * Bv[n] * u[b, t, e]
+                    acc += Cv[n] * h[b, e, n]
+                zz = 2.0 * hidden[b, t, e]
+                y[b, t, e] = (acc + D[e] * u[b, t, e]) * zz * _sig(zz)
+    _close(out, y, 1e-12, "layer wiring: out")
+    _close(h_end, h, 1e-12, "layer wiring: state")
+    _close(cache, np.transpose(hidden[:, L - 3:, :], (0, 2, 1)), 0.0, "layer wiring: conv cache")
+
+
+def pin_layer_prefill_split(orc):
+    """A layer over L tokens equals the layer over the first L1 tokens followed by
+    the layer over the rest from the returned ssm_state and conv_cache."""
+    rng = _rng(73)
+    Bt, L, L1, Dm, E, N = 2, 11, 4, 5, 6, 3
+    wts = _layer_weights(rng, Dm, E, N)
+    hidden = rng.standard_normal((Bt, L, Dm))
+    kw = dict(D=wts["D"], dt_min=1e-3, dt_max=0.3)
+    args = [wts[k] for k in ("W_in", "conv_w", "W_x", "dt_w", "dt_bias", "A", "W_out")]
+    o_all, h_all, c_all = orc.ssm_layer_forward(hidden, *args, **kw)
+    o1, h1, c1 = orc.ssm_layer_forward(hidden[:, :L1], *args, **kw)
+    o2, h2, c2 = orc.ssm_layer_forward(hidden[:, L1:], *args, conv_cache=c1, ssm_state=h1, **kw)
+    _close(np.concatenate([o1, o2], axis=1), o_all, 1e-12, "layer split: out")
+    _close(h2, h_all, 1e-12, "layer split: state")
+    _close(c2, c_all, 0.0, "layer split: cache")
+
+
+def pin_layer_projections_linear(orc):
+    """out_proj is linear in its weight (2 W_out doubles the output), a zero
+    hidden input from a zero state gives a zero output, and the output of a
+    single token depends on nothing after it."""
+    rng = _rng(74)
+    Bt, L, Dm, E, N = 1, 6, 4, 5, 2
+    wts = _layer_weights(rng, Dm, E, N)
+    hidden = rng.standard_normal((Bt, L, Dm))
+    args = lambda W_out: [wts[k] for k in ("W_in", "conv_w", "W_x", "dt_w", "dt_bias", "A")] + [W_out]
+    o1, _, _ = orc.ssm_layer_forward(hidden, *args(wts["W_out"]), D=wts["D"], dt_min=1e-3, dt_max=0.3)
+    o2, _, _ = orc.ssm_layer_forward(hidden, *args(2.0 * wts["W_out"]), D=wts["D"], dt_min=1e-3, dt_max=0.3)
+    _close(o2, 2.0 * o1, 1e-12, "layer: out_proj linear")
+    o0, h0, _ = orc.ssm_layer_forward(np.zeros_like(hidden), *args(wts["W_out"]), D=wts["D"], dt_min=1e-3,
+                                      dt_max=0.3)
+    assert np.all(o0 == 0.0) and np.all(h0 == 0.0), "layer: zero input must give zero output and state"
+    h2 = hidden.copy()
+    h2[:, 3:] += 1.0
+    o3, _, _ = orc.ssm_layer_forward(h2, *args(wts["W_out"]), D=wts["D"], dt_min=1e-3, dt_max=0.3)
+    _close(o3[:, :3], o1[:, :3], 0.0, "layer: causal")
+
 ALL_PINS = [
     pin_unrolled_product_sum,
     pin_recurrence_equals_convolution,
@@ -521,4 +636,8 @@ ALL_PINS = [
     pin_zero_cases,
     pin_affine_monoid_and_blelloch,
     pin_ssd_terms,
+    pin_linear_brute_force,
+    pin_layer_wiring,
+    pin_layer_prefill_split,
+    pin_layer_projections_linear,
 ]

@@ -43,6 +43,17 @@ MUTATIONS = {
     "a_from_log_sign": ("return -np.exp(_f64(A_log))", "return np.exp(_f64(A_log))"),
     "ssd_ragged_tail_dropped": ("for c in range((L + Q - 1) // Q):", "for c in range(L // Q):"),
     "ssd_gate_sigmoid": ("    return out * silu(_f64(z))", "    return out * sigmoid(_f64(z))"),
+    "layer_xz_swapped": ("x_branch, z = xz[..., :E], xz[..., E:]", "z, x_branch = xz[..., :E], xz[..., E:]"),
+    "layer_xproj_on_x": ("dbc = linear(u, W_x)", "dbc = linear(x_branch, W_x)"),
+    "layer_bc_swapped": ("B, C, dt_raw = dbc[..., :N], dbc[..., N:2 * N], dbc[..., 2 * N]",
+                         "C, B, dt_raw = dbc[..., :N], dbc[..., N:2 * N], dbc[..., 2 * N]"),
+    "layer_dt_from_first": ("B, C, dt_raw = dbc[..., :N], dbc[..., N:2 * N], dbc[..., 2 * N]",
+                            "B, C, dt_raw = dbc[..., 1:N + 1], dbc[..., N + 1:2 * N + 1], dbc[..., 0]"),
+    "layer_no_gate": ("y, h, cache = ssm_layer_scan(x_branch, A, B, C, D=D, z=z,",
+                      "y, h, cache = ssm_layer_scan(x_branch, A, B, C, D=D, z=None,"),
+    "layer_state_not_passed": ("dt_min=dt_min, dt_max=dt_max, ssm_state=ssm_state)\n    return linear(y, W_out)",
+                               "dt_min=dt_min, dt_max=dt_max, ssm_state=None)\n    return linear(y, W_out)"),
+    "linear_weight_transposed": ("return _f64(x) @ _f64(W).T", "return _f64(x) @ _f64(W)[:, ::-1].T"),
     "ssd_seq_gate_dropped": ("    return _gate(out, z), S\n\n\ndef ssd_chunk_scan",
                           "    return out, S\n\n\ndef ssd_chunk_scan"),
 }
