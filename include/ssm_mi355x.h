@@ -283,6 +283,11 @@ ssm_status_t ssm_chunk_decode_check(const ssm_chunk_decode_params_t *p);
  *           about 16 mantissa bits
  *   weight  (out_features, in_features) bf16 (the (out, in) layout of a weight)
  *   out     (rows, out_features) out_dtype; must not overlap x or weight
+ *   workspace  optional device scratch (256-byte aligned): with at least
+ *           ssm_linear_workspace_size(p) bytes a shape with too few output
+ *           tiles to fill the GPU splits the in_features sum into ranges
+ *           whose fp32 partials are added in range order; with less (or
+ *           NULL) it runs unsplit.  Either way the result is deterministic.
  * fp32 accumulation.  x, weight and out must be 16-byte aligned;
  * in_features % 8 == 0; out_features % 4 == 0.
  * ---------------------------------------------------------------------- */
@@ -294,9 +299,12 @@ typedef struct ssm_linear_params {
   const void *weight;
   void *out;
   int32_t out_dtype;
+  void *workspace;
+  size_t workspace_bytes;
 } ssm_linear_params_t;
 
 ssm_status_t ssm_linear_fwd(const ssm_linear_params_t *p, void *stream);
+size_t ssm_linear_workspace_size(const ssm_linear_params_t *p);
 ssm_status_t ssm_linear_check(const ssm_linear_params_t *p);
 
 /* ------------------------------------------------------------------------ */

@@ -72,6 +72,7 @@ class LinearParams(ctypes.Structure):
     _fields_ = [
         ("struct_size", ctypes.c_uint32), ("rows", _i32), ("in_features", _i32), ("out_features", _i32),
         ("x", _vp), ("x_dtype", _i32), ("weight", _vp), ("out", _vp), ("out_dtype", _i32),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -80,7 +81,7 @@ EXPORTED = [
     "ssm_decode_step", "ssm_decode_check",
     "ssm_chunk_scan_fwd", "ssm_chunk_scan_workspace_size", "ssm_chunk_scan_check",
     "ssm_chunk_decode_step", "ssm_chunk_decode_check",
-    "ssm_linear_fwd", "ssm_linear_check",
+    "ssm_linear_fwd", "ssm_linear_workspace_size", "ssm_linear_check",
     "ssm_status_string", "ssm_last_error", "ssm_abi_version", "ssm_params_sizeof", "ssm_set_timing_events",
 ]
 
@@ -117,6 +118,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_chunk_decode_check.restype = _i32
     L.ssm_linear_fwd.argtypes = [ctypes.POINTER(LinearParams), _vp]
     L.ssm_linear_fwd.restype = _i32
+    L.ssm_linear_workspace_size.argtypes = [ctypes.POINTER(LinearParams)]
+    L.ssm_linear_workspace_size.restype = ctypes.c_size_t
     L.ssm_linear_check.argtypes = [ctypes.POINTER(LinearParams)]
     L.ssm_linear_check.restype = _i32
     L.ssm_status_string.argtypes = [_i32]
@@ -392,10 +395,11 @@ def chunk_decode_step(x, dt, A, B, C, state, *, D=None, dt_bias=None, dt_softplu
     return call if prepare else call.run()
 
 
-def linear_fwd(x, weight, *, out=None, out_dtype=None, stream=None, prepare=False):
+def linear_fwd(x, weight, *, out=None, out_dtype=None, workspace=None, stream=None, prepare=False):
     """A projection without bias (ssm_linear_fwd): out[..., o] = sum_i x[..., i] weight[o, i], with x
-    (..., in) bf16 or f32 and weight (out, in) bf16.  Returns out (..., out), or with prepare=True a
-    Call that enqueues this same call again on each run()."""
+    (..., in) bf16 or f32 and weight (out, in) bf16.  A workspace of ssm_linear_workspace_size() bytes
+    is allocated when none is given (workspace=False runs without one).  Returns out (..., out), or
+    with prepare=True a Call that enqueues this same call again on each run()."""
     L_ = lib()
     n_out, n_in = weight.shape
     lead = tuple(x.shape[:-1])
@@ -411,5 +415,11 @@ def linear_fwd(x, weight, *, out=None, out_dtype=None, stream=None, prepare=Fals
     p.weight = _ptr(weight, "weight", (n_out, n_in), torch.bfloat16, dev)
     p.out = _ptr(out, "out", lead + (n_out,), device=dev)
     p.out_dtype = _code(out, "out")
-    call = Call(L_.ssm_linear_fwd, p, _stream(dev, stream), out, (x, weight))
+    if workspace is None:
+        need = L_.ssm_linear_workspace_size(ctypes.byref(p))
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else False
+    if workspace is not False:
+        p.workspace = _ptr(workspace, "workspace", device=dev)
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    call = Call(L_.ssm_linear_fwd, p, _stream(dev, stream), out, (x, weight, workspace))
     return call if prepare else call.run()

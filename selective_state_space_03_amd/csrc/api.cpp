@@ -371,6 +371,13 @@ ssm_status_t linear_check(const ssm_linear_params_t* p) {
   const Range out{p->out, M * N * esize(p->out_dtype)};
   if (overlaps(out, {p->x, M * K * esize(p->x_dtype)}) || overlaps(out, {p->weight, N * K * 2}))
     return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "out");
+  if (p->workspace) {
+    if (reinterpret_cast<uintptr_t>(p->workspace) & 255)
+      return fail(SSM_ERR_INVALID_ARG, "%s must be 256-byte aligned", "workspace");
+    const Range ws{p->workspace, p->workspace_bytes};
+    if (overlaps(ws, out) || overlaps(ws, {p->x, M * K * esize(p->x_dtype)}) || overlaps(ws, {p->weight, N * K * 2}))
+      return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "workspace");
+  }
   return SSM_OK;
 }
 
@@ -591,7 +598,15 @@ ssm_status_t ssm_linear_fwd(const ssm_linear_params_t* p, void* stream) {
   g.N = p->out_features;
   g.K = p->in_features;
   g.n_split = p->out_features;
+  g.ws = static_cast<float*>(p->workspace);
+  g.ws_bytes = p->workspace ? p->workspace_bytes : 0;
   return hip_status(ssm::launch_gemm(g, p->x_dtype, p->out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t ssm_linear_workspace_size(const ssm_linear_params_t* p) {
+  if (!p || p->struct_size != sizeof(ssm_linear_params_t)) return 0;
+  if (p->rows <= 0 || p->in_features <= 0 || p->out_features <= 0) return 0;
+  return ssm::gemm_workspace_bytes(p->rows, p->out_features, p->in_features, p->x_dtype);
 }
 
 const char* ssm_status_string(int32_t status) {

@@ -176,16 +176,23 @@ hipError_t launch_chunk_decode(const ChunkDecodeLaunch& l, hipStream_t stream);
 // A (M, K) bf16 or f32 with row stride lda; W (N, K) bf16 with row stride ldw;
 // output columns [0, n_split) go to C0 (row stride ldc0), [n_split, N) to C1
 // (row stride ldc1, column index n - n_split).  Requires K % 8 == 0, N % 4 ==
-// 0, n_split == N or n_split % 128 == 0, 16-byte aligned rows and pointers.
+// 0, n_split == N or n_split % 256 == 0, 16-byte aligned rows and pointers.
+// A workspace (ws, ws_bytes) lets a shape with too few output tiles for the
+// chip split K and add fp32 partials; without one it runs unsplit.
 struct GemmArgs {
   const void* A;
   const uint16_t* W;
   void* C0;
   void* C1;
+  float* ws;
+  size_t ws_bytes;
   int lda, ldw, ldc0, ldc1;
   int M, N, K, n_split;
+  int kchunk;  // set by the launcher
 };
 
+// Workspace for the fastest split of this shape (0: none needed).
+size_t gemm_workspace_bytes(int M, int N, int K, int a_dtype);
 hipError_t launch_gemm(const GemmArgs& g, int a_dtype, int out_dtype, hipStream_t stream);
 
 }  // namespace ssm

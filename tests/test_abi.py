@@ -265,11 +265,17 @@ def test_linear_validation(L):
         "out_align": (_lin(out=_addr(3) + 4), 1),
         "out_over_x": (_lin(out=_addr(1) + 1024), 1),
         "out_over_w": (_lin(out=_addr(2) + 4096), 1),
+        "ws_align": (_lin(workspace=_addr(4) + 16, workspace_bytes=1 << 20), 1),
+        "ws_over_out": (_lin(workspace=_addr(3) + 256, workspace_bytes=1 << 20), 1),
     }
     for name, (p, want) in cases.items():
         assert L.ssm_linear_check(ctypes.byref(p)) == want, (name, L.ssm_last_error())
     assert L.ssm_linear_fwd(ctypes.byref(_lin(rows=0, x=None, out=None)), None) == 0
     assert L.ssm_linear_fwd(ctypes.byref(_lin(in_features=12)), None) == 2
+    # the in_proj shape fills the GPU with tiles: no workspace; out_proj does not
+    assert L.ssm_linear_workspace_size(ctypes.byref(_lin())) == 0
+    big = L.ssm_linear_workspace_size(ctypes.byref(_lin(in_features=7680, out_features=2560)))
+    assert big > 0 and big % (2048 * 2560 * 4) == 0
 
 
 def test_binding_refuses_cpu_tensors(L):
