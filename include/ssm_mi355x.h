@@ -307,13 +307,59 @@ ssm_status_t ssm_linear_fwd(const ssm_linear_params_t *p, void *stream);
 size_t ssm_linear_workspace_size(const ssm_linear_params_t *p);
 ssm_status_t ssm_linear_check(const ssm_linear_params_t *p);
 
+/* ------------------------------------------------------------------------
+ * The whole layer forward (page "Axon-SSM: selective state space model",
+ * section "Algorithm"), T = batch * seqlen tokens:
+ *   [x_branch | z] = in_proj(hidden)                   w_in (2E, D) bf16
+ *   u = SiLU(causal depthwise conv1d(x_branch))        conv_w (E, K), conv_b (E) or NULL
+ *   [B | C | dt_raw] = x_proj(u)                       w_x (2N+1, E) bf16, in that order
+ *   dt = clip(softplus(dt_w * dt_raw + dt_bias), dt_min, dt_max)   dt_w, dt_bias (E)
+ *   y = scan(u, dt, A, B, C) + D u, gated by SiLU(z)   A (E, N), D (E) or NULL
+ *   out = out_proj(y)                                  w_out (D, E) bf16
+ * hidden (Bt, L, D) hidden_dtype; out (Bt, L, D) out_dtype; conv caches
+ * (Bt, E, K-1) f32 and states (Bt, E, N) f32 as in ssm_scan_fwd (each NULL-able;
+ * in and out may be the same buffer).  The activations between the steps
+ * (x_branch, z, y: fp32; B, C, dt_raw: fp32) live in the workspace, which
+ * must hold ssm_layer_workspace_size(p) bytes (256-byte aligned).
+ * Supported: N = 16, K = 4, E % 256 == 0, D % 8 == 0; hidden, the weights,
+ * out, conv_w and A 16-byte aligned.
+ * Timing events (ssm_set_timing_events) bracket the whole layer.
+ * ---------------------------------------------------------------------- */
+typedef struct ssm_layer_params {
+  uint32_t struct_size; /* = sizeof(ssm_layer_params_t) */
+  int32_t batch, seqlen, d_model, dim, d_state, conv_k;
+  const void *hidden;
+  int32_t hidden_dtype;
+  const void *w_in;
+  const float *conv_w, *conv_b;
+  const void *w_x;
+  const float *dt_w, *dt_bias;
+  int32_t dt_softplus;
+  float dt_min, dt_max;
+  const float *A;
+  const float *D;
+  const void *w_out;
+  const float *conv_cache_in;
+  float *conv_cache_out;
+  const float *ssm_state_in;
+  float *ssm_state_out;
+  void *out;
+  int32_t out_dtype;
+  void *workspace;
+  size_t workspace_bytes;
+} ssm_layer_params_t;
+
+ssm_status_t ssm_layer_fwd(const ssm_layer_params_t *p, void *stream);
+size_t ssm_layer_workspace_size(const ssm_layer_params_t *p);
+ssm_status_t ssm_layer_check(const ssm_layer_params_t *p);
+
 /* ------------------------------------------------------------------------ */
 const char *ssm_status_string(int32_t status);
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char *ssm_last_error(void);
 int32_t ssm_abi_version(void);
 /* sizeof of a params struct: which = 0 scan, 1 decode, 2 chunk, 3 chunk
- * decode, 4 linear; 0 otherwise. */
+ * decode, 4 linear, 5 layer; 0 otherwise. */
 size_t ssm_params_sizeof(int32_t which);
 
 /* Kernel timing for measurement tools.  start and stop are hipEvent_t handles

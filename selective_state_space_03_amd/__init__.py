@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     chunk_decode_step,
     chunk_scan_fwd,
     decode_step,
+    layer_fwd,
     lib,
     linear_fwd,
     scan_fwd,

@@ -76,12 +76,24 @@ class LinearParams(ctypes.Structure):
     ]
 
 
+class LayerParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("batch", _i32), ("seqlen", _i32), ("d_model", _i32), ("dim", _i32),
+        ("d_state", _i32), ("conv_k", _i32), ("hidden", _vp), ("hidden_dtype", _i32), ("w_in", _vp),
+        ("conv_w", _vp), ("conv_b", _vp), ("w_x", _vp), ("dt_w", _vp), ("dt_bias", _vp), ("dt_softplus", _i32),
+        ("dt_min", _f32), ("dt_max", _f32), ("A", _vp), ("D", _vp), ("w_out", _vp), ("conv_cache_in", _vp),
+        ("conv_cache_out", _vp), ("ssm_state_in", _vp), ("ssm_state_out", _vp), ("out", _vp), ("out_dtype", _i32),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 EXPORTED = [
     "ssm_scan_fwd", "ssm_scan_workspace_size", "ssm_scan_check",
     "ssm_decode_step", "ssm_decode_check",
     "ssm_chunk_scan_fwd", "ssm_chunk_scan_workspace_size", "ssm_chunk_scan_check",
     "ssm_chunk_decode_step", "ssm_chunk_decode_check",
     "ssm_linear_fwd", "ssm_linear_workspace_size", "ssm_linear_check",
+    "ssm_layer_fwd", "ssm_layer_workspace_size", "ssm_layer_check",
     "ssm_status_string", "ssm_last_error", "ssm_abi_version", "ssm_params_sizeof", "ssm_set_timing_events",
 ]
 
@@ -122,6 +134,12 @@ def lib() -> ctypes.CDLL:
     L.ssm_linear_workspace_size.restype = ctypes.c_size_t
     L.ssm_linear_check.argtypes = [ctypes.POINTER(LinearParams)]
     L.ssm_linear_check.restype = _i32
+    L.ssm_layer_fwd.argtypes = [ctypes.POINTER(LayerParams), _vp]
+    L.ssm_layer_fwd.restype = _i32
+    L.ssm_layer_workspace_size.argtypes = [ctypes.POINTER(LayerParams)]
+    L.ssm_layer_workspace_size.restype = ctypes.c_size_t
+    L.ssm_layer_check.argtypes = [ctypes.POINTER(LayerParams)]
+    L.ssm_layer_check.restype = _i32
     L.ssm_status_string.argtypes = [_i32]
     L.ssm_status_string.restype = ctypes.c_char_p
     L.ssm_last_error.argtypes = []
@@ -132,7 +150,7 @@ def lib() -> ctypes.CDLL:
     L.ssm_params_sizeof.restype = ctypes.c_size_t
     L.ssm_set_timing_events.argtypes = [_vp, _vp]
     L.ssm_set_timing_events.restype = None
-    for i, st in enumerate((ScanParams, DecodeParams, ChunkParams, ChunkDecodeParams, LinearParams)):
+    for i, st in enumerate((ScanParams, DecodeParams, ChunkParams, ChunkDecodeParams, LinearParams, LayerParams)):
         if L.ssm_params_sizeof(i) != ctypes.sizeof(st):
             raise RuntimeError(f"ctypes mirror of params struct {i} does not match the library")
     _lib = L
@@ -422,4 +440,53 @@ def linear_fwd(x, weight, *, out=None, out_dtype=None, workspace=None, stream=No
         p.workspace = _ptr(workspace, "workspace", device=dev)
         p.workspace_bytes = workspace.numel() * workspace.element_size()
     call = Call(L_.ssm_linear_fwd, p, _stream(dev, stream), out, (x, weight, workspace))
+    return call if prepare else call.run()
+
+
+def layer_fwd(hidden, w_in, conv_w, w_x, dt_w, A, w_out, *, dt_bias=None, D=None, conv_b=None, conv_cache_in=None,
+              conv_cache_out=None, ssm_state_in=None, ssm_state_out=None, dt_softplus=True, dt_min=None, dt_max=None,
+              out=None, out_dtype=None, workspace=None, stream=None, prepare=False):
+    """The whole layer forward (ssm_layer_fwd): in_proj, conv + SiLU, x_proj, scan with the gate, out_proj.
+    hidden (batch, L, D); w_in (2E, D), w_x (2N+1, E), w_out (D, E) bf16; conv_w (E, 4), dt_w (E), A (E, N)
+    fp32.  Returns out (batch, L, D), or with prepare=True a Call that enqueues this same call again."""
+    L_ = lib()
+    batch, seqlen, d_model = hidden.shape
+    dim, d_state = A.shape
+    dev = hidden.device
+    if out is None:
+        out = torch.empty((batch, seqlen, d_model), dtype=out_dtype or hidden.dtype, device=dev)
+    f32, bf = torch.float32, torch.bfloat16
+    p = LayerParams()
+    p.struct_size = ctypes.sizeof(LayerParams)
+    p.batch, p.seqlen, p.d_model, p.dim, p.d_state = batch, seqlen, d_model, dim, d_state
+    p.conv_k = conv_w.shape[1]
+    p.hidden = _ptr(hidden, "hidden", (batch, seqlen, d_model), device=dev)
+    p.hidden_dtype = _code(hidden, "hidden")
+    p.w_in = _ptr(w_in, "w_in", (2 * dim, d_model), bf, dev)
+    p.conv_w = _ptr(conv_w, "conv_w", (dim, p.conv_k), f32, dev)
+    p.conv_b = _ptr(conv_b, "conv_b", (dim,), f32, dev)
+    p.w_x = _ptr(w_x, "w_x", (2 * d_state + 1, dim), bf, dev)
+    p.dt_w = _ptr(dt_w, "dt_w", (dim,), f32, dev)
+    p.dt_bias = _ptr(dt_bias, "dt_bias", (dim,), f32, dev)
+    p.dt_softplus = 1 if dt_softplus else 0
+    p.dt_min = _bound(dt_min, -math.inf)
+    p.dt_max = _bound(dt_max, math.inf)
+    p.A = _ptr(A, "A", (dim, d_state), f32, dev)
+    p.D = _ptr(D, "D", (dim,), f32, dev)
+    p.w_out = _ptr(w_out, "w_out", (d_model, dim), bf, dev)
+    kc = p.conv_k - 1
+    p.conv_cache_in = _ptr(conv_cache_in, "conv_cache_in", (batch, dim, kc), f32, dev)
+    p.conv_cache_out = _ptr(conv_cache_out, "conv_cache_out", (batch, dim, kc), f32, dev)
+    p.ssm_state_in = _ptr(ssm_state_in, "ssm_state_in", (batch, dim, d_state), f32, dev)
+    p.ssm_state_out = _ptr(ssm_state_out, "ssm_state_out", (batch, dim, d_state), f32, dev)
+    p.out = _ptr(out, "out", (batch, seqlen, d_model), device=dev)
+    p.out_dtype = _code(out, "out")
+    need = L_.ssm_layer_workspace_size(ctypes.byref(p))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    p.workspace = _ptr(workspace, "workspace", device=dev)
+    p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    call = Call(L_.ssm_layer_fwd, p, _stream(dev, stream), out,
+                (hidden, w_in, conv_w, conv_b, w_x, dt_w, dt_bias, A, D, w_out, conv_cache_in, conv_cache_out,
+                 ssm_state_in, ssm_state_out, workspace))
     return call if prepare else call.run()

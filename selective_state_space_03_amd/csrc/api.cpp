@@ -381,6 +381,141 @@ ssm_status_t linear_check(const ssm_linear_params_t* p) {
   return SSM_OK;
 }
 
+// ---------------------------------------------------------------- layer
+
+// The layer's workspace: activations between the steps, then the scratch of
+// the scan and of the projections (each piece 256-byte aligned).
+struct LayerWs {
+  size_t x, z, y, part, B, C, r, scan, gemm, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+// The scan step of the layer as an ssm_scan_fwd call on the workspace's
+// activations (x_branch, z, B, C, dt_raw and y in fp32).
+ssm_scan_params_t layer_scan_params(const ssm_layer_params_t* p, char* ws, const LayerWs& o) {
+  ssm_scan_params_t sp{};
+  sp.struct_size = sizeof(ssm_scan_params_t);
+  sp.batch = p->batch;
+  sp.seqlen = p->seqlen;
+  sp.dim = p->dim;
+  sp.d_state = p->d_state;
+  sp.conv_k = p->conv_k;
+  sp.x = ws ? ws + o.x : nullptr;
+  sp.x_dtype = SSM_F32;
+  sp.conv_w = p->conv_w;
+  sp.conv_b = p->conv_b;
+  sp.conv_cache_in = p->conv_cache_in;
+  sp.conv_cache_out = p->conv_cache_out;
+  sp.dt = ws ? ws + o.r : nullptr;
+  sp.dt_dtype = SSM_F32;
+  sp.dt_rank1 = 1;
+  sp.dt_w = p->dt_w;
+  sp.dt_bias = p->dt_bias;
+  sp.dt_softplus = p->dt_softplus;
+  sp.dt_min = p->dt_min;
+  sp.dt_max = p->dt_max;
+  sp.A = p->A;
+  sp.B = ws ? ws + o.B : nullptr;
+  sp.C = ws ? ws + o.C : nullptr;
+  sp.bc_dtype = SSM_F32;
+  sp.D = p->D;
+  sp.z = ws ? ws + o.z : nullptr;
+  sp.z_dtype = SSM_F32;
+  sp.ssm_state_in = p->ssm_state_in;
+  sp.ssm_state_out = p->ssm_state_out;
+  sp.y = ws ? ws + o.y : nullptr;
+  sp.y_dtype = SSM_F32;
+  sp.time_split = 0;
+  sp.workspace = ws ? ws + o.scan : nullptr;
+  sp.workspace_bytes = o.gemm - o.scan;
+  return sp;
+}
+
+LayerWs layer_ws(const ssm_layer_params_t* p) {
+  LayerWs o{};
+  const size_t T = static_cast<size_t>(p->batch) * p->seqlen, E = p->dim, N = p->d_state, Dm = p->d_model;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  o.x = take(T * E * 4);
+  o.z = take(T * E * 4);
+  o.y = take(T * E * 4);
+  o.part = take(T > 0 ? ssm::xproj_partial_bytes(static_cast<int>(T), p->dim) : 0);
+  o.B = take(T * N * 4);
+  o.C = take(T * N * 4);
+  o.r = take(T * 4);
+  o.scan = off;
+  ssm_scan_params_t sp = layer_scan_params(p, nullptr, o);
+  off += align256(T > 0 ? ssm_scan_workspace_size(&sp) : 0);
+  o.gemm = off;
+  size_t g = 0;
+  if (T > 0) {
+    g = std::max(ssm::gemm_workspace_bytes(static_cast<int>(T), static_cast<int>(2 * E), static_cast<int>(Dm), SSM_BF16),
+                 ssm::gemm_workspace_bytes(static_cast<int>(T), static_cast<int>(Dm), static_cast<int>(E), SSM_F32));
+  }
+  off += align256(g);
+  o.total = off;
+  return o;
+}
+
+ssm_status_t layer_check(const ssm_layer_params_t* p) {
+  if (!p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "params");
+  if (p->struct_size != sizeof(ssm_layer_params_t))
+    return fail(SSM_ERR_INVALID_ARG, "%s does not match this library", "struct_size");
+  if (p->batch < 0 || p->seqlen < 0 || p->d_model <= 0 || p->dim <= 0 || p->d_state <= 0)
+    return fail(SSM_ERR_INVALID_ARG, "%s: negative or zero size", "dims");
+  if (p->d_state != ssm::kScanN) return fail(SSM_ERR_UNSUPPORTED, "%s must be 16", "d_state");
+  if (p->conv_k != ssm::kConvK) return fail(SSM_ERR_UNSUPPORTED, "%s must be 4", "conv_k");
+  if (p->dim % 256 != 0) return fail(SSM_ERR_UNSUPPORTED, "%s must be a multiple of 256", "dim");
+  if (p->d_model % 8 != 0) return fail(SSM_ERR_UNSUPPORTED, "%s must be a multiple of 8", "d_model");
+  if (!valid_dtype(p->hidden_dtype) || !valid_dtype(p->out_dtype))
+    return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "hidden/out_dtype");
+  if (!p->w_in || !p->conv_w || !p->w_x || !p->dt_w || !p->A || !p->w_out)
+    return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "w_in/conv_w/w_x/dt_w/A/w_out");
+  ssm_status_t s = check_dt_bounds(p->dt_min, p->dt_max);
+  if (s != SSM_OK) return s;
+  if (!aligned16(p->w_in) || !aligned16(p->conv_w) || !aligned16(p->w_x) || !aligned16(p->A) || !aligned16(p->w_out))
+    return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "weights/conv_w/A");
+  const size_t T = static_cast<size_t>(p->batch) * p->seqlen;
+  if (T == 0) return SSM_OK;
+  if (T * static_cast<size_t>(p->dim) > 0x7fffffffULL)
+    return fail(SSM_ERR_UNSUPPORTED, "%s too large", "batch*seqlen*dim");
+  if (!p->hidden || !p->out) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "hidden/out");
+  if (!aligned16(p->hidden) || !aligned16(p->out))
+    return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "hidden/out");
+  const size_t E = p->dim, N = p->d_state, Dm = p->d_model;
+  const Range out{p->out, T * Dm * esize(p->out_dtype)};
+  const Range ins[] = {
+      {p->hidden, T * Dm * esize(p->hidden_dtype)}, {p->w_in, 2 * E * Dm * 2}, {p->conv_w, E * 4 * 4},
+      {p->conv_b, p->conv_b ? E * 4 : 0},          {p->w_x, (2 * N + 1) * E * 2}, {p->dt_w, E * 4},
+      {p->dt_bias, p->dt_bias ? E * 4 : 0},        {p->A, E * N * 4},        {p->D, p->D ? E * 4 : 0},
+      {p->w_out, Dm * E * 2},
+      {p->conv_cache_in, p->conv_cache_in ? p->batch * E * 3 * 4 : 0},
+      {p->conv_cache_out, p->conv_cache_out ? p->batch * E * 3 * 4 : 0},
+      {p->ssm_state_in, p->ssm_state_in ? p->batch * E * N * 4 : 0},
+      {p->ssm_state_out, p->ssm_state_out ? p->batch * E * N * 4 : 0},
+  };
+  for (const Range& r : ins)
+    if (overlaps(out, r)) return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "out");
+  const LayerWs o = layer_ws(p);
+  if (!p->workspace || p->workspace_bytes < o.total)
+    return fail(SSM_ERR_WORKSPACE, "%s is missing or smaller than ssm_layer_workspace_size()", "workspace");
+  if (reinterpret_cast<uintptr_t>(p->workspace) & 255)
+    return fail(SSM_ERR_INVALID_ARG, "%s must be 256-byte aligned", "workspace");
+  const Range ws{p->workspace, o.total};
+  if (overlaps(ws, out)) return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "workspace");
+  for (const Range& r : ins)
+    if (overlaps(ws, r)) return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "workspace");
+  // the scan step's own constraints (cache/state aliasing and alignment)
+  char* wsp = static_cast<char*>(p->workspace);
+  ssm_scan_params_t sp = layer_scan_params(p, wsp, o);
+  return scan_check(&sp);
+}
+
 ssm_status_t hip_status(hipError_t e) {
   if (e == hipSuccess) return ok();
   return fail(SSM_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
@@ -609,6 +744,100 @@ size_t ssm_linear_workspace_size(const ssm_linear_params_t* p) {
   return ssm::gemm_workspace_bytes(p->rows, p->out_features, p->in_features, p->x_dtype);
 }
 
+ssm_status_t ssm_layer_check(const ssm_layer_params_t* p) {
+  const ssm_status_t s = layer_check(p);
+  return s == SSM_OK ? ok() : s;
+}
+
+size_t ssm_layer_workspace_size(const ssm_layer_params_t* p) {
+  if (!p || p->struct_size != sizeof(ssm_layer_params_t)) return 0;
+  if (p->batch < 0 || p->seqlen < 0 || p->d_model <= 0 || p->dim <= 0 || p->d_state != ssm::kScanN) return 0;
+  if (p->conv_k != ssm::kConvK) return 0;
+  return layer_ws(p).total;
+}
+
+ssm_status_t ssm_layer_fwd(const ssm_layer_params_t* p, void* stream) {
+  const ssm_status_t s = layer_check(p);
+  if (s != SSM_OK) return s;
+  const int T = p->batch * p->seqlen;
+  if (T == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const LayerWs o = layer_ws(p);
+  char* ws = static_cast<char*>(p->workspace);
+  // the caller's timing events bracket the whole layer, not its inner launches
+  const ssm::TimingEvents ev = g_timing;
+  g_timing = ssm::TimingEvents{};
+  auto done = [&](ssm_status_t r) {
+    g_timing = ev;
+    return r;
+  };
+  if (ev.start) {
+    const hipError_t e = hipEventRecord(ev.start, st);
+    if (e != hipSuccess) return done(hip_status(e));
+  }
+  // 1. in_proj: columns [0, E) -> x_branch, [E, 2E) -> z (fp32)
+  ssm::GemmArgs gi{};
+  gi.A = p->hidden;
+  gi.W = static_cast<const uint16_t*>(p->w_in);
+  gi.C0 = ws + o.x;
+  gi.C1 = ws + o.z;
+  gi.ws = reinterpret_cast<float*>(ws + o.gemm);
+  gi.ws_bytes = o.total - o.gemm;
+  gi.lda = p->d_model;
+  gi.ldw = p->d_model;
+  gi.ldc0 = gi.ldc1 = p->dim;
+  gi.M = T;
+  gi.N = 2 * p->dim;
+  gi.K = p->d_model;
+  gi.n_split = p->dim;
+  hipError_t e = ssm::launch_gemm(gi, p->hidden_dtype, SSM_F32, st);
+  if (e != hipSuccess) return done(hip_status(e));
+  // 2. conv + SiLU + x_proj -> B, C, dt_raw
+  ssm::XprojArgs xa{};
+  xa.x = reinterpret_cast<const float*>(ws + o.x);
+  xa.conv_w = p->conv_w;
+  xa.conv_b = p->conv_b;
+  xa.conv_cache_in = p->conv_cache_in;
+  xa.w_x = static_cast<const uint16_t*>(p->w_x);
+  xa.part = reinterpret_cast<float*>(ws + o.part);
+  xa.B = reinterpret_cast<float*>(ws + o.B);
+  xa.C = reinterpret_cast<float*>(ws + o.C);
+  xa.dt_raw = reinterpret_cast<float*>(ws + o.r);
+  xa.batch = p->batch;
+  xa.seqlen = p->seqlen;
+  xa.dim = p->dim;
+  xa.d_state = p->d_state;
+  xa.nout = 2 * p->d_state + 1;
+  e = ssm::launch_xproj(xa, st);
+  if (e != hipSuccess) return done(hip_status(e));
+  // 3. the scan (conv + SiLU again from x_branch, dt, recurrence, D, gate)
+  ssm_scan_params_t sp = layer_scan_params(p, ws, o);
+  const ssm_status_t ss = ssm_scan_fwd(&sp, stream);
+  if (ss != SSM_OK) return done(ss);
+  // 4. out_proj from the fp32 y
+  ssm::GemmArgs go{};
+  go.A = ws + o.y;
+  go.W = static_cast<const uint16_t*>(p->w_out);
+  go.C0 = p->out;
+  go.C1 = nullptr;
+  go.ws = reinterpret_cast<float*>(ws + o.gemm);
+  go.ws_bytes = o.total - o.gemm;
+  go.lda = p->dim;
+  go.ldw = p->dim;
+  go.ldc0 = go.ldc1 = p->d_model;
+  go.M = T;
+  go.N = p->d_model;
+  go.K = p->dim;
+  go.n_split = p->d_model;
+  e = ssm::launch_gemm(go, SSM_F32, p->out_dtype, st);
+  if (e != hipSuccess) return done(hip_status(e));
+  if (ev.stop) {
+    e = hipEventRecord(ev.stop, st);
+    if (e != hipSuccess) return done(hip_status(e));
+  }
+  return done(ok());
+}
+
 const char* ssm_status_string(int32_t status) {
   switch (status) {
     case SSM_OK: return "SSM_OK";
@@ -636,6 +865,7 @@ size_t ssm_params_sizeof(int32_t which) {
     case 2: return sizeof(ssm_chunk_params_t);
     case 3: return sizeof(ssm_chunk_decode_params_t);
     case 4: return sizeof(ssm_linear_params_t);
+    case 5: return sizeof(ssm_layer_params_t);
     default: return 0;
   }
 }

@@ -195,4 +195,22 @@ struct GemmArgs {
 size_t gemm_workspace_bytes(int M, int N, int K, int a_dtype);
 hipError_t launch_gemm(const GemmArgs& g, int a_dtype, int out_dtype, hipStream_t stream);
 
+// ---- x_proj of the layer (conv + SiLU recomputed from x) -------------------
+struct XprojArgs {
+  const float* x;              // (T, E) x_branch, T = batch * seqlen
+  const float* conv_w;         // (E, 4)
+  const float* conv_b;         // (E) or null
+  const float* conv_cache_in;  // (batch, E, 3) or null (zeros)
+  const uint16_t* w_x;         // (nout, E) bf16
+  float* part;                 // partial sums (splits, T, 48)
+  float* B;                    // (T, d_state)
+  float* C;                    // (T, d_state)
+  float* dt_raw;               // (T)
+  int batch, seqlen, dim, d_state, nout;
+};
+
+int xproj_splits(int tokens, int dim);
+size_t xproj_partial_bytes(int tokens, int dim);
+hipError_t launch_xproj(const XprojArgs& a, hipStream_t stream);
+
 }  // namespace ssm

@@ -168,3 +168,36 @@ def ssd_decode_gpu(w: W.Workload, state, t=0, *, out_dtype=torch.float32, x_f32=
                                 dt_softplus=o["dt_softplus"], dt_min=o["dt_min"], dt_max=o["dt_max"],
                                 z=tok("z", z_f32), out_dtype=out_dtype, stream=stream)
     return out
+
+
+# ---------------------------------------------------------------------- layer
+
+def layer_gpu(w: W.Workload, *, tokens=None, out_dtype=torch.float32, cache_in=None, state_in=None,
+              want_state=True, want_cache=True):
+    """ssm_layer_fwd on the workload's hidden states [:, tokens] (all when None)."""
+    d = w.dims
+    o = w.opts
+    hidden = dev_tensor(w, "hidden")
+    if tokens is not None:
+        hidden = hidden[:, tokens].contiguous()
+    Bt, E, N = d["batch"], d["dim"], d["d_state"]
+    st = torch.empty((Bt, E, N), dtype=torch.float32, device=DEV) if want_state else None
+    cc = torch.empty((Bt, E, 3), dtype=torch.float32, device=DEV) if want_cache else None
+    out = ssm.layer_fwd(hidden, dev_tensor(w, "W_in"), dev_tensor(w, "conv_w"), dev_tensor(w, "W_x"),
+                        dev_tensor(w, "dt_w"), dev_tensor(w, "A"), dev_tensor(w, "W_out"),
+                        dt_bias=dev_tensor(w, "dt_bias"), D=dev_tensor(w, "D"), conv_cache_in=cache_in,
+                        conv_cache_out=cc, ssm_state_in=state_in, ssm_state_out=st, dt_softplus=o["dt_softplus"],
+                        dt_min=o["dt_min"], dt_max=o["dt_max"], out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, st, cc
+
+
+def layer_oracle(w: W.Workload, *, tokens=None, cache_in=None, state_in=None):
+    o = w.opts
+    f = w.f64
+    hidden = f("hidden")
+    if tokens is not None:
+        hidden = hidden[:, tokens]
+    return O.ssm_layer_forward(hidden, f("W_in"), f("conv_w"), f("W_x"), f("dt_w"), f("dt_bias"), f("A"),
+                               f("W_out"), D=f("D"), conv_cache=cache_in, ssm_state=state_in,
+                               dt_softplus=o["dt_softplus"], dt_min=float(o["dt_min"]), dt_max=float(o["dt_max"]))
