@@ -18,7 +18,8 @@ Prints ONE JSON line.  Besides the throughput it carries
   the algorithmic work per unit);
 * cpu_baseline: the float64 oracle on the same workload on this host's CPU;
 * parts: the other entry points at their workloads (bulk scan, 8-layer decode
-  step, chunked SSD, SSD-form decode step), each with its own kernel roofline.
+  step, chunked SSD, SSD-form decode step, the whole layer forward with its
+  two projection GEMMs), each with its own kernel roofline.
 Counters of HBM traffic come from rocprofv3 runs recorded in profiles/; each
 is reported only while its kernel's sources still hash to the recorded value.
 """
@@ -60,7 +61,8 @@ def parse():
                     help="time segments per sequence for the scan (0: the library's choice)")
     ap.add_argument("--no-parts", action="store_true", help="skip the decode / SSD / other-scan lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--only", choices=("prefill", "bulk", "decode", "ssd", "ssd_decode", "copy"), default=None,
+    ap.add_argument("--only", choices=("prefill", "bulk", "decode", "ssd", "ssd_decode", "layer", "in_proj", "out_proj",
+                                       "copy"), default=None,
                     help="run just this workload's timed loop, no JSON line (for profiler runs); 'copy' "
                          "copies 1 GiB device to device, the calibration for the HBM byte counters")
     return ap.parse_args()
@@ -81,6 +83,7 @@ KERNEL_SOURCES = {
     "scan_main_prefill": SCAN_SOURCES, "scan_pass1_prefill": SCAN_SOURCES,
     "scan_main_bulk": SCAN_SOURCES, "scan_pass1_bulk": SCAN_SOURCES,
     "decode": ("decode_step.hip",), "ssd": ("ssd_chunk.hip",), "ssd_decode": ("ssd_decode.hip",),
+    "gemm_in_proj": ("gemm.hip",), "gemm_out_proj": ("gemm.hip",),
 }
 
 
@@ -356,6 +359,39 @@ def ssd_calls(torch, ssm, W, device):
                         flops=flops)
 
 
+def layer_calls(torch, ssm, W, device):
+    """The whole Axon-SSM layer forward at the page's sizes (batch 1, 2048
+    tokens, D 2560, E 7680, N 16), random bf16 weights, bf16 output."""
+    w = W.layer_prefill()
+    o, d = w.opts, w.dims
+    args = [dev_tensor(torch, w, k, device) for k in ("hidden", "W_in", "conv_w", "W_x", "dt_w", "A", "W_out")]
+    T, Dm, E, N = d["batch"] * d["seqlen"], d["d_model"], d["dim"], d["d_state"]
+    out = torch.empty((d["batch"], d["seqlen"], Dm), dtype=torch.bfloat16, device=device)
+    call = ssm.layer_fwd(*args, dt_bias=dev_tensor(torch, w, "dt_bias", device), D=dev_tensor(torch, w, "D", device),
+                         dt_min=o["dt_min"], dt_max=o["dt_max"], out=out, prepare=True)
+    # dense flops of the projections plus the scan's per channel-step work
+    flops = 2 * T * Dm * 2 * E + 2 * T * E * (2 * N + 1) + 2 * T * E * Dm + FLOPS_PER_CH_STEP["prefill"] * T * E
+    return [call], dict(batch=d["batch"], seq_len=d["seqlen"], d_model=Dm, dim=E, d_state=N, flops=flops)
+
+
+GEMM_SHAPES = {"in_proj": (2048, 2560, 15360, "bf16"), "out_proj": (2048, 7680, 2560, "f32")}
+
+
+def gemm_calls(torch, ssm, which, device):
+    """One layer projection through ssm_linear_fwd at the layer prefill's shape:
+    in_proj (2048 x 2560 -> 15360, bf16 input) or out_proj (2048 x 7680 -> 2560,
+    fp32 input entering as a bf16 value/remainder pair)."""
+    M, K, N, xdt = GEMM_SHAPES[which]
+    g = torch.Generator(device="cpu").manual_seed(46)
+    x = torch.randn((M, K), generator=g).to(device, torch.bfloat16 if xdt == "bf16" else torch.float32)
+    wt = (torch.randn((N, K), generator=g) / K ** 0.5).to(device, torch.bfloat16)
+    out = torch.empty((M, N), dtype=torch.float32, device=device)
+    call = ssm.linear_fwd(x, wt, out=out, prepare=True)
+    # MFMA work: a value/remainder pair doubles the products of an fp32 input
+    return [call], dict(M=M, K=K, N=N, x_dtype=xdt, flops=2 * M * N * K,
+                        mfma_flops=2 * M * N * K * (2 if xdt == "f32" else 1))
+
+
 def roof_hbm(nbytes, kernel_ms, traffic):
     gbs = nbytes / (kernel_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -419,6 +455,17 @@ def main():
         per_call = graph_time(torch, graph, launches, a.steps)
         log(f"ssd_decode: {per_call * 1e3:.2f} us per step ({launches} launches per graph, {a.steps} replays), "
             f"{cfg['bytes'] / (per_call * 1e-3) / 1e9:.0f} GB/s")
+        return
+    if a.only == "layer":
+        calls, cfg = layer_calls(torch, ssm, W, dev)
+        wall, kmean, _ = timed_loop(torch, ssm, calls, a.steps, a.warmup)
+        log(f"layer: {wall:.3f} ms/step, {kmean * 1e3:.1f} us per layer (events around the whole layer)")
+        return
+    if a.only in ("in_proj", "out_proj"):
+        calls, cfg = gemm_calls(torch, ssm, a.only, dev)
+        wall, kmean, _ = timed_loop(torch, ssm, calls, a.steps, a.warmup)
+        log(f"{a.only}: {wall:.3f} ms/step, main GEMM kernel {kmean * 1e3:.1f} us, "
+            f"{cfg['flops'] / (kmean * 1e-3) / 1e12:.0f} TFLOP/s")
         return
     if a.only == "ssd":
         calls, cfg = ssd_calls(torch, ssm, W, dev)
@@ -521,6 +568,32 @@ def main():
             "timing": "HIP graph of 8 tokens x 4 state sets, events around 8 replays",
             "config": {k: cfg5[k] for k in ("batch", "nheads", "headdim", "ngroups", "d_state", "layers")}}
         del graph
+        torch.cuda.empty_cache()
+
+        log("part: whole layer forward (in_proj, x_proj, scan, out_proj)")
+        c6, cfg6 = layer_calls(torch, ssm, W, dev)
+        wall6, km6, _ = timed_loop(torch, ssm, c6, 10, 2)
+        tok6 = cfg6["batch"] * cfg6["seq_len"]
+        gemms = {}
+        for which in ("in_proj", "out_proj"):
+            cg, cfgg = gemm_calls(torch, ssm, which, dev)
+            _, kmg, _ = timed_loop(torch, ssm, cg, 10, 2)
+            tf = cfgg["flops"] / (kmg * 1e-3) / 1e12
+            gemms[which] = {
+                "kernel_us": round(kmg * 1e3, 2),
+                "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                             "traffic": recorded_traffic(f"gemm_{which}")},
+                "mfma_work_frac": round(cfgg["mfma_flops"] / (kmg * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                "config": {k: cfgg[k] for k in ("M", "K", "N", "x_dtype")}}
+            del cg
+        parts["layer_forward"] = {
+            "tokens_per_s": round(tok6 / (wall6 * 1e-3), 1), "ms_per_call": round(wall6, 4),
+            "us_per_layer": round(km6 * 1e3, 2),
+            "tflops": round(cfg6["flops"] / (km6 * 1e-3) / 1e12, 1),
+            "projections": gemms,
+            "config": {k: cfg6[k] for k in ("batch", "seq_len", "d_model", "dim", "d_state")}}
+        del c6
         torch.cuda.empty_cache()
         out["parts"] = parts
 

@@ -76,8 +76,11 @@ __device__ __forceinline__ int xcd_tile() {
 // second: lane l supplies row l % 32 of its operand at k = 8 (l / 32) .. + 7,
 // and holds in accumulator register r the output (n = 8 (r / 4) + 4 (l / 32)
 // + r % 4, m = l % 32) of the block, i.e. four runs of 4 consecutive columns.
+#ifndef GEMM_WPE
+#define GEMM_WPE 1
+#endif
 template <typename AT, typename OT, int GM, int GN, int BK, bool EDGE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GEMM_WPE, GEMM_WPE))) void gemm_kernel(GemmArgs g) {
   constexpr bool kSplit = std::is_same<AT, float>::value;
   static_assert(BK % 16 == 0, "whole MFMA K steps");
   using C = Cfg<GM, GN, BK, kSplit>;
