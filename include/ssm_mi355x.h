@@ -56,6 +56,12 @@ extern "C" {
 /* element types (int32 fields in the structs below) */
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
 
+/* How B is discretized.  SSM_EULER: dB u = dt B u (the "dB * x_t" of the
+ * Axon-SSM page's kernel section and the dt[s] x[s] of the velog page's chunk
+ * formula).  SSM_ZOH: the zero-order hold of the molayo page's "Technical
+ * details", dB u = ((e^{dt A} - 1) / A) B u.  The decay is e^{dt A} in both. */
+typedef enum { SSM_EULER = 0, SSM_ZOH = 1 } ssm_discretization_t;
+
 /* return codes */
 typedef enum {
   SSM_OK = 0,
@@ -98,6 +104,7 @@ typedef enum {
  *   time_split    0: the library chooses; >= 1: split the sequence into at most that
  *                 many segments scanned in parallel and combined (at most 32; each
  *                 segment keeps at least 4 steps)
+ *   discretization SSM_EULER or SSM_ZOH (see ssm_discretization_t)
  * Supported: N = 16.  L = 0 only copies the state/cache inputs to the outputs.
  * ---------------------------------------------------------------------- */
 typedef struct ssm_scan_params {
@@ -131,6 +138,7 @@ typedef struct ssm_scan_params {
   int32_t time_split;
   void *workspace;
   size_t workspace_bytes;
+  int32_t discretization; /* SSM_EULER (0): dB u = dt B u; SSM_ZOH (1): ((e^{dt A} - 1) / A) B u */
 } ssm_scan_params_t;
 
 ssm_status_t ssm_scan_fwd(const ssm_scan_params_t *p, void *stream);
@@ -175,6 +183,7 @@ typedef struct ssm_decode_params {
   float *ssm_state;
   void *y;
   int32_t y_dtype;
+  int32_t discretization; /* as in ssm_scan_params_t */
 } ssm_decode_params_t;
 
 ssm_status_t ssm_decode_step(const ssm_decode_params_t *p, void *stream);

@@ -207,14 +207,14 @@ def selective_scan(u, dt, A, B, C, D=None, z=None, ssm_state=None, discretizatio
 
 def ssm_layer_scan(x, A, B, C, *, D=None, z=None, conv_w=None, conv_b=None, conv_cache=None,
                    dt=None, dt_raw=None, dt_w=None, dt_bias=None, dt_softplus=True,
-                   dt_min=None, dt_max=None, ssm_state=None):
+                   dt_min=None, dt_max=None, ssm_state=None, discretization="euler"):
     """The scan stage of the Axon-SSM layer (page "Axon-SSM", "Algorithm"), from
     x_branch to the gated output, plus the decode cache.
 
     * conv_w (E, K) given: u = SiLU(causal_depthwise_conv1d(x)); else u = x.
     * dt: either dt (Bt, L, E) given directly, or dt_raw (Bt, L) with dt_w (E)
       (the rank-1 dt_proj).  Then compute_dt(dt_bias, softplus, [dt_min, dt_max]).
-    * selective_scan(u, dt, A, B, C, D, z, ssm_state).
+    * selective_scan(u, dt, A, B, C, D, z, ssm_state, discretization).
 
     Returns (y, ssm_state_out, conv_cache_out or None).
     """
@@ -228,13 +228,13 @@ def ssm_layer_scan(x, A, B, C, *, D=None, z=None, conv_w=None, conv_b=None, conv
     else:
         pre = _f64(dt)
     dtv = compute_dt(pre, dt_bias, dt_min, dt_max, use_softplus=dt_softplus)
-    y, h = selective_scan(u, dtv, A, B, C, D=D, z=z, ssm_state=ssm_state)
+    y, h = selective_scan(u, dtv, A, B, C, D=D, z=z, ssm_state=ssm_state, discretization=discretization)
     return y, h, cache_out
 
 
 def decode_step(x_t, A, B_t, C_t, *, conv_cache, ssm_state, D=None, z_t=None, conv_w=None,
                 conv_b=None, dt_t=None, dt_raw_t=None, dt_w=None, dt_bias=None,
-                dt_softplus=True, dt_min=None, dt_max=None):
+                dt_softplus=True, dt_min=None, dt_max=None, discretization="euler"):
     """One decode step (Axon-SSM page, "Autoregressive decoding", step 2): concat
     conv_cache with the new token, run exactly one scan step from ssm_state and
     return the updated caches.  It is ssm_layer_scan with L = 1.
@@ -249,7 +249,7 @@ def decode_step(x_t, A, B_t, C_t, *, conv_cache, ssm_state, D=None, z_t=None, co
         dt=None if dt_t is None else _f64(dt_t)[:, None, :],
         dt_raw=None if dt_raw_t is None else _f64(dt_raw_t)[:, None],
         dt_w=dt_w, dt_bias=dt_bias, dt_softplus=dt_softplus, dt_min=dt_min, dt_max=dt_max,
-        ssm_state=ssm_state)
+        ssm_state=ssm_state, discretization=discretization)
     return y[:, 0, :], cache, h
 
 

@@ -33,6 +33,7 @@ class ScanParams(ctypes.Structure):
         ("A", _vp), ("B", _vp), ("C", _vp), ("bc_dtype", _i32), ("D", _vp), ("z", _vp), ("z_dtype", _i32),
         ("ssm_state_in", _vp), ("ssm_state_out", _vp), ("y", _vp), ("y_dtype", _i32), ("time_split", _i32),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("discretization", _i32),
     ]
 
 
@@ -44,6 +45,7 @@ class DecodeParams(ctypes.Structure):
         ("dt_softplus", _i32), ("dt_min", _f32), ("dt_max", _f32), ("A", _vp), ("B", _vp), ("C", _vp),
         ("bc_dtype", _i32), ("D", _vp), ("z", _vp), ("z_dtype", _i32), ("ssm_state", _vp), ("y", _vp),
         ("y_dtype", _i32),
+        ("discretization", _i32),
     ]
 
 
@@ -195,6 +197,13 @@ def _ptr(t, name, shape=None, dtype=None, device=None):
     return t.data_ptr() if t.numel() > 0 else None
 
 
+def _discretization(name):
+    codes = {"euler": 0, "zoh": 1}
+    if name not in codes:
+        raise ValueError(f"discretization must be one of {sorted(codes)}, got {name!r}")
+    return codes[name]
+
+
 def _stream(device, stream):
     s = stream if stream is not None else torch.cuda.current_stream(device)
     return ctypes.c_void_p(s.cuda_stream)
@@ -234,8 +243,9 @@ def _bound(v, default):
 def scan_fwd(x, A, B, C, dt, *, D=None, z=None, conv_w=None, conv_b=None, conv_cache_in=None,
              conv_cache_out=None, dt_rank1=False, dt_w=None, dt_bias=None, dt_softplus=True,
              dt_min=None, dt_max=None, ssm_state_in=None, ssm_state_out=None, y=None,
-             y_dtype=None, time_split=0, workspace=None, stream=None, prepare=False):
-    """Full-sequence selective scan (ssm_scan_fwd).  Returns y (batch, L, E), or
+             y_dtype=None, time_split=0, workspace=None, discretization="euler", stream=None, prepare=False):
+    """Full-sequence selective scan (ssm_scan_fwd); discretization "euler" (dt B u) or "zoh"
+    (((e^{dt A} - 1) / A) B u).  Returns y (batch, L, E), or
     with prepare=True a Call that enqueues this same call again on each run()."""
     L_ = lib()
     batch, seqlen, dim = x.shape
@@ -274,6 +284,7 @@ def scan_fwd(x, A, B, C, dt, *, D=None, z=None, conv_w=None, conv_b=None, conv_c
     p.y = _ptr(y, "y", (batch, seqlen, dim), device=dev)
     p.y_dtype = _code(y, "y")
     p.time_split = int(time_split)
+    p.discretization = _discretization(discretization)
     need = L_.ssm_scan_workspace_size(ctypes.byref(p))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -287,8 +298,8 @@ def scan_fwd(x, A, B, C, dt, *, D=None, z=None, conv_w=None, conv_b=None, conv_c
 
 def decode_step(x, A, B, C, dt, ssm_state, *, conv_cache=None, D=None, z=None, conv_w=None, conv_b=None,
                 dt_rank1=False, dt_w=None, dt_bias=None, dt_softplus=True, dt_min=None, dt_max=None,
-                y=None, y_dtype=None, stream=None, prepare=False):
-    """One decode step (ssm_decode_step): updates ssm_state and conv_cache in place, returns y (batch, E)
+                y=None, y_dtype=None, discretization="euler", stream=None, prepare=False):
+    """One decode step (ssm_decode_step; discretization as in scan_fwd): updates ssm_state and conv_cache in place, returns y (batch, E)
     (with prepare=True, a Call that enqueues this same step again on each run())."""
     L_ = lib()
     batch, dim = x.shape
@@ -324,6 +335,7 @@ def decode_step(x, A, B, C, dt, ssm_state, *, conv_cache=None, D=None, z=None, c
     p.ssm_state = _ptr(ssm_state, "ssm_state", (batch, dim, d_state), f32, dev)
     p.y = _ptr(y, "y", (batch, dim), device=dev)
     p.y_dtype = _code(y, "y")
+    p.discretization = _discretization(discretization)
     call = Call(L_.ssm_decode_step, p, _stream(dev, stream), y, (x, A, B, C, dt, ssm_state, conv_cache, D, z,
                                                                 conv_w, conv_b, dt_w, dt_bias))
     return call if prepare else call.run()

@@ -101,6 +101,7 @@ ssm::ScanLaunch scan_variant(const ssm_scan_params_t* p) {
   l.bc_dtype = p->bc_dtype;
   l.dt_mode = p->dt_rank1 ? 0 : (p->dt_dtype == SSM_BF16 ? 2 : 1);
   l.conv = p->conv_w != nullptr;
+  l.zoh = p->discretization == SSM_ZOH;
   l.k.has_z = p->z ? 1 : 0;
   return l;
 }
@@ -129,6 +130,8 @@ ssm_status_t scan_check(const ssm_scan_params_t* p) {
   if (!p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "params");
   if (p->struct_size != sizeof(ssm_scan_params_t))
     return fail(SSM_ERR_INVALID_ARG, "%s does not match this library", "struct_size");
+  if (p->discretization != SSM_EULER && p->discretization != SSM_ZOH)
+    return fail(SSM_ERR_INVALID_ARG, "%s must be SSM_EULER or SSM_ZOH", "discretization");
   if (p->batch < 0 || p->seqlen < 0 || p->dim <= 0)
     return fail(SSM_ERR_INVALID_ARG, "%s: negative size or dim <= 0", "batch/seqlen/dim");
   if (p->d_state <= 0) return fail(SSM_ERR_INVALID_ARG, "%s must be positive", "d_state");
@@ -197,6 +200,8 @@ ssm_status_t decode_check(const ssm_decode_params_t* p) {
   if (!p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "params");
   if (p->struct_size != sizeof(ssm_decode_params_t))
     return fail(SSM_ERR_INVALID_ARG, "%s does not match this library", "struct_size");
+  if (p->discretization != SSM_EULER && p->discretization != SSM_ZOH)
+    return fail(SSM_ERR_INVALID_ARG, "%s must be SSM_EULER or SSM_ZOH", "discretization");
   if (p->batch < 0 || p->dim <= 0) return fail(SSM_ERR_INVALID_ARG, "%s: negative size or dim <= 0", "batch/dim");
   if (p->d_state <= 0) return fail(SSM_ERR_INVALID_ARG, "%s must be positive", "d_state");
   if (p->d_state != ssm::kScanN) return fail(SSM_ERR_UNSUPPORTED, "%s must be 16", "d_state");
@@ -579,6 +584,7 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_params_t* p, void* stream) {
   l.bc_dtype = v.bc_dtype;
   l.dt_mode = v.dt_mode;
   l.conv = v.conv;
+  l.zoh = v.zoh;
   l.B = p->B;
   l.C = p->C;
   l.bc_out = static_cast<float*>(p->workspace);
@@ -623,6 +629,7 @@ ssm_status_t ssm_decode_step(const ssm_decode_params_t* p, void* stream) {
   l.bc_dtype = p->bc_dtype;
   l.dt_mode = p->dt_rank1 ? 0 : (p->dt_dtype == SSM_BF16 ? 2 : 1);
   l.conv = p->conv_w != nullptr;
+  l.zoh = p->discretization == SSM_ZOH;
   return hip_status(ssm::launch_decode(l, static_cast<hipStream_t>(stream)));
 }
 

@@ -42,7 +42,8 @@ __device__ __forceinline__ void load4(const bf16s* p, float (&v)[4]) {
   v[3] = __uint_as_float(r.y & 0xffff0000u);
 }
 
-template <typename XT, typename YT, typename BT, int DTM, bool CONV>
+// ZOH: B enters as ((e^{dt A} - 1) / A) B u instead of dt B u.
+template <typename XT, typename YT, typename BT, int DTM, bool CONV, bool ZOH>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeKernelArgs a) {
   using DT = typename std::conditional<DTM == 2, bf16s, float>::type;
   const int q = threadIdx.x & 3;
@@ -90,7 +91,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeKernelArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float an = exp2_fast(dt * (av[j] * kLog2e));
-    hout[j] = fmaf(an, hin[j], dtu * bq[j]);
+    if (ZOH) {
+      const float coef = dt * zoh_phi(dt * av[j], an);
+      hout[j] = fmaf(an, hin[j], (coef * u) * bq[j]);
+    } else {
+      hout[j] = fmaf(an, hin[j], dtu * bq[j]);
+    }
     acc = fmaf(cq4[j], hout[j], acc);
   }
   acc += __shfl_xor(acc, 1, 4);
@@ -114,10 +120,16 @@ hipError_t go(const DecodeLaunch& l, hipStream_t s) {
   const size_t total = static_cast<size_t>(l.k.batch) * l.k.dim;
   const unsigned blocks = static_cast<unsigned>((total + 63) / 64);
   return timed_launch(s, [&] {
-    if (l.conv)
-      hipLaunchKernelGGL((decode_kernel<XT, YT, BT, DTM, true>), dim3(blocks), dim3(256), 0, s, l.k);
-    else
-      hipLaunchKernelGGL((decode_kernel<XT, YT, BT, DTM, false>), dim3(blocks), dim3(256), 0, s, l.k);
+    if (l.zoh) {
+      if (l.conv)
+        hipLaunchKernelGGL((decode_kernel<XT, YT, BT, DTM, true, true>), dim3(blocks), dim3(256), 0, s, l.k);
+      else
+        hipLaunchKernelGGL((decode_kernel<XT, YT, BT, DTM, false, true>), dim3(blocks), dim3(256), 0, s, l.k);
+    } else if (l.conv) {
+      hipLaunchKernelGGL((decode_kernel<XT, YT, BT, DTM, true, false>), dim3(blocks), dim3(256), 0, s, l.k);
+    } else {
+      hipLaunchKernelGGL((decode_kernel<XT, YT, BT, DTM, false, false>), dim3(blocks), dim3(256), 0, s, l.k);
+    }
   });
 }
 

@@ -113,7 +113,9 @@ __device__ __forceinline__ void decay(float dt, float al0, const float4* al2, fl
 
 enum Mode { kPass1 = 1, kMain = 2 };
 
-template <typename XT, typename YT, int DTM, bool CONV, bool GATE>
+// ZOH: B enters as ((e^{dt A} - 1) / A) B u (zero-order hold) instead of
+// dt B u.
+template <typename XT, typename YT, int DTM, bool CONV, bool GATE, bool ZOH>
 struct Scan {
   using DT = typename std::conditional<DTM == 2, bf16s, float>::type;
   using XIO = BufIO<XT>;
@@ -215,7 +217,8 @@ struct Scan {
   // dt for the segment's decay product.
   template <bool POW, bool FULL>
   __device__ __forceinline__ void step(int t, const Tile& T, int i, float (&h)[kScanN], float (&win)[3],
-                                       float& sdt, const float (&asat)[kScanN], float (&bv)[kScanN]) const {
+                                       float& sdt, const float (&asat)[kScanN], const float (&zsat)[kScanN],
+                                       float (&bv)[kScanN]) const {
     constexpr bool has_z = FULL && GATE;
     float cv[kScanN];
     if (FULL) {
@@ -242,9 +245,14 @@ struct Scan {
     const float gate = has_z ? silu(XIO::f32(T.z[i])) : 1.0f;
     if (__all(pre >= sat_pre)) {
       if (!FULL) sdt += dt_max;
-      const float dtu = dt_max * u;
+      if (ZOH) {
 #pragma unroll
-      for (int n = 0; n < kScanN; ++n) h[n] = fmaf(dtu, bv[n], asat[n] * h[n]);
+        for (int n = 0; n < kScanN; ++n) h[n] = fmaf(zsat[n] * u, bv[n], asat[n] * h[n]);
+      } else {
+        const float dtu = dt_max * u;
+#pragma unroll
+        for (int n = 0; n < kScanN; ++n) h[n] = fmaf(dtu, bv[n], asat[n] * h[n]);
+      }
     } else {
       float dt;
       if (dt_softplus) {
@@ -261,8 +269,23 @@ struct Scan {
       const float dtu = dt * u;
       float dA[kScanN];
       decay<POW>(dt, c.al0, al2, dA);
+      if (ZOH) {
+        const int lane = threadIdx.x & 63;
 #pragma unroll
-      for (int n = 0; n < kScanN; ++n) h[n] = fmaf(dtu, bv[n], dA[n] * h[n]);
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = al2[q * 64 + lane];  // A log2(e)
+          const float av[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int n = 4 * q + r;
+            const float coef = dt * zoh_phi(dt * av[r] * kLn2, dA[n]);
+            h[n] = fmaf(coef * u, bv[n], dA[n] * h[n]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < kScanN; ++n) h[n] = fmaf(dtu, bv[n], dA[n] * h[n]);
+      }
       // keeps this update in its branch (merged with the other one, the decay
       // factors would be copied into common registers every step)
 #pragma unroll
@@ -290,10 +313,11 @@ struct Scan {
   // second set of SGPRs).
   template <bool POW, bool FULL>
   __device__ __forceinline__ void block(int tb, const Tile& T, float (&h)[kScanN], float (&win)[3],
-                                        float& sdt, const float (&asat)[kScanN], float (&bv)[kScanN]) const {
+                                        float& sdt, const float (&asat)[kScanN], const float (&zsat)[kScanN],
+                                        float (&bv)[kScanN]) const {
 #pragma unroll
     for (int i = 0; i < kBlk; ++i) {
-      step<POW, FULL>(tb + i, T, i, h, win, sdt, asat, bv);
+      step<POW, FULL>(tb + i, T, i, h, win, sdt, asat, zsat, bv);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -301,10 +325,11 @@ struct Scan {
   // The steps tb .. t1-1 (fewer than kBlk) of an already loaded tile.
   template <bool POW, bool FULL>
   __device__ __forceinline__ void partial(int tb, int t1, const Tile& T, float (&h)[kScanN], float (&win)[3],
-                                          float& sdt, const float (&asat)[kScanN], float (&bv)[kScanN]) const {
+                                          float& sdt, const float (&asat)[kScanN], const float (&zsat)[kScanN],
+                                        float (&bv)[kScanN]) const {
 #pragma unroll
     for (int i = 0; i < kBlk - 1; ++i) {
-      if (tb + i < t1) step<POW, FULL>(tb + i, T, i, h, win, sdt, asat, bv);
+      if (tb + i < t1) step<POW, FULL>(tb + i, T, i, h, win, sdt, asat, zsat, bv);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -318,6 +343,20 @@ struct Scan {
     const int nfull = (t1 - t0) / kBlk;
     float asat[kScanN];             // exp(dt_max A[e, n]): the decay on the upper clip
     decay<POW>(dt_max, c.al0, al2, asat);
+    float zsat[kScanN];             // ZOH: (exp(dt_max A[e, n]) - 1) / A[e, n]
+    if (ZOH) {
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = al2[q * 64 + lane];
+        const float av[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) zsat[4 * q + r] = dt_max * zoh_phi(dt_max * av[r] * kLn2, asat[4 * q + r]);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < kScanN; ++n) zsat[n] = 0.0f;
+    }
     float bv[kScanN];               // B of the current step
     load_b(t0, bv);
     Tile A, B;
@@ -327,22 +366,22 @@ struct Scan {
 #pragma unroll 1
     for (; k + 2 <= nfull; k += 2) {
       load_block<FULL>(tb + kBlk, B);
-      block<POW, FULL>(tb, A, h, win, sdt, asat, bv);
+      block<POW, FULL>(tb, A, h, win, sdt, asat, zsat, bv);
       load_block<FULL>(tb + 2 * kBlk, A);
-      block<POW, FULL>(tb + kBlk, B, h, win, sdt, asat, bv);
+      block<POW, FULL>(tb + kBlk, B, h, win, sdt, asat, zsat, bv);
       tb += 2 * kBlk;
     }
     if (k < nfull) {
       load_block<FULL>(tb + kBlk, B);
-      block<POW, FULL>(tb, A, h, win, sdt, asat, bv);
-      partial<POW, FULL>(tb + kBlk, t1, B, h, win, sdt, asat, bv);
+      block<POW, FULL>(tb, A, h, win, sdt, asat, zsat, bv);
+      partial<POW, FULL>(tb + kBlk, t1, B, h, win, sdt, asat, zsat, bv);
     } else {
-      partial<POW, FULL>(tb, t1, A, h, win, sdt, asat, bv);
+      partial<POW, FULL>(tb, t1, A, h, win, sdt, asat, zsat, bv);
     }
   }
 };
 
-template <typename XT, typename YT, int DTM, bool CONV, bool GATE, int MODE>
+template <typename XT, typename YT, int DTM, bool CONV, bool GATE, bool ZOH, int MODE>
 __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
   const int lane = threadIdx.x;
   // block -> (segment, batch, channel group), channel groups fastest: the
@@ -384,7 +423,7 @@ __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
     c.cw0 = c.cw1 = c.cw2 = c.cw3 = c.cb = 0.0f;
   }
   const bool use_pow = __all(prog);
-  const Scan<XT, YT, DTM, CONV, GATE> S(a, c, s_al2);
+  const Scan<XT, YT, DTM, CONV, GATE, ZOH> S(a, c, s_al2);
   const int t0 = seg * a.seg_len;
   const int t1 = min(t0 + a.seg_len, a.seqlen);
   float win[3] = {0.0f, 0.0f, 0.0f};
@@ -437,13 +476,13 @@ __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
   }
 }
 
-template <typename XT, typename YT, int DTM, bool CONV, bool GATE>
+template <typename XT, typename YT, int DTM, bool CONV, bool GATE, bool ZOH>
 hipError_t launch_scan_t(const ScanLaunch& l, hipStream_t stream) {
   const ScanKernelArgs& a = l.k;
   const unsigned groups = static_cast<unsigned>(a.batch) * static_cast<unsigned>(a.n_egroups);
   if (groups == 0) return hipSuccess;
   if (a.nseg > 1) {
-    hipLaunchKernelGGL((scan_kernel<XT, YT, DTM, CONV, GATE, kPass1>), dim3(groups * (a.nseg - 1)), dim3(64), 0,
+    hipLaunchKernelGGL((scan_kernel<XT, YT, DTM, CONV, GATE, ZOH, kPass1>), dim3(groups * (a.nseg - 1)), dim3(64), 0,
                        stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -451,13 +490,19 @@ hipError_t launch_scan_t(const ScanLaunch& l, hipStream_t stream) {
     if (err != hipSuccess) return err;
   }
   return timed_launch(stream, [&] {
-    hipLaunchKernelGGL((scan_kernel<XT, YT, DTM, CONV, GATE, kMain>), dim3(groups * a.nseg), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((scan_kernel<XT, YT, DTM, CONV, GATE, ZOH, kMain>), dim3(groups * a.nseg), dim3(64), 0, stream,
+                       a);
   });
+}
+
+template <typename XT, typename YT, int DTM, bool CONV, bool GATE>
+hipError_t pick_zoh(const ScanLaunch& l, hipStream_t s) {
+  return l.zoh ? launch_scan_t<XT, YT, DTM, CONV, GATE, true>(l, s) : launch_scan_t<XT, YT, DTM, CONV, GATE, false>(l, s);
 }
 
 template <typename XT, typename YT, int DTM, bool CONV>
 hipError_t pick_gate(const ScanLaunch& l, hipStream_t s) {
-  return l.k.has_z ? launch_scan_t<XT, YT, DTM, CONV, true>(l, s) : launch_scan_t<XT, YT, DTM, CONV, false>(l, s);
+  return l.k.has_z ? pick_zoh<XT, YT, DTM, CONV, true>(l, s) : pick_zoh<XT, YT, DTM, CONV, false>(l, s);
 }
 
 template <typename XT, typename YT, int DTM>
@@ -476,12 +521,12 @@ hipError_t pick_dt(const ScanLaunch& l, hipStream_t s) {
 
 // Resident workgroups (one wave each) per CU of the full-segment kernel of a
 // variant, from the runtime's occupancy calculator; cached per variant.
-template <typename XT, typename YT, int DTM, bool CONV, bool GATE>
+template <typename XT, typename YT, int DTM, bool CONV, bool GATE, bool ZOH>
 int occupancy_t() {
   static int cached = 0;
   int n = __atomic_load_n(&cached, __ATOMIC_RELAXED);
   if (n > 0) return n;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_kernel<XT, YT, DTM, CONV, GATE, kMain>, 64, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan_kernel<XT, YT, DTM, CONV, GATE, ZOH, kMain>, 64, 0) !=
           hipSuccess ||
       n <= 0)
     return 0;
@@ -491,7 +536,8 @@ int occupancy_t() {
 
 template <typename XT, typename YT, int DTM, bool CONV>
 int occ_gate(const ScanLaunch& l) {
-  return l.k.has_z ? occupancy_t<XT, YT, DTM, CONV, true>() : occupancy_t<XT, YT, DTM, CONV, false>();
+  if (l.zoh) return l.k.has_z ? occupancy_t<XT, YT, DTM, CONV, true, true>() : occupancy_t<XT, YT, DTM, CONV, false, true>();
+  return l.k.has_z ? occupancy_t<XT, YT, DTM, CONV, true, false>() : occupancy_t<XT, YT, DTM, CONV, false, false>();
 }
 
 template <typename XT, typename YT, int DTM>

@@ -75,6 +75,23 @@ __device__ __forceinline__ float dt_softplus_clip(float pre, float lo, float hi,
 
 __device__ __forceinline__ float dt_clip(float pre, float lo, float hi) { return fminf(fmaxf(pre, lo), hi); }
 
+// phi(z) = (e^z - 1) / z, given e^z (ez), for the zero-order-hold input
+// coefficient (e^{dt A} - 1) / A = dt phi(dt A).  For |z| <= 1/2 the quotient
+// would lose digits to cancellation, so there phi is its Taylor series
+// 1 + z/2 + z^2/6 + ... through z^7/8! (truncation below 2e-7 relative); beyond
+// it the quotient itself is accurate to a few ulp.
+__device__ __forceinline__ float zoh_phi(float z, float ez) {
+  float p = 1.0f / 40320.0f;
+  p = fmaf(p, z, 1.0f / 5040.0f);
+  p = fmaf(p, z, 1.0f / 720.0f);
+  p = fmaf(p, z, 1.0f / 120.0f);
+  p = fmaf(p, z, 1.0f / 24.0f);
+  p = fmaf(p, z, 1.0f / 6.0f);
+  p = fmaf(p, z, 0.5f);
+  p = fmaf(p, z, 1.0f);
+  return fabsf(z) <= 0.5f ? p : (ez - 1.0f) * rcp_fast(z);
+}
+
 // Non-temporal 16-byte load and store, for data touched once per launch (a
 // recurrent state streamed through a decode step).
 typedef float v4f __attribute__((ext_vector_type(4)));

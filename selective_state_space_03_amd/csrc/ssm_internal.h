@@ -67,6 +67,7 @@ struct ScanLaunch {
   int x_dtype, y_dtype, bc_dtype;
   int dt_mode;  // 0 rank-1 f32, 1 full f32, 2 full bf16
   bool conv;
+  bool zoh;     // zero-order-hold input coefficient instead of dt
   const void* B;
   const void* C;
   float* bc_out;  // = k.bc, written by the packing kernel
@@ -112,6 +113,7 @@ struct DecodeLaunch {
   DecodeKernelArgs k;
   int x_dtype, y_dtype, bc_dtype, dt_mode;
   bool conv;
+  bool zoh;  // zero-order-hold input coefficient instead of dt
 };
 
 hipError_t launch_decode(const DecodeLaunch& l, hipStream_t stream);

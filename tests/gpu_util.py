@@ -47,7 +47,7 @@ def check(got, want, tol, what, out_bf16=False):
 # ---------------------------------------------------------------------- scan
 
 def scan_gpu(w: W.Workload, *, y_dtype=torch.float32, time_split=0, state_in=None, cache_in=None,
-             want_state=True, want_cache=True, y_fill=None):
+             want_state=True, want_cache=True, y_fill=None, discretization="euler"):
     o = w.opts
     d = w.dims
     Bt, E, N = d["batch"], d["dim"], d["d_state"]
@@ -61,7 +61,8 @@ def scan_gpu(w: W.Workload, *, y_dtype=torch.float32, time_split=0, state_in=Non
         D=dev_tensor(w, "D"), z=dev_tensor(w, "z"), conv_w=dev_tensor(w, "conv_w") if o["conv"] else None,
         conv_cache_in=cache_in, conv_cache_out=cc, dt_rank1=o["dt_rank1"], dt_w=dev_tensor(w, "dt_w"),
         dt_bias=dev_tensor(w, "dt_bias"), dt_softplus=o["dt_softplus"], dt_min=o["dt_min"], dt_max=o["dt_max"],
-        ssm_state_in=state_in, ssm_state_out=st, y=y, y_dtype=y_dtype, time_split=time_split)
+        ssm_state_in=state_in, ssm_state_out=st, y=y, y_dtype=y_dtype, time_split=time_split,
+        discretization=discretization)
     torch.cuda.synchronize()
     return y, st, cc
 
@@ -76,7 +77,8 @@ def _sel(a, batches, channels, axis_e):
     return a
 
 
-def scan_oracle(w: W.Workload, *, state_in=None, cache_in=None, batches=None, channels=None):
+def scan_oracle(w: W.Workload, *, state_in=None, cache_in=None, batches=None, channels=None,
+                discretization="euler"):
     """Oracle on (a sample of) the workload: batches / channels index lists.
     Channels of the diagonal scan are independent, so a sample is exact."""
     o = w.opts
@@ -95,7 +97,7 @@ def scan_oracle(w: W.Workload, *, state_in=None, cache_in=None, batches=None, ch
     return O.ssm_layer_scan(
         x, ch(f("A")), B, C, D=ch(f("D")), z=z, conv_w=ch(f("conv_w")) if o["conv"] else None,
         conv_cache=cci, dt_bias=ch(f("dt_bias")), dt_softplus=o["dt_softplus"], dt_min=float(o["dt_min"]),
-        dt_max=float(o["dt_max"]), ssm_state=sti, **dt_kw)
+        dt_max=float(o["dt_max"]), ssm_state=sti, discretization=discretization, **dt_kw)
 
 
 # ---------------------------------------------------------------------- SSD

@@ -616,6 +616,37 @@ def pin_layer_projections_linear(orc):
     o3, _, _ = orc.ssm_layer_forward(h2, *args(wts["W_out"]), D=wts["D"], dt_min=1e-3, dt_max=0.3)
     _close(o3[:, :3], o1[:, :3], 0.0, "layer: causal")
 
+
+def pin_zoh_steady_state(orc):
+    """Zero-order hold keeps the continuous system's fixed point: with constant
+    u and B, x' = A x + B u settles at -B u / A, and the ZOH recurrence
+    h <- e^{dt A} h + ((e^{dt A} - 1) / A) B u has exactly that fixed point for
+    any dt (Euler's, dt B u / (1 - e^{dt A}), does not).  After enough steps
+    the state matches it; the one-step coefficient is checked against expm1."""
+    Bt, L, E, N = 1, 1000, 3, 4  # slowest mode: e^{-0.05 * 1000} of the initial gap left
+    A = -np.array([[0.5, 1.0, 2.0, 4.0]] * E)
+    u = np.full((Bt, L, E), 0.7)
+    Bv = np.array([0.3, -1.2, 2.0, 0.9])
+    B = np.tile(Bv, (Bt, L, 1))
+    C = np.ones((Bt, L, N))
+    dt = np.full((Bt, L, E), 0.1)
+    _, h = orc.selective_scan(u, dt, A, B, C, discretization="zoh")
+    want = -Bv[None, :] * 0.7 / A  # (E, N)
+    _close(h[0], want, 1e-7, "zoh steady state")
+    _, h_e = orc.selective_scan(u, dt, A, B, C, discretization="euler")
+    assert np.max(np.abs(h_e[0] - want)) > 1e-3, "euler must not share the zoh fixed point"
+    # one step from zero: h_1 = (e^{dt A} - 1) / A * B u
+    _, h1 = orc.selective_scan(u[:, :1], dt[:, :1], A, B[:, :1], C[:, :1], discretization="zoh")
+    _close(h1[0], np.expm1(0.1 * A) / A * Bv[None, :] * 0.7, 1e-14, "zoh one step")
+    # and the layer scan / decode step pass the choice through
+    y_l, h_l, _ = orc.ssm_layer_scan(u[:, :5], A, B[:, :5], C[:, :5], dt=dt[:, :5], dt_softplus=False,
+                                     discretization="zoh")
+    y_s, h_s = orc.selective_scan(u[:, :5], dt[:, :5], A, B[:, :5], C[:, :5], discretization="zoh")
+    _close(y_l, y_s, 0.0, "layer scan zoh")
+    y_d, _, h_d = orc.decode_step(u[:, 0], A, B[:, 0], C[:, 0], conv_cache=None, ssm_state=None, dt_t=dt[:, 0],
+                                  dt_softplus=False, discretization="zoh")
+    _close(h_d, h1, 0.0, "decode step zoh")
+
 ALL_PINS = [
     pin_unrolled_product_sum,
     pin_recurrence_equals_convolution,
@@ -640,4 +671,5 @@ ALL_PINS = [
     pin_layer_wiring,
     pin_layer_prefill_split,
     pin_layer_projections_linear,
+    pin_zoh_steady_state,
 ]

@@ -54,6 +54,9 @@ MUTATIONS = {
     "layer_state_not_passed": ("dt_min=dt_min, dt_max=dt_max, ssm_state=ssm_state)\n    return linear(y, W_out)",
                                "dt_min=dt_min, dt_max=dt_max, ssm_state=None)\n    return linear(y, W_out)"),
     "linear_weight_transposed": ("return _f64(x) @ _f64(W).T", "return _f64(x) @ _f64(W)[:, ::-1].T"),
+    "zoh_not_passed_by_layer": ("ssm_state=ssm_state, discretization=discretization)\n    return y, h, cache_out",
+                                "ssm_state=ssm_state)\n    return y, h, cache_out"),
+    "zoh_coef_uses_dt": ("dB = (dA - 1.0) / A[None, :, :] * B[:, t, None, :]", "dB = dtt * dA * B[:, t, None, :]"),
     "ssd_seq_gate_dropped": ("    return _gate(out, z), S\n\n\ndef ssd_chunk_scan",
                           "    return out, S\n\n\ndef ssd_chunk_scan"),
 }
