@@ -87,7 +87,9 @@ def test_scan_validation(L):
     ok = _scan()
     assert L.ssm_scan_check(ctypes.byref(ok)) == 0, L.ssm_last_error()
     assert L.ssm_scan_workspace_size(ctypes.byref(ok)) >= 2 * 64 * 32 * 4
+    assert L.ssm_scan_check(ctypes.byref(_scan(discretization=1))) == 0, L.ssm_last_error()
     cases = {
+        "discretization": (_scan(discretization=2), 1),
         "d_state": (_scan(d_state=8), 2),
         "neg": (_scan(batch=-1), 1),
         "bounds": (_scan(dt_min=0.5, dt_max=0.1), 1),
@@ -135,7 +137,9 @@ def _decode(**kw):
 
 def test_decode_validation(L):
     assert L.ssm_decode_check(ctypes.byref(_decode())) == 0, L.ssm_last_error()
+    assert L.ssm_decode_check(ctypes.byref(_decode(discretization=1))) == 0, L.ssm_last_error()
     cases = {
+        "discretization": (_decode(discretization=-1), 1),
         "no_cache": (_decode(conv_cache=None), 1),
         "state_align": (_decode(ssm_state=_addr(8) + 4), 1),
         "d_state": (_decode(d_state=32), 2),
