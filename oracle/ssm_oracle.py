@@ -57,6 +57,7 @@ __all__ = [
     "decode_step",
     "linear",
     "ssm_layer_forward",
+    "ssm_layer_scan_backward",
     "affine_compose",
     "blelloch_exclusive_scan",
     "selective_scan_chunked",
@@ -251,6 +252,121 @@ def decode_step(x_t, A, B_t, C_t, *, conv_cache, ssm_state, D=None, z_t=None, co
         dt_w=dt_w, dt_bias=dt_bias, dt_softplus=dt_softplus, dt_min=dt_min, dt_max=dt_max,
         ssm_state=ssm_state, discretization=discretization)
     return y[:, 0, :], cache, h
+
+
+# --------------------------------------------------------------------------
+# Backward of the scan stage (Mamba/SSM basics page: production training
+# recomputes intermediates in the backward pass instead of storing them)
+# --------------------------------------------------------------------------
+
+def ssm_layer_scan_backward(x, A, B, C, dy, *, D=None, z=None, conv_w=None, conv_b=None, conv_cache=None,
+                            dt=None, dt_raw=None, dt_w=None, dt_bias=None, dt_softplus=True, dt_min=None,
+                            dt_max=None, ssm_state=None, dstate_out=None):
+    """Gradients of a loss L through ssm_layer_scan (Euler form), given
+    dy = dL/dy (Bt, L, E) and optionally dstate_out = dL/dh_L (Bt, E, N).
+
+    Reverse mode written out step by step from the forward's definition:
+      y_t = yc_t * SiLU(z_t),  yc_t = sum_n C_t[n] h_t[n] + D u_t
+      h_t = a_t h_{t-1} + dt_t u_t B_t,  a_t = exp(dt_t A)
+      dt_t = clip(softplus(pre_t)),  pre_t = dt_w r_t + dt_bias  (or dt_raw + dt_bias)
+      u_t = SiLU(xc_t),  xc_t = sum_k w[k] xpad[t + k] + conv_b
+    With G_t = dL/dh_t, walked from t = L-1 down to 0:
+      G_t = dyc_t C_t + a_{t+1} G_{t+1}   (G_L = dstate_out)
+    Returns a dict of gradients (float64) with the inputs' shapes: x, z, B, C,
+    A, D, dt (or dt_raw and dt_w), dt_bias, conv_w, conv_b, conv_cache,
+    ssm_state (None where the input was None)."""
+    x = _f64(x)
+    A = _f64(A)
+    B = _f64(B)
+    C = _f64(C)
+    dy = _f64(dy)
+    Bt, L, E = x.shape
+    N = A.shape[1]
+    # forward intermediates (recomputed here from the inputs)
+    if conv_w is not None:
+        K = _f64(conv_w).shape[1]
+        xc, _ = causal_depthwise_conv1d(x, conv_w, conv_b, conv_cache)
+        u = silu(xc)
+    else:
+        u = x
+    pre = dt_proj_rank1(dt_raw, dt_w) if dt_w is not None else _f64(dt)
+    if dt_bias is not None:
+        pre = pre + _f64(dt_bias)
+    sp = softplus(pre) if dt_softplus else pre
+    lo = -np.inf if dt_min is None else float(dt_min)
+    hi = np.inf if dt_max is None else float(dt_max)
+    dtv = np.minimum(np.maximum(sp, lo), hi)
+    hs = np.zeros((Bt, L + 1, E, N))  # hs[:, t + 1] = h_t, hs[:, 0] = initial state
+    if ssm_state is not None:
+        hs[:, 0] = _f64(ssm_state)
+    for t in range(L):
+        a = np.exp(dtv[:, t, :, None] * A[None])
+        hs[:, t + 1] = a * hs[:, t] + (dtv[:, t] * u[:, t])[..., None] * B[:, t, None, :]
+    yc = np.einsum("bten,btn->bte", hs[:, 1:], C)
+    if D is not None:
+        yc = yc + _f64(D)[None, None, :] * u
+    out = {}
+    if z is not None:
+        zf = _f64(z)
+        sg = sigmoid(zf)
+        gate = zf * sg
+        dyc = dy * gate
+        out["z"] = dy * yc * (sg * (1.0 + zf * (1.0 - sg)))  # SiLU'(z) = s (1 + z (1 - s))
+    else:
+        dyc = dy
+        out["z"] = None
+    du = dyc * _f64(D)[None, None, :] if D is not None else np.zeros_like(u)
+    out["D"] = np.sum(dyc * u, axis=(0, 1)) if D is not None else None
+    dB = np.zeros_like(B)
+    dC = np.einsum("bte,bten->btn", dyc, hs[:, 1:])
+    dA = np.zeros_like(A)
+    ddt = np.zeros((Bt, L, E))
+    G_next = np.zeros((Bt, E, N)) if dstate_out is None else _f64(dstate_out).copy()
+    a_next = np.ones((Bt, E, N))  # a_{t+1}; unused at t = L-1 (G_next is dL/dh_L there)
+    for t in range(L - 1, -1, -1):
+        G = dyc[:, t, :, None] * C[:, t, None, :] + a_next * G_next if t < L - 1 else \
+            dyc[:, t, :, None] * C[:, t, None, :] + G_next
+        a = np.exp(dtv[:, t, :, None] * A[None])
+        h_prev = hs[:, t]
+        # h_t = a h_{t-1} + dt u B
+        ddt[:, t] = np.sum(G * (A[None] * a * h_prev + u[:, t, :, None] * B[:, t, None, :]), axis=-1)
+        du[:, t] += np.sum(G * dtv[:, t, :, None] * B[:, t, None, :], axis=-1)
+        dB[:, t] = np.einsum("ben,be->bn", G, dtv[:, t] * u[:, t])
+        dA += np.sum(G * dtv[:, t, :, None] * a * h_prev, axis=0)
+        G_next, a_next = G, a
+    out["ssm_state"] = a_next * G_next if ssm_state is not None else None
+    out["A"], out["B"], out["C"] = dA, dB, dC
+    # dt = clip(softplus(pre)): the clip passes the gradient strictly inside its bounds
+    inside = (sp > lo) & (sp < hi)
+    dpre = ddt * inside * (sigmoid(pre) if dt_softplus else 1.0)
+    out["dt_bias"] = np.sum(dpre, axis=(0, 1)) if dt_bias is not None else None
+    if dt_w is not None:
+        out["dt_raw"] = np.einsum("bte,e->bt", dpre, _f64(dt_w))
+        out["dt_w"] = np.einsum("bte,bt->e", dpre, _f64(dt_raw))
+        out["dt"] = None
+    else:
+        out["dt"] = dpre
+        out["dt_raw"] = out["dt_w"] = None
+    # u = SiLU(xc), xc = sum_k w[k] xpad[t + k] + b
+    if conv_w is not None:
+        w = _f64(conv_w)
+        s_xc = sigmoid(xc)
+        dxc = du * (s_xc * (1.0 + xc * (1.0 - s_xc)))
+        head = np.zeros((Bt, K - 1, E)) if conv_cache is None else np.transpose(_f64(conv_cache), (0, 2, 1))
+        xpad = np.concatenate([head, x], axis=1)
+        dxpad = np.zeros_like(xpad)
+        dw = np.zeros_like(w)
+        for k in range(K):
+            dxpad[:, k:k + L, :] += dxc * w[None, None, :, k]
+            dw[:, k] = np.sum(dxc * xpad[:, k:k + L, :], axis=(0, 1))
+        out["conv_w"] = dw
+        out["conv_b"] = np.sum(dxc, axis=(0, 1)) if conv_b is not None else None
+        out["x"] = dxpad[:, K - 1:, :]
+        out["conv_cache"] = np.transpose(dxpad[:, :K - 1, :], (0, 2, 1)) if conv_cache is not None else None
+    else:
+        out["x"] = du
+        out["conv_w"] = out["conv_b"] = out["conv_cache"] = None
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -647,6 +647,77 @@ def pin_zoh_steady_state(orc):
                                   dt_softplus=False, discretization="zoh")
     _close(h_d, h1, 0.0, "decode step zoh")
 
+
+def _fd_check(orc, fwd_kwargs, grads, keys, rng, what, eps=1e-6, tol=1e-6):
+    """Central differences of L = sum(dy * y) + sum(dstate_out * h_L) against the
+    backward's gradients, for every element of every input in `keys`."""
+    dy = fwd_kwargs.pop("_dy")
+    dso = fwd_kwargs.pop("_dstate_out")
+
+    def loss(kw):
+        y, h, _ = orc.ssm_layer_scan(**kw)
+        val = float(np.sum(dy * y))
+        if dso is not None:
+            val += float(np.sum(dso * h))
+        return val
+
+    for key in keys:
+        base = np.array(fwd_kwargs[key], dtype=np.float64)
+        num = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            for sgn in (1.0, -1.0):
+                pert = base.copy()
+                pert[idx] += sgn * eps
+                kw = dict(fwd_kwargs)
+                kw[key] = pert
+                num[idx] += sgn * loss(kw)
+        num /= 2 * eps
+        g = grads[key]
+        scale = max(1.0, float(np.max(np.abs(num))))
+        err = float(np.max(np.abs(g - num)))
+        assert err <= tol * scale, f"{what}: d/d{key} max|err| {err:.3e} > {tol:.1e} * {scale:.3e}"
+    fwd_kwargs["_dy"], fwd_kwargs["_dstate_out"] = dy, dso
+
+
+def pin_backward_finite_differences(orc):
+    """The scan-stage backward against central finite differences of the
+    forward, for every input: (1) conv, rank-1 dt with softplus, gate, D,
+    initial state, conv cache and a gradient on the final state, clip bounds
+    out of reach; (2) E-wide dt without softplus and with some steps clipped
+    at either bound, no conv, gate or D."""
+    rng = _rng(81)
+    Bt, L, E, N = 2, 5, 3, 4
+    kw = dict(x=rng.standard_normal((Bt, L, E)), A=-rng.uniform(0.5, 3.0, (E, N)),
+              B=rng.standard_normal((Bt, L, N)), C=rng.standard_normal((Bt, L, N)), D=rng.standard_normal(E),
+              z=rng.standard_normal((Bt, L, E)), conv_w=rng.standard_normal((E, 4)) * 0.5,
+              conv_b=rng.standard_normal(E) * 0.2, conv_cache=rng.standard_normal((Bt, E, 3)),
+              dt_raw=rng.standard_normal((Bt, L)), dt_w=rng.standard_normal(E) * 0.5,
+              dt_bias=rng.standard_normal(E) * 0.5 - 1.0, dt_min=1e-4, dt_max=50.0,
+              ssm_state=rng.standard_normal((Bt, E, N)))
+    kw["_dy"] = rng.standard_normal((Bt, L, E))
+    kw["_dstate_out"] = rng.standard_normal((Bt, E, N))
+    fwd = {k: v for k, v in kw.items() if not k.startswith("_")}
+    g = orc.ssm_layer_scan_backward(dy=kw["_dy"], dstate_out=kw["_dstate_out"], **fwd)
+    names = {"x": "x", "A": "A", "B": "B", "C": "C", "D": "D", "z": "z", "conv_w": "conv_w", "conv_b": "conv_b",
+             "conv_cache": "conv_cache", "dt_raw": "dt_raw", "dt_w": "dt_w", "dt_bias": "dt_bias",
+             "ssm_state": "ssm_state"}
+    _fd_check(orc, kw, {k: g[v] for k, v in names.items()}, list(names), rng, "backward (conv, rank-1 dt)")
+
+    Bt, L, E, N = 1, 6, 2, 3
+    dt_e = rng.uniform(0.02, 0.4, (Bt, L, E))
+    dt_e[0, 1, 0] = 0.005   # below dt_min: clipped, no gradient
+    dt_e[0, 4, 1] = 0.9     # above dt_max
+    kw = dict(x=rng.standard_normal((Bt, L, E)), A=-rng.uniform(0.5, 3.0, (E, N)),
+              B=rng.standard_normal((Bt, L, N)), C=rng.standard_normal((Bt, L, N)), dt=dt_e,
+              dt_bias=np.zeros(E), dt_softplus=False, dt_min=0.01, dt_max=0.5)
+    kw["_dy"] = rng.standard_normal((Bt, L, E))
+    kw["_dstate_out"] = None
+    fwd = {k: v for k, v in kw.items() if not k.startswith("_")}
+    g = orc.ssm_layer_scan_backward(dy=kw["_dy"], **fwd)
+    assert g["dt"][0, 1, 0] == 0.0 and g["dt"][0, 4, 1] == 0.0, "clipped steps carry no dt gradient"
+    _fd_check(orc, kw, {k: g[k] for k in ("x", "A", "B", "C", "dt", "dt_bias")}, ["x", "A", "B", "C", "dt", "dt_bias"],
+              rng, "backward (E-wide dt, clipped)")
+
 ALL_PINS = [
     pin_unrolled_product_sum,
     pin_recurrence_equals_convolution,
@@ -672,4 +743,5 @@ ALL_PINS = [
     pin_layer_prefill_split,
     pin_layer_projections_linear,
     pin_zoh_steady_state,
+    pin_backward_finite_differences,
 ]

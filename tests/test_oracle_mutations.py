@@ -57,6 +57,14 @@ MUTATIONS = {
     "zoh_not_passed_by_layer": ("ssm_state=ssm_state, discretization=discretization)\n    return y, h, cache_out",
                                 "ssm_state=ssm_state)\n    return y, h, cache_out"),
     "zoh_coef_uses_dt": ("dB = (dA - 1.0) / A[None, :, :] * B[:, t, None, :]", "dB = dtt * dA * B[:, t, None, :]"),
+    "bwd_gate_derivative": ("out[\"z\"] = dy * yc * (sg * (1.0 + zf * (1.0 - sg)))", "out[\"z\"] = dy * yc * sg"),
+    "bwd_no_decay_in_G": ("C[:, t, None, :] + a_next * G_next if t < L - 1", "C[:, t, None, :] + G_next if t < L - 1"),
+    "bwd_dA_missing_decay": ("dA += np.sum(G * dtv[:, t, :, None] * a * h_prev, axis=0)",
+                             "dA += np.sum(G * dtv[:, t, :, None] * h_prev, axis=0)"),
+    "bwd_clip_ignored": ("inside = (sp > lo) & (sp < hi)", "inside = np.ones_like(sp, dtype=bool)"),
+    "bwd_conv_taps_reversed": ("dxpad[:, k:k + L, :] += dxc * w[None, None, :, k]",
+                               "dxpad[:, k:k + L, :] += dxc * w[None, None, :, K - 1 - k]"),
+    "bwd_state_in_no_decay": ("out[\"ssm_state\"] = a_next * G_next if", "out[\"ssm_state\"] = G_next if"),
     "ssd_seq_gate_dropped": ("    return _gate(out, z), S\n\n\ndef ssd_chunk_scan",
                           "    return out, S\n\n\ndef ssd_chunk_scan"),
 }
