@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--no-parts", action="store_true", help="skip the decode / SSD / other-scan lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--only", choices=("prefill", "bulk", "decode", "ssd", "ssd_decode", "layer", "in_proj", "out_proj",
-                                       "copy"), default=None,
+                                       "scan_bwd", "copy"), default=None,
                     help="run just this workload's timed loop, no JSON line (for profiler runs); 'copy' "
                          "copies 1 GiB device to device, the calibration for the HBM byte counters")
     return ap.parse_args()
@@ -83,7 +83,7 @@ KERNEL_SOURCES = {
     "scan_main_prefill": SCAN_SOURCES, "scan_pass1_prefill": SCAN_SOURCES,
     "scan_main_bulk": SCAN_SOURCES, "scan_pass1_bulk": SCAN_SOURCES,
     "decode": ("decode_step.hip",), "ssd": ("ssd_chunk.hip",), "ssd_decode": ("ssd_decode.hip",),
-    "gemm_in_proj": ("gemm.hip",), "gemm_out_proj": ("gemm.hip",),
+    "gemm_in_proj": ("gemm.hip",), "gemm_out_proj": ("gemm.hip",), "scan_bwd": ("scan_bwd.hip",),
 }
 
 
@@ -374,6 +374,23 @@ def layer_calls(torch, ssm, W, device):
     return [call], dict(batch=d["batch"], seq_len=d["seqlen"], d_model=Dm, dim=E, d_state=N, flops=flops)
 
 
+def bwd_calls(torch, ssm, W, device):
+    """Backward of the layer-prefill scan (batch 1, 2048 tokens, E 7680, N 16):
+    all gradients, upstream gradient dy ~ N(0,1) fp32."""
+    w = W.scan_prefill()
+    o, d = w.opts, w.dims
+    t = lambda k: dev_tensor(torch, w, k, device)  # noqa: E731
+    g = torch.Generator(device="cpu").manual_seed(47)
+    dy = torch.randn((d["batch"], d["seqlen"], d["dim"]), generator=g).to(device)
+    call = ssm.scan_bwd(t("x"), t("A"), t("B"), t("C"), t("dt"), dy, D=t("D"), z=t("z"), conv_w=t("conv_w"),
+                        dt_rank1=True, dt_w=t("dt_w"), dt_bias=t("dt_bias"), dt_min=o["dt_min"], dt_max=o["dt_max"],
+                        prepare=True)
+    Bt, L, E, N = d["batch"], d["seqlen"], d["dim"], d["d_state"]
+    # algorithmic bytes: inputs x, z (bf16), dy (fp32), r, B, C once; gradients dx, dz (fp32), dB, dC, dr
+    byts = Bt * L * E * (2 + 2 + 4 + 4 + 4) + Bt * L * (4 + 4 + 2 * N * 2 + 2 * N * 4)
+    return [call], dict(batch=Bt, seq_len=L, dim=E, d_state=N, bytes=byts)
+
+
 GEMM_SHAPES = {"in_proj": (2048, 2560, 15360, "bf16"), "out_proj": (2048, 7680, 2560, "f32")}
 
 
@@ -455,6 +472,11 @@ def main():
         per_call = graph_time(torch, graph, launches, a.steps)
         log(f"ssd_decode: {per_call * 1e3:.2f} us per step ({launches} launches per graph, {a.steps} replays), "
             f"{cfg['bytes'] / (per_call * 1e-3) / 1e9:.0f} GB/s")
+        return
+    if a.only == "scan_bwd":
+        calls, cfg = bwd_calls(torch, ssm, W, dev)
+        wall, kmean, _ = timed_loop(torch, ssm, calls, a.steps, a.warmup)
+        log(f"scan_bwd: {wall:.3f} ms/step, main backward kernel {kmean * 1e3:.1f} us")
         return
     if a.only == "layer":
         calls, cfg = layer_calls(torch, ssm, W, dev)
@@ -568,6 +590,22 @@ def main():
             "timing": "HIP graph of 8 tokens x 4 state sets, events around 8 replays",
             "config": {k: cfg5[k] for k in ("batch", "nheads", "headdim", "ngroups", "d_state", "layers")}}
         del graph
+        torch.cuda.empty_cache()
+
+        log("part: backward of the scan stage")
+        c7, cfg7 = bwd_calls(torch, ssm, W, dev)
+        wall7, km7, _ = timed_loop(torch, ssm, c7, 10, 2)
+        tok7 = cfg7["batch"] * cfg7["seq_len"]
+        # the main backward kernel per channel-step: forward recompute (decay 4 exp-lanes x 4 states,
+        # update) and the backward step, counted as in FLOPS_PER_CH_STEP: about 3x the forward's 138
+        ch7 = tok7 * cfg7["dim"]
+        parts["scan_backward"] = {
+            "tokens_per_s": round(tok7 / (wall7 * 1e-3), 1), "ms_per_call": round(wall7, 4),
+            "main_kernel_us": round(km7 * 1e3, 2),
+            "roofline": roof_hbm(cfg7["bytes"], wall7, recorded_traffic("scan_bwd")),
+            "roofline_note": "HBM bytes of the inputs read once and the gradients written once over the whole call",
+            "config": {k: cfg7[k] for k in ("batch", "seq_len", "dim", "d_state")}}
+        del c7
         torch.cuda.empty_cache()
 
         log("part: whole layer forward (in_proj, x_proj, scan, out_proj)")

@@ -237,6 +237,54 @@ size_t ssm_chunk_scan_workspace_size(const ssm_chunk_params_t *p);
 ssm_status_t ssm_chunk_scan_check(const ssm_chunk_params_t *p);
 
 /* ------------------------------------------------------------------------
+ * Backward of ssm_scan_fwd (Euler form) with recomputation (page "Mamba/SSM
+ * basics", the production recipe after "Technical details": intermediate
+ * states are recomputed in the backward pass instead of being stored).  Given
+ * dy = dL/dy (Bt, L, E) dy_dtype and optionally dstate_out = dL/dh_L
+ * (Bt, E, N) f32, writes the gradients of L with respect to the forward's
+ * inputs, all f32 and in the inputs' shapes:
+ *   dx (Bt, L, E); dz (Bt, L, E) when z was given; ddt: (Bt, L) for a rank-1
+ *   dt (gradient of r), else (Bt, L, E); ddt_w (E) for a rank-1 dt; ddt_bias (E);
+ *   dA (E, N); dB, dC (Bt, L, N); dD (E); dconv_w (E, 4), dconv_b (E) and
+ *   dconv_cache (Bt, E, 3) when there is a conv; dstate_in (Bt, E, N).
+ * Any gradient pointer may be NULL (not written).  The forward inputs are the
+ * fields of the same names in ssm_scan_params_t with the same rules; the
+ * clip passes gradient strictly inside (dt_min, dt_max).  Sums over
+ * channels and time are taken in a fixed order (results are deterministic).
+ * The workspace holds ssm_scan_bwd_workspace_size(p) bytes (256-byte aligned).
+ * Supported: N = 16, Euler discretization; dy_dtype f32 or bf16.
+ * ---------------------------------------------------------------------- */
+typedef struct ssm_scan_bwd_params {
+  uint32_t struct_size; /* = sizeof(ssm_scan_bwd_params_t) */
+  int32_t batch, seqlen, dim, d_state, conv_k;
+  const void *x;
+  int32_t x_dtype;
+  const float *conv_w, *conv_b, *conv_cache_in;
+  const void *dt;
+  int32_t dt_dtype, dt_rank1;
+  const float *dt_w, *dt_bias;
+  int32_t dt_softplus;
+  float dt_min, dt_max;
+  const float *A;
+  const void *B, *C;
+  int32_t bc_dtype;
+  const float *D;
+  const void *z;
+  int32_t z_dtype;
+  const float *ssm_state_in;
+  const void *dy;
+  int32_t dy_dtype;
+  const float *dstate_out;
+  float *dx, *dz, *ddt, *ddt_w, *ddt_bias, *dA, *dB, *dC, *dD, *dconv_w, *dconv_b, *dconv_cache, *dstate_in;
+  void *workspace;
+  size_t workspace_bytes;
+} ssm_scan_bwd_params_t;
+
+ssm_status_t ssm_scan_bwd(const ssm_scan_bwd_params_t *p, void *stream);
+size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_params_t *p);
+ssm_status_t ssm_scan_bwd_check(const ssm_scan_bwd_params_t *p);
+
+/* ------------------------------------------------------------------------
  * One decode step of the multi-head scan, in place (page "What is the Mamba
  * model?", section "chunkscan": the state that the chunked scan passes from
  * chunk to chunk, advanced by a chunk of one token).  For each (b, h):
@@ -368,7 +416,7 @@ const char *ssm_status_string(int32_t status);
 const char *ssm_last_error(void);
 int32_t ssm_abi_version(void);
 /* sizeof of a params struct: which = 0 scan, 1 decode, 2 chunk, 3 chunk
- * decode, 4 linear, 5 layer; 0 otherwise. */
+ * decode, 4 linear, 5 layer, 6 scan backward; 0 otherwise. */
 size_t ssm_params_sizeof(int32_t which);
 
 /* Kernel timing for measurement tools.  start and stop are hipEvent_t handles

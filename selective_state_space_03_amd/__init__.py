@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     layer_fwd,
     lib,
     linear_fwd,
+    scan_bwd,
     scan_fwd,
     set_timing_events,
 )

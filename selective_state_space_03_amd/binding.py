@@ -89,6 +89,19 @@ class LayerParams(ctypes.Structure):
     ]
 
 
+class ScanBwdParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("batch", _i32), ("seqlen", _i32), ("dim", _i32), ("d_state", _i32),
+        ("conv_k", _i32), ("x", _vp), ("x_dtype", _i32), ("conv_w", _vp), ("conv_b", _vp), ("conv_cache_in", _vp),
+        ("dt", _vp), ("dt_dtype", _i32), ("dt_rank1", _i32), ("dt_w", _vp), ("dt_bias", _vp), ("dt_softplus", _i32),
+        ("dt_min", _f32), ("dt_max", _f32), ("A", _vp), ("B", _vp), ("C", _vp), ("bc_dtype", _i32), ("D", _vp),
+        ("z", _vp), ("z_dtype", _i32), ("ssm_state_in", _vp), ("dy", _vp), ("dy_dtype", _i32), ("dstate_out", _vp),
+        ("dx", _vp), ("dz", _vp), ("ddt", _vp), ("ddt_w", _vp), ("ddt_bias", _vp), ("dA", _vp), ("dB", _vp),
+        ("dC", _vp), ("dD", _vp), ("dconv_w", _vp), ("dconv_b", _vp), ("dconv_cache", _vp), ("dstate_in", _vp),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 EXPORTED = [
     "ssm_scan_fwd", "ssm_scan_workspace_size", "ssm_scan_check",
     "ssm_decode_step", "ssm_decode_check",
@@ -96,6 +109,7 @@ EXPORTED = [
     "ssm_chunk_decode_step", "ssm_chunk_decode_check",
     "ssm_linear_fwd", "ssm_linear_workspace_size", "ssm_linear_check",
     "ssm_layer_fwd", "ssm_layer_workspace_size", "ssm_layer_check",
+    "ssm_scan_bwd", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd_check",
     "ssm_status_string", "ssm_last_error", "ssm_abi_version", "ssm_params_sizeof", "ssm_set_timing_events",
 ]
 
@@ -142,6 +156,12 @@ def lib() -> ctypes.CDLL:
     L.ssm_layer_workspace_size.restype = ctypes.c_size_t
     L.ssm_layer_check.argtypes = [ctypes.POINTER(LayerParams)]
     L.ssm_layer_check.restype = _i32
+    L.ssm_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdParams), _vp]
+    L.ssm_scan_bwd.restype = _i32
+    L.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanBwdParams)]
+    L.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
+    L.ssm_scan_bwd_check.argtypes = [ctypes.POINTER(ScanBwdParams)]
+    L.ssm_scan_bwd_check.restype = _i32
     L.ssm_status_string.argtypes = [_i32]
     L.ssm_status_string.restype = ctypes.c_char_p
     L.ssm_last_error.argtypes = []
@@ -152,7 +172,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_params_sizeof.restype = ctypes.c_size_t
     L.ssm_set_timing_events.argtypes = [_vp, _vp]
     L.ssm_set_timing_events.restype = None
-    for i, st in enumerate((ScanParams, DecodeParams, ChunkParams, ChunkDecodeParams, LinearParams, LayerParams)):
+    for i, st in enumerate((ScanParams, DecodeParams, ChunkParams, ChunkDecodeParams, LinearParams, LayerParams,
+                            ScanBwdParams)):
         if L.ssm_params_sizeof(i) != ctypes.sizeof(st):
             raise RuntimeError(f"ctypes mirror of params struct {i} does not match the library")
     _lib = L
@@ -501,4 +522,79 @@ def layer_fwd(hidden, w_in, conv_w, w_x, dt_w, A, w_out, *, dt_bias=None, D=None
     call = Call(L_.ssm_layer_fwd, p, _stream(dev, stream), out,
                 (hidden, w_in, conv_w, conv_b, w_x, dt_w, dt_bias, A, D, w_out, conv_cache_in, conv_cache_out,
                  ssm_state_in, ssm_state_out, workspace))
+    return call if prepare else call.run()
+
+
+def scan_bwd(x, A, B, C, dt, dy, *, D=None, z=None, conv_w=None, conv_b=None, conv_cache_in=None, dt_rank1=False,
+             dt_w=None, dt_bias=None, dt_softplus=True, dt_min=None, dt_max=None, ssm_state_in=None,
+             dstate_out=None, workspace=None, stream=None, prepare=False):
+    """Backward of scan_fwd (ssm_scan_bwd): the forward's inputs plus dy (and optionally the gradient on
+    the final state).  Returns a dict of fp32 gradients named after the inputs (x, z, dt, dt_w, dt_bias,
+    A, B, C, D, conv_w, conv_b, conv_cache, ssm_state), present for the inputs that were given, or with
+    prepare=True a Call whose run() enqueues it again (its .out is that dict)."""
+    L_ = lib()
+    batch, seqlen, dim = x.shape
+    d_state = A.shape[1]
+    dev = x.device
+    f32 = torch.float32
+    p = ScanBwdParams()
+    p.struct_size = ctypes.sizeof(ScanBwdParams)
+    p.batch, p.seqlen, p.dim, p.d_state = batch, seqlen, dim, d_state
+    p.conv_k = conv_w.shape[1] if conv_w is not None else 0
+    p.x = _ptr(x, "x", (batch, seqlen, dim), device=dev)
+    p.x_dtype = _code(x, "x")
+    p.conv_w = _ptr(conv_w, "conv_w", (dim, p.conv_k) if conv_w is not None else None, f32, dev)
+    p.conv_b = _ptr(conv_b, "conv_b", (dim,), f32, dev)
+    p.conv_cache_in = _ptr(conv_cache_in, "conv_cache_in", (batch, dim, 3), f32, dev)
+    p.dt_rank1 = 1 if dt_rank1 else 0
+    p.dt = _ptr(dt, "dt", (batch, seqlen) if dt_rank1 else (batch, seqlen, dim), device=dev)
+    p.dt_dtype = _code(dt, "dt")
+    p.dt_w = _ptr(dt_w, "dt_w", (dim,), f32, dev)
+    p.dt_bias = _ptr(dt_bias, "dt_bias", (dim,), f32, dev)
+    p.dt_softplus = 1 if dt_softplus else 0
+    p.dt_min = _bound(dt_min, -math.inf)
+    p.dt_max = _bound(dt_max, math.inf)
+    p.A = _ptr(A, "A", (dim, d_state), f32, dev)
+    p.B = _ptr(B, "B", (batch, seqlen, d_state), device=dev)
+    p.C = _ptr(C, "C", (batch, seqlen, d_state), B.dtype, dev)
+    p.bc_dtype = _code(B, "B")
+    p.D = _ptr(D, "D", (dim,), f32, dev)
+    p.z = _ptr(z, "z", (batch, seqlen, dim), device=dev)
+    p.z_dtype = _code(z, "z") if z is not None else 0
+    p.ssm_state_in = _ptr(ssm_state_in, "ssm_state_in", (batch, dim, d_state), f32, dev)
+    p.dy = _ptr(dy, "dy", (batch, seqlen, dim), device=dev)
+    p.dy_dtype = _code(dy, "dy")
+    p.dstate_out = _ptr(dstate_out, "dstate_out", (batch, dim, d_state), f32, dev)
+    e = lambda *shape: torch.empty(shape, dtype=f32, device=dev)  # noqa: E731
+    g = {"x": e(batch, seqlen, dim), "A": e(dim, d_state), "B": e(batch, seqlen, d_state),
+         "C": e(batch, seqlen, d_state), "dt": e(batch, seqlen) if dt_rank1 else e(batch, seqlen, dim)}
+    if z is not None:
+        g["z"] = e(batch, seqlen, dim)
+    if dt_rank1:
+        g["dt_w"] = e(dim)
+    if dt_bias is not None:
+        g["dt_bias"] = e(dim)
+    if D is not None:
+        g["D"] = e(dim)
+    if conv_w is not None:
+        g["conv_w"] = e(dim, p.conv_k)
+        if conv_b is not None:
+            g["conv_b"] = e(dim)
+        if conv_cache_in is not None:
+            g["conv_cache"] = e(batch, dim, 3)
+    if ssm_state_in is not None:
+        g["ssm_state"] = e(batch, dim, d_state)
+    for key, field in (("x", "dx"), ("z", "dz"), ("dt", "ddt"), ("dt_w", "ddt_w"), ("dt_bias", "ddt_bias"),
+                       ("A", "dA"), ("B", "dB"), ("C", "dC"), ("D", "dD"), ("conv_w", "dconv_w"),
+                       ("conv_b", "dconv_b"), ("conv_cache", "dconv_cache"), ("ssm_state", "dstate_in")):
+        if key in g:
+            setattr(p, field, g[key].data_ptr() if g[key].numel() > 0 else None)
+    need = L_.ssm_scan_bwd_workspace_size(ctypes.byref(p))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    p.workspace = _ptr(workspace, "workspace", device=dev)
+    p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    call = Call(L_.ssm_scan_bwd, p, _stream(dev, stream), g,
+                (x, A, B, C, dt, dy, D, z, conv_w, conv_b, conv_cache_in, dt_w, dt_bias, ssm_state_in, dstate_out,
+                 workspace))
     return call if prepare else call.run()

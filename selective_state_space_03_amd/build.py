@@ -14,7 +14,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libssm_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["api.cpp", "scan_fused.hip", "scan_xy_bb.hip", "scan_xy_bf.hip", "scan_xy_fb.hip", "scan_xy_ff.hip",
-           "decode_step.hip", "ssd_chunk.hip", "ssd_decode.hip", "gemm.hip", "layer.hip"]
+           "decode_step.hip", "ssd_chunk.hip", "ssd_decode.hip", "gemm.hip", "layer.hip", "scan_bwd.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code: the compiler

@@ -521,6 +521,111 @@ ssm_status_t layer_check(const ssm_layer_params_t* p) {
   return scan_check(&sp);
 }
 
+// ---------------------------------------------------------------- scan backward
+
+struct BwdWs {
+  size_t hs, qs, sdt, dxc, pB, pC, pr, pe, pw, total;
+};
+
+BwdWs bwd_ws(const ssm_scan_bwd_params_t* p) {
+  BwdWs o{};
+  const size_t Bt = p->batch, L = p->seqlen, E = p->dim, N = ssm::kScanN;
+  const size_t S = L > 0 ? ssm::bwd_segments(p->seqlen) : 0, G = (E + 15) / 16;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  o.hs = take(Bt * S * E * N * 4);
+  o.qs = take(Bt * S * E * N * 4);
+  o.sdt = take(Bt * S * E * 4);
+  o.dxc = take(p->conv_w ? Bt * L * E * 4 : 0);
+  o.pB = take(Bt * L * G * N * 4);
+  o.pC = take(Bt * L * G * N * 4);
+  o.pr = take(p->dt_rank1 ? Bt * L * G * 4 : 0);
+  o.pe = take(Bt * S * E * ssm::kBwdPe * 4);
+  o.pw = take(p->conv_w ? Bt * ((L + ssm::kConvChunk - 1) / ssm::kConvChunk) * E * 5 * 4 : 0);
+  o.total = off;
+  return o;
+}
+
+ssm_status_t bwd_check(const ssm_scan_bwd_params_t* p) {
+  if (!p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "params");
+  if (p->struct_size != sizeof(ssm_scan_bwd_params_t))
+    return fail(SSM_ERR_INVALID_ARG, "%s does not match this library", "struct_size");
+  if (p->batch < 0 || p->seqlen < 0 || p->dim <= 0) return fail(SSM_ERR_INVALID_ARG, "%s: negative size or dim <= 0", "dims");
+  if (p->d_state != ssm::kScanN) return fail(SSM_ERR_UNSUPPORTED, "%s must be 16", "d_state");
+  if (!valid_dtype(p->x_dtype) || !valid_dtype(p->bc_dtype) || !valid_dtype(p->dt_dtype) ||
+      !valid_dtype(p->dy_dtype) || (p->z && !valid_dtype(p->z_dtype)))
+    return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "x/bc/dt/dy/z_dtype");
+  if (p->z && p->z_dtype != p->x_dtype) return fail(SSM_ERR_UNSUPPORTED, "%s must equal x_dtype", "z_dtype");
+  if (!p->A) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "A");
+  if (p->conv_w) {
+    if (p->conv_k != ssm::kConvK) return fail(SSM_ERR_UNSUPPORTED, "%s must be 4", "conv_k");
+    if (!aligned16(p->conv_w)) return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "conv_w");
+  } else if (p->conv_b || p->conv_cache_in || p->dconv_w || p->dconv_b || p->dconv_cache) {
+    return fail(SSM_ERR_INVALID_ARG, "%s given without conv_w", "conv_b/conv_cache_in/dconv_*");
+  }
+  if (p->dt_rank1) {
+    if (p->dt_dtype != SSM_F32) return fail(SSM_ERR_UNSUPPORTED, "%s: rank-1 dt input must be f32", "dt_dtype");
+    if (!p->dt_w) return fail(SSM_ERR_INVALID_ARG, "%s is NULL with dt_rank1", "dt_w");
+  } else if (p->ddt_w) {
+    return fail(SSM_ERR_INVALID_ARG, "%s needs a rank-1 dt", "ddt_w");
+  }
+  if (p->dz && !p->z) return fail(SSM_ERR_INVALID_ARG, "%s given without z", "dz");
+  ssm_status_t s = check_dt_bounds(p->dt_min, p->dt_max);
+  if (s != SSM_OK) return s;
+  const size_t Bt = p->batch, L = p->seqlen, E = p->dim, N = ssm::kScanN;
+  if (Bt * L * E > 0x7fffffffULL) return fail(SSM_ERR_UNSUPPORTED, "%s too large", "batch*seqlen*dim");
+  if (Bt * L == 0) return SSM_OK;
+  if (!p->x || !p->B || !p->C || !p->dt || !p->dy) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "x/B/C/dt/dy");
+  if (!aligned16(p->A)) return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "A");
+  if ((reinterpret_cast<uintptr_t>(p->B) | reinterpret_cast<uintptr_t>(p->C)) & (p->bc_dtype == SSM_BF16 ? 7 : 15))
+    return fail(SSM_ERR_INVALID_ARG, "%s must be aligned to 4 elements", "B/C");
+  const size_t xe = esize(p->x_dtype);
+  const Range ins[] = {
+      {p->x, Bt * L * E * xe},
+      {p->z, p->z ? Bt * L * E * xe : 0},
+      {p->dt, p->dt_rank1 ? Bt * L * 4 : Bt * L * E * esize(p->dt_dtype)},
+      {p->dy, Bt * L * E * esize(p->dy_dtype)},
+      {p->B, Bt * L * N * esize(p->bc_dtype)},
+      {p->C, Bt * L * N * esize(p->bc_dtype)},
+      {p->A, E * N * 4},
+      {p->ssm_state_in, p->ssm_state_in ? Bt * E * N * 4 : 0},
+      {p->dstate_out, p->dstate_out ? Bt * E * N * 4 : 0},
+      {p->conv_cache_in, p->conv_cache_in ? Bt * E * 3 * 4 : 0},
+  };
+  const Range outs[] = {
+      {p->dx, p->dx ? Bt * L * E * 4 : 0},        {p->dz, p->dz ? Bt * L * E * 4 : 0},
+      {p->ddt, p->ddt ? (p->dt_rank1 ? Bt * L * 4 : Bt * L * E * 4) : 0},
+      {p->ddt_w, p->ddt_w ? E * 4 : 0},           {p->ddt_bias, p->ddt_bias ? E * 4 : 0},
+      {p->dA, p->dA ? E * N * 4 : 0},             {p->dB, p->dB ? Bt * L * N * 4 : 0},
+      {p->dC, p->dC ? Bt * L * N * 4 : 0},        {p->dD, p->dD ? E * 4 : 0},
+      {p->dconv_w, p->dconv_w ? E * 4 * 4 : 0},   {p->dconv_b, p->dconv_b ? E * 4 : 0},
+      {p->dconv_cache, p->dconv_cache ? Bt * E * 3 * 4 : 0},
+      {p->dstate_in, p->dstate_in ? Bt * E * N * 4 : 0},
+  };
+  const size_t n_out = sizeof(outs) / sizeof(outs[0]);
+  for (size_t i = 0; i < n_out; ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return fail(SSM_ERR_INVALID_ARG, "%s overlaps an input", "a gradient output");
+    for (size_t j = i + 1; j < n_out; ++j)
+      if (overlaps(outs[i], outs[j])) return fail(SSM_ERR_INVALID_ARG, "%s overlap each other", "gradient outputs");
+  }
+  const BwdWs o = bwd_ws(p);
+  if (!p->workspace || p->workspace_bytes < o.total)
+    return fail(SSM_ERR_WORKSPACE, "%s is missing or smaller than ssm_scan_bwd_workspace_size()", "workspace");
+  if (reinterpret_cast<uintptr_t>(p->workspace) & 255)
+    return fail(SSM_ERR_INVALID_ARG, "%s must be 256-byte aligned", "workspace");
+  const Range ws{p->workspace, o.total};
+  for (const Range& r : ins)
+    if (overlaps(ws, r)) return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "workspace");
+  for (const Range& r : outs)
+    if (overlaps(ws, r)) return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "workspace");
+  return SSM_OK;
+}
+
 ssm_status_t hip_status(hipError_t e) {
   if (e == hipSuccess) return ok();
   return fail(SSM_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
@@ -845,6 +950,78 @@ ssm_status_t ssm_layer_fwd(const ssm_layer_params_t* p, void* stream) {
   return done(ok());
 }
 
+ssm_status_t ssm_scan_bwd_check(const ssm_scan_bwd_params_t* p) {
+  const ssm_status_t s = bwd_check(p);
+  return s == SSM_OK ? ok() : s;
+}
+
+size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_params_t* p) {
+  if (!p || p->struct_size != sizeof(ssm_scan_bwd_params_t)) return 0;
+  if (p->batch < 0 || p->seqlen < 0 || p->dim <= 0) return 0;
+  return bwd_ws(p).total;
+}
+
+ssm_status_t ssm_scan_bwd(const ssm_scan_bwd_params_t* p, void* stream) {
+  const ssm_status_t s = bwd_check(p);
+  if (s != SSM_OK) return s;
+  if (static_cast<size_t>(p->batch) * p->seqlen == 0) return ok();
+  const BwdWs o = bwd_ws(p);
+  char* ws = static_cast<char*>(p->workspace);
+  auto wf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  ssm::BwdArgs a{};
+  a.x = p->x;
+  a.dt = p->dt;
+  a.dt_w = p->dt_rank1 ? p->dt_w : nullptr;
+  a.dt_bias = p->dt_bias;
+  a.A = p->A;
+  a.B = p->B;
+  a.C = p->C;
+  a.D = p->D;
+  a.z = p->z;
+  a.conv_w = p->conv_w;
+  a.conv_b = p->conv_b;
+  a.conv_cache_in = p->conv_cache_in;
+  a.state_in = p->ssm_state_in;
+  a.dy = p->dy;
+  a.dstate_out = p->dstate_out;
+  a.dx = p->dx;
+  a.dz = p->dz;
+  a.ddt = p->ddt;
+  a.ddt_w = p->ddt_w;
+  a.ddt_bias = p->ddt_bias;
+  a.dA = p->dA;
+  a.dB = p->dB;
+  a.dC = p->dC;
+  a.dD = p->dD;
+  a.dconv_w = p->dconv_w;
+  a.dconv_b = p->dconv_b;
+  a.dconv_cache = p->dconv_cache;
+  a.dstate_in = p->dstate_in;
+  a.hs = wf(o.hs);
+  a.qs = wf(o.qs);
+  a.sdt = wf(o.sdt);
+  a.dxc = p->conv_w ? wf(o.dxc) : nullptr;
+  a.pB = wf(o.pB);
+  a.pC = wf(o.pC);
+  a.pr = p->dt_rank1 ? wf(o.pr) : nullptr;
+  a.pe = wf(o.pe);
+  a.pw = p->conv_w ? wf(o.pw) : nullptr;
+  a.batch = p->batch;
+  a.seqlen = p->seqlen;
+  a.dim = p->dim;
+  a.nseg = ssm::bwd_segments(p->seqlen);
+  a.ngroups16 = (p->dim + 15) / 16;
+  a.x_bf16 = p->x_dtype == SSM_BF16;
+  a.dt_bf16 = p->dt_dtype == SSM_BF16;
+  a.dt_rank1 = p->dt_rank1 ? 1 : 0;
+  a.bc_bf16 = p->bc_dtype == SSM_BF16;
+  a.dy_bf16 = p->dy_dtype == SSM_BF16;
+  a.dt_softplus = p->dt_softplus ? 1 : 0;
+  a.dt_min = p->dt_min;
+  a.dt_max = p->dt_max;
+  return hip_status(ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* ssm_status_string(int32_t status) {
   switch (status) {
     case SSM_OK: return "SSM_OK";
@@ -873,6 +1050,7 @@ size_t ssm_params_sizeof(int32_t which) {
     case 3: return sizeof(ssm_chunk_decode_params_t);
     case 4: return sizeof(ssm_linear_params_t);
     case 5: return sizeof(ssm_layer_params_t);
+    case 6: return sizeof(ssm_scan_bwd_params_t);
     default: return 0;
   }
 }

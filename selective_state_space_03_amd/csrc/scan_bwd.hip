@@ -1,0 +1,500 @@
+// Backward of the scan stage for gfx950, with recomputation.
+//
+// Page "Mamba/SSM basics" (molayo), the section after "Technical details":
+// production training recomputes intermediate states in the backward pass
+// instead of materialising them in HBM.  Here nothing of size (L, E, N) is
+// stored: the sequence is cut into segments of kSeg steps and
+//   1. bwd_summary: per segment, the state at its end starting from zero and
+//      the reverse-time gradient at its start starting from zero (both linear
+//      in what enters the segment), and the sum of dt over it;
+//   2. bwd_compose: per (batch, channel, state), the state entering every
+//      segment (forward through the segments, from the initial state) and
+//      the gradient entering every segment from its right (backward, from the
+//      gradient on the final state), which also gives the initial state's
+//      gradient;
+//   3. bwd_main: per segment, the states of its kSeg steps are recomputed
+//      into registers and walked backward, producing every gradient of the
+//      step; gradients summed over channels (B, C, a rank-1 dt) leave as
+//      per-wave partials, gradients summed over time (A, D, dt_w, dt_bias) as
+//      per-segment partials, and the conv input gradient as dL/dxc;
+//   4. the conv's transpose and the reductions, all in a fixed order.
+// Reverse recurrence (G_t = dL/dh_t, Q_t = a_t G_t, a_t = exp(dt_t A)):
+//   G_t = dyc_t C_t + Q_{t+1},  dyc_t = dy_t SiLU(z_t),  Q at the end = dL/dh_L.
+// Lanes: 4 per (batch, channel), each holding 4 of the 16 states, so a
+// segment's 16 recomputed states take 64 registers per lane (32 steps spilled
+// the history to scratch memory) and the sums over states are two cross-lane
+// adds.
+#include "ssm_device.h"
+#include "ssm_internal.h"
+
+#include <type_traits>
+
+namespace ssm {
+namespace {
+
+constexpr int kSeg = kBwdSeg;  // steps per segment (16)
+
+__device__ __forceinline__ float ldx(const void* p, size_t i, bool bf) {
+  return bf ? ld<bf16s>(p, i) : ld<float>(p, i);
+}
+
+// 4 consecutive entries (f32 or bf16) from a 4-element-aligned address
+__device__ __forceinline__ void load4v(const void* p, size_t i, bool bf, float (&v)[4]) {
+  if (bf) {
+    const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    v[0] = __uint_as_float(r.x << 16);
+    v[1] = __uint_as_float(r.x & 0xffff0000u);
+    v[2] = __uint_as_float(r.y << 16);
+    v[3] = __uint_as_float(r.y & 0xffff0000u);
+  } else {
+    const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    v[0] = f.x;
+    v[1] = f.y;
+    v[2] = f.z;
+    v[3] = f.w;
+  }
+}
+
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __shfl_xor(v, 1, 4);
+  v += __shfl_xor(v, 2, 4);
+  return v;
+}
+
+// sum over the 16 channels of the wave (lanes with the same state quarter)
+__device__ __forceinline__ float chan_sum(float v) {
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float dsilu(float x) {
+  const float s = rcp_fast(1.0f + exp2_fast(-x * kLog2e));
+  return s * (1.0f + x * (1.0f - s));
+}
+
+// Per-lane context: which (batch, channel, state quarter) and its constants.
+struct Lane {
+  const BwdArgs& a;
+  int b, e, q, gw;
+  bool act;
+  float Al2[4], An[4];  // A[e][4q + j] log2(e), A[e][4q + j]
+  float cw[4], cb, dtw, dtb, d;
+
+  __device__ Lane(const BwdArgs& args, int b_, int gw_) : a(args), b(b_), gw(gw_) {
+    const int lane = threadIdx.x & 63;
+    q = lane & 3;
+    const int e_raw = 16 * gw + (lane >> 2);
+    act = e_raw < a.dim;
+    e = act ? e_raw : a.dim - 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      An[j] = a.A[static_cast<size_t>(e) * kScanN + 4 * q + j];
+      Al2[j] = An[j] * kLog2e;
+    }
+    if (a.conv_w) {
+      const float4 w = reinterpret_cast<const float4*>(a.conv_w)[e];
+      cw[0] = w.x;
+      cw[1] = w.y;
+      cw[2] = w.z;
+      cw[3] = w.w;
+      cb = a.conv_b ? a.conv_b[e] : 0.0f;
+    } else {
+      cw[0] = cw[1] = cw[2] = cw[3] = cb = 0.0f;
+    }
+    dtw = a.dt_rank1 ? a.dt_w[e] : 0.0f;
+    dtb = a.dt_bias ? a.dt_bias[e] : 0.0f;
+    d = a.D ? a.D[e] : 0.0f;
+  }
+  __device__ size_t be(int t) const { return (static_cast<size_t>(b) * a.seqlen + t) * a.dim + e; }
+  // raw x at time t (t < 0: the conv cache, oldest first, or zeros)
+  __device__ float raw(int t) const {
+    if (t >= 0) return ldx(a.x, be(t), a.x_bf16);
+    if (a.conv_cache_in) return a.conv_cache_in[(static_cast<size_t>(b) * a.dim + e) * 3 + (3 + t)];
+    return 0.0f;
+  }
+  // u_t and the conv output xc_t
+  __device__ float u_at(int t, float& xc) const {
+    if (!a.conv_w) {
+      xc = 0.0f;
+      return ldx(a.x, be(t), a.x_bf16);
+    }
+    xc = fmaf(cw[0], raw(t - 3), fmaf(cw[1], raw(t - 2), fmaf(cw[2], raw(t - 1), fmaf(cw[3], raw(t), cb))));
+    return silu(xc);
+  }
+  __device__ float pre_at(int t) const {
+    if (a.dt_rank1) return fmaf(dtw, static_cast<const float*>(a.dt)[static_cast<size_t>(b) * a.seqlen + t], dtb);
+    return ldx(a.dt, be(t), a.dt_bf16) + dtb;
+  }
+  // dt = clip(softplus(pre)); inside: strictly between the bounds; dsp: the
+  // derivative of softplus (or 1)
+  __device__ float dt_of(float pre, bool& inside, float& dsp) const {
+    float sp;
+    if (a.dt_softplus) {
+      sp = softplus(pre);
+      dsp = rcp_fast(1.0f + exp2_fast(-pre * kLog2e));
+    } else {
+      sp = pre;
+      dsp = 1.0f;
+    }
+    inside = sp > a.dt_min && sp < a.dt_max;
+    return fminf(fmaxf(sp, a.dt_min), a.dt_max);
+  }
+  __device__ void bc(int t, const void* p, float (&v)[4]) const {
+    load4v(p, (static_cast<size_t>(b) * a.seqlen + t) * kScanN + 4 * q, a.bc_bf16, v);
+  }
+  __device__ void decay(float dt, float (&av)[4]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) av[j] = exp2_fast(dt * Al2[j]);
+  }
+  __device__ float gate(int t, float& zv) const {
+    if (!a.z) {
+      zv = 0.0f;
+      return 1.0f;
+    }
+    zv = ldx(a.z, be(t), a.x_bf16);
+    return silu(zv);
+  }
+};
+
+// wave -> (batch, channel group of 16, segment)
+__device__ __forceinline__ void wave_ids(const BwdArgs& a, int& b, int& gw, int& s) {
+  int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  gw = w % a.ngroups16;
+  w /= a.ngroups16;
+  b = w % a.batch;
+  s = w / a.batch;
+}
+
+__global__ __launch_bounds__(256) void bwd_summary(BwdArgs a) {
+  int b, gw, s;
+  wave_ids(a, b, gw, s);
+  if (s >= a.nseg) return;
+  const Lane c(a, b, gw);
+  const int t0 = s * kSeg, t1 = min(a.seqlen, t0 + kSeg);
+  float h[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sdt = 0.0f;
+  for (int t = t0; t < t1; ++t) {
+    float xc, bv[4], av[4];
+    const float u = c.u_at(t, xc);
+    bool inside;
+    float dsp;
+    const float dt = c.dt_of(c.pre_at(t), inside, dsp);
+    c.bc(t, a.B, bv);
+    c.decay(dt, av);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h[j] = fmaf(av[j], h[j], dt * u * bv[j]);
+    sdt += dt;
+  }
+  float Q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = t1 - 1; t >= t0; --t) {
+    float cv[4], av[4], zv;
+    bool inside;
+    float dsp;
+    const float dt = c.dt_of(c.pre_at(t), inside, dsp);
+    c.bc(t, a.C, cv);
+    c.decay(dt, av);
+    const float dyc = ldx(a.dy, c.be(t), a.dy_bf16) * c.gate(t, zv);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Q[j] = av[j] * fmaf(dyc, cv[j], Q[j]);
+  }
+  if (!c.act) return;
+  const size_t o = ((static_cast<size_t>(b) * a.nseg + s) * a.dim + c.e) * kScanN + 4 * c.q;
+  *reinterpret_cast<float4*>(a.hs + o) = make_float4(h[0], h[1], h[2], h[3]);
+  *reinterpret_cast<float4*>(a.qs + o) = make_float4(Q[0], Q[1], Q[2], Q[3]);
+  if (c.q == 0) a.sdt[(static_cast<size_t>(b) * a.nseg + s) * a.dim + c.e] = sdt;
+}
+
+// one thread per (batch, channel, state)
+__global__ __launch_bounds__(256) void bwd_compose(BwdArgs a) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const size_t total = static_cast<size_t>(a.batch) * a.dim * kScanN;
+  if (i >= total) return;
+  const int n = static_cast<int>(i % kScanN);
+  const int e = static_cast<int>((i / kScanN) % a.dim);
+  const int b = static_cast<int>(i / (static_cast<size_t>(kScanN) * a.dim));
+  const float al2 = a.A[static_cast<size_t>(e) * kScanN + n] * kLog2e;
+  auto at = [&](int s) { return ((static_cast<size_t>(b) * a.nseg + s) * a.dim + e) * kScanN + n; };
+  auto sd = [&](int s) { return a.sdt[(static_cast<size_t>(b) * a.nseg + s) * a.dim + e]; };
+  float hcur = a.state_in ? a.state_in[(static_cast<size_t>(b) * a.dim + e) * kScanN + n] : 0.0f;
+  for (int s = 0; s < a.nseg; ++s) {
+    const float loc = a.hs[at(s)];
+    a.hs[at(s)] = hcur;  // the state entering segment s
+    hcur = fmaf(exp2_fast(al2 * sd(s)), hcur, loc);
+  }
+  float qcur = a.dstate_out ? a.dstate_out[(static_cast<size_t>(b) * a.dim + e) * kScanN + n] : 0.0f;
+  for (int s = a.nseg - 1; s >= 0; --s) {
+    const float loc = a.qs[at(s)];
+    a.qs[at(s)] = qcur;  // the gradient entering segment s from its right
+    qcur = fmaf(exp2_fast(al2 * sd(s)), qcur, loc);
+  }
+  if (a.dstate_in) a.dstate_in[(static_cast<size_t>(b) * a.dim + e) * kScanN + n] = qcur;
+}
+
+__global__ __launch_bounds__(256) void bwd_main(BwdArgs a) {
+  int b, gw, s;
+  wave_ids(a, b, gw, s);
+  if (s >= a.nseg) return;
+  const Lane c(a, b, gw);
+  const int t0 = s * kSeg, t1 = min(a.seqlen, t0 + kSeg);
+  const size_t so = ((static_cast<size_t>(b) * a.nseg + s) * a.dim + c.e) * kScanN + 4 * c.q;
+  float hin[4], Q[4];
+  {
+    const float4 hv = *reinterpret_cast<const float4*>(a.hs + so);
+    const float4 qv = *reinterpret_cast<const float4*>(a.qs + so);
+    hin[0] = hv.x; hin[1] = hv.y; hin[2] = hv.z; hin[3] = hv.w;
+    Q[0] = qv.x; Q[1] = qv.y; Q[2] = qv.z; Q[3] = qv.w;
+  }
+  // the segment's states, recomputed
+  float hist[kSeg][4];
+  {
+    float h[4] = {hin[0], hin[1], hin[2], hin[3]};
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) {
+      if (t0 + i < t1) {
+        const int t = t0 + i;
+        float xc, bv[4], av[4];
+        const float u = c.u_at(t, xc);
+        bool inside;
+        float dsp;
+        const float dt = c.dt_of(c.pre_at(t), inside, dsp);
+        c.bc(t, a.B, bv);
+        c.decay(dt, av);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[j] = fmaf(av[j], h[j], dt * u * bv[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hist[i][j] = h[j];
+    }
+  }
+  const float actf = c.act ? 1.0f : 0.0f;
+  float dA[4] = {0.0f, 0.0f, 0.0f, 0.0f}, dD = 0.0f, ddtw = 0.0f, ddtb = 0.0f;
+#pragma unroll
+  for (int i = kSeg - 1; i >= 0; --i) {
+    if (t0 + i >= t1) continue;
+    const int t = t0 + i;
+    float hprev[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hprev[j] = i > 0 ? hist[i - 1][j] : hin[j];
+    float xc, bv[4], cv[4], av[4], zv;
+    const float u = c.u_at(t, xc);
+    bool inside;
+    float dsp;
+    const float pre = c.pre_at(t);
+    const float dt = c.dt_of(pre, inside, dsp);
+    c.bc(t, a.B, bv);
+    c.bc(t, a.C, cv);
+    c.decay(dt, av);
+    const float dy = ldx(a.dy, c.be(t), a.dy_bf16);
+    const float g = c.gate(t, zv);
+    const float dyc = dy * g;
+    float G[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) G[j] = fmaf(dyc, cv[j], Q[j]);
+    // dz = dy * yc * SiLU'(z), yc = C . h_t + D u
+    if (a.z) {
+      float yp = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) yp = fmaf(cv[j], hist[i][j], yp);
+      const float yc = fmaf(c.d, u, quad_sum(yp));
+      if (a.dz && c.act && c.q == 0) a.dz[c.be(t)] = dy * yc * dsilu(zv);
+    }
+    float pdt = 0.0f, pdu = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pdt = fmaf(G[j], fmaf(c.An[j] * av[j], hprev[j], u * bv[j]), pdt);
+      pdu = fmaf(G[j] * dt, bv[j], pdu);
+      dA[j] = fmaf(G[j] * dt * av[j], hprev[j], dA[j]);
+    }
+    const float ddt = quad_sum(pdt);
+    const float du = fmaf(dyc, c.d, quad_sum(pdu));
+    // dB_t = sum_e G dt u, dC_t = sum_e dyc h_t: this wave's 16 channels
+    float sB[4], sC[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sB[j] = chan_sum(actf * G[j] * dt * u);
+      sC[j] = chan_sum(actf * dyc * hist[i][j]);
+    }
+    const int lane = threadIdx.x & 63;
+    if (lane < 4) {
+      const size_t po = ((static_cast<size_t>(b) * a.seqlen + t) * a.ngroups16 + gw) * kScanN + 4 * lane;
+      *reinterpret_cast<float4*>(a.pB + po) = make_float4(sB[0], sB[1], sB[2], sB[3]);
+      *reinterpret_cast<float4*>(a.pC + po) = make_float4(sC[0], sC[1], sC[2], sC[3]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Q[j] = av[j] * G[j];
+    dD = fmaf(dyc, u, dD);
+    const float dpre = inside ? ddt * dsp : 0.0f;
+    ddtb += dpre;
+    if (a.dt_rank1) {
+      const float r = static_cast<const float*>(a.dt)[static_cast<size_t>(b) * a.seqlen + t];
+      ddtw = fmaf(dpre, r, ddtw);
+      const float sr = chan_sum(c.q == 0 ? actf * dpre * c.dtw : 0.0f);
+      if (lane == 0) a.pr[(static_cast<size_t>(b) * a.seqlen + t) * a.ngroups16 + gw] = sr;
+    } else if (a.ddt && c.act && c.q == 0) {
+      a.ddt[c.be(t)] = dpre;
+    }
+    if (c.act && c.q == 0) {
+      if (a.conv_w) a.dxc[c.be(t)] = du * dsilu(xc);
+      else if (a.dx) a.dx[c.be(t)] = du;
+    }
+  }
+  if (!c.act) return;
+  float* pe = a.pe + ((static_cast<size_t>(b) * a.nseg + s) * a.dim + c.e) * kBwdPe;
+  *reinterpret_cast<float4*>(pe + 4 * c.q) = make_float4(dA[0], dA[1], dA[2], dA[3]);
+  if (c.q == 0) {
+    pe[16] = dD;
+    pe[17] = ddtw;
+    pe[18] = ddtb;
+  }
+}
+
+// conv transpose: dx[t] = sum_k w[k] dxc[t + 3 - k]; one thread per (b, t, e)
+__global__ __launch_bounds__(256) void bwd_conv_dx(BwdArgs a) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const size_t total = static_cast<size_t>(a.batch) * a.seqlen * a.dim;
+  if (i >= total) return;
+  const int e = static_cast<int>(i % a.dim);
+  const int t = static_cast<int>((i / a.dim) % a.seqlen);
+  const float4 w = reinterpret_cast<const float4*>(a.conv_w)[e];
+  const float wk[4] = {w.x, w.y, w.z, w.w};
+  float v = 0.0f;
+#pragma unroll
+  for (int k = 3; k >= 0; --k) {
+    const int tt = t + 3 - k;
+    if (tt < a.seqlen) v = fmaf(wk[k], a.dxc[i + static_cast<size_t>(3 - k) * a.dim], v);
+  }
+  if (a.dx) a.dx[i] = v;
+}
+
+// conv weights, bias and cache gradients: per channel, partial sums over
+// chunks of kConvChunk time steps of one batch row (one thread per (chunk,
+// channel)); the cache gradient from the first 3 steps of each row
+__global__ __launch_bounds__(256) void bwd_conv_w(BwdArgs a) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int chunk = blockIdx.y;  // over batch * chunks per row
+  if (e >= a.dim) return;
+  const int cpr = (a.seqlen + kConvChunk - 1) / kConvChunk;
+  const int b = chunk / cpr, c0 = (chunk % cpr) * kConvChunk;
+  const int c1 = min(a.seqlen, c0 + kConvChunk);
+  const float* cache = a.conv_cache_in ? a.conv_cache_in + (static_cast<size_t>(b) * a.dim + e) * 3 : nullptr;
+  auto raw = [&](int t) -> float {
+    if (t >= 0) return ldx(a.x, (static_cast<size_t>(b) * a.seqlen + t) * a.dim + e, a.x_bf16);
+    return cache ? cache[3 + t] : 0.0f;
+  };
+  float dw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, db = 0.0f;
+  for (int t = c0; t < c1; ++t) {
+    const float g = a.dxc[(static_cast<size_t>(b) * a.seqlen + t) * a.dim + e];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dw[k] = fmaf(g, raw(t - 3 + k), dw[k]);
+    db += g;
+  }
+  float* pw = a.pw + (static_cast<size_t>(chunk) * a.dim + e) * 5;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pw[k] = dw[k];
+  pw[4] = db;
+  if (c0 == 0 && a.dconv_cache) {
+    // xpad position j (0..2) is cache entry j: d = sum_{k <= j} dxc[j - k] w[k]
+    const float4 w = reinterpret_cast<const float4*>(a.conv_w)[e];
+    const float wk[4] = {w.x, w.y, w.z, w.w};
+    for (int j = 0; j < 3; ++j) {
+      float v = 0.0f;
+      for (int k = 0; k <= j; ++k) {
+        const int tt = j - k;
+        if (tt < a.seqlen) v = fmaf(a.dxc[(static_cast<size_t>(b) * a.seqlen + tt) * a.dim + e], wk[k], v);
+      }
+      a.dconv_cache[(static_cast<size_t>(b) * a.dim + e) * 3 + j] = v;
+    }
+  }
+}
+
+// sums over the channel groups: dB, dC (one thread per (b, t, n)) and the
+// rank-1 dt (one thread per (b, t))
+__global__ __launch_bounds__(256) void bwd_reduce_bc(BwdArgs a) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const size_t bt = static_cast<size_t>(a.batch) * a.seqlen;
+  if (i < bt * kScanN) {
+    const size_t row = i / kScanN;
+    const int n = static_cast<int>(i % kScanN);
+    float sb = 0.0f, sc = 0.0f;
+    for (int g = 0; g < a.ngroups16; ++g) {
+      sb += a.pB[(row * a.ngroups16 + g) * kScanN + n];
+      sc += a.pC[(row * a.ngroups16 + g) * kScanN + n];
+    }
+    if (a.dB) a.dB[i] = sb;
+    if (a.dC) a.dC[i] = sc;
+  }
+  if (a.dt_rank1 && a.ddt && i < bt) {
+    float sr = 0.0f;
+    for (int g = 0; g < a.ngroups16; ++g) sr += a.pr[i * a.ngroups16 + g];
+    a.ddt[i] = sr;
+  }
+}
+
+// sums over (batch, segment) of the per-channel gradients and over time
+// chunks of the conv parameters; one thread per (channel, item)
+__global__ __launch_bounds__(256) void bwd_reduce_e(BwdArgs a) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  constexpr int kItems = kBwdPe + 5;
+  if (i >= static_cast<size_t>(a.dim) * kItems) return;
+  const int e = static_cast<int>(i / kItems), j = static_cast<int>(i % kItems);
+  float v = 0.0f;
+  if (j < kBwdPe) {
+    if (j >= 19) return;
+    for (int b = 0; b < a.batch; ++b)
+      for (int s = 0; s < a.nseg; ++s) v += a.pe[((static_cast<size_t>(b) * a.nseg + s) * a.dim + e) * kBwdPe + j];
+    if (j < kScanN) {
+      if (a.dA) a.dA[static_cast<size_t>(e) * kScanN + j] = v;
+    } else if (j == 16) {
+      if (a.dD) a.dD[e] = v;
+    } else if (j == 17) {
+      if (a.ddt_w) a.ddt_w[e] = v;
+    } else {
+      if (a.ddt_bias) a.ddt_bias[e] = v;
+    }
+    return;
+  }
+  if (!a.conv_w) return;
+  const int k = j - kBwdPe;  // 0..3 weights, 4 bias
+  const int chunks = a.batch * ((a.seqlen + kConvChunk - 1) / kConvChunk);
+  for (int c = 0; c < chunks; ++c) v += a.pw[(static_cast<size_t>(c) * a.dim + e) * 5 + k];
+  if (k < 4) {
+    if (a.dconv_w) a.dconv_w[static_cast<size_t>(e) * 4 + k] = v;
+  } else if (a.dconv_b) {
+    a.dconv_b[e] = v;
+  }
+}
+
+unsigned blocks_for(size_t n) { return static_cast<unsigned>((n + 255) / 256); }
+
+}  // namespace
+
+int bwd_segments(int seqlen) { return (seqlen + kSeg - 1) / kSeg; }
+
+hipError_t launch_scan_bwd(const BwdArgs& a, hipStream_t s) {
+  if (a.batch == 0 || a.seqlen == 0) return hipSuccess;
+  const size_t waves = static_cast<size_t>(a.batch) * a.ngroups16 * a.nseg;
+  const unsigned wblocks = static_cast<unsigned>((waves + 3) / 4);
+  hipLaunchKernelGGL(bwd_summary, dim3(wblocks), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_compose, dim3(blocks_for(static_cast<size_t>(a.batch) * a.dim * kScanN)), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = timed_launch(s, [&] { hipLaunchKernelGGL(bwd_main, dim3(wblocks), dim3(256), 0, s, a); });
+  if (e != hipSuccess) return e;
+  const size_t bt = static_cast<size_t>(a.batch) * a.seqlen;
+  if (a.conv_w) {
+    hipLaunchKernelGGL(bwd_conv_dx, dim3(blocks_for(bt * a.dim)), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int chunks = a.batch * ((a.seqlen + kConvChunk - 1) / kConvChunk);
+    hipLaunchKernelGGL(bwd_conv_w, dim3(blocks_for(a.dim), chunks), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(bwd_reduce_bc, dim3(blocks_for(bt * kScanN)), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_reduce_e, dim3(blocks_for(static_cast<size_t>(a.dim) * (kBwdPe + 5))), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ssm

@@ -174,6 +174,41 @@ struct ChunkDecodeLaunch {
 
 hipError_t launch_chunk_decode(const ChunkDecodeLaunch& l, hipStream_t stream);
 
+// ---- backward of the scan stage --------------------------------------------
+constexpr int kBwdSeg = 16;     // time steps per segment (states recomputed in registers)
+constexpr int kBwdPe = 20;      // per-(batch, segment, channel) partial: dA[16], dD, ddt_w, ddt_bias, pad
+constexpr int kConvChunk = 64;  // time steps per partial of the conv weight gradient
+
+struct BwdArgs {
+  // forward inputs
+  const void* x;
+  const void* dt;
+  const float* dt_w;
+  const float* dt_bias;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* conv_w;
+  const float* conv_b;
+  const float* conv_cache_in;
+  const float* state_in;
+  // incoming gradients
+  const void* dy;
+  const float* dstate_out;
+  // gradients (fp32; null: not written)
+  float *dx, *dz, *ddt, *ddt_w, *ddt_bias, *dA, *dB, *dC, *dD, *dconv_w, *dconv_b, *dconv_cache, *dstate_in;
+  // workspace
+  float *hs, *qs, *sdt, *dxc, *pB, *pC, *pr, *pe, *pw;
+  int batch, seqlen, dim, nseg, ngroups16;
+  int x_bf16, dt_bf16, dt_rank1, bc_bf16, dy_bf16, dt_softplus;
+  float dt_min, dt_max;
+};
+
+int bwd_segments(int seqlen);
+hipError_t launch_scan_bwd(const BwdArgs& a, hipStream_t stream);
+
 // ---- projection GEMM: C = A W^T --------------------------------------------
 // A (M, K) bf16 or f32 with row stride lda; W (N, K) bf16 with row stride ldw;
 // output columns [0, n_split) go to C0 (row stride ldc0), [n_split, N) to C1

@@ -203,3 +203,36 @@ def layer_oracle(w: W.Workload, *, tokens=None, cache_in=None, state_in=None):
     return O.ssm_layer_forward(hidden, f("W_in"), f("conv_w"), f("W_x"), f("dt_w"), f("dt_bias"), f("A"),
                                f("W_out"), D=f("D"), conv_cache=cache_in, ssm_state=state_in,
                                dt_softplus=o["dt_softplus"], dt_min=float(o["dt_min"]), dt_max=float(o["dt_max"]))
+
+
+# ---------------------------------------------------------------------- scan backward
+
+def scan_bwd_gpu(w: W.Workload, dy, *, state_in=None, cache_in=None, dstate_out=None):
+    """ssm_scan_bwd on the workload with the upstream gradient dy (numpy, fp32)."""
+    o = w.opts
+    tt = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)  # noqa
+    g = ssm.scan_bwd(
+        dev_tensor(w, "x"), dev_tensor(w, "A"), dev_tensor(w, "B"), dev_tensor(w, "C"), dev_tensor(w, "dt"), tt(dy),
+        D=dev_tensor(w, "D"), z=dev_tensor(w, "z"), conv_w=dev_tensor(w, "conv_w") if o["conv"] else None,
+        conv_cache_in=tt(cache_in), dt_rank1=o["dt_rank1"], dt_w=dev_tensor(w, "dt_w"),
+        dt_bias=dev_tensor(w, "dt_bias"), dt_softplus=o["dt_softplus"], dt_min=o["dt_min"], dt_max=o["dt_max"],
+        ssm_state_in=tt(state_in), dstate_out=tt(dstate_out))
+    torch.cuda.synchronize()
+    return {k: np64(v) for k, v in g.items()}
+
+
+def scan_bwd_oracle(w: W.Workload, dy, *, state_in=None, cache_in=None, dstate_out=None):
+    o = w.opts
+    f = w.f64
+    kw = dict(D=f("D"), z=f("z"), conv_w=f("conv_w") if o["conv"] else None, conv_cache=cache_in,
+              dt_bias=f("dt_bias"), dt_softplus=o["dt_softplus"], dt_min=float(o["dt_min"]),
+              dt_max=float(o["dt_max"]), ssm_state=state_in, dstate_out=dstate_out)
+    if o["dt_rank1"]:
+        kw.update(dt_raw=f("dt"), dt_w=f("dt_w"))
+    else:
+        kw.update(dt=f("dt"))
+    g = O.ssm_layer_scan_backward(f("x"), f("A"), f("B"), f("C"), np.asarray(dy, np.float64), **kw)
+    # name the rank-1 input's gradient like the GPU side ("dt" is the input r there)
+    if o["dt_rank1"]:
+        g["dt"] = g.pop("dt_raw")
+    return {k: v for k, v in g.items() if v is not None}
