@@ -61,10 +61,15 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
-// sum over the 16 channels of the wave (lanes with the same state quarter)
+// sum over the 16 channels of the wave (lanes with the same state quarter):
+// the 4 channels of a 16-lane row by DPP row rotations, then across rows
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float chan_sum(float v) {
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+  v += dpp<0x124>(v);  // row_ror:4
+  v += dpp<0x128>(v);  // row_ror:8
   v += __shfl_xor(v, 16);
   v += __shfl_xor(v, 32);
   return v;
@@ -384,10 +389,15 @@ __global__ __launch_bounds__(256) void bwd_conv_w(BwdArgs a) {
     return cache ? cache[3 + t] : 0.0f;
   };
   float dw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, db = 0.0f;
+  float win[4] = {0.0f, raw(c0 - 3), raw(c0 - 2), raw(c0 - 1)};  // raw x at t-3 .. t
   for (int t = c0; t < c1; ++t) {
+    win[0] = win[1];
+    win[1] = win[2];
+    win[2] = win[3];
+    win[3] = raw(t);
     const float g = a.dxc[(static_cast<size_t>(b) * a.seqlen + t) * a.dim + e];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) dw[k] = fmaf(g, raw(t - 3 + k), dw[k]);
+    for (int k = 0; k < 4; ++k) dw[k] = fmaf(g, win[k], dw[k]);
     db += g;
   }
   float* pw = a.pw + (static_cast<size_t>(chunk) * a.dim + e) * 5;
@@ -409,26 +419,41 @@ __global__ __launch_bounds__(256) void bwd_conv_w(BwdArgs a) {
   }
 }
 
-// sums over the channel groups: dB, dC (one thread per (b, t, n)) and the
-// rank-1 dt (one thread per (b, t))
+// sums over the channel groups, one workgroup per (b, t) row: thread (slice,
+// n) adds the groups slice, slice + 16, ... of dB and dC, then the 16 slices
+// are added in order (the rank-1 dt the same way over 256 slices)
 __global__ __launch_bounds__(256) void bwd_reduce_bc(BwdArgs a) {
-  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  const size_t bt = static_cast<size_t>(a.batch) * a.seqlen;
-  if (i < bt * kScanN) {
-    const size_t row = i / kScanN;
-    const int n = static_cast<int>(i % kScanN);
-    float sb = 0.0f, sc = 0.0f;
-    for (int g = 0; g < a.ngroups16; ++g) {
-      sb += a.pB[(row * a.ngroups16 + g) * kScanN + n];
-      sc += a.pC[(row * a.ngroups16 + g) * kScanN + n];
-    }
-    if (a.dB) a.dB[i] = sb;
-    if (a.dC) a.dC[i] = sc;
+  __shared__ float sb[16][kScanN], sc[16][kScanN], sr[256];
+  const size_t row = blockIdx.x;
+  const int n = threadIdx.x & 15, sl = threadIdx.x >> 4;
+  const float* pb = a.pB + row * a.ngroups16 * kScanN;
+  const float* pc = a.pC + row * a.ngroups16 * kScanN;
+  float vb = 0.0f, vc = 0.0f;
+  for (int g = sl; g < a.ngroups16; g += 16) {
+    vb += pb[g * kScanN + n];
+    vc += pc[g * kScanN + n];
   }
-  if (a.dt_rank1 && a.ddt && i < bt) {
-    float sr = 0.0f;
-    for (int g = 0; g < a.ngroups16; ++g) sr += a.pr[i * a.ngroups16 + g];
-    a.ddt[i] = sr;
+  sb[sl][n] = vb;
+  sc[sl][n] = vc;
+  float vr = 0.0f;
+  if (a.dt_rank1) {
+    for (int g = threadIdx.x; g < a.ngroups16; g += 256) vr += a.pr[row * a.ngroups16 + g];
+  }
+  sr[threadIdx.x] = vr;
+  __syncthreads();
+  if (threadIdx.x < kScanN) {
+    float tb = 0.0f, tc = 0.0f;
+    for (int k = 0; k < 16; ++k) {
+      tb += sb[k][threadIdx.x];
+      tc += sc[k][threadIdx.x];
+    }
+    if (a.dB) a.dB[row * kScanN + threadIdx.x] = tb;
+    if (a.dC) a.dC[row * kScanN + threadIdx.x] = tc;
+  }
+  if (threadIdx.x == 0 && a.dt_rank1 && a.ddt) {
+    float t = 0.0f;
+    for (int k = 0; k < 256; ++k) t += sr[k];
+    a.ddt[row] = t;
   }
 }
 
@@ -491,7 +516,7 @@ hipError_t launch_scan_bwd(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(bwd_conv_w, dim3(blocks_for(a.dim), chunks), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(bwd_reduce_bc, dim3(blocks_for(bt * kScanN)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_reduce_bc, dim3(static_cast<unsigned>(bt)), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_reduce_e, dim3(blocks_for(static_cast<size_t>(a.dim) * (kBwdPe + 5))), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -1,9 +1,9 @@
 """GPU parity of ssm_scan_bwd (the scan stage's backward, with states
 recomputed per 16-step segment) against the float64 oracle's reverse-mode
 ssm_layer_scan_backward, through the C ABI.  Every gradient is fp32 computed
-from exact inputs; sums over up to 2^12 time steps or channels are taken in a
-different order than the oracle's, so each gradient is checked at
-max|err| <= 1e-4 max|grad| (about 2^-13: fp32 rounding of the longest sums)."""
+from exact inputs, so each gradient is held to the fp32 bound
+max|err| <= 1e-5 max|grad| (measured: at most 7e-7 at full size, the sums
+over time and channels taken in another order than the oracle's)."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +12,7 @@ import ssm_workloads as W
 from gpu_util import check, scan_bwd_gpu, scan_bwd_oracle
 
 pytestmark = pytest.mark.gpu
-TOL = 1e-4
+TOL = 1e-5
 
 
 def _dy(w, seed=31):
