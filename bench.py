@@ -613,15 +613,15 @@ def main():
         wall6, km6, _ = timed_loop(torch, ssm, c6, 10, 2)
         tok6 = cfg6["batch"] * cfg6["seq_len"]
         gemms = {}
-        for which in ("in_proj", "out_proj"):
-            cg, cfgg = gemm_calls(torch, ssm, which, dev)
+        for proj in ("in_proj", "out_proj"):
+            cg, cfgg = gemm_calls(torch, ssm, proj, dev)
             _, kmg, _ = timed_loop(torch, ssm, cg, 10, 2)
             tf = cfgg["flops"] / (kmg * 1e-3) / 1e12
-            gemms[which] = {
+            gemms[proj] = {
                 "kernel_us": round(kmg * 1e3, 2),
                 "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                             "traffic": recorded_traffic(f"gemm_{which}")},
+                             "traffic": recorded_traffic(f"gemm_{proj}")},
                 "mfma_work_frac": round(cfgg["mfma_flops"] / (kmg * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                 "config": {k: cfgg[k] for k in ("M", "K", "N", "x_dtype")}}
             del cg
