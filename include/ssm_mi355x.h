@@ -205,6 +205,9 @@ ssm_status_t ssm_decode_check(const ssm_decode_params_t *p);
  * A sequence that is not a whole number of chunks ends with a shorter chunk
  * (the same formulas over its own length).  x, B, C, out (and z) must be
  * 16-byte aligned.
+ * Workspace: ssm_chunk_scan_workspace_size() bytes of device memory, 256-byte
+ * aligned, owned by the caller (zero when the sequences are not cut into
+ * segments); its contents on entry do not matter.
  * Supported: x and B/C in bf16, N = 64, P % 16 == 0 and P <= 128, chunk_size = 128.
  * ---------------------------------------------------------------------- */
 typedef struct ssm_chunk_params {
@@ -230,6 +233,10 @@ typedef struct ssm_chunk_params {
   size_t workspace_bytes;
   const void *z;        /* (Bt, L, H, P) z_dtype or NULL: out *= SiLU(z) after the D skip */
   int32_t z_dtype;
+  int32_t segments;     /* 0: chosen by the library; else cut each sequence into this many
+                           runs of whole chunks (at most 16, and at most one per chunk) that
+                           start from states composed ahead of them; the result is the same
+                           up to rounding order */
 } ssm_chunk_params_t;
 
 ssm_status_t ssm_chunk_scan_fwd(const ssm_chunk_params_t *p, void *stream);

@@ -57,6 +57,7 @@ class ChunkParams(ctypes.Structure):
         ("A", _vp), ("B", _vp), ("C", _vp), ("bc_dtype", _i32), ("D", _vp), ("d_per_channel", _i32),
         ("state_in", _vp), ("state_out", _vp), ("out", _vp), ("out_dtype", _i32),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t), ("z", _vp), ("z_dtype", _i32),
+        ("segments", _i32),
     ]
 
 
@@ -364,9 +365,10 @@ def decode_step(x, A, B, C, dt, ssm_state, *, conv_cache=None, D=None, z=None, c
 
 def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size=128, D=None, dt_bias=None, dt_softplus=True, dt_min=None,
                    dt_max=None, state_in=None, state_out=None, out=None, out_dtype=None, z=None, workspace=None,
-                   stream=None, prepare=False):
+                   segments=0, stream=None, prepare=False):
     """Multi-head chunked scan (ssm_chunk_scan_fwd).  Returns out (batch, L, H, P), or
-    with prepare=True a Call that enqueues this same call again on each run()."""
+    with prepare=True a Call that enqueues this same call again on each run().
+    segments: 0 lets the library cut the sequences; n > 0 forces n segments."""
     L_ = lib()
     batch, seqlen, nheads, headdim = x.shape
     ngroups, d_state = B.shape[2], B.shape[3]
@@ -398,6 +400,7 @@ def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size=128, D=None, dt_bias=None, dt_s
     p.out_dtype = _code(out, "out")
     p.z = _ptr(z, "z", (batch, seqlen, nheads, headdim), device=dev)
     p.z_dtype = _code(z, "z") if z is not None else 0
+    p.segments = int(segments)
     need = L_.ssm_chunk_scan_workspace_size(ctypes.byref(p))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

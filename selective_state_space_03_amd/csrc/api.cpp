@@ -253,7 +253,7 @@ ssm_status_t decode_check(const ssm_decode_params_t* p) {
 
 size_t chunk_ws(const ssm_chunk_params_t* p) {
   if (p->batch <= 0 || p->seqlen <= 0) return 0;
-  return ssm::chunk_workspace_bytes(p->batch, p->seqlen, p->nheads, p->headdim, p->ngroups);
+  return ssm::chunk_workspace_bytes(p->batch, p->seqlen, p->nheads, p->headdim, p->segments);
 }
 
 ssm_status_t chunk_check(const ssm_chunk_params_t* p) {
@@ -264,6 +264,8 @@ ssm_status_t chunk_check(const ssm_chunk_params_t* p) {
       p->d_state <= 0 || p->chunk_size <= 0)
     return fail(SSM_ERR_INVALID_ARG, "%s: negative or zero size", "dims");
   if (p->nheads % p->ngroups != 0) return fail(SSM_ERR_INVALID_ARG, "%s", "nheads must be a multiple of ngroups");
+  if (p->segments < 0 || p->segments > ssm::kSsdMaxSeg)
+    return fail(SSM_ERR_INVALID_ARG, "%s must be in [0, 16]", "segments");
   if (p->d_state != ssm::kSsdN) return fail(SSM_ERR_UNSUPPORTED, "%s must be 64", "d_state");
   if (p->chunk_size != ssm::kSsdQ) return fail(SSM_ERR_UNSUPPORTED, "%s must be 128", "chunk_size");
   if (p->headdim % 16 != 0 || p->headdim > ssm::kSsdMaxP)
@@ -772,6 +774,10 @@ ssm_status_t ssm_chunk_scan_fwd(const ssm_chunk_params_t* p, void* stream) {
   k.headdim = p->headdim;
   k.ngroups = p->ngroups;
   k.nchunks = (p->seqlen + p->chunk_size - 1) / p->chunk_size;
+  const ssm::ChunkSplit sp = ssm::chunk_split(p->batch, p->seqlen, p->nheads, p->headdim, p->segments);
+  k.nseg = sp.nseg;
+  k.cps = sp.cps;
+  k.ppseg = sp.ppseg;
   k.z = p->z;
   k.z_bf16 = p->z && p->z_dtype == SSM_BF16 ? 1 : 0;
   k.d_per_channel = p->d_per_channel ? 1 : 0;

@@ -11,33 +11,50 @@
 // scan): prev_states <- e^{dA[Q-1]} prev_states + sum_s e^{dA[Q-1]-dA[s]} dt[s]
 // x[s] (outer) B[s], which is the unrolled product-sum form applied to a chunk.
 //
-// Mapping: one workgroup (4 waves) per (batch, head, 16- or 32-wide slice of
-// headdim) walks all chunks in order, so the state (PT x N, fp32) stays in MFMA
-// accumulators and the outer chunk loop of the page runs on the device.  Per
-// chunk: C, B (both layouts), x (transposed) and the dt cumsum are staged in
-// LDS while the next chunk's loads are in flight; each wave owns two 16-row
-// blocks of the chunk (rows w and 7-w, equal causal work):
-//   cb^T blocks   = B_J C_I^T            v_mfma_f32_16x16x32_bf16
-//   M (masked)    = cb . 2^(dA_l - dA_s) . dt_s, the exponent masked to -inf
-//                   for s > l before the exponential
-//   intra         = M X_J                v_mfma_f32_16x16x16_bf16, M split hi+lo
-//   state readout = C_I S^T              v_mfma_f32_16x16x32_bf16, S split hi+lo
-//   state update  = (w.x)^T B            v_mfma_f32_16x16x32_bf16, w.x split hi+lo
-// where the hi/lo split (a bf16 value plus the bf16 of its remainder) keeps the
-// operands that are not exact bf16 inputs at about 16 mantissa bits.
+// Mapping.  One workgroup (8 waves) per (batch, head, segment of the
+// sequence) walks the segment's chunks in order with the head's whole state
+// (P x N, fp32) in MFMA accumulators, so C B^T and the decay-weighted matrix M
+// of a chunk are formed once per head (they do not depend on the headdim
+// column).  The incoming state of every segment but the first comes from two
+// small launches before it: ssd_summary_kernel reduces pieces of up to 16
+// chunks to (state reached from zero, total log2 decay) -- the state update
+// alone, parallel over pieces -- and ssd_compose_kernel chains them per state
+// element in order, S <- 2^decay S + S_piece, which is the same recurrence
+// taken a piece at a time.
+//
+// Per chunk: C, B (both layouts), x (transposed) and dt are staged in LDS while
+// the next chunk's loads are in flight; every wave scans dt * A in registers
+// and fills a share of the decay tables; wave (q, half) owns the 16-row blocks
+// q and 7 - q of the chunk (9 causal blocks, the same for every wave) for half
+// of the 16-wide headdim strips, and for each block J <= I
+//   cb^T block     = B_J C_I^T              v_mfma_f32_16x16x32_bf16
+//   M (masked)     = cb . 2^(dA_l - dA_s) . dt_s, the skip D on its diagonal
+//   out^T[strip]  += X_J^T M^T              v_mfma_f32_16x16x16_bf16, M hi + lo
+// then the readout of the incoming state, (S C_I^T) scaled by 2^dA[l]
+// (v_mfma_f32_16x16x32_bf16, S split hi + lo), and the state update
+//   S <- 2^dA[Q-1] S + X^T (w . B)          v_mfma_f32_16x16x32_bf16, w.B hi + lo
+// with w[s] = 2^(dA[Q-1] - dA[s]) dt[s].  The hi/lo split (a bf16 value plus
+// the bf16 of its remainder) keeps the operands that are not exact bf16 inputs
+// at about 16 mantissa bits.
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace ssm {
 namespace {
 
-constexpr int kQ = kSsdQ;  // 128 tokens per chunk
-constexpr int kN = kSsdN;  // 64 states
-constexpr int kRowN = kN + 8;   // padded LDS row of N bf16 (144 bytes)
-constexpr int kRowQ = kQ + 8;   // padded LDS row of Q bf16 (272 bytes)
-constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kQ = kSsdQ;        // 128 tokens per chunk
+constexpr int kN = kSsdN;        // 64 states
+constexpr int kRowN = kN + 8;    // padded LDS row of N bf16 (144 bytes)
+constexpr int kRowQ = kQ + 8;    // padded LDS row of Q bf16 (272 bytes)
+constexpr int kThreads = 512;    // 8 waves
+constexpr int kPiece = 16;       // chunks per summary piece
+constexpr int kMaxSeg = kSsdMaxSeg;  // segments per sequence at most
+#ifndef SSD_KUNROLL
+#define SSD_KUNROLL 1
+#endif
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -45,9 +62,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Column of element s in row r of the transposed tiles (Bt, Xt): the 16-byte
 // blocks of a row are permuted by the row's 8-row group, so the transposing
-// stores (one row per 8-row group across the lanes of a wave) fall in
-// different banks.  Reads of 4 or 8 consecutive elements inside one block stay
-// contiguous.
+// stores fall in different banks.  Reads of 4 or 8 consecutive elements
+// inside one block stay contiguous.
 __device__ __forceinline__ int swz(int r, int s) { return ((((s >> 3) ^ (r >> 3)) & 15) << 3) | (s & 7); }
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
@@ -59,68 +75,238 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
   lo = bf16_bits(v - bf16_val(hi));
 }
 
-template <int PT>
-struct alignas(16) Smem {
-  uint16_t C[kQ][kRowN];    // C chunk, row-major [l][n]
-  uint16_t B[kQ][kRowN];    // B chunk, row-major [s][n]
-  uint16_t Bt[kN][kRowQ];   // B chunk transposed [n][swz(n, s)]
-  uint16_t Xt[PT][kRowQ];   // x chunk slice transposed [p][swz(p, s)]
-  uint16_t XWh[PT][kRowQ];  // wS[s] x[s][p], transposed, bf16 high part
-  uint16_t XWl[PT][kRowQ];  //                              bf16 low part
-  uint16_t Shi[PT][kRowN];  // state entering the chunk, [p][n], bf16 high part
-  uint16_t Slo[PT][kRowN];  //                                   bf16 low part
-  float O[kQ][PT + 4];      // the chunk's output tile, stored to HBM row by row
-  float EL[8][kQ];          // 2^(dA[l] - dA[16 J]) for l >= 16 J
-  float ESD[kQ];            // 2^(dA[16 (s / 16)] - dA[s]) dt[s]
-  float dA[kQ];             // inclusive cumsum of dt * A * log2(e)
-  float dt[kQ];             // dt after softplus and clip
-  float wS[kQ];             // 2^(dA[Q-1] - dA[s]) * dt[s]: state-update weights
-  float eA[kQ];             // 2^dA[l]: decay of the incoming state
+// bf16 j of a 16-byte piece
+__device__ __forceinline__ uint32_t half16(const uint4& v, int j) {
+  return (reinterpret_cast<const uint32_t*>(&v)[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+}
+
+// Headdim P = 16 NS.  Waves 0-3 take strips [0, NS0), waves 4-7 [NS0, NS).
+template <int NS>
+struct Cfg {
+  static constexpr int P = 16 * NS;
+  static constexpr int NS0 = (NS + 1) / 2;
+  static constexpr int NS1 = NS - NS0;
+  static constexpr int XI = (128 * NS + kThreads - 1) / kThreads;  // x (row pair, piece) items per thread
+  static constexpr int JS = (NS + 1) / 2;                            // state blocks per wave, at most
 };
 
-// Workgroup of NW = 4 * (PT / 16) waves.  Loads: C and B as 16-byte pieces,
-// RPT consecutive rows per thread (so B can be written transposed with one
-// LDS store per n); x two rows per thread.
-template <int PT>
-struct Shape {
-  static constexpr int NPT = PT / 16;        // 16-wide subtiles of the headdim slice
-  static constexpr int NW = 4 * NPT;         // waves
-  static constexpr int NT = 64 * NW;         // threads
-  static constexpr int RPT = 1024 / NT;      // rows of C / B per thread (8 pieces per row)
-  static constexpr int XPR = PT / 8;         // x pieces per row
-  static constexpr int XT = 64 * XPR;        // threads loading x (2 rows each)
+template <int NS>
+struct alignas(16) HeadSmem {
+  uint16_t C[kQ][kRowN];         // C chunk, row-major [l][n]
+  uint16_t B[kQ][kRowN];         // B chunk, row-major [s][n]
+  uint16_t Bt[kN][kRowQ];        // B chunk transposed [n][swz(n, s)]
+  uint16_t Xt[16 * NS][kRowQ];   // x chunk transposed [p][swz(p, s)]
+  uint16_t Shi[16 * NS][kRowN];  // state entering the chunk, [p][n], bf16 high part
+  uint16_t Slo[16 * NS][kRowN];  //                                   bf16 low part
+  float EL[8][kQ];               // 2^(dA[l] - dA[16 J]) for l >= 16 J
+  float ESD[kQ];                 // 2^(dA[16 (s / 16)] - dA[s]) dt[s]
+  float dA[kQ];                  // inclusive cumsum of dt * A * log2(e)
+  float dt[kQ];                  // dt after softplus and clip
+  float wS[kQ];                  // 2^(dA[Q-1] - dA[s]) * dt[s]: state-update weights
+  float eA[kQ];                  // 2^dA[l]: decay of the incoming state
 };
 
-template <int PT>
+template <int NS>
+struct alignas(16) SummSmem {
+  uint16_t Bt[kN][kRowQ];
+  uint16_t Xt[16 * NS][kRowQ];
+  float dt[kQ];
+  float wS[kQ];
+};
+
+template <int NS>
 struct ChunkRegs {
-  uint4 c[Shape<PT>::RPT], b[Shape<PT>::RPT], x[2];
+  uint4 c[2], b[2], x[Cfg<NS>::XI][2];
   float dt;
   int valid;  // tokens of this chunk inside the sequence (fewer in a ragged last chunk)
 };
 
+// Workspace (floats): the state entering segments 1 .. nseg-1, then the
+// piece summaries (state from zero) and the pieces' log2 decays.
+__host__ __device__ inline size_t ws_sin_floats(const ChunkKernelArgs& a) {
+  return static_cast<size_t>(a.batch) * a.nheads * (a.nseg - 1) * a.headdim * kN;
+}
+__host__ __device__ inline size_t ws_piece_floats(const ChunkKernelArgs& a) {
+  return static_cast<size_t>(a.batch) * a.nheads * (a.nseg - 1) * a.ppseg * a.headdim * kN;
+}
+__host__ __device__ inline size_t ws_dec_floats(const ChunkKernelArgs& a) {
+  return static_cast<size_t>(a.batch) * a.nheads * (a.nseg - 1) * a.ppseg;
+}
+
+// Shared pieces of both kernels: chunk loads into registers, their LDS
+// stores, the dt scan and the state-update MFMAs.
+template <int NS>
+struct ChunkIo {
+  const ChunkKernelArgs& a;
+  int b, h, g, tid;
+  int rg, pc;  // C / B: row pair, 8-column piece
+
+  __device__ ChunkIo(const ChunkKernelArgs& args, int b_, int h_, int tid_)
+      : a(args), b(b_), h(h_), g(h_ / (args.nheads / args.ngroups)), tid(tid_), rg(tid_ >> 3), pc(tid_ & 7) {}
+
+  // Rows past the end of the sequence (a ragged last chunk) load as zeros;
+  // their dt is set to 0 when stored, so they neither add to nor decay the
+  // state.  Rows of C are loaded when WITH_C.
+  template <bool kRag, bool WITH_C>
+  __device__ __forceinline__ void load(int c, ChunkRegs<NS>& R) const {
+    constexpr int P = Cfg<NS>::P;
+    const int L = a.seqlen, H = a.nheads, G = a.ngroups;
+    const size_t tok = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
+    R.valid = kRag ? L - c * kQ : kQ;
+    const uint16_t* Cc = static_cast<const uint16_t*>(a.C) + (tok * G + g) * kN;
+    const uint16_t* Bc = static_cast<const uint16_t*>(a.B) + (tok * G + g) * kN;
+    const uint16_t* xc = static_cast<const uint16_t*>(a.x) + (tok * H + h) * P;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 2 * rg + i;
+      const int o = r * G * kN + 8 * pc;
+      const bool in = !kRag || r < R.valid;
+      if constexpr (WITH_C) R.c[i] = load16_if(Cc + o, in);
+      R.b[i] = load16_if(Bc + o, in);
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg<NS>::XI; ++i) {
+      const int q = tid + kThreads * i;
+      if (Cfg<NS>::XI * kThreads == 128 * NS || q < 128 * NS) {
+        const int rgx = q / (2 * NS), pcx = q % (2 * NS);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * rgx + e;
+          const bool in = !kRag || r < R.valid;
+          R.x[i][e] = load16_if(xc + static_cast<size_t>(r) * H * P + 8 * pcx, in);
+        }
+      }
+    }
+    if (tid < R.valid) R.dt = a.dt[(tok + tid) * H + h];
+  }
+
+  template <bool kRag, bool WITH_C>
+  __device__ __forceinline__ void store(const ChunkRegs<NS>& R, uint16_t (*C)[kRowN], uint16_t (*B)[kRowN],
+                                        uint16_t (*Bt)[kRowQ], uint16_t (*Xt)[kRowQ], float* dts, float dtb) const {
+    if constexpr (WITH_C) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        *reinterpret_cast<uint4*>(&C[2 * rg + i][8 * pc]) = R.c[i];
+        *reinterpret_cast<uint4*>(&B[2 * rg + i][8 * pc]) = R.b[i];
+      }
+    }
+    // B transposed: 2 consecutive s for each of the 8 n of this piece
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint32_t*>(&Bt[8 * pc + j][swz(8 * pc + j, 2 * rg)]) =
+          half16(R.b[0], j) | (half16(R.b[1], j) << 16);
+#pragma unroll
+    for (int i = 0; i < Cfg<NS>::XI; ++i) {
+      const int q = tid + kThreads * i;
+      if (Cfg<NS>::XI * kThreads == 128 * NS || q < 128 * NS) {
+        const int rgx = q / (2 * NS), pcx = q % (2 * NS);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<uint32_t*>(&Xt[8 * pcx + j][swz(8 * pcx + j, 2 * rgx)]) =
+              half16(R.x[i][0], j) | (half16(R.x[i][1], j) << 16);
+      }
+    }
+    if (tid < kQ) {
+      const float pre = R.dt + dtb;
+      const float d = a.dt_softplus ? dt_softplus_clip(pre, a.dt_min, a.dt_max, a.sp_lo, a.sp_hi)
+                                    : __builtin_amdgcn_fmed3f(pre, a.dt_min, a.dt_max);
+      dts[tid] = !kRag || tid < R.valid ? d : 0.0f;
+    }
+  }
+};
+
+// Inclusive scan of the chunk's dt * A * log2(e) across a wave: lane holds
+// steps 2 lane and 2 lane + 1 (d0, d1); `last` is the chunk total.
+struct Scan2 {
+  float v0, v1, d0, d1, last;
+};
+__device__ __forceinline__ Scan2 scan_chunk(const float* dts, int lane, float Al2) {
+  const float2 dt2 = *reinterpret_cast<const float2*>(&dts[2 * lane]);
+  Scan2 r;
+  r.v0 = dt2.x;
+  r.v1 = dt2.y;
+  const float a0 = dt2.x * Al2, a1 = dt2.y * Al2;
+  float incl = a0 + a1;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  r.d0 = incl - a1;
+  r.d1 = incl;
+  r.last = __shfl(incl, 63);
+  return r;
+}
+
+// State update of the blocks (pb = (w >> 2) + 2 j, nb = w & 3) a wave owns:
+// S[j] <- dlast S[j] + sum_s x[s][p] (wS[s] B[s][n]).  The lane holds
+// S[p = 16 pb + 4 lg + r][n = 16 nb + li].
+template <int NS>
+__device__ __forceinline__ void state_update(f32x4 (&S)[Cfg<NS>::JS], float dlast, const uint16_t (*Bt)[kRowQ],
+                                             const uint16_t (*Xt)[kRowQ], const float* wS, int w, int li, int lg) {
+  const int nb = w & 3, pb0 = w >> 2;
+  const int nrow = 16 * nb + li;
+  bf16x8 bwh[4], bwl[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int s0 = 32 * kk + 8 * lg;
+    const bf16x8 bt = *reinterpret_cast<const bf16x8*>(&Bt[nrow][swz(nrow, s0)]);
+    const float4 w0 = *reinterpret_cast<const float4*>(&wS[s0]);
+    const float4 w1 = *reinterpret_cast<const float4*>(&wS[s0 + 4]);
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = static_cast<float>(bt[j]) * wv[j];
+      const __bf16 hv = static_cast<__bf16>(v);
+      bwh[kk][j] = hv;
+      bwl[kk][j] = static_cast<__bf16>(v - static_cast<float>(hv));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < Cfg<NS>::JS; ++j) {
+    const int pb = pb0 + 2 * j;
+    if (pb < NS) {
+      const int prow = 16 * pb + li;
+      f32x4 acc_hi = S[j] * dlast, acc_lo = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 xa = *reinterpret_cast<const bf16x8*>(&Xt[prow][swz(prow, 32 * kk + 8 * lg)]);
+        acc_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bwh[kk], acc_hi, 0, 0, 0);
+        acc_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bwl[kk], acc_lo, 0, 0, 0);
+      }
+      S[j] = acc_hi + acc_lo;
+    }
+  }
+}
+
+// Workgroup order: segment slowest, then batch, then head, so that the
+// workgroups running at once cover all heads of a segment (they read the same
+// B and C rows).
+__device__ __forceinline__ void decode_bid(const ChunkKernelArgs& a, int bid, int& b, int& h, int& k) {
+  h = bid % a.nheads;
+  bid /= a.nheads;
+  b = bid % a.batch;
+  k = bid / a.batch;
+}
+
+// ---- main kernel --------------------------------------------------------
 // GATE: the output is multiplied by SiLU(z).  Whole chunks run in the loop;
 // a ragged last chunk (L not a multiple of Q) runs after it in its own copy
 // of the chunk step, so the loop carries no row tests.
-template <typename OT, int PT, bool GATE>
-__global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
-  using Sh = Shape<PT>;
-  constexpr int NPT = Sh::NPT, NW = Sh::NW, NT = Sh::NT, RPT = Sh::RPT, XPR = Sh::XPR;
-  __shared__ Smem<PT> sm;
+template <typename OT, int NS, bool GATE>
+__global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
+  using Cf = Cfg<NS>;
+  constexpr int P = Cf::P, NS0 = Cf::NS0, NS1 = Cf::NS1, JS = Cf::JS;
+  __shared__ HeadSmem<NS> sm;
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
   const int li = lane & 15;
   const int lg = lane >> 4;
 
-  const int ntiles = a.headdim / PT;
-  int bid = blockIdx.x;
-  const int ptile = bid % ntiles;
-  bid /= ntiles;
-  const int h = bid % a.nheads;
-  const int b = bid / a.nheads;
-  const int g = h / (a.nheads / a.ngroups);
-  const int p0 = ptile * PT;
-  const int H = a.nheads, P = a.headdim, G = a.ngroups, L = a.seqlen;
+  int b, h, seg;
+  decode_bid(a, blockIdx.x, b, h, seg);
+  const int H = a.nheads, L = a.seqlen;
   const float Al2 = a.A[h] * kLog2e;
   const float dtb = a.dt_bias ? a.dt_bias[h] : 0.0f;
   // The decay between positions s <= l of a chunk is 2^(dA[l] - dA[s]).  It is
@@ -130,252 +316,202 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
   // block then stay under 2^90).  Otherwise each element takes its own
   // exponential.
   const bool factored = a.dt_max * fabsf(Al2) < 6.0f;
+  const ChunkIo<NS> io(a, b, h, tid);
 
-  const uint16_t* __restrict__ xg = static_cast<const uint16_t*>(a.x);
-  const uint16_t* __restrict__ Bg = static_cast<const uint16_t*>(a.B);
-  const uint16_t* __restrict__ Cg = static_cast<const uint16_t*>(a.C);
+  // chunks of this segment: [c_beg, c_end); whole ones below nfull
+  const int nfull = L / kQ;
+  const int c_beg = seg * a.cps;
+  const int c_end = min(a.nchunks, c_beg + a.cps);
+  const int c_whole = min(c_end, nfull);
 
-  const int rg = tid >> 3, pc = tid & 7;            // C / B: row group, 8-column piece
-  const int rgx = tid / XPR, pcx = tid % XPR;       // x: row pair, 8-column piece
-  const bool xload = tid < Sh::XT;
-
-  // Rows past the end of the sequence (the ragged last chunk) load as zeros,
-  // and their dt is set to 0 below: they add nothing to the state, do not
-  // decay it, and their outputs are not stored.
-  auto load_chunk = [&](int c, ChunkRegs<PT>& R, auto ragged) {
-    constexpr bool kRag = decltype(ragged)::value;
-    // chunk bases are wave-uniform; per-lane offsets fit in 32 bits
-    const size_t tok = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
-    R.valid = kRag ? L - c * kQ : kQ;
-    const uint16_t* Cc = Cg + (tok * G + g) * kN;
-    const uint16_t* Bc = Bg + (tok * G + g) * kN;
-    const uint16_t* xc = xg + (tok * H + h) * P + p0;
+  // State blocks of this wave (see state_update)
+  f32x4 S[JS];
+  const size_t bh = static_cast<size_t>(b) * H + h;
+  const float* s_in = seg == 0 ? a.state_in : a.ws + (bh * (a.nseg - 1) + (seg - 1)) * P * kN;
+  {
+    const int nb = w & 3, pb0 = w >> 2;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = RPT * rg + i;
-      const int o = r * G * kN + 8 * pc;
-      const bool in = !kRag || r < R.valid;
-      R.c[i] = load16_if(Cc + o, in);
-      R.b[i] = load16_if(Bc + o, in);
-    }
-    if (xload) {
+    for (int j = 0; j < JS; ++j) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = 2 * rgx + i;
-        const bool in = !kRag || r < R.valid;
-        R.x[i] = load16_if(xc + r * H * P + 8 * pcx, in);
+      for (int r = 0; r < 4; ++r) {
+        const int p = 16 * (pb0 + 2 * j) + 4 * lg + r;
+        S[j][r] = (s_in != nullptr && pb0 + 2 * j < NS)
+                      ? s_in[(seg == 0 ? bh * P * kN : 0) + static_cast<size_t>(p) * kN + 16 * nb + li]
+                      : 0.0f;
       }
     }
-    if (tid < R.valid) R.dt = a.dt[tok * H + h + tid * H];
-  };
-
-  // bf16 j of a 16-byte piece
-  auto half = [](const uint4& v, int j) -> uint32_t {
-    return (reinterpret_cast<const uint32_t*>(&v)[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
-  };
-
-  auto store_chunk = [&](const ChunkRegs<PT>& R, auto ragged) {
-    constexpr bool kRag = decltype(ragged)::value;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      *reinterpret_cast<uint4*>(&sm.C[RPT * rg + i][8 * pc]) = R.c[i];
-      *reinterpret_cast<uint4*>(&sm.B[RPT * rg + i][8 * pc]) = R.b[i];
-    }
-    // B transposed: RPT consecutive s for each of the 8 n of this piece
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if constexpr (RPT == 4) {
-        const uint32_t lo = half(R.b[0], j) | (half(R.b[1], j) << 16);
-        const uint32_t hi = half(R.b[2], j) | (half(R.b[3], j) << 16);
-        *reinterpret_cast<uint2*>(&sm.Bt[8 * pc + j][swz(8 * pc + j, 4 * rg)]) = make_uint2(lo, hi);
-      } else {
-        *reinterpret_cast<uint32_t*>(&sm.Bt[8 * pc + j][swz(8 * pc + j, 2 * rg)]) = half(R.b[0], j) | (half(R.b[1], j) << 16);
-      }
-    }
-    if (xload) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<uint32_t*>(&sm.Xt[8 * pcx + j][swz(8 * pcx + j, 2 * rgx)]) = half(R.x[0], j) | (half(R.x[1], j) << 16);
-    }
-    if (tid < kQ) {
-      const float pre = R.dt + dtb;
-      const float d = a.dt_softplus ? dt_softplus_clip(pre, a.dt_min, a.dt_max, a.sp_lo, a.sp_hi)
-                                    : __builtin_amdgcn_fmed3f(pre, a.dt_min, a.dt_max);
-      sm.dt[tid] = !kRag || tid < R.valid ? d : 0.0f;
-    }
-  };
-
-  // State block of this wave: n in [16 nb, 16 nb + 16), p in [16 ps, 16 ps + 16);
-  // lane holds S[p = 16 ps + 4 lg + r][n = 16 nb + li].
-  const int nb = w & 3, ps = w >> 2;
-  f32x4 S;
-  const size_t sbase = ((static_cast<size_t>(b) * H + h) * P + p0) * kN;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int p = 16 * ps + 4 * lg + r;
-    S[r] = a.state_in ? a.state_in[sbase + static_cast<size_t>(p) * kN + 16 * nb + li] : 0.0f;
   }
   auto publish_state = [&]() {
+    const int nb = w & 3, pb0 = w >> 2;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int p = 16 * ps + 4 * lg + r;
-      uint16_t hi, lo;
-      split_bf16(S[r], hi, lo);
-      sm.Shi[p][16 * nb + li] = hi;
-      sm.Slo[p][16 * nb + li] = lo;
+    for (int j = 0; j < JS; ++j) {
+      if (pb0 + 2 * j < NS) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int p = 16 * (pb0 + 2 * j) + 4 * lg + r;
+          uint16_t hi, lo;
+          split_bf16(S[j][r], hi, lo);
+          sm.Shi[p][16 * nb + li] = hi;
+          sm.Slo[p][16 * nb + li] = lo;
+        }
+      }
     }
   };
   publish_state();
 
-  // Output items of this wave: 16-row block I of the chunk and 16-column
-  // subtile pt; (w, 0) and (7 - w, NPT - 1) have 9 causal 16x16 blocks
-  // between them, for every wave.
-  const int I0 = w, I1 = 7 - w;
-  const int pt1 = NPT - 1;
-  float dv0 = 0.0f, dv1 = 0.0f;  // D for the lane's output column of each item
-  if (a.D) {
-    const int pa = p0 + li, pb = p0 + 16 * pt1 + li;
-    dv0 = a.d_per_channel ? a.D[static_cast<size_t>(h) * P + pa] : a.D[h];
-    dv1 = a.d_per_channel ? a.D[static_cast<size_t>(h) * P + pb] : a.D[h];
-  }
+  // Output items: 16-row blocks I0 = q and I1 = 7 - q, strips [sb, sb + ns)
+  const int q = w & 3, hw = w >> 2;
+  const int I0 = q, I1 = 7 - q;
+  const int sb = hw ? NS0 : 0;
+  const int ns = NS0 == NS1 ? NS0 : (hw ? NS1 : NS0);
+  // D: per head, added on the diagonal of M; per channel, after the sums
+  const bool dch = a.D != nullptr && a.d_per_channel;
+  const float dhead = (a.D != nullptr && !a.d_per_channel) ? a.D[h] : 0.0f;
 
-  ChunkRegs<PT> R;
-  const int nfull = L / kQ;  // whole chunks; a ragged one follows when L % Q != 0
-  // One chunk step: stage chunk c (already in R) in LDS, prefetch the next
-  // whole chunk, emit the chunk's outputs and advance the state.
+  ChunkRegs<NS> R;
   auto chunk_step = [&](const int c, auto ragged) {
     constexpr bool kRag = decltype(ragged)::value;
-    __syncthreads();  // the previous chunk's LDS readers are done
-    store_chunk(R, ragged);
-    if (!kRag && c + 1 < nfull) load_chunk(c + 1, R, std::false_type{});
-    __syncthreads();
+    // (every reader of the previous chunk's tiles passed the barrier before
+    // the state was published)
+    io.template store<kRag, true>(R, sm.C, sm.B, sm.Bt, sm.Xt, sm.dt, dtb);
+    if (!kRag && c + 1 < c_whole) io.template load<false, true>(c + 1, R);
 
-    // Every wave scans the chunk's log2 decays in registers (lane: steps
-    // 2 lane and 2 lane + 1), then writes its share of the tables.
-    {
-      const float2 dt2 = *reinterpret_cast<const float2*>(&sm.dt[2 * lane]);
-      const float v0 = dt2.x * Al2, v1 = dt2.y * Al2;
-      float incl = v0 + v1;
+    // gate values of this wave's outputs (row l = 16 I + li, columns
+    // 16 st + 4 lg .. + 3), fetched now so their latency overlaps the sums
+    const size_t tok0 = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
+    const int valid = kRag ? L - c * kQ : kQ;
+    uint4 zr[2][NS0];
+    if constexpr (GATE) {
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-      }
-      const float d0 = incl - v1, d1 = incl;  // dA[2 lane], dA[2 lane + 1]
-      const float last = __shfl(incl, 63);
-      // 16-blocks: wave w fills EL[J] for J = w, w + NW, ...
+      for (int it = 0; it < 2; ++it) {
+        const int l = 16 * (it ? I1 : I0) + li;
 #pragma unroll
-      for (int J = w; J < 8; J += NW) {
-        const float ref = __shfl(d0, 8 * J);  // dA[16 J]
-        if (2 * lane >= 16 * J) {
-          sm.EL[J][2 * lane] = exp2_fast(d0 - ref);
-          sm.EL[J][2 * lane + 1] = exp2_fast(d1 - ref);
+        for (int t = 0; t < NS0; ++t) {
+          zr[it][t] = make_uint4(0u, 0u, 0u, 0u);
+          if (t < ns && (!kRag || l < valid)) {
+            const size_t e = ((tok0 + l) * H + h) * P + 16 * (sb + t) + 4 * lg;
+            if (a.z_bf16) {
+              const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.z) + e);
+              zr[it][t].x = v.x;
+              zr[it][t].y = v.y;
+            } else {
+              zr[it][t] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.z) + e);
+            }
+          }
         }
       }
+    }
+    __syncthreads();
+
+    // Every wave scans the chunk's log2 decays in registers, then writes its
+    // share of the tables (wave w: EL[w]; waves 0 and 1 the per-step rows).
+    const Scan2 sc = scan_chunk(sm.dt, lane, Al2);
+    {
+      const int J = w;
+      const float ref = __shfl(sc.d0, 8 * J);  // dA[16 J]
+      if (2 * lane >= 16 * J) {
+        sm.EL[J][2 * lane] = exp2_fast(sc.d0 - ref);
+        sm.EL[J][2 * lane + 1] = exp2_fast(sc.d1 - ref);
+      }
       if (w == 0) {
-        const float ref = __shfl(d0, 8 * (lane >> 3));  // dA at the start of this lane's 16-block
-        sm.ESD[2 * lane] = exp2_fast(ref - d0) * dt2.x;
-        sm.ESD[2 * lane + 1] = exp2_fast(ref - d1) * dt2.y;
-        sm.dA[2 * lane] = d0;
-        sm.dA[2 * lane + 1] = d1;
+        const float r16 = __shfl(sc.d0, 8 * (lane >> 3));  // dA at the start of this lane's 16-block
+        sm.ESD[2 * lane] = exp2_fast(r16 - sc.d0) * sc.v0;
+        sm.ESD[2 * lane + 1] = exp2_fast(r16 - sc.d1) * sc.v1;
+        sm.dA[2 * lane] = sc.d0;
+        sm.dA[2 * lane + 1] = sc.d1;
       } else if (w == 1) {
-        sm.eA[2 * lane] = exp2_fast(d0);
-        sm.eA[2 * lane + 1] = exp2_fast(d1);
-        sm.wS[2 * lane] = exp2_fast(last - d0) * dt2.x;
-        sm.wS[2 * lane + 1] = exp2_fast(last - d1) * dt2.y;
+        sm.eA[2 * lane] = exp2_fast(sc.d0);
+        sm.eA[2 * lane + 1] = exp2_fast(sc.d1);
+        sm.wS[2 * lane] = exp2_fast(sc.last - sc.d0) * sc.v0;
+        sm.wS[2 * lane + 1] = exp2_fast(sc.last - sc.d1) * sc.v1;
       }
     }
     __syncthreads();
 
-    // x weighted for the state update, split into bf16 high and low parts:
-    // XW[p][s] = wS[s] x[s][p] (every thread a few elements)
-#pragma unroll
-    for (int idx = tid; idx < PT * (kQ / 8); idx += NT) {
-      const int p = idx / (kQ / 8), s0 = 8 * (idx % (kQ / 8));
-      const bf16x8 xr = *reinterpret_cast<const bf16x8*>(&sm.Xt[p][swz(p, s0)]);
-      const float4 w0 = *reinterpret_cast<const float4*>(&sm.wS[s0]);
-      const float4 w1 = *reinterpret_cast<const float4*>(&sm.wS[s0 + 4]);
-      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      bf16x8 hi8, lo8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = static_cast<float>(xr[j]) * wv[j];
-        const __bf16 hv = static_cast<__bf16>(v);
-        hi8[j] = hv;
-        lo8[j] = static_cast<__bf16>(v - static_cast<float>(hv));
-      }
-      *reinterpret_cast<bf16x8*>(&sm.XWh[p][s0]) = hi8;
-      *reinterpret_cast<bf16x8*>(&sm.XWl[p][s0]) = lo8;
-    }
-
-    // Intra-chunk sums of both items: 16x16 blocks J = 0..I of each, walked
-    // together (k-th block of each item in step k) with the LDS operands of
-    // step k + 1 loaded while step k computes.  M = cb . decay . dt, masked
-    // on the diagonal block, split into bf16 high and low parts for the MFMA.
+    // Intra-chunk sums of both items: blocks J = 0..I of each, walked together
+    // (J-th block of each item in step J) with the LDS operands of step J + 1
+    // loaded while step J computes.
     struct Ops {
-      float el;     // factored: 2^(dA[l] - dA[16 J]); otherwise dA[l]
-      float4 e4;    // factored: 2^(dA[16 J] - dA[s]) dt[s]; otherwise dA[s]
-      s16x4 xv;     // x[s][p] for the MFMA B operand
+      float el;   // factored: 2^(dA[l] - dA[16 J]); otherwise dA[l]
+      float4 e4;  // factored: 2^(dA[16 J] - dA[s]) dt[s]; otherwise dA[s]
     };
-    auto load_ops = [&](int I, int J, int pt) {
+    auto load_ops = [&](int I, int J) {
       Ops o;
       const int l_row = 16 * I + li, s0 = 16 * J + 4 * lg;
       o.el = factored ? sm.EL[J][l_row] : sm.dA[l_row];
       o.e4 = *reinterpret_cast<const float4*>(factored ? &sm.ESD[s0] : &sm.dA[s0]);
-      o.xv = *reinterpret_cast<const s16x4*>(&sm.Xt[16 * pt + li][swz(16 * pt + li, s0)]);
       return o;
     };
-    // cb^T block (I, J) from the B rows of block J and the C rows of block I:
-    // cb[r] = cb[l = 16 I + li][s = 16 J + 4 lg + r]
-    auto intra = [&](int I, int J, const bf16x8 (&bj)[2], const bf16x8 (&ci)[2], const Ops& o, f32x4& acc_hi,
-                     f32x4& acc_lo) {
+    // cb^T block (I, J): lane holds cb[l = 16 I + li][s = 16 J + 4 lg + r],
+    // which is the B operand M^T[s][l] of the next product as it stands.
+    auto intra = [&](int I, int J, const bf16x8 (&bj)[2], const bf16x8 (&ci)[2], const Ops& o,
+                     f32x4 (&acc)[NS0]) {
       f32x4 cb = {0.0f, 0.0f, 0.0f, 0.0f};
       cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bj[0], ci[0], cb, 0, 0, 0);
       cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bj[1], ci[1], cb, 0, 0, 0);
-      const int l_row = 16 * I + li;
       const float ev[4] = {o.e4.x, o.e4.y, o.e4.z, o.e4.w};
-      float dv4[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-      if (!factored) {
+      float m[4];
+      if (factored) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m[r] = cb[r] * o.el * ev[r];
+      } else {
         const float4 d4 = *reinterpret_cast<const float4*>(&sm.dt[16 * J + 4 * lg]);
-        dv4[0] = d4.x; dv4[1] = d4.y; dv4[2] = d4.z; dv4[3] = d4.w;
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m[r] = cb[r] * exp2_fast(o.el - ev[r]) * dv4[r];
+      }
+      if (J == I) {
+        // causal mask (only the diagonal block has s > l), applied after the
+        // product so a masked overflow never reaches the sum; D on the diagonal
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = 4 * lg + r;
+          m[r] = s < li ? m[r] : (s == li ? m[r] + dhead : 0.0f);
+        }
       }
       s16x4 mhi, mlo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float m = factored ? cb[r] * o.el * ev[r] : cb[r] * exp2_fast(o.el - ev[r]) * dv4[r];
-        // causal mask (only the diagonal block has s > l), applied after the
-        // product so a masked overflow never reaches the sum
-        const float mv = (J < I || 16 * J + 4 * lg + r <= l_row) ? m : 0.0f;
         uint16_t hi, lo;
-        split_bf16(mv, hi, lo);
+        split_bf16(m[r], hi, lo);
         mhi[r] = static_cast<short>(hi);
         mlo[r] = static_cast<short>(lo);
       }
-      acc_hi = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mhi, o.xv, acc_hi, 0, 0, 0);
-      acc_lo = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mlo, o.xv, acc_lo, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NS0; ++t) {
+        if (t < ns) {
+          const int prow = 16 * (sb + t) + li;
+          const s16x4 xv = *reinterpret_cast<const s16x4*>(&sm.Xt[prow][swz(prow, 16 * J + 4 * lg)]);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xv, mhi, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xv, mlo, acc[t], 0, 0, 0);
+        }
+      }
     };
     auto rows16 = [&](const uint16_t (*M)[kRowN], int blk, bf16x8 (&v)[2]) {
       v[0] = *reinterpret_cast<const bf16x8*>(&M[16 * blk + li][8 * lg]);
       v[1] = *reinterpret_cast<const bf16x8*>(&M[16 * blk + li][32 + 8 * lg]);
     };
     const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4 a0h = zero4, a0l = zero4, a1h = zero4, a1l = zero4;
-    {
-      bf16x8 c0[2], c1[2], bj[2];
-      rows16(sm.C, I0, c0);
-      rows16(sm.C, I1, c1);
-      rows16(sm.B, 0, bj);
-      Ops o0 = load_ops(I0, 0, 0), o1 = load_ops(I1, 0, pt1);
+    f32x4 acc0[NS0], acc1[NS0];
 #pragma unroll
+    for (int t = 0; t < NS0; ++t) acc0[t] = acc1[t] = zero4;
+    bf16x8 c0[2], c1[2];
+    rows16(sm.C, I0, c0);
+    rows16(sm.C, I1, c1);
+    {
+      bf16x8 bj[2];
+      rows16(sm.B, 0, bj);
+      Ops o0 = load_ops(I0, 0), o1 = load_ops(I1, 0);
+#pragma unroll SSD_KUNROLL
       for (int k = 0; k < 8; ++k) {
         // block k + 1's operands while block k computes (past an item's
         // diagonal they are valid LDS, loaded and not used)
         const int kn = k < 7 ? k + 1 : 7;
         bf16x8 bn[2];
         rows16(sm.B, kn, bn);
-        const Ops n0 = load_ops(I0, kn, 0), n1 = load_ops(I1, kn, pt1);
-        if (k <= I0) intra(I0, k, bj, c0, o0, a0h, a0l);
-        if (k <= I1) intra(I1, k, bj, c1, o1, a1h, a1l);
+        const Ops n0 = load_ops(I0, kn), n1 = load_ops(I1, kn);
+        if (k <= I0) intra(I0, k, bj, c0, o0, acc0);
+        if (k <= I1) intra(I1, k, bj, c1, o1, acc1);
         bj[0] = bn[0];
         bj[1] = bn[1];
         o0 = n0;
@@ -383,142 +519,307 @@ __global__ __launch_bounds__(Shape<PT>::NT) void ssd_kernel(ChunkKernelArgs a) {
       }
     }
 
-    // Readout of the incoming state, (C_I S^T)[l][p] scaled by 2^dA[l], plus
-    // the skip, into the LDS output tile.  Lane holds rows l = 16 I + 4 lg + r
-    // at column p = 16 pt + li.
-    auto finish = [&](const int I, const int pt, const f32x4& acc_hi, const f32x4& acc_lo, const float dv) {
-      f32x4 sr_hi = zero4, sr_lo = zero4;
+    // Readout of the incoming state, (S C_I^T)[p][l] scaled by 2^dA[l], added
+    // to the sums; then the per-channel skip, the gate and the store.  The
+    // lane holds rows p = 16 st + 4 lg + r of column l = 16 I + li.
+    auto finish = [&](const int it, const bf16x8 (&ci)[2], f32x4 (&acc)[NS0]) {
+      const int I = it ? I1 : I0;
+      const int l = 16 * I + li;
+      const float eAl = sm.eA[l];
+      const bool orow = !kRag || l < valid;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sm.C[16 * I + li][32 * kk + 8 * lg]);
-        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(&sm.Shi[16 * pt + li][32 * kk + 8 * lg]);
-        const bf16x8 sl = *reinterpret_cast<const bf16x8*>(&sm.Slo[16 * pt + li][32 * kk + 8 * lg]);
-        sr_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, sh, sr_hi, 0, 0, 0);
-        sr_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, sl, sr_lo, 0, 0, 0);
-      }
-      const int p = 16 * pt + li;
-      const float4 e4 = *reinterpret_cast<const float4*>(&sm.eA[16 * I + 4 * lg]);
-      const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
-      const s16x4 xv = *reinterpret_cast<const s16x4*>(&sm.Xt[p][swz(p, 16 * I + 4 * lg)]);
+      for (int t = 0; t < NS0; ++t) {
+        if (t < ns) {
+          const int st = sb + t;
+          f32x4 sr_hi = zero4, sr_lo = zero4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float xr = bf16_val(static_cast<uint16_t>(xv[r]));
-        sm.O[16 * I + 4 * lg + r][p] = fmaf(dv, xr, fmaf(ev[r], sr_hi[r] + sr_lo[r], acc_hi[r] + acc_lo[r]));
+          for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 sh = *reinterpret_cast<const bf16x8*>(&sm.Shi[16 * st + li][32 * kk + 8 * lg]);
+            const bf16x8 sl = *reinterpret_cast<const bf16x8*>(&sm.Slo[16 * st + li][32 * kk + 8 * lg]);
+            sr_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sh, ci[kk], sr_hi, 0, 0, 0);
+            sr_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl, ci[kk], sr_lo, 0, 0, 0);
+          }
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = fmaf(eAl, sr_hi[r] + sr_lo[r], acc[t][r]);
+          if (dch) {
+            const float4 d4 = *reinterpret_cast<const float4*>(a.D + static_cast<size_t>(h) * P + 16 * st + 4 * lg);
+            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int p = 16 * st + 4 * lg + r;
+              v[r] = fmaf(dv[r], bf16_val(sm.Xt[p][swz(p, l)]), v[r]);
+            }
+          }
+          if constexpr (GATE) {
+            float zv[4];
+            if (a.z_bf16) {
+              zv[0] = __uint_as_float(zr[it][t].x << 16);
+              zv[1] = __uint_as_float(zr[it][t].x & 0xffff0000u);
+              zv[2] = __uint_as_float(zr[it][t].y << 16);
+              zv[3] = __uint_as_float(zr[it][t].y & 0xffff0000u);
+            } else {
+              zv[0] = __uint_as_float(zr[it][t].x);
+              zv[1] = __uint_as_float(zr[it][t].y);
+              zv[2] = __uint_as_float(zr[it][t].z);
+              zv[3] = __uint_as_float(zr[it][t].w);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] *= silu(zv[r]);
+          }
+          if (orow) {
+            const size_t e = ((tok0 + l) * H + h) * P + 16 * st + 4 * lg;
+            if constexpr (sizeof(OT) == 4) {
+              *reinterpret_cast<float4*>(static_cast<float*>(a.out) + e) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+              uint2 o;
+              o.x = bf16_bits(v[0]) | (static_cast<uint32_t>(bf16_bits(v[1])) << 16);
+              o.y = bf16_bits(v[2]) | (static_cast<uint32_t>(bf16_bits(v[3])) << 16);
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + e) = o;
+            }
+          }
+        }
       }
     };
-    // The output pieces: thread tid stores 8 values of row l = tid / PPR (all
-    // of the tile's pieces, one per thread).  Its gate values are fetched
-    // here so that their latency overlaps the state readout.
-    constexpr int PPR = PT / 8;  // 8-value pieces per row
-    static_assert(kQ * PPR == NT, "one output piece per thread");
-    const int ol = tid / PPR, oq = tid % PPR;
-    const size_t tok0 = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
-    const size_t e0 = ((tok0 + ol) * H + h) * P + p0 + 8 * oq;
-    const bool orow = !kRag || ol < L - c * kQ;
-    uint4 zr0 = make_uint4(0u, 0u, 0u, 0u), zr1 = zr0;
-    if constexpr (GATE) {
-      if (orow) {
-        if (a.z_bf16) {
-          zr0 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.z) + e0);
-        } else {
-          zr0 = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.z) + e0);
-          zr1 = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.z) + e0 + 4);
-        }
-      }
-    }
-    finish(I0, 0, a0h, a0l, dv0);
-    finish(I1, pt1, a1h, a1l, dv1);
-    __syncthreads();  // output tile and XW complete; every wave is done reading Shi/Slo
+    finish(0, c0, acc0);
+    finish(1, c1, acc1);
 
-    // ---- the output tile to HBM: whole 16-byte pieces of each row (rows of
-    // the sequence only), times SiLU(z) when gated
-    if (orow) {
-      const float4 v0 = *reinterpret_cast<const float4*>(&sm.O[ol][8 * oq]);
-      const float4 v1 = *reinterpret_cast<const float4*>(&sm.O[ol][8 * oq + 4]);
-      float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      if constexpr (GATE) {
-        float zv[8];
-        if (a.z_bf16) {
-          const uint32_t zw[4] = {zr0.x, zr0.y, zr0.z, zr0.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            zv[2 * j] = __uint_as_float(zw[j] << 16);
-            zv[2 * j + 1] = __uint_as_float(zw[j] & 0xffff0000u);
-          }
-        } else {
-          const uint32_t zw[8] = {zr0.x, zr0.y, zr0.z, zr0.w, zr1.x, zr1.y, zr1.z, zr1.w};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) zv[j] = __uint_as_float(zw[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] *= silu(zv[j]);
-      }
-      if constexpr (sizeof(OT) == 4) {
-        float* o = static_cast<float*>(a.out) + e0;
-        *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
-      } else {
-        uint4 o;
-        o.x = bf16_bits(v[0]) | (static_cast<uint32_t>(bf16_bits(v[1])) << 16);
-        o.y = bf16_bits(v[2]) | (static_cast<uint32_t>(bf16_bits(v[3])) << 16);
-        o.z = bf16_bits(v[4]) | (static_cast<uint32_t>(bf16_bits(v[5])) << 16);
-        o.w = bf16_bits(v[6]) | (static_cast<uint32_t>(bf16_bits(v[7])) << 16);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + e0) = o;
-      }
-    }
-
-    // ---- state update of this wave's block: S <- 2^dA[Q-1] S + XW^T B
-    const float dlast = exp2_fast(sm.dA[kQ - 1]);
-    f32x4 acc_hi = S * dlast, acc_lo = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int s0 = 32 * kk + 8 * lg;
-      const bf16x8 xh = *reinterpret_cast<const bf16x8*>(&sm.XWh[16 * ps + li][s0]);
-      const bf16x8 xl = *reinterpret_cast<const bf16x8*>(&sm.XWl[16 * ps + li][s0]);
-      const bf16x8 bt = *reinterpret_cast<const bf16x8*>(&sm.Bt[16 * nb + li][swz(16 * nb + li, s0)]);
-      acc_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bt, acc_hi, 0, 0, 0);
-      acc_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bt, acc_lo, 0, 0, 0);
-    }
-    S = acc_hi + acc_lo;
+    // ---- state update (registers), published once every wave has read
+    // the incoming state
+    state_update<NS>(S, exp2_fast(sc.last), sm.Bt, sm.Xt, sm.wS, w, li, lg);
+    __syncthreads();
     publish_state();
   };
-  if (nfull > 0) load_chunk(0, R, std::false_type{});
-  for (int c = 0; c < nfull; ++c) chunk_step(c, std::false_type{});
-  if (nfull * kQ < L) {
-    load_chunk(nfull, R, std::true_type{});
+
+  if (c_beg < c_whole) io.template load<false, true>(c_beg, R);
+  for (int c = c_beg; c < c_whole; ++c) chunk_step(c, std::false_type{});
+  if (c_end > nfull && c_beg <= nfull) {
+    io.template load<true, true>(nfull, R);
     chunk_step(nfull, std::true_type{});
   }
 
-  if (a.state_out) {
+  if (a.state_out && seg == a.nseg - 1) {
+    const int nb = w & 3, pb0 = w >> 2;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int p = 16 * ps + 4 * lg + r;
-      a.state_out[sbase + static_cast<size_t>(p) * kN + 16 * nb + li] = S[r];
+    for (int j = 0; j < JS; ++j) {
+      if (pb0 + 2 * j < NS) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int p = 16 * (pb0 + 2 * j) + 4 * lg + r;
+          a.state_out[bh * P * kN + static_cast<size_t>(p) * kN + 16 * nb + li] = S[j][r];
+        }
+      }
     }
   }
 }
 
-template <typename OT, int PT>
+// ---- segment pieces: state reached from zero and total log2 decay --------
+// Workgroup (piece j of segment k < nseg - 1, batch, head); the piece covers
+// chunks [k cps + j kPiece, min(k cps + (j + 1) kPiece, (k + 1) cps)), all
+// whole (the ragged chunk, if any, is the last chunk of the last segment).
+template <int NS>
+__global__ __launch_bounds__(kThreads) void ssd_summary_kernel(ChunkKernelArgs a) {
+  using Cf = Cfg<NS>;
+  constexpr int P = Cf::P, JS = Cf::JS;
+  __shared__ SummSmem<NS> sm;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+
+  const int npieces = (a.nseg - 1) * a.ppseg;
+  int bid = blockIdx.x;
+  const int piece = bid % npieces;
+  bid /= npieces;
+  const int h = bid % a.nheads;
+  const int b = bid / a.nheads;
+  const int seg = piece / a.ppseg, j = piece % a.ppseg;
+  const int c_beg = seg * a.cps + j * kPiece;
+  const int c_end = min(c_beg + kPiece, (seg + 1) * a.cps);
+  const float Al2 = a.A[h] * kLog2e;
+  const float dtb = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const ChunkIo<NS> io(a, b, h, tid);
+
+  f32x4 S[JS];
+#pragma unroll
+  for (int t = 0; t < JS; ++t) S[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float dec = 0.0f;
+
+  ChunkRegs<NS> R;
+  if (c_beg < c_end) io.template load<false, false>(c_beg, R);
+  for (int c = c_beg; c < c_end; ++c) {
+    __syncthreads();  // the previous chunk's LDS readers are done
+    io.template store<false, false>(R, nullptr, nullptr, sm.Bt, sm.Xt, sm.dt, dtb);
+    if (c + 1 < c_end) io.template load<false, false>(c + 1, R);
+    __syncthreads();
+    const Scan2 sc = scan_chunk(sm.dt, lane, Al2);
+    if (w == 0) {
+      sm.wS[2 * lane] = exp2_fast(sc.last - sc.d0) * sc.v0;
+      sm.wS[2 * lane + 1] = exp2_fast(sc.last - sc.d1) * sc.v1;
+    }
+    dec += sc.last;
+    __syncthreads();
+    state_update<NS>(S, exp2_fast(sc.last), sm.Bt, sm.Xt, sm.wS, w, li, lg);
+  }
+
+  const size_t bh = static_cast<size_t>(b) * a.nheads + h;
+  const size_t slot = bh * npieces + piece;
+  float* out = a.ws + ws_sin_floats(a) + slot * P * kN;
+  const int nb = w & 3, pb0 = w >> 2;
+#pragma unroll
+  for (int t = 0; t < JS; ++t) {
+    if (pb0 + 2 * t < NS) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = 16 * (pb0 + 2 * t) + 4 * lg + r;
+        out[static_cast<size_t>(p) * kN + 16 * nb + li] = S[t][r];
+      }
+    }
+  }
+  if (tid == 0) a.ws[ws_sin_floats(a) + ws_piece_floats(a) + slot] = dec;
+}
+
+// ---- state entering each segment: the pieces chained in order ------------
+// Thread per (batch, head, state element); S <- 2^decay S + S_piece over the
+// pieces of segments 0 .. nseg - 2, starting from state_in (or zeros).
+__global__ __launch_bounds__(256) void ssd_compose_kernel(ChunkKernelArgs a) {
+  const int PN = a.headdim * kN;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= PN) return;
+  const size_t bh = blockIdx.y;
+  const int npieces = (a.nseg - 1) * a.ppseg;
+  float s = a.state_in ? a.state_in[bh * PN + e] : 0.0f;
+  const float* pieces = a.ws + ws_sin_floats(a) + bh * npieces * PN;
+  const float* decs = a.ws + ws_sin_floats(a) + ws_piece_floats(a) + bh * npieces;
+  float* sin = a.ws + bh * (a.nseg - 1) * PN;
+  for (int k = 0; k < a.nseg - 1; ++k) {
+    for (int j = 0; j < a.ppseg; ++j) {
+      const int pc = k * a.ppseg + j;
+      s = fmaf(exp2_fast(decs[pc]), s, pieces[static_cast<size_t>(pc) * PN + e]);
+    }
+    sin[static_cast<size_t>(k) * PN + e] = s;
+  }
+}
+
+template <int NS>
+int resident_blocks_per_cu() {
+  static int cached = 0;
+  int v = __atomic_load_n(&cached, __ATOMIC_RELAXED);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ssd_kernel<bf16s, NS, false>, kThreads, 0) != hipSuccess ||
+      n <= 0)
+    n = 1;
+  __atomic_store_n(&cached, n, __ATOMIC_RELAXED);
+  return n;
+}
+
+int resident_blocks(int headdim) {
+  static int cu_count[64] = {};
+  int dev = 0;
+  int cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    int c = __atomic_load_n(&cu_count[dev], __ATOMIC_RELAXED);
+    if (c <= 0 && hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+      __atomic_store_n(&cu_count[dev], c, __ATOMIC_RELAXED);
+    if (c > 0) cus = c;
+  }
+  int per = 1;
+  switch (headdim / 16) {
+    case 1: per = resident_blocks_per_cu<1>(); break;
+    case 2: per = resident_blocks_per_cu<2>(); break;
+    case 3: per = resident_blocks_per_cu<3>(); break;
+    case 4: per = resident_blocks_per_cu<4>(); break;
+    case 5: per = resident_blocks_per_cu<5>(); break;
+    case 6: per = resident_blocks_per_cu<6>(); break;
+    case 7: per = resident_blocks_per_cu<7>(); break;
+    default: per = resident_blocks_per_cu<8>(); break;
+  }
+  return cus * per;
+}
+
+template <typename OT, int NS>
 hipError_t go(const ChunkLaunch& l, hipStream_t s) {
   const ChunkKernelArgs& k = l.k;
-  const unsigned blocks = static_cast<unsigned>(k.batch) * k.nheads * (k.headdim / PT);
-  if (blocks == 0) return hipSuccess;
+  const unsigned heads = static_cast<unsigned>(k.batch) * k.nheads;
+  if (heads == 0) return hipSuccess;
+  if (k.nseg > 1) {
+    const unsigned pieces = heads * static_cast<unsigned>((k.nseg - 1) * k.ppseg);
+    hipLaunchKernelGGL((ssd_summary_kernel<NS>), dim3(pieces), dim3(kThreads), 0, s, k);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned pn = static_cast<unsigned>(k.headdim * kN);
+    hipLaunchKernelGGL(ssd_compose_kernel, dim3((pn + 255) / 256, heads), dim3(256), 0, s, k);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const unsigned blocks = heads * static_cast<unsigned>(k.nseg);
   return timed_launch(s, [&] {
     if (k.z != nullptr)
-      hipLaunchKernelGGL((ssd_kernel<OT, PT, true>), dim3(blocks), dim3(Shape<PT>::NT), 0, s, k);
+      hipLaunchKernelGGL((ssd_kernel<OT, NS, true>), dim3(blocks), dim3(kThreads), 0, s, k);
     else
-      hipLaunchKernelGGL((ssd_kernel<OT, PT, false>), dim3(blocks), dim3(Shape<PT>::NT), 0, s, k);
+      hipLaunchKernelGGL((ssd_kernel<OT, NS, false>), dim3(blocks), dim3(kThreads), 0, s, k);
   });
+}
+
+template <typename OT>
+hipError_t go_ns(const ChunkLaunch& l, hipStream_t s) {
+  switch (l.k.headdim / 16) {
+    case 1: return go<OT, 1>(l, s);
+    case 2: return go<OT, 2>(l, s);
+    case 3: return go<OT, 3>(l, s);
+    case 4: return go<OT, 4>(l, s);
+    case 5: return go<OT, 5>(l, s);
+    case 6: return go<OT, 6>(l, s);
+    case 7: return go<OT, 7>(l, s);
+    case 8: return go<OT, 8>(l, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-size_t chunk_workspace_bytes(int, int, int, int, int) { return 0; }
+// Segments per sequence: the caller's count (at most one per chunk), else
+// enough (batch, head, segment) workgroups to fill the device once, with at
+// least 8 chunks per segment.
+ChunkSplit chunk_split(int batch, int seqlen, int nheads, int headdim, int segments) {
+  ChunkSplit sp{1, 0, 0};
+  const int nchunks = (seqlen + kQ - 1) / kQ;
+  sp.cps = nchunks;
+  const long heads = static_cast<long>(batch) * nheads;
+  if (heads <= 0 || nchunks < 2 || headdim <= 0) return sp;
+  int s;
+  if (segments > 0) {
+    s = std::min(segments, nchunks);
+  } else {
+    if (nchunks < 16) return sp;
+    const long slots = resident_blocks(headdim);
+    s = heads >= slots ? 1 : static_cast<int>(slots / heads);
+    s = std::min(std::min(s, kMaxSeg), nchunks / 8);
+  }
+  if (s <= 1) return sp;
+  sp.cps = (nchunks + s - 1) / s;
+  sp.nseg = (nchunks + sp.cps - 1) / sp.cps;
+  sp.ppseg = (sp.cps + kPiece - 1) / kPiece;
+  return sp;
+}
+
+size_t chunk_workspace_bytes(int batch, int seqlen, int nheads, int headdim, int segments) {
+  const ChunkSplit sp = chunk_split(batch, seqlen, nheads, headdim, segments);
+  if (sp.nseg <= 1) return 0;
+  ChunkKernelArgs a{};
+  a.batch = batch;
+  a.nheads = nheads;
+  a.headdim = headdim;
+  a.nseg = sp.nseg;
+  a.ppseg = sp.ppseg;
+  return (ws_sin_floats(a) + ws_piece_floats(a) + ws_dec_floats(a)) * sizeof(float);
+}
 
 hipError_t launch_chunk(const ChunkLaunch& l, hipStream_t stream) {
-  const bool p32 = l.k.headdim % 32 == 0;
-  if (l.out_dtype == kBF16) return p32 ? go<bf16s, 32>(l, stream) : go<bf16s, 16>(l, stream);
-  return p32 ? go<float, 32>(l, stream) : go<float, 16>(l, stream);
+  if (l.out_dtype == kBF16) return go_ns<bf16s>(l, stream);
+  return go_ns<float>(l, stream);
 }
 
 }  // namespace ssm

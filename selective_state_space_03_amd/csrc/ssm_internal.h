@@ -122,6 +122,7 @@ hipError_t launch_decode(const DecodeLaunch& l, hipStream_t stream);
 constexpr int kSsdN = 64;
 constexpr int kSsdQ = 128;
 constexpr int kSsdMaxP = 128;
+constexpr int kSsdMaxSeg = 16;
 
 struct ChunkKernelArgs {
   const void* x;
@@ -135,18 +136,26 @@ struct ChunkKernelArgs {
   float* state_out;
   void* out;
   const void* z;  // gate (Bt, L, H, P) or null
-  float* ws;  // workspace
+  float* ws;  // workspace: segment states and piece summaries (nseg > 1)
   int batch, seqlen, nheads, headdim, ngroups, nchunks, d_per_channel, z_bf16;
   float dt_min, dt_max, sp_lo, sp_hi;
   int dt_softplus;
+  int nseg, cps, ppseg;  // segments per sequence, chunks per segment, summary pieces per segment
 };
+
+// How a sequence of the chunked scan is cut into segments (one workgroup per
+// batch, head and segment).
+struct ChunkSplit {
+  int nseg, cps, ppseg;
+};
+ChunkSplit chunk_split(int batch, int seqlen, int nheads, int headdim, int segments);
 
 struct ChunkLaunch {
   ChunkKernelArgs k;
   int x_dtype, bc_dtype, out_dtype;
 };
 
-size_t chunk_workspace_bytes(int batch, int seqlen, int nheads, int headdim, int ngroups);
+size_t chunk_workspace_bytes(int batch, int seqlen, int nheads, int headdim, int segments);
 hipError_t launch_chunk(const ChunkLaunch& l, hipStream_t stream);
 
 // ---- SSD-form decode step ------------------------------------------------

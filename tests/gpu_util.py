@@ -103,7 +103,7 @@ def scan_oracle(w: W.Workload, *, state_in=None, cache_in=None, batches=None, ch
 # ---------------------------------------------------------------------- SSD
 
 def ssd_gpu(w: W.Workload, *, out_dtype=torch.float32, state_in=None, want_state=True, D_override=None,
-            z_f32=False):
+            z_f32=False, segments=0):
     """The workload's gate z (when it has one) goes in as bf16, or as its fp32
     widening with z_f32."""
     d = w.dims
@@ -119,7 +119,7 @@ def ssd_gpu(w: W.Workload, *, out_dtype=torch.float32, state_in=None, want_state
     out = ssm.chunk_scan_fwd(dev_tensor(w, "x"), dev_tensor(w, "dt"), dev_tensor(w, "A"), dev_tensor(w, "B"),
                              dev_tensor(w, "C"), chunk_size=d["chunk_size"], D=D, dt_bias=dev_tensor(w, "dt_bias"),
                              dt_softplus=o["dt_softplus"], dt_min=o["dt_min"], dt_max=o["dt_max"],
-                             state_in=state_in, state_out=st, out_dtype=out_dtype, z=z)
+                             state_in=state_in, state_out=st, out_dtype=out_dtype, z=z, segments=segments)
     torch.cuda.synchronize()
     return out, st
 

@@ -188,12 +188,34 @@ def test_chunk_validation(L):
         "out_over_x": (_chunk(out=_addr(1) + 2), 1),
         "out_align": (_chunk(out=_addr(6) + 8), 1),
         "x_align": (_chunk(x=_addr(1) + 2), 1),
+        "segments_neg": (_chunk(segments=-1), 1),
+        "segments_big": (_chunk(segments=17), 1),
+        "ws_small": (_chunk(segments=4, workspace_bytes=1024), 3),
+        "ws_align": (_chunk(segments=4, workspace=_addr(20) + 16), 1),
     }
     for name, (p, want) in cases.items():
         assert L.ssm_chunk_scan_check(ctypes.byref(p)) == want, (name, L.ssm_last_error())
     assert L.ssm_chunk_scan_fwd(ctypes.byref(_chunk(d_state=16)), None) == 2
     # a sequence that is not a whole number of chunks is accepted
     assert L.ssm_chunk_scan_check(ctypes.byref(_chunk(seqlen=1000))) == 0, L.ssm_last_error()
+
+
+def test_chunk_workspace_size(L):
+    """Forced segments: per (batch, head), the state entering each segment
+    after the first, one (P x N) state and one decay per summary piece of up
+    to 16 chunks of the segments before the last; none for one segment."""
+    L.ssm_chunk_scan_workspace_size.restype = ctypes.c_size_t
+    size = lambda **kw: L.ssm_chunk_scan_workspace_size(ctypes.byref(_chunk(**kw)))
+    P, N, heads = 96, 64, 8
+    assert size(segments=1) == 0
+    assert size(segments=1, seqlen=100) == 0
+    # 8 chunks in 4 segments of 2: 3 incoming states, 3 pieces
+    assert size(segments=4) == 4 * heads * (3 * P * N + 3 * (P * N + 1))
+    # 36 chunks (ragged) in 2 segments of 18: 1 incoming state, 2 pieces
+    assert size(segments=2, seqlen=4500) == 4 * heads * (P * N + 2 * (P * N + 1))
+    # more segments than chunks: one chunk per segment
+    assert size(segments=16, seqlen=300) == 4 * heads * (2 * P * N + 2 * (P * N + 1))
+    assert size(segments=4, seqlen=0) == 0
 
 
 def _cdec(**kw):

@@ -114,6 +114,38 @@ def test_ssd_ragged_leaves_padding_untouched():
     check(np64(view), oo, TOL, "ssd ragged into view")
 
 
+@pytest.mark.parametrize("segments,seqlen,headdim", [(2, 4500, 48), (3, 2085, 96), (5, 4500, 32), (16, 2048, 16),
+                                                     (4, 1100, 128), (2, 2176, 80)])
+def test_ssd_segments(segments, seqlen, headdim):
+    """Sequences cut into segments whose incoming states are composed from
+    summaries of pieces of up to 16 chunks: against the oracle's chunked and
+    sequential forms, with a starting state, a gate and a ragged tail where L
+    is not a multiple of 128; and against the same call in one segment."""
+    w = _small(batch=2, seqlen=seqlen, nheads=3, headdim=headdim, ngroups=1, gated=True, unsaturated=True)
+    rng = np.random.Generator(np.random.PCG64(23))
+    st_in = rng.standard_normal((2, 3, headdim, 64)).astype(np.float32)
+    out, st = ssd_gpu(w, state_in=torch.from_numpy(st_in).to(DEV), segments=segments)
+    oo, so = ssd_oracle(w, state_in=st_in)
+    check(np64(out), oo, TOL, f"ssd segments={segments} out")
+    check(np64(st), so, TOL, f"ssd segments={segments} state")
+    oo, so = ssd_oracle(w, state_in=st_in, sequential=True)
+    check(np64(out), oo, TOL, f"ssd segments={segments} out vs sequential")
+    check(np64(st), so, TOL, f"ssd segments={segments} state vs sequential")
+    o1, s1 = ssd_gpu(w, state_in=torch.from_numpy(st_in).to(DEV), segments=1)
+    check(np64(out), np64(o1), TOL, "segmented vs one segment")
+    check(np64(st), np64(s1), TOL, "segmented vs one segment state")
+
+
+def test_ssd_segments_saturated_decay():
+    """Strong decay (saturated dt, |A| up to 16): states that reach the far
+    segments are tiny; the per-element exponential path of the decay."""
+    w = _small(batch=1, seqlen=3000, nheads=4, headdim=64, ngroups=2)
+    out, st = ssd_gpu(w, segments=6, out_dtype=torch.bfloat16)
+    oo, so = ssd_oracle(w)
+    check(np64(out), oo, TOL, "ssd saturated segments out", out_bf16=True)
+    check(np64(st), so, TOL, "ssd saturated segments state")
+
+
 @pytest.mark.parametrize("z_f32,out_bf16", [(False, False), (True, False), (False, True)])
 def test_ssd_gate(z_f32, out_bf16):
     """out * SiLU(z) with z in bf16 or fp32, ragged tail included."""
