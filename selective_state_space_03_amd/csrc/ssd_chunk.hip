@@ -75,6 +75,20 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
   lo = bf16_bits(v - bf16_val(hi));
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// (bf16(a), bf16(b)) in one word, a in the low half (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+// hi/lo split of a pair: hi = bf16 of each, lo = bf16 of each remainder
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pk_bf16(a, b);
+  lo = pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
 // bf16 j of a 16-byte piece
 __device__ __forceinline__ uint32_t half16(const uint4& v, int j) {
   return (reinterpret_cast<const uint32_t*>(&v)[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
@@ -138,18 +152,18 @@ __host__ __device__ inline size_t ws_dec_floats(const ChunkKernelArgs& a) {
 template <int NS>
 struct ChunkIo {
   const ChunkKernelArgs& a;
-  int b, h, g, tid;
-  int rg, pc;  // C / B: row pair, 8-column piece
+  int b, h, g;
 
-  __device__ ChunkIo(const ChunkKernelArgs& args, int b_, int h_, int tid_)
-      : a(args), b(b_), h(h_), g(h_ / (args.nheads / args.ngroups)), tid(tid_), rg(tid_ >> 3), pc(tid_ & 7) {}
+  __device__ ChunkIo(const ChunkKernelArgs& args, int b_, int h_)
+      : a(args), b(b_), h(h_), g(h_ / (args.nheads / args.ngroups)) {}
 
   // Rows past the end of the sequence (a ragged last chunk) load as zeros;
   // their dt is set to 0 when stored, so they neither add to nor decay the
   // state.  Rows of C are loaded when WITH_C.
   template <bool kRag, bool WITH_C>
-  __device__ __forceinline__ void load(int c, ChunkRegs<NS>& R) const {
+  __device__ __forceinline__ void load(int c, ChunkRegs<NS>& R, int tid) const {
     constexpr int P = Cfg<NS>::P;
+    const int rg = tid >> 3, pc = tid & 7;  // C / B: row pair, 8-column piece
     const int L = a.seqlen, H = a.nheads, G = a.ngroups;
     const size_t tok = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
     R.valid = kRag ? L - c * kQ : kQ;
@@ -182,7 +196,9 @@ struct ChunkIo {
 
   template <bool kRag, bool WITH_C>
   __device__ __forceinline__ void store(const ChunkRegs<NS>& R, uint16_t (*C)[kRowN], uint16_t (*B)[kRowN],
-                                        uint16_t (*Bt)[kRowQ], uint16_t (*Xt)[kRowQ], float* dts, float dtb) const {
+                                        uint16_t (*Bt)[kRowQ], uint16_t (*Xt)[kRowQ], float* dts, float dtb,
+                                        int tid) const {
+    const int rg = tid >> 3, pc = tid & 7;
     if constexpr (WITH_C) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -220,21 +236,37 @@ struct ChunkIo {
 struct Scan2 {
   float v0, v1, d0, d1, last;
 };
+// v of the lane selected by DPP control CTRL in the rows of ROWS; 0 where
+// the source lane does not exist or the row is not selected
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp0(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, true));
+}
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
+// 16-lane row, then the last lane of row 0 (2) added to row 1 (3), then lane
+// 31 to rows 2 and 3.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp0<0x111, 0xF>(v);  // row_shr:1
+  v += dpp0<0x112, 0xF>(v);  // row_shr:2
+  v += dpp0<0x114, 0xF>(v);  // row_shr:4
+  v += dpp0<0x118, 0xF>(v);  // row_shr:8
+  v += dpp0<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp0<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
 __device__ __forceinline__ Scan2 scan_chunk(const float* dts, int lane, float Al2) {
   const float2 dt2 = *reinterpret_cast<const float2*>(&dts[2 * lane]);
   Scan2 r;
   r.v0 = dt2.x;
   r.v1 = dt2.y;
   const float a0 = dt2.x * Al2, a1 = dt2.y * Al2;
-  float incl = a0 + a1;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
+  const float incl = wave_prefix_sum(a0 + a1);
   r.d0 = incl - a1;
   r.d1 = incl;
-  r.last = __shfl(incl, 63);
+  r.last = lane_value(incl, 63);
   return r;
 }
 
@@ -254,13 +286,15 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[Cfg<NS>::JS], float dlas
     const float4 w0 = *reinterpret_cast<const float4*>(&wS[s0]);
     const float4 w1 = *reinterpret_cast<const float4*>(&wS[s0 + 4]);
     const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    const uint4 bw = __builtin_bit_cast(uint4, bt);
+    const uint32_t bwd[4] = {bw.x, bw.y, bw.z, bw.w};
+    uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float v = static_cast<float>(bt[j]) * wv[j];
-      const __bf16 hv = static_cast<__bf16>(v);
-      bwh[kk][j] = hv;
-      bwl[kk][j] = static_cast<__bf16>(v - static_cast<float>(hv));
-    }
+    for (int j = 0; j < 4; ++j)
+      split2(__uint_as_float(bwd[j] << 16) * wv[2 * j], __uint_as_float(bwd[j] & 0xffff0000u) * wv[2 * j + 1], hi[j],
+             lo[j]);
+    bwh[kk] = __builtin_bit_cast(bf16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+    bwl[kk] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
   }
 #pragma unroll
   for (int j = 0; j < Cfg<NS>::JS; ++j) {
@@ -299,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
   constexpr int P = Cf::P, NS0 = Cf::NS0, NS1 = Cf::NS1, JS = Cf::JS;
   __shared__ HeadSmem<NS> sm;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
   const int lane = tid & 63;
   const int li = lane & 15;
   const int lg = lane >> 4;
@@ -316,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
   // block then stay under 2^90).  Otherwise each element takes its own
   // exponential.
   const bool factored = a.dt_max * fabsf(Al2) < 6.0f;
-  const ChunkIo<NS> io(a, b, h, tid);
+  const ChunkIo<NS> io(a, b, h);
 
   // chunks of this segment: [c_beg, c_end); whole ones below nfull
   const int nfull = L / kQ;
@@ -341,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
       }
     }
   }
-  auto publish_state = [&]() {
+  auto publish_state = [&](int li, int lg) {
     const int nb = w & 3, pb0 = w >> 2;
 #pragma unroll
     for (int j = 0; j < JS; ++j) {
@@ -357,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
       }
     }
   };
-  publish_state();
+  publish_state(li, lg);
 
   // Output items: 16-row blocks I0 = q and I1 = 7 - q, strips [sb, sb + ns)
   const int q = w & 3, hw = w >> 2;
@@ -371,10 +405,17 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
   ChunkRegs<NS> R;
   auto chunk_step = [&](const int c, auto ragged) {
     constexpr bool kRag = decltype(ragged)::value;
+    // Lane indexes re-derived from an opaque copy of the thread id: the LDS
+    // and global offsets built from them are then formed inside the loop
+    // instead of being hoisted out of it, which would hold some hundred
+    // registers across the whole loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
     // (every reader of the previous chunk's tiles passed the barrier before
     // the state was published)
-    io.template store<kRag, true>(R, sm.C, sm.B, sm.Bt, sm.Xt, sm.dt, dtb);
-    if (!kRag && c + 1 < c_whole) io.template load<false, true>(c + 1, R);
+    io.template store<kRag, true>(R, sm.C, sm.B, sm.Bt, sm.Xt, sm.dt, dtb, tid);
+    if (!kRag && c + 1 < c_whole) io.template load<false, true>(c + 1, R, tid);
 
     // gate values of this wave's outputs (row l = 16 I + li, columns
     // 16 st + 4 lg .. + 3), fetched now so their latency overlaps the sums
@@ -428,30 +469,47 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
     }
     __syncthreads();
 
-    // Intra-chunk sums of both items: blocks J = 0..I of each, walked together
-    // (J-th block of each item in step J) with the LDS operands of step J + 1
-    // loaded while step J computes.
+    // Intra-chunk sums of one item (16-row block I): blocks J = 0..I in a
+    // software pipeline -- in step J the C B^T product of block J + 1 is
+    // issued, the LDS operands of blocks J + 1 (decays, x^T) and J + 2 (B
+    // rows) are fetched, and block J's M is formed and multiplied -- with
+    // the diagonal block (masked, D on its diagonal) peeled off the loop.
     struct Ops {
-      float el;   // factored: 2^(dA[l] - dA[16 J]); otherwise dA[l]
-      float4 e4;  // factored: 2^(dA[16 J] - dA[s]) dt[s]; otherwise dA[s]
+      float el;           // factored: 2^(dA[l] - dA[16 J]); otherwise dA[l]
+      float4 e4;          // factored: 2^(dA[16 J] - dA[s]) dt[s]; otherwise dA[s]
+      s16x4 xv[NS0];      // x^T[p][s] fragments of the wave's strips
     };
-    auto load_ops = [&](int I, int J) {
-      Ops o;
+    auto rows16 = [&](const uint16_t (*M)[kRowN], int blk, bf16x8 (&v)[2]) {
+      v[0] = *reinterpret_cast<const bf16x8*>(&M[16 * blk + li][8 * lg]);
+      v[1] = *reinterpret_cast<const bf16x8*>(&M[16 * blk + li][32 + 8 * lg]);
+    };
+    auto load_ops = [&](int I, int J, Ops& o, auto fac) {
+      constexpr bool kFac = decltype(fac)::value;
       const int l_row = 16 * I + li, s0 = 16 * J + 4 * lg;
-      o.el = factored ? sm.EL[J][l_row] : sm.dA[l_row];
-      o.e4 = *reinterpret_cast<const float4*>(factored ? &sm.ESD[s0] : &sm.dA[s0]);
-      return o;
+      o.el = kFac ? sm.EL[J][l_row] : sm.dA[l_row];
+      o.e4 = *reinterpret_cast<const float4*>(kFac ? &sm.ESD[s0] : &sm.dA[s0]);
+#pragma unroll
+      for (int t = 0; t < NS0; ++t) {
+        if (t < ns) {
+          const int prow = 16 * (sb + t) + li;
+          o.xv[t] = *reinterpret_cast<const s16x4*>(&sm.Xt[prow][swz(prow, s0)]);
+        }
+      }
     };
-    // cb^T block (I, J): lane holds cb[l = 16 I + li][s = 16 J + 4 lg + r],
-    // which is the B operand M^T[s][l] of the next product as it stands.
-    auto intra = [&](int I, int J, const bf16x8 (&bj)[2], const bf16x8 (&ci)[2], const Ops& o,
-                     f32x4 (&acc)[NS0]) {
+    auto cbT = [&](const bf16x8 (&bj)[2], const bf16x8 (&ci)[2]) {
       f32x4 cb = {0.0f, 0.0f, 0.0f, 0.0f};
       cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bj[0], ci[0], cb, 0, 0, 0);
       cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bj[1], ci[1], cb, 0, 0, 0);
+      return cb;
+    };
+    // block (I, J): lane holds cb[l = 16 I + li][s = 16 J + 4 lg + r], which
+    // is the B operand M^T[s][l] of the x^T M^T product as it stands
+    auto block = [&](int J, const f32x4& cb, const Ops& o, f32x4 (&acc)[NS0], auto fac, auto diag) {
+      constexpr bool kFac = decltype(fac)::value;
+      constexpr bool kDiag = decltype(diag)::value;
       const float ev[4] = {o.e4.x, o.e4.y, o.e4.z, o.e4.w};
       float m[4];
-      if (factored) {
+      if constexpr (kFac) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) m[r] = cb[r] * o.el * ev[r];
       } else {
@@ -460,64 +518,46 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) m[r] = cb[r] * exp2_fast(o.el - ev[r]) * dv4[r];
       }
-      if (J == I) {
-        // causal mask (only the diagonal block has s > l), applied after the
-        // product so a masked overflow never reaches the sum; D on the diagonal
+      if constexpr (kDiag) {
+        // causal mask, applied after the product so a masked overflow never
+        // reaches the sum; the per-head skip D on the diagonal
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int s = 4 * lg + r;
           m[r] = s < li ? m[r] : (s == li ? m[r] + dhead : 0.0f);
         }
       }
-      s16x4 mhi, mlo;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint16_t hi, lo;
-        split_bf16(m[r], hi, lo);
-        mhi[r] = static_cast<short>(hi);
-        mlo[r] = static_cast<short>(lo);
-      }
+      uint32_t h01, l01, h23, l23;
+      split2(m[0], m[1], h01, l01);
+      split2(m[2], m[3], h23, l23);
+      const s16x4 mhi = __builtin_bit_cast(s16x4, make_uint2(h01, h23));
+      const s16x4 mlo = __builtin_bit_cast(s16x4, make_uint2(l01, l23));
 #pragma unroll
       for (int t = 0; t < NS0; ++t) {
         if (t < ns) {
-          const int prow = 16 * (sb + t) + li;
-          const s16x4 xv = *reinterpret_cast<const s16x4*>(&sm.Xt[prow][swz(prow, 16 * J + 4 * lg)]);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xv, mhi, acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xv, mlo, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(o.xv[t], mhi, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(o.xv[t], mlo, acc[t], 0, 0, 0);
         }
       }
     };
-    auto rows16 = [&](const uint16_t (*M)[kRowN], int blk, bf16x8 (&v)[2]) {
-      v[0] = *reinterpret_cast<const bf16x8*>(&M[16 * blk + li][8 * lg]);
-      v[1] = *reinterpret_cast<const bf16x8*>(&M[16 * blk + li][32 + 8 * lg]);
+    auto item = [&](const int I, const bf16x8 (&ci)[2], f32x4 (&acc)[NS0], auto fac) {
+      bf16x8 b0[2], b1[2];
+      Ops cur, nxt;
+      rows16(sm.B, 0, b0);
+      rows16(sm.B, I > 0 ? 1 : 0, b1);
+      load_ops(I, 0, cur, fac);
+      f32x4 cb = cbT(b0, ci);
+      for (int J = 0; J < I; ++J) {
+        const f32x4 cbn = cbT(b1, ci);   // block J + 1
+        rows16(sm.B, min(J + 2, 7), b1);  // block J + 2 (loaded, not used, past the diagonal)
+        load_ops(I, J + 1, nxt, fac);
+        block(J, cb, cur, acc, fac, std::false_type{});
+        cb = cbn;
+        cur = nxt;
+      }
+      block(I, cb, cur, acc, fac, std::true_type{});
     };
     const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4 acc0[NS0], acc1[NS0];
-#pragma unroll
-    for (int t = 0; t < NS0; ++t) acc0[t] = acc1[t] = zero4;
-    bf16x8 c0[2], c1[2];
-    rows16(sm.C, I0, c0);
-    rows16(sm.C, I1, c1);
-    {
-      bf16x8 bj[2];
-      rows16(sm.B, 0, bj);
-      Ops o0 = load_ops(I0, 0), o1 = load_ops(I1, 0);
-#pragma unroll SSD_KUNROLL
-      for (int k = 0; k < 8; ++k) {
-        // block k + 1's operands while block k computes (past an item's
-        // diagonal they are valid LDS, loaded and not used)
-        const int kn = k < 7 ? k + 1 : 7;
-        bf16x8 bn[2];
-        rows16(sm.B, kn, bn);
-        const Ops n0 = load_ops(I0, kn), n1 = load_ops(I1, kn);
-        if (k <= I0) intra(I0, k, bj, c0, o0, acc0);
-        if (k <= I1) intra(I1, k, bj, c1, o1, acc1);
-        bj[0] = bn[0];
-        bj[1] = bn[1];
-        o0 = n0;
-        o1 = n1;
-      }
-    }
 
     // Readout of the incoming state, (S C_I^T)[p][l] scaled by 2^dA[l], added
     // to the sums; then the per-channel skip, the gate and the store.  The
@@ -527,6 +567,17 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
       const int l = 16 * I + li;
       const float eAl = sm.eA[l];
       const bool orow = !kRag || l < valid;
+      bf16x8 sh[NS0][2], sl[NS0][2];
+#pragma unroll
+      for (int t = 0; t < NS0; ++t) {
+        if (t < ns) {
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            sh[t][kk] = *reinterpret_cast<const bf16x8*>(&sm.Shi[16 * (sb + t) + li][32 * kk + 8 * lg]);
+            sl[t][kk] = *reinterpret_cast<const bf16x8*>(&sm.Slo[16 * (sb + t) + li][32 * kk + 8 * lg]);
+          }
+        }
+      }
 #pragma unroll
       for (int t = 0; t < NS0; ++t) {
         if (t < ns) {
@@ -534,10 +585,8 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
           f32x4 sr_hi = zero4, sr_lo = zero4;
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 sh = *reinterpret_cast<const bf16x8*>(&sm.Shi[16 * st + li][32 * kk + 8 * lg]);
-            const bf16x8 sl = *reinterpret_cast<const bf16x8*>(&sm.Slo[16 * st + li][32 * kk + 8 * lg]);
-            sr_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sh, ci[kk], sr_hi, 0, 0, 0);
-            sr_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl, ci[kk], sr_lo, 0, 0, 0);
+            sr_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sh[t][kk], ci[kk], sr_hi, 0, 0, 0);
+            sr_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl[t][kk], ci[kk], sr_lo, 0, 0, 0);
           }
           float v[4];
 #pragma unroll
@@ -572,29 +621,40 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
             if constexpr (sizeof(OT) == 4) {
               *reinterpret_cast<float4*>(static_cast<float*>(a.out) + e) = make_float4(v[0], v[1], v[2], v[3]);
             } else {
-              uint2 o;
-              o.x = bf16_bits(v[0]) | (static_cast<uint32_t>(bf16_bits(v[1])) << 16);
-              o.y = bf16_bits(v[2]) | (static_cast<uint32_t>(bf16_bits(v[3])) << 16);
-              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + e) = o;
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + e) =
+                  make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
             }
           }
         }
       }
     };
-    finish(0, c0, acc0);
-    finish(1, c1, acc1);
+    // each item's sums, then its outputs
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int I = it ? I1 : I0;
+      f32x4 acc[NS0];
+#pragma unroll
+      for (int t = 0; t < NS0; ++t) acc[t] = zero4;
+      bf16x8 ci[2];
+      rows16(sm.C, I, ci);
+      if (factored)
+        item(I, ci, acc, std::true_type{});
+      else
+        item(I, ci, acc, std::false_type{});
+      finish(it, ci, acc);
+    }
 
     // ---- state update (registers), published once every wave has read
     // the incoming state
     state_update<NS>(S, exp2_fast(sc.last), sm.Bt, sm.Xt, sm.wS, w, li, lg);
     __syncthreads();
-    publish_state();
+    publish_state(li, lg);
   };
 
-  if (c_beg < c_whole) io.template load<false, true>(c_beg, R);
+  if (c_beg < c_whole) io.template load<false, true>(c_beg, R, tid);
   for (int c = c_beg; c < c_whole; ++c) chunk_step(c, std::false_type{});
   if (c_end > nfull && c_beg <= nfull) {
-    io.template load<true, true>(nfull, R);
+    io.template load<true, true>(nfull, R, tid);
     chunk_step(nfull, std::true_type{});
   }
 
@@ -623,7 +683,7 @@ __global__ __launch_bounds__(kThreads) void ssd_summary_kernel(ChunkKernelArgs a
   constexpr int P = Cf::P, JS = Cf::JS;
   __shared__ SummSmem<NS> sm;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
   const int lane = tid & 63;
   const int li = lane & 15;
   const int lg = lane >> 4;
@@ -639,7 +699,7 @@ __global__ __launch_bounds__(kThreads) void ssd_summary_kernel(ChunkKernelArgs a
   const int c_end = min(c_beg + kPiece, (seg + 1) * a.cps);
   const float Al2 = a.A[h] * kLog2e;
   const float dtb = a.dt_bias ? a.dt_bias[h] : 0.0f;
-  const ChunkIo<NS> io(a, b, h, tid);
+  const ChunkIo<NS> io(a, b, h);
 
   f32x4 S[JS];
 #pragma unroll
@@ -647,11 +707,14 @@ __global__ __launch_bounds__(kThreads) void ssd_summary_kernel(ChunkKernelArgs a
   float dec = 0.0f;
 
   ChunkRegs<NS> R;
-  if (c_beg < c_end) io.template load<false, false>(c_beg, R);
+  if (c_beg < c_end) io.template load<false, false>(c_beg, R, tid);
   for (int c = c_beg; c < c_end; ++c) {
+    int tid = threadIdx.x;  // opaque copy: offsets formed inside the loop (see ssd_kernel)
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
     __syncthreads();  // the previous chunk's LDS readers are done
-    io.template store<false, false>(R, nullptr, nullptr, sm.Bt, sm.Xt, sm.dt, dtb);
-    if (c + 1 < c_end) io.template load<false, false>(c + 1, R);
+    io.template store<false, false>(R, nullptr, nullptr, sm.Bt, sm.Xt, sm.dt, dtb, tid);
+    if (c + 1 < c_end) io.template load<false, false>(c + 1, R, tid);
     __syncthreads();
     const Scan2 sc = scan_chunk(sm.dt, lane, Al2);
     if (w == 0) {
