@@ -15,18 +15,20 @@
 // sequence) walks the segment's chunks in order with the head's whole state
 // (P x N, fp32) in MFMA accumulators, so C B^T and the decay-weighted matrix M
 // of a chunk are formed once per head (they do not depend on the headdim
-// column).  The incoming state of every segment but the first comes from two
+// column).  Waves 0-3 form the chunk's outputs; waves 4-7 own the state (one
+// 16-wide n-block each), load and stage the chunks, scan the decays and
+// advance the state while waves 0-3 compute, one wave of each kind per SIMD.  The incoming state of every segment but the first comes from two
 // small launches before it: ssd_summary_kernel reduces pieces of up to 16
 // chunks to (state reached from zero, total log2 decay) -- the state update
 // alone, parallel over pieces -- and ssd_compose_kernel chains them per state
 // element in order, S <- 2^decay S + S_piece, which is the same recurrence
 // taken a piece at a time.
 //
-// Per chunk: C, B (both layouts), x (transposed) and dt are staged in LDS while
-// the next chunk's loads are in flight; every wave scans dt * A in registers
-// and fills a share of the decay tables; wave (q, half) owns the 16-row blocks
-// q and 7 - q of the chunk (9 causal blocks, the same for every wave) for half
-// of the 16-wide headdim strips, and for each block J <= I
+// Per chunk: the state waves stage C, B (both layouts), x (transposed) and dt
+// in LDS while the next chunk's loads are in flight, scan dt * A in registers
+// and fill the decay tables; output wave q owns the 16-row blocks q and 7 - q
+// of the chunk (9 causal blocks, the same for every wave) for all 16-wide
+// headdim strips, and for each block J <= I
 //   cb^T block     = B_J C_I^T              v_mfma_f32_16x16x32_bf16
 //   M (masked)     = cb . 2^(dA_l - dA_s) . dt_s, the skip D on its diagonal
 //   out^T[strip]  += X_J^T M^T              v_mfma_f32_16x16x16_bf16, M hi + lo
@@ -94,31 +96,34 @@ __device__ __forceinline__ uint32_t half16(const uint4& v, int j) {
   return (reinterpret_cast<const uint32_t*>(&v)[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
 }
 
-// Headdim P = 16 NS.  Waves 0-3 take strips [0, NS0), waves 4-7 [NS0, NS).
-template <int NS>
-struct Cfg {
-  static constexpr int P = 16 * NS;
-  static constexpr int NS0 = (NS + 1) / 2;
-  static constexpr int NS1 = NS - NS0;
-  static constexpr int XI = (128 * NS + kThreads - 1) / kThreads;  // x (row pair, piece) items per thread
-  static constexpr int JS = (NS + 1) / 2;                            // state blocks per wave, at most
+constexpr int kIoThreads = 256;  // threads of the state waves (4 x 64)
+
+// Decay tables of one chunk
+struct alignas(16) DecayTables {
+  float EL[8][kQ];  // 2^(dA[l] - dA[16 J]) for l >= 16 J
+  float ESD[kQ];    // 2^(dA[16 (s / 16)] - dA[s]) dt[s]
+  float dA[kQ];     // inclusive cumsum of dt * A * log2(e)
+  float dt[kQ];     // dt after softplus and clip
+  float wS[kQ];     // 2^(dA[Q-1] - dA[s]) * dt[s]: state-update weights
+  float eA[kQ];     // 2^dA[l]: decay of the incoming state (eA[Q-1]: of the whole chunk)
 };
 
-template <int NS>
+// The chunk's tiles, and NB copies of the incoming state and of the decay
+// tables (two: those of the next chunk are written while the current ones
+// are read).
+template <int NS, int NB>
 struct alignas(16) HeadSmem {
-  uint16_t C[kQ][kRowN];         // C chunk, row-major [l][n]
-  uint16_t B[kQ][kRowN];         // B chunk, row-major [s][n]
-  uint16_t Bt[kN][kRowQ];        // B chunk transposed [n][swz(n, s)]
-  uint16_t Xt[16 * NS][kRowQ];   // x chunk transposed [p][swz(p, s)]
-  uint16_t Shi[16 * NS][kRowN];  // state entering the chunk, [p][n], bf16 high part
-  uint16_t Slo[16 * NS][kRowN];  //                                   bf16 low part
-  float EL[8][kQ];               // 2^(dA[l] - dA[16 J]) for l >= 16 J
-  float ESD[kQ];                 // 2^(dA[16 (s / 16)] - dA[s]) dt[s]
-  float dA[kQ];                  // inclusive cumsum of dt * A * log2(e)
-  float dt[kQ];                  // dt after softplus and clip
-  float wS[kQ];                  // 2^(dA[Q-1] - dA[s]) * dt[s]: state-update weights
-  float eA[kQ];                  // 2^dA[l]: decay of the incoming state
+  uint16_t C[kQ][kRowN];             // C chunk, row-major [l][n]
+  uint16_t B[kQ][kRowN];             // B chunk, row-major [s][n]
+  uint16_t Bt[kN][kRowQ];            // B chunk transposed [n][swz(n, s)]
+  uint16_t Xt[16 * NS][kRowQ];       // x chunk transposed [p][swz(p, s)]
+  uint16_t Shi[NB][16 * NS][kRowN];  // state entering the chunk, [p][n], bf16 high part
+  uint16_t Slo[NB][16 * NS][kRowN];  //                                   bf16 low part
+  DecayTables tb[NB];
 };
+constexpr size_t kLdsBytes = 160 * 1024;
+template <int NS>
+constexpr int kStateBuffers = sizeof(HeadSmem<NS, 2>) <= kLdsBytes ? 2 : 1;
 
 template <int NS>
 struct alignas(16) SummSmem {
@@ -128,9 +133,13 @@ struct alignas(16) SummSmem {
   float wS[kQ];
 };
 
-template <int NS>
+// A chunk in registers, loaded by NT threads: RPT rows of C and B and XI
+// (row pair, 8-column piece) items of x per thread.  Headdim P = 16 NS.
+template <int NS, int NT>
 struct ChunkRegs {
-  uint4 c[2], b[2], x[Cfg<NS>::XI][2];
+  static constexpr int RPT = 1024 / NT;
+  static constexpr int XI = (128 * NS + NT - 1) / NT;
+  uint4 c[RPT], b[RPT], x[XI][2];
   float dt;
   int valid;  // tokens of this chunk inside the sequence (fewer in a ragged last chunk)
 };
@@ -149,8 +158,10 @@ __host__ __device__ inline size_t ws_dec_floats(const ChunkKernelArgs& a) {
 
 // Shared pieces of both kernels: chunk loads into registers, their LDS
 // stores, the dt scan and the state-update MFMAs.
-template <int NS>
+template <int NS, int NT>
 struct ChunkIo {
+  using Regs = ChunkRegs<NS, NT>;
+  static constexpr int RPT = Regs::RPT, XI = Regs::XI;
   const ChunkKernelArgs& a;
   int b, h, g;
 
@@ -160,10 +171,10 @@ struct ChunkIo {
   // Rows past the end of the sequence (a ragged last chunk) load as zeros;
   // their dt is set to 0 when stored, so they neither add to nor decay the
   // state.  Rows of C are loaded when WITH_C.
-  template <bool kRag, bool WITH_C>
-  __device__ __forceinline__ void load(int c, ChunkRegs<NS>& R, int tid) const {
-    constexpr int P = Cfg<NS>::P;
-    const int rg = tid >> 3, pc = tid & 7;  // C / B: row pair, 8-column piece
+  template <bool kRag, bool WITH_C, bool WITH_DT = true>
+  __device__ __forceinline__ void load(int c, Regs& R, int tid) const {
+    constexpr int P = 16 * NS;
+    const int rg = tid >> 3, pc = tid & 7;  // C / B: row group, 8-column piece
     const int L = a.seqlen, H = a.nheads, G = a.ngroups;
     const size_t tok = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
     R.valid = kRag ? L - c * kQ : kQ;
@@ -171,17 +182,17 @@ struct ChunkIo {
     const uint16_t* Bc = static_cast<const uint16_t*>(a.B) + (tok * G + g) * kN;
     const uint16_t* xc = static_cast<const uint16_t*>(a.x) + (tok * H + h) * P;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 2 * rg + i;
+    for (int i = 0; i < RPT; ++i) {
+      const int r = RPT * rg + i;
       const int o = r * G * kN + 8 * pc;
       const bool in = !kRag || r < R.valid;
       if constexpr (WITH_C) R.c[i] = load16_if(Cc + o, in);
       R.b[i] = load16_if(Bc + o, in);
     }
 #pragma unroll
-    for (int i = 0; i < Cfg<NS>::XI; ++i) {
-      const int q = tid + kThreads * i;
-      if (Cfg<NS>::XI * kThreads == 128 * NS || q < 128 * NS) {
+    for (int i = 0; i < XI; ++i) {
+      const int q = tid + NT * i;
+      if (XI * NT == 128 * NS || q < 128 * NS) {
         const int rgx = q / (2 * NS), pcx = q % (2 * NS);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -191,30 +202,37 @@ struct ChunkIo {
         }
       }
     }
-    if (tid < R.valid) R.dt = a.dt[(tok + tid) * H + h];
+    if (WITH_DT && tid < R.valid) R.dt = a.dt[(tok + tid) * H + h];
   }
 
-  template <bool kRag, bool WITH_C>
-  __device__ __forceinline__ void store(const ChunkRegs<NS>& R, uint16_t (*C)[kRowN], uint16_t (*B)[kRowN],
+  template <bool kRag, bool WITH_C, bool WITH_DT = true>
+  __device__ __forceinline__ void store(const Regs& R, uint16_t (*C)[kRowN], uint16_t (*B)[kRowN],
                                         uint16_t (*Bt)[kRowQ], uint16_t (*Xt)[kRowQ], float* dts, float dtb,
                                         int tid) const {
     const int rg = tid >> 3, pc = tid & 7;
     if constexpr (WITH_C) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        *reinterpret_cast<uint4*>(&C[2 * rg + i][8 * pc]) = R.c[i];
-        *reinterpret_cast<uint4*>(&B[2 * rg + i][8 * pc]) = R.b[i];
+      for (int i = 0; i < RPT; ++i) {
+        *reinterpret_cast<uint4*>(&C[RPT * rg + i][8 * pc]) = R.c[i];
+        *reinterpret_cast<uint4*>(&B[RPT * rg + i][8 * pc]) = R.b[i];
       }
     }
-    // B transposed: 2 consecutive s for each of the 8 n of this piece
+    // B transposed: RPT consecutive s for each of the 8 n of this piece
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<uint32_t*>(&Bt[8 * pc + j][swz(8 * pc + j, 2 * rg)]) =
-          half16(R.b[0], j) | (half16(R.b[1], j) << 16);
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (RPT == 4) {
+        const uint32_t lo = half16(R.b[0], j) | (half16(R.b[1], j) << 16);
+        const uint32_t hi = half16(R.b[2], j) | (half16(R.b[3], j) << 16);
+        *reinterpret_cast<uint2*>(&Bt[8 * pc + j][swz(8 * pc + j, 4 * rg)]) = make_uint2(lo, hi);
+      } else {
+        *reinterpret_cast<uint32_t*>(&Bt[8 * pc + j][swz(8 * pc + j, 2 * rg)]) =
+            half16(R.b[0], j) | (half16(R.b[1], j) << 16);
+      }
+    }
 #pragma unroll
-    for (int i = 0; i < Cfg<NS>::XI; ++i) {
-      const int q = tid + kThreads * i;
-      if (Cfg<NS>::XI * kThreads == 128 * NS || q < 128 * NS) {
+    for (int i = 0; i < XI; ++i) {
+      const int q = tid + NT * i;
+      if (XI * NT == 128 * NS || q < 128 * NS) {
         const int rgx = q / (2 * NS), pcx = q % (2 * NS);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -222,7 +240,7 @@ struct ChunkIo {
               half16(R.x[i][0], j) | (half16(R.x[i][1], j) << 16);
       }
     }
-    if (tid < kQ) {
+    if (WITH_DT && tid < kQ) {
       const float pre = R.dt + dtb;
       const float d = a.dt_softplus ? dt_softplus_clip(pre, a.dt_min, a.dt_max, a.sp_lo, a.sp_hi)
                                     : __builtin_amdgcn_fmed3f(pre, a.dt_min, a.dt_max);
@@ -270,13 +288,13 @@ __device__ __forceinline__ Scan2 scan_chunk(const float* dts, int lane, float Al
   return r;
 }
 
-// State update of the blocks (pb = (w >> 2) + 2 j, nb = w & 3) a wave owns:
+// State update of the blocks (pb = pb0 + PSTRIDE j < NS, nb) a wave owns:
 // S[j] <- dlast S[j] + sum_s x[s][p] (wS[s] B[s][n]).  The lane holds
 // S[p = 16 pb + 4 lg + r][n = 16 nb + li].
-template <int NS>
-__device__ __forceinline__ void state_update(f32x4 (&S)[Cfg<NS>::JS], float dlast, const uint16_t (*Bt)[kRowQ],
-                                             const uint16_t (*Xt)[kRowQ], const float* wS, int w, int li, int lg) {
-  const int nb = w & 3, pb0 = w >> 2;
+template <int NS, int NB, int PSTRIDE>
+__device__ __forceinline__ void state_update(f32x4 (&S)[NB], float dlast, const uint16_t (*Bt)[kRowQ],
+                                             const uint16_t (*Xt)[kRowQ], const float* wS, int nb, int pb0, int li,
+                                             int lg) {
   const int nrow = 16 * nb + li;
   bf16x8 bwh[4], bwl[4];
 #pragma unroll
@@ -297,8 +315,8 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[Cfg<NS>::JS], float dlas
     bwl[kk] = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
   }
 #pragma unroll
-  for (int j = 0; j < Cfg<NS>::JS; ++j) {
-    const int pb = pb0 + 2 * j;
+  for (int j = 0; j < NB; ++j) {
+    const int pb = pb0 + PSTRIDE * j;
     if (pb < NS) {
       const int prow = 16 * pb + li;
       f32x4 acc_hi = S[j] * dlast, acc_lo = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -329,14 +347,13 @@ __device__ __forceinline__ void decode_bid(const ChunkKernelArgs& a, int bid, in
 // of the chunk step, so the loop carries no row tests.
 template <typename OT, int NS, bool GATE>
 __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
-  using Cf = Cfg<NS>;
-  constexpr int P = Cf::P, NS0 = Cf::NS0, NS1 = Cf::NS1, JS = Cf::JS;
-  __shared__ HeadSmem<NS> sm;
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
-  const int lane = tid & 63;
-  const int li = lane & 15;
-  const int lg = lane >> 4;
+  constexpr int P = 16 * NS;
+  using Io = ChunkIo<NS, kIoThreads>;
+  constexpr int NB = kStateBuffers<NS>;
+  __shared__ HeadSmem<NS, NB> sm;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, held in a scalar register
+  const bool sw = w >= 4;    // state wave (n-block w - 4); else output wave (row blocks w, 7 - w)
+  const int u = w & 3;
 
   int b, h, seg;
   decode_bid(a, blockIdx.x, b, h, seg);
@@ -350,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
   // block then stay under 2^90).  Otherwise each element takes its own
   // exponential.
   const bool factored = a.dt_max * fabsf(Al2) < 6.0f;
-  const ChunkIo<NS> io(a, b, h);
+  const Io io(a, b, h);
 
   // chunks of this segment: [c_beg, c_end); whole ones below nfull
   const int nfull = L / kQ;
@@ -358,126 +375,179 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
   const int c_end = min(a.nchunks, c_beg + a.cps);
   const int c_whole = min(c_end, nfull);
 
-  // State blocks of this wave (see state_update)
-  f32x4 S[JS];
   const size_t bh = static_cast<size_t>(b) * H + h;
-  const float* s_in = seg == 0 ? a.state_in : a.ws + (bh * (a.nseg - 1) + (seg - 1)) * P * kN;
-  {
-    const int nb = w & 3, pb0 = w >> 2;
-#pragma unroll
-    for (int j = 0; j < JS; ++j) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = 16 * (pb0 + 2 * j) + 4 * lg + r;
-        S[j][r] = (s_in != nullptr && pb0 + 2 * j < NS)
-                      ? s_in[(seg == 0 ? bh * P * kN : 0) + static_cast<size_t>(p) * kN + 16 * nb + li]
-                      : 0.0f;
-      }
-    }
-  }
-  auto publish_state = [&](int li, int lg) {
-    const int nb = w & 3, pb0 = w >> 2;
-#pragma unroll
-    for (int j = 0; j < JS; ++j) {
-      if (pb0 + 2 * j < NS) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int p = 16 * (pb0 + 2 * j) + 4 * lg + r;
-          uint16_t hi, lo;
-          split_bf16(S[j][r], hi, lo);
-          sm.Shi[p][16 * nb + li] = hi;
-          sm.Slo[p][16 * nb + li] = lo;
-        }
-      }
-    }
-  };
-  publish_state(li, lg);
 
-  // Output items: 16-row blocks I0 = q and I1 = 7 - q, strips [sb, sb + ns)
-  const int q = w & 3, hw = w >> 2;
-  const int I0 = q, I1 = 7 - q;
-  const int sb = hw ? NS0 : 0;
-  const int ns = NS0 == NS1 ? NS0 : (hw ? NS1 : NS0);
-  // D: per head, added on the diagonal of M; per channel, after the sums
+  // Output waves: 16-row blocks I0 = w and I1 = 7 - w.  D per head is added
+  // on the diagonal of M; D per channel after the sums.
+  const int I0 = u, I1 = 7 - u;
   const bool dch = a.D != nullptr && a.d_per_channel;
   const float dhead = (a.D != nullptr && !a.d_per_channel) ? a.D[h] : 0.0f;
 
-  ChunkRegs<NS> R;
-  auto chunk_step = [&](const int c, auto ragged) {
+  // The two kinds of wave run loops of their own (same chunks, two barriers
+  // per chunk), so neither holds the other's registers.  Chunk c uses state
+  // and table buffer c % NB.  With two buffers the state waves write the
+  // next chunk's tables and incoming state while the output waves work on
+  // the current chunk; with one, between the chunk's last barrier and the
+  // staging of the next.
+  if (sw) {
+    // The state, held by the state waves: p-blocks 0..NS-1 of n-block u; the
+    // lane holds S[p = 16 j + 4 lg + r][n = 16 u + li].
+    f32x4 S[NS];
+    auto publish_state = [&](int buf, int li, int lg) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int p = 16 * j + 4 * lg + r;
+          uint16_t hi, lo;
+          split_bf16(S[j][r], hi, lo);
+          sm.Shi[buf][p][16 * u + li] = hi;
+          sm.Slo[buf][p][16 * u + li] = lo;
+        }
+      }
+    };
+    // dt of chunk c for state wave 0: lane holds rows 2 lane and 2 lane + 1
+    auto load_dt = [&](int c, int lane) {
+      const size_t tok = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
+      const int valid = min(kQ, L - c * kQ);
+      float2 r = make_float2(0.0f, 0.0f);
+      if (2 * lane < valid) r.x = a.dt[(tok + 2 * lane) * H + h];
+      if (2 * lane + 1 < valid) r.y = a.dt[(tok + 2 * lane + 1) * H + h];
+      return r;
+    };
+    // decay tables of chunk c (raw dt in dt2) into buffer buf, by state wave
+    // 0: the chunk's log2 decays scanned across its lanes
+    auto tables = [&](int c, int buf, float2 dt2, int lane) {
+      const int valid = min(kQ, L - c * kQ);
+      auto dt_of = [&](float raw, int row) {
+        const float pre = raw + dtb;
+        const float d = a.dt_softplus ? dt_softplus_clip(pre, a.dt_min, a.dt_max, a.sp_lo, a.sp_hi)
+                                      : __builtin_amdgcn_fmed3f(pre, a.dt_min, a.dt_max);
+        return row < valid ? d : 0.0f;  // rows past the end neither add nor decay
+      };
+      const float v0 = dt_of(dt2.x, 2 * lane), v1 = dt_of(dt2.y, 2 * lane + 1);
+      const float a0 = v0 * Al2, a1 = v1 * Al2;
+      const float incl = wave_prefix_sum(a0 + a1);
+      const float d0 = incl - a1, d1 = incl, last = lane_value(incl, 63);
+      DecayTables& t = sm.tb[buf];
+#pragma unroll
+      for (int J = 0; J < 8; ++J) {
+        const float ref = lane_value(d0, 8 * J);  // dA[16 J]
+        if (2 * lane >= 16 * J)
+          *reinterpret_cast<float2*>(&t.EL[J][2 * lane]) = make_float2(exp2_fast(d0 - ref), exp2_fast(d1 - ref));
+      }
+      const float r16 = __shfl(d0, 8 * (lane >> 3));  // dA at the start of this lane's 16-block
+      *reinterpret_cast<float2*>(&t.ESD[2 * lane]) = make_float2(exp2_fast(r16 - d0) * v0, exp2_fast(r16 - d1) * v1);
+      *reinterpret_cast<float2*>(&t.dA[2 * lane]) = make_float2(d0, d1);
+      *reinterpret_cast<float2*>(&t.dt[2 * lane]) = make_float2(v0, v1);
+      *reinterpret_cast<float2*>(&t.eA[2 * lane]) = make_float2(exp2_fast(d0), exp2_fast(d1));
+      *reinterpret_cast<float2*>(&t.wS[2 * lane]) =
+          make_float2(exp2_fast(last - d0) * v0, exp2_fast(last - d1) * v1);
+    };
+
+    typename Io::Regs R;
+    float2 dtn = make_float2(0.0f, 0.0f);  // raw dt of the next chunk (state wave 0)
+    auto load_chunk = [&](int c, int tid) {
+      if (c >= nfull)
+        io.template load<true, true, false>(c, R, tid - kIoThreads);
+      else
+        io.template load<false, true, false>(c, R, tid - kIoThreads);
+      if (u == 0) dtn = load_dt(c, tid & 63);
+    };
+    {
+      const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+      const float* s_in = seg == 0 ? (a.state_in ? a.state_in + bh * P * kN : nullptr)
+                                   : a.ws + (bh * (a.nseg - 1) + (seg - 1)) * P * kN;
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S[j][r] = s_in != nullptr ? s_in[static_cast<size_t>(16 * j + 4 * lg + r) * kN + 16 * u + li] : 0.0f;
+      if (c_beg < c_end) {
+        load_chunk(c_beg, threadIdx.x);
+        publish_state(c_beg % NB, li, lg);
+        if (u == 0) tables(c_beg, c_beg % NB, dtn, lane);
+      }
+    }
+    for (int c = c_beg; c < c_end; ++c) {
+      // Lane indexes re-derived from an opaque copy of the thread id: the LDS
+      // and global offsets built from them are then formed inside the loop
+      // instead of being hoisted out of it, which would hold some hundred
+      // registers across the whole loop.
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
+      const int buf = c % NB, nbuf = (c + 1) % NB;
+      // ---- stage the chunk (every reader of the previous chunk's tiles
+      // passed the last barrier)
+      io.template store<false, true, false>(R, sm.C, sm.B, sm.Bt, sm.Xt, nullptr, dtb, tid - kIoThreads);
+      __syncthreads();
+      // the next chunk's loads, in flight while the chunk is processed
+      if (c + 1 < c_end) load_chunk(c + 1, tid);
+      // ---- state update (registers); published for the next chunk once
+      // the output waves no longer read the buffer
+      state_update<NS, NS, 1>(S, sm.tb[buf].eA[kQ - 1], sm.Bt, sm.Xt, sm.tb[buf].wS, u, 0, li, lg);
+      if constexpr (NB == 2) {
+        publish_state(nbuf, li, lg);
+        if (u == 0 && c + 1 < c_end) tables(c + 1, nbuf, dtn, lane);
+        __syncthreads();
+      } else {
+        __syncthreads();
+        publish_state(nbuf, li, lg);
+        if (u == 0 && c + 1 < c_end) tables(c + 1, nbuf, dtn, lane);
+      }
+    }
+    if (a.state_out && seg == a.nseg - 1) {
+      const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          a.state_out[bh * P * kN + static_cast<size_t>(16 * j + 4 * lg + r) * kN + 16 * u + li] = S[j][r];
+    }
+    return;
+  }
+
+  auto out_step = [&](const int c, auto ragged) {
     constexpr bool kRag = decltype(ragged)::value;
-    // Lane indexes re-derived from an opaque copy of the thread id: the LDS
-    // and global offsets built from them are then formed inside the loop
-    // instead of being hoisted out of it, which would hold some hundred
-    // registers across the whole loop.
-    int tid = threadIdx.x;
+    int tid = threadIdx.x;  // opaque copy, as in the state waves' loop
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
-    // (every reader of the previous chunk's tiles passed the barrier before
-    // the state was published)
-    io.template store<kRag, true>(R, sm.C, sm.B, sm.Bt, sm.Xt, sm.dt, dtb, tid);
-    if (!kRag && c + 1 < c_whole) io.template load<false, true>(c + 1, R, tid);
-
-    // gate values of this wave's outputs (row l = 16 I + li, columns
-    // 16 st + 4 lg .. + 3), fetched now so their latency overlaps the sums
     const size_t tok0 = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
     const int valid = kRag ? L - c * kQ : kQ;
-    uint4 zr[2][NS0];
-    if constexpr (GATE) {
+    // gate values of item it (row l = 16 I + li, columns 16 st + 4 lg .. + 3),
+    // fetched before its sums so that their latency overlaps them
+    auto load_gate = [&](int it, uint4 (&zr)[NS]) {
+      const int l = 16 * (it ? I1 : I0) + li;
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int l = 16 * (it ? I1 : I0) + li;
-#pragma unroll
-        for (int t = 0; t < NS0; ++t) {
-          zr[it][t] = make_uint4(0u, 0u, 0u, 0u);
-          if (t < ns && (!kRag || l < valid)) {
-            const size_t e = ((tok0 + l) * H + h) * P + 16 * (sb + t) + 4 * lg;
-            if (a.z_bf16) {
-              const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.z) + e);
-              zr[it][t].x = v.x;
-              zr[it][t].y = v.y;
-            } else {
-              zr[it][t] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.z) + e);
-            }
+      for (int t = 0; t < NS; ++t) {
+        zr[t] = make_uint4(0u, 0u, 0u, 0u);
+        if (!kRag || l < valid) {
+          const size_t e = ((tok0 + l) * H + h) * P + 16 * t + 4 * lg;
+          if (a.z_bf16) {
+            const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.z) + e);
+            zr[t].x = v.x;
+            zr[t].y = v.y;
+          } else {
+            zr[t] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.z) + e);
           }
         }
       }
-    }
-    __syncthreads();
-
-    // Every wave scans the chunk's log2 decays in registers, then writes its
-    // share of the tables (wave w: EL[w]; waves 0 and 1 the per-step rows).
-    const Scan2 sc = scan_chunk(sm.dt, lane, Al2);
-    {
-      const int J = w;
-      const float ref = __shfl(sc.d0, 8 * J);  // dA[16 J]
-      if (2 * lane >= 16 * J) {
-        sm.EL[J][2 * lane] = exp2_fast(sc.d0 - ref);
-        sm.EL[J][2 * lane + 1] = exp2_fast(sc.d1 - ref);
-      }
-      if (w == 0) {
-        const float r16 = __shfl(sc.d0, 8 * (lane >> 3));  // dA at the start of this lane's 16-block
-        sm.ESD[2 * lane] = exp2_fast(r16 - sc.d0) * sc.v0;
-        sm.ESD[2 * lane + 1] = exp2_fast(r16 - sc.d1) * sc.v1;
-        sm.dA[2 * lane] = sc.d0;
-        sm.dA[2 * lane + 1] = sc.d1;
-      } else if (w == 1) {
-        sm.eA[2 * lane] = exp2_fast(sc.d0);
-        sm.eA[2 * lane + 1] = exp2_fast(sc.d1);
-        sm.wS[2 * lane] = exp2_fast(sc.last - sc.d0) * sc.v0;
-        sm.wS[2 * lane + 1] = exp2_fast(sc.last - sc.d1) * sc.v1;
-      }
-    }
-    __syncthreads();
-
-    // Intra-chunk sums of one item (16-row block I): blocks J = 0..I in a
-    // software pipeline -- in step J the C B^T product of block J + 1 is
-    // issued, the LDS operands of blocks J + 1 (decays, x^T) and J + 2 (B
-    // rows) are fetched, and block J's M is formed and multiplied -- with
-    // the diagonal block (masked, D on its diagonal) peeled off the loop.
+    };
+    __syncthreads();  // the chunk, its tables and its incoming state are in place
+    const DecayTables& tb = sm.tb[c % NB];
+    const uint16_t (*Shi)[kRowN] = sm.Shi[c % NB];
+    const uint16_t (*Slo)[kRowN] = sm.Slo[c % NB];
+    // ---- outputs.  Intra-chunk sums of one item (16-row block I): blocks
+    // J = 0..I in a software pipeline -- in step J the C B^T product of
+    // block J + 1 is issued, the LDS operands of blocks J + 1 (decays,
+    // x^T) and J + 2 (B rows) are fetched, and block J's M is formed and
+    // multiplied -- with the diagonal block (masked, D on its diagonal)
+    // peeled off the loop.
     struct Ops {
-      float el;           // factored: 2^(dA[l] - dA[16 J]); otherwise dA[l]
-      float4 e4;          // factored: 2^(dA[16 J] - dA[s]) dt[s]; otherwise dA[s]
-      s16x4 xv[NS0];      // x^T[p][s] fragments of the wave's strips
+      float el;         // factored: 2^(dA[l] - dA[16 J]); otherwise dA[l]
+      float4 e4;        // factored: 2^(dA[16 J] - dA[s]) dt[s]; otherwise dA[s]
+      s16x4 xv[NS];     // x^T[p][s] fragments of the strips
     };
     auto rows16 = [&](const uint16_t (*M)[kRowN], int blk, bf16x8 (&v)[2]) {
       v[0] = *reinterpret_cast<const bf16x8*>(&M[16 * blk + li][8 * lg]);
@@ -486,14 +556,12 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
     auto load_ops = [&](int I, int J, Ops& o, auto fac) {
       constexpr bool kFac = decltype(fac)::value;
       const int l_row = 16 * I + li, s0 = 16 * J + 4 * lg;
-      o.el = kFac ? sm.EL[J][l_row] : sm.dA[l_row];
-      o.e4 = *reinterpret_cast<const float4*>(kFac ? &sm.ESD[s0] : &sm.dA[s0]);
+      o.el = kFac ? tb.EL[J][l_row] : tb.dA[l_row];
+      o.e4 = *reinterpret_cast<const float4*>(kFac ? &tb.ESD[s0] : &tb.dA[s0]);
 #pragma unroll
-      for (int t = 0; t < NS0; ++t) {
-        if (t < ns) {
-          const int prow = 16 * (sb + t) + li;
-          o.xv[t] = *reinterpret_cast<const s16x4*>(&sm.Xt[prow][swz(prow, s0)]);
-        }
+      for (int t = 0; t < NS; ++t) {
+        const int prow = 16 * t + li;
+        o.xv[t] = *reinterpret_cast<const s16x4*>(&sm.Xt[prow][swz(prow, s0)]);
       }
     };
     auto cbT = [&](const bf16x8 (&bj)[2], const bf16x8 (&ci)[2]) {
@@ -504,7 +572,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
     };
     // block (I, J): lane holds cb[l = 16 I + li][s = 16 J + 4 lg + r], which
     // is the B operand M^T[s][l] of the x^T M^T product as it stands
-    auto block = [&](int J, const f32x4& cb, const Ops& o, f32x4 (&acc)[NS0], auto fac, auto diag) {
+    auto block = [&](int J, const f32x4& cb, const Ops& o, f32x4 (&acc)[NS], auto fac, auto diag) {
       constexpr bool kFac = decltype(fac)::value;
       constexpr bool kDiag = decltype(diag)::value;
       const float ev[4] = {o.e4.x, o.e4.y, o.e4.z, o.e4.w};
@@ -513,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) m[r] = cb[r] * o.el * ev[r];
       } else {
-        const float4 d4 = *reinterpret_cast<const float4*>(&sm.dt[16 * J + 4 * lg]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&tb.dt[16 * J + 4 * lg]);
         const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) m[r] = cb[r] * exp2_fast(o.el - ev[r]) * dv4[r];
@@ -533,97 +601,97 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
       const s16x4 mhi = __builtin_bit_cast(s16x4, make_uint2(h01, h23));
       const s16x4 mlo = __builtin_bit_cast(s16x4, make_uint2(l01, l23));
 #pragma unroll
-      for (int t = 0; t < NS0; ++t) {
-        if (t < ns) {
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(o.xv[t], mhi, acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(o.xv[t], mlo, acc[t], 0, 0, 0);
-        }
+      for (int t = 0; t < NS; ++t) {
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(o.xv[t], mhi, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(o.xv[t], mlo, acc[t], 0, 0, 0);
       }
     };
-    auto item = [&](const int I, const bf16x8 (&ci)[2], f32x4 (&acc)[NS0], auto fac) {
+    auto item = [&](const int I, const bf16x8 (&ci)[2], f32x4 (&acc)[NS], auto fac) {
       bf16x8 b0[2], b1[2];
       Ops cur, nxt;
       rows16(sm.B, 0, b0);
       rows16(sm.B, I > 0 ? 1 : 0, b1);
       load_ops(I, 0, cur, fac);
       f32x4 cb = cbT(b0, ci);
-      for (int J = 0; J < I; ++J) {
-        const f32x4 cbn = cbT(b1, ci);   // block J + 1
+      // one off-diagonal step: block J from (cb, o), block J + 1's operands into o2
+      auto step = [&](int J, const Ops& o, Ops& o2) {
+        const f32x4 cbn = cbT(b1, ci);    // block J + 1
         rows16(sm.B, min(J + 2, 7), b1);  // block J + 2 (loaded, not used, past the diagonal)
-        load_ops(I, J + 1, nxt, fac);
-        block(J, cb, cur, acc, fac, std::false_type{});
+        load_ops(I, J + 1, o2, fac);
+        block(J, cb, o, acc, fac, std::false_type{});
         cb = cbn;
-        cur = nxt;
+      };
+      // two steps per trip so that the operand sets swap roles instead of
+      // being copied
+      int J = 0;
+      for (; J + 2 <= I; J += 2) {
+        step(J, cur, nxt);
+        step(J + 1, nxt, cur);
       }
-      block(I, cb, cur, acc, fac, std::true_type{});
+      if (J < I) {
+        step(J, cur, nxt);
+        block(I, cb, nxt, acc, fac, std::true_type{});
+      } else {
+        block(I, cb, cur, acc, fac, std::true_type{});
+      }
     };
-    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Readout of the incoming state, (S C_I^T)[p][l] scaled by 2^dA[l], added
-    // to the sums; then the per-channel skip, the gate and the store.  The
-    // lane holds rows p = 16 st + 4 lg + r of column l = 16 I + li.
-    auto finish = [&](const int it, const bf16x8 (&ci)[2], f32x4 (&acc)[NS0]) {
+    // Readout of the incoming state, (S C_I^T)[p][l] scaled by 2^dA[l],
+    // added to the sums; then the per-channel skip, the gate and the
+    // store.  The lane holds rows p = 16 st + 4 lg + r of column
+    // l = 16 I + li.
+    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto finish = [&](const int it, const bf16x8 (&ci)[2], f32x4 (&acc)[NS], const uint4 (&zr)[NS], auto per_ch) {
+      constexpr bool kDch = decltype(per_ch)::value;
       const int I = it ? I1 : I0;
       const int l = 16 * I + li;
-      const float eAl = sm.eA[l];
+      const float eAl = tb.eA[l];
       const bool orow = !kRag || l < valid;
-      bf16x8 sh[NS0][2], sl[NS0][2];
 #pragma unroll
-      for (int t = 0; t < NS0; ++t) {
-        if (t < ns) {
+      for (int st = 0; st < NS; ++st) {
+        f32x4 sr_hi = zero4, sr_lo = zero4;
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            sh[t][kk] = *reinterpret_cast<const bf16x8*>(&sm.Shi[16 * (sb + t) + li][32 * kk + 8 * lg]);
-            sl[t][kk] = *reinterpret_cast<const bf16x8*>(&sm.Slo[16 * (sb + t) + li][32 * kk + 8 * lg]);
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 sh = *reinterpret_cast<const bf16x8*>(&Shi[16 * st + li][32 * kk + 8 * lg]);
+          const bf16x8 sl = *reinterpret_cast<const bf16x8*>(&Slo[16 * st + li][32 * kk + 8 * lg]);
+          sr_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sh, ci[kk], sr_hi, 0, 0, 0);
+          sr_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl, ci[kk], sr_lo, 0, 0, 0);
+        }
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = fmaf(eAl, sr_hi[r] + sr_lo[r], acc[st][r]);
+        if constexpr (kDch) {
+          const float4 d4 = *reinterpret_cast<const float4*>(a.D + static_cast<size_t>(h) * P + 16 * st + 4 * lg);
+          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int p = 16 * st + 4 * lg + r;
+            v[r] = fmaf(dv[r], bf16_val(sm.Xt[p][swz(p, l)]), v[r]);
           }
         }
-      }
-#pragma unroll
-      for (int t = 0; t < NS0; ++t) {
-        if (t < ns) {
-          const int st = sb + t;
-          f32x4 sr_hi = zero4, sr_lo = zero4;
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            sr_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sh[t][kk], ci[kk], sr_hi, 0, 0, 0);
-            sr_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl[t][kk], ci[kk], sr_lo, 0, 0, 0);
+        if constexpr (GATE) {
+          float zv[4];
+          if (a.z_bf16) {
+            zv[0] = __uint_as_float(zr[st].x << 16);
+            zv[1] = __uint_as_float(zr[st].x & 0xffff0000u);
+            zv[2] = __uint_as_float(zr[st].y << 16);
+            zv[3] = __uint_as_float(zr[st].y & 0xffff0000u);
+          } else {
+            zv[0] = __uint_as_float(zr[st].x);
+            zv[1] = __uint_as_float(zr[st].y);
+            zv[2] = __uint_as_float(zr[st].z);
+            zv[3] = __uint_as_float(zr[st].w);
           }
-          float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = fmaf(eAl, sr_hi[r] + sr_lo[r], acc[t][r]);
-          if (dch) {
-            const float4 d4 = *reinterpret_cast<const float4*>(a.D + static_cast<size_t>(h) * P + 16 * st + 4 * lg);
-            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int p = 16 * st + 4 * lg + r;
-              v[r] = fmaf(dv[r], bf16_val(sm.Xt[p][swz(p, l)]), v[r]);
-            }
-          }
-          if constexpr (GATE) {
-            float zv[4];
-            if (a.z_bf16) {
-              zv[0] = __uint_as_float(zr[it][t].x << 16);
-              zv[1] = __uint_as_float(zr[it][t].x & 0xffff0000u);
-              zv[2] = __uint_as_float(zr[it][t].y << 16);
-              zv[3] = __uint_as_float(zr[it][t].y & 0xffff0000u);
-            } else {
-              zv[0] = __uint_as_float(zr[it][t].x);
-              zv[1] = __uint_as_float(zr[it][t].y);
-              zv[2] = __uint_as_float(zr[it][t].z);
-              zv[3] = __uint_as_float(zr[it][t].w);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] *= silu(zv[r]);
-          }
-          if (orow) {
-            const size_t e = ((tok0 + l) * H + h) * P + 16 * st + 4 * lg;
-            if constexpr (sizeof(OT) == 4) {
-              *reinterpret_cast<float4*>(static_cast<float*>(a.out) + e) = make_float4(v[0], v[1], v[2], v[3]);
-            } else {
-              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + e) =
-                  make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
-            }
+          for (int r = 0; r < 4; ++r) v[r] *= silu(zv[r]);
+        }
+        if (orow) {
+          const size_t e = ((tok0 + l) * H + h) * P + 16 * st + 4 * lg;
+          if constexpr (sizeof(OT) == 4) {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + e) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + e) =
+                make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
           }
         }
       }
@@ -632,45 +700,26 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int I = it ? I1 : I0;
-      f32x4 acc[NS0];
+      f32x4 acc[NS];
 #pragma unroll
-      for (int t = 0; t < NS0; ++t) acc[t] = zero4;
+      for (int t = 0; t < NS; ++t) acc[t] = zero4;
+      uint4 zr[NS];
+      if constexpr (GATE) load_gate(it, zr);
       bf16x8 ci[2];
       rows16(sm.C, I, ci);
       if (factored)
         item(I, ci, acc, std::true_type{});
       else
         item(I, ci, acc, std::false_type{});
-      finish(it, ci, acc);
+      if (dch)
+        finish(it, ci, acc, zr, std::true_type{});
+      else
+        finish(it, ci, acc, zr, std::false_type{});
     }
-
-    // ---- state update (registers), published once every wave has read
-    // the incoming state
-    state_update<NS>(S, exp2_fast(sc.last), sm.Bt, sm.Xt, sm.wS, w, li, lg);
-    __syncthreads();
-    publish_state(li, lg);
+    __syncthreads();  // the chunk's tiles, tables and state have been read
   };
-
-  if (c_beg < c_whole) io.template load<false, true>(c_beg, R, tid);
-  for (int c = c_beg; c < c_whole; ++c) chunk_step(c, std::false_type{});
-  if (c_end > nfull && c_beg <= nfull) {
-    io.template load<true, true>(nfull, R, tid);
-    chunk_step(nfull, std::true_type{});
-  }
-
-  if (a.state_out && seg == a.nseg - 1) {
-    const int nb = w & 3, pb0 = w >> 2;
-#pragma unroll
-    for (int j = 0; j < JS; ++j) {
-      if (pb0 + 2 * j < NS) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int p = 16 * (pb0 + 2 * j) + 4 * lg + r;
-          a.state_out[bh * P * kN + static_cast<size_t>(p) * kN + 16 * nb + li] = S[j][r];
-        }
-      }
-    }
-  }
+  for (int c = c_beg; c < c_whole; ++c) out_step(c, std::false_type{});
+  if (c_end > nfull && c_beg <= nfull) out_step(nfull, std::true_type{});
 }
 
 // ---- segment pieces: state reached from zero and total log2 decay --------
@@ -679,8 +728,8 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
 // whole (the ragged chunk, if any, is the last chunk of the last segment).
 template <int NS>
 __global__ __launch_bounds__(kThreads) void ssd_summary_kernel(ChunkKernelArgs a) {
-  using Cf = Cfg<NS>;
-  constexpr int P = Cf::P, JS = Cf::JS;
+  constexpr int P = 16 * NS, JS = (NS + 1) / 2;  // state blocks per wave: p-blocks (w >> 2) + 2 j, n-block w & 3
+  using Io = ChunkIo<NS, kThreads>;
   __shared__ SummSmem<NS> sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
@@ -699,14 +748,14 @@ __global__ __launch_bounds__(kThreads) void ssd_summary_kernel(ChunkKernelArgs a
   const int c_end = min(c_beg + kPiece, (seg + 1) * a.cps);
   const float Al2 = a.A[h] * kLog2e;
   const float dtb = a.dt_bias ? a.dt_bias[h] : 0.0f;
-  const ChunkIo<NS> io(a, b, h);
+  const Io io(a, b, h);
 
   f32x4 S[JS];
 #pragma unroll
   for (int t = 0; t < JS; ++t) S[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float dec = 0.0f;
 
-  ChunkRegs<NS> R;
+  typename Io::Regs R;
   if (c_beg < c_end) io.template load<false, false>(c_beg, R, tid);
   for (int c = c_beg; c < c_end; ++c) {
     int tid = threadIdx.x;  // opaque copy: offsets formed inside the loop (see ssd_kernel)
@@ -723,7 +772,7 @@ __global__ __launch_bounds__(kThreads) void ssd_summary_kernel(ChunkKernelArgs a
     }
     dec += sc.last;
     __syncthreads();
-    state_update<NS>(S, exp2_fast(sc.last), sm.Bt, sm.Xt, sm.wS, w, li, lg);
+    state_update<NS, JS, 2>(S, exp2_fast(sc.last), sm.Bt, sm.Xt, sm.wS, w & 3, w >> 2, li, lg);
   }
 
   const size_t bh = static_cast<size_t>(b) * a.nheads + h;
