@@ -18,6 +18,10 @@
 //      per-wave partials, gradients summed over time (A, D, dt_w, dt_bias) as
 //      per-segment partials, and the conv input gradient as dL/dxc;
 //   4. the conv's transpose and the reductions, all in a fixed order.
+// A wave first stages its segment's inputs in LDS (x with the conv's three
+// earlier steps, dt's pre-activation, dy, z for its 16 channels; B and C of
+// the segment), with coalesced loads issued together, so the steps read LDS
+// instead of waiting on a dozen dependent global loads each.
 // Reverse recurrence (G_t = dL/dh_t, Q_t = a_t G_t, a_t = exp(dt_t A)):
 //   G_t = dyc_t C_t + Q_{t+1},  dyc_t = dy_t SiLU(z_t),  Q at the end = dL/dh_L.
 // Lanes: 4 per (batch, channel), each holding 4 of the 16 states, so a
@@ -80,6 +84,65 @@ __device__ __forceinline__ float dsilu(float x) {
   return s * (1.0f + x * (1.0f - s));
 }
 
+// One segment's inputs for the 16 channels of a wave.  Rows past the end of
+// the sequence are not written and not read.
+struct SegStage {
+  float xr[kSeg + 3][16];  // raw x at t0 - 3 + i (the conv cache or zeros before the start)
+  float pre[kSeg][16];     // dt pre-activation (bias included)
+  float dy[kSeg][16];
+  float z[kSeg][16];
+  float B[kSeg][kScanN];
+  float C[kSeg][kScanN];
+};
+
+// Stage segment [t0, t1) of batch b for channel group gw: lane (r, j) loads
+// channel j of rows r, r + 4, ...; B and C rows are contiguous (4 values a
+// lane).
+__device__ __forceinline__ void stage_segment(const BwdArgs& a, int b, int gw, int t0, int t1, SegStage& S) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, r = lane >> 4;
+  const int e = min(16 * gw + j, a.dim - 1);
+  const size_t row0 = static_cast<size_t>(b) * a.seqlen;
+  const float dtw = a.dt_rank1 ? a.dt_w[e] : 0.0f;
+  const float dtb = a.dt_bias ? a.dt_bias[e] : 0.0f;
+#pragma unroll
+  for (int i0 = 0; i0 < kSeg + 3; i0 += 4) {
+    const int i = i0 + r;
+    const int t = t0 - 3 + i;
+    if (i < kSeg + 3 && t < t1) {
+      float v = 0.0f;
+      if (t >= 0)
+        v = ldx(a.x, (row0 + t) * a.dim + e, a.x_bf16);
+      else if (a.conv_cache_in)
+        v = a.conv_cache_in[(static_cast<size_t>(b) * a.dim + e) * 3 + (3 + t)];
+      S.xr[i][j] = v;
+    }
+  }
+#pragma unroll
+  for (int i0 = 0; i0 < kSeg; i0 += 4) {
+    const int i = i0 + r;
+    const int t = t0 + i;
+    if (t < t1) {
+      const size_t be = (row0 + t) * a.dim + e;
+      S.pre[i][j] = a.dt_rank1 ? fmaf(dtw, static_cast<const float*>(a.dt)[row0 + t], dtb) : ldx(a.dt, be, a.dt_bf16) + dtb;
+      S.dy[i][j] = ldx(a.dy, be, a.dy_bf16);
+      S.z[i][j] = a.z ? ldx(a.z, be, a.x_bf16) : 0.0f;
+    }
+  }
+  if (t0 + (lane >> 2) < t1) {
+    float v[4];
+    const size_t o = (row0 + t0) * kScanN + 4 * lane;
+    load4v(a.B, o, a.bc_bf16, v);
+    *reinterpret_cast<float4*>(&S.B[lane >> 2][4 * (lane & 3)]) = make_float4(v[0], v[1], v[2], v[3]);
+    load4v(a.C, o, a.bc_bf16, v);
+    *reinterpret_cast<float4*>(&S.C[lane >> 2][4 * (lane & 3)]) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  // the wave's own LDS writes complete before its reads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Per-lane context: which (batch, channel, state quarter) and its constants.
 struct Lane {
   const BwdArgs& a;
@@ -114,24 +177,32 @@ struct Lane {
     d = a.D ? a.D[e] : 0.0f;
   }
   __device__ size_t be(int t) const { return (static_cast<size_t>(b) * a.seqlen + t) * a.dim + e; }
-  // raw x at time t (t < 0: the conv cache, oldest first, or zeros)
-  __device__ float raw(int t) const {
-    if (t >= 0) return ldx(a.x, be(t), a.x_bf16);
-    if (a.conv_cache_in) return a.conv_cache_in[(static_cast<size_t>(b) * a.dim + e) * 3 + (3 + t)];
-    return 0.0f;
-  }
-  // u_t and the conv output xc_t
-  __device__ float u_at(int t, float& xc) const {
+  // staged values of step i of the segment (channel slot j = lane / 4)
+  __device__ float su_at(const SegStage& S, int i, float& xc) const {
+    const int j = (threadIdx.x & 63) >> 2;
     if (!a.conv_w) {
       xc = 0.0f;
-      return ldx(a.x, be(t), a.x_bf16);
+      return S.xr[i + 3][j];
     }
-    xc = fmaf(cw[0], raw(t - 3), fmaf(cw[1], raw(t - 2), fmaf(cw[2], raw(t - 1), fmaf(cw[3], raw(t), cb))));
+    xc = fmaf(cw[0], S.xr[i][j], fmaf(cw[1], S.xr[i + 1][j], fmaf(cw[2], S.xr[i + 2][j], fmaf(cw[3], S.xr[i + 3][j], cb))));
     return silu(xc);
   }
-  __device__ float pre_at(int t) const {
-    if (a.dt_rank1) return fmaf(dtw, static_cast<const float*>(a.dt)[static_cast<size_t>(b) * a.seqlen + t], dtb);
-    return ldx(a.dt, be(t), a.dt_bf16) + dtb;
+  __device__ float spre(const SegStage& S, int i) const { return S.pre[i][(threadIdx.x & 63) >> 2]; }
+  __device__ void sbc(const float (*M)[kScanN], int i, float (&v)[4]) const {
+    const float4 f = *reinterpret_cast<const float4*>(&M[i][4 * q]);
+    v[0] = f.x;
+    v[1] = f.y;
+    v[2] = f.z;
+    v[3] = f.w;
+  }
+  __device__ float sdy(const SegStage& S, int i) const { return S.dy[i][(threadIdx.x & 63) >> 2]; }
+  __device__ float sgate(const SegStage& S, int i, float& zv) const {
+    if (!a.z) {
+      zv = 0.0f;
+      return 1.0f;
+    }
+    zv = S.z[i][(threadIdx.x & 63) >> 2];
+    return silu(zv);
   }
   // dt = clip(softplus(pre)); inside: strictly between the bounds; dsp: the
   // derivative of softplus (or 1)
@@ -147,20 +218,9 @@ struct Lane {
     inside = sp > a.dt_min && sp < a.dt_max;
     return fminf(fmaxf(sp, a.dt_min), a.dt_max);
   }
-  __device__ void bc(int t, const void* p, float (&v)[4]) const {
-    load4v(p, (static_cast<size_t>(b) * a.seqlen + t) * kScanN + 4 * q, a.bc_bf16, v);
-  }
   __device__ void decay(float dt, float (&av)[4]) const {
 #pragma unroll
     for (int j = 0; j < 4; ++j) av[j] = exp2_fast(dt * Al2[j]);
-  }
-  __device__ float gate(int t, float& zv) const {
-    if (!a.z) {
-      zv = 0.0f;
-      return 1.0f;
-    }
-    zv = ldx(a.z, be(t), a.x_bf16);
-    return silu(zv);
   }
 };
 
@@ -174,19 +234,23 @@ __device__ __forceinline__ void wave_ids(const BwdArgs& a, int& b, int& gw, int&
 }
 
 __global__ __launch_bounds__(256) void bwd_summary(BwdArgs a) {
+  __shared__ SegStage stage[4];
   int b, gw, s;
   wave_ids(a, b, gw, s);
   if (s >= a.nseg) return;
   const Lane c(a, b, gw);
   const int t0 = s * kSeg, t1 = min(a.seqlen, t0 + kSeg);
+  SegStage& S = stage[threadIdx.x >> 6];
+  stage_segment(a, b, gw, t0, t1, S);
   float h[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sdt = 0.0f;
   for (int t = t0; t < t1; ++t) {
+    const int i = t - t0;
     float xc, bv[4], av[4];
-    const float u = c.u_at(t, xc);
+    const float u = c.su_at(S, i, xc);
     bool inside;
     float dsp;
-    const float dt = c.dt_of(c.pre_at(t), inside, dsp);
-    c.bc(t, a.B, bv);
+    const float dt = c.dt_of(c.spre(S, i), inside, dsp);
+    c.sbc(S.B, i, bv);
     c.decay(dt, av);
 #pragma unroll
     for (int j = 0; j < 4; ++j) h[j] = fmaf(av[j], h[j], dt * u * bv[j]);
@@ -194,13 +258,14 @@ __global__ __launch_bounds__(256) void bwd_summary(BwdArgs a) {
   }
   float Q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int t = t1 - 1; t >= t0; --t) {
+    const int i = t - t0;
     float cv[4], av[4], zv;
     bool inside;
     float dsp;
-    const float dt = c.dt_of(c.pre_at(t), inside, dsp);
-    c.bc(t, a.C, cv);
+    const float dt = c.dt_of(c.spre(S, i), inside, dsp);
+    c.sbc(S.C, i, cv);
     c.decay(dt, av);
-    const float dyc = ldx(a.dy, c.be(t), a.dy_bf16) * c.gate(t, zv);
+    const float dyc = c.sdy(S, i) * c.sgate(S, i, zv);
 #pragma unroll
     for (int j = 0; j < 4; ++j) Q[j] = av[j] * fmaf(dyc, cv[j], Q[j]);
   }
@@ -238,11 +303,14 @@ __global__ __launch_bounds__(256) void bwd_compose(BwdArgs a) {
 }
 
 __global__ __launch_bounds__(256) void bwd_main(BwdArgs a) {
+  __shared__ SegStage stage[4];
   int b, gw, s;
   wave_ids(a, b, gw, s);
   if (s >= a.nseg) return;
   const Lane c(a, b, gw);
   const int t0 = s * kSeg, t1 = min(a.seqlen, t0 + kSeg);
+  SegStage& S = stage[threadIdx.x >> 6];
+  stage_segment(a, b, gw, t0, t1, S);
   const size_t so = ((static_cast<size_t>(b) * a.nseg + s) * a.dim + c.e) * kScanN + 4 * c.q;
   float hin[4], Q[4];
   {
@@ -258,13 +326,12 @@ __global__ __launch_bounds__(256) void bwd_main(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < kSeg; ++i) {
       if (t0 + i < t1) {
-        const int t = t0 + i;
         float xc, bv[4], av[4];
-        const float u = c.u_at(t, xc);
+        const float u = c.su_at(S, i, xc);
         bool inside;
         float dsp;
-        const float dt = c.dt_of(c.pre_at(t), inside, dsp);
-        c.bc(t, a.B, bv);
+        const float dt = c.dt_of(c.spre(S, i), inside, dsp);
+        c.sbc(S.B, i, bv);
         c.decay(dt, av);
 #pragma unroll
         for (int j = 0; j < 4; ++j) h[j] = fmaf(av[j], h[j], dt * u * bv[j]);
@@ -283,16 +350,16 @@ __global__ __launch_bounds__(256) void bwd_main(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) hprev[j] = i > 0 ? hist[i - 1][j] : hin[j];
     float xc, bv[4], cv[4], av[4], zv;
-    const float u = c.u_at(t, xc);
+    const float u = c.su_at(S, i, xc);
     bool inside;
     float dsp;
-    const float pre = c.pre_at(t);
+    const float pre = c.spre(S, i);
     const float dt = c.dt_of(pre, inside, dsp);
-    c.bc(t, a.B, bv);
-    c.bc(t, a.C, cv);
+    c.sbc(S.B, i, bv);
+    c.sbc(S.C, i, cv);
     c.decay(dt, av);
-    const float dy = ldx(a.dy, c.be(t), a.dy_bf16);
-    const float g = c.gate(t, zv);
+    const float dy = c.sdy(S, i);
+    const float g = c.sgate(S, i, zv);
     const float dyc = dy * g;
     float G[4];
 #pragma unroll
