@@ -59,45 +59,62 @@ __device__ __forceinline__ void load4v(const void* p, size_t i, bool bf, float (
   }
 }
 
-__device__ __forceinline__ float quad_sum(float v) {
-  v += __shfl_xor(v, 1, 4);
-  v += __shfl_xor(v, 2, 4);
-  return v;
-}
-
-// sum over the 16 channels of the wave (lanes with the same state quarter):
-// the 4 channels of a 16-lane row by DPP row rotations, then across rows
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float chan_sum(float v) {
-  v += dpp<0x124>(v);  // row_ror:4
-  v += dpp<0x128>(v);  // row_ror:8
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
-}
-
 __device__ __forceinline__ float dsilu(float x) {
   const float s = rcp_fast(1.0f + exp2_fast(-x * kLog2e));
   return s * (1.0f + x * (1.0f - s));
 }
 
-// One segment's inputs for the 16 channels of a wave.  Rows past the end of
-// the sequence are not written and not read.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// sum over the 4 lanes of a channel (DPP quad permutations 1 0 3 2, 2 3 0 1)
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  return v;
+}
+
+// v of the same lane in the other 16-lane row of its pair (rows 0 <-> 1,
+// 2 <-> 3) and in the other 32-lane half, by the permlane swaps, each added
+// to v
+__device__ __forceinline__ float add_row_swap(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+  return __builtin_bit_cast(float, static_cast<int>(p[0])) + __builtin_bit_cast(float, static_cast<int>(p[1]));
+}
+__device__ __forceinline__ float add_half_swap(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), false, false);
+  return __builtin_bit_cast(float, static_cast<int>(p[0])) + __builtin_bit_cast(float, static_cast<int>(p[1]));
+}
+
+// sum over the 16 channels of the wave (lanes with the same state quarter):
+// the 4 channels of a 16-lane row by DPP row rotations, then across rows
+__device__ __forceinline__ float chan_sum(float v) {
+  v += dpp<0x124>(v);  // row_ror:4
+  v += dpp<0x128>(v);  // row_ror:8
+  return add_half_swap(add_row_swap(v));
+}
+
+
+// One segment's inputs for the 16 channels of a wave, with the per-channel
+// quantities of each step computed once (not by each of a channel's four
+// lanes).  Rows past the end of the sequence are not read.
 struct SegStage {
   float xr[kSeg + 3][16];  // raw x at t0 - 3 + i (the conv cache or zeros before the start)
-  float pre[kSeg][16];     // dt pre-activation (bias included)
-  float dy[kSeg][16];
-  float z[kSeg][16];
+  float u[kSeg][16];       // u_t = SiLU(conv) (or x)
+  float dt[kSeg][16];      // dt_t
+  float dpf[kSeg][16];     // d dt / d pre: softplus' strictly inside the clip, else 0
+  float dyc[kSeg][16];     // dy_t SiLU(z_t) (or dy_t)
+  float dzf[kSeg][16];     // dy_t SiLU'(z_t)
+  float dsx[kSeg][16];     // SiLU'(conv output) (or 1)
   float B[kSeg][kScanN];
   float C[kSeg][kScanN];
 };
 
 // Stage segment [t0, t1) of batch b for channel group gw: lane (r, j) loads
-// channel j of rows r, r + 4, ...; B and C rows are contiguous (4 values a
-// lane).
+// channel j of rows r, r + 4, ... and computes those rows' per-channel
+// quantities; B and C rows are contiguous (4 values a lane).
 __device__ __forceinline__ void stage_segment(const BwdArgs& a, int b, int gw, int t0, int t1, SegStage& S) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, r = lane >> 4;
@@ -118,15 +135,16 @@ __device__ __forceinline__ void stage_segment(const BwdArgs& a, int b, int gw, i
       S.xr[i][j] = v;
     }
   }
+  float pre[kSeg / 4], dy[kSeg / 4], z[kSeg / 4];
 #pragma unroll
-  for (int i0 = 0; i0 < kSeg; i0 += 4) {
-    const int i = i0 + r;
-    const int t = t0 + i;
+  for (int k = 0; k < kSeg / 4; ++k) {
+    const int t = t0 + r + 4 * k;
+    pre[k] = dy[k] = z[k] = 0.0f;
     if (t < t1) {
       const size_t be = (row0 + t) * a.dim + e;
-      S.pre[i][j] = a.dt_rank1 ? fmaf(dtw, static_cast<const float*>(a.dt)[row0 + t], dtb) : ldx(a.dt, be, a.dt_bf16) + dtb;
-      S.dy[i][j] = ldx(a.dy, be, a.dy_bf16);
-      S.z[i][j] = a.z ? ldx(a.z, be, a.x_bf16) : 0.0f;
+      pre[k] = a.dt_rank1 ? fmaf(dtw, static_cast<const float*>(a.dt)[row0 + t], dtb) : ldx(a.dt, be, a.dt_bf16) + dtb;
+      dy[k] = ldx(a.dy, be, a.dy_bf16);
+      if (a.z) z[k] = ldx(a.z, be, a.x_bf16);
     }
   }
   if (t0 + (lane >> 2) < t1) {
@@ -141,6 +159,53 @@ __device__ __forceinline__ void stage_segment(const BwdArgs& a, int b, int gw, i
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __builtin_amdgcn_wave_barrier();
+  float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cb = 0.0f;
+  if (a.conv_w) {
+    const float4 w = reinterpret_cast<const float4*>(a.conv_w)[e];
+    cw[0] = w.x;
+    cw[1] = w.y;
+    cw[2] = w.z;
+    cw[3] = w.w;
+    cb = a.conv_b ? a.conv_b[e] : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < kSeg / 4; ++k) {
+    const int i = r + 4 * k;
+    if (t0 + i < t1) {
+      float u, dsx = 1.0f;
+      if (a.conv_w) {
+        const float xc = fmaf(cw[0], S.xr[i][j], fmaf(cw[1], S.xr[i + 1][j], fmaf(cw[2], S.xr[i + 2][j],
+                                                                                 fmaf(cw[3], S.xr[i + 3][j], cb))));
+        u = silu(xc);
+        dsx = dsilu(xc);
+      } else {
+        u = S.xr[i + 3][j];
+      }
+      float sp, dsp;
+      if (a.dt_softplus) {
+        sp = softplus(pre[k]);
+        dsp = rcp_fast(1.0f + exp2_fast(-pre[k] * kLog2e));
+      } else {
+        sp = pre[k];
+        dsp = 1.0f;
+      }
+      const bool inside = sp > a.dt_min && sp < a.dt_max;
+      S.u[i][j] = u;
+      S.dt[i][j] = fminf(fmaxf(sp, a.dt_min), a.dt_max);
+      S.dpf[i][j] = inside ? dsp : 0.0f;
+      S.dsx[i][j] = dsx;
+      if (a.z) {
+        S.dyc[i][j] = dy[k] * silu(z[k]);
+        S.dzf[i][j] = dy[k] * dsilu(z[k]);
+      } else {
+        S.dyc[i][j] = dy[k];
+        S.dzf[i][j] = 0.0f;
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
 }
 
 // Per-lane context: which (batch, channel, state quarter) and its constants.
@@ -149,7 +214,7 @@ struct Lane {
   int b, e, q, gw;
   bool act;
   float Al2[4], An[4];  // A[e][4q + j] log2(e), A[e][4q + j]
-  float cw[4], cb, dtw, dtb, d;
+  float dtw, d;
 
   __device__ Lane(const BwdArgs& args, int b_, int gw_) : a(args), b(b_), gw(gw_) {
     const int lane = threadIdx.x & 63;
@@ -162,61 +227,18 @@ struct Lane {
       An[j] = a.A[static_cast<size_t>(e) * kScanN + 4 * q + j];
       Al2[j] = An[j] * kLog2e;
     }
-    if (a.conv_w) {
-      const float4 w = reinterpret_cast<const float4*>(a.conv_w)[e];
-      cw[0] = w.x;
-      cw[1] = w.y;
-      cw[2] = w.z;
-      cw[3] = w.w;
-      cb = a.conv_b ? a.conv_b[e] : 0.0f;
-    } else {
-      cw[0] = cw[1] = cw[2] = cw[3] = cb = 0.0f;
-    }
     dtw = a.dt_rank1 ? a.dt_w[e] : 0.0f;
-    dtb = a.dt_bias ? a.dt_bias[e] : 0.0f;
     d = a.D ? a.D[e] : 0.0f;
   }
   __device__ size_t be(int t) const { return (static_cast<size_t>(b) * a.seqlen + t) * a.dim + e; }
-  // staged values of step i of the segment (channel slot j = lane / 4)
-  __device__ float su_at(const SegStage& S, int i, float& xc) const {
-    const int j = (threadIdx.x & 63) >> 2;
-    if (!a.conv_w) {
-      xc = 0.0f;
-      return S.xr[i + 3][j];
-    }
-    xc = fmaf(cw[0], S.xr[i][j], fmaf(cw[1], S.xr[i + 1][j], fmaf(cw[2], S.xr[i + 2][j], fmaf(cw[3], S.xr[i + 3][j], cb))));
-    return silu(xc);
-  }
-  __device__ float spre(const SegStage& S, int i) const { return S.pre[i][(threadIdx.x & 63) >> 2]; }
+  // staged value of step i of the segment for this lane's channel (slot lane / 4)
+  __device__ static float at(const float (*M)[16], int i) { return M[i][(threadIdx.x & 63) >> 2]; }
   __device__ void sbc(const float (*M)[kScanN], int i, float (&v)[4]) const {
     const float4 f = *reinterpret_cast<const float4*>(&M[i][4 * q]);
     v[0] = f.x;
     v[1] = f.y;
     v[2] = f.z;
     v[3] = f.w;
-  }
-  __device__ float sdy(const SegStage& S, int i) const { return S.dy[i][(threadIdx.x & 63) >> 2]; }
-  __device__ float sgate(const SegStage& S, int i, float& zv) const {
-    if (!a.z) {
-      zv = 0.0f;
-      return 1.0f;
-    }
-    zv = S.z[i][(threadIdx.x & 63) >> 2];
-    return silu(zv);
-  }
-  // dt = clip(softplus(pre)); inside: strictly between the bounds; dsp: the
-  // derivative of softplus (or 1)
-  __device__ float dt_of(float pre, bool& inside, float& dsp) const {
-    float sp;
-    if (a.dt_softplus) {
-      sp = softplus(pre);
-      dsp = rcp_fast(1.0f + exp2_fast(-pre * kLog2e));
-    } else {
-      sp = pre;
-      dsp = 1.0f;
-    }
-    inside = sp > a.dt_min && sp < a.dt_max;
-    return fminf(fmaxf(sp, a.dt_min), a.dt_max);
   }
   __device__ void decay(float dt, float (&av)[4]) const {
 #pragma unroll
@@ -245,11 +267,9 @@ __global__ __launch_bounds__(256) void bwd_summary(BwdArgs a) {
   float h[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sdt = 0.0f;
   for (int t = t0; t < t1; ++t) {
     const int i = t - t0;
-    float xc, bv[4], av[4];
-    const float u = c.su_at(S, i, xc);
-    bool inside;
-    float dsp;
-    const float dt = c.dt_of(c.spre(S, i), inside, dsp);
+    float bv[4], av[4];
+    const float u = Lane::at(S.u, i);
+    const float dt = Lane::at(S.dt, i);
     c.sbc(S.B, i, bv);
     c.decay(dt, av);
 #pragma unroll
@@ -259,13 +279,11 @@ __global__ __launch_bounds__(256) void bwd_summary(BwdArgs a) {
   float Q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int t = t1 - 1; t >= t0; --t) {
     const int i = t - t0;
-    float cv[4], av[4], zv;
-    bool inside;
-    float dsp;
-    const float dt = c.dt_of(c.spre(S, i), inside, dsp);
+    float cv[4], av[4];
+    const float dt = Lane::at(S.dt, i);
     c.sbc(S.C, i, cv);
     c.decay(dt, av);
-    const float dyc = c.sdy(S, i) * c.sgate(S, i, zv);
+    const float dyc = Lane::at(S.dyc, i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) Q[j] = av[j] * fmaf(dyc, cv[j], Q[j]);
   }
@@ -287,17 +305,41 @@ __global__ __launch_bounds__(256) void bwd_compose(BwdArgs a) {
   const float al2 = a.A[static_cast<size_t>(e) * kScanN + n] * kLog2e;
   auto at = [&](int s) { return ((static_cast<size_t>(b) * a.nseg + s) * a.dim + e) * kScanN + n; };
   auto sd = [&](int s) { return a.sdt[(static_cast<size_t>(b) * a.nseg + s) * a.dim + e]; };
+  // blocks of 8 segments: the block's loads are all issued before its chain
+  constexpr int kB = 8;
   float hcur = a.state_in ? a.state_in[(static_cast<size_t>(b) * a.dim + e) * kScanN + n] : 0.0f;
-  for (int s = 0; s < a.nseg; ++s) {
-    const float loc = a.hs[at(s)];
-    a.hs[at(s)] = hcur;  // the state entering segment s
-    hcur = fmaf(exp2_fast(al2 * sd(s)), hcur, loc);
+  for (int s0 = 0; s0 < a.nseg; s0 += kB) {
+    float loc[kB], dec[kB];
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      const int s = min(s0 + k, a.nseg - 1);
+      loc[k] = a.hs[at(s)];
+      dec[k] = sd(s);
+    }
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      if (s0 + k < a.nseg) {
+        a.hs[at(s0 + k)] = hcur;  // the state entering segment s0 + k
+        hcur = fmaf(exp2_fast(al2 * dec[k]), hcur, loc[k]);
+      }
+    }
   }
   float qcur = a.dstate_out ? a.dstate_out[(static_cast<size_t>(b) * a.dim + e) * kScanN + n] : 0.0f;
-  for (int s = a.nseg - 1; s >= 0; --s) {
-    const float loc = a.qs[at(s)];
-    a.qs[at(s)] = qcur;  // the gradient entering segment s from its right
-    qcur = fmaf(exp2_fast(al2 * sd(s)), qcur, loc);
+  for (int s0 = a.nseg - 1; s0 >= 0; s0 -= kB) {
+    float loc[kB], dec[kB];
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      const int s = max(s0 - k, 0);
+      loc[k] = a.qs[at(s)];
+      dec[k] = sd(s);
+    }
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      if (s0 - k >= 0) {
+        a.qs[at(s0 - k)] = qcur;  // the gradient entering segment s0 - k from its right
+        qcur = fmaf(exp2_fast(al2 * dec[k]), qcur, loc[k]);
+      }
+    }
   }
   if (a.dstate_in) a.dstate_in[(static_cast<size_t>(b) * a.dim + e) * kScanN + n] = qcur;
 }
@@ -326,11 +368,9 @@ __global__ __launch_bounds__(256) void bwd_main(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < kSeg; ++i) {
       if (t0 + i < t1) {
-        float xc, bv[4], av[4];
-        const float u = c.su_at(S, i, xc);
-        bool inside;
-        float dsp;
-        const float dt = c.dt_of(c.spre(S, i), inside, dsp);
+        float bv[4], av[4];
+        const float u = Lane::at(S.u, i);
+        const float dt = Lane::at(S.dt, i);
         c.sbc(S.B, i, bv);
         c.decay(dt, av);
 #pragma unroll
@@ -349,18 +389,13 @@ __global__ __launch_bounds__(256) void bwd_main(BwdArgs a) {
     float hprev[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) hprev[j] = i > 0 ? hist[i - 1][j] : hin[j];
-    float xc, bv[4], cv[4], av[4], zv;
-    const float u = c.su_at(S, i, xc);
-    bool inside;
-    float dsp;
-    const float pre = c.spre(S, i);
-    const float dt = c.dt_of(pre, inside, dsp);
+    float bv[4], cv[4], av[4];
+    const float u = Lane::at(S.u, i);
+    const float dt = Lane::at(S.dt, i);
     c.sbc(S.B, i, bv);
     c.sbc(S.C, i, cv);
     c.decay(dt, av);
-    const float dy = c.sdy(S, i);
-    const float g = c.sgate(S, i, zv);
-    const float dyc = dy * g;
+    const float dyc = Lane::at(S.dyc, i);
     float G[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) G[j] = fmaf(dyc, cv[j], Q[j]);
@@ -370,7 +405,7 @@ __global__ __launch_bounds__(256) void bwd_main(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) yp = fmaf(cv[j], hist[i][j], yp);
       const float yc = fmaf(c.d, u, quad_sum(yp));
-      if (a.dz && c.act && c.q == 0) a.dz[c.be(t)] = dy * yc * dsilu(zv);
+      if (a.dz && c.act && c.q == 0) a.dz[c.be(t)] = Lane::at(S.dzf, i) * yc;
     }
     float pdt = 0.0f, pdu = 0.0f;
 #pragma unroll
@@ -397,7 +432,7 @@ __global__ __launch_bounds__(256) void bwd_main(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) Q[j] = av[j] * G[j];
     dD = fmaf(dyc, u, dD);
-    const float dpre = inside ? ddt * dsp : 0.0f;
+    const float dpre = ddt * Lane::at(S.dpf, i);
     ddtb += dpre;
     if (a.dt_rank1) {
       const float r = static_cast<const float*>(a.dt)[static_cast<size_t>(b) * a.seqlen + t];
@@ -408,7 +443,7 @@ __global__ __launch_bounds__(256) void bwd_main(BwdArgs a) {
       a.ddt[c.be(t)] = dpre;
     }
     if (c.act && c.q == 0) {
-      if (a.conv_w) a.dxc[c.be(t)] = du * dsilu(xc);
+      if (a.conv_w) a.dxc[c.be(t)] = du * Lane::at(S.dsx, i);
       else if (a.dx) a.dx[c.be(t)] = du;
     }
   }
@@ -422,22 +457,32 @@ __global__ __launch_bounds__(256) void bwd_main(BwdArgs a) {
   }
 }
 
-// conv transpose: dx[t] = sum_k w[k] dxc[t + 3 - k]; one thread per (b, t, e)
+// conv transpose: dx[t] = sum_k w[k] dxc[t + 3 - k]; one thread per (b, run
+// of kDxRun steps, e), dxc read once into a sliding window
+constexpr int kDxRun = 16;
 __global__ __launch_bounds__(256) void bwd_conv_dx(BwdArgs a) {
   const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  const size_t total = static_cast<size_t>(a.batch) * a.seqlen * a.dim;
-  if (i >= total) return;
+  const int runs = (a.seqlen + kDxRun - 1) / kDxRun;
+  const size_t total = static_cast<size_t>(a.batch) * runs * a.dim;
+  if (i >= total || !a.dx) return;
   const int e = static_cast<int>(i % a.dim);
-  const int t = static_cast<int>((i / a.dim) % a.seqlen);
+  const int run = static_cast<int>((i / a.dim) % runs);
+  const int b = static_cast<int>(i / (static_cast<size_t>(a.dim) * runs));
+  const int t0 = run * kDxRun;
+  const size_t row = static_cast<size_t>(b) * a.seqlen;
   const float4 w = reinterpret_cast<const float4*>(a.conv_w)[e];
-  const float wk[4] = {w.x, w.y, w.z, w.w};
-  float v = 0.0f;
+  float g[kDxRun + 3];
 #pragma unroll
-  for (int k = 3; k >= 0; --k) {
-    const int tt = t + 3 - k;
-    if (tt < a.seqlen) v = fmaf(wk[k], a.dxc[i + static_cast<size_t>(3 - k) * a.dim], v);
+  for (int k = 0; k < kDxRun + 3; ++k) {
+    const int t = t0 + k;
+    g[k] = t < a.seqlen ? a.dxc[(row + t) * a.dim + e] : 0.0f;
   }
-  if (a.dx) a.dx[i] = v;
+#pragma unroll
+  for (int k = 0; k < kDxRun; ++k) {
+    const int t = t0 + k;
+    if (t < a.seqlen)
+      a.dx[(row + t) * a.dim + e] = fmaf(w.x, g[k + 3], fmaf(w.y, g[k + 2], fmaf(w.z, g[k + 1], w.w * g[k])));
+  }
 }
 
 // conv weights, bias and cache gradients: per channel, partial sums over
@@ -535,6 +580,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_e(BwdArgs a) {
   if (j < kBwdPe) {
     if (j >= 19) return;
     for (int b = 0; b < a.batch; ++b)
+#pragma unroll 8
       for (int s = 0; s < a.nseg; ++s) v += a.pe[((static_cast<size_t>(b) * a.nseg + s) * a.dim + e) * kBwdPe + j];
     if (j < kScanN) {
       if (a.dA) a.dA[static_cast<size_t>(e) * kScanN + j] = v;
@@ -550,6 +596,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_e(BwdArgs a) {
   if (!a.conv_w) return;
   const int k = j - kBwdPe;  // 0..3 weights, 4 bias
   const int chunks = a.batch * ((a.seqlen + kConvChunk - 1) / kConvChunk);
+#pragma unroll 8
   for (int c = 0; c < chunks; ++c) v += a.pw[(static_cast<size_t>(c) * a.dim + e) * 5 + k];
   if (k < 4) {
     if (a.dconv_w) a.dconv_w[static_cast<size_t>(e) * 4 + k] = v;
@@ -577,7 +624,8 @@ hipError_t launch_scan_bwd(const BwdArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const size_t bt = static_cast<size_t>(a.batch) * a.seqlen;
   if (a.conv_w) {
-    hipLaunchKernelGGL(bwd_conv_dx, dim3(blocks_for(bt * a.dim)), dim3(256), 0, s, a);
+    const size_t runs = static_cast<size_t>(a.batch) * ((a.seqlen + kDxRun - 1) / kDxRun);
+    hipLaunchKernelGGL(bwd_conv_dx, dim3(blocks_for(runs * a.dim)), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int chunks = a.batch * ((a.seqlen + kConvChunk - 1) / kConvChunk);
     hipLaunchKernelGGL(bwd_conv_w, dim3(blocks_for(a.dim), chunks), dim3(256), 0, s, a);
