@@ -114,7 +114,9 @@ struct SegStage {
 
 // Stage segment [t0, t1) of batch b for channel group gw: lane (r, j) loads
 // channel j of rows r, r + 4, ... and computes those rows' per-channel
-// quantities; B and C rows are contiguous (4 values a lane).
+// quantities (with FULL, also the derivative factors only the main pass
+// uses); B and C rows are contiguous (4 values a lane).
+template <bool FULL>
 __device__ __forceinline__ void stage_segment(const BwdArgs& a, int b, int gw, int t0, int t1, SegStage& S) {
   const int lane = threadIdx.x & 63;
   const int j = lane & 15, r = lane >> 4;
@@ -177,29 +179,25 @@ __device__ __forceinline__ void stage_segment(const BwdArgs& a, int b, int gw, i
         const float xc = fmaf(cw[0], S.xr[i][j], fmaf(cw[1], S.xr[i + 1][j], fmaf(cw[2], S.xr[i + 2][j],
                                                                                  fmaf(cw[3], S.xr[i + 3][j], cb))));
         u = silu(xc);
-        dsx = dsilu(xc);
+        if (FULL) dsx = dsilu(xc);
       } else {
         u = S.xr[i + 3][j];
       }
-      float sp, dsp;
+      float sp, dsp = 1.0f;
       if (a.dt_softplus) {
         sp = softplus(pre[k]);
-        dsp = rcp_fast(1.0f + exp2_fast(-pre[k] * kLog2e));
+        if (FULL) dsp = rcp_fast(1.0f + exp2_fast(-pre[k] * kLog2e));
       } else {
         sp = pre[k];
-        dsp = 1.0f;
       }
-      const bool inside = sp > a.dt_min && sp < a.dt_max;
       S.u[i][j] = u;
       S.dt[i][j] = fminf(fmaxf(sp, a.dt_min), a.dt_max);
-      S.dpf[i][j] = inside ? dsp : 0.0f;
-      S.dsx[i][j] = dsx;
-      if (a.z) {
-        S.dyc[i][j] = dy[k] * silu(z[k]);
-        S.dzf[i][j] = dy[k] * dsilu(z[k]);
-      } else {
-        S.dyc[i][j] = dy[k];
-        S.dzf[i][j] = 0.0f;
+      S.dyc[i][j] = a.z ? dy[k] * silu(z[k]) : dy[k];
+      if (FULL) {
+        const bool inside = sp > a.dt_min && sp < a.dt_max;
+        S.dpf[i][j] = inside ? dsp : 0.0f;
+        S.dsx[i][j] = dsx;
+        S.dzf[i][j] = a.z ? dy[k] * dsilu(z[k]) : 0.0f;
       }
     }
   }
@@ -263,29 +261,33 @@ __global__ __launch_bounds__(256) void bwd_summary(BwdArgs a) {
   const Lane c(a, b, gw);
   const int t0 = s * kSeg, t1 = min(a.seqlen, t0 + kSeg);
   SegStage& S = stage[threadIdx.x >> 6];
-  stage_segment(a, b, gw, t0, t1, S);
+  stage_segment<false>(a, b, gw, t0, t1, S);
+  // the decays of the forward walk are kept for the backward one
   float h[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sdt = 0.0f;
-  for (int t = t0; t < t1; ++t) {
-    const int i = t - t0;
-    float bv[4], av[4];
-    const float u = Lane::at(S.u, i);
-    const float dt = Lane::at(S.dt, i);
-    c.sbc(S.B, i, bv);
-    c.decay(dt, av);
+  float ah[kSeg][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) h[j] = fmaf(av[j], h[j], dt * u * bv[j]);
-    sdt += dt;
+  for (int i = 0; i < kSeg; ++i) {
+    if (t0 + i < t1) {
+      float bv[4];
+      const float u = Lane::at(S.u, i);
+      const float dt = Lane::at(S.dt, i);
+      c.sbc(S.B, i, bv);
+      c.decay(dt, ah[i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h[j] = fmaf(ah[i][j], h[j], dt * u * bv[j]);
+      sdt += dt;
+    }
   }
   float Q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int t = t1 - 1; t >= t0; --t) {
-    const int i = t - t0;
-    float cv[4], av[4];
-    const float dt = Lane::at(S.dt, i);
-    c.sbc(S.C, i, cv);
-    c.decay(dt, av);
-    const float dyc = Lane::at(S.dyc, i);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) Q[j] = av[j] * fmaf(dyc, cv[j], Q[j]);
+  for (int i = kSeg - 1; i >= 0; --i) {
+    if (t0 + i < t1) {
+      float cv[4];
+      c.sbc(S.C, i, cv);
+      const float dyc = Lane::at(S.dyc, i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Q[j] = ah[i][j] * fmaf(dyc, cv[j], Q[j]);
+    }
   }
   if (!c.act) return;
   const size_t o = ((static_cast<size_t>(b) * a.nseg + s) * a.dim + c.e) * kScanN + 4 * c.q;
@@ -352,7 +354,7 @@ __global__ __launch_bounds__(256) void bwd_main(BwdArgs a) {
   const Lane c(a, b, gw);
   const int t0 = s * kSeg, t1 = min(a.seqlen, t0 + kSeg);
   SegStage& S = stage[threadIdx.x >> 6];
-  stage_segment(a, b, gw, t0, t1, S);
+  stage_segment<true>(a, b, gw, t0, t1, S);
   const size_t so = ((static_cast<size_t>(b) * a.nseg + s) * a.dim + c.e) * kScanN + 4 * c.q;
   float hin[4], Q[4];
   {
