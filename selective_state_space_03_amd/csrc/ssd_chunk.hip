@@ -331,14 +331,29 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NB], float dlast, const 
   }
 }
 
-// Workgroup order: segment slowest, then batch, then head, so that the
-// workgroups running at once cover all heads of a segment (they read the same
-// B and C rows).
+// Workgroup order.  Workgroups are handed to the 8 XCDs in turn, so block
+// index i runs on XCD i % 8.  A head's x slice (P bf16 per token) shares its
+// 128-byte lines with the neighbouring heads', so when the head count is a
+// multiple of 8, the heads are cut into 8 runs of consecutive heads and run m
+// goes to XCD m (neighbours share that XCD's L2).  The batch varies next,
+// then the segment (main kernel) or the summary piece, slowest.
+__device__ __forceinline__ void decode_heads(const ChunkKernelArgs& a, int bid, int& h, int& rest) {
+  if (a.nheads % 8 == 0) {
+    const int run = a.nheads / 8;
+    const int xcd = bid & 7;
+    rest = bid >> 3;
+    h = xcd * run + rest % run;
+    rest /= run;
+  } else {
+    h = bid % a.nheads;
+    rest = bid / a.nheads;
+  }
+}
 __device__ __forceinline__ void decode_bid(const ChunkKernelArgs& a, int bid, int& b, int& h, int& k) {
-  h = bid % a.nheads;
-  bid /= a.nheads;
-  b = bid % a.batch;
-  k = bid / a.batch;
+  int rest;
+  decode_heads(a, bid, h, rest);
+  b = rest % a.batch;
+  k = rest / a.batch;
 }
 
 // ---- main kernel --------------------------------------------------------
@@ -726,10 +741,11 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
 // Workgroup (piece j of segment k < nseg - 1, batch, head); the piece covers
 // chunks [k cps + j kPiece, min(k cps + (j + 1) kPiece, (k + 1) cps)), all
 // whole (the ragged chunk, if any, is the last chunk of the last segment).
+// Four waves; wave w owns n-block w of the piece's state for all p-blocks.
 template <int NS>
-__global__ __launch_bounds__(kThreads) void ssd_summary_kernel(ChunkKernelArgs a) {
-  constexpr int P = 16 * NS, JS = (NS + 1) / 2;  // state blocks per wave: p-blocks (w >> 2) + 2 j, n-block w & 3
-  using Io = ChunkIo<NS, kThreads>;
+__global__ __launch_bounds__(kIoThreads) void ssd_summary_kernel(ChunkKernelArgs a) {
+  constexpr int P = 16 * NS;
+  using Io = ChunkIo<NS, kIoThreads>;
   __shared__ SummSmem<NS> sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, held in a scalar register
@@ -738,11 +754,10 @@ __global__ __launch_bounds__(kThreads) void ssd_summary_kernel(ChunkKernelArgs a
   const int lg = lane >> 4;
 
   const int npieces = (a.nseg - 1) * a.ppseg;
-  int bid = blockIdx.x;
-  const int piece = bid % npieces;
-  bid /= npieces;
-  const int h = bid % a.nheads;
-  const int b = bid / a.nheads;
+  int h, rest;
+  decode_heads(a, blockIdx.x, h, rest);
+  const int b = rest % a.batch;
+  const int piece = rest / a.batch;
   const int seg = piece / a.ppseg, j = piece % a.ppseg;
   const int c_beg = seg * a.cps + j * kPiece;
   const int c_end = min(c_beg + kPiece, (seg + 1) * a.cps);
@@ -750,9 +765,9 @@ __global__ __launch_bounds__(kThreads) void ssd_summary_kernel(ChunkKernelArgs a
   const float dtb = a.dt_bias ? a.dt_bias[h] : 0.0f;
   const Io io(a, b, h);
 
-  f32x4 S[JS];
+  f32x4 S[NS];
 #pragma unroll
-  for (int t = 0; t < JS; ++t) S[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < NS; ++t) S[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float dec = 0.0f;
 
   typename Io::Regs R;
@@ -772,23 +787,16 @@ __global__ __launch_bounds__(kThreads) void ssd_summary_kernel(ChunkKernelArgs a
     }
     dec += sc.last;
     __syncthreads();
-    state_update<NS, JS, 2>(S, exp2_fast(sc.last), sm.Bt, sm.Xt, sm.wS, w & 3, w >> 2, li, lg);
+    state_update<NS, NS, 1>(S, exp2_fast(sc.last), sm.Bt, sm.Xt, sm.wS, w, 0, li, lg);
   }
 
   const size_t bh = static_cast<size_t>(b) * a.nheads + h;
   const size_t slot = bh * npieces + piece;
   float* out = a.ws + ws_sin_floats(a) + slot * P * kN;
-  const int nb = w & 3, pb0 = w >> 2;
 #pragma unroll
-  for (int t = 0; t < JS; ++t) {
-    if (pb0 + 2 * t < NS) {
+  for (int t = 0; t < NS; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = 16 * (pb0 + 2 * t) + 4 * lg + r;
-        out[static_cast<size_t>(p) * kN + 16 * nb + li] = S[t][r];
-      }
-    }
-  }
+    for (int r = 0; r < 4; ++r) out[static_cast<size_t>(16 * t + 4 * lg + r) * kN + 16 * w + li] = S[t][r];
   if (tid == 0) a.ws[ws_sin_floats(a) + ws_piece_floats(a) + slot] = dec;
 }
 
@@ -858,7 +866,7 @@ hipError_t go(const ChunkLaunch& l, hipStream_t s) {
   if (heads == 0) return hipSuccess;
   if (k.nseg > 1) {
     const unsigned pieces = heads * static_cast<unsigned>((k.nseg - 1) * k.ppseg);
-    hipLaunchKernelGGL((ssd_summary_kernel<NS>), dim3(pieces), dim3(kThreads), 0, s, k);
+    hipLaunchKernelGGL((ssd_summary_kernel<NS>), dim3(pieces), dim3(kIoThreads), 0, s, k);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned pn = static_cast<unsigned>(k.headdim * kN);
