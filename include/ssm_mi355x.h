@@ -347,13 +347,14 @@ ssm_status_t ssm_chunk_decode_check(const ssm_chunk_decode_params_t *p);
  *           about 16 mantissa bits
  *   weight  (out_features, in_features) bf16 (the (out, in) layout of a weight)
  *   out     (rows, out_features) out_dtype; must not overlap x or weight
- *   workspace  optional device scratch (256-byte aligned): with at least
- *           ssm_linear_workspace_size(p) bytes a shape with too few output
- *           tiles to fill the GPU splits the in_features sum into ranges
- *           whose fp32 partials are added in range order; with less (or
- *           NULL) it runs unsplit.  Either way the result is deterministic.
- * fp32 accumulation.  x, weight and out must be 16-byte aligned;
- * in_features % 8 == 0; out_features % 4 == 0.
+ *   workspace  device scratch of ssm_linear_workspace_size(p) bytes (256-byte
+ *           aligned, owned by the caller, contents on entry irrelevant):
+ *           none for a bf16 x; for an f32 x its bf16 value and remainder and
+ *           an fp32 product.  Missing or short: SSM_ERR_WORKSPACE.
+ * fp32 accumulation.  The products run in the ROCm GEMM library (hipBLASLt),
+ * the same algorithm for a given shape and device, so results repeat bit for
+ * bit.  x, weight and out must be 16-byte aligned; in_features % 8 == 0;
+ * out_features % 4 == 0.
  * ---------------------------------------------------------------------- */
 typedef struct ssm_linear_params {
   uint32_t struct_size; /* = sizeof(ssm_linear_params_t) */

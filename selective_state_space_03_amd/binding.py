@@ -452,7 +452,7 @@ def chunk_decode_step(x, dt, A, B, C, state, *, D=None, dt_bias=None, dt_softplu
 def linear_fwd(x, weight, *, out=None, out_dtype=None, workspace=None, stream=None, prepare=False):
     """A projection without bias (ssm_linear_fwd): out[..., o] = sum_i x[..., i] weight[o, i], with x
     (..., in) bf16 or f32 and weight (out, in) bf16.  A workspace of ssm_linear_workspace_size() bytes
-    is allocated when none is given (workspace=False runs without one).  Returns out (..., out), or
+    is allocated when none is given (an f32 x needs one; workspace=False passes none).  Returns out (..., out), or
     with prepare=True a Call that enqueues this same call again on each run()."""
     L_ = lib()
     n_out, n_in = weight.shape

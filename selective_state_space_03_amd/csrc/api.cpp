@@ -385,6 +385,9 @@ ssm_status_t linear_check(const ssm_linear_params_t* p) {
     if (overlaps(ws, out) || overlaps(ws, {p->x, M * K * esize(p->x_dtype)}) || overlaps(ws, {p->weight, N * K * 2}))
       return fail(SSM_ERR_INVALID_ARG, "%s overlaps another tensor", "workspace");
   }
+  const size_t need = ssm::gemm_workspace_bytes(p->rows, p->out_features, p->in_features, p->x_dtype);
+  if (need > 0 && (!p->workspace || p->workspace_bytes < need))
+    return fail(SSM_ERR_WORKSPACE, "%s is missing or smaller than ssm_linear_workspace_size()", "workspace");
   return SSM_OK;
 }
 

@@ -1,384 +1,204 @@
-// Projection GEMMs of the layer for gfx950: C = A W^T with W (N, K) in bf16
-// (a weight stored as (out, in)), A (M, K) in bf16 or fp32, fp32 accumulation.
+// Projection GEMMs of the layer: C = A W^T with W (N, K) in bf16 (a weight
+// stored as (out, in)), A (M, K) in bf16 or fp32, fp32 accumulation.
 //
 // Page "Axon-SSM: selective state space model", section "Algorithm": in_proj
 // (D -> 2E, split into x_branch and z) and out_proj (E -> D) are dense
-// projections of every token.  They are the only dense contractions of the
-// layer and run on the matrix cores:
-//   v_mfma_f32_32x32x16_bf16, a 128x64 tile per wave (128 accumulator
-//   registers), 8 waves per workgroup (256x256 output tile, two waves per SIMD
-//   so one computes while the other waits on LDS), K in steps staged in LDS
-//   (double-buffered, the next step's global loads in flight during the
-//   current step's MFMAs; fragments of the next MFMA sub-step read from LDS
-//   while the current one computes).  Measured against one 128x128 wave per
-//   SIMD: in_proj 221 vs 233 us, out_proj 200 vs 228 us.
-// An fp32 A operand (the scan output feeding out_proj) is split on its way
-// into LDS into a bf16 high part and the bf16 of the remainder, and both are
-// multiplied (about 16 mantissa bits, so the product keeps fp32-level
-// accuracy); a bf16 A (the layer input) is used as it is.
-// The MFMA takes W rows as its first operand and A rows as its second, so each
-// lane ends with 4 consecutive output columns of one row: 16-byte (fp32) or
-// 8-byte (bf16) stores.  Columns n >= n_split go to a second output (in_proj's
-// z half), so the split costs nothing.
+// projections of every token, plain GEMMs with nothing to fuse, so they go to
+// the ROCm GEMM library (hipBLASLt) on the matrix cores.  What is done here:
+//   * the layout: row-major C = A W^T is the column-major product
+//     C^T = W A^T, i.e. hipBLASLt's D = op(W) op(A) with op(W) = T on W seen
+//     column-major (K x N) and A seen column-major (K x M);
+//   * in_proj's output columns >= n_split go to a second buffer (z): one call
+//     per half, on the matching rows of W;
+//   * an fp32 A (the scan output feeding out_proj) is split into a bf16 value
+//     and the bf16 of its remainder (about 16 mantissa bits, so the product
+//     keeps fp32-level accuracy), and the two halves are multiplied in turn,
+//     the second accumulating onto the first (beta = 1) in fp32;
+//   * plans (descriptors, layouts and the library's first heuristic choice
+//     among algorithms that need no workspace) are made once per shape and
+//     device and kept.
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
-#include <algorithm>
-#include <type_traits>
+#include <hipblaslt/hipblaslt.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
 
 namespace ssm {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+// fp32 A -> bf16 value and bf16 remainder, 4 elements a thread
+__global__ __launch_bounds__(256) void split_hi_lo(const float* __restrict__ A, int lda, int M, int K,
+                                                   uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
+  const size_t q = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int kq = K / 4;
+  if (q >= static_cast<size_t>(M) * kq) return;
+  const int m = static_cast<int>(q / kq), k = 4 * static_cast<int>(q % kq);
+  const float4 v = *reinterpret_cast<const float4*>(A + static_cast<size_t>(m) * lda + k);
+  const float f[4] = {v.x, v.y, v.z, v.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(f[j]));
+    l[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(f[j] - __uint_as_float(h[j] << 16)));
+  }
+  const size_t o = static_cast<size_t>(m) * K + k;
+  *reinterpret_cast<uint2*>(hi + o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  *reinterpret_cast<uint2*>(lo + o) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+}
 
-#ifndef GEMM_WN
-#define GEMM_WN 4
-#endif
-constexpr int kWavesN = GEMM_WN;           // waves along N (2 along M)
-constexpr int kThreads = 128 * kWavesN;    // 8 waves: 2 x 4 over the output tile
+// fp32 (M, N) contiguous -> bf16 rows of pitch ldc, 4 elements a thread
+__global__ __launch_bounds__(256) void to_bf16(const float* __restrict__ T, int M, int N, uint16_t* __restrict__ C,
+                                               int ldc) {
+  const size_t q = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int nq = N / 4;
+  if (q >= static_cast<size_t>(M) * nq) return;
+  const int m = static_cast<int>(q / nq), n = 4 * static_cast<int>(q % nq);
+  const float4 v = *reinterpret_cast<const float4*>(T + static_cast<size_t>(m) * N + n);
+  const uint32_t b0 = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v.x));
+  const uint32_t b1 = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v.y));
+  const uint32_t b2 = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v.z));
+  const uint32_t b3 = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v.w));
+  *reinterpret_cast<uint2*>(C + static_cast<size_t>(m) * ldc + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+}
 
-// GM x GN 32x32 MFMA blocks per wave (wave tile 32 GM rows of A by 32 GN rows
-// of W), so the workgroup tile is BM = 64 GM by BN = 64 GN; K steps of BK.
-template <int GM, int GN, int BK, bool SPLIT>
-struct Cfg {
-  static constexpr int BM = 64 * GM, BN = 32 * GN * kWavesN;
-  static constexpr int kPitch = BK + 8;  // LDS row pitch in bf16 (rows land on different banks)
-  static constexpr int APR = SPLIT ? BK / 4 : BK / 8;  // 16-byte pieces per A row of a K step
-  static constexpr int WPR = BK / 8;
-  static constexpr int AP = BM * APR / kThreads;  // A pieces per thread
-  static constexpr int WP = BN * WPR / kThreads;
-  static_assert(BM * APR % kThreads == 0 && BN * WPR % kThreads == 0, "whole pieces per thread");
+unsigned blocks_for(size_t n) { return static_cast<unsigned>((n + 255) / 256); }
+
+// ---- hipBLASLt plans ------------------------------------------------------
+struct Plan {
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t lw = nullptr, la = nullptr, lc = nullptr;
+  hipblasLtMatmulAlgo_t algo{};
 };
 
-template <int GM, int GN, int BK, bool SPLIT>
-struct GemmSmem {
-  using C = Cfg<GM, GN, BK, SPLIT>;
-  uint16_t A[2][C::BM][C::kPitch];
-  uint16_t Alo[SPLIT ? 2 : 1][SPLIT ? C::BM : 1][C::kPitch];
-  uint16_t W[2][C::BN][C::kPitch];
-};
+// (device, M, N, K, lda, ldw, ldc, output type, accumulate)
+using PlanKey = std::tuple<int, int, int, int, int, int, int, int, int>;
 
-__device__ __forceinline__ uint32_t bf16_rne(float v) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+std::mutex g_lt_mutex;
+hipblasLtHandle_t g_lt_handle[64] = {};
+std::map<PlanKey, Plan> g_plans;
+
+hipError_t lt_status(hipblasStatus_t s) { return s == HIPBLAS_STATUS_SUCCESS ? hipSuccess : hipErrorUnknown; }
+
+// The plan for D (M x N row-major, pitch ldc, type out) = A (M x K bf16, pitch
+// lda) * W (N x K bf16, pitch ldw)^T (+ D when acc).
+hipError_t get_plan(int M, int N, int K, int lda, int ldw, int ldc, int out_dtype, bool acc, const Plan** plan,
+                    hipblasLtHandle_t* handle) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_lt_mutex);
+  if (g_lt_handle[dev] == nullptr) {
+    e = lt_status(hipblasLtCreate(&g_lt_handle[dev]));
+    if (e != hipSuccess) return e;
+  }
+  *handle = g_lt_handle[dev];
+  const PlanKey key{dev, M, N, K, lda, ldw, ldc, out_dtype, acc ? 1 : 0};
+  auto it = g_plans.find(key);
+  if (it != g_plans.end()) {
+    *plan = &it->second;
+    return hipSuccess;
+  }
+  Plan p;
+  const hipDataType dt = out_dtype == kBF16 ? HIP_R_16BF : HIP_R_32F;
+  auto fail = [&](hipError_t err) {
+    if (p.desc) hipblasLtMatmulDescDestroy(p.desc);
+    if (p.lw) hipblasLtMatrixLayoutDestroy(p.lw);
+    if (p.la) hipblasLtMatrixLayoutDestroy(p.la);
+    if (p.lc) hipblasLtMatrixLayoutDestroy(p.lc);
+    return err;
+  };
+  if ((e = lt_status(hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F))) != hipSuccess) return fail(e);
+  const hipblasOperation_t tw = HIPBLAS_OP_T, ta = HIPBLAS_OP_N;
+  if ((e = lt_status(hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &tw, sizeof(tw)))) !=
+      hipSuccess)
+    return fail(e);
+  if ((e = lt_status(hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &ta, sizeof(ta)))) !=
+      hipSuccess)
+    return fail(e);
+  if ((e = lt_status(hipblasLtMatrixLayoutCreate(&p.lw, HIP_R_16BF, K, N, ldw))) != hipSuccess) return fail(e);
+  if ((e = lt_status(hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, K, M, lda))) != hipSuccess) return fail(e);
+  if ((e = lt_status(hipblasLtMatrixLayoutCreate(&p.lc, dt, N, M, ldc))) != hipSuccess) return fail(e);
+  hipblasLtMatmulPreference_t pref = nullptr;
+  if ((e = lt_status(hipblasLtMatmulPreferenceCreate(&pref))) != hipSuccess) return fail(e);
+  const uint64_t no_ws = 0;
+  e = lt_status(hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &no_ws,
+                                                      sizeof(no_ws)));
+  hipblasLtMatmulHeuristicResult_t res{};
+  int found = 0;
+  if (e == hipSuccess)
+    e = lt_status(hipblasLtMatmulAlgoGetHeuristic(*handle, p.desc, p.lw, p.la, p.lc, p.lc, pref, 1, &res, &found));
+  hipblasLtMatmulPreferenceDestroy(pref);
+  if (e != hipSuccess) return fail(e);
+  if (found < 1) return fail(hipErrorNotSupported);
+  p.algo = res.algo;
+  auto ins = g_plans.emplace(key, p);
+  *plan = &ins.first->second;
+  return hipSuccess;
 }
 
-// blockIdx.x -> tile: each XCD (workgroups are dealt to the 8 XCDs in turn)
-// takes a contiguous range of tiles, and inside it the M tiles of one N tile
-// are consecutive, so a W tile is fetched once per L2 and reused.
-__device__ __forceinline__ int xcd_tile() {
-  const int n = gridDim.x, per = n / 8, rem = n % 8;
-  const int x = blockIdx.x % 8, s = blockIdx.x / 8;
-  return (x < rem) ? x * (per + 1) + s : rem * (per + 1) + (x - rem) * per + s;
+hipError_t matmul(const uint16_t* A, int lda, const uint16_t* W, int ldw, void* D, int ldc, int M, int N, int K,
+                  int out_dtype, bool acc, hipStream_t s) {
+  const Plan* p = nullptr;
+  hipblasLtHandle_t h = nullptr;
+  hipError_t e = get_plan(M, N, K, lda, ldw, ldc, out_dtype, acc, &p, &h);
+  if (e != hipSuccess) return e;
+  const float alpha = 1.0f, beta = acc ? 1.0f : 0.0f;
+  return lt_status(hipblasLtMatmul(h, p->desc, &alpha, W, p->lw, A, p->la, &beta, D, p->lc, D, p->lc, &p->algo,
+                                   nullptr, 0, s));
 }
 
-// K split: blockIdx.y takes K range [ky Kc, min(K, (ky + 1) Kc)) and, when
-// there is more than one range, writes its fp32 partial tile to ws[ky]
-// (M x N); gemm_reduce adds the partials in order.
-// EDGE: the shape has partial tiles (M, N or K not a multiple of the tile),
-// so loads and stores are guarded; otherwise they are not.
-//
-// v_mfma_f32_32x32x16_bf16 with W rows as the first operand and A rows as the
-// second: lane l supplies row l % 32 of its operand at k = 8 (l / 32) .. + 7,
-// and holds in accumulator register r the output (n = 8 (r / 4) + 4 (l / 32)
-// + r % 4, m = l % 32) of the block, i.e. four runs of 4 consecutive columns.
-#ifndef GEMM_WPE
-#define GEMM_WPE 2
-#endif
-template <typename AT, typename OT, int GM, int GN, int BK, bool EDGE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GEMM_WPE, GEMM_WPE))) void gemm_kernel(GemmArgs g) {
-  constexpr bool kSplit = std::is_same<AT, float>::value;
-  static_assert(BK % 16 == 0, "whole MFMA K steps");
-  using C = Cfg<GM, GN, BK, kSplit>;
-  constexpr int BM = C::BM, BN = C::BN;
-  __shared__ GemmSmem<GM, GN, BK, kSplit> sm;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, lh = lane >> 5;
-
-  const int tiles_m = (g.M + BM - 1) / BM;
-  const int t = xcd_tile();
-  const int m0 = (t % tiles_m) * BM, n0 = (t / tiles_m) * BN;
-  const int kbeg = blockIdx.y * g.kchunk;
-  const int kend = min(g.K, kbeg + g.kchunk);
-
-  uint4 sa[C::AP], sw[C::WP];
-  // A guarded piece is loaded from a clamped (valid) address and zeroed after,
-  // which keeps the loads free of branches.
-  auto piece = [&](const char* base, size_t ld_bytes, int row, int rows, int col_bytes, int k, int klim) -> uint4 {
-    if constexpr (!EDGE) {
-      return *reinterpret_cast<const uint4*>(base + static_cast<size_t>(row) * ld_bytes + col_bytes);
-    } else {
-      const bool ok = row < rows && k < klim;
-      const int rc = ok ? row : 0;
-      const int cc = ok ? col_bytes : 0;
-      uint4 v = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(rc) * ld_bytes + cc);
-      if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
-      return v;
-    }
-  };
-  const char* Ab = static_cast<const char*>(g.A);
-  const char* Wb = reinterpret_cast<const char*>(g.W);
-  constexpr int kAes = kSplit ? 4 : 2;  // bytes per A element
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < C::AP; ++i) {
-      const int idx = tid + kThreads * i, r = idx / C::APR, pc = idx % C::APR;
-      const int k = k0 + (kSplit ? 4 : 8) * pc;
-      sa[i] = piece(Ab, static_cast<size_t>(g.lda) * kAes, m0 + r, g.M, k * kAes, k, kend);
-    }
-#pragma unroll
-    for (int i = 0; i < C::WP; ++i) {
-      const int idx = tid + kThreads * i, r = idx / C::WPR, pc = idx % C::WPR;
-      const int k = k0 + 8 * pc;
-      sw[i] = piece(Wb, static_cast<size_t>(g.ldw) * 2, n0 + r, g.N, k * 2, k, kend);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::AP; ++i) {
-      const int idx = tid + kThreads * i, r = idx / C::APR, pc = idx % C::APR;
-      if constexpr (kSplit) {
-        const float v[4] = {__uint_as_float(sa[i].x), __uint_as_float(sa[i].y), __uint_as_float(sa[i].z),
-                            __uint_as_float(sa[i].w)};
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          hi[j] = bf16_rne(v[j]);
-          lo[j] = bf16_rne(v[j] - __uint_as_float(hi[j] << 16));
-        }
-        *reinterpret_cast<uint2*>(&sm.A[buf][r][4 * pc]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-        *reinterpret_cast<uint2*>(&sm.Alo[buf][r][4 * pc]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
-      } else {
-        *reinterpret_cast<uint4*>(&sm.A[buf][r][8 * pc]) = sa[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::WP; ++i) {
-      const int idx = tid + kThreads * i, r = idx / C::WPR, pc = idx % C::WPR;
-      *reinterpret_cast<uint4*>(&sm.W[buf][r][8 * pc]) = sw[i];
-    }
-  };
-
-  // wave tile: A rows [32 GM wm, +32 GM), W rows [32 GN wn, +32 GN)
-  const int wm = w & 1, wn = w >> 1;
-  f32x16 acc[GN][GM];
-#pragma unroll
-  for (int j = 0; j < GN; ++j)
-#pragma unroll
-    for (int i = 0; i < GM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
-
-  // One K step from LDS buffer buf in MFMA sub-steps of 16: the fragments of
-  // sub-step kk + 1 are read while those of kk feed the matrix cores, and the
-  // scheduler is told to interleave the two.
-  struct Frags {
-    bf16x8 w[GN], a[GM], alo[kSplit ? GM : 1];
-  };
-  auto read_frags = [&](int buf, int kk, Frags& f) {
-    const int k = 16 * kk + 8 * lh;
-#pragma unroll
-    for (int j = 0; j < GN; ++j) f.w[j] = *reinterpret_cast<const bf16x8*>(&sm.W[buf][32 * GN * wn + 32 * j + l32][k]);
-#pragma unroll
-    for (int i = 0; i < GM; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(&sm.A[buf][32 * GM * wm + 32 * i + l32][k]);
-    if constexpr (kSplit) {
-#pragma unroll
-      for (int i = 0; i < GM; ++i)
-        f.alo[i] = *reinterpret_cast<const bf16x8*>(&sm.Alo[buf][32 * GM * wm + 32 * i + l32][k]);
-    }
-  };
-  auto mfmas = [&](const Frags& f) {
-#pragma unroll
-    for (int j = 0; j < GN; ++j)
-#pragma unroll
-      for (int i = 0; i < GM; ++i) acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[j], f.a[i], acc[j][i], 0, 0, 0);
-    if constexpr (kSplit) {
-#pragma unroll
-      for (int j = 0; j < GN; ++j)
-#pragma unroll
-        for (int i = 0; i < GM; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[j], f.alo[i], acc[j][i], 0, 0, 0);
-    }
-  };
-  constexpr int kReads = GN + GM * (kSplit ? 2 : 1);
-  constexpr int kMfmas = GN * GM * (kSplit ? 2 : 1);
-  constexpr int kPer = kMfmas / kReads > 0 ? kMfmas / kReads : 1;
-  auto compute = [&](int buf) {
-    Frags f[2];
-    read_frags(buf, 0, f[0]);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      if (kk + 1 < BK / 16) {
-        read_frags(buf, kk + 1, f[(kk + 1) & 1]);
-        mfmas(f[kk & 1]);
-#pragma unroll
-        for (int r = 0; r < kReads; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
-        }
-        if (kMfmas > kPer * kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kPer * kReads, 0);
-      } else {
-        mfmas(f[kk & 1]);
-      }
-    }
-  };
-
-  const int KT = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
-  if (KT > 0) {
-    gload(kbeg);
-    sstore(0);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) gload(kbeg + (kt + 1) * BK);
-    compute(kt & 1);
-    if (kt + 1 < KT) sstore((kt + 1) & 1);
-    __syncthreads();
-  }
-
-  // acc[j][i] lane (l32, lh), register 4 q + e: row m = m0 + 32 GM wm + 32 i
-  // + l32, column n = n0 + 32 GN wn + 32 j + 8 q + 4 lh + e
-  const int mb = m0 + 32 * GM * wm + l32;
-  const int nb = 32 * GN * wn + 4 * lh;
-  if (gridDim.y > 1) {  // fp32 partial of this K range
-    float* part = g.ws + static_cast<size_t>(blockIdx.y) * g.M * g.N;
-#pragma unroll
-    for (int i = 0; i < GM; ++i) {
-      const int m = mb + 32 * i;
-      if (EDGE && m >= g.M) continue;
-#pragma unroll
-      for (int j = 0; j < GN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + nb + 32 * j + 8 * q;
-          if (EDGE && n >= g.N) continue;
-          const f32x16& v = acc[j][i];
-          *reinterpret_cast<float4*>(part + static_cast<size_t>(m) * g.N + n) =
-              make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-        }
-    }
-    return;
-  }
-  const bool second = n0 >= g.n_split;
-  void* out = second ? g.C1 : g.C0;
-  const int ncol0 = second ? n0 - g.n_split : n0;
-  const int ncols = second ? g.N - g.n_split : g.n_split;
-  const int ldc = second ? g.ldc1 : g.ldc0;
-#pragma unroll
-  for (int i = 0; i < GM; ++i) {
-    const int m = mb + 32 * i;
-    if (EDGE && m >= g.M) continue;
-#pragma unroll
-    for (int j = 0; j < GN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = ncol0 + nb + 32 * j + 8 * q;
-        if (EDGE && c >= ncols) continue;  // ncols % 4 == 0: a 4-column piece is all in or all out
-        const f32x16& v = acc[j][i];
-        const size_t o = static_cast<size_t>(m) * ldc + c;
-        if constexpr (std::is_same<OT, float>::value) {
-          *reinterpret_cast<float4*>(static_cast<float*>(out) + o) =
-              make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-        } else {
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) =
-              make_uint2(bf16_rne(v[4 * q]) | (bf16_rne(v[4 * q + 1]) << 16),
-                         bf16_rne(v[4 * q + 2]) | (bf16_rne(v[4 * q + 3]) << 16));
-        }
-      }
-  }
-}
-
-// Sum of the K-range partials (in range order) into the outputs, 4 columns a
-// thread.
-template <typename OT>
-__global__ __launch_bounds__(256) void gemm_reduce(GemmArgs g, int parts) {
-  const size_t q = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;  // 4-column piece
-  const size_t total = static_cast<size_t>(g.M) * (g.N / 4);
-  if (q >= total) return;
-  const size_t m = q / (g.N / 4);
-  const int n = static_cast<int>(q - m * (g.N / 4)) * 4;
-  const size_t plane = static_cast<size_t>(g.M) * g.N;
-  float4 s = reinterpret_cast<const float4*>(g.ws)[q];
-  for (int p = 1; p < parts; ++p) {
-    const float4 v = reinterpret_cast<const float4*>(g.ws + p * plane)[q];
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
-  }
-  const bool second = n >= g.n_split;
-  void* out = second ? g.C1 : g.C0;
-  const size_t o = m * (second ? g.ldc1 : g.ldc0) + (second ? n - g.n_split : n);
-  if constexpr (std::is_same<OT, float>::value) {
-    *reinterpret_cast<float4*>(static_cast<float*>(out) + o) = s;
-  } else {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) =
-        make_uint2(bf16_rne(s.x) | (bf16_rne(s.y) << 16), bf16_rne(s.z) | (bf16_rne(s.w) << 16));
-  }
-}
-
-#ifndef GEMM_FM
-#define GEMM_FM 4
-#endif
-#ifndef GEMM_FN
-#define GEMM_FN 2
-#endif
-#ifndef GEMM_BK
-#define GEMM_BK 64
-#endif
-#ifndef GEMM_SPLIT_BK
-#define GEMM_SPLIT_BK 32
-#endif
-
-// K ranges for a shape: one when the tiles alone fill the chip, else enough to
-// reach about 240 workgroups (one per CU, 256 CUs), keeping each range at
-// least 1024 deep; only as many as the workspace holds partials for.
-int k_parts(int M, int N, int K, bool split_a, size_t ws_bytes) {
-  const int BM = 64 * GEMM_FM, BN = 32 * GEMM_FN * kWavesN;
-  (void)split_a;
-  const long tiles = static_cast<long>((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  if (tiles >= 160 || K < 2048) return 1;
-  int parts = static_cast<int>(std::min<long>((240 + tiles - 1) / tiles, K / 1024));
-  const size_t plane = static_cast<size_t>(M) * N * 4;
-  while (parts > 1 && static_cast<size_t>(parts) * plane > ws_bytes) --parts;
-  return std::max(parts, 1);
-}
-
-template <typename AT, typename OT>
-hipError_t go(const GemmArgs& g0, hipStream_t s) {
-  constexpr bool kSplit = std::is_same<AT, float>::value;
-  constexpr int FM = GEMM_FM, FN = GEMM_FN, BK = kSplit ? GEMM_SPLIT_BK : GEMM_BK;
-  using C = Cfg<FM, FN, BK, kSplit>;
-  GemmArgs g = g0;
-  const unsigned tiles = static_cast<unsigned>((g.M + C::BM - 1) / C::BM) * static_cast<unsigned>((g.N + C::BN - 1) / C::BN);
-  if (tiles == 0) return hipSuccess;
-  const int parts = k_parts(g.M, g.N, g.K, kSplit, g.ws != nullptr ? g.ws_bytes : 0);
-  g.kchunk = (g.K + parts * BK - 1) / (parts * BK) * BK;
-  // whole tiles everywhere (the K ranges included): the unguarded kernel
-  if (g.n_split != g.N && g.n_split % C::BN != 0) return hipErrorInvalidValue;  // a tile would straddle the split
-  const bool edge = g.M % C::BM != 0 || g.N % C::BN != 0 || g.K % g.kchunk != 0;
-  hipError_t e = timed_launch(s, [&] {
-    if (edge)
-      hipLaunchKernelGGL((gemm_kernel<AT, OT, FM, FN, BK, true>), dim3(tiles, parts), dim3(kThreads), 0, s, g);
-    else
-      hipLaunchKernelGGL((gemm_kernel<AT, OT, FM, FN, BK, false>), dim3(tiles, parts), dim3(kThreads), 0, s, g);
-  });
-  if (e != hipSuccess || parts == 1) return e;
-  const size_t pieces = static_cast<size_t>(g.M) * (g.N / 4);
-  hipLaunchKernelGGL((gemm_reduce<OT>), dim3(static_cast<unsigned>((pieces + 255) / 256)), dim3(256), 0, s, g, parts);
-  return hipGetLastError();
-}
+size_t split_bytes(int M, int K) { return (static_cast<size_t>(M) * K * 2 + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
+// fp32 A: its bf16 value and remainder (M x K each), and an fp32 (M x N)
+// product for a bf16 output.
 size_t gemm_workspace_bytes(int M, int N, int K, int a_dtype) {
-  const int parts = k_parts(M, N, K, a_dtype == kF32, ~static_cast<size_t>(0));
-  return parts > 1 ? static_cast<size_t>(parts) * M * N * 4 : 0;
+  if (a_dtype != kF32) return 0;
+  return 2 * split_bytes(M, K) + static_cast<size_t>(M) * N * 4;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int a_dtype, int out_dtype, hipStream_t stream) {
-  if (a_dtype == kBF16) return out_dtype == kBF16 ? go<bf16s, bf16s>(g, stream) : go<bf16s, float>(g, stream);
-  return out_dtype == kBF16 ? go<float, bf16s>(g, stream) : go<float, float>(g, stream);
+  if (g.M == 0 || g.N == 0) return hipSuccess;
+  hipError_t r = hipSuccess;  // the library calls' status (timed_launch reports launch errors)
+  if (a_dtype == kBF16) {
+    const uint16_t* A = static_cast<const uint16_t*>(g.A);
+    const int n0 = g.C1 ? g.n_split : g.N;
+    const hipError_t e = timed_launch(stream, [&] {
+      r = matmul(A, g.lda, g.W, g.ldw, g.C0, g.ldc0, g.M, n0, g.K, out_dtype, false, stream);
+      if (r == hipSuccess && g.C1)
+        r = matmul(A, g.lda, g.W + static_cast<size_t>(n0) * g.ldw, g.ldw, g.C1, g.ldc1, g.M, g.N - n0, g.K,
+                   out_dtype, false, stream);
+    });
+    return r != hipSuccess ? r : e;
+  }
+  // fp32 A: split, then value and remainder products accumulated in fp32
+  if (g.C1 || g.K % 4 != 0 || g.lda % 4 != 0 || g.N % 4 != 0) return hipErrorInvalidValue;
+  if (g.ws == nullptr || g.ws_bytes < gemm_workspace_bytes(g.M, g.N, g.K, kF32)) return hipErrorInvalidValue;
+  char* ws = reinterpret_cast<char*>(g.ws);
+  uint16_t* hi = reinterpret_cast<uint16_t*>(ws);
+  uint16_t* lo = reinterpret_cast<uint16_t*>(ws + split_bytes(g.M, g.K));
+  float* tmp = reinterpret_cast<float*>(ws + 2 * split_bytes(g.M, g.K));
+  hipLaunchKernelGGL(split_hi_lo, dim3(blocks_for(static_cast<size_t>(g.M) * (g.K / 4))), dim3(256), 0, stream,
+                     static_cast<const float*>(g.A), g.lda, g.M, g.K, hi, lo);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool direct = out_dtype == kF32;
+  void* D = direct ? g.C0 : tmp;
+  const int ldd = direct ? g.ldc0 : g.N;
+  e = timed_launch(stream, [&] {
+    r = matmul(hi, g.K, g.W, g.ldw, D, ldd, g.M, g.N, g.K, kF32, false, stream);
+    if (r == hipSuccess) r = matmul(lo, g.K, g.W, g.ldw, D, ldd, g.M, g.N, g.K, kF32, true, stream);
+  });
+  if (r != hipSuccess) return r;
+  if (e != hipSuccess || direct) return e;
+  hipLaunchKernelGGL(to_bf16, dim3(blocks_for(static_cast<size_t>(g.M) * (g.N / 4))), dim3(256), 0, stream, tmp, g.M,
+                     g.N, static_cast<uint16_t*>(g.C0), g.ldc0);
+  return hipGetLastError();
 }
 
 }  // namespace ssm

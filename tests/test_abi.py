@@ -295,15 +295,20 @@ def test_linear_validation(L):
         "out_over_w": (_lin(out=_addr(2) + 4096), 1),
         "ws_align": (_lin(workspace=_addr(4) + 16, workspace_bytes=1 << 20), 1),
         "ws_over_out": (_lin(workspace=_addr(3) + 256, workspace_bytes=1 << 20), 1),
+        "ws_missing_f32": (_lin(x_dtype=0), 3),
+        "ws_short_f32": (_lin(x_dtype=0, workspace=_addr(4), workspace_bytes=1 << 20), 3),
     }
     for name, (p, want) in cases.items():
         assert L.ssm_linear_check(ctypes.byref(p)) == want, (name, L.ssm_last_error())
     assert L.ssm_linear_fwd(ctypes.byref(_lin(rows=0, x=None, out=None)), None) == 0
     assert L.ssm_linear_fwd(ctypes.byref(_lin(in_features=12)), None) == 2
-    # the in_proj shape fills the GPU with tiles: no workspace; out_proj does not
+    # a bf16 input needs no workspace; an fp32 input its bf16 value and
+    # remainder (rows x in_features each) and an fp32 product
+    L.ssm_linear_workspace_size.restype = ctypes.c_size_t
     assert L.ssm_linear_workspace_size(ctypes.byref(_lin())) == 0
-    big = L.ssm_linear_workspace_size(ctypes.byref(_lin(in_features=7680, out_features=2560)))
-    assert big > 0 and big % (2048 * 2560 * 4) == 0
+    assert L.ssm_linear_workspace_size(ctypes.byref(_lin(in_features=7680, out_features=2560))) == 0
+    f32 = L.ssm_linear_workspace_size(ctypes.byref(_lin(in_features=7680, out_features=2560, x_dtype=0)))
+    assert f32 == 2 * 2048 * 7680 * 2 + 2048 * 2560 * 4
 
 
 def _layer(**kw):
