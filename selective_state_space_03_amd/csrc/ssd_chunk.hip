@@ -31,7 +31,7 @@
 // headdim strips, and for each block J <= I
 //   cb^T block     = B_J C_I^T              v_mfma_f32_16x16x32_bf16
 //   M (masked)     = cb . 2^(dA_l - dA_s) . dt_s, the skip D on its diagonal
-//   out^T[strip]  += X_J^T M^T              v_mfma_f32_16x16x16_bf16, M hi + lo
+//   out^T[strip]  += X_J^T M^T              v_mfma_f32_16x16x32_bf16, M hi + lo as K = 32
 // then the readout of the incoming state, (S C_I^T) scaled by 2^dA[l]
 // (v_mfma_f32_16x16x32_bf16, S split hi + lo), and the state update
 //   S <- 2^dA[Q-1] S + X^T (w . B)          v_mfma_f32_16x16x32_bf16, w.B hi + lo
@@ -613,12 +613,14 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
       uint32_t h01, l01, h23, l23;
       split2(m[0], m[1], h01, l01);
       split2(m[2], m[3], h23, l23);
-      const s16x4 mhi = __builtin_bit_cast(s16x4, make_uint2(h01, h23));
-      const s16x4 mlo = __builtin_bit_cast(s16x4, make_uint2(l01, l23));
+      // hi and lo as one K = 32 product: the lane's k slots 0-3 carry
+      // (x, M hi) and slots 4-7 (x, M lo) for the same four s
+      const bf16x8 mhl = __builtin_bit_cast(bf16x8, make_uint4(h01, h23, l01, l23));
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(o.xv[t], mhi, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(o.xv[t], mlo, acc[t], 0, 0, 0);
+        const uint2 xu = __builtin_bit_cast(uint2, o.xv[t]);
+        const bf16x8 xx = __builtin_bit_cast(bf16x8, make_uint4(xu.x, xu.y, xu.x, xu.y));
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xx, mhl, acc[t], 0, 0, 0);
       }
     };
     auto item = [&](const int I, const bf16x8 (&ci)[2], f32x4 (&acc)[NS], auto fac) {
