@@ -102,8 +102,8 @@ typedef enum {
  *   workspace     device scratch of at least ssm_scan_workspace_size(p) bytes (may be
  *                 NULL when that size is 0); 256-byte aligned; not touched by other calls
  *   time_split    0: the library chooses; >= 1: split the sequence into at most that
- *                 many segments scanned in parallel and combined (at most 32; each
- *                 segment keeps at least 4 steps)
+ *                 many segments scanned in parallel and combined (at most 32; every
+ *                 segment but the last spans a multiple of 8 steps)
  *   discretization SSM_EULER or SSM_ZOH (see ssm_discretization_t)
  * Supported: N = 16.  L = 0 only copies the state/cache inputs to the outputs.
  * ---------------------------------------------------------------------- */

@@ -86,11 +86,13 @@ ssm_status_t check_dt_bounds(float lo, float hi) {
 // (the summary pass and the composition cost a fixed amount per segment), and
 // every segment past the first starts at t >= 4, so only the first reads the
 // conv cache (which the last one may overwrite in place).
-// Segment length for s segments: ceil(L / s) rounded up to whole tiles, so
-// only the last segment of a sequence ends inside a tile.
+// Segment length for s segments: ceil(L / s) rounded up to whole rescaling
+// periods of the scaled-state form (two load tiles), so every segment starts
+// where the rescaled B/C rows start a period and only the last one ends
+// inside it.
 int scan_seg_len(int L, int s) {
   const int seg = (L + s - 1) / s;
-  return (seg + ssm::kScanBlk - 1) / ssm::kScanBlk * ssm::kScanBlk;
+  return (seg + ssm::kScanResc - 1) / ssm::kScanResc * ssm::kScanResc;
 }
 
 // The kernel variant a call selects (what the occupancy depends on).
@@ -698,6 +700,16 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_params_t* p, void* stream) {
   l.B = p->B;
   l.C = p->C;
   l.bc_out = static_cast<float*>(p->workspace);
+  // the scaled-state form needs a finite upper clip (its rescaling factors are
+  // powers of exp(dt_max A)); the kernels also check, per wave, that A is the
+  // same in every channel and that the factors stay in range
+  if (p->discretization == SSM_EULER && std::isfinite(p->dt_max) && p->seqlen > 0 && p->batch > 0) {
+    char* ws = static_cast<char*>(p->workspace);
+    l.bcg_out = reinterpret_cast<float*>(ws + ssm::scan_bcg_offset(p->batch, p->seqlen));
+    l.qtab_out = reinterpret_cast<float*>(ws + ssm::scan_qtab_offset(p->batch, p->seqlen));
+  }
+  k.bcg = l.bcg_out;
+  k.qtab = l.qtab_out;
   if (p->batch == 0) return ok();
   return hip_status(ssm::launch_scan(l, static_cast<hipStream_t>(stream)));
 }

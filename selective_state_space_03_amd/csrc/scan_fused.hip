@@ -20,7 +20,8 @@
 // segment, issued as a buffer load whose per-lane offset never changes (the
 // step's position travels in the scalar offset).  B_t and C_t are the same for
 // every channel of a batch row: they are packed once into 128-byte fp32 rows
-// that each step reads with scalar loads (see scan_fused_impl.h).
+// (plain, and rescaled for the scaled-state form) that each step reads with
+// scalar loads (see scan_fused_impl.h).
 //
 // Time split (nseg > 1): launch 1 reduces segments 0..nseg-2 to their
 // summaries (segment 0 from the true initial state, the others from zero);
@@ -33,15 +34,34 @@
 namespace ssm {
 namespace {
 
-// Pack B and C (bf16 or fp32) into fp32 rows [B0..B15, C0..C15].
+// Pack B and C (bf16 or fp32) into fp32 rows [B0..B15, C0..C15].  With
+// outg: also the rows of the scaled-state form, B_t[n] q_n^-(j+1) and
+// C_t[n] q_n^(j+1) with q_n = exp(dt_max A[0, n]) and j = t mod kScanResc,
+// and the table qtab[k][n] = q_n^k (k = 0..kScanResc).  The factors are
+// exponentials taken in double precision and rounded once, so a product
+// q^-(i+1) q^(j+1) or q^-(i+1) q^k is the decay over its steps to within a
+// few fp32 roundings.  The grid has at least 256 threads, so the table is
+// always complete.
 template <typename BT>
 __global__ void pack_bc_kernel(const BT* __restrict__ B, const BT* __restrict__ C, float* __restrict__ out,
-                               size_t rows) {
+                               float* __restrict__ outg, float* __restrict__ qtab, const float* __restrict__ A,
+                               float dt_max, int seqlen, size_t rows) {
   const size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
+  if (outg && i < static_cast<size_t>(kScanTab)) {
+    const int k = static_cast<int>(i) / kScanN, n = static_cast<int>(i) % kScanN;
+    qtab[i] = static_cast<float>(exp(static_cast<double>(k) * dt_max * A[n]));
+  }
   if (i >= rows * kBcRow) return;
   const size_t row = i / kBcRow;
   const int col = static_cast<int>(i % kBcRow);
-  out[i] = col < kScanN ? to_f32(B[row * kScanN + col]) : to_f32(C[row * kScanN + col - kScanN]);
+  const float v = col < kScanN ? to_f32(B[row * kScanN + col]) : to_f32(C[row * kScanN + col - kScanN]);
+  out[i] = v;
+  if (outg) {
+    const int j = static_cast<int>(row % static_cast<size_t>(seqlen)) % kScanResc + 1;
+    const int n = col % kScanN;
+    const double e = (col < kScanN ? -j : j) * static_cast<double>(dt_max) * A[n];
+    outg[i] = static_cast<float>(static_cast<double>(v) * exp(e));
+  }
 }
 
 // One row more than there are tokens: each step also loads the next step's
@@ -50,6 +70,7 @@ size_t bc_bytes(int batch, int seqlen) {
   const size_t rows = static_cast<size_t>(batch) * seqlen + 1;
   return (rows * kBcRow * sizeof(float) + 255) & ~static_cast<size_t>(255);
 }
+constexpr size_t kQtabBytes = (kScanTab * sizeof(float) + 255) & ~static_cast<size_t>(255);
 
 // Affine composition of the segment summaries, one thread per (batch,
 // channel, state): slot 0 already holds segment 0's end state (it started from
@@ -97,7 +118,7 @@ hipError_t launch_scan_compose(const ScanKernelArgs& a, hipStream_t stream) {
 
 size_t scan_workspace_bytes(int batch, int seqlen, int dim, int nseg) {
   if (batch <= 0 || seqlen <= 0) return 0;
-  size_t bytes = bc_bytes(batch, seqlen);
+  size_t bytes = scan_summary_offset(batch, seqlen);
   if (nseg > 1) {
     const size_t groups = static_cast<size_t>(batch) * ((dim + 63) / 64);
     bytes += groups * (nseg - 1) * (kScanN + 1) * 64 * sizeof(float);
@@ -105,7 +126,9 @@ size_t scan_workspace_bytes(int batch, int seqlen, int dim, int nseg) {
   return bytes;
 }
 
-size_t scan_summary_offset(int batch, int seqlen) { return bc_bytes(batch, seqlen); }
+size_t scan_bcg_offset(int batch, int seqlen) { return bc_bytes(batch, seqlen); }
+size_t scan_qtab_offset(int batch, int seqlen) { return 2 * bc_bytes(batch, seqlen); }
+size_t scan_summary_offset(int batch, int seqlen) { return 2 * bc_bytes(batch, seqlen) + kQtabBytes; }
 
 long scan_resident_waves(const ScanLaunch& l) {
   // CU count per device, asked once (no runtime query inside stream capture)
@@ -133,10 +156,12 @@ hipError_t launch_scan(const ScanLaunch& l, hipStream_t stream) {
     const unsigned blocks = static_cast<unsigned>((total + threads - 1) / threads);
     if (l.bc_dtype == kBF16) {
       hipLaunchKernelGGL(pack_bc_kernel<bf16s>, dim3(blocks), dim3(threads), 0, stream,
-                         static_cast<const bf16s*>(l.B), static_cast<const bf16s*>(l.C), l.bc_out, rows);
+                         static_cast<const bf16s*>(l.B), static_cast<const bf16s*>(l.C), l.bc_out, l.bcg_out,
+                         l.qtab_out, l.k.A, l.k.dt_max, l.k.seqlen, rows);
     } else {
       hipLaunchKernelGGL(pack_bc_kernel<float>, dim3(blocks), dim3(threads), 0, stream,
-                         static_cast<const float*>(l.B), static_cast<const float*>(l.C), l.bc_out, rows);
+                         static_cast<const float*>(l.B), static_cast<const float*>(l.C), l.bc_out, l.bcg_out,
+                         l.qtab_out, l.k.A, l.k.dt_max, l.k.seqlen, rows);
     }
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -29,6 +29,21 @@
 // small launch composes them in order into every segment's incoming state
 // (scan_fused.hip), and launch 3 runs all segments in full.  Summaries travel
 // through the workspace.
+//
+// Scaled-state form.  When A[e, n] is the same in all channels of the wave
+// (A[e, n] = A[0, n]; the initialisation A_log = log(1..N) has this) and dt
+// has a finite upper clip, the upper-clip decay q_n = exp(dt_max A[0, n]) is
+// uniform across the wave.  Inside a period of kScanResc steps starting at
+// t0 the lane keeps g_n = h_n(t) q_n^-(t - t0 + 1) instead of h_n(t); then
+//   g_n <- g_n + dt u B'_n                    (step at the upper clip)
+//   g_n <- g_n exp((dt - dt_max) A[e, n]) + dt u B'_n   (any other step)
+//   y = sum_n C'_n g_n + D u
+// with B'_n = B_n q_n^-(t - t0 + 1) and C'_n = C_n q_n^(t - t0 + 1) taken
+// from the rescaled rows, and at the end of the period h_n = g_n q_n^k for the
+// k steps taken.  It is the same recurrence regrouped: the decay of a step
+// moves into the row factors, so a step at the clip costs one FMA per state
+// for the update instead of a multiply and an FMA.  The factors stay within
+// exp(+-32) (checked per wave, else the plain form runs).
 #include <type_traits>
 
 #include "ssm_device.h"
@@ -38,6 +53,7 @@ namespace ssm {
 namespace {
 
 constexpr int kBlk = kScanBlk;          // steps per block: one tile of vector loads
+constexpr unsigned kCuSlots = 256;      // compute units the workgroups go round (MI355X)
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any range: the store is dropped
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
 
@@ -128,6 +144,8 @@ struct Scan {
   const LaneCtx c;
   rsrc_t rx, rz, rdt, ry;
   const cfloat* rows;              // this batch row's packed B/C rows (constant memory)
+  const cfloat* rows_g;            // the same rows rescaled for the scaled-state form
+  const cfloat* qtab;              // q_n^k as [k][n], k = 0..kScanResc
   uint32_t vo_x[kBlk];             // per-lane byte offset of step i of a tile (x and z)
   uint32_t vo_d[kBlk];             // the same for an E-wide dt of another element size
   uint32_t vy;                     // per-lane byte offset in a y row; out of range for idle lanes
@@ -157,6 +175,8 @@ struct Scan {
       rb_dt = 4;
     }
     rows = (const cfloat*)(a.bc + tok0 * kBcRow);
+    rows_g = (const cfloat*)(a.bcg ? a.bcg + tok0 * kBcRow : a.bc);
+    qtab = (const cfloat*)(a.qtab ? a.qtab : a.bc);
 #pragma unroll
     for (int i = 0; i < kBlk; ++i) {
       vo_x[i] = static_cast<uint32_t>(c.e) * XIO::bytes + i * rb_x;
@@ -202,9 +222,10 @@ struct Scan {
   }
 
   // B_t (the first half of the packed row of step t) into SGPRs: wave-uniform
-  // scalar loads.
+  // scalar loads.  G: the rescaled row.
+  template <bool G>
   __device__ __forceinline__ void load_b(int t, float (&bv)[kScanN]) const {
-    const cfloat* row = rows + static_cast<size_t>(t) * kBcRow;
+    const cfloat* row = (G ? rows_g : rows) + static_cast<size_t>(t) * kBcRow;
 #pragma unroll
     for (int n = 0; n < kScanN; ++n) bv[n] = row[n];
   }
@@ -214,15 +235,19 @@ struct Scan {
   // its latency is covered by the row-independent work at the start of the
   // next step and at most one row of each is held in SGPRs.  FULL: readout,
   // skip, gate, store.  Otherwise state update only and the running sum of
-  // dt for the segment's decay product.
-  template <bool POW, bool FULL>
+  // dt for the segment's decay product.  G: h holds the scaled state g and
+  // the rows are the rescaled ones.
+  template <bool POW, bool FULL, bool G>
   __device__ __forceinline__ void step(int t, const Tile& T, int i, float (&h)[kScanN], float (&win)[3],
                                        float& sdt, const float (&asat)[kScanN], const float (&zsat)[kScanN],
-                                       float (&bv)[kScanN]) const {
+                                       float (&bv)[kScanN], float (&bn)[kScanN]) const {
     constexpr bool has_z = FULL && GATE;
+    // the summary pass holds no C row, so its B rows are double-buffered:
+    // B_{t+1} is requested a whole step before it is used
+    if (!FULL) load_b<G>(t + 1, bn);
     float cv[kScanN];
     if (FULL) {
-      const cfloat* row = rows + static_cast<size_t>(t) * kBcRow;
+      const cfloat* row = (G ? rows_g : rows) + static_cast<size_t>(t) * kBcRow;
 #pragma unroll
       for (int n = 0; n < kScanN; ++n) cv[n] = row[kScanN + n];
     }
@@ -243,9 +268,14 @@ struct Scan {
     // computed for the step.  Both branches update h in place
     // (h = (a h) + dt u B).
     const float gate = has_z ? silu(XIO::f32(T.z[i])) : 1.0f;
+    // G: the branches only set dt u and, off the clip, scale g in place; the
+    // FMA with B' after them is common, so g stays in one set of registers
+    float dtu_g = 0.0f;
     if (__all(pre >= sat_pre)) {
       if (!FULL) sdt += dt_max;
-      if (ZOH) {
+      if (G) {
+        dtu_g = dt_max * u;
+      } else if (ZOH) {
 #pragma unroll
         for (int n = 0; n < kScanN; ++n) h[n] = fmaf(zsat[n] * u, bv[n], asat[n] * h[n]);
       } else {
@@ -268,8 +298,9 @@ struct Scan {
       if (!FULL) sdt += dt;
       const float dtu = dt * u;
       float dA[kScanN];
-      decay<POW>(dt, c.al0, al2, dA);
-      if (ZOH) {
+      // G: the decay relative to the clip's, exp((dt - dt_max) A) >= 1
+      decay<POW>(G ? dt - dt_max : dt, c.al0, al2, dA);
+      if (ZOH && !G) {
         const int lane = threadIdx.x & 63;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -282,6 +313,10 @@ struct Scan {
             h[n] = fmaf(coef * u, bv[n], dA[n] * h[n]);
           }
         }
+      } else if (G) {
+        dtu_g = dtu;
+#pragma unroll
+        for (int n = 0; n < kScanN; ++n) h[n] *= dA[n];
       } else {
 #pragma unroll
         for (int n = 0; n < kScanN; ++n) h[n] = fmaf(dtu, bv[n], dA[n] * h[n]);
@@ -291,6 +326,10 @@ struct Scan {
 #pragma unroll
       for (int n = 0; n < kScanN; ++n) asm volatile("" : "+v"(h[n]));
     }
+    if (G) {
+#pragma unroll
+      for (int n = 0; n < kScanN; ++n) h[n] = fmaf(dtu_g, bv[n], h[n]);
+    }
     if (!FULL) {
       // nothing reads the state between steps of the summary pass; pin it
       // here, or the compiler interleaves several steps of the recurrence and
@@ -299,52 +338,69 @@ struct Scan {
       for (int n = 0; n < kScanN; ++n) asm volatile("" : "+v"(h[n]));
     }
     if (FULL) {
+      // B_t is dead once the state is updated: B_{t+1} goes into the same
+      // registers now, and its latency is covered by the readout, the store
+      // and the start of the next step
+      __builtin_amdgcn_sched_barrier(0);
+      load_b<G>(t + 1, bv);
       float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int n = 0; n < kScanN; ++n) acc[n & 3] = fmaf(cv[n], h[n], acc[n & 3]);
       const float yv = fmaf(c.d, u, (acc[0] + acc[1]) + (acc[2] + acc[3])) * gate;
       YIO::store(yv, ry, vy, static_cast<uint32_t>(t) * rb_y);
     }
-    load_b(t + 1, bv);
   }
 
   // The kBlk steps of a full tile.  The scheduling barrier keeps each step's
   // scalar loads inside the step (hoisted across steps they would need a
   // second set of SGPRs).
-  template <bool POW, bool FULL>
+  template <bool POW, bool FULL, bool G>
   __device__ __forceinline__ void block(int tb, const Tile& T, float (&h)[kScanN], float (&win)[3],
                                         float& sdt, const float (&asat)[kScanN], const float (&zsat)[kScanN],
-                                        float (&bv)[kScanN]) const {
+                                        float (&bv0)[kScanN], float (&bv1)[kScanN]) const {
+    static_assert(kBlk % 2 == 0, "every tile starts with B in the first buffer");
 #pragma unroll
     for (int i = 0; i < kBlk; ++i) {
-      step<POW, FULL>(tb + i, T, i, h, win, sdt, asat, zsat, bv);
+      if (FULL || (i & 1) == 0) step<POW, FULL, G>(tb + i, T, i, h, win, sdt, asat, zsat, bv0, bv1);
+      else step<POW, FULL, G>(tb + i, T, i, h, win, sdt, asat, zsat, bv1, bv0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   // The steps tb .. t1-1 (fewer than kBlk) of an already loaded tile.
-  template <bool POW, bool FULL>
+  template <bool POW, bool FULL, bool G>
   __device__ __forceinline__ void partial(int tb, int t1, const Tile& T, float (&h)[kScanN], float (&win)[3],
                                           float& sdt, const float (&asat)[kScanN], const float (&zsat)[kScanN],
-                                        float (&bv)[kScanN]) const {
+                                          float (&bv0)[kScanN], float (&bv1)[kScanN]) const {
 #pragma unroll
     for (int i = 0; i < kBlk - 1; ++i) {
-      if (tb + i < t1) step<POW, FULL>(tb + i, T, i, h, win, sdt, asat, zsat, bv);
+      if (tb + i < t1) {
+        if (FULL || (i & 1) == 0) step<POW, FULL, G>(tb + i, T, i, h, win, sdt, asat, zsat, bv0, bv1);
+        else step<POW, FULL, G>(tb + i, T, i, h, win, sdt, asat, zsat, bv1, bv0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   // Scan steps [t0, t1) from state h.  Two tiles alternate: while one is
   // consumed the next one's loads are in flight, and as the roles swap by
-  // program position no register copy ever waits on a load.
-  template <bool POW, bool FULL>
+  // program position no register copy ever waits on a load.  G: the
+  // scaled-state form (t0 is a multiple of kScanResc = 2 tiles); h is
+  // rescaled back after every pair of tiles and at the end.
+  template <bool POW, bool FULL, bool G>
   __device__ __forceinline__ void run(int t0, int t1, float (&h)[kScanN], float (&win)[3], float& sdt) const {
+    static_assert(kScanResc == 2 * kBlk, "a rescaling period is the loop's pair of tiles");
     if (t0 >= t1) return;
     const int nfull = (t1 - t0) / kBlk;
     float asat[kScanN];             // exp(dt_max A[e, n]): the decay on the upper clip
-    decay<POW>(dt_max, c.al0, al2, asat);
+    if (G) {
+#pragma unroll
+      for (int n = 0; n < kScanN; ++n) asat[n] = 0.0f;
+    } else {
+      decay<POW>(dt_max, c.al0, al2, asat);
+    }
     float zsat[kScanN];             // ZOH: (exp(dt_max A[e, n]) - 1) / A[e, n]
-    if (ZOH) {
+    if (ZOH && !G) {
       const int lane = threadIdx.x & 63;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -357,8 +413,8 @@ struct Scan {
 #pragma unroll
       for (int n = 0; n < kScanN; ++n) zsat[n] = 0.0f;
     }
-    float bv[kScanN];               // B of the current step
-    load_b(t0, bv);
+    float bv[kScanN], bw[kScanN];   // B of the current step (and, summary pass, of the next)
+    load_b<G>(t0, bv);
     Tile A, B;
     load_block<FULL>(t0, A);
     int tb = t0;
@@ -366,27 +422,60 @@ struct Scan {
 #pragma unroll 1
     for (; k + 2 <= nfull; k += 2) {
       load_block<FULL>(tb + kBlk, B);
-      block<POW, FULL>(tb, A, h, win, sdt, asat, zsat, bv);
+      block<POW, FULL, G>(tb, A, h, win, sdt, asat, zsat, bv, bw);
       load_block<FULL>(tb + 2 * kBlk, A);
-      block<POW, FULL>(tb + kBlk, B, h, win, sdt, asat, zsat, bv);
+      block<POW, FULL, G>(tb + kBlk, B, h, win, sdt, asat, zsat, bv, bw);
+      if (G) {
+        // h = g q^kScanResc: the period is over
+#pragma unroll
+        for (int n = 0; n < kScanN; ++n) h[n] *= qtab[kScanResc * kScanN + n];
+      }
       tb += 2 * kBlk;
     }
     if (k < nfull) {
       load_block<FULL>(tb + kBlk, B);
-      block<POW, FULL>(tb, A, h, win, sdt, asat, zsat, bv);
-      partial<POW, FULL>(tb + kBlk, t1, B, h, win, sdt, asat, zsat, bv);
+      block<POW, FULL, G>(tb, A, h, win, sdt, asat, zsat, bv, bw);
+      partial<POW, FULL, G>(tb + kBlk, t1, B, h, win, sdt, asat, zsat, bv, bw);
     } else {
-      partial<POW, FULL>(tb, t1, A, h, win, sdt, asat, zsat, bv);
+      partial<POW, FULL, G>(tb, t1, A, h, win, sdt, asat, zsat, bv, bw);
     }
+    if (G) {
+      // the t1 - tb (< kScanResc) steps of the last, unfinished period
+      const cfloat* q = qtab + (t1 - tb) * kScanN;
+#pragma unroll
+      for (int n = 0; n < kScanN; ++n) h[n] *= q[n];
+    }
+  }
+
+  // run() in the variant the wave qualifies for (no scaled-state form with ZOH)
+  template <bool FULL>
+  __device__ __forceinline__ void run_any(bool pow, bool g, int t0, int t1, float (&h)[kScanN], float (&win)[3],
+                                          float& sdt) const {
+    if constexpr (!ZOH) {
+      if (g) {
+        if (pow) run<true, FULL, true>(t0, t1, h, win, sdt);
+        else run<false, FULL, true>(t0, t1, h, win, sdt);
+        return;
+      }
+    }
+    if (pow) run<true, FULL, false>(t0, t1, h, win, sdt);
+    else run<false, FULL, false>(t0, t1, h, win, sdt);
   }
 };
 
 template <typename XT, typename YT, int DTM, bool CONV, bool GATE, bool ZOH, int MODE>
 __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
   const int lane = threadIdx.x;
-  // block -> (segment, batch, channel group), channel groups fastest: the
-  // neighbouring workgroups, spread over the XCDs, share their B/C rows.
-  int bid = blockIdx.x;
+  // block -> (segment, batch, channel group).  Workgroups are handed out
+  // round-robin, so block i runs on compute unit i % kCuSlots (8 XCDs x 32
+  // CUs on MI355X, measured) in round i / kCuSlots.  The blocks of one CU
+  // get consecutive positions of the (segment, batch, channel group) order,
+  // channel groups fastest, so the waves a CU holds walk the same B/C rows
+  // and find them in its scalar cache.  Any CU count gives a bijection.
+  const unsigned nblk = gridDim.x;
+  const unsigned full = nblk / kCuSlots, rem = nblk % kCuSlots;
+  const unsigned slot = blockIdx.x % kCuSlots, round = blockIdx.x / kCuSlots;
+  int bid = static_cast<int>(slot * full + min(slot, rem) + round);
   const int g = uniform(bid % a.n_egroups);
   bid /= a.n_egroups;
   LaneCtx c;
@@ -398,13 +487,18 @@ __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
 
   __shared__ float4 s_al2[4 * 64];
   bool prog = true;
+  bool same = true;    // A[e, :] = A[0, :]
+  float span = 0.0f;   // max_n |A[0, n]|
   const float a0 = a.A[static_cast<size_t>(c.e) * kScanN];
   float al2v[kScanN];
 #pragma unroll
   for (int n = 0; n < kScanN; ++n) {
     const float an = a.A[static_cast<size_t>(c.e) * kScanN + n];
+    const float ar = a.A[n];
     al2v[n] = an * kLog2e;
     prog = prog && (an == static_cast<float>(n + 1) * a0);
+    same = same && (an == ar);
+    span = fmaxf(span, fabsf(ar));
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -423,6 +517,9 @@ __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
     c.cw0 = c.cw1 = c.cw2 = c.cw3 = c.cb = 0.0f;
   }
   const bool use_pow = __all(prog);
+  // the scaled-state form: rescaled rows present (finite dt_max, Euler), A
+  // the same in every channel of the wave, factors within exp(+-32)
+  const bool use_g = !ZOH && a.bcg != nullptr && __all(same) && kScanResc * a.dt_max * span <= 32.0f;
   const Scan<XT, YT, DTM, CONV, GATE, ZOH> S(a, c, s_al2);
   const int t0 = seg * a.seg_len;
   const int t1 = min(t0 + a.seg_len, a.seqlen);
@@ -452,16 +549,14 @@ __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
   if (MODE == kPass1) {
     // summary of segments 0..nseg-2: the end state from the true initial state
     // (segment 0) or from zero (the others), and the sum of dt
-    if (use_pow) S.template run<true, false>(t0, t1, h, win, sdt);
-    else S.template run<false, false>(t0, t1, h, win, sdt);
+    S.template run_any<false>(use_pow, use_g, t0, t1, h, win, sdt);
     float* ss = summ + static_cast<size_t>(seg) * (kScanN + 1) * 64;
 #pragma unroll
     for (int n = 0; n < kScanN; ++n) ss[n * 64 + lane] = h[n];
     ss[kScanN * 64 + lane] = sdt;
     return;
   }
-  if (use_pow) S.template run<true, true>(t0, t1, h, win, sdt);
-  else S.template run<false, true>(t0, t1, h, win, sdt);
+  S.template run_any<true>(use_pow, use_g, t0, t1, h, win, sdt);
   if (seg == a.nseg - 1 && c.act) {
     if (a.state_out) {
 #pragma unroll

@@ -33,12 +33,18 @@ hipError_t timed_launch(hipStream_t s, F&& launch) {
 
 // ---- fused scan ----------------------------------------------------------
 // B and C are repacked per (batch, t) into one fp32 row [B0..B15, C0..C15] so
-// the scan kernel reads them with wave-uniform scalar loads.
+// the scan kernel reads them with wave-uniform scalar loads.  A second set of
+// rows holds them rescaled for the scaled-state form of the recurrence (see
+// scan_fused_impl.h): B_t[n] q_n^-(j+1) and C_t[n] q_n^(j+1), where
+// q_n = exp(dt_max A[0, n]) and j = t mod kScanResc, next to a table of q_n^k
+// for k = 0..kScanResc.
 constexpr int kScanN = 16;         // d_state handled by the fused scan
 constexpr int kBcRow = 32;         // floats per packed row
 constexpr int kScanMaxSplit = 32;  // time segments per sequence
 constexpr int kConvK = 4;
 constexpr int kScanBlk = 4;        // steps per tile of prefetched vector loads
+constexpr int kScanResc = 2 * kScanBlk;  // steps between rescalings of the scaled state (a pair of tiles); segments start at multiples of it
+constexpr int kScanTab = (kScanResc + 1) * kScanN;  // floats of the q_n^k table
 
 struct ScanKernelArgs {
   const void* x;
@@ -46,6 +52,8 @@ struct ScanKernelArgs {
   const void* dt;        // rank-1 r (batch, seqlen) f32, or full (batch, seqlen, dim)
   void* y;
   const float* bc;       // packed rows (batch*seqlen + padding, kBcRow)
+  const float* bcg;      // the rescaled rows, same shape; null: no scaled-state form
+  const float* qtab;     // q_n^k, [k][n] for k = 0..kScanResc
   float* summ;           // per-segment summaries (time split only)
   const float* A;        // (dim, 16)
   const float* D;        // (dim) or null
@@ -70,7 +78,9 @@ struct ScanLaunch {
   bool zoh;     // zero-order-hold input coefficient instead of dt
   const void* B;
   const void* C;
-  float* bc_out;  // = k.bc, written by the packing kernel
+  float* bc_out;   // = k.bc, written by the packing kernel
+  float* bcg_out;  // = k.bcg (or null), written by the packing kernel
+  float* qtab_out; // = k.qtab, written by the packing kernel with bcg_out
 };
 
 struct bf16s;
@@ -85,6 +95,10 @@ int scan_occupancy_xy(const ScanLaunch& l);
 // Workgroups of the full-segment scan kernel that the current device holds at
 // once (CUs x resident workgroups per CU), or 0 when it cannot be queried.
 long scan_resident_waves(const ScanLaunch& l);
+// Workspace layout of a scan call: plain rows, rescaled rows, the q_n^k
+// table, then the segment summaries.
+size_t scan_bcg_offset(int batch, int seqlen);
+size_t scan_qtab_offset(int batch, int seqlen);
 size_t scan_summary_offset(int batch, int seqlen);
 hipError_t launch_scan(const ScanLaunch& l, hipStream_t stream);
 

@@ -62,6 +62,37 @@ def test_scan_general_A(split):
     _parity(w, TOL_F32, time_split=split)
 
 
+@pytest.mark.parametrize("unsat", [False, True])
+@pytest.mark.parametrize("split", [1, 3])
+def test_scan_uniform_A_not_power(unsat, split):
+    """A the same in every channel but not a multiple of its first entry: the
+    scaled-state form with one exponential per state on steps off the clip."""
+    w = W.scan_tiny(batch=2, seqlen=203, dim=130, unsaturated=unsat)
+    rng = np.random.Generator(np.random.PCG64(8))
+    row = -rng.uniform(0.3, 16.0, 16)
+    w.arrays["A"] = np.broadcast_to(row, w.arrays["A"].shape).astype(np.float32).copy()
+    _parity(w, TOL_F32, time_split=split)
+
+
+@pytest.mark.parametrize("split", [1, 5])
+def test_scan_mixed_waves(split):
+    """Channels 64..127 (the second wave) get their own A: that wave runs the
+    plain form while its neighbours run the scaled-state form."""
+    w = W.scan_prefill(batch=2, seqlen=300, dim=200, unsaturated=True)
+    rng = np.random.Generator(np.random.PCG64(9))
+    w.arrays["A"][64:128] = (-rng.uniform(0.3, 16.0, (64, 16))).astype(np.float32)
+    _parity(w, TOL_BF16, time_split=split)
+
+
+@pytest.mark.parametrize("dt_max", [1.0, float("inf")])
+def test_scan_wide_or_open_clip(dt_max):
+    """dt_max = 1 (kScanResc dt_max max|A| = 128 > 32) and no upper clip at
+    all: the scaled-state form is off and the plain form gives the result."""
+    w = W.scan_tiny(batch=1, seqlen=96, dim=80, unsaturated=True)
+    w.opts = dict(w.opts, dt_max=dt_max)
+    _parity(w, TOL_F32, time_split=2)
+
+
 def test_scan_fp32_with_conv():
     """All-fp32 inputs with the conv on and a conv bias-free window from a given cache."""
     w = W.scan_prefill(batch=2, seqlen=70, dim=96, unsaturated=True)
