@@ -154,9 +154,10 @@ struct Scan {
   float sat_pre;                   // pre-activations at or above this give dt = dt_max
   bool dt_softplus;
   const float4* al2;               // A[e, n] log2(e) as [n / 4][lane] float4s (LDS)
+  float4* sat4;                    // exp(dt_max A[e, n]), the same layout (LDS; plain form)
 
-  __device__ Scan(const ScanKernelArgs& a_, const LaneCtx& c_, const float4* al2_)
-      : a(a_), c(c_), al2(al2_) {
+  __device__ Scan(const ScanKernelArgs& a_, const LaneCtx& c_, const float4* al2_, float4* sat4_)
+      : a(a_), c(c_), al2(al2_), sat4(sat4_) {
     const uint32_t L = a.seqlen, E = a.dim;
     const size_t tok0 = static_cast<size_t>(c.b) * L;  // first token of this batch row
     // each descriptor covers exactly this batch row: loads past its end read 0
@@ -279,9 +280,18 @@ struct Scan {
 #pragma unroll
         for (int n = 0; n < kScanN; ++n) h[n] = fmaf(zsat[n] * u, bv[n], asat[n] * h[n]);
       } else {
+        // the clip decays come from LDS: held in registers through the loop
+        // they would cost the kernel a wave per SIMD
         const float dtu = dt_max * u;
+        const int lane = threadIdx.x & 63;
 #pragma unroll
-        for (int n = 0; n < kScanN; ++n) h[n] = fmaf(dtu, bv[n], asat[n] * h[n]);
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = sat4[q * 64 + lane];
+          h[4 * q + 0] = fmaf(dtu, bv[4 * q + 0], v.x * h[4 * q + 0]);
+          h[4 * q + 1] = fmaf(dtu, bv[4 * q + 1], v.y * h[4 * q + 1]);
+          h[4 * q + 2] = fmaf(dtu, bv[4 * q + 2], v.z * h[4 * q + 2]);
+          h[4 * q + 3] = fmaf(dtu, bv[4 * q + 3], v.w * h[4 * q + 3]);
+        }
       }
     } else {
       float dt;
@@ -398,6 +408,12 @@ struct Scan {
       for (int n = 0; n < kScanN; ++n) asat[n] = 0.0f;
     } else {
       decay<POW>(dt_max, c.al0, al2, asat);
+      if (!ZOH) {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          sat4[q * 64 + lane] = make_float4(asat[4 * q], asat[4 * q + 1], asat[4 * q + 2], asat[4 * q + 3]);
+      }
     }
     float zsat[kScanN];             // ZOH: (exp(dt_max A[e, n]) - 1) / A[e, n]
     if (ZOH && !G) {
@@ -486,6 +502,7 @@ __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
   c.e = c.act ? e_raw : a.dim - 1;
 
   __shared__ float4 s_al2[4 * 64];
+  __shared__ float4 s_sat[4 * 64];
   bool prog = true;
   bool same = true;    // A[e, :] = A[0, :]
   float span = 0.0f;   // max_n |A[0, n]|
@@ -520,7 +537,7 @@ __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
   // the scaled-state form: rescaled rows present (finite dt_max, Euler), A
   // the same in every channel of the wave, factors within exp(+-32)
   const bool use_g = !ZOH && a.bcg != nullptr && __all(same) && kScanResc * a.dt_max * span <= 32.0f;
-  const Scan<XT, YT, DTM, CONV, GATE, ZOH> S(a, c, s_al2);
+  const Scan<XT, YT, DTM, CONV, GATE, ZOH> S(a, c, s_al2, s_sat);
   const int t0 = seg * a.seg_len;
   const int t1 = min(t0 + a.seg_len, a.seqlen);
   float win[3] = {0.0f, 0.0f, 0.0f};
