@@ -208,7 +208,8 @@ ssm_status_t ssm_decode_check(const ssm_decode_params_t *p);
  * Workspace: ssm_chunk_scan_workspace_size() bytes of device memory, 256-byte
  * aligned, owned by the caller (zero when the sequences are not cut into
  * segments); its contents on entry do not matter.
- * Supported: x and B/C in bf16, N = 64, P % 16 == 0 and P <= 128, chunk_size = 128.
+ * Supported: x and B/C in bf16, N = 64, P % 16 == 0 and P <= 128, chunk_size = 128, and
+ * seqlen * max(nheads * headdim, ngroups * d_state) * 2 bytes (one batch row) below 4 GiB.
  * ---------------------------------------------------------------------- */
 typedef struct ssm_chunk_params {
   uint32_t struct_size; /* = sizeof(ssm_chunk_params_t) */

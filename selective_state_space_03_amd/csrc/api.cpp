@@ -277,6 +277,13 @@ ssm_status_t chunk_check(const ssm_chunk_params_t* p) {
   if (p->x_dtype != SSM_BF16 || p->bc_dtype != SSM_BF16)
     return fail(SSM_ERR_UNSUPPORTED, "%s must be bf16", "x_dtype/bc_dtype");
   if (p->z && !valid_dtype(p->z_dtype)) return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "z_dtype");
+  // whole chunks are read through buffer descriptors of one batch row with
+  // 32-bit byte offsets
+  if (static_cast<unsigned long long>(p->seqlen) *
+          std::max<unsigned long long>(static_cast<unsigned long long>(p->nheads) * p->headdim,
+                                       static_cast<unsigned long long>(p->ngroups) * p->d_state) * 2ull >
+      0xffffffffull)
+    return fail(SSM_ERR_UNSUPPORTED, "%s", "one batch row of x, B or C must stay below 4 GiB (seqlen too long)");
   if ((reinterpret_cast<uintptr_t>(p->x) | reinterpret_cast<uintptr_t>(p->B) | reinterpret_cast<uintptr_t>(p->C) |
        reinterpret_cast<uintptr_t>(p->out) | reinterpret_cast<uintptr_t>(p->z)) & 15)
     return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "x/B/C/out/z");

@@ -160,7 +160,9 @@ struct Scan {
       : a(a_), c(c_), al2(al2_), sat4(sat4_) {
     const uint32_t L = a.seqlen, E = a.dim;
     const size_t tok0 = static_cast<size_t>(c.b) * L;  // first token of this batch row
-    // each descriptor covers exactly this batch row: loads past its end read 0
+    // each descriptor covers this batch row (the per-lane offsets are range
+    // checked against it; the scalar step offsets stay inside it by
+    // construction, see load_block)
     rx = make_rsrc(static_cast<const char*>(a.x) + tok0 * E * XIO::bytes, L * E * XIO::bytes);
     rz = make_rsrc(static_cast<const char*>(a.z ? a.z : a.x) + tok0 * E * XIO::bytes, L * E * XIO::bytes);
     ry = make_rsrc(static_cast<char*>(a.y) + tok0 * E * YIO::bytes, L * E * YIO::bytes);
@@ -208,17 +210,30 @@ struct Scan {
   };
 
   // Loads of steps tb .. tb+kBlk-1.  Steps past the segment are loaded too
-  // (and never used); past the batch row the descriptor returns zeros.
+  // (and never used).  The buffer range check covers the per-lane offset
+  // but not the scalar one, so a tile reaching past the end of the batch row
+  // (the last one of a sequence) takes its rows one by one, clamped to the
+  // last row: every access stays inside the tensor.
   template <bool FULL>
   __device__ __forceinline__ void load_block(int tb, Tile& T) const {
     constexpr bool has_z = FULL && GATE;
-    const uint32_t sx = static_cast<uint32_t>(tb) * rb_x;
-    const uint32_t sd = static_cast<uint32_t>(tb) * rb_dt;
+    if (tb + kBlk <= a.seqlen) {
+      const uint32_t sx = static_cast<uint32_t>(tb) * rb_x;
+      const uint32_t sd = static_cast<uint32_t>(tb) * rb_dt;
 #pragma unroll
-    for (int i = 0; i < kBlk; ++i) {
-      T.x[i] = XIO::load(rx, vo_x[i], sx);
-      T.d[i] = DIO::load(rdt, kDtSharesX ? vo_x[i] : vo_d[i], kDtSharesX ? sx : sd);
-      if (has_z) T.z[i] = XIO::load(rz, vo_x[i], sx);
+      for (int i = 0; i < kBlk; ++i) {
+        T.x[i] = XIO::load(rx, vo_x[i], sx);
+        T.d[i] = DIO::load(rdt, kDtSharesX ? vo_x[i] : vo_d[i], kDtSharesX ? sx : sd);
+        if (has_z) T.z[i] = XIO::load(rz, vo_x[i], sx);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBlk; ++i) {
+        const uint32_t r = static_cast<uint32_t>(min(tb + i, a.seqlen - 1));
+        T.x[i] = XIO::load(rx, vo_x[0], r * rb_x);
+        T.d[i] = DIO::load(rdt, kDtSharesX ? vo_x[0] : vo_d[0], r * (kDtSharesX ? rb_x : rb_dt));
+        if (has_z) T.z[i] = XIO::load(rz, vo_x[0], r * rb_x);
+      }
     }
   }
 

@@ -62,6 +62,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+// 16 bytes at byte offset vo + so of a raw buffer
+__device__ __forceinline__ uint4 ld128(rsrc_t r, uint32_t vo, uint32_t so) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Column of element s in row r of the transposed tiles (Bt, Xt): the 16-byte
 // blocks of a row are permuted by the row's 8-row group, so the transposing
 // stores fall in different banks.  Reads of 4 or 8 consecutive elements
@@ -164,9 +176,74 @@ struct ChunkIo {
   static constexpr int RPT = Regs::RPT, XI = Regs::XI;
   const ChunkKernelArgs& a;
   int b, h, g;
+  // Buffer descriptors of this (batch, head)'s x, B, C and dt rows.  Whole
+  // chunks are read through them: the lane's offset is fixed for the whole
+  // walk and the chunk's position goes in the scalar offset, so a chunk's
+  // loads need no per-chunk address arithmetic.  (With 64-bit addresses
+  // formed per chunk, registers still read by loads in flight were
+  // overwritten and every such reuse waited for those loads.)
+  rsrc_t rx, rb, rc, rdt;
 
   __device__ ChunkIo(const ChunkKernelArgs& args, int b_, int h_)
-      : a(args), b(b_), h(h_), g(h_ / (args.nheads / args.ngroups)) {}
+      : a(args), b(b_), h(h_), g(h_ / (args.nheads / args.ngroups)) {
+    constexpr size_t P = 16 * NS;
+    const size_t L = a.seqlen, H = a.nheads, G = a.ngroups;
+    const size_t L1 = L > 0 ? L - 1 : 0;
+    rx = make_rsrc(static_cast<const uint16_t*>(a.x) + (b * L * H + h) * P,
+                   static_cast<uint32_t>((L1 * H * P + P) * 2));
+    rb = make_rsrc(static_cast<const uint16_t*>(a.B) + (b * L * G + g) * kN,
+                   static_cast<uint32_t>((L1 * G * kN + kN) * 2));
+    rc = make_rsrc(static_cast<const uint16_t*>(a.C) + (b * L * G + g) * kN,
+                   static_cast<uint32_t>((L1 * G * kN + kN) * 2));
+    rdt = make_rsrc(a.dt + b * L * H + h, static_cast<uint32_t>((L1 * H + 1) * 4));
+  }
+
+  // The lane's byte offsets for whole-chunk loads (io thread tid).
+  struct Offs {
+    uint32_t bc[RPT];
+    uint32_t x[XI][2];
+    uint32_t dt;
+  };
+  __device__ __forceinline__ Offs offsets(int tid) const {
+    constexpr int P = 16 * NS;
+    const int rg = tid >> 3, pc = tid & 7;
+    const int H = a.nheads, G = a.ngroups;
+    Offs o;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) o.bc[i] = static_cast<uint32_t>(((RPT * rg + i) * G * kN + 8 * pc) * 2);
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      const int q = tid + NT * i;
+      const int rgx = q / (2 * NS), pcx = q % (2 * NS);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) o.x[i][e] = static_cast<uint32_t>(((2 * rgx + e) * H * P + 8 * pcx) * 2);
+    }
+    o.dt = static_cast<uint32_t>(tid * H * 4);
+    return o;
+  }
+
+  // A whole chunk c through the descriptors (io thread tid, offsets o).
+  template <bool WITH_C, bool WITH_DT = true>
+  __device__ __forceinline__ void load_whole(int c, Regs& R, const Offs& o, int tid) const {
+    constexpr uint32_t P = 16 * NS;
+    const uint32_t H = a.nheads, G = a.ngroups;
+    const uint32_t row0 = static_cast<uint32_t>(c) * kQ;
+    const uint32_t sbc = row0 * G * kN * 2, sx = row0 * H * P * 2, sdt = row0 * H * 4;
+    R.valid = kQ;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      if constexpr (WITH_C) R.c[i] = ld128(rc, o.bc[i], sbc);
+      R.b[i] = ld128(rb, o.bc[i], sbc);
+    }
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      if (XI * NT == 128 * NS || tid + NT * i < 128 * NS) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) R.x[i][e] = ld128(rx, o.x[i][e], sx);
+      }
+    }
+    if (WITH_DT && tid < kQ) R.dt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdt, o.dt, sdt, 0));
+  }
 
   // Rows past the end of the sequence (a ragged last chunk) load as zeros;
   // their dt is set to 0 when stored, so they neither add to nor decay the
@@ -422,12 +499,21 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
       }
     };
     // dt of chunk c for state wave 0: lane holds rows 2 lane and 2 lane + 1
-    auto load_dt = [&](int c, int lane) {
+    // lane offsets of those rows in the head's dt descriptor (whole chunks)
+    const uint32_t vdt0 = static_cast<uint32_t>(2 * (threadIdx.x & 63) * H * 4);
+    const uint32_t vdt1 = vdt0 + static_cast<uint32_t>(H * 4);
+    auto load_dt = [&](int c, int lane, bool whole) {
       const size_t tok = static_cast<size_t>(b) * L + static_cast<size_t>(c) * kQ;
-      const int valid = min(kQ, L - c * kQ);
       float2 r = make_float2(0.0f, 0.0f);
-      if (2 * lane < valid) r.x = a.dt[(tok + 2 * lane) * H + h];
-      if (2 * lane + 1 < valid) r.y = a.dt[(tok + 2 * lane + 1) * H + h];
+      if (whole) {
+        const uint32_t so = static_cast<uint32_t>(c) * kQ * H * 4;
+        r.x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(io.rdt, vdt0, so, 0));
+        r.y = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(io.rdt, vdt1, so, 0));
+      } else {
+        const int valid = min(kQ, L - c * kQ);
+        if (2 * lane < valid) r.x = a.dt[(tok + 2 * lane) * H + h];
+        if (2 * lane + 1 < valid) r.y = a.dt[(tok + 2 * lane + 1) * H + h];
+      }
       return r;
     };
     // decay tables of chunk c (raw dt in dt2) into buffer buf, by state wave
@@ -462,12 +548,15 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
 
     typename Io::Regs R;
     float2 dtn = make_float2(0.0f, 0.0f);  // raw dt of the next chunk (state wave 0)
+    // dt first: the tables wait for it, and loads complete in order, so
+    // issued last it would hold the tables until the whole chunk had landed
+    const typename Io::Offs offs = io.offsets(threadIdx.x - kIoThreads);
     auto load_chunk = [&](int c, int tid) {
+      if (u == 0) dtn = load_dt(c, tid & 63, c < nfull);
       if (c >= nfull)
         io.template load<true, true, false>(c, R, tid - kIoThreads);
       else
-        io.template load<false, true, false>(c, R, tid - kIoThreads);
-      if (u == 0) dtn = load_dt(c, tid & 63);
+        io.template load_whole<true, false>(c, R, offs, tid - kIoThreads);
     };
     {
       const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
@@ -478,6 +567,11 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           S[j][r] = s_in != nullptr ? s_in[static_cast<size_t>(16 * j + 4 * lg + r) * kN + 16 * u + li] : 0.0f;
+      // the loads of S complete here on every path: otherwise the wait for
+      // them is placed at S's first use inside the chunk loop, where it runs
+      // every chunk and also waits for the next chunk's loads in flight
+#pragma unroll
+      for (int j = 0; j < NS; ++j) asm volatile("" : "+v"(S[j]));
       if (c_beg < c_end) {
         load_chunk(c_beg, threadIdx.x);
         publish_state(c_beg % NB, li, lg);
@@ -773,14 +867,15 @@ __global__ __launch_bounds__(kIoThreads) void ssd_summary_kernel(ChunkKernelArgs
   float dec = 0.0f;
 
   typename Io::Regs R;
-  if (c_beg < c_end) io.template load<false, false>(c_beg, R, tid);
+  const typename Io::Offs offs = io.offsets(tid);
+  if (c_beg < c_end) io.template load_whole<false>(c_beg, R, offs, tid);
   for (int c = c_beg; c < c_end; ++c) {
     int tid = threadIdx.x;  // opaque copy: offsets formed inside the loop (see ssd_kernel)
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
     __syncthreads();  // the previous chunk's LDS readers are done
     io.template store<false, false>(R, nullptr, nullptr, sm.Bt, sm.Xt, sm.dt, dtb, tid);
-    if (c + 1 < c_end) io.template load<false, false>(c + 1, R, tid);
+    if (c + 1 < c_end) io.template load_whole<false>(c + 1, R, offs, tid);
     __syncthreads();
     const Scan2 sc = scan_chunk(sm.dt, lane, Al2);
     if (w == 0) {

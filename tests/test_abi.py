@@ -184,6 +184,7 @@ def test_chunk_validation(L):
         "d_state": (_chunk(d_state=16), 2),
         "chunk": (_chunk(chunk_size=64, seqlen=1024), 2),
         "headdim": (_chunk(headdim=100), 2),
+        "row_over_4GiB": (_chunk(seqlen=1 << 22), 2),
         "null_A": (_chunk(A=None), 1),
         "out_over_x": (_chunk(out=_addr(1) + 2), 1),
         "out_align": (_chunk(out=_addr(6) + 8), 1),
