@@ -222,6 +222,36 @@ struct ChunkIo {
     return o;
   }
 
+  // Part k of load_whole: 0 the C rows, 1 the B rows, 2 + i the x slot i,
+  // 2 + XI the dt row.
+  template <bool WITH_C, bool WITH_DT = true>
+  __device__ __forceinline__ void load_whole_part(int c, Regs& R, const Offs& o, int tid, int k) const {
+    constexpr uint32_t P = 16 * NS;
+    const uint32_t H = a.nheads, G = a.ngroups;
+    const uint32_t row0 = static_cast<uint32_t>(c) * kQ;
+    const uint32_t sbc = row0 * G * kN * 2, sx = row0 * H * P * 2, sdt = row0 * H * 4;
+    R.valid = kQ;
+    if (k == 0) {
+      if constexpr (WITH_C) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) R.c[i] = ld128(rc, o.bc[i], sbc);
+      }
+    } else if (k == 1) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) R.b[i] = ld128(rb, o.bc[i], sbc);
+    } else if (k < 2 + XI) {
+#pragma unroll
+      for (int i = 0; i < XI; ++i) {
+        if (k == 2 + i && (XI * NT == 128 * NS || tid + NT * i < 128 * NS)) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) R.x[i][e] = ld128(rx, o.x[i][e], sx);
+        }
+      }
+    } else if (WITH_DT && tid < kQ) {
+      R.dt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdt, o.dt, sdt, 0));
+    }
+  }
+
   // A whole chunk c through the descriptors (io thread tid, offsets o).
   template <bool WITH_C, bool WITH_DT = true>
   __device__ __forceinline__ void load_whole(int c, Regs& R, const Offs& o, int tid) const {
@@ -368,10 +398,13 @@ __device__ __forceinline__ Scan2 scan_chunk(const float* dts, int lane, float Al
 // State update of the blocks (pb = pb0 + PSTRIDE j < NS, nb) a wave owns:
 // S[j] <- dlast S[j] + sum_s x[s][p] (wS[s] B[s][n]).  The lane holds
 // S[p = 16 pb + 4 lg + r][n = 16 nb + li].
-template <int NS, int NB, int PSTRIDE>
+// between(j) runs after the products of block j (the main kernel issues the
+// next chunk's loads there, a part at a time, so their issue overlaps the
+// matrix products instead of preceding them).
+template <int NS, int NB, int PSTRIDE, typename Between>
 __device__ __forceinline__ void state_update(f32x4 (&S)[NB], float dlast, const uint16_t (*Bt)[kRowQ],
                                              const uint16_t (*Xt)[kRowQ], const float* wS, int nb, int pb0, int li,
-                                             int lg) {
+                                             int lg, Between&& between) {
   const int nrow = 16 * nb + li;
   bf16x8 bwh[4], bwl[4];
 #pragma unroll
@@ -405,6 +438,7 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NB], float dlast, const 
       }
       S[j] = acc_hi + acc_lo;
     }
+    between(j);
   }
 }
 
@@ -592,10 +626,25 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
       io.template store<false, true, false>(R, sm.C, sm.B, sm.Bt, sm.Xt, nullptr, dtb, tid - kIoThreads);
       __syncthreads();
       // the next chunk's loads, in flight while the chunk is processed
-      if (c + 1 < c_end) load_chunk(c + 1, tid);
-      // ---- state update (registers); published for the next chunk once
-      // the output waves no longer read the buffer
-      state_update<NS, NS, 1>(S, sm.tb[buf].eA[kQ - 1], sm.Bt, sm.Xt, sm.tb[buf].wS, u, 0, li, lg);
+      // ---- state update (registers), with the next chunk's loads issued
+      // between its blocks (a ragged next chunk: all before it); published
+      // for the next chunk once the output waves no longer read the buffer
+      const bool more = c + 1 < c_end, whole_next = c + 1 < nfull;
+      if (more && !whole_next) load_chunk(c + 1, tid);
+      state_update<NS, NS, 1>(S, sm.tb[buf].eA[kQ - 1], sm.Bt, sm.Xt, sm.tb[buf].wS, u, 0, li, lg, [&](int j) {
+        if (more && whole_next) {
+          constexpr int kParts = 3 + Io::XI;  // C rows, B rows, the x slots, dt
+#pragma unroll
+          for (int k = 0; k < kParts; ++k)
+            if (k == j || (j == NS - 1 && k > j)) {
+              if (k == kParts - 1) {
+                if (u == 0) dtn = load_dt(c + 1, lane, true);
+              } else {
+                io.template load_whole_part<true, false>(c + 1, R, offs, tid - kIoThreads, k);
+              }
+            }
+        }
+      });
       if constexpr (NB == 2) {
         publish_state(nbuf, li, lg);
         if (u == 0 && c + 1 < c_end) tables(c + 1, nbuf, dtn, lane);
@@ -884,7 +933,7 @@ __global__ __launch_bounds__(kIoThreads) void ssd_summary_kernel(ChunkKernelArgs
     }
     dec += sc.last;
     __syncthreads();
-    state_update<NS, NS, 1>(S, exp2_fast(sc.last), sm.Bt, sm.Xt, sm.wS, w, 0, li, lg);
+    state_update<NS, NS, 1>(S, exp2_fast(sc.last), sm.Bt, sm.Xt, sm.wS, w, 0, li, lg, [](int) {});
   }
 
   const size_t bh = static_cast<size_t>(b) * a.nheads + h;
