@@ -60,15 +60,23 @@ __global__ __launch_bounds__(256) void xproj_kernel(XprojArgs a) {
   for (int jt = 0; jt < 3; ++jt) acc[jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const float* xrow = a.x + static_cast<size_t>(tok) * E;
+  // this lane's 8 channels of the token's row at e; the next step's are
+  // requested before the current step is worked on, so the stream from
+  // memory overlaps the arithmetic
+  auto load_row = [&](int e, float (&v)[8]) {
+    const float4 p0 = *reinterpret_cast<const float4*>(xrow + e);
+    const float4 p1 = *reinterpret_cast<const float4*>(xrow + e + 4);
+    v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+    v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+  };
+  float nxt[8];
+  if (e_beg < e_end) load_row(e_beg + 8 * lg, nxt);
   for (int e0 = e_beg; e0 < e_end; e0 += 32) {
     const int e = e0 + 8 * lg;  // this lane's 8 channels
     float cur[8];
-    {
-      const float4 p0 = *reinterpret_cast<const float4*>(xrow + e);
-      const float4 p1 = *reinterpret_cast<const float4*>(xrow + e + 4);
-      cur[0] = p0.x; cur[1] = p0.y; cur[2] = p0.z; cur[3] = p0.w;
-      cur[4] = p1.x; cur[5] = p1.y; cur[6] = p1.z; cur[7] = p1.w;
-    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) cur[c] = nxt[c];
+    if (e0 + 32 < e_end) load_row(e + 32, nxt);
     // rows t-1, t-2, t-3: from lanes li-1.. of this row; lanes whose source is
     // outside the row (li < k) read memory; positions before the sequence
     // start read the conv cache (oldest first) or zeros
@@ -145,6 +153,8 @@ __global__ __launch_bounds__(256) void xproj_reduce(XprojArgs a, int parts) {
   if (q >= static_cast<size_t>(T) * a.nout) return;
   const int tok = static_cast<int>(q / a.nout), j = static_cast<int>(q % a.nout);
   float s = 0.0f;
+  // loads issued eight at a time, the additions still in range order
+#pragma unroll 8
   for (int p = 0; p < parts; ++p) s += a.part[(static_cast<size_t>(p) * T + tok) * kJ + j];
   const int N = a.d_state;
   if (j < N) a.B[static_cast<size_t>(tok) * N + j] = s;
@@ -157,7 +167,7 @@ __global__ __launch_bounds__(256) void xproj_reduce(XprojArgs a, int parts) {
 int xproj_splits(int tokens, int dim) {
   const int tiles = (tokens + kTokTile - 1) / kTokTile;
   const int ksteps = dim / 32;
-  int s = std::max(1, std::min(ksteps, (512 + tiles - 1) / tiles));
+  int s = std::max(1, std::min(ksteps, (768 + tiles - 1) / tiles));  // 768 workgroups: 3 waves per SIMD
   const int per = (ksteps + s - 1) / s;
   return (ksteps + per - 1) / per;  // no empty range
 }
