@@ -396,8 +396,10 @@ __device__ __forceinline__ Scan2 scan_chunk(const float* dts, int lane, float Al
 }
 
 // State update of the blocks (pb = pb0 + PSTRIDE j < NS, nb) a wave owns:
-// S[j] <- dlast S[j] + sum_s x[s][p] (wS[s] B[s][n]).  The lane holds
-// S[p = 16 pb + 4 lg + r][n = 16 nb + li].
+// S[j] <- dlast S[j] + sum_s x[s][p] (wS[s] B[s][n]), formed as the
+// transpose (w.B)^T x so that the lane holds four consecutive n of one p:
+// S[p = 16 pb + li][n = 16 nb + 4 lg + r], which it publishes with one
+// 8-byte store per half.
 // between(j) runs after the products of block j (the main kernel issues the
 // next chunk's loads there, a part at a time, so their issue overlaps the
 // matrix products instead of preceding them).
@@ -433,8 +435,8 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NB], float dlast, const 
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const bf16x8 xa = *reinterpret_cast<const bf16x8*>(&Xt[prow][swz(prow, 32 * kk + 8 * lg)]);
-        acc_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bwh[kk], acc_hi, 0, 0, 0);
-        acc_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bwl[kk], acc_lo, 0, 0, 0);
+        acc_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwh[kk], xa, acc_hi, 0, 0, 0);
+        acc_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwl[kk], xa, acc_lo, 0, 0, 0);
       }
       S[j] = acc_hi + acc_lo;
     }
@@ -517,19 +519,17 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
   // staging of the next.
   if (sw) {
     // The state, held by the state waves: p-blocks 0..NS-1 of n-block u; the
-    // lane holds S[p = 16 j + 4 lg + r][n = 16 u + li].
+    // lane holds S[p = 16 j + li][n = 16 u + 4 lg + r].
     f32x4 S[NS];
     auto publish_state = [&](int buf, int li, int lg) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int p = 16 * j + 4 * lg + r;
-          uint16_t hi, lo;
-          split_bf16(S[j][r], hi, lo);
-          sm.Shi[buf][p][16 * u + li] = hi;
-          sm.Slo[buf][p][16 * u + li] = lo;
-        }
+        const int p = 16 * j + li, n0 = 16 * u + 4 * lg;
+        uint32_t h01, l01, h23, l23;
+        split2(S[j][0], S[j][1], h01, l01);
+        split2(S[j][2], S[j][3], h23, l23);
+        *reinterpret_cast<uint2*>(&sm.Shi[buf][p][n0]) = make_uint2(h01, h23);
+        *reinterpret_cast<uint2*>(&sm.Slo[buf][p][n0]) = make_uint2(l01, l23);
       }
     };
     // dt of chunk c for state wave 0: lane holds rows 2 lane and 2 lane + 1
@@ -600,7 +600,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
       for (int j = 0; j < NS; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          S[j][r] = s_in != nullptr ? s_in[static_cast<size_t>(16 * j + 4 * lg + r) * kN + 16 * u + li] : 0.0f;
+          S[j][r] = s_in != nullptr ? s_in[static_cast<size_t>(16 * j + li) * kN + 16 * u + 4 * lg + r] : 0.0f;
       // the loads of S complete here on every path: otherwise the wait for
       // them is placed at S's first use inside the chunk loop, where it runs
       // every chunk and also waits for the next chunk's loads in flight
@@ -661,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
       for (int j = 0; j < NS; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          a.state_out[bh * P * kN + static_cast<size_t>(16 * j + 4 * lg + r) * kN + 16 * u + li] = S[j][r];
+          a.state_out[bh * P * kN + static_cast<size_t>(16 * j + li) * kN + 16 * u + 4 * lg + r] = S[j][r];
     }
     return;
   }
@@ -942,7 +942,7 @@ __global__ __launch_bounds__(kIoThreads) void ssd_summary_kernel(ChunkKernelArgs
 #pragma unroll
   for (int t = 0; t < NS; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) out[static_cast<size_t>(16 * t + 4 * lg + r) * kN + 16 * w + li] = S[t][r];
+    for (int r = 0; r < 4; ++r) out[static_cast<size_t>(16 * t + li) * kN + 16 * w + 4 * lg + r] = S[t][r];
   if (tid == 0) a.ws[ws_sin_floats(a) + ws_piece_floats(a) + slot] = dec;
 }
 
