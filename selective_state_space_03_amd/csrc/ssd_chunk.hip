@@ -64,8 +64,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 using rsrc_t = __amdgpu_buffer_rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
+// The descriptor's words pass through readfirstlane: they are uniform, and
+// the compiler must know it, or it wraps every load in a loop over the
+// distinct descriptors of the wave's lanes.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), kRsrcWord3);
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* base = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)), kRsrcWord3);
 }
 // 16 bytes at byte offset vo + so of a raw buffer
 __device__ __forceinline__ uint4 ld128(rsrc_t r, uint32_t vo, uint32_t so) {
@@ -630,21 +637,24 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
       // between its blocks (a ragged next chunk: all before it); published
       // for the next chunk once the output waves no longer read the buffer
       const bool more = c + 1 < c_end, whole_next = c + 1 < nfull;
-      if (more && !whole_next) load_chunk(c + 1, tid);
-      state_update<NS, NS, 1>(S, sm.tb[buf].eA[kQ - 1], sm.Bt, sm.Xt, sm.tb[buf].wS, u, 0, li, lg, [&](int j) {
-        if (more && whole_next) {
-          constexpr int kParts = 3 + Io::XI;  // C rows, B rows, the x slots, dt
+      if (more && whole_next) {
+        // dt first: the tables wait only for it (loads complete in order)
+        state_update<NS, NS, 1>(S, sm.tb[buf].eA[kQ - 1], sm.Bt, sm.Xt, sm.tb[buf].wS, u, 0, li, lg, [&](int j) {
+          constexpr int kParts = 3 + Io::XI;  // dt, C rows, B rows, the x slots
 #pragma unroll
           for (int k = 0; k < kParts; ++k)
             if (k == j || (j == NS - 1 && k > j)) {
-              if (k == kParts - 1) {
+              if (k == 0) {
                 if (u == 0) dtn = load_dt(c + 1, lane, true);
               } else {
-                io.template load_whole_part<true, false>(c + 1, R, offs, tid - kIoThreads, k);
+                io.template load_whole_part<true, false>(c + 1, R, offs, tid - kIoThreads, k - 1);
               }
             }
-        }
-      });
+        });
+      } else {
+        if (more) load_chunk(c + 1, tid);  // the ragged last chunk
+        state_update<NS, NS, 1>(S, sm.tb[buf].eA[kQ - 1], sm.Bt, sm.Xt, sm.tb[buf].wS, u, 0, li, lg, [](int) {});
+      }
       if constexpr (NB == 2) {
         publish_state(nbuf, li, lg);
         if (u == 0 && c + 1 < c_end) tables(c + 1, nbuf, dtn, lane);
