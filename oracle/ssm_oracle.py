@@ -28,7 +28,7 @@ written from the pages, in their order and notation:
 * "Mamba/SSM basics" (molayo), section "Technical details" (zero-order-hold
   discretization), used only by the optional ZOH form of B.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 B is discretized as dt*B (Euler, the "dB*x_t" of _ssm_fma and the dt[s]*x[s] of
 the chunk formula); D*u is added before the gate; y_t reads h_t after the update
 (inclusive); the conv is a cross-correlation whose last tap multiplies the

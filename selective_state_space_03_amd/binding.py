@@ -123,7 +123,7 @@ def lib() -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing (run __graft_entry__.build())")
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing (build it with selective_state_space_03_amd.build.build())")
     L = ctypes.CDLL(LIB_PATH)
     L.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanParams), _vp]
     L.ssm_scan_fwd.restype = _i32
