@@ -551,7 +551,7 @@ __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
   const bool use_pow = __all(prog);
   // the scaled-state form: rescaled rows present (finite dt_max, Euler), A
   // the same in every channel of the wave, factors within exp(+-32)
-  const bool use_g = !ZOH && a.bcg != nullptr && __all(same) && kScanResc * a.dt_max * span <= 32.0f;
+  const bool use_g = !ZOH && a.bcg != nullptr && __all(same) && kScanResc * fabsf(a.dt_max) * span <= 32.0f;
   const Scan<XT, YT, DTM, CONV, GATE, ZOH> S(a, c, s_al2, s_sat);
   const int t0 = seg * a.seg_len;
   const int t1 = min(t0 + a.seg_len, a.seqlen);
