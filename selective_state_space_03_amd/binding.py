@@ -231,6 +231,17 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _empty(shape, dtype, device, stream):
+    """torch.empty for a buffer the library writes on `stream`.  torch's caching
+    allocator ties a block to the stream current at allocation; when the call
+    runs on another stream the block is also recorded on that one, so it is not
+    handed out again before the work queued there has finished with it."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        t.record_stream(stream)
+    return t
+
+
 class Call:
     """One marshalled entry-point call.  run() enqueues it (again) on the same
     stream with the same buffers and returns the output tensor; the tensors
@@ -274,7 +285,7 @@ def scan_fwd(x, A, B, C, dt, *, D=None, z=None, conv_w=None, conv_b=None, conv_c
     dev = x.device
     d_state = A.shape[1]
     if y is None:
-        y = torch.empty((batch, seqlen, dim), dtype=y_dtype or x.dtype, device=dev)
+        y = _empty((batch, seqlen, dim), y_dtype or x.dtype, dev, stream)
     f32 = torch.float32
     p = ScanParams()
     p.struct_size = ctypes.sizeof(ScanParams)
@@ -309,7 +320,7 @@ def scan_fwd(x, A, B, C, dt, *, D=None, z=None, conv_w=None, conv_b=None, conv_c
     p.discretization = _discretization(discretization)
     need = L_.ssm_scan_workspace_size(ctypes.byref(p))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _empty(need, torch.uint8, dev, stream)
     p.workspace = _ptr(workspace, "workspace", device=dev)
     p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     call = Call(L_.ssm_scan_fwd, p, _stream(dev, stream), y, (x, A, B, C, dt, D, z, conv_w, conv_b, conv_cache_in,
@@ -328,7 +339,7 @@ def decode_step(x, A, B, C, dt, ssm_state, *, conv_cache=None, D=None, z=None, c
     dev = x.device
     d_state = A.shape[1]
     if y is None:
-        y = torch.empty((batch, dim), dtype=y_dtype or x.dtype, device=dev)
+        y = _empty((batch, dim), y_dtype or x.dtype, dev, stream)
     f32 = torch.float32
     p = DecodeParams()
     p.struct_size = ctypes.sizeof(DecodeParams)
@@ -374,7 +385,7 @@ def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size=128, D=None, dt_bias=None, dt_s
     ngroups, d_state = B.shape[2], B.shape[3]
     dev = x.device
     if out is None:
-        out = torch.empty((batch, seqlen, nheads, headdim), dtype=out_dtype or x.dtype, device=dev)
+        out = _empty((batch, seqlen, nheads, headdim), out_dtype or x.dtype, dev, stream)
     f32 = torch.float32
     p = ChunkParams()
     p.struct_size = ctypes.sizeof(ChunkParams)
@@ -403,7 +414,7 @@ def chunk_scan_fwd(x, dt, A, B, C, *, chunk_size=128, D=None, dt_bias=None, dt_s
     p.segments = int(segments)
     need = L_.ssm_chunk_scan_workspace_size(ctypes.byref(p))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _empty(need, torch.uint8, dev, stream)
     p.workspace = _ptr(workspace, "workspace", device=dev)
     p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     call = Call(L_.ssm_chunk_scan_fwd, p, _stream(dev, stream), out, (x, dt, A, B, C, D, dt_bias, state_in,
@@ -421,7 +432,7 @@ def chunk_decode_step(x, dt, A, B, C, state, *, D=None, dt_bias=None, dt_softplu
     ngroups, d_state = B.shape[1], B.shape[2]
     dev = x.device
     if out is None:
-        out = torch.empty((batch, nheads, headdim), dtype=out_dtype or x.dtype, device=dev)
+        out = _empty((batch, nheads, headdim), out_dtype or x.dtype, dev, stream)
     f32 = torch.float32
     p = ChunkDecodeParams()
     p.struct_size = ctypes.sizeof(ChunkDecodeParams)
@@ -460,7 +471,7 @@ def linear_fwd(x, weight, *, out=None, out_dtype=None, workspace=None, stream=No
     rows = math.prod(lead)
     dev = x.device
     if out is None:
-        out = torch.empty(lead + (n_out,), dtype=out_dtype or x.dtype, device=dev)
+        out = _empty(lead + (n_out,), out_dtype or x.dtype, dev, stream)
     p = LinearParams()
     p.struct_size = ctypes.sizeof(LinearParams)
     p.rows, p.in_features, p.out_features = rows, n_in, n_out
@@ -471,7 +482,7 @@ def linear_fwd(x, weight, *, out=None, out_dtype=None, workspace=None, stream=No
     p.out_dtype = _code(out, "out")
     if workspace is None:
         need = L_.ssm_linear_workspace_size(ctypes.byref(p))
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else False
+        workspace = _empty(need, torch.uint8, dev, stream) if need > 0 else False
     if workspace is not False:
         p.workspace = _ptr(workspace, "workspace", device=dev)
         p.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -490,7 +501,7 @@ def layer_fwd(hidden, w_in, conv_w, w_x, dt_w, A, w_out, *, dt_bias=None, D=None
     dim, d_state = A.shape
     dev = hidden.device
     if out is None:
-        out = torch.empty((batch, seqlen, d_model), dtype=out_dtype or hidden.dtype, device=dev)
+        out = _empty((batch, seqlen, d_model), out_dtype or hidden.dtype, dev, stream)
     f32, bf = torch.float32, torch.bfloat16
     p = LayerParams()
     p.struct_size = ctypes.sizeof(LayerParams)
@@ -519,7 +530,7 @@ def layer_fwd(hidden, w_in, conv_w, w_x, dt_w, A, w_out, *, dt_bias=None, D=None
     p.out_dtype = _code(out, "out")
     need = L_.ssm_layer_workspace_size(ctypes.byref(p))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _empty(need, torch.uint8, dev, stream)
     p.workspace = _ptr(workspace, "workspace", device=dev)
     p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     call = Call(L_.ssm_layer_fwd, p, _stream(dev, stream), out,
@@ -568,7 +579,7 @@ def scan_bwd(x, A, B, C, dt, dy, *, D=None, z=None, conv_w=None, conv_b=None, co
     p.dy = _ptr(dy, "dy", (batch, seqlen, dim), device=dev)
     p.dy_dtype = _code(dy, "dy")
     p.dstate_out = _ptr(dstate_out, "dstate_out", (batch, dim, d_state), f32, dev)
-    e = lambda *shape: torch.empty(shape, dtype=f32, device=dev)  # noqa: E731
+    e = lambda *shape: _empty(shape, f32, dev, stream)  # noqa: E731
     g = {"x": e(batch, seqlen, dim), "A": e(dim, d_state), "B": e(batch, seqlen, d_state),
          "C": e(batch, seqlen, d_state), "dt": e(batch, seqlen) if dt_rank1 else e(batch, seqlen, dim)}
     if z is not None:
@@ -594,7 +605,7 @@ def scan_bwd(x, A, B, C, dt, dy, *, D=None, z=None, conv_w=None, conv_b=None, co
             setattr(p, field, g[key].data_ptr() if g[key].numel() > 0 else None)
     need = L_.ssm_scan_bwd_workspace_size(ctypes.byref(p))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _empty(need, torch.uint8, dev, stream)
     p.workspace = _ptr(workspace, "workspace", device=dev)
     p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     call = Call(L_.ssm_scan_bwd, p, _stream(dev, stream), g,

@@ -692,6 +692,9 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_params_t* p, void* stream) {
   k.summ = k.nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(p->workspace) +
                                                  ssm::scan_summary_offset(p->batch, p->seqlen))
                       : nullptr;
+  k.head = k.nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(p->workspace) +
+                                                 ssm::scan_head_offset(p->batch, p->seqlen, p->dim, k.nseg))
+                      : nullptr;
   k.dt_min = p->dt_min;
   k.dt_max = p->dt_max;
   softplus_thresholds(p->dt_min, p->dt_max, &k.sp_lo, &k.sp_hi);

@@ -116,14 +116,17 @@ hipError_t launch_scan_compose(const ScanKernelArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+size_t scan_head_offset(int batch, int seqlen, int dim, int nseg) {
+  const size_t groups = static_cast<size_t>(batch) * ((dim + 63) / 64);
+  return scan_summary_offset(batch, seqlen) + groups * (nseg - 1) * (kScanN + 1) * 64 * sizeof(float);
+}
+
 size_t scan_workspace_bytes(int batch, int seqlen, int dim, int nseg) {
   if (batch <= 0 || seqlen <= 0) return 0;
-  size_t bytes = scan_summary_offset(batch, seqlen);
-  if (nseg > 1) {
-    const size_t groups = static_cast<size_t>(batch) * ((dim + 63) / 64);
-    bytes += groups * (nseg - 1) * (kScanN + 1) * 64 * sizeof(float);
-  }
-  return bytes;
+  if (nseg <= 1) return scan_summary_offset(batch, seqlen);
+  // summaries, then segment 0's starting state and conv window per lane
+  const size_t groups = static_cast<size_t>(batch) * ((dim + 63) / 64);
+  return scan_head_offset(batch, seqlen, dim, nseg) + groups * kScanHead * 64 * sizeof(float);
 }
 
 size_t scan_bcg_offset(int batch, int seqlen) { return bc_bytes(batch, seqlen); }

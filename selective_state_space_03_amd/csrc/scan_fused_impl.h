@@ -555,17 +555,31 @@ __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
   const Scan<XT, YT, DTM, CONV, GATE, ZOH> S(a, c, s_al2, s_sat);
   const int t0 = seg * a.seg_len;
   const int t1 = min(t0 + a.seg_len, a.seqlen);
-  float win[3] = {0.0f, 0.0f, 0.0f};
-  if (CONV) {
-    win[0] = S.raw_at(t0 - 3);
-    win[1] = S.raw_at(t0 - 2);
-    win[2] = S.raw_at(t0 - 1);
-  }
-  float h[kScanN];
-  float sdt = 0.0f;
   const size_t sbase = (static_cast<size_t>(c.b) * a.dim + c.e) * kScanN;
   // summaries: [(b, g)][segment][16 states + sum dt][lane]
   float* summ = a.summ + (static_cast<size_t>(c.b) * a.n_egroups + g) * (a.nseg - 1) * (kScanN + 1) * 64;
+  // segment 0's starting state and conv window: [(b, g)][16 states + 3][lane]
+  float* head = a.head + (static_cast<size_t>(c.b) * a.n_egroups + g) * kScanHead * 64;
+  // With a time split, the last segment of the full pass writes the final
+  // state and conv cache, which may be the very buffers the initial ones are
+  // read from (in-place update), and nothing orders it after segment 0 of the
+  // same pass.  So only the summary pass reads the initial state and cache;
+  // it saves them for segment 0 of the full pass.
+  const bool saved_start = MODE == kMain && seg == 0 && a.nseg > 1;
+  float win[3] = {0.0f, 0.0f, 0.0f};
+  if (CONV) {
+    if (saved_start) {
+      win[0] = head[(kScanN + 0) * 64 + lane];
+      win[1] = head[(kScanN + 1) * 64 + lane];
+      win[2] = head[(kScanN + 2) * 64 + lane];
+    } else {
+      win[0] = S.raw_at(t0 - 3);
+      win[1] = S.raw_at(t0 - 2);
+      win[2] = S.raw_at(t0 - 1);
+    }
+  }
+  float h[kScanN];
+  float sdt = 0.0f;
 
   if (MODE == kMain && seg > 0) {
     // state entering this segment, left in slot seg-1 by the composition of
@@ -573,9 +587,20 @@ __global__ __launch_bounds__(64, 3) void scan_kernel(ScanKernelArgs a) {
     const float* sin = summ + static_cast<size_t>(seg - 1) * (kScanN + 1) * 64;
 #pragma unroll
     for (int n = 0; n < kScanN; ++n) h[n] = sin[n * 64 + lane];
+  } else if (saved_start) {
+#pragma unroll
+    for (int n = 0; n < kScanN; ++n) h[n] = head[n * 64 + lane];
   } else {
 #pragma unroll
     for (int n = 0; n < kScanN; ++n) h[n] = (seg == 0 && a.state_in) ? a.state_in[sbase + n] : 0.0f;
+  }
+
+  if (MODE == kPass1 && seg == 0) {
+#pragma unroll
+    for (int n = 0; n < kScanN; ++n) head[n * 64 + lane] = h[n];
+    head[(kScanN + 0) * 64 + lane] = win[0];
+    head[(kScanN + 1) * 64 + lane] = win[1];
+    head[(kScanN + 2) * 64 + lane] = win[2];
   }
 
   if (MODE == kPass1) {

@@ -497,11 +497,14 @@ __global__ __launch_bounds__(kThreads) void ssd_kernel(ChunkKernelArgs a) {
   const float dtb = a.dt_bias ? a.dt_bias[h] : 0.0f;
   // The decay between positions s <= l of a chunk is 2^(dA[l] - dA[s]).  It is
   // factored through the start of s's 16-block, 2^(dA[l] - dA[16 J]) times
-  // 2^(dA[16 J] - dA[s]), two tables shared by the workgroup, when the second
-  // factor cannot overflow: |dt A| log2(e) below 6 per step (the 15 steps of a
-  // block then stay under 2^90).  Otherwise each element takes its own
-  // exponential.
-  const bool factored = a.dt_max * fabsf(Al2) < 6.0f;
+  // 2^(dA[16 J] - dA[s]), two tables shared by the workgroup, when neither
+  // factor can overflow: |dt A| log2(e) below 6 per step (the 15 steps of a
+  // block then stay under 2^90 either way).  Otherwise each element takes its
+  // own exponential.  |dt| is bounded by |dt_max| after a softplus (dt > 0 up
+  // to the upper clip, or dt = dt_max when that clip is negative) and by the
+  // larger of the two clip magnitudes without one (dt may be negative).
+  const float dt_abs = a.dt_softplus ? fabsf(a.dt_max) : fmaxf(fabsf(a.dt_min), fabsf(a.dt_max));
+  const bool factored = dt_abs * fabsf(Al2) < 6.0f;
   const Io io(a, b, h);
 
   // chunks of this segment: [c_beg, c_end); whole ones below nfull

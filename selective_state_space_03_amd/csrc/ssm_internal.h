@@ -45,6 +45,7 @@ constexpr int kConvK = 4;
 constexpr int kScanBlk = 4;        // steps per tile of prefetched vector loads
 constexpr int kScanResc = 2 * kScanBlk;  // steps between rescalings of the scaled state (a pair of tiles); segments start at multiples of it
 constexpr int kScanTab = (kScanResc + 1) * kScanN;  // floats of the q_n^k table
+constexpr int kScanHead = kScanN + kConvK - 1;      // floats per lane of a saved segment-0 start
 
 struct ScanKernelArgs {
   const void* x;
@@ -55,6 +56,7 @@ struct ScanKernelArgs {
   const float* bcg;      // the rescaled rows, same shape; null: no scaled-state form
   const float* qtab;     // q_n^k, [k][n] for k = 0..kScanResc
   float* summ;           // per-segment summaries (time split only)
+  float* head;           // segment 0's starting state and conv window, saved by the summary pass
   const float* A;        // (dim, 16)
   const float* D;        // (dim) or null
   const float* dt_w;     // (dim) or null
@@ -96,10 +98,12 @@ int scan_occupancy_xy(const ScanLaunch& l);
 // once (CUs x resident workgroups per CU), or 0 when it cannot be queried.
 long scan_resident_waves(const ScanLaunch& l);
 // Workspace layout of a scan call: plain rows, rescaled rows, the q_n^k
-// table, then the segment summaries.
+// table, then (time split only) the segment summaries and the saved starts
+// of segment 0.
 size_t scan_bcg_offset(int batch, int seqlen);
 size_t scan_qtab_offset(int batch, int seqlen);
 size_t scan_summary_offset(int batch, int seqlen);
+size_t scan_head_offset(int batch, int seqlen, int dim, int nseg);
 hipError_t launch_scan(const ScanLaunch& l, hipStream_t stream);
 
 // ---- decode step ---------------------------------------------------------

@@ -131,11 +131,13 @@ def test_decode_bf16_and_full_dt():
     check(np64(st), ho, TOL, "decode bf16 state")
 
 
-def test_decode_full_size():
+@pytest.mark.parametrize("unsat", [False, True])
+def test_decode_full_size(unsat):
     """Batched decode at full size: batch 64, E 7680, a 256-token prefill then 1024
     decode steps; oracle on 48 sampled channels of every batch row; the final
-    state also equals the GPU's 1280-token prefill."""
-    w = W.decode_stream()
+    state also equals the GPU's 1280-token prefill.  unsat: the dt recipe
+    shifted so softplus and both clip edges run."""
+    w = W.decode_stream(unsaturated=unsat)
     ch = np.sort(np.random.Generator(np.random.PCG64(41)).choice(7680, 48, replace=False))
     st, cc = _run(w, 256, 1024, ch, collect_every=97)
     p = _params(w)

@@ -93,6 +93,28 @@ def test_scan_wide_or_open_clip(dt_max):
     _parity(w, TOL_F32, time_split=2)
 
 
+@pytest.mark.parametrize("dt_min,dt_max,L", [(-0.1, -0.05, 40), (-1.2, -1.0, 4)])
+def test_scan_negative_dt_without_softplus(dt_min, dt_max, L):
+    """No softplus and a negative upper clip (every dt negative, so the decay
+    factors exceed 1): 8 |dt_max| max|A| is 6.4 for dt_max = -0.05 (inside the
+    scaled-state form's exp(+-32) range) and 128 for dt_max = -1 (outside it:
+    the plain form runs).  Lengths keep the growth inside fp32.  A is one row
+    shared by every channel but not a run of multiples of its first entry, so
+    each decay is its own exponential: with every factor above 1 the recurrence
+    amplifies old rounding errors instead of forgetting them, and the powers
+    the (n+1)-structured A would take by repeated products add up to ~16
+    roundings per step (40 such steps exceed the 1e-5 bound without any
+    fault in the code)."""
+    w = W.scan_tiny(batch=2, seqlen=L, dim=96, unsaturated=True)
+    rng = np.random.Generator(np.random.PCG64(12))
+    row = -rng.uniform(0.3, 16.0, 16)
+    row[np.argmax(-row)] = -16.0
+    w.arrays["A"] = np.broadcast_to(row, w.arrays["A"].shape).astype(np.float32).copy()
+    w.opts = dict(w.opts, dt_softplus=False, dt_min=np.float32(dt_min), dt_max=np.float32(dt_max))
+    for split in (1, 2):
+        _parity(w, TOL_F32, time_split=split)
+
+
 def test_scan_fp32_with_conv():
     """All-fp32 inputs with the conv on and a conv bias-free window from a given cache."""
     w = W.scan_prefill(batch=2, seqlen=70, dim=96, unsaturated=True)
@@ -192,14 +214,67 @@ def test_scan_prefill_full_size():
         assert np.array_equal(np64(cc.index_select(1, idx)), co)
 
 
-def test_scan_bulk_full_size():
-    """Bulk scan at full size (batch 8, L 4096, E 7680, bf16 u/dt/z); oracle on 48
-    sampled channels of batches 0 and 7."""
-    w = W.scan_bulk()
+@pytest.mark.parametrize("unsat", [False, True])
+def test_scan_bulk_full_size(unsat):
+    """Bulk scan at full size (batch 8, L 4096, E 7680, bf16 u/dt/z) in the launch
+    configuration the benchmark times (the library's own time split), fp32 output
+    held to 2e-3 max|y| and bf16 output to the same plus its rounding bound;
+    oracle on 48 sampled channels of batches 0 and 7.  unsat: the dt recipe
+    shifted so softplus and both clip edges run (the decay off the clip)."""
+    w = W.scan_bulk(unsaturated=unsat)
     ch = _sample(7680, 48, 22)
     yo, ho, _ = scan_oracle(w, batches=[0, 7], channels=ch)
-    y, st, _ = scan_gpu(w, y_dtype=torch.bfloat16)
     idx = torch.from_numpy(ch).to(DEV)
     bidx = torch.tensor([0, 7], device=DEV)
-    check(np64(y.index_select(0, bidx).index_select(2, idx)), yo, TOL_BF16, "bulk full y", out_bf16=True)
-    check(np64(st.index_select(0, bidx).index_select(1, idx)), ho, TOL_BF16, "bulk full state")
+    for y_dtype in (torch.float32, torch.bfloat16):
+        y, st, _ = scan_gpu(w, y_dtype=y_dtype)
+        check(np64(y.index_select(0, bidx).index_select(2, idx)), yo, TOL_BF16, f"bulk full y {y_dtype}",
+              out_bf16=(y_dtype == torch.bfloat16))
+        check(np64(st.index_select(0, bidx).index_select(1, idx)), ho, TOL_BF16, "bulk full state")
+        del y, st
+        torch.cuda.empty_cache()
+
+
+def test_scan_prefill_full_size_unsaturated():
+    """The layer prefill at full size (batch 1, L 2048, E 7680) with the dt recipe
+    shifted off the clip, in the library's own time split; fp32 output; oracle on
+    96 sampled channels."""
+    w = W.scan_prefill(unsaturated=True)
+    ch = _sample(7680, 96, 23)
+    yo, ho, co = scan_oracle(w, channels=ch)
+    y, st, cc = scan_gpu(w, y_dtype=torch.float32)
+    idx = torch.from_numpy(ch).to(DEV)
+    check(np64(y.index_select(2, idx)), yo, TOL_BF16, "prefill full unsat y")
+    check(np64(st.index_select(1, idx)), ho, TOL_BF16, "prefill full unsat state")
+    assert np.array_equal(np64(cc.index_select(1, idx)), co)
+
+
+def test_scan_in_place_split_beyond_residency():
+    """State and conv cache updated in place (outputs aliasing the inputs) with a
+    forced time split whose grid is several times what the GPU holds at once
+    (batch 8, L 1024, E 7680, 6 segments: 5760 one-wave workgroups), so the
+    last segment of a sequence may finish before its first segment starts:
+    segment 0 must still start from the given state and cache.  Oracle on 32
+    sampled channels of batches 0 and 7."""
+    w = W.scan_prefill(batch=8, seqlen=1024, unsaturated=True)
+    rng = np.random.Generator(np.random.PCG64(24))
+    st_in = rng.standard_normal((8, 7680, 16)).astype(np.float32)
+    cc_in = rng.standard_normal((8, 7680, 3)).astype(np.float32)
+    ch = _sample(7680, 32, 25)
+    yo, ho, co = scan_oracle(w, state_in=st_in.astype(np.float64), cache_in=cc_in.astype(np.float64),
+                             batches=[0, 7], channels=ch)
+    import selective_state_space_03_amd as ssm
+    st = torch.from_numpy(st_in).to(DEV)
+    cc = torch.from_numpy(cc_in).to(DEV)
+    o = w.opts
+    y = ssm.scan_fwd(dev_tensor(w, "x"), dev_tensor(w, "A"), dev_tensor(w, "B"), dev_tensor(w, "C"),
+                     dev_tensor(w, "dt"), D=dev_tensor(w, "D"), z=dev_tensor(w, "z"), conv_w=dev_tensor(w, "conv_w"),
+                     conv_cache_in=cc, conv_cache_out=cc, dt_rank1=True, dt_w=dev_tensor(w, "dt_w"),
+                     dt_bias=dev_tensor(w, "dt_bias"), dt_min=o["dt_min"], dt_max=o["dt_max"], ssm_state_in=st,
+                     ssm_state_out=st, y_dtype=torch.float32, time_split=6)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(ch).to(DEV)
+    bidx = torch.tensor([0, 7], device=DEV)
+    check(np64(y.index_select(0, bidx).index_select(2, idx)), yo, TOL_BF16, "in-place split y")
+    check(np64(st.index_select(0, bidx).index_select(1, idx)), ho, TOL_BF16, "in-place split state")
+    assert np.array_equal(np64(cc.index_select(0, bidx).index_select(1, idx)), co)

@@ -50,6 +50,22 @@ def test_ssd_state_in_and_per_channel_D_and_bf16_out():
     check(np64(st), so, TOL, "ssd state")
 
 
+@pytest.mark.parametrize("dt_min,dt_max,seqlen", [(-0.05, 0.1, 512), (-0.6, -0.4, 6)])
+def test_ssd_negative_dt_without_softplus(dt_min, dt_max, seqlen):
+    """No softplus and a negative lower clip: dt takes both signs (the decay
+    grows on negative steps; the raw values N(0, 1.1) put about half the steps
+    on each clip, so the state decays on the whole), or is negative throughout
+    (dt in [-0.6, -0.4]: |dt A| log2(e) reaches 13.8 per step, past the
+    factored-decay bound, for the heads with |A| above 6.9).  Lengths keep the
+    growth inside fp32 (max|out| 358 and 4.7e12)."""
+    w = _small(batch=1, seqlen=seqlen, nheads=4, ngroups=1)
+    w.opts = dict(w.opts, dt_softplus=False, dt_min=np.float32(dt_min), dt_max=np.float32(dt_max))
+    out, st = ssd_gpu(w)
+    oo, so = ssd_oracle(w, sequential=True)
+    check(np64(out), oo, TOL, f"ssd out dt in [{dt_min}, {dt_max}]")
+    check(np64(st), so, TOL, f"ssd state dt in [{dt_min}, {dt_max}]")
+
+
 def test_ssd_matches_sequential_definition():
     """Against the oracle's plain recurrence (not its chunked form)."""
     w = _small(batch=1, seqlen=256, nheads=2, ngroups=1, unsaturated=True)
@@ -67,10 +83,13 @@ def test_ssd_deterministic_and_complete():
     assert torch.isfinite(o1).all()
 
 
-def test_ssd_long_full_size():
+@pytest.mark.parametrize("unsat", [False, True])
+def test_ssd_long_full_size(unsat):
     """Long-context chunked scan at full size: batch 1, L 65536 (512 chunks),
-    80 heads x 96, 1 group, N 64; oracle on heads 0, 37 and 79."""
-    w = W.ssd_long()
+    80 heads x 96, 1 group, N 64, in the library's own segment split; oracle on
+    heads 0, 37 and 79.  unsat: the dt recipe shifted so softplus and both
+    clip edges run."""
+    w = W.ssd_long(unsaturated=unsat)
     heads = [0, 37, 79]
     oo, so = ssd_oracle(w, heads=heads)
     for out_dtype in (torch.float32, torch.bfloat16):
