@@ -84,6 +84,30 @@ def _diag_a(dim, d_state):
     return np.ascontiguousarray(np.broadcast_to(row, (dim, d_state)))
 
 
+A_INITS = ("diag", "log_init", "random")
+
+
+def _a_matrix(rng, dim, d_state, a_init):
+    """A (dim, d_state) fp32 in one of three forms:
+    diag      -1 .. -d_state stored exactly (the A_log = log(1..N) initialisation);
+    log_init  the same initialisation as a model stores it: A_log = log(1..N) and
+              A = -exp(A_log), both rounded to fp32 (several entries then differ
+              from -(n+1) in the last bit, as a trained or loaded A does);
+    random    A_log ~ U[0, ln 16] drawn per (channel, state), A = -exp(A_log) in
+              fp32: no structure shared across channels or states.
+    Only `random` draws from rng (after every other draw of the workload)."""
+    if a_init == "diag":
+        return _diag_a(dim, d_state)
+    if a_init == "log_init":
+        a_log = np.log(np.arange(1, d_state + 1, dtype=np.float32)).astype(np.float32)
+        row = (-np.exp(a_log)).astype(np.float32)
+        return np.ascontiguousarray(np.broadcast_to(row, (dim, d_state)))
+    if a_init == "random":
+        a_log = rng.uniform(0.0, np.log(16.0), (dim, d_state)).astype(np.float32)
+        return (-np.exp(a_log)).astype(np.float32)
+    raise ValueError(f"a_init must be one of {A_INITS}, got {a_init!r}")
+
+
 def scan_tiny(batch=1, seqlen=64, dim=16, d_state=16, seed=1, unsaturated=False):
     """Tiny fp32 scan.  Draws: u, z, B, C ~ N(0,1); D ~ N(0,1); r ~ N(0,1) (batch, L);
     w_dt, b_dt ~ N(0, 0.5).  dt = clip(softplus(w_dt * r + b_dt), 1e-3, 0.1)."""
@@ -106,11 +130,11 @@ def scan_tiny(batch=1, seqlen=64, dim=16, d_state=16, seed=1, unsaturated=False)
         set(), dict(dt_rank1=True, dt_softplus=True, dt_min=DT_MIN, dt_max=DT_MAX, conv=False))
 
 
-def scan_prefill(batch=1, seqlen=2048, dim=7680, d_state=16, seed=2, unsaturated=False):
+def scan_prefill(batch=1, seqlen=2048, dim=7680, d_state=16, seed=2, unsaturated=False, a_init="diag"):
     """Bit-Axon SSM layer prefill.  Draws: x_branch, z ~ N(0,1) -> bf16 (batch, L, E);
     conv_w ~ N(0, 0.5) (E, 4) fp32, no bias; B, C ~ N(0,1) -> bf16 (batch, L, N);
     r ~ N(0,1) fp32 (batch, L); w_dt, b_dt ~ N(0, 0.5) (E); D ~ N(0,1) (E).
-    Zero ssm_state and conv_cache in."""
+    Zero ssm_state and conv_cache in.  a_init: see _a_matrix."""
     rng = np.random.Generator(np.random.PCG64(seed))
     x = bf16_bits(_normal(rng, (batch, seqlen, dim)))
     z = bf16_bits(_normal(rng, (batch, seqlen, dim)))
@@ -124,20 +148,21 @@ def scan_prefill(batch=1, seqlen=2048, dim=7680, d_state=16, seed=2, unsaturated
     if unsaturated:
         r *= np.float32(2.0)
         b_dt = _normal(rng, (dim,), 1.0, -4.0)
+    A = _a_matrix(rng, dim, d_state, a_init)
     return Workload(
-        "scan_prefill" + ("_unsat" if unsaturated else ""), "scan",
+        "scan_prefill" + ("_unsat" if unsaturated else "") + ("" if a_init == "diag" else "_" + a_init), "scan",
         dict(batch=batch, seqlen=seqlen, dim=dim, d_state=d_state),
-        dict(x=x, z=z, conv_w=conv_w, B=B, C=C, dt=r, dt_w=w_dt, dt_bias=b_dt, D=D,
-             A=_diag_a(dim, d_state)),
+        dict(x=x, z=z, conv_w=conv_w, B=B, C=C, dt=r, dt_w=w_dt, dt_bias=b_dt, D=D, A=A),
         {"x", "z", "B", "C"},
         dict(dt_rank1=True, dt_softplus=True, dt_min=DT_MIN, dt_max=DT_MAX, conv=True))
 
 
-def scan_bulk(batch=8, seqlen=4096, dim=7680, d_state=16, seed=3, unsaturated=False):
+def scan_bulk(batch=8, seqlen=4096, dim=7680, d_state=16, seed=3, unsaturated=False, a_init="diag"):
     """Bandwidth-bound bulk scan.  Draws: u, z ~ N(0,1) -> bf16 (batch, L, E);
     dt_raw ~ N(0, 0.5) -> bf16 (batch, L, E) (E-wide, the dt_proj output);
     dt_bias ~ N(0, 0.5) (E); B, C ~ N(0,1) -> bf16 (batch, L, N); D ~ N(0,1) (E).
-    dt = clip(softplus(dt_raw + dt_bias), 1e-3, 0.1) is formed by the consumer."""
+    dt = clip(softplus(dt_raw + dt_bias), 1e-3, 0.1) is formed by the consumer.
+    a_init: see _a_matrix."""
     rng = np.random.Generator(np.random.PCG64(seed))
     u = bf16_bits(_normal(rng, (batch, seqlen, dim)))
     z = bf16_bits(_normal(rng, (batch, seqlen, dim)))
@@ -149,10 +174,11 @@ def scan_bulk(batch=8, seqlen=4096, dim=7680, d_state=16, seed=3, unsaturated=Fa
     D = _normal(rng, (dim,))
     if unsaturated:
         b_dt = _normal(rng, (dim,), 1.0, -4.0)
+    A = _a_matrix(rng, dim, d_state, a_init)
     return Workload(
-        "scan_bulk" + ("_unsat" if unsaturated else ""), "scan",
+        "scan_bulk" + ("_unsat" if unsaturated else "") + ("" if a_init == "diag" else "_" + a_init), "scan",
         dict(batch=batch, seqlen=seqlen, dim=dim, d_state=d_state),
-        dict(x=u, z=z, dt=dt, dt_bias=b_dt, B=B, C=C, D=D, A=_diag_a(dim, d_state)),
+        dict(x=u, z=z, dt=dt, dt_bias=b_dt, B=B, C=C, D=D, A=A),
         {"x", "z", "dt", "B", "C"},
         dict(dt_rank1=False, dt_softplus=True, dt_min=DT_MIN, dt_max=DT_MAX, conv=False))
 

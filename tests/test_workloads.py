@@ -44,3 +44,25 @@ def test_saturation_of_default_recipe():
     q = W.scan_tiny(seqlen=4096, dim=64, unsaturated=True)
     pre = q.arrays["dt_w"][None, None, :] * q.arrays["dt"][..., None] + q.arrays["dt_bias"]
     assert 0.05 < np.mean(pre >= -2.2522) < 0.5 and np.mean(pre <= -6.9073) > 0.01
+
+
+def test_a_init_forms():
+    """The three forms of A: the exact diagonal, the same initialisation as a
+    model stores it (fp32 log then fp32 exp: the entries for 5, 10, 11, 13 and
+    15 land an ulp or two off, so A is no longer a run of multiples of its first
+    entry), and independent random rows; the other draws are unchanged."""
+    base = W.scan_bulk(batch=1, seqlen=8, dim=64)
+    li = W.scan_bulk(batch=1, seqlen=8, dim=64, a_init="log_init")
+    rnd = W.scan_bulk(batch=1, seqlen=8, dim=64, a_init="random")
+    diag = -np.arange(1, 17, dtype=np.float32)
+    assert np.array_equal(base.arrays["A"][5], diag)
+    off = np.nonzero(li.arrays["A"][0] != diag)[0] + 1
+    assert list(off) == [5, 10, 11, 13, 15]
+    assert np.all(np.abs(li.arrays["A"][0] - diag) <= 2 * np.spacing(np.abs(diag)))
+    assert np.array_equal(li.arrays["A"][0], li.arrays["A"][63])
+    A = rnd.arrays["A"]
+    assert A.shape == (64, 16) and np.all(A <= -1.0) and np.all(A >= -16.0)
+    assert len(np.unique(A)) == A.size
+    for k in base.arrays:
+        if k != "A":
+            assert np.array_equal(base.arrays[k], li.arrays[k]) and np.array_equal(base.arrays[k], rnd.arrays[k]), k
