@@ -147,6 +147,33 @@ size_t ssm_scan_workspace_size(const ssm_scan_params_t *p);
 ssm_status_t ssm_scan_check(const ssm_scan_params_t *p);
 
 /* ------------------------------------------------------------------------
+ * ssm_scan_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and results as ssm_scan_fwd, with the
+ * workspace taken from a scratch array inside the library instead of the
+ * caller.  p->workspace must be NULL and p->workspace_bytes 0 (else
+ * SSM_ERR_INVALID_ARG); every other field is as for ssm_scan_fwd, and the
+ * caller still owns the inputs and outputs.  The call allocates nothing and
+ * calls no allocating routine.
+ *  - The scratch holds SSM_SCAN_NOALLOC_MAX_BYTES (64 MiB).  A call whose
+ *    ssm_scan_workspace_size(p) exceeds it returns SSM_ERR_WORKSPACE, with the
+ *    size in ssm_last_error(), before anything is launched.  (It covers, for
+ *    example, batch 8 x 4096 tokens and batch 1 x 2048 tokens at E 7680 with
+ *    the library's own time split.)
+ *  - Each GPU the library runs on holds one copy of the scratch for the life
+ *    of the process.  Its address on a device is looked up on the first call
+ *    made there (with that device current); a failure of that lookup returns
+ *    SSM_ERR_HIP.
+ *  - Every call on one GPU uses that GPU's single copy: calls that may run at
+ *    the same time on one GPU (different streams without ordering between
+ *    them, or different threads) race on it and must not overlap.  Calls on
+ *    one stream are ordered and safe.  Nothing in the scratch needs to start
+ *    at zero; it keeps the last call's contents.
+ * ---------------------------------------------------------------------- */
+#define SSM_SCAN_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+ssm_status_t ssm_scan_fwd_noalloc(const ssm_scan_params_t *p, void *stream);
+
+/* ------------------------------------------------------------------------
  * One decode step, in place.  Shapes as above with L = 1:
  *   x (Bt, E) x_dtype new token (pre-conv when conv_w != NULL); z (Bt, E) or NULL;
  *   dt: dt_rank1 ? (Bt) f32 r : (Bt, E) dt_dtype;  B, C (Bt, N) bc_dtype;

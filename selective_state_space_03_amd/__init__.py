@@ -15,5 +15,6 @@ from .binding import (  # noqa: F401
     linear_fwd,
     scan_bwd,
     scan_fwd,
+    scan_fwd_noalloc,
     set_timing_events,
 )

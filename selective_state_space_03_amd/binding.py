@@ -104,7 +104,7 @@ class ScanBwdParams(ctypes.Structure):
 
 
 EXPORTED = [
-    "ssm_scan_fwd", "ssm_scan_workspace_size", "ssm_scan_check",
+    "ssm_scan_fwd", "ssm_scan_workspace_size", "ssm_scan_check", "ssm_scan_fwd_noalloc",
     "ssm_decode_step", "ssm_decode_check",
     "ssm_chunk_scan_fwd", "ssm_chunk_scan_workspace_size", "ssm_chunk_scan_check",
     "ssm_chunk_decode_step", "ssm_chunk_decode_check",
@@ -131,6 +131,8 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_check.restype = _i32
     L.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanParams)]
     L.ssm_scan_workspace_size.restype = ctypes.c_size_t
+    L.ssm_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanParams), _vp]
+    L.ssm_scan_fwd_noalloc.restype = _i32
     L.ssm_decode_step.argtypes = [ctypes.POINTER(DecodeParams), _vp]
     L.ssm_decode_step.restype = _i32
     L.ssm_decode_check.argtypes = [ctypes.POINTER(DecodeParams)]
@@ -280,6 +282,30 @@ def scan_fwd(x, A, B, C, dt, *, D=None, z=None, conv_w=None, conv_b=None, conv_c
     """Full-sequence selective scan (ssm_scan_fwd); discretization "euler" (dt B u) or "zoh"
     (((e^{dt A} - 1) / A) B u).  Returns y (batch, L, E), or
     with prepare=True a Call that enqueues this same call again on each run()."""
+    return _scan(False, x, A, B, C, dt, D=D, z=z, conv_w=conv_w, conv_b=conv_b, conv_cache_in=conv_cache_in,
+                 conv_cache_out=conv_cache_out, dt_rank1=dt_rank1, dt_w=dt_w, dt_bias=dt_bias,
+                 dt_softplus=dt_softplus, dt_min=dt_min, dt_max=dt_max, ssm_state_in=ssm_state_in,
+                 ssm_state_out=ssm_state_out, y=y, y_dtype=y_dtype, time_split=time_split, workspace=workspace,
+                 discretization=discretization, stream=stream, prepare=prepare)
+
+
+def scan_fwd_noalloc(x, A, B, C, dt, *, D=None, z=None, conv_w=None, conv_b=None, conv_cache_in=None,
+                     conv_cache_out=None, dt_rank1=False, dt_w=None, dt_bias=None, dt_softplus=True,
+                     dt_min=None, dt_max=None, ssm_state_in=None, ssm_state_out=None, y=None,
+                     y_dtype=None, time_split=0, discretization="euler", stream=None, prepare=False):
+    """ssm_scan_fwd_noalloc: scan_fwd with the workspace taken from the library's
+    own device scratch (no workspace argument; calls on one GPU must not overlap).
+    Returns y, or with prepare=True a Call."""
+    return _scan(True, x, A, B, C, dt, D=D, z=z, conv_w=conv_w, conv_b=conv_b, conv_cache_in=conv_cache_in,
+                 conv_cache_out=conv_cache_out, dt_rank1=dt_rank1, dt_w=dt_w, dt_bias=dt_bias,
+                 dt_softplus=dt_softplus, dt_min=dt_min, dt_max=dt_max, ssm_state_in=ssm_state_in,
+                 ssm_state_out=ssm_state_out, y=y, y_dtype=y_dtype, time_split=time_split, workspace=None,
+                 discretization=discretization, stream=stream, prepare=prepare)
+
+
+def _scan(noalloc, x, A, B, C, dt, *, D, z, conv_w, conv_b, conv_cache_in, conv_cache_out, dt_rank1, dt_w, dt_bias,
+          dt_softplus, dt_min, dt_max, ssm_state_in, ssm_state_out, y, y_dtype, time_split, workspace,
+          discretization, stream, prepare):
     L_ = lib()
     batch, seqlen, dim = x.shape
     dev = x.device
@@ -318,14 +344,15 @@ def scan_fwd(x, A, B, C, dt, *, D=None, z=None, conv_w=None, conv_b=None, conv_c
     p.y_dtype = _code(y, "y")
     p.time_split = int(time_split)
     p.discretization = _discretization(discretization)
-    need = L_.ssm_scan_workspace_size(ctypes.byref(p))
-    if workspace is None and need > 0:
-        workspace = _empty(need, torch.uint8, dev, stream)
-    p.workspace = _ptr(workspace, "workspace", device=dev)
-    p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    call = Call(L_.ssm_scan_fwd, p, _stream(dev, stream), y, (x, A, B, C, dt, D, z, conv_w, conv_b, conv_cache_in,
-                                                             conv_cache_out, dt_w, dt_bias, ssm_state_in,
-                                                             ssm_state_out, workspace))
+    if not noalloc:
+        need = L_.ssm_scan_workspace_size(ctypes.byref(p))
+        if workspace is None and need > 0:
+            workspace = _empty(need, torch.uint8, dev, stream)
+        p.workspace = _ptr(workspace, "workspace", device=dev)
+        p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    fn = L_.ssm_scan_fwd_noalloc if noalloc else L_.ssm_scan_fwd
+    call = Call(fn, p, _stream(dev, stream), y, (x, A, B, C, dt, D, z, conv_w, conv_b, conv_cache_in,
+                                                conv_cache_out, dt_w, dt_bias, ssm_state_in, ssm_state_out, workspace))
     return call if prepare else call.run()
 
 

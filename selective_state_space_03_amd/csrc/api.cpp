@@ -649,6 +649,7 @@ ssm_status_t hip_status(hipError_t e) {
 
 namespace ssm {
 TimingEvents timing_events() { return g_timing; }
+static_assert(kScanScratchBytes == SSM_SCAN_NOALLOC_MAX_BYTES, "scratch size in the header and the library differ");
 }  // namespace ssm
 
 extern "C" {
@@ -663,9 +664,12 @@ size_t ssm_scan_workspace_size(const ssm_scan_params_t* p) {
   return scan_ws(p);
 }
 
-ssm_status_t ssm_scan_fwd(const ssm_scan_params_t* p, void* stream) {
-  const ssm_status_t s = scan_check(p);
-  if (s != SSM_OK) return s;
+}  // extern "C"
+
+namespace {
+
+// The launch of a validated scan call (its workspace already in place).
+ssm_status_t scan_launch(const ssm_scan_params_t* p, void* stream) {
   ssm::ScanLaunch l{};
   ssm::ScanKernelArgs& k = l.k;
   k.x = p->x;
@@ -722,6 +726,45 @@ ssm_status_t ssm_scan_fwd(const ssm_scan_params_t* p, void* stream) {
   k.qtab = l.qtab_out;
   if (p->batch == 0) return ok();
   return hip_status(ssm::launch_scan(l, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status_t ssm_scan_fwd(const ssm_scan_params_t* p, void* stream) {
+  const ssm_status_t s = scan_check(p);
+  if (s != SSM_OK) return s;
+  return scan_launch(p, stream);
+}
+
+ssm_status_t ssm_scan_fwd_noalloc(const ssm_scan_params_t* p, void* stream) {
+  if (!p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "params");
+  if (p->struct_size != sizeof(ssm_scan_params_t))
+    return fail(SSM_ERR_INVALID_ARG, "%s does not match this library", "struct_size");
+  if (p->workspace || p->workspace_bytes)
+    return fail(SSM_ERR_INVALID_ARG, "%s must be NULL and 0: this entry point uses the library's own scratch",
+                "workspace/workspace_bytes");
+  // sizes first, so a request past the scratch fails before the device is touched
+  if (p->batch >= 0 && p->seqlen >= 0 && p->dim > 0 && p->d_state == ssm::kScanN &&
+      p->time_split >= 0 && p->time_split <= ssm::kScanMaxSplit) {
+    const size_t need = scan_ws(p);
+    if (need > ssm::kScanScratchBytes) {
+      char buf[192];
+      std::snprintf(buf, sizeof(buf), "needs %zu bytes of scratch; ssm_scan_fwd_noalloc holds at most %zu",
+                    need, static_cast<size_t>(ssm::kScanScratchBytes));
+      return fail(SSM_ERR_WORKSPACE, "%s", buf);
+    }
+  }
+  void* scratch = nullptr;
+  const hipError_t e = ssm::scan_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e);
+  ssm_scan_params_t q = *p;
+  q.workspace = scratch;
+  q.workspace_bytes = ssm::kScanScratchBytes;
+  const ssm_status_t s = scan_check(&q);
+  if (s != SSM_OK) return s;
+  return scan_launch(&q, stream);
 }
 
 ssm_status_t ssm_decode_check(const ssm_decode_params_t* p) {

@@ -28,11 +28,23 @@
 // a small launch composes them in order into every segment's incoming state;
 // the last launch runs all segments in full.  Summaries travel through the
 // workspace.
+#include <mutex>
+
 #include "ssm_device.h"
 #include "ssm_internal.h"
 
 namespace ssm {
+
+// Workspace of ssm_scan_fwd_noalloc (packed and rescaled B/C rows, the decay
+// table, segment summaries), for callers that cannot allocate device memory.
+// In host code this name is only a stand-in for the symbol: its device
+// address comes from hipGetSymbolAddress on each device (scan_scratch) and
+// is the only form in which host code hands the array to a kernel.
+static __device__ __align__(256) unsigned char scratch[kScanScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
 
 // Pack B and C (bf16 or fp32) into fp32 rows [B0..B15, C0..C15].  With
 // outg: also the rows of the scaled-state form, B_t[n] q_n^-(j+1) and
@@ -132,6 +144,25 @@ size_t scan_workspace_bytes(int batch, int seqlen, int dim, int nseg) {
 size_t scan_bcg_offset(int batch, int seqlen) { return bc_bytes(batch, seqlen); }
 size_t scan_qtab_offset(int batch, int seqlen) { return 2 * bc_bytes(batch, seqlen); }
 size_t scan_summary_offset(int batch, int seqlen) { return 2 * bc_bytes(batch, seqlen) + kQtabBytes; }
+
+hipError_t scan_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 long scan_resident_waves(const ScanLaunch& l) {
   // CU count per device, asked once (no runtime query inside stream capture)

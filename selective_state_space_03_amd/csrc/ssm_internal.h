@@ -105,6 +105,12 @@ size_t scan_qtab_offset(int batch, int seqlen);
 size_t scan_summary_offset(int batch, int seqlen);
 size_t scan_head_offset(int batch, int seqlen, int dim, int nseg);
 hipError_t launch_scan(const ScanLaunch& l, hipStream_t stream);
+// The no-allocation scan entry point's scratch: a file-scope device array of
+// kScanScratchBytes (one copy per device, held until the process ends).
+// Writes its device address on the current device to *ptr; the address is
+// looked up once per device (hipGetSymbolAddress) and kept.
+constexpr size_t kScanScratchBytes = size_t(64) << 20;
+hipError_t scan_scratch(void** ptr);
 
 // ---- decode step ---------------------------------------------------------
 struct DecodeKernelArgs {

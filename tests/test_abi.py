@@ -122,6 +122,22 @@ def test_scan_validation(L):
     assert L.ssm_scan_check(None) == 1
 
 
+def test_scan_noalloc_validation(L):
+    """ssm_scan_fwd_noalloc refuses, before touching a device: a NULL or
+    mismatched struct, a workspace of the caller's (it uses its own scratch),
+    and a call whose workspace would exceed the 64 MiB scratch."""
+    fn = L.ssm_scan_fwd_noalloc
+    assert fn(None, None) == 1
+    assert fn(ctypes.byref(_scan(workspace=None, workspace_bytes=0, struct_size=8)), None) == 1
+    assert fn(ctypes.byref(_scan()), None) == 1
+    assert b"scratch" in L.ssm_last_error()
+    assert fn(ctypes.byref(_scan(workspace=None, workspace_bytes=16)), None) == 1
+    big = _scan(workspace=None, workspace_bytes=0, batch=64, seqlen=4096, dim=128)
+    assert L.ssm_scan_workspace_size(ctypes.byref(big)) > 64 << 20
+    assert fn(ctypes.byref(big), None) == 3
+    assert b"at most 67108864" in L.ssm_last_error()
+
+
 def _decode(**kw):
     from selective_state_space_03_amd import binding as b
 
