@@ -1,25 +1,30 @@
 #!/usr/bin/env python3
 """Throughput of the selective-scan hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|bulk]
-                    [--no-parts] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload bulk|prefill]
+                    [--no-parts] [--no-cpu] [--no-variants]
 
-A step is one ssm_scan_fwd call (conv1d + SiLU, dt, scan, readout, skip, gate,
-final state and conv cache) over one batch of the workload, with every input
-already resident in HBM.  The default workload is the Bit-Axon layer prefill
-(batch 1, L 2048, E 7680, N 16, bf16 x/z/B/C, bf16 y); --workload bulk times
-the bulk scan (batch 8, L 4096, E 7680, bf16 u/dt/z/y).  Inputs are the seeded
-synthetic recipes of ssm_workloads.py.
+A step is one ssm_scan_fwd call (dt, scan, readout, skip, gate, final state;
+conv1d + SiLU and the conv cache too for the prefill) over one batch of the
+workload, with every input already resident in HBM.  The default workload is
+the bandwidth-bound bulk scan (batch 8, L 4096, E 7680, N 16, bf16 u/dt/z/B/C,
+bf16 y), on which the HBM bar is judged; --workload prefill times the Bit-Axon
+layer prefill (batch 1, L 2048, E 7680, conv1d k=4, rank-1 dt).  Inputs are
+the seeded synthetic recipes of ssm_workloads.py.
 
 Prints ONE JSON line.  Besides the throughput it carries
 * roofline: the main scan kernel's duration, measured with HIP events that the
-  library records on its own launch stream around that kernel, against its
-  roofline (FLOPS_PER_CH_STEP and the byte counts beside each workload give
-  the algorithmic work per unit);
-* cpu_baseline: the float64 oracle on the same workload on this host's CPU;
-* parts: the other entry points at their workloads (bulk scan, 8-layer decode
-  step, chunked SSD, SSD-form decode step, the whole layer forward with its
-  two projection GEMMs), each with its own kernel roofline.
+  library records on its own launch stream around that kernel, against the
+  HBM roofline (the workload's algorithmic bytes over that duration), plus the
+  same for the whole call (every kernel of the step, back-to-back launches);
+* variants: the same workload with A as a model stores it (fp32 -exp(log n))
+  and on the general path (random per-channel A, dt off the clip), which take
+  the kernel's slower decay forms;
+* cpu_baseline: the float64 oracle on the same workload on this host's CPU
+  cores (channels sharded over worker processes), plus one core on one shard;
+* parts: the other entry points at their workloads (prefill or bulk scan,
+  8-layer decode step, chunked SSD, SSD-form decode step, backward, the whole
+  layer forward with its two projection GEMMs), each with its own roofline.
 Counters of HBM traffic come from rocprofv3 runs recorded in profiles/; each
 is reported only while its kernel's sources still hash to the recorded value.
 """
@@ -49,20 +54,29 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix, published
 # (4 fma = 8), SiLU of its output (4) and the rank-1 dt with softplus and clip
 # (6) add 18 for the layer prefill.
 FLOPS_PER_CH_STEP = {"prefill": 138.0, "bulk": 120.0}
+# The backward's main walk per channel-step (bwd_main): the forward recomputed
+# over the segment (decay 16 x (mul + exp) = 32, update 1 + 16 x 2 = 33,
+# dt and u 6), then the reverse step: the state gradient G = dyc C + a G'
+# (16 x 3 = 48), dA and dt terms (16 x 2 + 16 x 2 = 64), du (16 x 2 + 2 = 34),
+# dB and dC (16 x 2 = 32, their channel sums not counted), dz and the SiLU
+# derivatives (8): 257.
+BWD_FLOPS_PER_CH_STEP = 257.0
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=("prefill", "bulk"), default="prefill")
+    ap.add_argument("--workload", choices=("prefill", "bulk"), default="bulk")
+    ap.add_argument("--no-variants", action="store_true", help="skip the model-A and general-path timings")
     ap.add_argument("--split", type=int, default=0,
                     help="time segments per sequence for the scan (0: the library's choice)")
     ap.add_argument("--no-parts", action="store_true", help="skip the decode / SSD / other-scan lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--only", choices=("prefill", "bulk", "decode", "ssd", "ssd_decode", "layer", "in_proj", "out_proj",
-                                       "scan_bwd", "copy"), default=None,
+    ap.add_argument("--only", choices=("prefill", "bulk", "bulk_general", "prefill_general", "decode", "ssd",
+                                       "ssd_decode", "layer", "in_proj", "out_proj", "scan_bwd", "copy"),
+                    default=None,
                     help="run just this workload's timed loop, no JSON line (for profiler runs); 'copy' "
                          "copies 1 GiB device to device, the calibration for the HBM byte counters")
     return ap.parse_args()
@@ -79,9 +93,11 @@ def log(msg):
 # to the recorded value.
 SCAN_SOURCES = ("scan_fused.hip", "scan_fused_impl.h", "scan_xy_bb.hip", "scan_xy_bf.hip", "scan_xy_fb.hip",
                 "scan_xy_ff.hip")
+# the kernels of one ssm_scan_fwd call, in launch order (the time split's
+# summary pass and composition run only when the sequence is cut)
+SCAN_CALL_KERNELS = ("pack", "pass1", "compose", "main")
 KERNEL_SOURCES = {
-    "scan_main_prefill": SCAN_SOURCES, "scan_pass1_prefill": SCAN_SOURCES,
-    "scan_main_bulk": SCAN_SOURCES, "scan_pass1_bulk": SCAN_SOURCES,
+    **{f"scan_{k}_{w}": SCAN_SOURCES for k in SCAN_CALL_KERNELS for w in ("prefill", "bulk")},
     "decode": ("decode_step.hip",), "ssd": ("ssd_chunk.hip",), "ssd_decode": ("ssd_decode.hip",),
     "gemm_in_proj": ("gemm.hip",), "gemm_out_proj": ("gemm.hip",), "scan_bwd": ("scan_bwd.hip",),
 }
@@ -120,6 +136,20 @@ def recorded_traffic(kernel_key):
     except KeyError:
         return None
     return (fetch + write) * 1024.0
+
+
+def call_traffic(workload):
+    """HBM bytes of every kernel of one scan call (recorded profiles), summed;
+    None unless each kernel the call ran has a current record."""
+    total, seen = 0.0, 0
+    for k in SCAN_CALL_KERNELS:
+        t = recorded_traffic(f"scan_{k}_{workload}")
+        if t is None:
+            continue
+        total += t
+        seen += 1
+    main = recorded_traffic(f"scan_main_{workload}")
+    return total if (seen and main is not None) else None
 
 
 def dev_tensor(torch, w, key, device):
@@ -186,8 +216,18 @@ def timed_loop(torch, ssm, calls, steps, warmup, per_step=1, per_launch=True):
 
 # ------------------------------------------------------------------- workloads
 
-def scan_calls(torch, ssm, W, which, sets, device, stream=None, split=0):
-    w = W.scan_prefill() if which == "prefill" else W.scan_bulk()
+def make_scan_workload(W, which, variant="base"):
+    """The headline recipes (variant "base"), A as a model stores it
+    ("log_init": fp32 -exp(fp32 log(1..16)), which breaks the exact power
+    structure), or the general path ("general": random per-channel A and the
+    dt recipe shifted off the clip)."""
+    kw = {"base": {}, "log_init": dict(a_init="log_init"),
+          "general": dict(a_init="random", unsaturated=True)}[variant]
+    return W.scan_prefill(**kw) if which == "prefill" else W.scan_bulk(**kw)
+
+
+def scan_calls(torch, ssm, W, which, sets, device, stream=None, split=0, w=None):
+    w = w if w is not None else make_scan_workload(W, which)
     o, d = w.opts, w.dims
     calls = []
     for _ in range(sets):
@@ -443,26 +483,158 @@ def roof_hbm(nbytes, kernel_ms, traffic):
 
 # ----------------------------------------------------------------------- CPU
 
-def cpu_baseline(W):
-    """The float64 oracle on the whole layer-prefill workload, single-threaded."""
+_CPU = {}
+
+
+def _slice64(w, key, ch, axis):
+    """Channels `ch` of a workload array along `axis`, widened to float64 (the
+    bf16 bit patterns are sliced before they are widened)."""
+    a = np.take(w.arrays[key], ch, axis=axis)
+    if key in w.bf16:
+        return W_bf16_to_f64(a)
+    return np.asarray(a, np.float64)
+
+
+def W_bf16_to_f64(bits):
+    return (np.ascontiguousarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _oracle_shard(ch):
+    """The float64 oracle on channels `ch` of the workload in _CPU, on one core
+    (BLAS limited to one thread).  Returns the seconds it took."""
     from oracle import ssm_oracle as O
     from threadpoolctl import threadpool_limits
-    w = W.scan_prefill()
-    f, o = w.f64, w.opts
-    args = dict(D=f("D"), z=f("z"), conv_w=f("conv_w"), dt_raw=f("dt"), dt_w=f("dt_w"), dt_bias=f("dt_bias"),
-                dt_softplus=o["dt_softplus"], dt_min=float(o["dt_min"]), dt_max=float(o["dt_max"]))
-    x, A, B, C = f("x"), f("A"), f("B"), f("C")
+    w = _CPU["w"]
+    o = w.opts
+    ch = np.asarray(ch)
+    kw = dict(D=_slice64(w, "D", ch, 0), z=_slice64(w, "z", ch, 2), dt_bias=_slice64(w, "dt_bias", ch, 0),
+              dt_softplus=o["dt_softplus"], dt_min=float(o["dt_min"]), dt_max=float(o["dt_max"]))
+    if o["conv"]:
+        kw["conv_w"] = _slice64(w, "conv_w", ch, 0)
+    if o["dt_rank1"]:
+        kw["dt_raw"] = w.f64("dt")
+        kw["dt_w"] = _slice64(w, "dt_w", ch, 0)
+    else:
+        kw["dt"] = _slice64(w, "dt", ch, 2)
+    x, A = _slice64(w, "x", ch, 2), _slice64(w, "A", ch, 0)
+    B, C = w.f64("B"), w.f64("C")
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        O.ssm_layer_scan(x, A, B, C, **args)
-        dt = time.perf_counter() - t0
+        O.ssm_layer_scan(x, A, B, C, **kw)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(w, name):
+    """The float64 oracle on the whole workload on this host: the channels
+    (independent given B, C and dt) split into one shard per available core,
+    each run by its own process; then one core on one shard, scaled to all
+    channels.  Runs before anything touches the GPU (the workers are forked)."""
+    import multiprocessing
+    cores = len(os.sched_getaffinity(0))
+    E = w.dims["dim"]
+    shards = np.array_split(np.arange(E), cores)
+    _CPU["w"] = w
+    ctx = multiprocessing.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        per = pool.map(_oracle_shard, shards)
+    wall = time.perf_counter() - t0
+    one = _oracle_shard(shards[0])
+    _CPU.clear()
     tokens = w.dims["batch"] * w.dims["seqlen"]
-    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole layer-prefill workload (1 x 2048 tokens x 7680 channels, float64 numpy, "
-                      f"{dt:.1f} s on one core of {len(os.sched_getaffinity(0))} available)"}
+    one_all = one * E / len(shards[0])
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": round(tokens / wall, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole {name} workload ({w.dims['batch']} x {w.dims['seqlen']} tokens x {E} channels), "
+                      f"float64 numpy, its channels split into {cores} shards run by {cores} processes "
+                      f"({wall:.1f} s wall, slowest shard {max(per):.1f} s; one thread each)",
+            "single_core": {"value": round(tokens / one_all, 1), "unit": "tokens/s", "cores": 1,
+                            "sample": f"one shard of {len(shards[0])} channels on one core ({one:.1f} s), "
+                                      f"scaled to {E} channels"},
+            "cpu_model": cpu}
 
 
 # ---------------------------------------------------------------------- main
+
+WORKLOAD_NAMES = {"bulk": "Bandwidth-bound bulk scan", "prefill": "Bit-Axon SSM layer prefill"}
+VARIANT_NOTES = {
+    "log_init": "A = -exp(log(1..16)) rounded to fp32 as a model stores it (5 of the 16 entries an ulp or two off "
+                "-(n+1), so the decays are one exponential each); dt recipe unchanged",
+    "general": "A = -exp(U[0, ln 16]) drawn per (channel, state); dt recipe shifted off the clip (bias N(-4, 1)): "
+               "one exponential per state and step, softplus on every step",
+}
+
+
+def scan_step_timing(torch, ssm, calls, steps, warmup, stream):
+    """Times the steps three ways: launched back to back with the library's HIP
+    events around each call's main kernel (the kernel roofline's source),
+    replayed from a HIP graph, and launched back to back with two events
+    around the whole region (the whole call).  Returns a dict of ms."""
+    with torch.cuda.stream(stream):
+        eager, kmean, kmed = timed_loop(torch, ssm, calls, steps, warmup)
+    graphs = capture_each(torch, calls, stream)
+    whole = capture_all(torch, calls, stream)
+    graph_ms = timed_graphs(torch, graphs, whole, steps, warmup)
+    del graphs, whole
+    with torch.cuda.stream(stream):
+        launch_ms, call_ms, _ = timed_loop(torch, ssm, calls, steps, warmup, per_launch=False)
+    return dict(eager=eager, kmean=kmean, kmed=kmed, graph=graph_ms, launch=launch_ms, call=call_ms,
+                step=min(graph_ms, launch_ms))
+
+
+def scan_line(which, cfg, t, tokens):
+    """Throughput and rooflines of one scan workload from its timings."""
+    byts = cfg["bytes"]
+    ch_steps = tokens * cfg["dim"]
+    gflop = FLOPS_PER_CH_STEP[which] * ch_steps / 1e9
+    kgbs = byts / (t["kmean"] * 1e-3) / 1e9
+    cgbs = byts / (t["call"] * 1e-3) / 1e9
+    traffic = recorded_traffic(f"scan_main_{which}")
+    roof = {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "scan_kernel (full pass)", "kernel_us": round(t["kmean"] * 1e3, 2),
+            "algorithmic_bytes": byts,
+            "whole_call": {"us": round(t["call"] * 1e3, 2), "achieved": round(cgbs, 1),
+                           "frac": round(cgbs / HBM_PEAK_GBS, 4), "traffic": call_traffic(which),
+                           "note": "every kernel of one call (B/C packing, and with a time split the summary "
+                                   "pass and composition), back-to-back launches; traffic summed over them"},
+            "alu": {"achieved_tflops": round(gflop / t["kmean"], 2), "peak_tflops": FP32_VECTOR_PEAK_TFLOPS,
+                    "frac": round(gflop / t["kmean"] / FP32_VECTOR_PEAK_TFLOPS, 4),
+                    "frac_of_unpacked": round(gflop / t["kmean"] / (FP32_VECTOR_PEAK_TFLOPS / 2), 4),
+                    "flops_per_channel_step": FLOPS_PER_CH_STEP[which]}}
+    if COPY_GBS:
+        roof["frac_of_copy"] = round(kgbs / COPY_GBS, 4)
+        roof["whole_call"]["frac_of_copy"] = round(cgbs / COPY_GBS, 4)
+    return roof
+
+
+def run_variants(torch, ssm, W, which, device, steps, warmup, split=0):
+    """The workload with A as a model stores it and on the general path."""
+    out = {}
+    for v in ("log_init", "general"):
+        log(f"variant: {which} {v}")
+        w = make_scan_workload(W, which, v)
+        stream = torch.cuda.Stream(device)
+        _, calls, cfg = scan_calls(torch, ssm, W, which, 1, device, stream=stream, split=split, w=w)
+        del w
+        with torch.cuda.stream(stream):
+            _, kmean, _ = timed_loop(torch, ssm, calls, steps, warmup)
+            _, call_ms, _ = timed_loop(torch, ssm, calls, steps, warmup, per_launch=False)
+        tokens = cfg["batch"] * cfg["seq_len"]
+        out[v] = {"note": VARIANT_NOTES[v], "ms_per_call": round(call_ms, 4),
+                  "tokens_per_s": round(tokens / (call_ms * 1e-3), 1),
+                  "main_kernel_us": round(kmean * 1e3, 2),
+                  "hbm_frac_of_main_kernel": round(cfg["bytes"] / (kmean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "hbm_frac_of_call": round(cfg["bytes"] / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del calls
+        torch.cuda.empty_cache()
+    return out
+
 
 def main():
     a = parse()
@@ -470,9 +642,23 @@ def main():
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (nothing here shards or "
               f"communicates across GPUs)", file=sys.stderr)
         sys.exit(2)
+    import ssm_workloads as W
+
+    which = a.only or a.workload
+    # the headline workload is drawn once; the oracle baseline runs on it
+    # before anything touches the GPU (its worker processes are forked)
+    head_w = None
+    cpu = None
+    if which in ("bulk", "prefill"):
+        log(f"generating the {which} workload")
+        head_w = make_scan_workload(W, which)
+        if not a.no_cpu and not a.only:
+            log("oracle on the host CPU cores")
+            cpu = cpu_baseline(head_w, WORKLOAD_NAMES[which])
+            log(f"oracle: {cpu['value']} tokens/s on {cpu['cores']} cores, {cpu['single_core']['value']} on one")
+
     import torch
     import selective_state_space_03_amd as ssm
-    import ssm_workloads as W
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
@@ -521,81 +707,79 @@ def main():
         _, kcall, _ = timed_loop(torch, ssm, calls, a.steps, a.warmup, per_launch=False)
         log(f"ssd: {wall:.3f} ms/step, main kernel {kmean * 1e3:.1f} us, whole call {kcall * 1e3:.1f} us")
         return
+    if a.only in ("bulk_general", "prefill_general"):
+        base = a.only.split("_")[0]
+        w = make_scan_workload(W, base, "general")
+        stream = torch.cuda.Stream(dev)
+        _, calls, cfg = scan_calls(torch, ssm, W, base, 1, dev, stream=stream, split=a.split, w=w)
+        with torch.cuda.stream(stream):
+            _, kmean, _ = timed_loop(torch, ssm, calls, a.steps, a.warmup)
+            _, call_ms, _ = timed_loop(torch, ssm, calls, a.steps, a.warmup, per_launch=False)
+        log(f"{a.only}: {call_ms:.3f} ms per call, main kernel {kmean * 1e3:.1f} us")
+        return
 
-    which = a.only or a.workload
     # rotate buffer sets so the working set exceeds the 256 MB last-level cache
     sets = 4 if which == "prefill" else 1
-    log(f"generating the {which} workload ({sets} buffer set(s))")
+    log(f"uploading the {which} workload ({sets} buffer set(s))")
     stream = torch.cuda.Stream(dev)
-    w, calls, cfg = scan_calls(torch, ssm, W, which, sets, dev, stream=stream, split=a.split)
-    with torch.cuda.stream(stream):
-        eager, kmean, kmed = timed_loop(torch, ssm, calls, a.steps, a.warmup)
-    # the timed steps: each call's launches replayed from a HIP graph, as a
-    # serving or training loop runs them (no Python between the kernels)
-    graphs = capture_each(torch, calls, stream)
-    whole = capture_all(torch, calls, stream)
-    graph_ms = timed_graphs(torch, graphs, whole, a.steps, a.warmup)
-    # the same steps launched back to back from Python with no per-call
-    # events (the queue stays ahead of the GPU); the step time reported is
-    # the faster of the two ways of running them
-    with torch.cuda.stream(stream):
-        launch_ms, _, _ = timed_loop(torch, ssm, calls, a.steps, a.warmup, per_launch=False)
-    wall = min(graph_ms, launch_ms)
-    log(f"{which}: {graph_ms:.3f} ms/step (graph replay), {launch_ms:.3f} ms/step (launches), {eager:.3f} ms/step "
-        f"eager with per-call events, main kernel mean {kmean * 1e3:.1f} us median {kmed * 1e3:.1f} us")
-    del graphs, whole
+    w, calls, cfg = scan_calls(torch, ssm, W, which, sets, dev, stream=stream, split=a.split, w=head_w)
+    del head_w
+    t = scan_step_timing(torch, ssm, calls, a.steps, a.warmup, stream)
+    log(f"{which}: {t['graph']:.3f} ms/step (graph replay), {t['launch']:.3f} ms/step (launches), "
+        f"{t['eager']:.3f} ms/step eager with per-call events, main kernel mean {t['kmean'] * 1e3:.1f} us "
+        f"median {t['kmed'] * 1e3:.1f} us, whole call {t['call'] * 1e3:.1f} us")
     if a.only:
         return
+    del calls, w
+    torch.cuda.empty_cache()
+    global COPY_GBS
+    COPY_GBS = copy_rate(torch, dev)
     tokens = cfg["batch"] * cfg["seq_len"]
-    ch_steps = tokens * cfg["dim"]
-    value = tokens / (wall * 1e-3)
-    gflop = FLOPS_PER_CH_STEP[which] * ch_steps / 1e9
-    achieved_tf = gflop / kmean  # GFLOP / ms = TFLOP/s
-    traffic = recorded_traffic(f"scan_main_{which}")
+    wall = t["step"]
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(wall, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": ("Bit-Axon SSM layer prefill" if which == "prefill" else "bulk selective scan"),
-                   "batch": cfg["batch"], "seq_len": cfg["seq_len"], "dim": cfg["dim"], "d_state": cfg["d_state"],
-                   "storage": "bf16 in/out, fp32 state", "buffer_sets": sets},
-        "timing": "each step one ssm_scan_fwd call; ms_per_step is the faster of graph_ms_per_step (the "
-                  "calls replayed from a HIP graph holding one step per buffer set) and launch_ms_per_step "
-                  "(the calls launched back to back from Python); eager_ms_per_step launches each call with "
-                  "HIP events around its main kernel",
-        "graph_ms_per_step": round(graph_ms, 4),
-        "launch_ms_per_step": round(launch_ms, 4),
-        "eager_ms_per_step": round(eager, 4),
+        "metric": METRIC, "value": round(tokens / (wall * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(wall, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[which], "batch": cfg["batch"], "seq_len": cfg["seq_len"],
+                   "dim": cfg["dim"], "d_state": cfg["d_state"],
+                   "storage": ("bf16 u/dt/z/B/C in, bf16 y out, fp32 state" if which == "bulk"
+                               else "bf16 x/z/B/C in, fp32 r, bf16 y out, fp32 state and conv cache"),
+                   "A": "-(1..16) exact (the A_log = log(1..16) initialisation)",
+                   "dt": ("E-wide bf16 pre-activation + bias, softplus, clip [1e-3, 0.1]" if which == "bulk"
+                          else "rank-1 dt_proj of r + bias, softplus, clip [1e-3, 0.1]"),
+                   "buffer_sets": sets},
+        "timing": "each step one ssm_scan_fwd call; ms_per_step is the faster of graph_ms_per_step (the calls "
+                  "replayed from a HIP graph) and launch_ms_per_step (the calls launched back to back from "
+                  "Python); eager_ms_per_step launches each call with the library's HIP events around its "
+                  "main kernel (the roofline's kernel time)",
+        "graph_ms_per_step": round(t["graph"], 4), "launch_ms_per_step": round(t["launch"], 4),
+        "eager_ms_per_step": round(t["eager"], 4),
         "hbm_gbps": round(cfg["bytes"] / (wall * 1e-3) / 1e9, 1),
         "hbm_frac": round(cfg["bytes"] / (wall * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "channel_steps_per_s": round(ch_steps / (wall * 1e-3), 1),
-        "roofline": {"bound": "alu", "achieved": round(achieved_tf, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved_tf / FP32_VECTOR_PEAK_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "scan_kernel (full-segment pass)",
-                     "kernel_us": round(kmean * 1e3, 2), "algorithmic_bytes": cfg["bytes"],
-                     "hbm_frac_of_kernel": round(cfg["bytes"] / (kmean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "channel_steps_per_s": round(tokens * cfg["dim"] / (wall * 1e-3), 1),
+        "roofline": scan_line(which, cfg, t, tokens),
+        "copy_gbps": round(COPY_GBS, 1),
     }
-    del calls
-    torch.cuda.empty_cache()
+    if not a.no_variants:
+        out["variants"] = run_variants(torch, ssm, W, which, dev, max(3, a.steps // 4), 2, split=a.split)
 
     if not a.no_parts:
-        global COPY_GBS
-        COPY_GBS = copy_rate(torch, dev)
-        out["copy_gbps"] = round(COPY_GBS, 1)
         parts = {}
         other = "bulk" if which == "prefill" else "prefill"
         log(f"part: {other} scan")
-        _, c2, cfg2 = scan_calls(torch, ssm, W, other, 4 if other == "prefill" else 1, dev)
-        st = 10 if other == "bulk" else 50
-        wall2, km2, _ = timed_loop(torch, ssm, c2, st, 2)
+        stream2 = torch.cuda.Stream(dev)
+        _, c2, cfg2 = scan_calls(torch, ssm, W, other, 4 if other == "prefill" else 1, dev, stream=stream2)
+        t2 = scan_step_timing(torch, ssm, c2, 20 if other == "prefill" else 5, 2, stream2)
         tok2 = cfg2["batch"] * cfg2["seq_len"]
         parts[f"scan_{other}"] = {
-            "tokens_per_s": round(tok2 / (wall2 * 1e-3), 1), "ms_per_call": round(wall2, 4),
-            "hbm_gbps": round(cfg2["bytes"] / (wall2 * 1e-3) / 1e9, 1),
-            "roofline": roof_hbm(cfg2["bytes"], km2, recorded_traffic(f"scan_main_{other}")),
+            "tokens_per_s": round(tok2 / (t2["step"] * 1e-3), 1), "ms_per_call": round(t2["step"], 4),
+            "hbm_gbps": round(cfg2["bytes"] / (t2["step"] * 1e-3) / 1e9, 1),
+            "roofline": scan_line(other, cfg2, t2, tok2),
             "config": {k: cfg2[k] for k in ("batch", "seq_len", "dim", "d_state")}}
         del c2
         torch.cuda.empty_cache()
+        if not a.no_variants:
+            parts[f"scan_{other}"]["variants"] = run_variants(torch, ssm, W, other, dev, 5, 2)
 
         log("part: decode step (8 state sets, replayed from a HIP graph)")
         graph, launches, cfg3 = decode_graph(torch, ssm, W, dev)
@@ -619,6 +803,7 @@ def main():
         r4["mfma_tflops"] = round(cfg4["flops"] / (km4 * 1e-3) / 1e12, 2)
         r4["mfma_frac"] = round(r4["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
         r4["whole_call_gbps"] = round(cfg4["bytes"] / (kc4 * 1e-3) / 1e9, 1)
+        r4["whole_call_frac"] = round(cfg4["bytes"] / (kc4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         parts["chunk_scan"] = {
             "tokens_per_s": round(cfg4["seq_len"] * cfg4["batch"] / (kc4 * 1e-3), 1),
             "ms_per_call": round(kc4, 4), "main_kernel_ms": round(km4, 4), "roofline": r4,
@@ -641,14 +826,19 @@ def main():
         c7, cfg7 = bwd_calls(torch, ssm, W, dev)
         wall7, km7, _ = timed_loop(torch, ssm, c7, 10, 2)
         tok7 = cfg7["batch"] * cfg7["seq_len"]
-        # the main backward kernel per channel-step: forward recompute (decay 4 exp-lanes x 4 states,
-        # update) and the backward step, counted as in FLOPS_PER_CH_STEP: about 3x the forward's 138
         ch7 = tok7 * cfg7["dim"]
+        tf7 = BWD_FLOPS_PER_CH_STEP * ch7 / (km7 * 1e-3) / 1e12
         parts["scan_backward"] = {
             "tokens_per_s": round(tok7 / (wall7 * 1e-3), 1), "ms_per_call": round(wall7, 4),
             "main_kernel_us": round(km7 * 1e3, 2),
-            "roofline": roof_hbm(cfg7["bytes"], wall7, recorded_traffic("scan_bwd")),
-            "roofline_note": "HBM bytes of the inputs read once and the gradients written once over the whole call",
+            "roofline": {"bound": "alu", "achieved": round(tf7, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf7 / FP32_VECTOR_PEAK_TFLOPS, 4),
+                         "frac_of_unpacked": round(tf7 / (FP32_VECTOR_PEAK_TFLOPS / 2), 4),
+                         "traffic": recorded_traffic("scan_bwd"),
+                         "kernel": "bwd_main (the backward walk over 16-step segments)",
+                         "flops_per_channel_step": BWD_FLOPS_PER_CH_STEP},
+            "hbm": {"algorithmic_bytes": cfg7["bytes"],
+                    "whole_call_frac": round(cfg7["bytes"] / (wall7 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
             "config": {k: cfg7[k] for k in ("batch", "seq_len", "dim", "d_state")}}
         del c7
         torch.cuda.empty_cache()
@@ -689,12 +879,8 @@ def main():
         ],
         "pages_absolute_numbers": None,
     }
-    if not a.no_cpu:
-        log("oracle on the host CPU")
-        cb = cpu_baseline(W)
-        if which != "prefill":
-            cb["sample"] += " (the oracle baseline is quoted on the layer prefill)"
-        out["cpu_baseline"] = cb
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
