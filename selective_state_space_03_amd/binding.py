@@ -14,7 +14,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libssm_mi355x.so")
+# SSM_MI355X_LIB names another build of the same library (the host-sanitized
+# one of build_sanitized.py, for the CPU-side checks)
+LIB_PATH = os.environ.get("SSM_MI355X_LIB") or os.path.join(_HERE, "libssm_mi355x.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED", 3: "SSM_ERR_WORKSPACE", 4: "SSM_ERR_HIP"}
