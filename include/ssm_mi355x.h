@@ -230,13 +230,22 @@ ssm_status_t ssm_decode_check(const ssm_decode_params_t *p);
  *   dA[l] = sum_{i<=l} dt[i] A_h inside each chunk of chunk_size tokens (inclusive);
  *   state passing: S <- e^{dA[Q-1]} S + sum_s e^{dA[Q-1]-dA[s]} dt[s] x[s] (outer) B[s].
  * A sequence that is not a whole number of chunks ends with a shorter chunk
- * (the same formulas over its own length).  x, B, C, out (and z) must be
- * 16-byte aligned.
+ * (the same formulas over its own length).
+ * Supported: chunk_size up to 256, d_state up to 128, headdim up to 128, x,
+ * B/C, z and out each in f32 or bf16, and seqlen * max(nheads * headdim,
+ * ngroups * d_state) * 2 bytes (one batch row) below 4 GiB.  Two kernels
+ * share the work: N = 64, chunk_size = 128, bf16 x and B/C and headdim a
+ * multiple of 16 run the matrix-core kernel (x, B, C, out and z 16-byte
+ * aligned; it may cut each sequence into segments, see `segments`); every
+ * other shape runs chunk by chunk on the vector ALUs in fp32 (pointers
+ * aligned to their element size; `segments` has no effect there: every chunk
+ * already starts from the state composed ahead of it).  The result is the
+ * same function either way, up to rounding order.
  * Workspace: ssm_chunk_scan_workspace_size() bytes of device memory, 256-byte
- * aligned, owned by the caller (zero when the sequences are not cut into
- * segments); its contents on entry do not matter.
- * Supported: x and B/C in bf16, N = 64, P % 16 == 0 and P <= 128, chunk_size = 128, and
- * seqlen * max(nheads * headdim, ngroups * d_state) * 2 bytes (one batch row) below 4 GiB.
+ * aligned, owned by the caller (zero for the matrix-core kernel when the
+ * sequences are not cut into segments; batch * nchunks * nheads * (headdim *
+ * d_state + 1) floats, rounded up, for the vector-ALU kernels); its contents
+ * on entry do not matter.
  * ---------------------------------------------------------------------- */
 typedef struct ssm_chunk_params {
   uint32_t struct_size; /* = sizeof(ssm_chunk_params_t) */

@@ -253,8 +253,19 @@ ssm_status_t decode_check(const ssm_decode_params_t* p) {
 
 // ---------------------------------------------------------------- chunked SSD
 
+// The tuned MFMA kernel takes N = 64, chunk_size = 128, bf16 x and B/C and a
+// headdim that is a multiple of 16 up to 128; every other supported shape
+// runs the vector-ALU chunked kernels of ssd_generic.hip.
+bool chunk_tuned(const ssm_chunk_params_t* p) {
+  return p->d_state == ssm::kSsdN && p->chunk_size == ssm::kSsdQ && p->x_dtype == SSM_BF16 &&
+         p->bc_dtype == SSM_BF16 && p->headdim % 16 == 0 && p->headdim <= ssm::kSsdMaxP;
+}
+
 size_t chunk_ws(const ssm_chunk_params_t* p) {
   if (p->batch <= 0 || p->seqlen <= 0) return 0;
+  if (!chunk_tuned(p))
+    return ssm::chunk_generic_workspace_bytes(p->batch, p->seqlen, p->nheads, p->headdim, p->d_state,
+                                              p->chunk_size);
   return ssm::chunk_workspace_bytes(p->batch, p->seqlen, p->nheads, p->headdim, p->segments);
 }
 
@@ -268,14 +279,11 @@ ssm_status_t chunk_check(const ssm_chunk_params_t* p) {
   if (p->nheads % p->ngroups != 0) return fail(SSM_ERR_INVALID_ARG, "%s", "nheads must be a multiple of ngroups");
   if (p->segments < 0 || p->segments > ssm::kSsdMaxSeg)
     return fail(SSM_ERR_INVALID_ARG, "%s must be in [0, 16]", "segments");
-  if (p->d_state != ssm::kSsdN) return fail(SSM_ERR_UNSUPPORTED, "%s must be 64", "d_state");
-  if (p->chunk_size != ssm::kSsdQ) return fail(SSM_ERR_UNSUPPORTED, "%s must be 128", "chunk_size");
-  if (p->headdim % 16 != 0 || p->headdim > ssm::kSsdMaxP)
-    return fail(SSM_ERR_UNSUPPORTED, "%s must be a multiple of 16 and at most 128", "headdim");
+  if (p->d_state > ssm::kSsdGenMaxN) return fail(SSM_ERR_UNSUPPORTED, "%s must be at most 128", "d_state");
+  if (p->chunk_size > ssm::kSsdGenMaxQ) return fail(SSM_ERR_UNSUPPORTED, "%s must be at most 256", "chunk_size");
+  if (p->headdim > ssm::kSsdMaxP) return fail(SSM_ERR_UNSUPPORTED, "%s must be at most 128", "headdim");
   if (!valid_dtype(p->x_dtype) || !valid_dtype(p->bc_dtype) || !valid_dtype(p->out_dtype))
     return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "x/bc/out_dtype");
-  if (p->x_dtype != SSM_BF16 || p->bc_dtype != SSM_BF16)
-    return fail(SSM_ERR_UNSUPPORTED, "%s must be bf16", "x_dtype/bc_dtype");
   if (p->z && !valid_dtype(p->z_dtype)) return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "z_dtype");
   // whole chunks are read through buffer descriptors of one batch row with
   // 32-bit byte offsets
@@ -284,9 +292,17 @@ ssm_status_t chunk_check(const ssm_chunk_params_t* p) {
                                        static_cast<unsigned long long>(p->ngroups) * p->d_state) * 2ull >
       0xffffffffull)
     return fail(SSM_ERR_UNSUPPORTED, "%s", "one batch row of x, B or C must stay below 4 GiB (seqlen too long)");
-  if ((reinterpret_cast<uintptr_t>(p->x) | reinterpret_cast<uintptr_t>(p->B) | reinterpret_cast<uintptr_t>(p->C) |
-       reinterpret_cast<uintptr_t>(p->out) | reinterpret_cast<uintptr_t>(p->z)) & 15)
+  if (chunk_tuned(p) &&
+      ((reinterpret_cast<uintptr_t>(p->x) | reinterpret_cast<uintptr_t>(p->B) | reinterpret_cast<uintptr_t>(p->C) |
+        reinterpret_cast<uintptr_t>(p->out) | reinterpret_cast<uintptr_t>(p->z)) & 15))
     return fail(SSM_ERR_INVALID_ARG, "%s must be 16-byte aligned", "x/B/C/out/z");
+  if (!chunk_tuned(p) &&
+      ((reinterpret_cast<uintptr_t>(p->x) & (esize(p->x_dtype) - 1)) |
+       (reinterpret_cast<uintptr_t>(p->B) & (esize(p->bc_dtype) - 1)) |
+       (reinterpret_cast<uintptr_t>(p->C) & (esize(p->bc_dtype) - 1)) |
+       (reinterpret_cast<uintptr_t>(p->out) & (esize(p->out_dtype) - 1)) |
+       (p->z ? reinterpret_cast<uintptr_t>(p->z) & (esize(p->z_dtype) - 1) : 0)))
+    return fail(SSM_ERR_INVALID_ARG, "%s must be aligned to their element size", "x/B/C/out/z");
   if (!p->A) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "A");
   ssm_status_t s = check_dt_bounds(p->dt_min, p->dt_max);
   if (s != SSM_OK) return s;
@@ -823,6 +839,42 @@ ssm_status_t ssm_chunk_scan_fwd(const ssm_chunk_params_t* p, void* stream) {
   const ssm_status_t s = chunk_check(p);
   if (s != SSM_OK) return s;
   if (p->batch == 0) return ok();
+  if (!chunk_tuned(p)) {
+    ssm::ChunkGenericArgs g{};
+    g.x = p->x;
+    g.dt = p->dt;
+    g.dt_bias = p->dt_bias;
+    g.A = p->A;
+    g.B = p->B;
+    g.C = p->C;
+    g.D = p->D;
+    g.state_in = p->state_in;
+    g.state_out = p->state_out;
+    g.out = p->out;
+    g.z = p->z;
+    g.chunk_state = static_cast<float*>(p->workspace);
+    g.chunk_decay = reinterpret_cast<float*>(static_cast<char*>(p->workspace) +
+                                             ssm::chunk_generic_decay_offset(p->batch, p->seqlen, p->nheads,
+                                                                             p->headdim, p->d_state, p->chunk_size));
+    g.batch = p->batch;
+    g.seqlen = p->seqlen;
+    g.nheads = p->nheads;
+    g.headdim = p->headdim;
+    g.ngroups = p->ngroups;
+    g.d_state = p->d_state;
+    g.chunk_size = p->chunk_size;
+    g.nchunks = (p->seqlen + p->chunk_size - 1) / p->chunk_size;
+    g.d_per_channel = p->d_per_channel ? 1 : 0;
+    g.x_bf16 = p->x_dtype == SSM_BF16;
+    g.bc_bf16 = p->bc_dtype == SSM_BF16;
+    g.z_bf16 = p->z && p->z_dtype == SSM_BF16;
+    g.out_bf16 = p->out_dtype == SSM_BF16;
+    g.dt_softplus = p->dt_softplus ? 1 : 0;
+    g.dt_min = p->dt_min;
+    g.dt_max = p->dt_max;
+    softplus_thresholds(p->dt_min, p->dt_max, &g.sp_lo, &g.sp_hi);
+    return hip_status(ssm::launch_chunk_generic(g, static_cast<hipStream_t>(stream)));
+  }
   ssm::ChunkLaunch l{};
   ssm::ChunkKernelArgs& k = l.k;
   k.x = p->x;

@@ -182,6 +182,36 @@ struct ChunkLaunch {
 size_t chunk_workspace_bytes(int batch, int seqlen, int nheads, int headdim, int segments);
 hipError_t launch_chunk(const ChunkLaunch& l, hipStream_t stream);
 
+// ---- chunked SSD, the other shapes (ssd_generic.hip) -----------------------
+// Any chunk size up to kSsdGenMaxQ, d_state up to kSsdGenMaxN, headdim up to
+// kSsdGenMaxP, x / B / C / z in fp32 or bf16; fp32 vector arithmetic.
+constexpr int kSsdGenMaxQ = 256;
+constexpr int kSsdGenMaxN = 128;
+constexpr int kSsdGenMaxP = 128;
+
+struct ChunkGenericArgs {
+  const void* x;
+  const float* dt;
+  const float* dt_bias;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const float* state_in;
+  float* state_out;
+  void* out;
+  const void* z;
+  float* chunk_state;  // workspace (batch, nchunks, H, P, N): chunk states, then the states entering each chunk
+  float* chunk_decay;  // workspace (batch, nchunks, H): e^{sum over the chunk of dt A_h}
+  int batch, seqlen, nheads, headdim, ngroups, d_state, chunk_size, nchunks, d_per_channel;
+  int x_bf16, bc_bf16, z_bf16, out_bf16, dt_softplus;
+  float dt_min, dt_max, sp_lo, sp_hi;
+};
+
+size_t chunk_generic_workspace_bytes(int batch, int seqlen, int nheads, int headdim, int d_state, int chunk_size);
+size_t chunk_generic_decay_offset(int batch, int seqlen, int nheads, int headdim, int d_state, int chunk_size);
+hipError_t launch_chunk_generic(const ChunkGenericArgs& a, hipStream_t stream);
+
 // ---- SSD-form decode step ------------------------------------------------
 struct ChunkDecodeKernelArgs {
   const void* x;        // (Bt, H, P)

@@ -197,9 +197,11 @@ def test_chunk_validation(L):
         "z_align": (_chunk(z=_addr(8) + 2), 1),
         "out_over_z": (_chunk(z=_addr(6) + 64), 1),
         "groups": (_chunk(ngroups=3), 1),
-        "d_state": (_chunk(d_state=16), 2),
-        "chunk": (_chunk(chunk_size=64, seqlen=1024), 2),
-        "headdim": (_chunk(headdim=100), 2),
+        "d_state": (_chunk(d_state=129), 2),
+        "chunk": (_chunk(chunk_size=257, seqlen=1024), 2),
+        "headdim": (_chunk(headdim=136), 2),
+        "general_x_align": (_chunk(d_state=32, x=_addr(1) + 1), 1),
+        "general_ws_small": (_chunk(d_state=32, workspace_bytes=1024), 3),
         "row_over_4GiB": (_chunk(seqlen=1 << 22), 2),
         "null_A": (_chunk(A=None), 1),
         "out_over_x": (_chunk(out=_addr(1) + 2), 1),
@@ -212,9 +214,15 @@ def test_chunk_validation(L):
     }
     for name, (p, want) in cases.items():
         assert L.ssm_chunk_scan_check(ctypes.byref(p)) == want, (name, L.ssm_last_error())
-    assert L.ssm_chunk_scan_fwd(ctypes.byref(_chunk(d_state=16)), None) == 2
+    assert L.ssm_chunk_scan_fwd(ctypes.byref(_chunk(d_state=200)), None) == 2
     # a sequence that is not a whole number of chunks is accepted
     assert L.ssm_chunk_scan_check(ctypes.byref(_chunk(seqlen=1000))) == 0, L.ssm_last_error()
+    # the shapes of the vector-ALU kernels: other chunk sizes, d_state, headdim
+    # and fp32 inputs (aligned to their element size only)
+    for kw in (dict(chunk_size=64), dict(chunk_size=256), dict(d_state=16), dict(d_state=32), dict(d_state=128),
+               dict(headdim=100), dict(x_dtype=0, bc_dtype=0), dict(x_dtype=0, x=_addr(1) + 4),
+               dict(chunk_size=48, d_state=24, headdim=40, seqlen=1000)):
+        assert L.ssm_chunk_scan_check(ctypes.byref(_chunk(**kw))) == 0, (kw, L.ssm_last_error())
 
 
 def test_chunk_workspace_size(L):
@@ -233,6 +241,12 @@ def test_chunk_workspace_size(L):
     # more segments than chunks: one chunk per segment
     assert size(segments=16, seqlen=300) == 4 * heads * (2 * P * N + 2 * (P * N + 1))
     assert size(segments=4, seqlen=0) == 0
+    # the vector-ALU kernels: one (P x N) state and one decay per (batch,
+    # chunk, head), each part rounded up to 256 bytes; segments do not matter
+    rnd = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    assert size(d_state=32) == rnd(4 * 8 * heads * P * 32) + rnd(4 * 8 * heads)
+    assert size(d_state=32, segments=4) == size(d_state=32)
+    assert size(chunk_size=64, seqlen=1000) == rnd(4 * 16 * heads * P * N) + rnd(4 * 16 * heads)
 
 
 def _cdec(**kw):
