@@ -613,6 +613,32 @@ def scan_line(which, cfg, t, tokens):
     return roof
 
 
+def seqlen_sweep(torch, ssm, W, device, lengths=(512, 2048, 8192, 32768)):
+    """The layer-prefill recipe (batch 1, E 7680) at several sequence lengths:
+    time per call, tokens/s, and the device memory the call needs beyond its
+    inputs and outputs (the library's workspace: packed B/C rows and segment
+    summaries), beside what storing every state (L, E, N) in fp32 would take."""
+    rows = []
+    for L in lengths:
+        w = W.scan_prefill(seqlen=L)
+        stream = torch.cuda.Stream(device)
+        _, calls, cfg = scan_calls(torch, ssm, W, "prefill", 1, device, stream=stream, w=w)
+        del w
+        ws = calls[0]._keep[-1]
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+        with torch.cuda.stream(stream):
+            _, call_ms, _ = timed_loop(torch, ssm, calls, 10, 2, per_launch=False)
+        E, N = cfg["dim"], cfg["d_state"]
+        rows.append({"seq_len": L, "ms_per_call": round(call_ms, 4), "tokens_per_s": round(L / (call_ms * 1e-3), 1),
+                     "workspace_bytes": ws_bytes, "inputs_outputs_bytes": cfg["bytes"],
+                     "all_states_fp32_bytes": 4 * L * E * N})
+        del calls
+        torch.cuda.empty_cache()
+    return {"note": "batch 1, E 7680, N 16, the layer-prefill recipe; the state carried between steps stays in "
+                    "registers, so memory grows with L only through the inputs, outputs and the workspace",
+            "rows": rows}
+
+
 def run_variants(torch, ssm, W, which, device, steps, warmup, split=0):
     """The workload with A as a model stores it and on the general path."""
     out = {}
@@ -780,6 +806,9 @@ def main():
         torch.cuda.empty_cache()
         if not a.no_variants:
             parts[f"scan_{other}"]["variants"] = run_variants(torch, ssm, W, other, dev, 5, 2)
+
+        log("part: sequence-length sweep of the layer prefill")
+        parts["prefill_seqlen_sweep"] = seqlen_sweep(torch, ssm, W, dev)
 
         log("part: decode step (8 state sets, replayed from a HIP graph)")
         graph, launches, cfg3 = decode_graph(torch, ssm, W, dev)
