@@ -560,7 +560,8 @@ struct BwdWs {
 BwdWs bwd_ws(const ssm_scan_bwd_params_t* p) {
   BwdWs o{};
   const size_t Bt = p->batch, L = p->seqlen, E = p->dim, N = ssm::kScanN;
-  const size_t S = L > 0 ? ssm::bwd_segments(p->seqlen) : 0, G = (E + 15) / 16;
+  const size_t S = L > 0 ? ssm::bwd_segments(p->seqlen) : 0, R = ssm::bwd_runs(static_cast<int>(S));
+  const size_t G = ssm::bwd_blocks64(p->dim);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -574,7 +575,7 @@ BwdWs bwd_ws(const ssm_scan_bwd_params_t* p) {
   o.pB = take(Bt * L * G * N * 4);
   o.pC = take(Bt * L * G * N * 4);
   o.pr = take(p->dt_rank1 ? Bt * L * G * 4 : 0);
-  o.pe = take(Bt * S * E * ssm::kBwdPe * 4);
+  o.pe = take(Bt * R * E * ssm::kBwdPe * 4);
   o.pw = take(p->conv_w ? Bt * ((L + ssm::kConvChunk - 1) / ssm::kConvChunk) * E * 5 * 4 : 0);
   o.total = off;
   return o;

@@ -12,11 +12,16 @@
 //      the gradient entering every segment from its right (backward, from the
 //      gradient on the final state), which also gives the initial state's
 //      gradient;
-//   3. bwd_main: per segment, the states of its kSeg steps are recomputed
-//      into registers and walked backward, producing every gradient of the
-//      step; gradients summed over channels (B, C, a rank-1 dt) leave as
-//      per-wave partials, gradients summed over time (A, D, dt_w, dt_bias) as
-//      per-segment partials, and the conv input gradient as dL/dxc;
+//   3. bwd_main: a wave walks a run of kBwdRun segments, last to first; per
+//      segment the states of its kSeg steps are recomputed into registers
+//      and walked backward, producing every gradient of the step, and the
+//      reverse-time gradient passes on to the segment before in registers
+//      (only the run's last segment takes it from the composition).
+//      Gradients summed over channels (B, C, a rank-1 dt) are summed over the
+//      wave's 16 channels in registers and over the workgroup's kBwdWg waves
+//      in LDS, and leave as one partial per (step, 64 channels); gradients
+//      summed over time (A, D, dt_w, dt_bias) leave as one partial per run;
+//      the conv input gradient as dL/dxc;
 //   4. the conv's transpose and the reductions, all in a fixed order.
 // A wave first stages its segment's inputs in LDS (x with the conv's three
 // earlier steps, dt's pre-activation, dy, z for its 16 channels; B and C of
@@ -214,11 +219,13 @@ struct Lane {
   float Al2[4], An[4];  // A[e][4q + j] log2(e), A[e][4q + j]
   float dtw, d;
 
-  __device__ Lane(const BwdArgs& args, int b_, int gw_) : a(args), b(b_), gw(gw_) {
+  // live: the wave has a channel group (false for the spare waves of a
+  // ragged last workgroup, which compute on a valid group and write nothing)
+  __device__ Lane(const BwdArgs& args, int b_, int gw_, bool live = true) : a(args), b(b_), gw(gw_) {
     const int lane = threadIdx.x & 63;
     q = lane & 3;
     const int e_raw = 16 * gw + (lane >> 2);
-    act = e_raw < a.dim;
+    act = live && e_raw < a.dim;
     e = act ? e_raw : a.dim - 1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -338,7 +345,10 @@ __global__ __launch_bounds__(256) void bwd_compose(BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < kB; ++k) {
       if (s0 - k >= 0) {
-        a.qs[at(s0 - k)] = qcur;  // the gradient entering segment s0 - k from its right
+        // the gradient entering segment s0 - k from its right, kept where a
+        // run of the main pass starts (its last segment)
+        const int s = s0 - k;
+        if (s % kBwdRun == kBwdRun - 1 || s == a.nseg - 1) a.qs[at(s)] = qcur;
         qcur = fmaf(exp2_fast(al2 * dec[k]), qcur, loc[k]);
       }
     }
@@ -346,111 +356,146 @@ __global__ __launch_bounds__(256) void bwd_compose(BwdArgs a) {
   if (a.dstate_in) a.dstate_in[(static_cast<size_t>(b) * a.dim + e) * kScanN + n] = qcur;
 }
 
-__global__ __launch_bounds__(256) void bwd_main(BwdArgs a) {
+// Workgroup (block of kBwdWg channel groups, batch, run of segments); wave
+// w takes group kBwdWg * block + w.  Three waves per SIMD.
+__global__ __launch_bounds__(256, 3) void bwd_main(BwdArgs a) {
   __shared__ SegStage stage[4];
-  int b, gw, s;
-  wave_ids(a, b, gw, s);
-  if (s >= a.nseg) return;
-  const Lane c(a, b, gw);
-  const int t0 = s * kSeg, t1 = min(a.seqlen, t0 + kSeg);
-  SegStage& S = stage[threadIdx.x >> 6];
-  stage_segment<true>(a, b, gw, t0, t1, S);
-  const size_t so = ((static_cast<size_t>(b) * a.nseg + s) * a.dim + c.e) * kScanN + 4 * c.q;
-  float hin[4], Q[4];
+  // per wave and step of the segment: dB over its 16 channels, then dC, then
+  // the rank-1 dt's channel sum (rows padded to 16-byte multiples)
+  constexpr int kPart = 2 * kScanN + 1, kPartRow = (kPart + 3) / 4 * 4;
+  __shared__ float part[kBwdWg][kSeg][kPartRow];
+  static_assert(kBwdWg == 4, "one wave per group, four waves per workgroup");
+  const int wave = threadIdx.x >> 6;
+  const int nblk = bwd_blocks64(a.dim);
+  int blk = blockIdx.x;
+  const int gq = blk % nblk;
+  blk /= nblk;
+  const int b = blk % a.batch;
+  const int run = blk / a.batch;
+  const int gw_raw = gq * kBwdWg + wave;
+  const bool live = gw_raw < a.ngroups16;
+  const int gw = live ? gw_raw : a.ngroups16 - 1;
+  const Lane c(a, b, gw, live);
+  SegStage& S = stage[wave];
+  const int lane = threadIdx.x & 63;
+  const int s_lo = run * kBwdRun, s_hi = min(a.nseg, s_lo + kBwdRun) - 1;
+  const float actf = c.act ? 1.0f : 0.0f;
+  float Q[4];
   {
-    const float4 hv = *reinterpret_cast<const float4*>(a.hs + so);
+    const size_t so = ((static_cast<size_t>(b) * a.nseg + s_hi) * a.dim + c.e) * kScanN + 4 * c.q;
     const float4 qv = *reinterpret_cast<const float4*>(a.qs + so);
-    hin[0] = hv.x; hin[1] = hv.y; hin[2] = hv.z; hin[3] = hv.w;
     Q[0] = qv.x; Q[1] = qv.y; Q[2] = qv.z; Q[3] = qv.w;
   }
-  // the segment's states, recomputed
-  float hist[kSeg][4];
-  {
-    float h[4] = {hin[0], hin[1], hin[2], hin[3]};
+  float dA[4] = {0.0f, 0.0f, 0.0f, 0.0f}, dD = 0.0f, ddtw = 0.0f, ddtb = 0.0f;
+#pragma unroll 1
+  for (int s = s_hi; s >= s_lo; --s) {
+    const int t0 = s * kSeg, t1 = min(a.seqlen, t0 + kSeg);
+    stage_segment<true>(a, b, gw, t0, t1, S);
+    float hin[4];
+    {
+      const size_t so = ((static_cast<size_t>(b) * a.nseg + s) * a.dim + c.e) * kScanN + 4 * c.q;
+      const float4 hv = *reinterpret_cast<const float4*>(a.hs + so);
+      hin[0] = hv.x; hin[1] = hv.y; hin[2] = hv.z; hin[3] = hv.w;
+    }
+    // the segment's states, recomputed
+    float hist[kSeg][4];
+    {
+      float h[4] = {hin[0], hin[1], hin[2], hin[3]};
 #pragma unroll
-    for (int i = 0; i < kSeg; ++i) {
-      if (t0 + i < t1) {
-        float bv[4], av[4];
-        const float u = Lane::at(S.u, i);
-        const float dt = Lane::at(S.dt, i);
-        c.sbc(S.B, i, bv);
-        c.decay(dt, av);
+      for (int i = 0; i < kSeg; ++i) {
+        if (t0 + i < t1) {
+          float bv[4], av[4];
+          const float u = Lane::at(S.u, i);
+          const float dt = Lane::at(S.dt, i);
+          c.sbc(S.B, i, bv);
+          c.decay(dt, av);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) h[j] = fmaf(av[j], h[j], dt * u * bv[j]);
+          for (int j = 0; j < 4; ++j) h[j] = fmaf(av[j], h[j], dt * u * bv[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hist[i][j] = h[j];
+      }
+    }
+#pragma unroll
+    for (int i = kSeg - 1; i >= 0; --i) {
+      if (t0 + i >= t1) continue;
+      const int t = t0 + i;
+      float hprev[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hprev[j] = i > 0 ? hist[i - 1][j] : hin[j];
+      float bv[4], cv[4], av[4];
+      const float u = Lane::at(S.u, i);
+      const float dt = Lane::at(S.dt, i);
+      c.sbc(S.B, i, bv);
+      c.sbc(S.C, i, cv);
+      c.decay(dt, av);
+      const float dyc = Lane::at(S.dyc, i);
+      float G[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) G[j] = fmaf(dyc, cv[j], Q[j]);
+      // dz = dy * yc * SiLU'(z), yc = C . h_t + D u
+      if (a.z) {
+        float yp = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yp = fmaf(cv[j], hist[i][j], yp);
+        const float yc = fmaf(c.d, u, quad_sum(yp));
+        if (a.dz && c.act && c.q == 0) a.dz[c.be(t)] = Lane::at(S.dzf, i) * yc;
+      }
+      float pdt = 0.0f, pdu = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pdt = fmaf(G[j], fmaf(c.An[j] * av[j], hprev[j], u * bv[j]), pdt);
+        pdu = fmaf(G[j] * dt, bv[j], pdu);
+        dA[j] = fmaf(G[j] * dt * av[j], hprev[j], dA[j]);
+      }
+      const float ddt = quad_sum(pdt);
+      const float du = fmaf(dyc, c.d, quad_sum(pdu));
+      // dB_t = sum_e G dt u, dC_t = sum_e dyc h_t: this wave's 16 channels,
+      // into LDS (lanes 0..3 hold states 4 lane .. 4 lane + 3)
+      float sB[4], sC[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sB[j] = chan_sum(actf * G[j] * dt * u);
+        sC[j] = chan_sum(actf * dyc * hist[i][j]);
+      }
+      if (lane < 4) {
+        *reinterpret_cast<float4*>(&part[wave][i][4 * lane]) = make_float4(sB[0], sB[1], sB[2], sB[3]);
+        *reinterpret_cast<float4*>(&part[wave][i][kScanN + 4 * lane]) = make_float4(sC[0], sC[1], sC[2], sC[3]);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) hist[i][j] = h[j];
+      for (int j = 0; j < 4; ++j) Q[j] = av[j] * G[j];
+      dD = fmaf(dyc, u, dD);
+      const float dpre = ddt * Lane::at(S.dpf, i);
+      ddtb += dpre;
+      if (a.dt_rank1) {
+        const float r = static_cast<const float*>(a.dt)[static_cast<size_t>(b) * a.seqlen + t];
+        ddtw = fmaf(dpre, r, ddtw);
+        const float sr = chan_sum(c.q == 0 ? actf * dpre * c.dtw : 0.0f);
+        if (lane == 0) part[wave][i][2 * kScanN] = sr;
+      } else if (a.ddt && c.act && c.q == 0) {
+        a.ddt[c.be(t)] = dpre;
+      }
+      if (c.act && c.q == 0) {
+        if (a.conv_w) a.dxc[c.be(t)] = du * Lane::at(S.dsx, i);
+        else if (a.dx) a.dx[c.be(t)] = du;
+      }
     }
-  }
-  const float actf = c.act ? 1.0f : 0.0f;
-  float dA[4] = {0.0f, 0.0f, 0.0f, 0.0f}, dD = 0.0f, ddtw = 0.0f, ddtb = 0.0f;
-#pragma unroll
-  for (int i = kSeg - 1; i >= 0; --i) {
-    if (t0 + i >= t1) continue;
-    const int t = t0 + i;
-    float hprev[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hprev[j] = i > 0 ? hist[i - 1][j] : hin[j];
-    float bv[4], cv[4], av[4];
-    const float u = Lane::at(S.u, i);
-    const float dt = Lane::at(S.dt, i);
-    c.sbc(S.B, i, bv);
-    c.sbc(S.C, i, cv);
-    c.decay(dt, av);
-    const float dyc = Lane::at(S.dyc, i);
-    float G[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) G[j] = fmaf(dyc, cv[j], Q[j]);
-    // dz = dy * yc * SiLU'(z), yc = C . h_t + D u
-    if (a.z) {
-      float yp = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) yp = fmaf(cv[j], hist[i][j], yp);
-      const float yc = fmaf(c.d, u, quad_sum(yp));
-      if (a.dz && c.act && c.q == 0) a.dz[c.be(t)] = Lane::at(S.dzf, i) * yc;
+    // the workgroup's partials of this segment: summed over its waves in a
+    // fixed order, one row per (step, block of 64 channels)
+    __syncthreads();
+    const int nb = t1 - t0;
+    for (int k = threadIdx.x; k < nb * kPart; k += 256) {
+      const int i = k / kPart, v = k % kPart;
+      const float sum = ((part[0][i][v] + part[1][i][v]) + part[2][i][v]) + part[3][i][v];
+      const size_t row = static_cast<size_t>(b) * a.seqlen + t0 + i;
+      if (v < kScanN) a.pB[(row * nblk + gq) * kScanN + v] = sum;
+      else if (v < 2 * kScanN) a.pC[(row * nblk + gq) * kScanN + (v - kScanN)] = sum;
+      else if (a.dt_rank1) a.pr[row * nblk + gq] = sum;
     }
-    float pdt = 0.0f, pdu = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pdt = fmaf(G[j], fmaf(c.An[j] * av[j], hprev[j], u * bv[j]), pdt);
-      pdu = fmaf(G[j] * dt, bv[j], pdu);
-      dA[j] = fmaf(G[j] * dt * av[j], hprev[j], dA[j]);
-    }
-    const float ddt = quad_sum(pdt);
-    const float du = fmaf(dyc, c.d, quad_sum(pdu));
-    // dB_t = sum_e G dt u, dC_t = sum_e dyc h_t: this wave's 16 channels
-    float sB[4], sC[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sB[j] = chan_sum(actf * G[j] * dt * u);
-      sC[j] = chan_sum(actf * dyc * hist[i][j]);
-    }
-    const int lane = threadIdx.x & 63;
-    if (lane < 4) {
-      const size_t po = ((static_cast<size_t>(b) * a.seqlen + t) * a.ngroups16 + gw) * kScanN + 4 * lane;
-      *reinterpret_cast<float4*>(a.pB + po) = make_float4(sB[0], sB[1], sB[2], sB[3]);
-      *reinterpret_cast<float4*>(a.pC + po) = make_float4(sC[0], sC[1], sC[2], sC[3]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) Q[j] = av[j] * G[j];
-    dD = fmaf(dyc, u, dD);
-    const float dpre = ddt * Lane::at(S.dpf, i);
-    ddtb += dpre;
-    if (a.dt_rank1) {
-      const float r = static_cast<const float*>(a.dt)[static_cast<size_t>(b) * a.seqlen + t];
-      ddtw = fmaf(dpre, r, ddtw);
-      const float sr = chan_sum(c.q == 0 ? actf * dpre * c.dtw : 0.0f);
-      if (lane == 0) a.pr[(static_cast<size_t>(b) * a.seqlen + t) * a.ngroups16 + gw] = sr;
-    } else if (a.ddt && c.act && c.q == 0) {
-      a.ddt[c.be(t)] = dpre;
-    }
-    if (c.act && c.q == 0) {
-      if (a.conv_w) a.dxc[c.be(t)] = du * Lane::at(S.dsx, i);
-      else if (a.dx) a.dx[c.be(t)] = du;
-    }
+    __syncthreads();
   }
   if (!c.act) return;
-  float* pe = a.pe + ((static_cast<size_t>(b) * a.nseg + s) * a.dim + c.e) * kBwdPe;
+  float* pe = a.pe + ((static_cast<size_t>(b) * bwd_runs(a.nseg) + run) * a.dim + c.e) * kBwdPe;
   *reinterpret_cast<float4*>(pe + 4 * c.q) = make_float4(dA[0], dA[1], dA[2], dA[3]);
   if (c.q == 0) {
     pe[16] = dD;
@@ -533,17 +578,18 @@ __global__ __launch_bounds__(256) void bwd_conv_w(BwdArgs a) {
   }
 }
 
-// sums over the channel groups, one workgroup per (b, t) row: thread (slice,
-// n) adds the groups slice, slice + 16, ... of dB and dC, then the 16 slices
-// are added in order (the rank-1 dt the same way over 256 slices)
+// sums over the 64-channel blocks, one workgroup per (b, t) row: thread
+// (slice, n) adds the blocks slice, slice + 16, ... of dB and dC, then the 16
+// slices are added in order (the rank-1 dt the same way over 256 slices)
 __global__ __launch_bounds__(256) void bwd_reduce_bc(BwdArgs a) {
   __shared__ float sb[16][kScanN], sc[16][kScanN], sr[256];
   const size_t row = blockIdx.x;
   const int n = threadIdx.x & 15, sl = threadIdx.x >> 4;
-  const float* pb = a.pB + row * a.ngroups16 * kScanN;
-  const float* pc = a.pC + row * a.ngroups16 * kScanN;
+  const int nblk = bwd_blocks64(a.dim);
+  const float* pb = a.pB + row * nblk * kScanN;
+  const float* pc = a.pC + row * nblk * kScanN;
   float vb = 0.0f, vc = 0.0f;
-  for (int g = sl; g < a.ngroups16; g += 16) {
+  for (int g = sl; g < nblk; g += 16) {
     vb += pb[g * kScanN + n];
     vc += pc[g * kScanN + n];
   }
@@ -551,7 +597,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(BwdArgs a) {
   sc[sl][n] = vc;
   float vr = 0.0f;
   if (a.dt_rank1) {
-    for (int g = threadIdx.x; g < a.ngroups16; g += 256) vr += a.pr[row * a.ngroups16 + g];
+    for (int g = threadIdx.x; g < nblk; g += 256) vr += a.pr[row * nblk + g];
   }
   sr[threadIdx.x] = vr;
   __syncthreads();
@@ -571,7 +617,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(BwdArgs a) {
   }
 }
 
-// sums over (batch, segment) of the per-channel gradients and over time
+// sums over (batch, segment run) of the per-channel gradients and over time
 // chunks of the conv parameters; one thread per (channel, item)
 __global__ __launch_bounds__(256) void bwd_reduce_e(BwdArgs a) {
   const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -581,9 +627,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_e(BwdArgs a) {
   float v = 0.0f;
   if (j < kBwdPe) {
     if (j >= 19) return;
+    const int runs = bwd_runs(a.nseg);
     for (int b = 0; b < a.batch; ++b)
 #pragma unroll 8
-      for (int s = 0; s < a.nseg; ++s) v += a.pe[((static_cast<size_t>(b) * a.nseg + s) * a.dim + e) * kBwdPe + j];
+      for (int r = 0; r < runs; ++r) v += a.pe[((static_cast<size_t>(b) * runs + r) * a.dim + e) * kBwdPe + j];
     if (j < kScanN) {
       if (a.dA) a.dA[static_cast<size_t>(e) * kScanN + j] = v;
     } else if (j == 16) {
@@ -617,12 +664,13 @@ hipError_t launch_scan_bwd(const BwdArgs& a, hipStream_t s) {
   if (a.batch == 0 || a.seqlen == 0) return hipSuccess;
   const size_t waves = static_cast<size_t>(a.batch) * a.ngroups16 * a.nseg;
   const unsigned wblocks = static_cast<unsigned>((waves + 3) / 4);
+  const unsigned mblocks = static_cast<unsigned>(static_cast<size_t>(a.batch) * bwd_blocks64(a.dim) * bwd_runs(a.nseg));
   hipLaunchKernelGGL(bwd_summary, dim3(wblocks), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_compose, dim3(blocks_for(static_cast<size_t>(a.batch) * a.dim * kScanN)), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  e = timed_launch(s, [&] { hipLaunchKernelGGL(bwd_main, dim3(wblocks), dim3(256), 0, s, a); });
+  e = timed_launch(s, [&] { hipLaunchKernelGGL(bwd_main, dim3(mblocks), dim3(256), 0, s, a); });
   if (e != hipSuccess) return e;
   const size_t bt = static_cast<size_t>(a.batch) * a.seqlen;
   if (a.conv_w) {

@@ -239,7 +239,9 @@ hipError_t launch_chunk_decode(const ChunkDecodeLaunch& l, hipStream_t stream);
 
 // ---- backward of the scan stage --------------------------------------------
 constexpr int kBwdSeg = 16;     // time steps per segment (states recomputed in registers)
-constexpr int kBwdPe = 20;      // per-(batch, segment, channel) partial: dA[16], dD, ddt_w, ddt_bias, pad
+constexpr int kBwdRun = 4;      // segments one wave of the main pass walks, last to first
+constexpr int kBwdWg = 4;       // 16-channel groups per main-pass workgroup (one wave each)
+constexpr int kBwdPe = 20;      // per-(batch, segment run, channel) partial: dA[16], dD, ddt_w, ddt_bias, pad
 constexpr int kConvChunk = 64;  // time steps per partial of the conv weight gradient
 
 struct BwdArgs {
@@ -270,6 +272,10 @@ struct BwdArgs {
 };
 
 int bwd_segments(int seqlen);
+// Segment runs (kBwdRun segments each) and main-pass channel blocks (kBwdWg
+// groups of 16 channels each): the granularity of the partial sums.
+__host__ __device__ inline int bwd_runs(int nseg) { return (nseg + kBwdRun - 1) / kBwdRun; }
+__host__ __device__ inline int bwd_blocks64(int dim) { return ((dim + 15) / 16 + kBwdWg - 1) / kBwdWg; }
 hipError_t launch_scan_bwd(const BwdArgs& a, hipStream_t stream);
 
 // ---- projection GEMM: C = A W^T --------------------------------------------

@@ -36,11 +36,13 @@ def test_bwd_tiny_fp32(unsat):
     _compare(W.scan_tiny(unsaturated=unsat))
 
 
-@pytest.mark.parametrize("seqlen", [1, 16, 37, 300])
+@pytest.mark.parametrize("seqlen", [1, 16, 37, 64, 65, 129, 300])
 def test_bwd_prefill_recipe(seqlen):
     """bf16 x/z, conv + SiLU, rank-1 dt, bf16 B/C at batch 2, E 200 (a ragged
-    channel group), with an initial state, a conv cache and a gradient on the
-    final state; ragged last segment."""
+    channel group, and a last block of four groups with three spare waves),
+    with an initial state, a conv cache and a gradient on the final state;
+    ragged last segment, and runs of four segments that end exactly at the
+    sequence end (64), one step past it (65) or part-way (129, 300)."""
     w = W.scan_prefill(batch=2, seqlen=seqlen, dim=200, unsaturated=True)
     rng = np.random.Generator(np.random.PCG64(5))
     _compare(w, state_in=rng.standard_normal((2, 200, 16)).astype(np.float32) * 0.5,
