@@ -554,7 +554,7 @@ ssm_status_t layer_check(const ssm_layer_params_t* p) {
 // ---------------------------------------------------------------- scan backward
 
 struct BwdWs {
-  size_t hs, qs, sdt, dxc, pB, pC, pr, pe, pw, total;
+  size_t hs, qs, sdt, xb, pB, pC, pr, pe, total;
 };
 
 BwdWs bwd_ws(const ssm_scan_bwd_params_t* p) {
@@ -571,12 +571,11 @@ BwdWs bwd_ws(const ssm_scan_bwd_params_t* p) {
   o.hs = take(Bt * S * E * N * 4);
   o.qs = take(Bt * S * E * N * 4);
   o.sdt = take(Bt * S * E * 4);
-  o.dxc = take(p->conv_w ? Bt * L * E * 4 : 0);
+  o.xb = take(p->conv_w ? Bt * R * 3 * E * 4 : 0);
   o.pB = take(Bt * L * G * N * 4);
   o.pC = take(Bt * L * G * N * 4);
   o.pr = take(p->dt_rank1 ? Bt * L * G * 4 : 0);
   o.pe = take(Bt * R * E * ssm::kBwdPe * 4);
-  o.pw = take(p->conv_w ? Bt * ((L + ssm::kConvChunk - 1) / ssm::kConvChunk) * E * 5 * 4 : 0);
   o.total = off;
   return o;
 }
@@ -1127,12 +1126,11 @@ ssm_status_t ssm_scan_bwd(const ssm_scan_bwd_params_t* p, void* stream) {
   a.hs = wf(o.hs);
   a.qs = wf(o.qs);
   a.sdt = wf(o.sdt);
-  a.dxc = p->conv_w ? wf(o.dxc) : nullptr;
+  a.xb = p->conv_w ? wf(o.xb) : nullptr;
   a.pB = wf(o.pB);
   a.pC = wf(o.pC);
   a.pr = p->dt_rank1 ? wf(o.pr) : nullptr;
   a.pe = wf(o.pe);
-  a.pw = p->conv_w ? wf(o.pw) : nullptr;
   a.batch = p->batch;
   a.seqlen = p->seqlen;
   a.dim = p->dim;

@@ -20,9 +20,13 @@
 //      Gradients summed over channels (B, C, a rank-1 dt) are summed over the
 //      wave's 16 channels in registers and over the workgroup's kBwdWg waves
 //      in LDS, and leave as one partial per (step, 64 channels); gradients
-//      summed over time (A, D, dt_w, dt_bias) leave as one partial per run;
-//      the conv input gradient as dL/dxc;
-//   4. the conv's transpose and the reductions, all in a fixed order.
+//      summed over time (A, D, dt_w, dt_bias, the conv weights and bias)
+//      leave as one partial per run.  The conv's transpose is applied on the
+//      way: walking backward, the four lanes of a channel hold the conv-output
+//      gradients of steps t .. t+3, so dx_t is a quad sum; only the first three
+//      steps of a run are kept, for the last three dx of the run before it;
+//   4. the run-boundary terms of dx, the conv cache's gradient and the
+//      reductions, all in a fixed order.
 // A wave first stages its segment's inputs in LDS (x with the conv's three
 // earlier steps, dt's pre-activation, dy, z for its 16 channels; B and C of
 // the segment), with coalesced loads issued together, so the steps read LDS
@@ -218,6 +222,7 @@ struct Lane {
   bool act;
   float Al2[4], An[4];  // A[e][4q + j] log2(e), A[e][4q + j]
   float dtw, d;
+  float wt;             // conv weight 3 - q: the tap that meets the conv-output gradient of step t + q
 
   // live: the wave has a channel group (false for the spare waves of a
   // ragged last workgroup, which compute on a valid group and write nothing)
@@ -234,6 +239,7 @@ struct Lane {
     }
     dtw = a.dt_rank1 ? a.dt_w[e] : 0.0f;
     d = a.D ? a.D[e] : 0.0f;
+    wt = a.conv_w ? a.conv_w[static_cast<size_t>(e) * 4 + (3 - q)] : 0.0f;
   }
   __device__ size_t be(int t) const { return (static_cast<size_t>(b) * a.seqlen + t) * a.dim + e; }
   // staged value of step i of the segment for this lane's channel (slot lane / 4)
@@ -387,6 +393,10 @@ __global__ __launch_bounds__(256, 3) void bwd_main(BwdArgs a) {
     Q[0] = qv.x; Q[1] = qv.y; Q[2] = qv.z; Q[3] = qv.w;
   }
   float dA[4] = {0.0f, 0.0f, 0.0f, 0.0f}, dD = 0.0f, ddtw = 0.0f, ddtb = 0.0f;
+  // conv: lane q's weight gradient dw[q], the bias gradient, and the
+  // conv-output gradient of step t + q (zero past the run's end)
+  float dwq = 0.0f, dbq = 0.0f, win = 0.0f;
+  const int run_t0 = s_lo * kSeg;
 #pragma unroll 1
   for (int s = s_hi; s >= s_lo; --s) {
     const int t0 = s * kSeg, t1 = min(a.seqlen, t0 + kSeg);
@@ -475,9 +485,23 @@ __global__ __launch_bounds__(256, 3) void bwd_main(BwdArgs a) {
       } else if (a.ddt && c.act && c.q == 0) {
         a.ddt[c.be(t)] = dpre;
       }
-      if (c.act && c.q == 0) {
-        if (a.conv_w) a.dxc[c.be(t)] = du * Lane::at(S.dsx, i);
-        else if (a.dx) a.dx[c.be(t)] = du;
+      if (a.conv_w) {
+        const float dxc = du * Lane::at(S.dsx, i);  // dL / d(conv output) at t
+        const float v = c.q == 0 ? dxc : win;       // lane q: that of step t + q
+        // dx_t = w3 dxc_t + w2 dxc_{t+1} + w1 dxc_{t+2} + w0 dxc_{t+3}; for
+        // the last three steps of a run the terms past its end are added
+        // by bwd_conv_fix
+        const float dxt = quad_sum(c.wt * v);
+        win = dpp<0x90>(v);                         // quad_perm 0 0 1 2: lane q <- lane q - 1
+        dwq = fmaf(dxc, S.xr[i + c.q][(threadIdx.x & 63) >> 2], dwq);  // tap q meets raw x_{t-3+q}
+        dbq += dxc;
+        if (c.act && c.q == 0) {
+          if (a.dx) a.dx[c.be(t)] = dxt;
+          if (t - run_t0 < 3)
+            a.xb[((static_cast<size_t>(b) * bwd_runs(a.nseg) + run) * 3 + (t - run_t0)) * a.dim + c.e] = dxc;
+        }
+      } else if (c.act && c.q == 0 && a.dx) {
+        a.dx[c.be(t)] = du;
       }
     }
     // the workgroup's partials of this segment: summed over its waves in a
@@ -497,85 +521,50 @@ __global__ __launch_bounds__(256, 3) void bwd_main(BwdArgs a) {
   if (!c.act) return;
   float* pe = a.pe + ((static_cast<size_t>(b) * bwd_runs(a.nseg) + run) * a.dim + c.e) * kBwdPe;
   *reinterpret_cast<float4*>(pe + 4 * c.q) = make_float4(dA[0], dA[1], dA[2], dA[3]);
+  pe[19 + c.q] = dwq;
   if (c.q == 0) {
     pe[16] = dD;
     pe[17] = ddtw;
     pe[18] = ddtb;
+    pe[23] = dbq;
   }
 }
 
-// conv transpose: dx[t] = sum_k w[k] dxc[t + 3 - k]; one thread per (b, run
-// of kDxRun steps, e), dxc read once into a sliding window
-constexpr int kDxRun = 16;
-__global__ __launch_bounds__(256) void bwd_conv_dx(BwdArgs a) {
+// The conv terms that cross a run boundary, one thread per (batch, run,
+// channel): the last three dx of the run before run r > 0 take the terms of
+// the first three conv-output gradients of run r; run 0's three give the
+// conv cache's gradient (cache entry j is x at j - 3: sum_{k <= j} w_k dxc_{j-k}).
+__global__ __launch_bounds__(256) void bwd_conv_fix(BwdArgs a) {
   const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int runs = (a.seqlen + kDxRun - 1) / kDxRun;
-  const size_t total = static_cast<size_t>(a.batch) * runs * a.dim;
-  if (i >= total || !a.dx) return;
+  const int runs = bwd_runs(a.nseg);
+  if (i >= static_cast<size_t>(a.batch) * runs * a.dim) return;
   const int e = static_cast<int>(i % a.dim);
-  const int run = static_cast<int>((i / a.dim) % runs);
+  const int r = static_cast<int>((i / a.dim) % runs);
   const int b = static_cast<int>(i / (static_cast<size_t>(a.dim) * runs));
-  const int t0 = run * kDxRun;
-  const size_t row = static_cast<size_t>(b) * a.seqlen;
-  const float4 w = reinterpret_cast<const float4*>(a.conv_w)[e];
-  float g[kDxRun + 3];
+  const int R = r * kBwdRun * kSeg;  // first step of run r
+  const float4 w4 = reinterpret_cast<const float4*>(a.conv_w)[e];
+  const float w[4] = {w4.x, w4.y, w4.z, w4.w};
+  float g[3];
 #pragma unroll
-  for (int k = 0; k < kDxRun + 3; ++k) {
-    const int t = t0 + k;
-    g[k] = t < a.seqlen ? a.dxc[(row + t) * a.dim + e] : 0.0f;
-  }
+  for (int k = 0; k < 3; ++k)
+    g[k] = R + k < a.seqlen ? a.xb[((static_cast<size_t>(b) * runs + r) * 3 + k) * a.dim + e] : 0.0f;
+  if (r == 0) {
+    if (a.dconv_cache) {
 #pragma unroll
-  for (int k = 0; k < kDxRun; ++k) {
-    const int t = t0 + k;
-    if (t < a.seqlen)
-      a.dx[(row + t) * a.dim + e] = fmaf(w.x, g[k + 3], fmaf(w.y, g[k + 2], fmaf(w.z, g[k + 1], w.w * g[k])));
-  }
-}
-
-// conv weights, bias and cache gradients: per channel, partial sums over
-// chunks of kConvChunk time steps of one batch row (one thread per (chunk,
-// channel)); the cache gradient from the first 3 steps of each row
-__global__ __launch_bounds__(256) void bwd_conv_w(BwdArgs a) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  const int chunk = blockIdx.y;  // over batch * chunks per row
-  if (e >= a.dim) return;
-  const int cpr = (a.seqlen + kConvChunk - 1) / kConvChunk;
-  const int b = chunk / cpr, c0 = (chunk % cpr) * kConvChunk;
-  const int c1 = min(a.seqlen, c0 + kConvChunk);
-  const float* cache = a.conv_cache_in ? a.conv_cache_in + (static_cast<size_t>(b) * a.dim + e) * 3 : nullptr;
-  auto raw = [&](int t) -> float {
-    if (t >= 0) return ldx(a.x, (static_cast<size_t>(b) * a.seqlen + t) * a.dim + e, a.x_bf16);
-    return cache ? cache[3 + t] : 0.0f;
-  };
-  float dw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, db = 0.0f;
-  float win[4] = {0.0f, raw(c0 - 3), raw(c0 - 2), raw(c0 - 1)};  // raw x at t-3 .. t
-  for (int t = c0; t < c1; ++t) {
-    win[0] = win[1];
-    win[1] = win[2];
-    win[2] = win[3];
-    win[3] = raw(t);
-    const float g = a.dxc[(static_cast<size_t>(b) * a.seqlen + t) * a.dim + e];
+      for (int j = 0; j < 3; ++j) {
+        float v = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) dw[k] = fmaf(g, win[k], dw[k]);
-    db += g;
-  }
-  float* pw = a.pw + (static_cast<size_t>(chunk) * a.dim + e) * 5;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) pw[k] = dw[k];
-  pw[4] = db;
-  if (c0 == 0 && a.dconv_cache) {
-    // xpad position j (0..2) is cache entry j: d = sum_{k <= j} dxc[j - k] w[k]
-    const float4 w = reinterpret_cast<const float4*>(a.conv_w)[e];
-    const float wk[4] = {w.x, w.y, w.z, w.w};
-    for (int j = 0; j < 3; ++j) {
-      float v = 0.0f;
-      for (int k = 0; k <= j; ++k) {
-        const int tt = j - k;
-        if (tt < a.seqlen) v = fmaf(a.dxc[(static_cast<size_t>(b) * a.seqlen + tt) * a.dim + e], wk[k], v);
+        for (int k = 0; k <= j; ++k) v = fmaf(g[j - k], w[k], v);
+        a.dconv_cache[(static_cast<size_t>(b) * a.dim + e) * 3 + j] = v;
       }
-      a.dconv_cache[(static_cast<size_t>(b) * a.dim + e) * 3 + j] = v;
     }
+    return;
   }
+  if (!a.dx) return;
+  float* dx = a.dx + (static_cast<size_t>(b) * a.seqlen + R) * a.dim + e;
+  dx[-3 * static_cast<ptrdiff_t>(a.dim)] += w[0] * g[0];
+  dx[-2 * static_cast<ptrdiff_t>(a.dim)] += fmaf(w[0], g[1], w[1] * g[0]);
+  dx[-1 * static_cast<ptrdiff_t>(a.dim)] += fmaf(w[0], g[2], fmaf(w[1], g[1], w[2] * g[0]));
 }
 
 // sums over the 64-channel blocks, one workgroup per (b, t) row: thread
@@ -617,41 +606,26 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(BwdArgs a) {
   }
 }
 
-// sums over (batch, segment run) of the per-channel gradients and over time
-// chunks of the conv parameters; one thread per (channel, item)
+// sums over (batch, segment run) of the per-channel gradients; one thread
+// per (channel, item)
 __global__ __launch_bounds__(256) void bwd_reduce_e(BwdArgs a) {
   const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  constexpr int kItems = kBwdPe + 5;
-  if (i >= static_cast<size_t>(a.dim) * kItems) return;
-  const int e = static_cast<int>(i / kItems), j = static_cast<int>(i % kItems);
+  if (i >= static_cast<size_t>(a.dim) * kBwdPe) return;
+  const int e = static_cast<int>(i / kBwdPe), j = static_cast<int>(i % kBwdPe);
+  float* out = nullptr;
+  if (j < kScanN) out = a.dA ? a.dA + static_cast<size_t>(e) * kScanN + j : nullptr;
+  else if (j == 16) out = a.dD ? a.dD + e : nullptr;
+  else if (j == 17) out = a.ddt_w ? a.ddt_w + e : nullptr;
+  else if (j == 18) out = a.ddt_bias ? a.ddt_bias + e : nullptr;
+  else if (j < 23) out = a.dconv_w ? a.dconv_w + static_cast<size_t>(e) * 4 + (j - 19) : nullptr;
+  else out = a.dconv_b ? a.dconv_b + e : nullptr;
+  if (!out) return;
+  const int runs = bwd_runs(a.nseg);
   float v = 0.0f;
-  if (j < kBwdPe) {
-    if (j >= 19) return;
-    const int runs = bwd_runs(a.nseg);
-    for (int b = 0; b < a.batch; ++b)
+  for (int b = 0; b < a.batch; ++b)
 #pragma unroll 8
-      for (int r = 0; r < runs; ++r) v += a.pe[((static_cast<size_t>(b) * runs + r) * a.dim + e) * kBwdPe + j];
-    if (j < kScanN) {
-      if (a.dA) a.dA[static_cast<size_t>(e) * kScanN + j] = v;
-    } else if (j == 16) {
-      if (a.dD) a.dD[e] = v;
-    } else if (j == 17) {
-      if (a.ddt_w) a.ddt_w[e] = v;
-    } else {
-      if (a.ddt_bias) a.ddt_bias[e] = v;
-    }
-    return;
-  }
-  if (!a.conv_w) return;
-  const int k = j - kBwdPe;  // 0..3 weights, 4 bias
-  const int chunks = a.batch * ((a.seqlen + kConvChunk - 1) / kConvChunk);
-#pragma unroll 8
-  for (int c = 0; c < chunks; ++c) v += a.pw[(static_cast<size_t>(c) * a.dim + e) * 5 + k];
-  if (k < 4) {
-    if (a.dconv_w) a.dconv_w[static_cast<size_t>(e) * 4 + k] = v;
-  } else if (a.dconv_b) {
-    a.dconv_b[e] = v;
-  }
+    for (int r = 0; r < runs; ++r) v += a.pe[((static_cast<size_t>(b) * runs + r) * a.dim + e) * kBwdPe + j];
+  *out = v;
 }
 
 unsigned blocks_for(size_t n) { return static_cast<unsigned>((n + 255) / 256); }
@@ -674,16 +648,13 @@ hipError_t launch_scan_bwd(const BwdArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const size_t bt = static_cast<size_t>(a.batch) * a.seqlen;
   if (a.conv_w) {
-    const size_t runs = static_cast<size_t>(a.batch) * ((a.seqlen + kDxRun - 1) / kDxRun);
-    hipLaunchKernelGGL(bwd_conv_dx, dim3(blocks_for(runs * a.dim)), dim3(256), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int chunks = a.batch * ((a.seqlen + kConvChunk - 1) / kConvChunk);
-    hipLaunchKernelGGL(bwd_conv_w, dim3(blocks_for(a.dim), chunks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_conv_fix, dim3(blocks_for(static_cast<size_t>(a.batch) * bwd_runs(a.nseg) * a.dim)),
+                       dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(bwd_reduce_bc, dim3(static_cast<unsigned>(bt)), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_reduce_e, dim3(blocks_for(static_cast<size_t>(a.dim) * (kBwdPe + 5))), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_reduce_e, dim3(blocks_for(static_cast<size_t>(a.dim) * kBwdPe)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -241,8 +241,7 @@ hipError_t launch_chunk_decode(const ChunkDecodeLaunch& l, hipStream_t stream);
 constexpr int kBwdSeg = 16;     // time steps per segment (states recomputed in registers)
 constexpr int kBwdRun = 4;      // segments one wave of the main pass walks, last to first
 constexpr int kBwdWg = 4;       // 16-channel groups per main-pass workgroup (one wave each)
-constexpr int kBwdPe = 20;      // per-(batch, segment run, channel) partial: dA[16], dD, ddt_w, ddt_bias, pad
-constexpr int kConvChunk = 64;  // time steps per partial of the conv weight gradient
+constexpr int kBwdPe = 24;      // per-(batch, segment run, channel) partial: dA[16], dD, ddt_w, ddt_bias, dconv_w[4], dconv_b
 
 struct BwdArgs {
   // forward inputs
@@ -265,7 +264,8 @@ struct BwdArgs {
   // gradients (fp32; null: not written)
   float *dx, *dz, *ddt, *ddt_w, *ddt_bias, *dA, *dB, *dC, *dD, *dconv_w, *dconv_b, *dconv_cache, *dstate_in;
   // workspace
-  float *hs, *qs, *sdt, *dxc, *pB, *pC, *pr, *pe, *pw;
+  // xb: the conv-output gradient of the first 3 steps of every run
+  float *hs, *qs, *sdt, *xb, *pB, *pC, *pr, *pe;
   int batch, seqlen, dim, nseg, ngroups16;
   int x_bf16, dt_bf16, dt_rank1, bc_bf16, dy_bf16, dt_softplus;
   float dt_min, dt_max;
