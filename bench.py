@@ -864,7 +864,7 @@ def main():
                          "unit": "TFLOP/s", "frac": round(tf7 / FP32_VECTOR_PEAK_TFLOPS, 4),
                          "frac_of_unpacked": round(tf7 / (FP32_VECTOR_PEAK_TFLOPS / 2), 4),
                          "traffic": recorded_traffic("scan_bwd"),
-                         "kernel": "bwd_main (the backward walk over 16-step segments)",
+                         "kernel": "bwd_main (the backward walk: runs of four 16-step segments per wave)",
                          "flops_per_channel_step": BWD_FLOPS_PER_CH_STEP},
             "hbm": {"algorithmic_bytes": cfg7["bytes"],
                     "whole_call_frac": round(cfg7["bytes"] / (wall7 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
