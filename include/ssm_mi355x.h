@@ -68,7 +68,8 @@ typedef enum {
   SSM_ERR_INVALID_ARG = 1, /* a null required pointer, a negative size, bad bounds, wrong struct_size */
   SSM_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement (e.g. d_state != 16) */
   SSM_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_size query */
-  SSM_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+  SSM_ERR_HIP = 4,         /* the HIP runtime rejected a launch */
+  SSM_ERR_INTERNAL = 5     /* debug builds only: a launch plan broke an invariant its kernels rely on */
 } ssm_status_t;
 
 /* ------------------------------------------------------------------------
@@ -472,6 +473,28 @@ size_t ssm_params_sizeof(int32_t which);
  * hipEventElapsedTime(start, stop) is that kernel's duration.  The events are
  * only recorded, never created, synchronised or destroyed by the library. */
 void ssm_set_timing_events(void *start, void *stop);
+
+/* ---- debug builds (SSM_DEBUG) ---------------------------------------------
+ * For callers that want the host-side bounds checks: a build of the library
+ * with SSM_DEBUG defined (libssm_mi355x_debug.so, the same kernels) checks,
+ * before every launch of ssm_scan_fwd(_noalloc), ssm_chunk_scan_fwd and
+ * ssm_scan_bwd, the launch plan against the buffers the call describes: each
+ * grid's mapping from block ids to work items is a bijection onto the work,
+ * the time segments, chunk segments and summary pieces tile the sequence as
+ * the kernels assume, and every workspace region a kernel indexes is
+ * 256-byte aligned, lies inside workspace_bytes and overlaps no other.  A
+ * failure returns SSM_ERR_INTERNAL (ssm_last_error() names the check) and
+ * launches nothing.
+ * ssm_debug_checks: launch plans checked so far in this process (-1: a build
+ *   without the checks).
+ * ssm_debug_check_{scan,chunk,scan_bwd}: validation plus the plan checks of
+ *   that entry point without launching anything (runs without a GPU; pointers
+ *   are compared, never dereferenced); SSM_ERR_UNSUPPORTED in builds without
+ *   the checks. */
+long ssm_debug_checks(void);
+ssm_status_t ssm_debug_check_scan(const ssm_scan_params_t *p);
+ssm_status_t ssm_debug_check_chunk(const ssm_chunk_params_t *p);
+ssm_status_t ssm_debug_check_scan_bwd(const ssm_scan_bwd_params_t *p);
 
 #ifdef __cplusplus
 }

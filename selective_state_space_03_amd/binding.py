@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SSM_MI355X_LIB") or os.path.join(_HERE, "libssm_mi355x.so")
 
 SSM_F32, SSM_BF16 = 0, 1
-STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED", 3: "SSM_ERR_WORKSPACE", 4: "SSM_ERR_HIP"}
+STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED", 3: "SSM_ERR_WORKSPACE", 4: "SSM_ERR_HIP",
+          5: "SSM_ERR_INTERNAL"}
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -114,6 +115,7 @@ EXPORTED = [
     "ssm_layer_fwd", "ssm_layer_workspace_size", "ssm_layer_check",
     "ssm_scan_bwd", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd_check",
     "ssm_status_string", "ssm_last_error", "ssm_abi_version", "ssm_params_sizeof", "ssm_set_timing_events",
+    "ssm_debug_checks", "ssm_debug_check_scan", "ssm_debug_check_chunk", "ssm_debug_check_scan_bwd",
 ]
 
 _lib = None
@@ -126,7 +128,14 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing (build it with selective_state_space_03_amd.build.build())")
-    L = ctypes.CDLL(LIB_PATH)
+    _lib = load(LIB_PATH)
+    return _lib
+
+
+def load(path) -> ctypes.CDLL:
+    """Load a build of the library at path (the regular one, or its SSM_DEBUG
+    twin) with the argument types of every entry point declared."""
+    L = ctypes.CDLL(path)
     L.ssm_scan_fwd.argtypes = [ctypes.POINTER(ScanParams), _vp]
     L.ssm_scan_fwd.restype = _i32
     L.ssm_scan_check.argtypes = [ctypes.POINTER(ScanParams)]
@@ -177,11 +186,18 @@ def lib() -> ctypes.CDLL:
     L.ssm_params_sizeof.restype = ctypes.c_size_t
     L.ssm_set_timing_events.argtypes = [_vp, _vp]
     L.ssm_set_timing_events.restype = None
+    L.ssm_debug_checks.argtypes = []
+    L.ssm_debug_checks.restype = ctypes.c_long
+    L.ssm_debug_check_scan.argtypes = [ctypes.POINTER(ScanParams)]
+    L.ssm_debug_check_scan.restype = _i32
+    L.ssm_debug_check_chunk.argtypes = [ctypes.POINTER(ChunkParams)]
+    L.ssm_debug_check_chunk.restype = _i32
+    L.ssm_debug_check_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdParams)]
+    L.ssm_debug_check_scan_bwd.restype = _i32
     for i, st in enumerate((ScanParams, DecodeParams, ChunkParams, ChunkDecodeParams, LinearParams, LayerParams,
                             ScanBwdParams)):
         if L.ssm_params_sizeof(i) != ctypes.sizeof(st):
             raise RuntimeError(f"ctypes mirror of params struct {i} does not match the library")
-    _lib = L
     return L
 
 

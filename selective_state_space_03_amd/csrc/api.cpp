@@ -2,11 +2,13 @@
 // validation (pure host code, runs without a GPU), workspace sizing, variant
 // choice and launch on the caller's stream.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <limits>
 #include <string>
+#include <vector>
 
 #include "../../include/ssm_mi355x.h"
 #include "ssm_internal.h"
@@ -260,6 +262,9 @@ bool chunk_tuned(const ssm_chunk_params_t* p) {
   return p->d_state == ssm::kSsdN && p->chunk_size == ssm::kSsdQ && p->x_dtype == SSM_BF16 &&
          p->bc_dtype == SSM_BF16 && p->headdim % 16 == 0 && p->headdim <= ssm::kSsdMaxP;
 }
+
+void chunk_plan(const ssm_chunk_params_t* p, ssm::ChunkGenericArgs& g, ssm::ChunkLaunch& l);
+ssm_status_t debug_chunk(const ssm_chunk_params_t* p, const ssm::ChunkGenericArgs& g, const ssm::ChunkLaunch& l);
 
 size_t chunk_ws(const ssm_chunk_params_t* p) {
   if (p->batch <= 0 || p->seqlen <= 0) return 0;
@@ -580,6 +585,9 @@ BwdWs bwd_ws(const ssm_scan_bwd_params_t* p) {
   return o;
 }
 
+void bwd_plan(const ssm_scan_bwd_params_t* p, ssm::BwdArgs& a);
+ssm_status_t debug_bwd(const ssm_scan_bwd_params_t* p, const ssm::BwdArgs& a);
+
 ssm_status_t bwd_check(const ssm_scan_bwd_params_t* p) {
   if (!p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "params");
   if (p->struct_size != sizeof(ssm_scan_bwd_params_t))
@@ -684,9 +692,9 @@ size_t ssm_scan_workspace_size(const ssm_scan_params_t* p) {
 
 namespace {
 
-// The launch of a validated scan call (its workspace already in place).
-ssm_status_t scan_launch(const ssm_scan_params_t* p, void* stream) {
-  ssm::ScanLaunch l{};
+// The launch plan of a validated scan call (its workspace already in place).
+void scan_plan(const ssm_scan_params_t* p, ssm::ScanLaunch& l) {
+  l = ssm::ScanLaunch{};
   ssm::ScanKernelArgs& k = l.k;
   k.x = p->x;
   k.z = p->z;
@@ -740,6 +748,16 @@ ssm_status_t scan_launch(const ssm_scan_params_t* p, void* stream) {
   }
   k.bcg = l.bcg_out;
   k.qtab = l.qtab_out;
+}
+
+ssm_status_t debug_scan(const ssm_scan_params_t* p, const ssm::ScanLaunch& l);
+
+// The launch of a validated scan call (its workspace already in place).
+ssm_status_t scan_launch(const ssm_scan_params_t* p, void* stream) {
+  ssm::ScanLaunch l;
+  scan_plan(p, l);
+  const ssm_status_t d = debug_scan(p, l);
+  if (d != SSM_OK) return d;
   if (p->batch == 0) return ok();
   return hip_status(ssm::launch_scan(l, static_cast<hipStream_t>(stream)));
 }
@@ -839,8 +857,23 @@ ssm_status_t ssm_chunk_scan_fwd(const ssm_chunk_params_t* p, void* stream) {
   const ssm_status_t s = chunk_check(p);
   if (s != SSM_OK) return s;
   if (p->batch == 0) return ok();
+  ssm::ChunkGenericArgs g{};
+  ssm::ChunkLaunch l{};
+  chunk_plan(p, g, l);
+  const ssm_status_t d = debug_chunk(p, g, l);
+  if (d != SSM_OK) return d;
+  if (!chunk_tuned(p)) return hip_status(ssm::launch_chunk_generic(g, static_cast<hipStream_t>(stream)));
+  return hip_status(ssm::launch_chunk(l, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The launch plan of a validated chunked-scan call: g for the vector-ALU path,
+// l for the tuned matrix-core one (the one chunk_tuned(p) picks is filled).
+void chunk_plan(const ssm_chunk_params_t* p, ssm::ChunkGenericArgs& g, ssm::ChunkLaunch& l) {
   if (!chunk_tuned(p)) {
-    ssm::ChunkGenericArgs g{};
     g.x = p->x;
     g.dt = p->dt;
     g.dt_bias = p->dt_bias;
@@ -873,9 +906,8 @@ ssm_status_t ssm_chunk_scan_fwd(const ssm_chunk_params_t* p, void* stream) {
     g.dt_min = p->dt_min;
     g.dt_max = p->dt_max;
     softplus_thresholds(p->dt_min, p->dt_max, &g.sp_lo, &g.sp_hi);
-    return hip_status(ssm::launch_chunk_generic(g, static_cast<hipStream_t>(stream)));
+    return;
   }
-  ssm::ChunkLaunch l{};
   ssm::ChunkKernelArgs& k = l.k;
   k.x = p->x;
   k.dt = p->dt;
@@ -908,8 +940,11 @@ ssm_status_t ssm_chunk_scan_fwd(const ssm_chunk_params_t* p, void* stream) {
   l.x_dtype = p->x_dtype;
   l.bc_dtype = p->bc_dtype;
   l.out_dtype = p->out_dtype;
-  return hip_status(ssm::launch_chunk(l, static_cast<hipStream_t>(stream)));
 }
+
+}  // namespace
+
+extern "C" {
 
 ssm_status_t ssm_chunk_decode_check(const ssm_chunk_decode_params_t* p) {
   const ssm_status_t s = chunk_decode_check(p);
@@ -1091,10 +1126,23 @@ ssm_status_t ssm_scan_bwd(const ssm_scan_bwd_params_t* p, void* stream) {
   const ssm_status_t s = bwd_check(p);
   if (s != SSM_OK) return s;
   if (static_cast<size_t>(p->batch) * p->seqlen == 0) return ok();
+  ssm::BwdArgs a{};
+  bwd_plan(p, a);
+  const ssm_status_t d = debug_bwd(p, a);
+  if (d != SSM_OK) return d;
+  return hip_status(ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The launch plan of a validated backward call.
+void bwd_plan(const ssm_scan_bwd_params_t* p, ssm::BwdArgs& a) {
   const BwdWs o = bwd_ws(p);
   char* ws = static_cast<char*>(p->workspace);
   auto wf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-  ssm::BwdArgs a{};
+  a = ssm::BwdArgs{};
   a.x = p->x;
   a.dt = p->dt;
   a.dt_w = p->dt_rank1 ? p->dt_w : nullptr;
@@ -1144,8 +1192,11 @@ ssm_status_t ssm_scan_bwd(const ssm_scan_bwd_params_t* p, void* stream) {
   a.dt_softplus = p->dt_softplus ? 1 : 0;
   a.dt_min = p->dt_min;
   a.dt_max = p->dt_max;
-  return hip_status(ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream)));
 }
+
+}  // namespace
+
+extern "C" {
 
 const char* ssm_status_string(int32_t status) {
   switch (status) {
@@ -1154,6 +1205,7 @@ const char* ssm_status_string(int32_t status) {
     case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED";
     case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE";
     case SSM_ERR_HIP: return "SSM_ERR_HIP";
+    case SSM_ERR_INTERNAL: return "SSM_ERR_INTERNAL";
     default: return "unknown status";
   }
 }
@@ -1178,6 +1230,283 @@ size_t ssm_params_sizeof(int32_t which) {
     case 6: return sizeof(ssm_scan_bwd_params_t);
     default: return 0;
   }
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- debug build
+// With SSM_DEBUG the host checks every launch plan before it goes out against
+// the buffers the call describes, restating from the kernels' own indexing what
+// each of them touches: the mapping from block ids to work items is a
+// bijection, segments, chunks and summary pieces tile the sequence as the
+// kernels assume, and every workspace region a kernel indexes is 256-byte
+// aligned, inside the workspace and disjoint from the others.  Without
+// SSM_DEBUG the checks compile to nothing.
+
+namespace {
+
+#ifdef SSM_DEBUG
+std::atomic<long> g_debug_checks{0};
+
+ssm_status_t dbg_fail(const char* what) { return fail(SSM_ERR_INTERNAL, "debug check failed: %s", what); }
+
+struct Region {
+  const char* what;
+  size_t off, bytes;
+};
+
+ssm_status_t dbg_regions(const Region* r, int n, size_t ws_bytes) {
+  for (int i = 0; i < n; ++i) {
+    if (r[i].bytes == 0) continue;
+    if (r[i].off % 256) return dbg_fail(r[i].what);
+    if (r[i].off > ws_bytes || r[i].bytes > ws_bytes - r[i].off) return dbg_fail(r[i].what);
+    for (int j = 0; j < i; ++j)
+      if (r[j].bytes && r[i].off < r[j].off + r[j].bytes && r[j].off < r[i].off + r[i].bytes)
+        return dbg_fail(r[i].what);
+  }
+  return SSM_OK;
+}
+
+bool dbg_same(const void* arg, const void* base, size_t off) {
+  return arg == static_cast<const void*>(static_cast<const char*>(base) + off);
+}
+
+// The scan kernels' block ids -> positions of the (segment, batch, channel
+// group) order over nblk blocks (CU slot i % 256, round i / 256, the slots'
+// runs of consecutive positions): a permutation of [0, nblk).
+bool dbg_scan_mapping(long nblk) {
+  if (nblk <= 0) return true;
+  std::vector<unsigned char> seen(static_cast<size_t>(nblk), 0);
+  const long slots = ssm::kScanCuSlots, full = nblk / slots, rem = nblk % slots;
+  for (long i = 0; i < nblk; ++i) {
+    const long slot = i % slots, round = i / slots;
+    const long bid = slot * full + std::min(slot, rem) + round;
+    if (bid < 0 || bid >= nblk || seen[static_cast<size_t>(bid)]) return false;
+    seen[static_cast<size_t>(bid)] = 1;
+  }
+  return true;
+}
+
+// The chunked scan's block ids -> (batch, head, segment or piece k) over
+// batch x heads x nk blocks (heads in runs of H / 8 per XCD when H % 8 == 0):
+// each item exactly once.
+bool dbg_chunk_mapping(long batch, long heads, long nk) {
+  const long n = batch * heads * nk;
+  if (n <= 0) return true;
+  std::vector<unsigned char> seen(static_cast<size_t>(n), 0);
+  for (long bid = 0; bid < n; ++bid) {
+    long h, rest;
+    if (heads % 8 == 0) {
+      const long run = heads / 8;
+      rest = bid >> 3;
+      h = (bid & 7) * run + rest % run;
+      rest /= run;
+    } else {
+      h = bid % heads;
+      rest = bid / heads;
+    }
+    const long b = rest % batch, k = rest / batch;
+    if (h >= heads || k >= nk) return false;
+    const size_t item = static_cast<size_t>((k * batch + b) * heads + h);
+    if (seen[item]) return false;
+    seen[item] = 1;
+  }
+  return true;
+}
+#endif
+
+ssm_status_t debug_scan(const ssm_scan_params_t* p, const ssm::ScanLaunch& l) {
+#ifdef SSM_DEBUG
+  const ssm::ScanKernelArgs& k = l.k;
+  const long Bt = p->batch, L = p->seqlen, E = p->dim;
+  if (static_cast<long>(k.n_egroups) * 64 < E || static_cast<long>(k.n_egroups - 1) * 64 >= E)
+    return dbg_fail("scan: 64-channel groups do not cover the channels exactly");
+  if (Bt > 0 && L > 0) {
+    if (k.nseg < 1 || k.nseg > ssm::kScanMaxSplit) return dbg_fail("scan: segment count");
+    if (k.nseg == 1) {
+      if (k.seg_len != L) return dbg_fail("scan: one segment must span the sequence");
+    } else {
+      if (k.seg_len % ssm::kScanResc) return dbg_fail("scan: segments must start on a rescaling period");
+      if (k.seg_len < ssm::kConvK)
+        return dbg_fail("scan: a segment past the first starts before step 3 (only segment 0 may read the conv cache)");
+      if (static_cast<long>(k.nseg - 1) * k.seg_len >= L || static_cast<long>(k.nseg) * k.seg_len < L)
+        return dbg_fail("scan: segments do not tile the sequence (one empty or steps left over)");
+    }
+    const long groups = Bt * k.n_egroups;
+    if (!dbg_scan_mapping(groups * (k.nseg - 1)) || !dbg_scan_mapping(groups * k.nseg))
+      return dbg_fail("scan: block mapping is not a bijection");
+    // every step also reads the next step's row: batch x L + 1 rows
+    const size_t rows = (static_cast<size_t>(Bt) * L + 1) * ssm::kBcRow * sizeof(float);
+    const size_t bcg = ssm::scan_bcg_offset(p->batch, p->seqlen), qt = ssm::scan_qtab_offset(p->batch, p->seqlen);
+    const size_t so = ssm::scan_summary_offset(p->batch, p->seqlen);
+    if (bcg < rows) return dbg_fail("scan: packed B/C rows region too small");
+    if (!dbg_same(k.bc, p->workspace, 0)) return dbg_fail("scan: packed rows pointer");
+    Region r[5];
+    int n = 0;
+    r[n++] = {"scan: packed B/C rows region", 0, rows};
+    if (k.bcg) {
+      if (!dbg_same(k.bcg, p->workspace, bcg) || !dbg_same(k.qtab, p->workspace, qt))
+        return dbg_fail("scan: rescaled rows / table pointers");
+      if (so - qt < ssm::kScanTab * sizeof(float)) return dbg_fail("scan: q^k table region too small");
+      r[n++] = {"scan: rescaled rows region", bcg, rows};
+      r[n++] = {"scan: q^k table region", qt, ssm::kScanTab * sizeof(float)};
+    }
+    if (k.nseg > 1) {
+      const size_t ho = ssm::scan_head_offset(p->batch, p->seqlen, p->dim, k.nseg);
+      const size_t sb = static_cast<size_t>(groups) * (k.nseg - 1) * (ssm::kScanN + 1) * 64 * sizeof(float);
+      const size_t hb = static_cast<size_t>(groups) * ssm::kScanHead * 64 * sizeof(float);
+      if (!dbg_same(k.summ, p->workspace, so) || !dbg_same(k.head, p->workspace, ho))
+        return dbg_fail("scan: summary / saved-start pointers");
+      r[n++] = {"scan: segment summaries region", so, sb};
+      r[n++] = {"scan: saved segment-0 start region", ho, hb};
+    }
+    const ssm_status_t s = dbg_regions(r, n, p->workspace_bytes);
+    if (s != SSM_OK) return s;
+  }
+  g_debug_checks.fetch_add(1, std::memory_order_relaxed);
+#else
+  (void)p;
+  (void)l;
+#endif
+  return SSM_OK;
+}
+
+ssm_status_t debug_chunk(const ssm_chunk_params_t* p, const ssm::ChunkGenericArgs& g, const ssm::ChunkLaunch& l) {
+#ifdef SSM_DEBUG
+  const long Bt = p->batch, L = p->seqlen, H = p->nheads;
+  if (!chunk_tuned(p)) {
+    const long Q = g.chunk_size, nch = g.nchunks;
+    if (nch * Q < L || (nch > 0 && (nch - 1) * Q >= L)) return dbg_fail("chunked scan: chunks do not tile the sequence");
+    const size_t st = static_cast<size_t>(Bt) * nch * H * g.headdim * g.d_state * sizeof(float);
+    const size_t dec_off = ssm::chunk_generic_decay_offset(p->batch, p->seqlen, p->nheads, p->headdim, p->d_state,
+                                                           p->chunk_size);
+    if (nch > 0) {
+      if (!dbg_same(g.chunk_state, p->workspace, 0) || !dbg_same(g.chunk_decay, p->workspace, dec_off))
+        return dbg_fail("chunked scan: workspace pointers");
+      const Region r[2] = {{"chunked scan: chunk states region", 0, st},
+                           {"chunked scan: chunk decays region", dec_off, static_cast<size_t>(Bt) * nch * H * sizeof(float)}};
+      const ssm_status_t s = dbg_regions(r, 2, p->workspace_bytes);
+      if (s != SSM_OK) return s;
+    }
+  } else {
+    const ssm::ChunkKernelArgs& k = l.k;
+    const long nch = k.nchunks;
+    if (nch * ssm::kSsdQ < L || (nch > 0 && (nch - 1) * ssm::kSsdQ >= L))
+      return dbg_fail("chunked scan: chunks do not tile the sequence");
+    if (k.nseg < 1 || k.nseg > ssm::kSsdMaxSeg) return dbg_fail("chunked scan: segment count");
+    if (static_cast<long>(k.nseg) * k.cps < nch || (k.nseg > 1 && static_cast<long>(k.nseg - 1) * k.cps >= nch))
+      return dbg_fail("chunked scan: segments do not tile the chunks");
+    if (!dbg_chunk_mapping(Bt, H, k.nseg)) return dbg_fail("chunked scan: main-kernel block mapping");
+    if (k.nseg > 1) {
+      if (static_cast<long>(k.ppseg) * ssm::kSsdPiece < k.cps || static_cast<long>(k.ppseg - 1) * ssm::kSsdPiece >= k.cps)
+        return dbg_fail("chunked scan: summary pieces do not tile a segment");
+      if (!dbg_chunk_mapping(Bt, H, static_cast<long>(k.nseg - 1) * k.ppseg))
+        return dbg_fail("chunked scan: summary-kernel block mapping");
+      // the states entering segments 1.., the pieces' states, their decays
+      const size_t pn = static_cast<size_t>(k.headdim) * ssm::kSsdN;
+      const size_t sin = static_cast<size_t>(Bt) * H * (k.nseg - 1) * pn;
+      const size_t pieces = static_cast<size_t>(Bt) * H * (k.nseg - 1) * k.ppseg;
+      const size_t need = (sin + pieces * pn + pieces) * sizeof(float);
+      if (!dbg_same(k.ws, p->workspace, 0) || need > p->workspace_bytes)
+        return dbg_fail("chunked scan: segment workspace runs past the workspace");
+    }
+  }
+  g_debug_checks.fetch_add(1, std::memory_order_relaxed);
+#else
+  (void)p;
+  (void)g;
+  (void)l;
+#endif
+  return SSM_OK;
+}
+
+ssm_status_t debug_bwd(const ssm_scan_bwd_params_t* p, const ssm::BwdArgs& a) {
+#ifdef SSM_DEBUG
+  const size_t Bt = p->batch, L = p->seqlen, E = p->dim, N = ssm::kScanN;
+  const long S = a.nseg, R = ssm::bwd_runs(a.nseg), G64 = ssm::bwd_blocks64(p->dim);
+  if (S * ssm::kBwdSeg < static_cast<long>(L) || (S - 1) * ssm::kBwdSeg >= static_cast<long>(L))
+    return dbg_fail("backward: segments do not tile the sequence");
+  if (R * ssm::kBwdRun < S || (R - 1) * ssm::kBwdRun >= S) return dbg_fail("backward: runs do not tile the segments");
+  if (static_cast<long>(a.ngroups16) * 16 < static_cast<long>(E) || static_cast<long>(a.ngroups16 - 1) * 16 >= static_cast<long>(E))
+    return dbg_fail("backward: 16-channel groups do not cover the channels exactly");
+  if (G64 * ssm::kBwdWg < a.ngroups16 || (G64 - 1) * ssm::kBwdWg >= a.ngroups16)
+    return dbg_fail("backward: workgroups of four groups do not cover the groups exactly");
+  const BwdWs o = bwd_ws(p);
+  const void* ws = p->workspace;
+  if (!dbg_same(a.hs, ws, o.hs) || !dbg_same(a.qs, ws, o.qs) || !dbg_same(a.sdt, ws, o.sdt) ||
+      !dbg_same(a.pB, ws, o.pB) || !dbg_same(a.pC, ws, o.pC) || !dbg_same(a.pe, ws, o.pe) ||
+      (a.xb && !dbg_same(a.xb, ws, o.xb)) || (a.pr && !dbg_same(a.pr, ws, o.pr)))
+    return dbg_fail("backward: workspace pointers");
+  const Region r[8] = {
+      {"backward: segment states region", o.hs, Bt * S * E * N * 4},
+      {"backward: segment gradients region", o.qs, Bt * S * E * N * 4},
+      {"backward: segment dt sums region", o.sdt, Bt * S * E * 4},
+      {"backward: run-start conv gradients region", o.xb, a.xb ? Bt * R * 3 * E * 4 : 0},
+      {"backward: dB partials region", o.pB, Bt * L * G64 * N * 4},
+      {"backward: dC partials region", o.pC, Bt * L * G64 * N * 4},
+      {"backward: rank-1 dt partials region", o.pr, a.pr ? Bt * L * G64 * 4 : 0},
+      {"backward: per-run channel partials region", o.pe, Bt * R * E * ssm::kBwdPe * 4},
+  };
+  const ssm_status_t s = dbg_regions(r, 8, p->workspace_bytes);
+  if (s != SSM_OK) return s;
+  g_debug_checks.fetch_add(1, std::memory_order_relaxed);
+#else
+  (void)p;
+  (void)a;
+#endif
+  return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+long ssm_debug_checks(void) {
+#ifdef SSM_DEBUG
+  return g_debug_checks.load(std::memory_order_relaxed);
+#else
+  return -1;
+#endif
+}
+
+ssm_status_t ssm_debug_check_scan(const ssm_scan_params_t* p) {
+#ifdef SSM_DEBUG
+  const ssm_status_t s = scan_check(p);
+  if (s != SSM_OK) return s;
+  ssm::ScanLaunch l;
+  scan_plan(p, l);
+  return debug_scan(p, l);
+#else
+  (void)p;
+  return fail(SSM_ERR_UNSUPPORTED, "%s", "this build has no debug checks (SSM_DEBUG)");
+#endif
+}
+
+ssm_status_t ssm_debug_check_chunk(const ssm_chunk_params_t* p) {
+#ifdef SSM_DEBUG
+  const ssm_status_t s = chunk_check(p);
+  if (s != SSM_OK || p->batch == 0) return s;
+  ssm::ChunkGenericArgs g{};
+  ssm::ChunkLaunch l{};
+  chunk_plan(p, g, l);
+  return debug_chunk(p, g, l);
+#else
+  (void)p;
+  return fail(SSM_ERR_UNSUPPORTED, "%s", "this build has no debug checks (SSM_DEBUG)");
+#endif
+}
+
+ssm_status_t ssm_debug_check_scan_bwd(const ssm_scan_bwd_params_t* p) {
+#ifdef SSM_DEBUG
+  const ssm_status_t s = bwd_check(p);
+  if (s != SSM_OK || static_cast<size_t>(p->batch) * p->seqlen == 0) return s;
+  ssm::BwdArgs a{};
+  bwd_plan(p, a);
+  return debug_bwd(p, a);
+#else
+  (void)p;
+  return fail(SSM_ERR_UNSUPPORTED, "%s", "this build has no debug checks (SSM_DEBUG)");
+#endif
 }
 
 }  // extern "C"

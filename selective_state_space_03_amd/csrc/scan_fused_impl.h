@@ -53,7 +53,7 @@ namespace ssm {
 namespace {
 
 constexpr int kBlk = kScanBlk;          // steps per block: one tile of vector loads
-constexpr unsigned kCuSlots = 256;      // compute units the workgroups go round (MI355X)
+constexpr unsigned kCuSlots = kScanCuSlots;  // compute units the workgroups go round (MI355X)
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any range: the store is dropped
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer descriptor, gfx9 family
 

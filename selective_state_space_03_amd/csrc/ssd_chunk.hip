@@ -52,7 +52,7 @@ constexpr int kN = kSsdN;        // 64 states
 constexpr int kRowN = kN + 8;    // padded LDS row of N bf16 (144 bytes)
 constexpr int kRowQ = kQ + 8;    // padded LDS row of Q bf16 (272 bytes)
 constexpr int kThreads = 512;    // 8 waves
-constexpr int kPiece = 16;       // chunks per summary piece
+constexpr int kPiece = kSsdPiece;  // chunks per summary piece
 constexpr int kMaxSeg = kSsdMaxSeg;  // segments per sequence at most
 #ifndef SSD_KUNROLL
 #define SSD_KUNROLL 1

@@ -41,6 +41,7 @@ hipError_t timed_launch(hipStream_t s, F&& launch) {
 constexpr int kScanN = 16;         // d_state handled by the fused scan
 constexpr int kBcRow = 32;         // floats per packed row
 constexpr int kScanMaxSplit = 32;  // time segments per sequence
+constexpr unsigned kScanCuSlots = 256;  // compute units the scan's workgroups go round (MI355X)
 constexpr int kConvK = 4;
 constexpr int kScanBlk = 4;        // steps per tile of prefetched vector loads
 constexpr int kScanResc = 2 * kScanBlk;  // steps between rescalings of the scaled state (a pair of tiles); segments start at multiples of it
@@ -147,6 +148,7 @@ constexpr int kSsdN = 64;
 constexpr int kSsdQ = 128;
 constexpr int kSsdMaxP = 128;
 constexpr int kSsdMaxSeg = 16;
+constexpr int kSsdPiece = 16;  // chunks per segment summary piece
 
 struct ChunkKernelArgs {
   const void* x;
