@@ -112,6 +112,7 @@ ssm::ScanLaunch scan_variant(const ssm_scan_params_t* p) {
 
 int scan_split(const ssm_scan_params_t* p) {
   const int L = p->seqlen;
+  if (p->batch <= 0 || L <= 0 || p->dim <= 0) return 1;  // no work: nothing to split, no workspace
   int s = p->time_split;
   if (s <= 0) {
     const long groups = static_cast<long>(p->batch) * ((p->dim + 63) / 64);

@@ -17,9 +17,12 @@ def dev_tensor(w: W.Workload, key: str, device=DEV):
     a = w.arrays.get(key)
     if a is None:
         return None
+    a = np.ascontiguousarray(a)
+    if not a.flags.writeable:  # torch wants a writable source even for a copy to the device
+        a = a.copy()
     if key in w.bf16:
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
-    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
 
 
 def np64(t: torch.Tensor) -> np.ndarray:

@@ -138,6 +138,21 @@ def test_scan_noalloc_validation(L):
     assert b"at most 67108864" in L.ssm_last_error()
 
 
+def test_empty_batch_calls_return_ok_without_launching(L):
+    """batch = 0 through the sizing, validation and launch paths of the scan,
+    the decode step and the chunked scan: OK, a zero workspace, nothing
+    launched (no GPU here), and no division by the empty work count."""
+    p = _scan(batch=0, x=None, y=None, B=None, C=None, dt=None, workspace=None, workspace_bytes=0)
+    for split in (0, 1, 7, 32):
+        p.time_split = split
+        assert L.ssm_scan_workspace_size(ctypes.byref(p)) == 0
+        assert L.ssm_scan_check(ctypes.byref(p)) == 0, L.ssm_last_error()
+        assert L.ssm_scan_fwd(ctypes.byref(p), None) == 0, L.ssm_last_error()
+    c = _chunk(batch=0, x=None, dt=None, B=None, C=None, out=None, workspace=None, workspace_bytes=0)
+    assert L.ssm_chunk_scan_workspace_size(ctypes.byref(c)) == 0
+    assert L.ssm_chunk_scan_fwd(ctypes.byref(c), None) == 0, L.ssm_last_error()
+
+
 def _decode(**kw):
     from selective_state_space_03_amd import binding as b
 
