@@ -1,8 +1,9 @@
 """A host-sanitized build of the library for the CPU-side checks: the C-ABI
-layer (api.cpp: argument validation, workspace sizing, dispatch) compiled with
-AddressSanitizer and UndefinedBehaviorSanitizer on the host side only, linked
-with the kernels' objects of the regular build (build.py, which must have run
-first).  Device code is never built with a sanitizer.
+layer (api.cpp: argument validation, workspace sizing, dispatch, and the
+SSM_DEBUG launch-plan checks) compiled with AddressSanitizer and
+UndefinedBehaviorSanitizer on the host side only, linked with the kernels'
+objects of the regular build (build.py, which must have run first).  Device
+code is never built with a sanitizer.
 
     python -m selective_state_space_03_amd.build_sanitized
 
@@ -42,7 +43,7 @@ def build_host_sanitized(verbose: bool = False) -> str:
     for s in HOST_SAN:  # host side only: each sanitizer flag behind -Xarch_host
         san += ["-Xarch_host", f"-fsanitize={s}"]
     cmd = [b.hipcc(), "-O1", "-g", "-std=c++17", "-fPIC", f"--offload-arch={b.ARCH}", "-I", b.INCLUDE, "-I", b.CSRC,
-           *san, "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all",
+           *san, "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all", "-DSSM_DEBUG",
            "-c", os.path.join(b.CSRC, "api.cpp"), "-o", api_obj]
     link = [os.path.join(LLVM_BIN, "clang++"), "-shared", "-fPIC", "-fsanitize=" + ",".join(HOST_SAN),
             "-shared-libasan", api_obj, *objs, "-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lamdhip64",
