@@ -59,7 +59,7 @@ def test_decode_edge_sizes(dim):
     rng = np.random.Generator(np.random.PCG64(31))
     st0 = rng.standard_normal((1, dim, 16)).astype(np.float32)
     cc0 = rng.standard_normal((1, dim, 3)).astype(np.float32)
-    t = lambda k: torch.from_numpy(np.ascontiguousarray(w.arrays[k])).to(DEV)  # noqa: E731
+    t = lambda k: torch.from_numpy(np.array(w.arrays[k], copy=True)).to(DEV)  # noqa: E731
     st = torch.from_numpy(st0.copy()).to(DEV)
     cc = torch.from_numpy(cc0.copy()).to(DEV)
     o = w.opts
