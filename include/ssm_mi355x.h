@@ -104,10 +104,19 @@ typedef enum {
  *                 NULL when that size is 0); 256-byte aligned; not touched by other calls
  *   time_split    0: the library chooses; >= 1: split the sequence into at most that
  *                 many segments scanned in parallel and combined (at most 32; every
- *                 segment but the last spans a multiple of 8 steps)
+ *                 segment but the last spans a multiple of 8 steps);
+ *                 SSM_SCAN_BLOCKED (-1): one pass over 16-step blocks, 16 channels per
+ *                 wave, blocks whose dt sits at dt_max in every channel computed as
+ *                 matrix-core products of per-block tables (the chunk form of the
+ *                 velog page's "chunkscan"); it takes bf16 x and z, an E-wide bf16
+ *                 dt, no conv, SSM_EULER, dim % 64 == 0, x/z/dt/bf16 y 8-byte and
+ *                 fp32 y and ssm_state_out 16-byte aligned (else SSM_ERR_UNSUPPORTED).
+ *                 With 0 the library takes it for such calls when batch * dim / 64 >= 768.
  *   discretization SSM_EULER or SSM_ZOH (see ssm_discretization_t)
  * Supported: N = 16.  L = 0 only copies the state/cache inputs to the outputs.
  * ---------------------------------------------------------------------- */
+#define SSM_SCAN_BLOCKED (-1) /* ssm_scan_params_t.time_split: the blocked single-pass scan */
+
 typedef struct ssm_scan_params {
   uint32_t struct_size; /* = sizeof(ssm_scan_params_t) */
   int32_t batch, seqlen, dim, d_state;

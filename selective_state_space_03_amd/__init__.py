@@ -6,6 +6,7 @@ from .binding import (  # noqa: F401
     EXPORTED,
     Call,
     LIB_PATH,
+    SCAN_BLOCKED,
     SsmError,
     chunk_decode_step,
     chunk_scan_fwd,

@@ -19,6 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SSM_MI355X_LIB") or os.path.join(_HERE, "libssm_mi355x.so")
 
 SSM_F32, SSM_BF16 = 0, 1
+# time_split value of the blocked single-pass scan (SSM_SCAN_BLOCKED in the header)
+SCAN_BLOCKED = -1
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARG", 2: "SSM_ERR_UNSUPPORTED", 3: "SSM_ERR_WORKSPACE", 4: "SSM_ERR_HIP",
           5: "SSM_ERR_INTERNAL"}
 

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 # The same kernels with the host-side launch-plan checks of api.cpp (SSM_DEBUG)
 DEBUG_LIB_PATH = os.path.join(PKG, "libssm_mi355x_debug.so")
 SOURCES = ["api.cpp", "scan_fused.hip", "scan_xy_bb.hip", "scan_xy_bf.hip", "scan_xy_fb.hip", "scan_xy_ff.hip",
-           "decode_step.hip", "ssd_chunk.hip", "ssd_generic.hip", "ssd_decode.hip", "gemm.hip", "layer.hip", "scan_bwd.hip"]
+           "decode_step.hip", "ssd_chunk.hip", "ssd_generic.hip", "ssd_decode.hip", "gemm.hip", "layer.hip", "scan_bwd.hip",
+           "scan_blocked.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code: the compiler

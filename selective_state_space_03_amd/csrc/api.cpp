@@ -127,7 +127,30 @@ int scan_split(const ssm_scan_params_t* p) {
   return (L + seg - 1) / seg;
 }
 
+// The blocked single-pass kernel (scan_blocked.hip) takes bf16 u and z, an
+// E-wide bf16 dt, no conv, Euler, whole 64-channel groups, and the alignment
+// of its 8- and 16-byte accesses.
+bool scan_blocked_fits(const ssm_scan_params_t* p) {
+  const auto al = [](const void* q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) & (a - 1)) == 0; };
+  return p->x_dtype == SSM_BF16 && (!p->z || p->z_dtype == SSM_BF16) && !p->dt_rank1 && p->dt_dtype == SSM_BF16 &&
+         !p->conv_w && p->discretization == SSM_EULER && p->d_state == ssm::kScanN && p->dim > 0 &&
+         p->dim % 64 == 0 && al(p->x, 8) && al(p->z, 8) && al(p->dt, 8) &&
+         al(p->y, p->y_dtype == SSM_BF16 ? 8 : 16) && al(p->ssm_state_out, 16);
+}
+
+// Whether a call runs the blocked kernel: asked for (time_split =
+// SSM_SCAN_BLOCKED), or chosen (time_split = 0) when it fits and the batch's
+// channel groups fill every CU three times over (below that the time-split
+// kernels keep more waves busy).
+bool scan_blocked(const ssm_scan_params_t* p) {
+  if (p->batch <= 0 || p->seqlen <= 0) return false;
+  if (p->time_split == SSM_SCAN_BLOCKED) return true;
+  return p->time_split == 0 && scan_blocked_fits(p) &&
+         static_cast<long>(p->batch) * (p->dim / 64) >= ssm::kBlkAutoGroups;
+}
+
 size_t scan_ws(const ssm_scan_params_t* p) {
+  if (scan_blocked(p)) return ssm::scan_blk_workspace_bytes(p->batch, p->seqlen);
   return ssm::scan_workspace_bytes(p->batch, p->seqlen, p->dim, scan_split(p));
 }
 
@@ -145,8 +168,13 @@ ssm_status_t scan_check(const ssm_scan_params_t* p) {
       !valid_dtype(p->dt_dtype) || (p->z && !valid_dtype(p->z_dtype)))
     return fail(SSM_ERR_INVALID_ARG, "%s: unknown dtype", "x/y/bc/dt/z_dtype");
   if (p->z && p->z_dtype != p->x_dtype) return fail(SSM_ERR_UNSUPPORTED, "%s must equal x_dtype", "z_dtype");
-  if (p->time_split < 0 || p->time_split > ssm::kScanMaxSplit)
-    return fail(SSM_ERR_INVALID_ARG, "%s must be in [0, 32]", "time_split");
+  if (p->time_split < SSM_SCAN_BLOCKED || p->time_split > ssm::kScanMaxSplit)
+    return fail(SSM_ERR_INVALID_ARG, "%s must be in [-1, 32]", "time_split");
+  if (p->time_split == SSM_SCAN_BLOCKED && !scan_blocked_fits(p))
+    return fail(SSM_ERR_UNSUPPORTED,
+                "%s: the blocked scan takes bf16 x/z, E-wide bf16 dt, no conv, Euler, dim % 64 == 0, x/z/dt/y "
+                "8-byte and ssm_state_out 16-byte aligned (fp32 y: 16-byte)",
+                "time_split = SSM_SCAN_BLOCKED");
   if (!p->A) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", "A");
   if (p->conv_w) {
     if (p->conv_k != ssm::kConvK) return fail(SSM_ERR_UNSUPPORTED, "%s must be 4", "conv_k");
@@ -751,10 +779,50 @@ void scan_plan(const ssm_scan_params_t* p, ssm::ScanLaunch& l) {
   k.qtab = l.qtab_out;
 }
 
+// The launch plan of a validated call of the blocked kernel.
+void scan_blk_plan(const ssm_scan_params_t* p, ssm::ScanBlkLaunch& l) {
+  l = ssm::ScanBlkLaunch{};
+  ssm::ScanBlkArgs& k = l.k;
+  k.x = static_cast<const uint16_t*>(p->x);
+  k.z = static_cast<const uint16_t*>(p->z);
+  k.dt = static_cast<const uint16_t*>(p->dt);
+  k.y = p->y;
+  char* ws = static_cast<char*>(p->workspace);
+  l.rec_out = reinterpret_cast<unsigned char*>(ws);
+  l.qv_out = reinterpret_cast<float*>(ws + ssm::scan_blk_qv_offset(p->batch, p->seqlen));
+  k.rec = l.rec_out;
+  k.qv = l.qv_out;
+  k.A = p->A;
+  k.D = p->D;
+  k.dt_bias = p->dt_bias;
+  k.state_in = p->ssm_state_in;
+  k.state_out = p->ssm_state_out;
+  k.batch = p->batch;
+  k.seqlen = p->seqlen;
+  k.dim = p->dim;
+  k.nrec = ssm::scan_blk_records(p->seqlen);
+  k.dt_min = p->dt_min;
+  k.dt_max = p->dt_max;
+  softplus_thresholds(p->dt_min, p->dt_max, &k.sp_lo, &k.sp_hi);
+  k.dt_softplus = p->dt_softplus ? 1 : 0;
+  l.y_dtype = p->y_dtype;
+  l.bc_dtype = p->bc_dtype;
+  l.B = p->B;
+  l.C = p->C;
+}
+
 ssm_status_t debug_scan(const ssm_scan_params_t* p, const ssm::ScanLaunch& l);
+ssm_status_t debug_scan_blk(const ssm_scan_params_t* p, const ssm::ScanBlkLaunch& l);
 
 // The launch of a validated scan call (its workspace already in place).
 ssm_status_t scan_launch(const ssm_scan_params_t* p, void* stream) {
+  if (scan_blocked(p)) {
+    ssm::ScanBlkLaunch bl;
+    scan_blk_plan(p, bl);
+    const ssm_status_t d = debug_scan_blk(p, bl);
+    if (d != SSM_OK) return d;
+    return hip_status(ssm::launch_scan_blocked(bl, static_cast<hipStream_t>(stream)));
+  }
   ssm::ScanLaunch l;
   scan_plan(p, l);
   const ssm_status_t d = debug_scan(p, l);
@@ -782,7 +850,7 @@ ssm_status_t ssm_scan_fwd_noalloc(const ssm_scan_params_t* p, void* stream) {
                 "workspace/workspace_bytes");
   // sizes first, so a request past the scratch fails before the device is touched
   if (p->batch >= 0 && p->seqlen >= 0 && p->dim > 0 && p->d_state == ssm::kScanN &&
-      p->time_split >= 0 && p->time_split <= ssm::kScanMaxSplit) {
+      p->time_split >= SSM_SCAN_BLOCKED && p->time_split <= ssm::kScanMaxSplit) {
     const size_t need = scan_ws(p);
     if (need > ssm::kScanScratchBytes) {
       char buf[192];
@@ -1372,6 +1440,39 @@ ssm_status_t debug_scan(const ssm_scan_params_t* p, const ssm::ScanLaunch& l) {
   return SSM_OK;
 }
 
+ssm_status_t debug_scan_blk(const ssm_scan_params_t* p, const ssm::ScanBlkLaunch& l) {
+#ifdef SSM_DEBUG
+  const ssm::ScanBlkArgs& k = l.k;
+  const long Bt = p->batch, L = p->seqlen, E = p->dim;
+  if (E % 64) return dbg_fail("blocked scan: channels are not whole 64-channel groups");
+  if (static_cast<long>(k.nrec) * ssm::kBlkT < L || static_cast<long>(k.nrec - 1) * ssm::kBlkT >= L)
+    return dbg_fail("blocked scan: blocks do not tile the sequence");
+  // workgroup i -> (batch row i % Bt, channel group i / Bt): each pair once
+  const long groups = E / 64, n = Bt * groups;
+  std::vector<unsigned char> seen(static_cast<size_t>(n), 0);
+  for (long i = 0; i < n; ++i) {
+    const long b = i % Bt, g = i / Bt;
+    if (g >= groups || seen[static_cast<size_t>(b * groups + g)]) return dbg_fail("blocked scan: workgroup mapping");
+    seen[static_cast<size_t>(b * groups + g)] = 1;
+  }
+  // every batch row's buffer range stays below 2^31 bytes (32-bit offsets)
+  const size_t ybytes = p->y_dtype == SSM_BF16 ? 2 : 4;
+  if (static_cast<size_t>(L) * E * ybytes >= 0x80000000ULL) return dbg_fail("blocked scan: batch row range");
+  const size_t recb = static_cast<size_t>(Bt) * k.nrec * ssm::kBlkRec;
+  const size_t qo = ssm::scan_blk_qv_offset(p->batch, p->seqlen);
+  if (!dbg_same(k.rec, p->workspace, 0) || !dbg_same(k.qv, p->workspace, qo)) return dbg_fail("blocked scan: workspace pointers");
+  const Region r[2] = {{"blocked scan: block records region", 0, recb},
+                       {"blocked scan: per-call values region", qo, ssm::kBlkQv * sizeof(float)}};
+  const ssm_status_t s = dbg_regions(r, 2, p->workspace_bytes);
+  if (s != SSM_OK) return s;
+  g_debug_checks.fetch_add(1, std::memory_order_relaxed);
+#else
+  (void)p;
+  (void)l;
+#endif
+  return SSM_OK;
+}
+
 ssm_status_t debug_chunk(const ssm_chunk_params_t* p, const ssm::ChunkGenericArgs& g, const ssm::ChunkLaunch& l) {
 #ifdef SSM_DEBUG
   const long Bt = p->batch, L = p->seqlen, H = p->nheads;
@@ -1474,6 +1575,11 @@ ssm_status_t ssm_debug_check_scan(const ssm_scan_params_t* p) {
 #ifdef SSM_DEBUG
   const ssm_status_t s = scan_check(p);
   if (s != SSM_OK) return s;
+  if (scan_blocked(p)) {
+    ssm::ScanBlkLaunch bl;
+    scan_blk_plan(p, bl);
+    return debug_scan_blk(p, bl);
+  }
   ssm::ScanLaunch l;
   scan_plan(p, l);
   return debug_scan(p, l);

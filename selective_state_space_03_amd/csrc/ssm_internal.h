@@ -113,6 +113,47 @@ hipError_t launch_scan(const ScanLaunch& l, hipStream_t stream);
 constexpr size_t kScanScratchBytes = size_t(64) << 20;
 hipError_t scan_scratch(void** ptr);
 
+// ---- blocked scan (scan_blocked.hip) ---------------------------------------
+// The whole sequence in one pass of 16-step blocks, 16 channels per wave, the
+// saturated blocks' recurrence as matrix-core products of per-block tables
+// (see scan_blocked.hip).  Takes bf16 x / z / E-wide dt, no conv, Euler, dim a
+// multiple of 64.
+constexpr int kBlkT = 16;           // steps per block
+constexpr int kBlkRec = 5120;       // bytes of a (batch, block) table record
+constexpr int kBlkQv = 16 + (kBlkT + 1) * kScanN + 1;  // floats: log2 q_n, q_n^k (k = 0..16), flag
+constexpr long kBlkAutoGroups = 3L * kScanCuSlots;  // 64-channel groups from which the library chooses it
+
+struct ScanBlkArgs {
+  const uint16_t* x;    // u (batch, L, E) bf16
+  const uint16_t* z;    // (batch, L, E) bf16 or null
+  const uint16_t* dt;   // pre-activation (batch, L, E) bf16
+  void* y;
+  const unsigned char* rec;  // (batch, nrec) records, written by the packing kernel
+  const float* qv;           // kBlkQv floats, written by the packing kernel
+  const float* A;            // (dim, 16)
+  const float* D;            // (dim) or null
+  const float* dt_bias;      // (dim) or null
+  const float* state_in;
+  float* state_out;
+  int batch, seqlen, dim, nrec;
+  float dt_min, dt_max, sp_lo, sp_hi;
+  int dt_softplus;
+};
+
+struct ScanBlkLaunch {
+  ScanBlkArgs k;
+  int y_dtype, bc_dtype;
+  const void* B;
+  const void* C;
+  unsigned char* rec_out;  // = k.rec
+  float* qv_out;           // = k.qv
+};
+
+inline int scan_blk_records(int seqlen) { return (seqlen + kBlkT - 1) / kBlkT; }
+size_t scan_blk_qv_offset(int batch, int seqlen);
+size_t scan_blk_workspace_bytes(int batch, int seqlen);
+hipError_t launch_scan_blocked(const ScanBlkLaunch& l, hipStream_t stream);
+
 // ---- decode step ---------------------------------------------------------
 struct DecodeKernelArgs {
   const void* x;

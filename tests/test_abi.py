@@ -122,6 +122,52 @@ def test_scan_validation(L):
     assert L.ssm_scan_check(None) == 1
 
 
+def _bulk(**kw):
+    """A call the blocked scan takes: bf16 x / z / E-wide dt, no conv, dim % 64 == 0."""
+    base = dict(batch=8, seqlen=4096, dim=7680, dt_rank1=0, dt_dtype=1, dt_w=None, z=_addr(9), z_dtype=1)
+    base.update(kw)
+    return _scan(**base)
+
+
+def test_scan_blocked_selection(L):
+    """time_split = SCAN_BLOCKED asks for the blocked single-pass scan and is
+    refused (SSM_ERR_UNSUPPORTED) for calls it does not take; time_split = 0
+    takes it at 768 or more 64-channel groups (its workspace: one 5120-byte
+    record per batch row and 16-step block, then 1280 bytes of per-call
+    values) and keeps the time-split kernels below that."""
+    from selective_state_space_03_amd import binding as b
+
+    ws = lambda p: L.ssm_scan_workspace_size(ctypes.byref(p))  # noqa: E731
+    blk = 8 * 256 * 5120 + 1280
+    assert ws(_bulk()) == blk
+    assert ws(_bulk(time_split=b.SCAN_BLOCKED)) == blk
+    assert ws(_bulk(time_split=4)) != blk
+    assert ws(_bulk(seqlen=4097, time_split=b.SCAN_BLOCKED)) == 8 * 257 * 5120 + 1280
+    assert ws(_bulk(batch=6)) != 6 * 256 * 5120 + 1280  # 720 groups: below the automatic threshold
+    assert ws(_bulk(batch=6, time_split=b.SCAN_BLOCKED)) == 6 * 256 * 5120 + 1280
+    assert L.ssm_scan_check(ctypes.byref(_bulk(time_split=b.SCAN_BLOCKED))) == 0, L.ssm_last_error()
+    assert L.ssm_scan_check(ctypes.byref(_bulk(time_split=b.SCAN_BLOCKED, z=None, D=_addr(10)))) == 0
+    refused = {
+        "rank1": _bulk(dt_rank1=1, dt_dtype=0, dt_w=_addr(7)),
+        "conv": _bulk(conv_w=_addr(11)),
+        "dim": _bulk(dim=7616 + 32),
+        "x_f32": _bulk(x_dtype=0, z_dtype=0),
+        "dt_f32": _bulk(dt_dtype=0),
+        "zoh": _bulk(discretization=1),
+        "x_align": _bulk(x=_addr(1) + 2),
+        "y_f32_align": _bulk(y_dtype=0, y=_addr(2) + 8),
+        "state_align": _bulk(ssm_state_out=_addr(12) + 8),
+    }
+    for name, p in refused.items():
+        p.time_split = b.SCAN_BLOCKED
+        assert L.ssm_scan_check(ctypes.byref(p)) == 2, (name, L.ssm_last_error())
+        assert b"blocked" in L.ssm_last_error(), name
+        p.time_split = 0  # the library's own choice falls back to the time-split kernels
+        assert L.ssm_scan_check(ctypes.byref(p)) == 0, (name, L.ssm_last_error())
+        assert ws(p) != blk, name
+    assert L.ssm_scan_check(ctypes.byref(_bulk(time_split=-2))) == 1
+
+
 def test_scan_noalloc_validation(L):
     """ssm_scan_fwd_noalloc refuses, before touching a device: a NULL or
     mismatched struct, a workspace of the caller's (it uses its own scratch),

@@ -64,6 +64,12 @@ def test_scan_plans(D):
         p.workspace_bytes = D.ssm_scan_workspace_size(ctypes.byref(p))
         _ok(D, D.ssm_debug_check_scan, p, kw)
         n += 1
+    # the blocked single-pass scan: ragged tails, one partial block, batches
+    for batch, seqlen, dim in itertools.product((1, 3, 8), (1, 15, 16, 17, 4096, 4099), (64, 192, 7680)):
+        p = _scan(batch=batch, seqlen=seqlen, dim=dim, time_split=-1, dt_rank1=0, dt_dtype=1, dt_w=None)
+        p.workspace_bytes = D.ssm_scan_workspace_size(ctypes.byref(p))
+        _ok(D, D.ssm_debug_check_scan, p, ("blocked", batch, seqlen, dim))
+        n += 1
     assert D.ssm_debug_checks() - before == n
 
 

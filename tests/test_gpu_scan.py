@@ -216,21 +216,23 @@ def test_scan_prefill_full_size():
 
 @pytest.mark.parametrize("unsat", [False, True])
 def test_scan_bulk_full_size(unsat):
-    """Bulk scan at full size (batch 8, L 4096, E 7680, bf16 u/dt/z) in the launch
-    configuration the benchmark times (the library's own time split), fp32 output
-    held to 2e-3 max|y| and bf16 output to the same plus its rounding bound;
-    oracle on 48 sampled channels of batches 0 and 7.  unsat: the dt recipe
-    shifted so softplus and both clip edges run (the decay off the clip)."""
+    """Bulk scan at full size (batch 8, L 4096, E 7680, bf16 u/dt/z): the library's
+    own choice (time_split 0: the blocked single-pass kernel at this size, the
+    launch configuration the benchmark times) and the time-split kernels with 4
+    segments; fp32 output held to 2e-3 max|y| and bf16 output to the same plus
+    its rounding bound; oracle on 48 sampled channels of batches 0 and 7.
+    unsat: the dt recipe shifted so softplus and both clip edges run (the decay
+    off the clip)."""
     w = W.scan_bulk(unsaturated=unsat)
     ch = _sample(7680, 48, 22)
     yo, ho, _ = scan_oracle(w, batches=[0, 7], channels=ch)
     idx = torch.from_numpy(ch).to(DEV)
     bidx = torch.tensor([0, 7], device=DEV)
-    for y_dtype in (torch.float32, torch.bfloat16):
-        y, st, _ = scan_gpu(w, y_dtype=y_dtype)
-        check(np64(y.index_select(0, bidx).index_select(2, idx)), yo, TOL_BF16, f"bulk full y {y_dtype}",
+    for split, y_dtype in ((0, torch.float32), (0, torch.bfloat16), (4, torch.float32)):
+        y, st, _ = scan_gpu(w, y_dtype=y_dtype, time_split=split)
+        check(np64(y.index_select(0, bidx).index_select(2, idx)), yo, TOL_BF16, f"bulk full y {y_dtype} split={split}",
               out_bf16=(y_dtype == torch.bfloat16))
-        check(np64(st.index_select(0, bidx).index_select(1, idx)), ho, TOL_BF16, "bulk full state")
+        check(np64(st.index_select(0, bidx).index_select(1, idx)), ho, TOL_BF16, f"bulk full state split={split}")
         del y, st
         torch.cuda.empty_cache()
 
