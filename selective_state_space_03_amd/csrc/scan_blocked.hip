@@ -450,10 +450,8 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
       //   d = (f - 1) g(s-1) + (dt - dt_max) u B'_s,   f = exp((dt - dt_max) A),
       // which every later state of the block carries: y_t += C'_t . d for
       // t >= s, and the state leaving the block gains d.
-      f32x4 H1, dsum = {0.0f, 0.0f, 0.0f, 0.0f};
       // u and the pre-activation of step st of this lane's channel sit in
-      // lane row st / 4; the sums over rows broadcast them (no branches, so
-      // that the work overlaps the products)
+      // lane row st / 4; the sums over rows broadcast them
       auto off_step = [&](int st, float& du, f32x4& fm1) {
         const int i0 = st & 3;
         const bool mine = r == (st >> 2);
@@ -461,7 +459,8 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
         const float ps = add_half(add_pair(mine ? pre[i0] : 0.0f));
         float dt;
         if (a.dt_softplus) {
-          const float sp = fminf(fmaxf(softplus(ps), a.dt_min), dt_max);
+          float sp = fminf(fmaxf(softplus(ps), a.dt_min), dt_max);
+          asm volatile("" : "+v"(sp));  // formed for every lane: no branch around it
           dt = ps >= a.sp_hi ? dt_max : (ps <= a.sp_lo ? a.dt_min : sp);
         } else {
           dt = dt_clip(ps, a.dt_min, dt_max);
@@ -471,23 +470,43 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) fm1[i] = need ? exp2_fast(fmaf(dt, al[i], -cq[i])) - 1.0f : 0.0f;
       };
-      products(G, yv, H1);
-      for (uint32_t rest = off; rest != 0; rest &= rest - 1) {
-        const int st = __builtin_ctz(rest);
-        float du;
-        f32x4 fm1;
-        off_step(st, du, fm1);
-        const f32x4 Hs = update(G, u_kept(0, st - 1));  // g(s-1) without the earlier steps' differences
+      // y_t += C'_t . d for t >= st: the readout with C' rows t < st zeroed
+      // (lane l carries row l % 16 of the A operand), accumulated into y
+      auto add_readout = [&](const f32x4& d, int st) {
+        const uint4 tcm = (l & 15) >= st ? tc : make_uint4(0u, 0u, 0u, 0u);
+        uint32_t h01, l01, h23, l23;
+        split2(d[0], d[1], h01, l01);
+        split2(d[2], d[3], h23, l23);
+        yv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(tcm), as_bf16x8(make_uint4(h01, h23, h01, h23)), yv, 0, 0, 0);
+        yv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(make_uint4(tcm.x, tcm.y, tcm.x, tcm.y)),
+                                                     as_bf16x8(make_uint4(l01, l23, 0u, 0u)), yv, 0, 0, 0);
+      };
+      auto diff = [&](int st, const f32x4& dprev, float du, const f32x4& fm1, const f32x4& Hs) {
         const float4 b4 = *reinterpret_cast<const float4*>(&RB[st * kN + 4 * r]);
         const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
         f32x4 d;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] = fmaf(fm1[i], Hs[i] + dsum[i], du * bv[i]);
+        for (int i = 0; i < 4; ++i) d[i] = fmaf(fm1[i], Hs[i] + dprev[i], du * bv[i]);
+        return d;
+      };
+      // the first step off the clip in straight-line code beside the products
+      const int st0 = __builtin_ctz(off);
+      float du0;
+      f32x4 fm10, H1;
+      off_step(st0, du0, fm10);
+      const f32x4 Hs0 = update(G, u_kept(0, st0 - 1));  // g(st0 - 1)
+      products(G, yv, H1);
+      f32x4 dsum = diff(st0, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, du0, fm10, Hs0);
+      add_readout(dsum, st0);
+      // the others in order: g(s-1) from the products plus the earlier differences
+      for (uint32_t rest = off & (off - 1); rest != 0; rest &= rest - 1) {
+        const int st = __builtin_ctz(rest);
+        float du;
+        f32x4 fm1;
+        off_step(st, du, fm1);
+        const f32x4 d = diff(st, dsum, du, fm1, update(G, u_kept(0, st - 1)));
         dsum += d;
-        // y_t += C'_t . d for t >= st
-        const f32x4 Yc = readout(d);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) yv[i] += (4 * r + i >= st) ? Yc[i] : 0.0f;
+        add_readout(d, st);
       }
       G = (H1 + dsum) * q16;
     } else {
