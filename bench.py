@@ -93,11 +93,14 @@ def log(msg):
 # to the recorded value.
 SCAN_SOURCES = ("scan_fused.hip", "scan_fused_impl.h", "scan_xy_bb.hip", "scan_xy_bf.hip", "scan_xy_fb.hip",
                 "scan_xy_ff.hip")
-# the kernels of one ssm_scan_fwd call, in launch order (the time split's
-# summary pass and composition run only when the sequence is cut)
+# the kernels of one ssm_scan_fwd call, in launch order: the time-split
+# kernels (the summary pass and composition run only when the sequence is
+# cut), or the blocked single pass (its table packing, then the scan)
 SCAN_CALL_KERNELS = ("pack", "pass1", "compose", "main")
+BLOCKED_CALL_KERNELS = ("blkpack", "blkmain")
 KERNEL_SOURCES = {
     **{f"scan_{k}_{w}": SCAN_SOURCES for k in SCAN_CALL_KERNELS for w in ("prefill", "bulk")},
+    **{f"scan_{k}_bulk": ("scan_blocked.hip",) for k in BLOCKED_CALL_KERNELS},
     "decode": ("decode_step.hip",), "ssd": ("ssd_chunk.hip",), "ssd_decode": ("ssd_decode.hip",),
     "gemm_in_proj": ("gemm.hip",), "gemm_out_proj": ("gemm.hip",), "scan_bwd": ("scan_bwd.hip",),
 }
@@ -138,17 +141,29 @@ def recorded_traffic(kernel_key):
     return (fetch + write) * 1024.0
 
 
-def call_traffic(workload):
+def blocked_path(which, split):
+    """Whether the library runs the blocked single pass for this workload: the
+    bulk recipe (bf16 u / z / E-wide dt, no conv, 960 channel groups) with the
+    library's own choice (time_split 0) or asked for (time_split -1)."""
+    return which == "bulk" and split in (0, -1)
+
+
+def main_kernel_key(which, split):
+    return "scan_blkmain_bulk" if blocked_path(which, split) else f"scan_main_{which}"
+
+
+def call_traffic(workload, split=0):
     """HBM bytes of every kernel of one scan call (recorded profiles), summed;
     None unless each kernel the call ran has a current record."""
+    blocked = blocked_path(workload, split)
     total, seen = 0.0, 0
-    for k in SCAN_CALL_KERNELS:
+    for k in (BLOCKED_CALL_KERNELS if blocked else SCAN_CALL_KERNELS):
         t = recorded_traffic(f"scan_{k}_{workload}")
         if t is None:
             continue
         total += t
         seen += 1
-    main = recorded_traffic(f"scan_main_{workload}")
+    main = recorded_traffic(main_kernel_key(workload, split))
     return total if (seen and main is not None) else None
 
 
@@ -587,22 +602,27 @@ def scan_step_timing(torch, ssm, calls, steps, warmup, stream):
                 step=min(graph_ms, launch_ms))
 
 
-def scan_line(which, cfg, t, tokens):
+def scan_line(which, cfg, t, tokens, split=0):
     """Throughput and rooflines of one scan workload from its timings."""
     byts = cfg["bytes"]
     ch_steps = tokens * cfg["dim"]
     gflop = FLOPS_PER_CH_STEP[which] * ch_steps / 1e9
     kgbs = byts / (t["kmean"] * 1e-3) / 1e9
     cgbs = byts / (t["call"] * 1e-3) / 1e9
-    traffic = recorded_traffic(f"scan_main_{which}")
+    blocked = blocked_path(which, split)
+    traffic = recorded_traffic(main_kernel_key(which, split))
     roof = {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "scan_kernel (full pass)", "kernel_us": round(t["kmean"] * 1e3, 2),
+            "kernel": ("scan_blk_kernel (the whole sequence in one pass of 16-step blocks)" if blocked
+                       else "scan_kernel (full pass)"),
+            "kernel_us": round(t["kmean"] * 1e3, 2),
             "algorithmic_bytes": byts,
             "whole_call": {"us": round(t["call"] * 1e3, 2), "achieved": round(cgbs, 1),
-                           "frac": round(cgbs / HBM_PEAK_GBS, 4), "traffic": call_traffic(which),
-                           "note": "every kernel of one call (B/C packing, and with a time split the summary "
-                                   "pass and composition), back-to-back launches; traffic summed over them"},
+                           "frac": round(cgbs / HBM_PEAK_GBS, 4), "traffic": call_traffic(which, split),
+                           "note": ("every kernel of one call (the per-block table packing and the scan)" if blocked
+                                    else "every kernel of one call (B/C packing, and with a time split the "
+                                         "summary pass and composition)") +
+                                   ", back-to-back launches; traffic summed over them"},
             "alu": {"achieved_tflops": round(gflop / t["kmean"], 2), "peak_tflops": FP32_VECTOR_PEAK_TFLOPS,
                     "frac": round(gflop / t["kmean"] / FP32_VECTOR_PEAK_TFLOPS, 4),
                     "frac_of_unpacked": round(gflop / t["kmean"] / (FP32_VECTOR_PEAK_TFLOPS / 2), 4),
@@ -783,7 +803,7 @@ def main():
         "hbm_gbps": round(cfg["bytes"] / (wall * 1e-3) / 1e9, 1),
         "hbm_frac": round(cfg["bytes"] / (wall * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "channel_steps_per_s": round(tokens * cfg["dim"] / (wall * 1e-3), 1),
-        "roofline": scan_line(which, cfg, t, tokens),
+        "roofline": scan_line(which, cfg, t, tokens, a.split),
         "copy_gbps": round(COPY_GBS, 1),
     }
     if not a.no_variants:
@@ -806,6 +826,22 @@ def main():
         torch.cuda.empty_cache()
         if not a.no_variants:
             parts[f"scan_{other}"]["variants"] = run_variants(torch, ssm, W, other, dev, 5, 2)
+
+        if blocked_path(which, a.split):
+            log("part: the bulk call on the time-split kernels (4 segments)")
+            stream5 = torch.cuda.Stream(dev)
+            _, c5, cfg5 = scan_calls(torch, ssm, W, which, 1, dev, stream=stream5, split=4)
+            with torch.cuda.stream(stream5):
+                _, km5, _ = timed_loop(torch, ssm, c5, 5, 2)
+                _, call5, _ = timed_loop(torch, ssm, c5, 5, 2, per_launch=False)
+            parts["scan_bulk_time_split_4"] = {
+                "note": "the same bulk call with time_split = 4: B/C packing, a summary pass over segments 0-2, "
+                        "their composition, and the full pass (the library's choice below 768 channel groups)",
+                "ms_per_call": round(call5, 4), "main_kernel_us": round(km5 * 1e3, 2),
+                "hbm_frac_of_call": round(cfg5["bytes"] / (call5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic_of_call": call_traffic(which, 4)}
+            del c5
+            torch.cuda.empty_cache()
 
         log("part: sequence-length sweep of the layer prefill")
         parts["prefill_seqlen_sweep"] = seqlen_sweep(torch, ssm, W, dev)

@@ -1447,13 +1447,18 @@ ssm_status_t debug_scan_blk(const ssm_scan_params_t* p, const ssm::ScanBlkLaunch
   if (E % 64) return dbg_fail("blocked scan: channels are not whole 64-channel groups");
   if (static_cast<long>(k.nrec) * ssm::kBlkT < L || static_cast<long>(k.nrec - 1) * ssm::kBlkT >= L)
     return dbg_fail("blocked scan: blocks do not tile the sequence");
-  // workgroup i -> (batch row i % Bt, channel group i / Bt): each pair once
+  // workgroup i -> position in the (batch row, channel group) order: XCD
+  // i % 8 takes a contiguous range, each of its 32 CUs ((i / 8) % 32) a run
+  // within it; each position once
   const long groups = E / 64, n = Bt * groups;
   std::vector<unsigned char> seen(static_cast<size_t>(n), 0);
   for (long i = 0; i < n; ++i) {
-    const long b = i % Bt, g = i / Bt;
-    if (g >= groups || seen[static_cast<size_t>(b * groups + g)]) return dbg_fail("blocked scan: workgroup mapping");
-    seen[static_cast<size_t>(b * groups + g)] = 1;
+    const long x = i % 8, k = i / 8;
+    const long cnt = n / 8 + (x < n % 8 ? 1 : 0), start = x * (n / 8) + std::min(x, n % 8);
+    const long c = k % 32, round = k / 32, full = cnt / 32, rem = cnt % 32;
+    const long p = start + c * full + std::min(c, rem) + round;
+    if (p < 0 || p >= n || seen[static_cast<size_t>(p)]) return dbg_fail("blocked scan: workgroup mapping");
+    seen[static_cast<size_t>(p)] = 1;
   }
   // every batch row's buffer range stays below 2^31 bytes (32-bit offsets)
   const size_t ybytes = p->y_dtype == SSM_BF16 ? 2 : 4;

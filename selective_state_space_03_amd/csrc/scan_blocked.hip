@@ -132,6 +132,18 @@ __device__ __forceinline__ float pair_sum(float a, float b, bool half) {
   const auto p = __builtin_amdgcn_permlane16_swap(ia, ib, false, false);
   return __builtin_bit_cast(float, static_cast<int>(p[0])) + __builtin_bit_cast(float, static_cast<int>(p[1]));
 }
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+// v OR-ed with the same lane of the other three 16-lane rows
+__device__ __forceinline__ uint32_t or_rows(uint32_t v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(static_cast<int>(v), static_cast<int>(v), false, false);
+  v = static_cast<uint32_t>(p[0]) | static_cast<uint32_t>(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(static_cast<int>(v), static_cast<int>(v), false, false);
+  return static_cast<uint32_t>(q[0]) | static_cast<uint32_t>(q[1]);
+}
+
 // v summed with the same lane of the other row of its pair (rows 0 <-> 1,
 // 2 <-> 3), and with the same lane of the other 32-lane half
 __device__ __forceinline__ float add_pair(float v) { return pair_sum(v, v, false); }
@@ -223,6 +235,23 @@ __global__ __launch_bounds__(256) void pack_blk_kernel(const BT* __restrict__ B,
   }
 }
 
+// Position in the (batch row, channel group) order of workgroup i of n.
+// Workgroups go to the XCDs round-robin (i mod 8) and within an XCD to its 32
+// CUs round-robin ((i / 8) mod 32), one of a few rounds.  XCD x takes a
+// contiguous range of positions (with 8 batch rows: one row, so its L2 holds
+// that row's table records), and each of its CUs a run of consecutive
+// positions within it, so the workgroups a CU holds at once read adjacent
+// 128-byte pieces of the same rows.
+__device__ __forceinline__ unsigned blk_position(unsigned i, unsigned n) {
+  constexpr unsigned kXcd = 8, kCus = kScanCuSlots / kXcd;
+  const unsigned x = i % kXcd, k = i / kXcd;
+  const unsigned cnt = n / kXcd + (x < n % kXcd ? 1u : 0u);
+  const unsigned start = x * (n / kXcd) + min(x, n % kXcd);
+  const unsigned c = k % kCus, round = k / kCus;
+  const unsigned full = cnt / kCus, rem = cnt % kCus;
+  return start + c * full + min(c, rem) + round;
+}
+
 template <typename YT>
 struct alignas(16) BlkSmem {
   uint16_t in[2][3][kT][kCh];       // u, dt, z of a block (bf16), units permuted by swz
@@ -270,14 +299,8 @@ template <typename YT, bool GATE>
 __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
   __shared__ BlkSmem<YT> sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l >> 4, e = l & 15;
-  // Workgroups go to the 256 CUs round-robin (block i on CU i mod 256, one
-  // of 3 or 4 rounds): the CU's slot takes a run of consecutive positions of
-  // the (batch row, channel group) order, so the workgroups a CU holds at
-  // once read adjacent 128-byte pieces of the same rows.
-  const unsigned nblk = gridDim.x, slot = blockIdx.x % kScanCuSlots, round = blockIdx.x / kScanCuSlots;
-  const unsigned full = nblk / kScanCuSlots, rem = nblk % kScanCuSlots;
-  const unsigned pos = slot * full + min(slot, rem) + round;
   const unsigned ngroups = static_cast<unsigned>(a.dim) / kCh;
+  const unsigned pos = blk_position(blockIdx.x, gridDim.x);
   const int b = static_cast<int>(pos / ngroups);
   const int g = static_cast<int>(pos % ngroups);
   const int c = g * kCh + 16 * w + e;  // this lane's channel; its states are 4r..4r+3
@@ -361,13 +384,21 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
       zf[i] = GATE ? bf16_val(sm.in[buf][2][s][idx]) : 0.0f;
       sat[i] = pre[i] >= sat_pre;
     }
-    // the steps of the wave's tile with some channel off the clip (bit t)
-    uint32_t off = 0;
+    // the steps of the wave's tile with some channel off the clip (bit t):
+    // each lane's bits at 4r + i, OR-ed over its row (DPP rotations) and over
+    // the rows (permlane swaps)
+    uint32_t off;
+    {
+      uint32_t v = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint64_t m = __ballot(!sat[i]);  // lane (r, e) <-> step 4r + i
-#pragma unroll
-      for (int q = 0; q < 4; ++q) off |= ((m >> (16 * q)) & 0xffffu) ? (1u << (4 * q + i)) : 0u;
+      for (int i = 0; i < 4; ++i) v |= sat[i] ? 0u : (1u << i);
+      v <<= 4 * r;
+      v |= dpp_u32<0x121>(v);  // row_ror:1
+      v |= dpp_u32<0x122>(v);  // row_ror:2
+      v |= dpp_u32<0x124>(v);  // row_ror:4
+      v |= dpp_u32<0x128>(v);  // row_ror:8
+      v = or_rows(v);
+      off = __builtin_amdgcn_readfirstlane(v);
     }
     const bool whole = clip_free && T == kT;
     f32x4 yv;
