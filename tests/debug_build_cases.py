@@ -1,6 +1,6 @@
 """Parity cases run through the SSM_DEBUG build of the library (the binding
 loads whatever SSM_MI355X_LIB names): scans with time splits (and the
-no-allocation entry point), the chunked scan with segments on both of its
+no-allocation entry point), the blocked single pass, the chunked scan with segments on both of its
 paths, and the backward, each against the float64 oracle.  Every launch is
 preceded by the debug build's plan checks; the last line printed is the
 number of plans they checked.  Run by tests/test_gpu_debug_build.py in a
@@ -43,6 +43,12 @@ def main():
                              ssm_state_out=st, y_dtype=torch.float32, time_split=5)
     torch.cuda.synchronize()
     check(np64(y), yo, 2e-3, "debug build scan (no allocation)")
+    # the blocked single pass (bulk recipe, ragged tail)
+    w = W.scan_bulk(batch=2, seqlen=300, dim=128, unsaturated=True)
+    yo, ho, _ = scan_oracle(w)
+    y, st, _ = scan_gpu(w, time_split=ssm.SCAN_BLOCKED)
+    check(np64(y), yo, 2e-3, "debug build blocked scan")
+    check(np64(st), ho, 2e-3, "debug build blocked scan state")
     # chunked scan: the tuned kernel with segments and pieces, then a shape of the vector-ALU path
     w = W.ssd_long(batch=2, seqlen=2085, nheads=3, headdim=96, ngroups=1, gated=True, unsaturated=True)
     out, st = ssd_gpu(w, segments=3)

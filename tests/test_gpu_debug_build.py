@@ -1,5 +1,6 @@
 """The SSM_DEBUG build of the library on the GPU: the parity cases of
-tests/debug_build_cases.py (scan with splits and without allocation, chunked
+tests/debug_build_cases.py (scan with splits and without allocation, the blocked
+single pass, chunked
 scan with segments on both paths, backward) pass with the host-side launch-plan
 checks in front of every launch, and the checks ran."""
 import os
@@ -22,5 +23,5 @@ def test_debug_build_parity_and_checks():
     out = res.stdout + res.stderr
     assert res.returncode == 0, out[-4000:]
     checks = int(res.stdout.strip().splitlines()[-1])
-    # 4 scans + 1 without allocation + 2 chunked scans + 1 backward
-    assert checks == 8, out[-2000:]
+    # 4 scans + 1 without allocation + 1 blocked + 2 chunked scans + 1 backward
+    assert checks == 9, out[-2000:]

@@ -48,6 +48,28 @@ def test_scan_graph_replays(split):
         assert torch.equal(y, y_ref) and torch.equal(st, st_ref) and torch.equal(cc, cc_ref)
 
 
+def test_blocked_scan_graph_replays():
+    """The blocked single pass (table packing + scan) captured and replayed."""
+    w = W.scan_bulk(batch=2, seqlen=300, dim=128)
+    y_ref, st_ref, _ = scan_gpu(w, time_split=ssm.SCAN_BLOCKED)
+    o = w.opts
+    stream = torch.cuda.Stream(DEV)
+    y = torch.empty((2, 300, 128), dtype=torch.float32, device=DEV)
+    st = torch.empty((2, 128, 16), dtype=torch.float32, device=DEV)
+    call = ssm.scan_fwd(dev_tensor(w, "x"), dev_tensor(w, "A"), dev_tensor(w, "B"), dev_tensor(w, "C"),
+                        dev_tensor(w, "dt"), D=dev_tensor(w, "D"), z=dev_tensor(w, "z"),
+                        dt_bias=dev_tensor(w, "dt_bias"), dt_min=o["dt_min"], dt_max=o["dt_max"],
+                        ssm_state_out=st, y=y, time_split=ssm.SCAN_BLOCKED, stream=stream, prepare=True)
+    g = _capture(call, stream)
+    for _ in range(3):
+        for t in (y, st):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref) and torch.equal(st, st_ref)
+
+
 def test_decode_graph_replays():
     w = W.decode_stream(batch=8, dim=200, prefill=0, steps=1)
     t = lambda k: torch.from_numpy(np.ascontiguousarray(w.arrays[k])).to(DEV)

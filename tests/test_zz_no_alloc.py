@@ -64,6 +64,17 @@ def test_noalloc_matches_scan_fwd_twice_second_smaller():
     _same(r2[0], r2[1], "second call")
 
 
+def test_noalloc_blocked_matches_scan_fwd():
+    """The blocked single pass through both entry points (its table records in
+    the scratch), twice, the second call smaller."""
+    w1 = W.scan_bulk(batch=2, seqlen=333, dim=192)
+    r1 = _both(w1, time_split=ssm.SCAN_BLOCKED)
+    _same(r1[0], r1[1], "blocked, first call")
+    w2 = W.scan_bulk(batch=1, seqlen=40, dim=64, unsaturated=True)
+    r2 = _both(w2, time_split=ssm.SCAN_BLOCKED)
+    _same(r2[0], r2[1], "blocked, second call")
+
+
 def test_noalloc_refuses_past_its_scratch():
     w = W.scan_bulk(batch=64, seqlen=4096, dim=64)
     pos, kw = _args(w)
