@@ -81,6 +81,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 using rsrc_t = __amdgpu_buffer_rsrc_t;
 
 // Raw buffer descriptor over [p, p + bytes).  The words pass through
@@ -144,10 +145,6 @@ __device__ __forceinline__ uint32_t or_rows(uint32_t v) {
   return static_cast<uint32_t>(q[0]) | static_cast<uint32_t>(q[1]);
 }
 
-// v summed with the same lane of the other row of its pair (rows 0 <-> 1,
-// 2 <-> 3), and with the same lane of the other 32-lane half
-__device__ __forceinline__ float add_pair(float v) { return pair_sum(v, v, false); }
-__device__ __forceinline__ float add_half(float v) { return pair_sum(v, v, true); }
 __device__ __forceinline__ float row_transpose_sum(float x0, float x1, float x2, float x3) {
   const float s02 = pair_sum(x0, x2, true);   // [x0(r0+r2) x0(r1+r3) x2(r0+r2) x2(r1+r3)]
   const float s13 = pair_sum(x1, x3, true);   // the same for x1, x3
@@ -314,12 +311,15 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
   const rsrc_t rr = make_rsrc(a.rec + static_cast<size_t>(b) * nb * kBlkRec, static_cast<uint32_t>(nb) * kBlkRec);
 
   // staging: this lane moves 4 consecutive channels (unit e) of step row 4w + r
+  // (the unit's element offset in a step row of the batch row's u / dt / z,
+  // and its position in the LDS row)
   const int srow = 4 * w + r;
-  const uint32_t col0 = static_cast<uint32_t>(g * kCh + 4 * e);
-  const int su = (e ^ swz(srow)) * 4;  // the unit's position in the LDS row
+  const uint32_t sel = static_cast<uint32_t>(srow) * E + static_cast<uint32_t>(g * kCh + 4 * e);
+  const int su = (e ^ swz(srow)) * 4;
+  const uint32_t blk_el = kT * E;  // elements of one block of a batch row's u, dt, z or y
   auto issue = [&](int j, Stage& S) {
     const bool in = j >= 0 && j < nb;
-    const uint32_t vo = in ? ((static_cast<uint32_t>(j) * kT + srow) * E + col0) * 2u : kOob;
+    const uint32_t vo = in ? (static_cast<uint32_t>(j) * blk_el + sel) * 2u : kOob;
     S.u = ld64(rx, vo);
     S.d = ld64(rd, vo);
     if (GATE) S.z = ld64(rz, vo);
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
   };
   auto store_y = [&](int j) {
     const bool in = j >= 0;
-    const uint32_t vo = in ? ((static_cast<uint32_t>(j) * kT + srow) * E + col0) * static_cast<uint32_t>(sizeof(YT)) : kOob;
+    const uint32_t vo = in ? (static_cast<uint32_t>(j) * blk_el + sel) * static_cast<uint32_t>(sizeof(YT)) : kOob;
     const auto v = *reinterpret_cast<const typename YUnit<YT>::type*>(&sm.yt[j & 1][srow][su]);
     YUnit<YT>::store(ry, vo, v);
   };
@@ -371,15 +371,25 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
   auto compute = [&](int j, int buf) {
     const int T = min(kT, static_cast<int>(L) - kT * j);
     // (vector types: an element picked by a uniform index stays in registers)
-    u32x4 uh;
+    // (u of steps 4r, 4r + 1 and 4r + 2, 4r + 3 as two packed pairs, read
+    // straight into the halves of a word)
+    u32x2 up;
     f32x4 uf, pre, zf;
     bool sat[4];
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      const int idx = ((cu ^ swz(4 * r + i)) << 2) + ce;
+      u16x2 p;
+      p.x = sm.in[buf][0][4 * r + i][idx];
+      p.y = sm.in[buf][0][4 * r + i + 1][idx];
+      up[i >> 1] = __builtin_bit_cast(uint32_t, p);
+      uf[i] = __uint_as_float(up[i >> 1] << 16);
+      uf[i + 1] = __uint_as_float(up[i >> 1] & 0xffff0000u);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = 4 * r + i;
       const int idx = ((cu ^ swz(s)) << 2) + ce;
-      uh[i] = sm.in[buf][0][s][idx];
-      uf[i] = bf16_val(uh[i]);
       pre[i] = bf16_val(sm.in[buf][1][s][idx]) + bias;
       zf[i] = GATE ? bf16_val(sm.in[buf][2][s][idx]) : 0.0f;
       sat[i] = pre[i] >= sat_pre;
@@ -406,10 +416,10 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
     // H + B''^T U (not rescaled), U = the tile's u kept on steps lo..hi.
     const uint4 tc = *reinterpret_cast<const uint4*>(&sm.rec[buf][kRecTC + l * 16]);
     auto u_kept = [&](int lo, int hi) {
-      uint32_t um[4];
+      uint32_t km[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) um[i] = (4 * r + i >= lo && 4 * r + i <= hi) ? uh[i] : 0u;
-      const uint32_t uw0 = um[0] | (um[1] << 16), uw1 = um[2] | (um[3] << 16);
+      for (int i = 0; i < 4; ++i) km[i] = (4 * r + i >= lo && 4 * r + i <= hi) ? 0xffffu << (16 * (i & 1)) : 0u;
+      const uint32_t uw0 = up[0] & (km[0] | km[1]), uw1 = up[1] & (km[2] | km[3]);
       return as_bf16x8(make_uint4(uw0, uw1, uw0, uw1));
     };
     // C' H for a state H (its bf16 hi + lo): C'hi Hhi + C'lo Hhi, then C'hi Hlo
@@ -481,13 +491,13 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
       //   d = (f - 1) g(s-1) + (dt - dt_max) u B'_s,   f = exp((dt - dt_max) A),
       // which every later state of the block carries: y_t += C'_t . d for
       // t >= s, and the state leaving the block gains d.
-      // u and the pre-activation of step st of this lane's channel sit in
-      // lane row st / 4; the sums over rows broadcast them
+      // u and the pre-activation of step st of this lane's channel, read
+      // again from the block's LDS copy (the four lanes of a channel read
+      // one address)
       auto off_step = [&](int st, float& du, f32x4& fm1) {
-        const int i0 = st & 3;
-        const bool mine = r == (st >> 2);
-        const float us = add_half(add_pair(mine ? uf[i0] : 0.0f));
-        const float ps = add_half(add_pair(mine ? pre[i0] : 0.0f));
+        const int idx = ((cu ^ swz(st)) << 2) + ce;
+        const float us = bf16_val(sm.in[buf][0][st][idx]);
+        const float ps = bf16_val(sm.in[buf][1][st][idx]) + bias;
         float dt;
         if (a.dt_softplus) {
           float sp = fminf(fmaxf(softplus(ps), a.dt_min), dt_max);
@@ -570,12 +580,22 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
       }
     }
     // y = (C . h + D u) SiLU(z), written to the block's y tile
+    const int yidx = ((cu ^ swz(4 * r)) << 2) + ce;  // (the same unit position in the lane's four rows)
+    auto y_at = [&](int i) {
+      const float v = fmaf(dcoef, uf[i], yv[i]);
+      return GATE ? v * silu(zf[i]) : v;
+    };
+    if constexpr (sizeof(YT) == 2) {
+      // two steps per conversion, the halves to two rows
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = 4 * r + i;
-      float v = fmaf(dcoef, uf[i], yv[i]);
-      if (GATE) v *= silu(zf[i]);
-      YUnit<YT>::put(&sm.yt[buf][s][((cu ^ swz(s)) << 2) + ce], v);
+      for (int i = 0; i < 4; i += 2) {
+        const uint32_t pk = pk_bf16(y_at(i), y_at(i + 1));
+        sm.yt[buf][4 * r + i][yidx].bits = static_cast<uint16_t>(pk);
+        sm.yt[buf][4 * r + i + 1][yidx].bits = static_cast<uint16_t>(pk >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) YUnit<YT>::put(&sm.yt[buf][4 * r + i][yidx], y_at(i));
     }
   };
 
@@ -606,7 +626,15 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
     __syncthreads();
     store_y(nb - 1);
   }
-  if (a.state_out) *reinterpret_cast<f32x4*>(a.state_out + so) = G;
+  if (a.state_out) {
+    // the offset formed again from an opaque copy of the thread id: kept from
+    // the start, it would hold two registers through the loop
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    const int c2 = g * kCh + 16 * (t >> 6) + (t & 15);
+    const size_t so2 = (static_cast<size_t>(b) * E + c2) * kN + 4 * ((t >> 4) & 3);
+    *reinterpret_cast<f32x4*>(a.state_out + so2) = G;
+  }
 }
 
 template <typename YT, bool GATE>
