@@ -411,7 +411,9 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
       off = __builtin_amdgcn_readfirstlane(v);
     }
     const bool whole = clip_free && T == kT;
-    f32x4 yv;
+    // y of the block's steps, and the state leaving it before the rescale
+    // (one multiply after the three paths join, into the loop's register)
+    f32x4 yv, Hn;
     // The block's matrix products: the readout C' H + M U and the update
     // H + B''^T U (not rescaled), U = the tile's u kept on steps lo..hi.
     const uint4 tc = *reinterpret_cast<const uint4*>(&sm.rec[buf][kRecTC + l * 16]);
@@ -482,9 +484,7 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
     };
     if (whole && off == 0) {
       // every step at the clip: the block's products
-      f32x4 H1;
-      products(G, yv, H1);
-      G = H1 * q16;
+      products(G, yv, Hn);
     } else if (whole && __builtin_popcount(off) <= kMaxOff) {
       // The block's products as if at the clip, then for each step s off the
       // clip (in order) the difference it makes to the scaled state,
@@ -549,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
         dsum += d;
         add_readout(d, st);
       }
-      G = (H1 + dsum) * q16;
+      Hn = H1 + dsum;
     } else {
       // step by step through the whole block
       fill_table();
@@ -572,12 +572,13 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) yv[i] = row_transpose_sum(P[i], P[4 + i], P[8 + i], P[12 + i]);
-      if (T == kT) {
-        G *= q16;
-      } else {
+      Hn = G;
+    }
+    if (T == kT) {
+      G = Hn * q16;
+    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) G[i] *= a.qv[kQvPow + T * kN + 4 * r + i];
-      }
+      for (int i = 0; i < 4; ++i) G[i] = Hn[i] * a.qv[kQvPow + T * kN + 4 * r + i];
     }
     // y = (C . h + D u) SiLU(z), written to the block's y tile
     const int yidx = ((cu ^ swz(4 * r)) << 2) + ce;  // (the same unit position in the lane's four rows)
