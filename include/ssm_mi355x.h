@@ -24,9 +24,15 @@
  *                       with the chunk-final state carried to the next chunk.
  *
  * Conventions shared by every entry point
- *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
- *    allocates nothing, keeps no per-call state, never copies between host and
- *    device and never synchronises.
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The scan,
+ *    chunked-scan, decode and backward entry points allocate nothing, keep no
+ *    per-call state, never copy between host and device and never
+ *    synchronise.  The projection entry points (ssm_linear_fwd,
+ *    ssm_layer_fwd) are the exception: the first call of a shape on a device
+ *    creates that device's hipBLASLt handle and the shape's matmul plan, both
+ *    of which allocate host and device memory inside the GEMM library, and
+ *    keeps them until the process ends; later calls of the same shape
+ *    allocate nothing.
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *    null stream) and the call returns at once.  Asynchronous kernel faults
  *    surface at the caller's next synchronisation.
