@@ -1449,15 +1449,19 @@ ssm_status_t debug_scan_blk(const ssm_scan_params_t* p, const ssm::ScanBlkLaunch
     return dbg_fail("blocked scan: blocks do not tile the sequence");
   // workgroup i -> position in the (batch row, channel group) order: XCD
   // i % 8 takes a contiguous range, each of its 32 CUs ((i / 8) % 32) a run
-  // within it; each position once
+  // within it, round (i / 8) / 32 of the run; each position once.  The kernel
+  // hands a run's positions to its rounds in an order taken from dt_bias (a
+  // permutation of 0 .. len - 1), so the runs must partition the positions
+  // and every round must fall inside its run.
   const long groups = E / 64, n = Bt * groups;
   std::vector<unsigned char> seen(static_cast<size_t>(n), 0);
   for (long i = 0; i < n; ++i) {
     const long x = i % 8, k = i / 8;
     const long cnt = n / 8 + (x < n % 8 ? 1 : 0), start = x * (n / 8) + std::min(x, n % 8);
     const long c = k % 32, round = k / 32, full = cnt / 32, rem = cnt % 32;
+    const long len = full + (c < rem ? 1 : 0);
     const long p = start + c * full + std::min(c, rem) + round;
-    if (p < 0 || p >= n || seen[static_cast<size_t>(p)]) return dbg_fail("blocked scan: workgroup mapping");
+    if (round >= len || p < 0 || p >= n || seen[static_cast<size_t>(p)]) return dbg_fail("blocked scan: workgroup mapping");
     seen[static_cast<size_t>(p)] = 1;
   }
   // every batch row's buffer range stays below 2^31 bytes (32-bit offsets)

@@ -239,14 +239,41 @@ __global__ __launch_bounds__(256) void pack_blk_kernel(const BT* __restrict__ B,
 // that row's table records), and each of its CUs a run of consecutive
 // positions within it, so the workgroups a CU holds at once read adjacent
 // 128-byte pieces of the same rows.
-__device__ __forceinline__ unsigned blk_position(unsigned i, unsigned n) {
+//
+// Within a run the positions are handed out worst first: ranked by the
+// smallest dt_bias among their 64 channels (ties by position), the lowest goes
+// to round 0.  A channel whose bias sits low has dt below its upper clip on
+// many steps, so its wave takes the per-step corrections on most blocks and
+// its workgroup runs longest; the oldest waves of a SIMD win its issue
+// arbitration, so a slow workgroup started first ends sooner.  The ranks are
+// a permutation of the run's rounds (a strict order), so the mapping stays a
+// bijection onto the positions.  skey: 4 floats of LDS; every thread of the
+// workgroup calls this (it holds a barrier).
+__device__ __forceinline__ unsigned blk_position(unsigned i, unsigned n, unsigned ngroups, const float* bias,
+                                                 float* skey) {
   constexpr unsigned kXcd = 8, kCus = kScanCuSlots / kXcd;
   const unsigned x = i % kXcd, k = i / kXcd;
   const unsigned cnt = n / kXcd + (x < n % kXcd ? 1u : 0u);
   const unsigned start = x * (n / kXcd) + min(x, n % kXcd);
   const unsigned c = k % kCus, round = k / kCus;
   const unsigned full = cnt / kCus, rem = cnt % kCus;
-  return start + c * full + min(c, rem) + round;
+  const unsigned run0 = start + c * full + min(c, rem);
+  const unsigned len = full + (c < rem ? 1u : 0u);  // rounds of this CU slot: round < len
+  if (bias == nullptr || len < 2 || len > 4) return run0 + round;
+  // wave j: the smallest bias of the run's position j (NaN counts as +inf)
+  const unsigned tid = threadIdx.x, wv = tid >> 6;
+  float v = INFINITY;
+  if (wv < len) v = bias[((run0 + wv) % ngroups) * kCh + (tid & 63)];
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+  if ((tid & 63) == 0) skey[wv] = v != v ? INFINITY : v;
+  __syncthreads();
+  unsigned sel = 0;
+  for (unsigned j = 0; j < len; ++j) {
+    unsigned rank = 0;
+    for (unsigned m = 0; m < len; ++m) rank += (skey[m] < skey[j] || (skey[m] == skey[j] && m < j)) ? 1u : 0u;
+    if (rank == round) sel = j;
+  }
+  return run0 + sel;
 }
 
 template <typename YT>
@@ -297,7 +324,8 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
   __shared__ BlkSmem<YT> sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l >> 4, e = l & 15;
   const unsigned ngroups = static_cast<unsigned>(a.dim) / kCh;
-  const unsigned pos = blk_position(blockIdx.x, gridDim.x);
+  __shared__ float skey[4];
+  const unsigned pos = blk_position(blockIdx.x, gridDim.x, ngroups, a.dt_bias, skey);
   const int b = static_cast<int>(pos / ngroups);
   const int g = static_cast<int>(pos % ngroups);
   const int c = g * kCh + 16 * w + e;  // this lane's channel; its states are 4r..4r+3

@@ -137,3 +137,35 @@ def test_library_choice_on_a_small_call():
         y, st = _run(w, time_split=split)
         check(np64(y), yo, TOL, f"y split={split}")
         check(np64(st), ho, TOL, f"state split={split}")
+
+
+@pytest.mark.parametrize("bias", ["recipe", "equal", "descending", "extremes"])
+def test_blocked_workgroup_order_from_bias(bias):
+    """The bulk grid (batch 8, E 7680: 960 channel groups, runs of three and
+    four groups per CU slot) over two blocks, with dt_bias ordering the groups
+    of each run differently: the recipe's draw, every bias equal (ties), biases
+    falling with the channel (every run reversed) and biases of +-1e30 in some
+    channels.  y starts as NaN and every output is compared with the oracle,
+    so a group written twice or never fails."""
+    w = W.scan_bulk(batch=8, seqlen=32, dim=7680)
+    b = np.array(w.arrays["dt_bias"], dtype=np.float32, copy=True)
+    if bias == "equal":
+        b[:] = np.float32(0.25)
+    elif bias == "descending":
+        b = np.linspace(1.0, -2.0, b.size, dtype=np.float32)
+    elif bias == "extremes":
+        b[5::97] = np.float32(-1e30)
+        b[11::89] = np.float32(1e30)
+    w.arrays["dt_bias"] = b
+    o = w.opts
+    y = torch.full((8, 32, 7680), float("nan"), dtype=torch.float32, device=DEV)
+    st = torch.full((8, 7680, 16), float("nan"), dtype=torch.float32, device=DEV)
+    ssm.scan_fwd(dev_tensor(w, "x"), dev_tensor(w, "A"), dev_tensor(w, "B"), dev_tensor(w, "C"), dev_tensor(w, "dt"),
+                 D=dev_tensor(w, "D"), z=dev_tensor(w, "z"), dt_bias=dev_tensor(w, "dt_bias"),
+                 dt_softplus=o["dt_softplus"], dt_min=o["dt_min"], dt_max=o["dt_max"], ssm_state_out=st, y=y,
+                 time_split=ssm.SCAN_BLOCKED)
+    torch.cuda.synchronize()
+    yo, ho, _ = scan_oracle(w)
+    assert not torch.isnan(y).any() and not torch.isnan(st).any()
+    check(np64(y), yo, TOL, f"blocked y, bias {bias}")
+    check(np64(st), ho, TOL, f"blocked state, bias {bias}")
