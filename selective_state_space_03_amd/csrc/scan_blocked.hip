@@ -488,13 +488,19 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
       __builtin_amdgcn_wave_barrier();
     };
+    // (dt u, dt) of the next step, read from LDS one step ahead: its use
+    // opens a step, so a read issued with the step's own B' and C' rows would
+    // stall every step for a whole LDS round trip (the rows are used later
+    // in the step; reading them ahead as well leaves too few registers)
+    float2 vn;
     // one step on the scaled state: the factor exp((dt - dt_max) A) where dt
     // is off the clip (exp(dt A) without the scaled form), then dt u B'; the
     // lane's part of the readout C' . g
     auto step = [&](int s) {
-      const float2 v = fbw[s * kFbRow + e];
+      const float2 v = vn;
       const float4 b4 = *reinterpret_cast<const float4*>(&RB[s * kN + 4 * r]);
       const float4 c4 = *reinterpret_cast<const float4*>(&RC[s * kN + 4 * r]);
+      if (s + 1 < kT) vn = fbw[(s + 1) * kFbRow + e];
       const bool need = !(clip_free && v.y == dt_max);
       if (__any(need)) {
         // the factors for every lane, then kept where needed (no branch)
@@ -581,6 +587,7 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
     } else {
       // step by step through the whole block
       fill_table();
+      vn = fbw[e];
       float P[kT];
       auto pinned = [&](int s) {
         P[s] = step(s);
