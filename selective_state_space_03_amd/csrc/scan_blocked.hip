@@ -151,6 +151,34 @@ __device__ __forceinline__ float row_transpose_sum(float x0, float x1, float x2,
   return pair_sum(s02, s13, false);           // [sum x0, sum x1, sum x2, sum x3]
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// sum over the 16 lanes of each row, in every lane of the row
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror
+  x += dpp_f32<0x140>(x);  // row_mirror
+  return x;
+}
+// rows 1 and 3 receive rows 0 and 2 (rows 0 and 2 keep their own)
+__device__ __forceinline__ float from_row_below(float x) {
+  const int i = __builtin_bit_cast(int, x);
+  return __builtin_bit_cast(float, static_cast<int>(__builtin_amdgcn_permlane16_swap(i, i, false, false)[0]));
+}
+// row 1 in every row
+__device__ __forceinline__ float row1_everywhere(float x) {
+  const int i = __builtin_bit_cast(int, x);
+  const int y = static_cast<int>(__builtin_amdgcn_permlane32_swap(i, i, false, false)[0]);
+  return __builtin_bit_cast(float, static_cast<int>(__builtin_amdgcn_permlane16_swap(y, y, false, false)[1]));
+}
+// x of lane src (any lane of the wave)
+__device__ __forceinline__ float lane_val(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+}
+
 // The 4-element units of a step row (8 bytes in bf16, 16 in fp32) are
 // XOR-permuted by the row's group of four, so the four rows a wave reads in
 // one instruction (steps 4r + i, r = 0..3) fall on different banks.
@@ -383,6 +411,13 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
     q16[i] = a.qv[kQvPow + kT * kN + 4 * r + i];
   }
   const bool scaled = a.qv[kQvFlag] != 0.0f;
+  // per state n: log2 decay per unit dt and log2 q, of A's row 0 (the row
+  // every channel has where they are used), for the one-channel path
+  __shared__ float s_al[kN], s_cq[kN];
+  if (tid < kN) {
+    s_al[tid] = a.A[tid] * kLog2e;
+    s_cq[tid] = a.qv[kQvLog + tid];
+  }
   // steps at the clip need no factor and full blocks at the clip take the
   // matrix cores when the scaled form holds for every channel of the wave
   const bool clip_free = scaled && __all(same);
@@ -437,6 +472,12 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
       v |= dpp_u32<0x128>(v);  // row_ror:8
       v = or_rows(v);
       off = __builtin_amdgcn_readfirstlane(v);
+    }
+    // the channels of the tile with a step off the clip (bit e)
+    uint32_t chm;
+    {
+      const uint64_t m = __ballot(!(sat[0] && sat[1] && sat[2] && sat[3]));
+      chm = static_cast<uint32_t>(m | (m >> 16) | (m >> 32) | (m >> 48)) & 0xffffu;
     }
     const bool whole = clip_free && T == kT;
     // y of the block's steps, and the state leaving it before the rescale
@@ -519,6 +560,79 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
     if (whole && off == 0) {
       // every step at the clip: the block's products
       products(G, yv, Hn);
+    } else if (whole && __builtin_popcount(chm) == 1 && __builtin_popcount(off) >= 2) {
+      // Every step off the clip in the tile is in one channel, ec.  The
+      // tile's products (as if at the clip) serve the other fifteen; channel
+      // ec's block is taken again with the lanes on its states and steps:
+      // lane (q, n) runs state n over steps 4q .. 4q + 3 from zero (the
+      // scaled form's step, g = f g + dt u B'_s), the four quarters' maps
+      // x -> P x + Q are composed in row order across the rows, the state
+      // entering each quarter follows from the one entering the block, and
+      // the readout C'_t . g(t) is summed over the sixteen states of a row.
+      products(G, yv, Hn);
+      const int ec = __builtin_ctz(chm);
+      // lane indices formed again from an opaque copy of the lane id: formed
+      // from the kernel's own, their addresses would be held through the loop
+      int lo = l;
+      asm volatile("" : "+v"(lo));
+      const int qr = lo >> 4, ne = lo & 15;
+      // state ne of channel ec entering the block: component ne % 4 of lane
+      // 16 (ne / 4) + ec
+      const int hs = 16 * (ne >> 2) + ec;
+      const float g0 = lane_val(G[0], hs), g1 = lane_val(G[1], hs), g2 = lane_val(G[2], hs), g3 = lane_val(G[3], hs);
+      const float h0 = (ne & 2) ? ((ne & 1) ? g3 : g2) : ((ne & 1) ? g1 : g0);
+      const float bc = lane_val(bias, ec);
+      const int cuc = 4 * w + (ec >> 2), cec = ec & 3;
+      f32x4 gq, pq;
+      float gl = 0.0f, pl = 1.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int st = 4 * qr + i;
+        const int idx = ((cuc ^ swz(st)) << 2) + cec;
+        const float us = bf16_val(sm.in[buf][0][st][idx]);
+        const float ps = bf16_val(sm.in[buf][1][st][idx]) + bc;
+        float dt;
+        if (a.dt_softplus) {
+          float sp = fminf(fmaxf(softplus(ps), a.dt_min), dt_max);
+          asm volatile("" : "+v"(sp));  // formed for every lane: no branch around it
+          dt = ps >= a.sp_hi ? dt_max : (ps <= a.sp_lo ? a.dt_min : sp);
+        } else {
+          dt = dt_clip(ps, a.dt_min, dt_max);
+        }
+        const float f = dt == dt_max ? 1.0f : exp2_fast(fmaf(dt, s_al[ne], -s_cq[ne]));
+        gl = fmaf(f, gl, (dt * us) * RB[st * kN + ne]);
+        pl *= f;
+        gq[i] = gl;
+        pq[i] = pl;
+      }
+      // inclusive composition over the rows: rows 1 and 3 after rows 0 and
+      // 2, then rows 2 and 3 after rows 0 .. 1
+      float P = pq[3], Q = gq[3];
+      {
+        const float Pb = from_row_below(P), Qb = from_row_below(Q);
+        const bool odd = (qr & 1) != 0;
+        Q = odd ? fmaf(P, Qb, Q) : Q;
+        P = odd ? P * Pb : P;
+        const float P1 = row1_everywhere(P), Q1 = row1_everywhere(Q);
+        const bool hi = qr >= 2;
+        Q = hi ? fmaf(P, Q1, Q) : Q;
+        P = hi ? P * P1 : P;
+      }
+      const float hout = fmaf(P, h0, Q);  // state ne after quarter qr
+      const float hin_up = lane_val(hout, (lo + 48) & 63);
+      const float hin = qr == 0 ? h0 : hin_up;
+      const bool mine = ne == ec;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float yr = row_sum16(RC[(4 * qr + i) * kN + ne] * fmaf(pq[i], hin, gq[i]));  // y of step 4qr + i
+        yv[i] = mine ? yr : yv[i];
+      }
+      // the state leaving the block: state 4qr + j of channel ec is in lane 48 + 4qr + j
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float hj = lane_val(hout, 48 + 4 * qr + j);
+        Hn[j] = mine ? hj : Hn[j];
+      }
     } else if (whole && __builtin_popcount(off) <= kMaxOff) {
       // The block's products as if at the clip, then for each step s off the
       // clip (in order) the difference it makes to the scaled state,

@@ -169,3 +169,34 @@ def test_blocked_workgroup_order_from_bias(bias):
     assert not torch.isnan(y).any() and not torch.isnan(st).any()
     check(np64(y), yo, TOL, f"blocked y, bias {bias}")
     check(np64(st), ho, TOL, f"blocked state, bias {bias}")
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_blocked_one_channel_off_clip(with_state):
+    """Saturated calls in which, inside a 16 x 16 tile, every step off the clip
+    belongs to one channel: 2, 5, 8 and all 16 steps of a block, in channels
+    at the first, a middle and the last lane column of a wave, in different
+    waves and batch rows; next to tiles with two channels off (the per-step
+    corrections) and one step off.  Against the oracle, fp32 output."""
+    w = W.scan_bulk(batch=2, seqlen=80, dim=128)
+    dt = w.arrays["dt"]
+    if not dt.flags.writeable:
+        dt = w.arrays["dt"] = dt.copy()
+    low = np.uint16(0xC0A0)  # bf16 -5.0: off the clip for any bias here
+    cells = []
+    cells += [(0, t, 0) for t in (1, 9)]                       # block 0, channel 0: two steps
+    cells += [(0, t, 23) for t in (16, 18, 21, 27, 31)]        # block 1, channel 23: five steps
+    cells += [(0, t, 47) for t in range(32, 48, 2)]            # block 2, channel 47: eight steps
+    cells += [(1, t, 64) for t in range(48, 64)]               # block 3, batch 1, channel 64: every step
+    cells += [(1, t, 127) for t in (64, 79)]                   # block 4, last channel: first and last step
+    cells += [(1, 3, 100), (1, 3, 101), (1, 20, 7), (1, 40, 90)]  # two channels / single steps elsewhere
+    for b, t, e in cells:
+        dt[b, t, e] = low
+    st_in = None
+    if with_state:
+        rng = np.random.Generator(np.random.PCG64(31))
+        st_in = rng.standard_normal((2, 128, 16)).astype(np.float32)
+    y, st = _run(w, state_in=torch.from_numpy(st_in).to(DEV) if with_state else None)
+    yo, ho, _ = scan_oracle(w, state_in=st_in.astype(np.float64) if with_state else None)
+    check(np64(y), yo, TOL, "blocked y, one channel off the clip")
+    check(np64(st), ho, TOL, "blocked state, one channel off the clip")
