@@ -560,8 +560,9 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
     if (whole && off == 0) {
       // every step at the clip: the block's products
       products(G, yv, Hn);
-    } else if (whole && __builtin_popcount(chm) == 1 && __builtin_popcount(off) >= 2) {
-      // Every step off the clip in the tile is in one channel, ec.  The
+    } else if (whole && __builtin_popcount(chm) == 1 && __builtin_popcount(off) >= 3) {
+      // Every step off the clip in the tile (three or more: with fewer the
+      // per-step corrections below cost less) is in one channel, ec.  The
       // tile's products (as if at the clip) serve the other fifteen; channel
       // ec's block is taken again with the lanes on its states and steps:
       // lane (q, n) runs state n over steps 4q .. 4q + 3 from zero (the

@@ -174,10 +174,11 @@ def test_blocked_workgroup_order_from_bias(bias):
 @pytest.mark.parametrize("with_state", [False, True])
 def test_blocked_one_channel_off_clip(with_state):
     """Saturated calls in which, inside a 16 x 16 tile, every step off the clip
-    belongs to one channel: 2, 5, 8 and all 16 steps of a block, in channels
-    at the first, a middle and the last lane column of a wave, in different
-    waves and batch rows; next to tiles with two channels off (the per-step
-    corrections) and one step off.  Against the oracle, fp32 output."""
+    belongs to one channel: 3, 5, 8 and all 16 steps of a block (the
+    one-channel path) and 2 steps (the per-step corrections), in channels at
+    the first, a middle and the last lane column of a wave, in different
+    waves and batch rows; next to tiles with two channels off and with one
+    step off.  Against the oracle, fp32 output."""
     w = W.scan_bulk(batch=2, seqlen=80, dim=128)
     dt = w.arrays["dt"]
     if not dt.flags.writeable:
@@ -188,6 +189,7 @@ def test_blocked_one_channel_off_clip(with_state):
     cells += [(0, t, 23) for t in (16, 18, 21, 27, 31)]        # block 1, channel 23: five steps
     cells += [(0, t, 47) for t in range(32, 48, 2)]            # block 2, channel 47: eight steps
     cells += [(1, t, 64) for t in range(48, 64)]               # block 3, batch 1, channel 64: every step
+    cells += [(0, t, 33) for t in (50, 55, 60)]                # block 3, channel 33: three steps
     cells += [(1, t, 127) for t in (64, 79)]                   # block 4, last channel: first and last step
     cells += [(1, 3, 100), (1, 3, 101), (1, 20, 7), (1, 40, 90)]  # two channels / single steps elsewhere
     for b, t, e in cells:
