@@ -584,24 +584,30 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
       const float h0 = (ne & 2) ? ((ne & 1) ? g3 : g2) : ((ne & 1) ? g1 : g0);
       const float bc = lane_val(bias, ec);
       const int cuc = 4 * w + (ec >> 2), cec = ec & 3;
+      // dt and dt u of step ne of channel ec, formed once per step (every
+      // lane of a row column ne alike) and handed to the lanes that run it
+      float dts, dus;
+      {
+        const int idx = ((cuc ^ swz(ne)) << 2) + cec;
+        const float us = bf16_val(sm.in[buf][0][ne][idx]);
+        const float ps = bf16_val(sm.in[buf][1][ne][idx]) + bc;
+        if (a.dt_softplus) {
+          float sp = fminf(fmaxf(softplus(ps), a.dt_min), dt_max);
+          asm volatile("" : "+v"(sp));  // formed for every lane: no branch around it
+          dts = ps >= a.sp_hi ? dt_max : (ps <= a.sp_lo ? a.dt_min : sp);
+        } else {
+          dts = dt_clip(ps, a.dt_min, dt_max);
+        }
+        dus = dts * us;
+      }
       f32x4 gq, pq;
       float gl = 0.0f, pl = 1.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int st = 4 * qr + i;
-        const int idx = ((cuc ^ swz(st)) << 2) + cec;
-        const float us = bf16_val(sm.in[buf][0][st][idx]);
-        const float ps = bf16_val(sm.in[buf][1][st][idx]) + bc;
-        float dt;
-        if (a.dt_softplus) {
-          float sp = fminf(fmaxf(softplus(ps), a.dt_min), dt_max);
-          asm volatile("" : "+v"(sp));  // formed for every lane: no branch around it
-          dt = ps >= a.sp_hi ? dt_max : (ps <= a.sp_lo ? a.dt_min : sp);
-        } else {
-          dt = dt_clip(ps, a.dt_min, dt_max);
-        }
+        const float dt = lane_val(dts, st), du = lane_val(dus, st);
         const float f = dt == dt_max ? 1.0f : exp2_fast(fmaf(dt, s_al[ne], -s_cq[ne]));
-        gl = fmaf(f, gl, (dt * us) * RB[st * kN + ne]);
+        gl = fmaf(f, gl, du * RB[st * kN + ne]);
         pl *= f;
         gq[i] = gl;
         pq[i] = pl;
