@@ -201,6 +201,14 @@ __global__ __launch_bounds__(256) void pack_blk_kernel(const BT* __restrict__ B,
   const int b = blockIdx.x / nrec, blk = blockIdx.x % nrec;
   const int t0 = blk * kT;
   const int T = min(kT, seqlen - t0);
+  const int s = tid >> 4, n = tid & 15;
+  // this thread's B and C entries are requested first, so their loads are in
+  // flight while A and the decay tables are formed
+  // (a step past the end reads the block's first row and is zeroed below:
+  // no branch, so nothing waits for these loads before the tables)
+  const bool in = s < T;
+  const size_t o = (static_cast<size_t>(b) * seqlen + t0 + (in ? s : 0)) * kN + n;
+  const BT braw = B[o], craw = C[o];
   const double dm = dt_max;
   double amax = 0.0;
   for (int n = 0; n < kN; ++n) amax = fmax(amax, fabs(static_cast<double>(A[n])));
@@ -211,17 +219,8 @@ __global__ __launch_bounds__(256) void pack_blk_kernel(const BT* __restrict__ B,
     qp[k][n] = exp(x);
     qm[k][n] = exp(-x);
   }
-  const int s = tid >> 4, n = tid & 15;
-  {
-    float bv = 0.0f, cv = 0.0f;
-    if (s < T) {
-      const size_t o = (static_cast<size_t>(b) * seqlen + t0 + s) * kN + n;
-      bv = to_f32(B[o]);
-      cv = to_f32(C[o]);
-    }
-    sB[s][n] = bv;
-    sC[s][n] = cv;
-  }
+  sB[s][n] = in ? to_f32(braw) : 0.0f;
+  sC[s][n] = in ? to_f32(craw) : 0.0f;
   __syncthreads();
   unsigned char* R = rec + (static_cast<size_t>(b) * nrec + blk) * kBlkRec;
   const double bs = static_cast<double>(sB[s][n]) * qm[s + 1][n];  // B'_s[n]
