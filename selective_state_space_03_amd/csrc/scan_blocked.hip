@@ -389,10 +389,13 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
     *reinterpret_cast<uint4*>(&sm.rec[buf][tid * 16]) = S.r16;
     *reinterpret_cast<uint32_t*>(&sm.rec[buf][4096 + tid * 4]) = S.r4;
   };
-  auto store_y = [&](int j) {
+  // y of block j leaves in two parts: its LDS read goes out first after a
+  // barrier (ahead of the staging writes, so its latency overlaps them), the
+  // store once the staging is written
+  auto read_y = [&](int j) { return *reinterpret_cast<const typename YUnit<YT>::type*>(&sm.yt[j & 1][srow][su]); };
+  auto put_y = [&](int j, const typename YUnit<YT>::type& v) {
     const bool in = j >= 0;
     const uint32_t vo = in ? (static_cast<uint32_t>(j) * blk_el + sel) * static_cast<uint32_t>(sizeof(YT)) : kOob;
-    const auto v = *reinterpret_cast<const typename YUnit<YT>::type*>(&sm.yt[j & 1][srow][su]);
     YUnit<YT>::store(ry, vo, v);
   };
 
@@ -767,20 +770,26 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   for (int k = -4; k < nb; k += 2) {
     __syncthreads();
-    commit(1, S1);  // block k + 1
-    store_y(k - 1);
+    {
+      const auto yu = read_y(k - 1);
+      commit(1, S1);  // block k + 1
+      put_y(k - 1, yu);
+    }
     issue(k + 3, S1);
     if (k >= 0) compute(k, 0);
     __syncthreads();
-    commit(0, S0);  // block k + 2
-    store_y(k);
+    {
+      const auto yu = read_y(k);
+      commit(0, S0);  // block k + 2
+      put_y(k, yu);
+    }
     issue(k + 4, S0);
     if (k + 1 >= 0 && k + 1 < nb) compute(k + 1, 1);
   }
   // with an even count the last block was computed in a second half
   if ((nb & 1) == 0) {
     __syncthreads();
-    store_y(nb - 1);
+    put_y(nb - 1, read_y(nb - 1));
   }
   if (a.state_out) {
     // the offset formed again from an opaque copy of the thread id: kept from
