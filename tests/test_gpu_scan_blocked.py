@@ -171,18 +171,21 @@ def test_blocked_workgroup_order_from_bias(bias):
     check(np64(st), ho, TOL, f"blocked state, bias {bias}")
 
 
-@pytest.mark.parametrize("with_state", [False, True])
-def test_blocked_one_channel_off_clip(with_state):
+@pytest.mark.parametrize("with_state,softplus", [(False, True), (True, True), (False, False)])
+def test_blocked_one_channel_off_clip(with_state, softplus):
     """Saturated calls in which, inside a 16 x 16 tile, every step off the clip
     belongs to one channel: 3, 5, 8 and all 16 steps of a block (the
     one-channel path) and 2 steps (the per-step corrections), in channels at
     the first, a middle and the last lane column of a wave, in different
     waves and batch rows; next to tiles with two channels off and with one
-    step off.  Against the oracle, fp32 output."""
+    step off.  Against the oracle, fp32 output.  Without softplus (dt =
+    clip(pre)) every other step is put at the clip by a pre-activation of 2."""
     w = W.scan_bulk(batch=2, seqlen=80, dim=128)
     dt = w.arrays["dt"]
     if not dt.flags.writeable:
         dt = w.arrays["dt"] = dt.copy()
+    if not softplus:
+        dt[:] = np.uint16(0x4000)  # bf16 2.0
     low = np.uint16(0xC0A0)  # bf16 -5.0: off the clip for any bias here
     cells = []
     cells += [(0, t, 0) for t in (1, 9)]                       # block 0, channel 0: two steps
@@ -198,7 +201,7 @@ def test_blocked_one_channel_off_clip(with_state):
     if with_state:
         rng = np.random.Generator(np.random.PCG64(31))
         st_in = rng.standard_normal((2, 128, 16)).astype(np.float32)
-    y, st = _run(w, state_in=torch.from_numpy(st_in).to(DEV) if with_state else None)
-    yo, ho, _ = scan_oracle(w, state_in=st_in.astype(np.float64) if with_state else None)
+    y, st = _run(w, state_in=torch.from_numpy(st_in).to(DEV) if with_state else None, dt_softplus=softplus)
+    yo, ho, _ = _oracle(w, state_in=st_in.astype(np.float64) if with_state else None, dt_softplus=softplus)
     check(np64(y), yo, TOL, "blocked y, one channel off the clip")
     check(np64(st), ho, TOL, "blocked state, one channel off the clip")
