@@ -174,6 +174,32 @@ __device__ __forceinline__ float row1_everywhere(float x) {
   const int y = static_cast<int>(__builtin_amdgcn_permlane32_swap(i, i, false, false)[0]);
   return __builtin_bit_cast(float, static_cast<int>(__builtin_amdgcn_permlane16_swap(y, y, false, false)[1]));
 }
+// x of lane i of this lane's quad
+__device__ __forceinline__ float quad_lane(float x, int i) {
+  const int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (i) {
+    case 0: r = __builtin_amdgcn_update_dpp(0, v, 0x00, 0xF, 0xF, false); break;  // quad_perm [0, 0, 0, 0]
+    case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x55, 0xF, 0xF, false); break;  // quad_perm [1, 1, 1, 1]
+    case 2: r = __builtin_amdgcn_update_dpp(0, v, 0xAA, 0xF, 0xF, false); break;  // quad_perm [2, 2, 2, 2]
+    default: r = __builtin_amdgcn_update_dpp(0, v, 0xFF, 0xF, 0xF, false); break;  // quad_perm [3, 3, 3, 3]
+  }
+  return __builtin_bit_cast(float, r);
+}
+// row q (1 .. 3) receives row q - 1: rows 1 and 3 from the pair swap, row 2
+// from the half swap of the pair swap's odd rows (each swap of a register
+// with itself)
+__device__ __forceinline__ float from_row_above(float x, int q) {
+  const int i = __builtin_bit_cast(int, x);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(i, i, false, false);  // [x0 x0 x2 x2], [x1 x1 x3 x3]
+  const int o = static_cast<int>(p16[1]);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(o, o, false, false);  // [x1 x1 x1 x1], ...
+  // both swaps run with every lane active: a swap sunk into the branch of a
+  // row's choice would not see the rows it reads from
+  int r1 = static_cast<int>(p16[0]), r2 = static_cast<int>(p32[0]);
+  asm volatile("" : "+v"(r1), "+v"(r2));
+  return __builtin_bit_cast(float, q == 2 ? r2 : r1);
+}
 // x of lane src (any lane of the wave)
 __device__ __forceinline__ float lane_val(float x, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
@@ -584,15 +610,17 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
       const int hs = 16 * (ne >> 2) + ec;
       const float g0 = lane_val(G[0], hs), g1 = lane_val(G[1], hs), g2 = lane_val(G[2], hs), g3 = lane_val(G[3], hs);
       const float h0 = (ne & 2) ? ((ne & 1) ? g3 : g2) : ((ne & 1) ? g1 : g0);
-      const float bc = lane_val(bias, ec);
+      const float bc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bias), ec));
       const int cuc = 4 * w + (ec >> 2), cec = ec & 3;
-      // dt and dt u of step ne of channel ec, formed once per step (every
-      // lane of a row column ne alike) and handed to the lanes that run it
+      // dt and dt u of step 4 qr + ne % 4 of channel ec, formed once per
+      // lane and handed to the other lanes of its quad (each quad runs the
+      // row's four steps)
       float dts, dus;
       {
-        const int idx = ((cuc ^ swz(ne)) << 2) + cec;
-        const float us = bf16_val(sm.in[buf][0][ne][idx]);
-        const float ps = bf16_val(sm.in[buf][1][ne][idx]) + bc;
+        const int sq = 4 * qr + (ne & 3);
+        const int idx = ((cuc ^ swz(sq)) << 2) + cec;
+        const float us = bf16_val(sm.in[buf][0][sq][idx]);
+        const float ps = bf16_val(sm.in[buf][1][sq][idx]) + bc;
         if (a.dt_softplus) {
           float sp = fminf(fmaxf(softplus(ps), a.dt_min), dt_max);
           asm volatile("" : "+v"(sp));  // formed for every lane: no branch around it
@@ -607,7 +635,7 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int st = 4 * qr + i;
-        const float dt = lane_val(dts, st), du = lane_val(dus, st);
+        const float dt = quad_lane(dts, i), du = quad_lane(dus, i);
         const float f = dt == dt_max ? 1.0f : exp2_fast(fmaf(dt, s_al[ne], -s_cq[ne]));
         gl = fmaf(f, gl, du * RB[st * kN + ne]);
         pl *= f;
@@ -618,17 +646,20 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
       // 2, then rows 2 and 3 after rows 0 .. 1
       float P = pq[3], Q = gq[3];
       {
-        const float Pb = from_row_below(P), Qb = from_row_below(Q);
+        float Pb = from_row_below(P), Qb = from_row_below(Q);
+        asm volatile("" : "+v"(Pb), "+v"(Qb));  // (formed with every lane active)
         const bool odd = (qr & 1) != 0;
         Q = odd ? fmaf(P, Qb, Q) : Q;
         P = odd ? P * Pb : P;
-        const float P1 = row1_everywhere(P), Q1 = row1_everywhere(Q);
+        float P1 = row1_everywhere(P), Q1 = row1_everywhere(Q);
+        asm volatile("" : "+v"(P1), "+v"(Q1));
         const bool hi = qr >= 2;
         Q = hi ? fmaf(P, Q1, Q) : Q;
         P = hi ? P * P1 : P;
       }
       const float hout = fmaf(P, h0, Q);  // state ne after quarter qr
-      const float hin_up = lane_val(hout, (lo + 48) & 63);
+      float hin_up = from_row_above(hout, qr);
+      asm volatile("" : "+v"(hin_up));  // (formed with every lane active)
       const float hin = qr == 0 ? h0 : hin_up;
       const bool mine = ne == ec;
 #pragma unroll
