@@ -608,7 +608,8 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
       // state ne of channel ec entering the block: component ne % 4 of lane
       // 16 (ne / 4) + ec
       const int hs = 16 * (ne >> 2) + ec;
-      const float g0 = lane_val(G[0], hs), g1 = lane_val(G[1], hs), g2 = lane_val(G[2], hs), g3 = lane_val(G[3], hs);
+      float g0 = lane_val(G[0], hs), g1 = lane_val(G[1], hs), g2 = lane_val(G[2], hs), g3 = lane_val(G[3], hs);
+      asm volatile("" : "+v"(g0), "+v"(g1), "+v"(g2), "+v"(g3));  // (read with every lane active)
       const float h0 = (ne & 2) ? ((ne & 1) ? g3 : g2) : ((ne & 1) ? g1 : g0);
       const float bc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bias), ec));
       const int cuc = 4 * w + (ec >> 2), cec = ec & 3;
@@ -664,13 +665,15 @@ __global__ __launch_bounds__(kThreads, 4) void scan_blk_kernel(ScanBlkArgs a) {
       const bool mine = ne == ec;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float yr = row_sum16(RC[(4 * qr + i) * kN + ne] * fmaf(pq[i], hin, gq[i]));  // y of step 4qr + i
+        float yr = row_sum16(RC[(4 * qr + i) * kN + ne] * fmaf(pq[i], hin, gq[i]));  // y of step 4qr + i
+        asm volatile("" : "+v"(yr));  // (summed with every lane active)
         yv[i] = mine ? yr : yv[i];
       }
       // the state leaving the block: state 4qr + j of channel ec is in lane 48 + 4qr + j
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float hj = lane_val(hout, 48 + 4 * qr + j);
+        float hj = lane_val(hout, 48 + 4 * qr + j);
+        asm volatile("" : "+v"(hj));  // (read with every lane active)
         Hn[j] = mine ? hj : Hn[j];
       }
     } else if (whole && __builtin_popcount(off) <= kMaxOff) {
