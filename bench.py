@@ -635,11 +635,17 @@ def scan_line(which, cfg, t, tokens, split=0):
 
 def seqlen_sweep(torch, ssm, W, device, lengths=(512, 2048, 8192, 32768)):
     """The layer-prefill recipe (batch 1, E 7680) at several sequence lengths:
-    time per call, tokens/s, and the device memory the call needs beyond its
+    time per call, tokens/s, the device memory the call needs beyond its
     inputs and outputs (the library's workspace: packed B/C rows and segment
-    summaries), beside what storing every state (L, E, N) in fp32 would take."""
+    summaries), the peak of device memory allocated for the call's tensors
+    while it runs (measured: inputs, outputs and workspace), beside what
+    storing every state (L, E, N) in fp32 would take."""
     rows = []
     for L in lengths:
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated(device)
+        torch.cuda.reset_peak_memory_stats(device)
         w = W.scan_prefill(seqlen=L)
         stream = torch.cuda.Stream(device)
         _, calls, cfg = scan_calls(torch, ssm, W, "prefill", 1, device, stream=stream, w=w)
@@ -648,10 +654,11 @@ def seqlen_sweep(torch, ssm, W, device, lengths=(512, 2048, 8192, 32768)):
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
         with torch.cuda.stream(stream):
             _, call_ms, _ = timed_loop(torch, ssm, calls, 10, 2, per_launch=False)
+        peak = torch.cuda.max_memory_allocated(device) - base
         E, N = cfg["dim"], cfg["d_state"]
         rows.append({"seq_len": L, "ms_per_call": round(call_ms, 4), "tokens_per_s": round(L / (call_ms * 1e-3), 1),
                      "workspace_bytes": ws_bytes, "inputs_outputs_bytes": cfg["bytes"],
-                     "all_states_fp32_bytes": 4 * L * E * N})
+                     "peak_device_bytes": int(peak), "all_states_fp32_bytes": 4 * L * E * N})
         del calls
         torch.cuda.empty_cache()
     return {"note": "batch 1, E 7680, N 16, the layer-prefill recipe; the state carried between steps stays in "
